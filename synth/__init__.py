@@ -1,0 +1,114 @@
+"""Seeded synthetic inputs for the Q4 verify GEMM.
+
+This module is the only code that both the HIP path's tests/benchmarks and the
+CPU oracle's checks draw on.  It holds none of the method's arithmetic: it
+draws random codes, scales, biases and activations and lays the three weight
+planes side by side in one byte buffer.  It never dequantises or multiplies.
+
+Value distributions (the synthetic workload that stands in for real model
+weights and activations):
+
+* 4-bit codes uniform on 0..15 (every byte uniform on 0..255);
+* scale = bf16(|N(0, 0.02)| + 1e-3), one per output row and group of 64;
+* bias  = bf16(-8 * scale + N(0, 0.002)) using the already rounded scale, so
+  the affine weights centre near zero as in a symmetric 4-bit code;
+* activations x = bf16(N(0, 1)).
+
+Buffer layout (planar, the library's layout 0): ``[codes N*K/2 bytes]
+[scales N*K/64 bf16][biases N*K/64 bf16]``, each plane row-major by output
+row; two codes per byte, the even input in the low nibble.
+
+Random numbers come from torch's generator on the target device, seeded by a
+SplitMix64 hash of ``(seed, stream id)``, so GB-sized weights are drawn on the
+GPU in milliseconds.  Values drawn on the CPU and on a GPU differ; every check
+therefore hands the oracle the very bytes the GPU consumed.
+"""
+from __future__ import annotations
+
+import torch
+
+GROUP = 64
+_MASK64 = (1 << 64) - 1
+
+
+def _splitmix64(z: int) -> int:
+    """One SplitMix64 output step (Steele, Lea and Flood, 2014)."""
+    z = (z + 0x9E3779B97F4A7C15) & _MASK64
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _MASK64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _MASK64
+    return z ^ (z >> 31)
+
+
+def stream_seed(seed: int, *ids: int) -> int:
+    """63-bit generator seed for tensor stream ``ids`` under ``seed``."""
+    z = _splitmix64(int(seed) & _MASK64)
+    for i in ids:
+        z = _splitmix64(z ^ (int(i) & _MASK64))
+    return z >> 1
+
+
+def _gen(device, seed: int, *ids: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(stream_seed(seed, *ids))
+    return g
+
+
+def packed_size(N: int, K: int) -> int:
+    """Byte count of the planar buffer (plane sizes added up)."""
+    return N * K // 2 + 2 * (2 * (N * K // GROUP))
+
+
+def planes(packed: torch.Tensor, N: int, K: int):
+    """Views ``(codes [N, K/2] u8, scales [N, K/64] bf16, biases [N, K/64]
+    bf16)`` into a planar buffer."""
+    G = K // GROUP
+    a = N * K // 2
+    b = a + 2 * N * G
+    c = b + 2 * N * G
+    codes = packed[:a].view(N, K // 2)
+    scales = packed[a:b].view(torch.bfloat16).view(N, G)
+    biases = packed[b:c].view(torch.bfloat16).view(N, G)
+    return codes, scales, biases
+
+
+def q4_weights(N: int, K: int, seed: int = 0, stream: int = 0,
+               device="cpu") -> torch.Tensor:
+    """Seeded packed Q4 weights [N, K] as a flat uint8 tensor on ``device``."""
+    if K % GROUP or N < 1 or K < GROUP:
+        raise ValueError(f"need N >= 1 and K a positive multiple of {GROUP}")
+    dev = torch.device(device)
+    packed = torch.empty(packed_size(N, K), dtype=torch.uint8, device=dev)
+    codes, scales, biases = planes(packed, N, K)
+    G = K // GROUP
+    codes.copy_(torch.randint(0, 256, (N, K // 2), dtype=torch.uint8,
+                              device=dev, generator=_gen(dev, seed, stream, 1)))
+    s32 = torch.randn((N, G), dtype=torch.float32, device=dev,
+                      generator=_gen(dev, seed, stream, 2)).mul_(0.02).abs_()
+    s16 = s32.add_(1e-3).to(torch.bfloat16)
+    scales.copy_(s16)
+    noise = torch.randn((N, G), dtype=torch.float32, device=dev,
+                        generator=_gen(dev, seed, stream, 3)).mul_(0.002)
+    biases.copy_((s16.float() * -8.0 + noise).to(torch.bfloat16))
+    return packed
+
+
+def activations(M: int, K: int, seed: int = 0, stream: int = 0,
+                device="cpu") -> torch.Tensor:
+    """Seeded bf16 activations x [M, K] ~ N(0, 1)."""
+    dev = torch.device(device)
+    x = torch.randn((M, K), dtype=torch.float32, device=dev,
+                    generator=_gen(dev, seed, stream, 4))
+    return x.to(torch.bfloat16)
+
+
+def bf16_bits(t: torch.Tensor):
+    """Raw bf16 bit patterns of a tensor as a numpy uint16 array (CPU)."""
+    return t.detach().to("cpu").contiguous().view(torch.int16).numpy().view(
+        "uint16")
+
+
+def from_bf16_bits(bits, device="cpu") -> torch.Tensor:
+    """bf16 tensor from raw uint16 bit patterns."""
+    import numpy as np
+    arr = np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)
+    return torch.from_numpy(arr.copy()).view(torch.bfloat16).to(device)

@@ -1,0 +1,100 @@
+"""Small helpers shared by the tests: exact arithmetic and buffer assembly.
+
+Nothing here computes the method: the exact-rational helpers below are the
+independent yardstick the oracle is checked against.
+"""
+from __future__ import annotations
+
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def read_golden(name: str) -> dict:
+    """Parse a ``name = value | citation`` fixture into {name: value}."""
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            lhs, _, _cite = line.partition("|")
+            key, _, val = lhs.partition("=")
+            val = val.strip()
+            out[key.strip()] = float(val) if "." in val else int(val)
+    return out
+
+
+def bf16_bits_of(values) -> np.ndarray:
+    """bf16 bit patterns (RNE) of float values given as numpy/python floats."""
+    t = torch.tensor(np.asarray(values, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def bits_to_float(bits) -> np.ndarray:
+    """float32 values of bf16 bit patterns (exact)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32)
+
+
+def assemble(codes: np.ndarray, scale_bits: np.ndarray,
+             bias_bits: np.ndarray) -> np.ndarray:
+    """Planar packed buffer from code bytes [N, K/2] and bf16 bit planes
+    [N, K/64]."""
+    N, half = codes.shape
+    K = 2 * half
+    packed = torch.empty(synth.packed_size(N, K), dtype=torch.uint8)
+    c, s, b = synth.planes(packed, N, K)
+    c.copy_(torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)))
+    s.view(torch.int16).copy_(torch.from_numpy(
+        np.ascontiguousarray(scale_bits, dtype=np.uint16).view(np.int16)))
+    b.view(torch.int16).copy_(torch.from_numpy(
+        np.ascontiguousarray(bias_bits, dtype=np.uint16).view(np.int16)))
+    return packed.numpy().copy()
+
+
+def split_planes(packed: np.ndarray, N: int, K: int):
+    """(codes u8 [N, K/2], scale bits u16 [N, K/64], bias bits u16 [N, K/64])."""
+    t = torch.from_numpy(np.ascontiguousarray(packed, dtype=np.uint8))
+    c, s, b = synth.planes(t, N, K)
+    return (c.numpy().copy(), s.view(torch.int16).numpy().view(np.uint16).copy(),
+            b.view(torch.int16).numpy().view(np.uint16).copy())
+
+
+def pack_codes(q: np.ndarray) -> np.ndarray:
+    """Code bytes [N, K/2] from 4-bit codes [N, K]: even k in the low nibble
+    (the reading of the byte order this build takes)."""
+    q = np.asarray(q, dtype=np.uint8)
+    assert q.max(initial=0) <= 15
+    return (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+
+
+def frac(x) -> Fraction:
+    return Fraction(float(x))
+
+
+def round_f32(v: Fraction) -> np.float32:
+    """Round an exact rational to the nearest fp32 (ties to even)."""
+    if v == 0:
+        return np.float32(0.0)
+    sign = -1 if v < 0 else 1
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    quantum_exp = max(e - 23, -149)
+    scaled = a / (Fraction(2) ** quantum_exp)
+    n = scaled.numerator // scaled.denominator
+    rem = scaled - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    val = Fraction(n) * Fraction(2) ** quantum_exp
+    if val >= Fraction(2) ** 128:
+        return np.float32(sign * np.inf)
+    return np.float32(sign * float(val))
