@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Benchmark of the Q4 verify GEMM on one MI355X.
+
+One step = one q4_gemm_verify call at M = 16 verify rows on the fused MLP
+gate+up projection of the 27B target (N = 34816 outputs, K = 5120 inputs,
+100,270,080 packed weight bytes), the shape the pages' model spends most of
+its weight bytes on.  The same shape is also timed at M = 1 (one decode row)
+for the M=16/M=1 time ratio.
+
+Protocol (the prediction-first page's order: stamp, count bytes, predict,
+warm up, measure):
+  * stamp: device, architecture, CU count, software versions, UTC time;
+  * algorithmic bytes per call = 9NK/16 (weights) + 2MK (x) + 4MN (y), and
+    the floor time at the 8 TB/s HBM peak, printed before measuring;
+  * weights are rotated over >= 1.2 GB of distinct copies so that neither the
+    L2 nor the 256 MB Infinity Cache can serve a repeated read;
+  * W warm-up steps, then K timed steps between device synchronisations;
+    each launch is also bracketed by HIP events on the launch stream, which
+    gives the per-launch kernel duration for the roofline figure.
+
+Output: one JSON line on stdout.  `value` is the effective bandwidth of the
+M = 16 step (algorithmic bytes / mean step time, inputs resident in HBM).
+`roofline.traffic` comes from the committed rocprofv3 counter summary when
+that summary was taken of the current kernel source, else null.
+`cpu_baseline` times the CPU oracle (test infrastructure, never tuned) on the
+host cores on the whole gate+up matrix at M = 16.
+"""
+from __future__ import annotations
+
+import argparse
+import datetime
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("Q4 verify GEMM effective HBM GB/s (% of peak) and M=16/M=1 time "
+          "ratio")
+HBM_PEAK_GBPS = 8000.0
+WORKLOADS = {
+    "gate_up": (34816, 5120),
+    "down": (5120, 17408),
+    "lm_head": (248320, 5120),
+    "attn_in": (14336, 5120),
+    "o_proj": (5120, 6144),
+    "gdn_in": (16640, 5120),
+}
+KERNEL_SOURCE = os.path.join(ROOT, "speculative_verify_gemm_q4_amd", "csrc",
+                             "q4verify_kernels.hip")
+COUNTERS = os.path.join(ROOT, "profiles",
+                        "q4_gemm_gate_up_34816x5120_counters.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def alg_bytes(M, N, K):
+    return 9 * N * K // 16 + 2 * M * K + 4 * M * N
+
+
+def kernel_source_hash():
+    with open(KERNEL_SOURCE, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
+
+
+def stamp(torch):
+    p = torch.cuda.get_device_properties(0)
+    return {
+        "device": p.name,
+        "arch": getattr(p, "gcnArchName", ""),
+        "cus": p.multi_processor_count,
+        "hbm_gib": round(p.total_memory / 2 ** 30, 1),
+        "torch": torch.__version__,
+        "hip": getattr(torch.version, "hip", None),
+        "host": platform.node(),
+        "utc": datetime.datetime.now(datetime.timezone.utc).isoformat(
+            timespec="seconds"),
+    }
+
+
+def load_traffic(M, N, K):
+    """Per-launch HBM bytes from the committed counter summary, if it was
+    taken of the current kernel source for this shape and M."""
+    if not os.path.exists(COUNTERS):
+        return None
+    try:
+        with open(COUNTERS) as fh:
+            rec = next(json.loads(line) for line in fh
+                       if line.strip().startswith("{"))
+    except (StopIteration, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    per_m = rec.get("per_M", {}).get(str(M))
+    if not per_m or rec.get("N") != N or rec.get("K") != K:
+        return None
+    return per_m.get("hbm_bytes_per_launch")
+
+
+def time_calls(torch, q4, xs, Ws, y, M, N, K, steps, warmup):
+    """Warm up, then time `steps` calls; returns (wall ms per step, list of
+    per-launch event durations in ms)."""
+    stream = torch.cuda.current_stream()
+    n_w = len(Ws)
+    for i in range(warmup):
+        q4.q4_gemm_verify(xs, Ws[i % n_w], y, M, N, K)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    outer0 = torch.cuda.Event(enable_timing=True)
+    outer1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    outer0.record(stream)
+    for i in range(steps):
+        starts[i].record(stream)
+        q4.q4_gemm_verify(xs, Ws[i % n_w], y, M, N, K)
+        ends[i].record(stream)
+    outer1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    per_launch = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    outer_ms = outer0.elapsed_time(outer1)
+    return outer_ms / steps, wall_ms / steps, per_launch
+
+
+def stream_probe(torch, q4, nbytes):
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.random_(0, 255)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        q4.q4_stream_read(buf, nbytes, sink)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = 10
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        q4.q4_stream_read(buf, nbytes, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del buf
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def cpu_baseline(torch, W, x16, N, K, budget_s):
+    import oracle
+    import synth
+    threads = min(16, len(os.sched_getaffinity(0)))
+    W_host = W.cpu().numpy()
+    x_bits = synth.bf16_bits(x16)
+    M = x16.shape[0]
+    # bounded sample: whole row blocks of the matrix until ~budget_s of work
+    rows = N
+    t0 = time.perf_counter()
+    done = 0
+    runs = 0
+    while True:
+        _, _, _, used = oracle.gemm(x_bits, W_host, N, K, threads=threads)
+        runs += 1
+        done += alg_bytes(M, N, K)
+        if time.perf_counter() - t0 >= budget_s or runs >= 20:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(done / dt / 1e9, 4), "unit": "GB/s",
+            "cores": used, "kind": "oracle",
+            "sample": f"whole {N}x{K} matrix at M={M}, {runs} run(s), "
+                      f"{dt:.1f} s, fp64 accumulation, {used} threads",
+            "s_per_call": round(dt / runs, 4), "rows": rows}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gate_up", choices=sorted(WORKLOADS))
+    ap.add_argument("--rotate-gb", type=float, default=1.2)
+    ap.add_argument("--cpu-budget-s", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU "
+              "path (the verify GEMM shards by output rows with no exchange; "
+              "see the design notes).  Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import speculative_verify_gemm_q4_amd as q4
+    q4.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    st = stamp(torch)
+    N, K = WORKLOADS[args.workload]
+    Mv = 16
+    b16, b1 = alg_bytes(Mv, N, K), alg_bytes(1, N, K)
+    log(f"stamp: {json.dumps(st)}")
+    log(f"bytes/call: M=16 {b16:,}  M=1 {b1:,}; floor at {HBM_PEAK_GBPS:.0f} "
+        f"GB/s: {b16 / HBM_PEAK_GBPS / 1e3:.2f} us / {b1 / HBM_PEAK_GBPS / 1e3:.2f}"
+        " us (prediction)")
+
+    wbytes = 9 * N * K // 16
+    copies = max(2, math.ceil(args.rotate_gb * 1e9 / wbytes))
+    Ws = [synth.q4_weights(N, K, seed=0, stream=i, device=dev)
+          for i in range(copies)]
+    x16 = synth.activations(Mv, K, seed=0, stream=100, device=dev)
+    x1 = x16[:1].contiguous()
+    y16 = torch.empty((Mv, N), dtype=torch.float32, device=dev)
+    y1 = torch.empty((1, N), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    # the timed steps (M = 16), then M = 1 the same way; then M = 16 again so
+    # the ratio uses A-B-A order
+    ms16a, wall16, launches16 = time_calls(torch, q4, x16, Ws, y16, Mv, N, K,
+                                           args.steps, args.warmup)
+    ms1, wall1, launches1 = time_calls(torch, q4, x1, Ws, y1, 1, N, K,
+                                       args.steps, args.warmup)
+    ms16b, _, launches16b = time_calls(torch, q4, x16, Ws, y16, Mv, N, K,
+                                       args.steps, args.warmup)
+    launch16 = sorted(launches16 + launches16b)
+    launch1 = sorted(launches1)
+    k16 = sum(launch16) / len(launch16)
+    k1 = sum(launch1) / len(launch1)
+    ms_per_step = ms16a
+    gbps16 = b16 / (ms_per_step * 1e-3) / 1e9
+    gbps1 = b1 / (ms1 * 1e-3) / 1e9
+    ach16 = b16 / (k16 * 1e-3) / 1e9
+    ach1 = b1 / (k1 * 1e-3) / 1e9
+    plan = q4.q4_gemm_verify_plan(Mv, N, K)
+    traffic = load_traffic(Mv, N, K)
+    log(f"M=16: {ms_per_step * 1e3:.2f} us/step ({gbps16:.0f} GB/s), kernel "
+        f"{k16 * 1e3:.2f} us ({ach16:.0f} GB/s); M=1: {ms1 * 1e3:.2f} us/step "
+        f"({gbps1:.0f} GB/s), kernel {k1 * 1e3:.2f} us ({ach1:.0f} GB/s)")
+
+    probe = None
+    if not args.no_probe:
+        probe = stream_probe(torch, q4, 2 * 1024 ** 3)
+        log(f"stream read probe: {probe:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(torch, Ws[0], x16, N, K, args.cpu_budget_s)
+        log(f"cpu oracle: {cpu}")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(gbps16, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Q4 codes/scales/biases, bf16 N(0,1) x)",
+        "config": {"workload": f"{args.workload}_{N}x{K}", "N": N, "K": K,
+                   "M": Mv, "weight_copies": copies,
+                   "parallelism": "single GPU", "plan": plan},
+        "frac_of_peak": round(gbps16 / HBM_PEAK_GBPS, 4),
+        "m1": {"ms_per_step": round(ms1, 6), "gbps": round(gbps1, 1),
+               "frac_of_peak": round(gbps1 / HBM_PEAK_GBPS, 4),
+               "kernel_us": round(k1 * 1e3, 3)},
+        "ratio_m16_m1": round(ms_per_step / ms1, 4),
+        "ratio_m16_m1_kernel": round(k16 / k1, 4),
+        "wall_ms_per_step": round(wall16, 6),
+        "stream_read_gbps": None if probe is None else round(probe, 1),
+        "frac_of_stream_read": None if probe is None else
+        round(gbps16 / probe, 4),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(ach16, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(ach16 / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": "gemm_verify_kernel",
+            "kernel_us": round(k16 * 1e3, 3),
+            "alg_bytes_per_launch": b16,
+        },
+        "cpu_baseline": cpu,
+        "stamp": st,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,170 @@
+/*
+ * q4verify.h -- C ABI of the skinny-M Q4 verify GEMM for AMD MI355X (gfx950).
+ *
+ * The operation.  A speculative-decoding verify step runs the target model
+ * once over a block of M draft rows; every linear layer then multiplies a
+ * 4-bit weight matrix by M activation rows, and the step is cheap only if each
+ * weight byte is read from memory once for all rows (Splash engine article,
+ * "144 tok/s needs 502 GB/s ...", section "Why Apple silicon, and why not the
+ * M5": the eight verify rows turn decode into an 8 x K x N GEMM; qwen-spec
+ * page, Notes and the figure beside them: a matmul that reads each weight tile
+ * once costs 1.02x for 16 rows against 1 row; goinfer page "Faster, with the
+ * same words", section "How it works": verify rows run in one pass).
+ *
+ * The weight format.  Splash engine article, section "The engine hard-codes
+ * the model": every group of 64 inputs of one output row holds 32 bytes of
+ * unsigned 4-bit codes q, one bf16 scale s and one bf16 bias b, and the weight
+ * is w = s * q + b; 16 weights take 9 bytes (q4PackedBytes), with no
+ * exceptions per tensor.  The pages do not fix the byte layout; this library
+ * reads the planar layout described at q4_pack_layout.
+ *
+ * Conventions for every entry point:
+ *   - Stateless and thread-safe; nothing is allocated, no stream is
+ *     synchronised.  Device work is enqueued on `stream` (a hipStream_t passed
+ *     as void*, NULL = the null stream) and runs asynchronously.
+ *   - All data pointers are device memory owned by the caller; the library
+ *     only borrows them for the duration of the enqueued work.
+ *   - Arguments are checked on the host before anything is enqueued; a bad
+ *     argument returns an error code and enqueues nothing.  Faults inside
+ *     enqueued work surface at the caller's next synchronisation.
+ *   - Return value: Q4_OK (0) or a negative q4_status.
+ */
+#ifndef Q4VERIFY_H
+#define Q4VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q4_ABI_VERSION 1u
+#define Q4_GROUP 64     /* inputs per scale/bias group                     */
+#define Q4_MAX_ROWS 16  /* largest activation block M of q4_gemm_verify     */
+
+typedef enum {
+  Q4_OK = 0,
+  Q4_EINVAL = -1,    /* a size, pointer or layout id is invalid            */
+  Q4_EALIGN = -2,    /* a pointer is not aligned as the call requires      */
+  Q4_EOVERFLOW = -3, /* a byte count does not fit 64 bits                  */
+  Q4_EDEVICE = -4,   /* no HIP device, or the current one is not gfx950    */
+  Q4_ELAUNCH = -5    /* the HIP runtime refused the launch                 */
+} q4_status;
+
+/* Layout ids accepted by q4_pack_layout. */
+#define Q4_LAYOUT_PLANAR 0u
+
+typedef struct {
+  uint32_t abi_version; /* Q4_ABI_VERSION                                  */
+  uint32_t layout_id;   /* Q4_LAYOUT_PLANAR                                 */
+  int64_t N;            /* output rows                                     */
+  int64_t K;            /* inputs per row, a multiple of Q4_GROUP           */
+  int64_t group;        /* Q4_GROUP                                        */
+  uint64_t total_bytes; /* N*K/16*9 exactly                                 */
+  uint64_t code_off, code_bytes;   /* 4-bit codes, N*K/2 bytes              */
+  uint64_t scale_off, scale_bytes; /* bf16 scales, N*K/64 values            */
+  uint64_t bias_off, bias_bytes;   /* bf16 biases, N*K/64 values            */
+} q4_layout;
+
+/*
+ * q4_pack_layout -- byte layout of a packed N x K weight matrix (host only).
+ *
+ * Follows q4PackedBytes (Splash engine article, section "The engine
+ * hard-codes the model"): total = N*K/16*9 bytes, computed with overflow
+ * checks.  Layout Q4_LAYOUT_PLANAR, a reading of the pages (they give sizes,
+ * not positions):
+ *   codes  at 0           : [N][K/2] bytes, row-major; byte n*K/2 + k/2
+ *                           holds input k of row n in its low nibble when k
+ *                           is even, in its high nibble when k is odd;
+ *   scales at N*K/2       : [N][K/64] bf16, row-major (group g of row n at
+ *                           index n*K/64 + g);
+ *   biases at N*K/2+N*K/32: [N][K/64] bf16, same order.
+ * Arguments: N >= 1, K >= 64 with K % 64 == 0, layout_id
+ * Q4_LAYOUT_PLANAR, `out` non-NULL (written only on success).
+ * Errors: Q4_EINVAL (bad size, id or NULL), Q4_EOVERFLOW (size > 2^64-1).
+ */
+int q4_pack_layout(int64_t N, int64_t K, uint32_t layout_id, q4_layout *out);
+
+/*
+ * q4_gemm_verify -- y[m][n] = sum_k x[m][k] * (s[n][k/64] * q[n][k] +
+ * b[n][k/64]) for 0 <= m < M, 0 <= n < N.
+ *
+ * The verify matmul of the pages (see the file comment): one pass over the
+ * packed weights serves all M rows.
+ *   x : device, bf16 [M][K] row-major, contiguous, 16-byte aligned.
+ *   W : device, packed N x K matrix in Q4_LAYOUT_PLANAR (total_bytes of
+ *       q4_pack_layout), 16-byte aligned.  Read only.
+ *   y : device, fp32 [M][N] row-major, contiguous, 4-byte aligned; fully
+ *       overwritten (no accumulation into prior contents).  Must not overlap
+ *       x or W.
+ *   M : 1..Q4_MAX_ROWS.  N : 1..2^31-1.  K : multiple of 64, 64..2^31-64.
+ *   stream : hipStream_t or NULL.
+ * Accumulation is fp32; results stay within 2e-3 * sum_k |x*w| + 1e-5 of the
+ * exact product, and a row's result does not depend on M or on the other
+ * rows of the block (rows are computed independently, in the same order).
+ * Errors: Q4_EINVAL, Q4_EALIGN, Q4_EOVERFLOW, Q4_EDEVICE, Q4_ELAUNCH.
+ */
+int q4_gemm_verify(const void *x, const void *W, float *y, int M, int64_t N,
+                   int64_t K, void *stream);
+
+/*
+ * q4_dequant -- W_out[n][k] = fp32(s * q + b), rounded once (test hook that
+ * exposes the kernels' reading of the format, same passage as above).
+ *   W     : device, packed N x K matrix in Q4_LAYOUT_PLANAR, 16-byte aligned.
+ *   W_out : device, fp32 [N][K] row-major, 16-byte aligned, overwritten.
+ * Errors: as q4_gemm_verify.
+ */
+int q4_dequant(const void *W, float *W_out, int64_t N, int64_t K,
+               void *stream);
+
+/*
+ * q4_stream_read -- measurement probe: read `bytes` bytes at `buf` once with
+ * 16-byte loads and write nothing unless a checksum hits a sentinel (then
+ * one uint32 to *sink).  Gives the streaming read rate the GEMM is measured
+ * against besides the HBM peak (the prediction-first page, section "What a
+ * Measurement Record Contains", keeps both the vendor figure and a measured
+ * streaming rate as denominators).
+ *   buf : device, 16-byte aligned; bytes a positive multiple of 16.
+ *   sink: device, one uint32.
+ */
+int q4_stream_read(const void *buf, uint64_t bytes, uint32_t *sink,
+                   void *stream);
+
+/*
+ * q4_stream_copy -- measurement probe: dst[i] = src[i] for `bytes` bytes with
+ * 16-byte loads and stores (the reference kernel of known traffic that the
+ * hardware byte counters are calibrated against).
+ *   src, dst : device, 16-byte aligned, not overlapping; bytes a positive
+ *              multiple of 16.
+ */
+int q4_stream_copy(const void *src, void *dst, uint64_t bytes, void *stream);
+
+/* Launch plan of q4_gemm_verify for one shape (host only, pure). */
+typedef struct {
+  uint32_t grid;         /* workgroups launched                            */
+  uint32_t block;        /* threads per workgroup (64 per wave)            */
+  uint32_t row_tiles;    /* 16-row output tiles per workgroup, one per wave
+                            column                                          */
+  uint32_t k_splits;     /* waves per tile, each taking a contiguous range
+                            of the K/64 groups; partial sums are added in
+                            split order inside the workgroup               */
+  uint32_t lookahead;    /* groups whose loads are issued ahead of use      */
+  uint32_t reserved;
+} q4_plan;
+
+/*
+ * q4_gemm_verify_plan -- the plan q4_gemm_verify(M, N, K) launches.  Same
+ * argument rules as q4_gemm_verify for M, N and K; `out` non-NULL.
+ * Errors: Q4_EINVAL, Q4_EOVERFLOW.
+ */
+int q4_gemm_verify_plan(int M, int64_t N, int64_t K, q4_plan *out);
+
+/* Human-readable name of a q4_status value (static string, never NULL). */
+const char *q4_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4VERIFY_H */

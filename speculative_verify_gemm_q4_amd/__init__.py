@@ -1,0 +1,24 @@
+"""Skinny-M Q4 verify GEMM for AMD MI355X (gfx950): Python binding.
+
+A thin ctypes layer over the C ABI in ``include/q4verify.h``: argument
+marshalling and shape/dtype/device checks only.  Every step of the
+computation runs in the HIP kernels of ``libq4verify.so``; if that library
+has not been built, importing the functions raises instead of falling back
+to anything else.
+
+Functions (same names as the C entry points):
+
+* :func:`q4_pack_layout` -- byte layout of a packed N x K matrix (host only).
+* :func:`q4_gemm_verify` -- y[M, N] = x[M, K] @ W^T for Q4 W, fp32 out.
+* :func:`q4_gemm_verify_plan` -- the launch plan of a shape (host only).
+* :func:`q4_dequant` -- fp32 weights of a packed matrix (test hook).
+* :func:`q4_stream_read`, :func:`q4_stream_copy` -- bandwidth probes.
+* :func:`q4_status_string` -- name of a status code.
+"""
+from ._lib import (GROUP, MAX_ROWS, Q4Error, LIB_PATH, lib_exports, load,
+                   q4_dequant, q4_gemm_verify, q4_gemm_verify_plan,
+                   q4_pack_layout, q4_status_string, q4_stream_copy, q4_stream_read)
+
+__all__ = ["GROUP", "MAX_ROWS", "Q4Error", "LIB_PATH", "lib_exports", "load",
+           "q4_dequant", "q4_gemm_verify", "q4_gemm_verify_plan", "q4_pack_layout",
+           "q4_status_string", "q4_stream_copy", "q4_stream_read"]

@@ -1,0 +1,182 @@
+"""ctypes binding of ``libq4verify.so`` (see include/q4verify.h)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libq4verify.so")
+
+GROUP = 64
+MAX_ROWS = 16
+LAYOUT_PLANAR = 0
+
+OK, EINVAL, EALIGN, EOVERFLOW, EDEVICE, ELAUNCH = 0, -1, -2, -3, -4, -5
+
+
+class Q4Error(RuntimeError):
+    """A nonzero status from the C ABI."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {q4_status_string(status)} ({status})")
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_uint32),
+                ("layout_id", ctypes.c_uint32),
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("group", ctypes.c_int64),
+                ("total_bytes", ctypes.c_uint64),
+                ("code_off", ctypes.c_uint64), ("code_bytes", ctypes.c_uint64),
+                ("scale_off", ctypes.c_uint64),
+                ("scale_bytes", ctypes.c_uint64),
+                ("bias_off", ctypes.c_uint64), ("bias_bytes", ctypes.c_uint64)]
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("grid", ctypes.c_uint32), ("block", ctypes.c_uint32),
+                ("row_tiles", ctypes.c_uint32), ("k_splits", ctypes.c_uint32),
+                ("lookahead", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+
+_lib = None
+
+_SIGNATURES = {
+    "q4_pack_layout": ([ctypes.c_int64, ctypes.c_int64, ctypes.c_uint32,
+                        ctypes.POINTER(_Layout)], ctypes.c_int),
+    "q4_gemm_verify": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                        ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                        ctypes.c_void_p], ctypes.c_int),
+    "q4_dequant": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                    ctypes.c_int64, ctypes.c_void_p], ctypes.c_int),
+    "q4_stream_read": ([ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                        ctypes.c_void_p], ctypes.c_int),
+    "q4_stream_copy": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
+                        ctypes.c_void_p], ctypes.c_int),
+    "q4_gemm_verify_plan": ([ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                             ctypes.POINTER(_Plan)], ctypes.c_int),
+    "q4_status_string": ([ctypes.c_int], ctypes.c_char_p),
+}
+
+
+def lib_exports():
+    """Names of the C entry points this binding uses."""
+    return sorted(_SIGNATURES)
+
+
+def load():
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it first with "
+                "`python -c 'import __graft_entry__ as g; g.build()'`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = lib
+    return _lib
+
+
+def q4_status_string(status: int) -> str:
+    return load().q4_status_string(int(status)).decode()
+
+
+def q4_pack_layout(N: int, K: int, layout_id: int = LAYOUT_PLANAR) -> dict:
+    out = _Layout()
+    st = load().q4_pack_layout(int(N), int(K), int(layout_id),
+                               ctypes.byref(out))
+    if st != OK:
+        raise Q4Error(st, f"q4_pack_layout({N}, {K}, {layout_id})")
+    return {name: getattr(out, name) for name, _ in _Layout._fields_}
+
+
+def q4_gemm_verify_plan(M: int, N: int, K: int) -> dict:
+    """The launch plan q4_gemm_verify uses for this shape (host only)."""
+    out = _Plan()
+    st = load().q4_gemm_verify_plan(int(M), int(N), int(K), ctypes.byref(out))
+    if st != OK:
+        raise Q4Error(st, f"q4_gemm_verify_plan({M}, {N}, {K})")
+    return {name: getattr(out, name) for name, _ in _Plan._fields_}
+
+
+def _stream_handle(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptr(t, name, dtype=None, numel=None, shape=None):
+    """Device pointer of a contiguous CUDA tensor after checking it."""
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, "
+                         f"got {tuple(t.shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, got {t.numel()}")
+    return t.data_ptr()
+
+
+def q4_gemm_verify(x, W, y, M: int, N: int, K: int, stream=None) -> None:
+    """y[M, N] = x[M, K] @ W^T.  x bf16 [M, K], W packed uint8, y fp32
+    [M, N]; all on the same GPU.  Enqueued on ``stream`` (default: torch's
+    current stream)."""
+    import torch
+    total = q4_pack_layout(N, K)["total_bytes"]
+    px = _ptr(x, "x", torch.bfloat16, shape=(M, K))
+    pw = _ptr(W, "W", torch.uint8, numel=total)
+    py = _ptr(y, "y", torch.float32, shape=(M, N))
+    if not (x.device == W.device == y.device):
+        raise ValueError("x, W and y must be on one device")
+    st = load().q4_gemm_verify(px, pw, py, int(M), int(N), int(K),
+                               _stream_handle(stream))
+    if st != OK:
+        raise Q4Error(st, "q4_gemm_verify")
+
+
+def q4_dequant(W, W_out, N: int, K: int, stream=None) -> None:
+    """W_out[N, K] fp32 = dequantised packed W."""
+    import torch
+    total = q4_pack_layout(N, K)["total_bytes"]
+    pw = _ptr(W, "W", torch.uint8, numel=total)
+    po = _ptr(W_out, "W_out", torch.float32, shape=(N, K))
+    if W.device != W_out.device:
+        raise ValueError("W and W_out must be on one device")
+    st = load().q4_dequant(pw, po, int(N), int(K), _stream_handle(stream))
+    if st != OK:
+        raise Q4Error(st, "q4_dequant")
+
+
+def q4_stream_read(buf, nbytes: int, sink, stream=None) -> None:
+    """Read ``nbytes`` of ``buf`` once; ``sink`` is an int32 GPU tensor with
+    at least one element."""
+    if nbytes > buf.numel() * buf.element_size():
+        raise ValueError("nbytes exceeds the buffer")
+    pb = _ptr(buf, "buf")
+    ps = _ptr(sink, "sink")
+    st = load().q4_stream_read(pb, int(nbytes), ps, _stream_handle(stream))
+    if st != OK:
+        raise Q4Error(st, "q4_stream_read")
+
+
+def q4_stream_copy(src, dst, nbytes: int, stream=None) -> None:
+    """Copy ``nbytes`` from src to dst."""
+    if nbytes > src.numel() * src.element_size() or \
+            nbytes > dst.numel() * dst.element_size():
+        raise ValueError("nbytes exceeds a buffer")
+    st = load().q4_stream_copy(_ptr(src, "src"), _ptr(dst, "dst"), int(nbytes),
+                               _stream_handle(stream))
+    if st != OK:
+        raise Q4Error(st, "q4_stream_copy")

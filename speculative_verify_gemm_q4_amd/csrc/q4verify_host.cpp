@@ -1,0 +1,166 @@
+// q4verify_host.cpp -- host-only part of the library: the packed layout,
+// argument checks, device check and status strings.  Nothing here touches the
+// GPU except check_device(), which asks the HIP runtime for the current
+// device's architecture.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "q4v_internal.h"
+
+namespace q4v {
+namespace {
+
+constexpr int64_t kMaxIndex = 2147483647;  // rows and inputs are int32 in kernels
+
+bool aligned(const void *p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+// N*K/16*9 with overflow checks (the q4PackedBytes rule of the Splash engine
+// article, section "The engine hard-codes the model").
+int packed_bytes(int64_t N, int64_t K, uint64_t *out) {
+  if (N < 1 || K < Q4_GROUP || K % Q4_GROUP != 0) return Q4_EINVAL;
+  uint64_t elements;
+  if (__builtin_mul_overflow(static_cast<uint64_t>(N),
+                             static_cast<uint64_t>(K), &elements))
+    return Q4_EOVERFLOW;
+  uint64_t bytes;
+  if (__builtin_mul_overflow(elements / 16u, uint64_t{9}, &bytes))
+    return Q4_EOVERFLOW;
+  *out = bytes;
+  return Q4_OK;
+}
+
+}  // namespace
+
+int check_matrix_shape(int64_t N, int64_t K) {
+  uint64_t bytes;
+  const int st = packed_bytes(N, K, &bytes);
+  if (st != Q4_OK) return st;
+  if (N > kMaxIndex || K > kMaxIndex - Q4_GROUP + 1) return Q4_EINVAL;
+  // Element offsets n*K (dequant output) are 64-bit in the kernels; they
+  // must also fit 64 bits as byte offsets of an fp32 array.
+  uint64_t elems, out_bytes;
+  if (__builtin_mul_overflow(static_cast<uint64_t>(N),
+                             static_cast<uint64_t>(K), &elems) ||
+      __builtin_mul_overflow(elems, uint64_t{4}, &out_bytes))
+    return Q4_EOVERFLOW;
+  return Q4_OK;
+}
+
+int check_gemm_args(const void *x, const void *W, const float *y, int M,
+                    int64_t N, int64_t K) {
+  if (M < 1 || M > Q4_MAX_ROWS) return Q4_EINVAL;
+  const int st = check_matrix_shape(N, K);
+  if (st != Q4_OK) return st;
+  if (x == nullptr || W == nullptr || y == nullptr) return Q4_EINVAL;
+  if (!aligned(x, 16) || !aligned(W, 16) || !aligned(y, 4)) return Q4_EALIGN;
+  return Q4_OK;
+}
+
+int check_dequant_args(const void *W, const float *W_out, int64_t N,
+                       int64_t K) {
+  const int st = check_matrix_shape(N, K);
+  if (st != Q4_OK) return st;
+  if (W == nullptr || W_out == nullptr) return Q4_EINVAL;
+  if (!aligned(W, 16) || !aligned(W_out, 16)) return Q4_EALIGN;
+  return Q4_OK;
+}
+
+int check_stream_args(const void *a, const void *b, uint64_t bytes) {
+  if (a == nullptr || b == nullptr || bytes == 0 || bytes % 16 != 0)
+    return Q4_EINVAL;
+  if (!aligned(a, 16)) return Q4_EALIGN;
+  return Q4_OK;
+}
+
+q4_plan plan_gemm(int M, int64_t N, int64_t K) {
+  (void)M;
+  // Waves per tile splitting K so that the grid holds enough waves (about 16
+  // per CU on 256 CUs) to keep the weight stream in flight, with at least
+  // four groups per wave; large-N shapes put several tiles in a workgroup.
+  const int64_t tiles = (N + 15) / 16;
+  const int64_t groups = K / Q4_GROUP;
+  int ksw = 1;
+  while (ksw < 16 && tiles * ksw < 4096 && groups >= 4 * ksw) ksw *= 2;
+  const int ntw = ksw >= 4 ? 1 : 4 / ksw;
+  q4_plan p;
+  std::memset(&p, 0, sizeof p);
+  p.row_tiles = static_cast<uint32_t>(ntw);
+  p.k_splits = static_cast<uint32_t>(ksw);
+  p.block = static_cast<uint32_t>(64 * ntw * ksw);
+  p.grid = static_cast<uint32_t>((tiles + ntw - 1) / ntw);
+  p.lookahead = 4;
+  return p;
+}
+
+int check_device() {
+  static std::atomic<int> verdict[256];  // 0 unknown, 1 gfx950, -1 other
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return Q4_EDEVICE;
+  }
+  if (dev >= 256) return Q4_EDEVICE;
+  int v = verdict[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return Q4_EDEVICE;
+    }
+    v = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    verdict[dev].store(v, std::memory_order_relaxed);
+  }
+  return v == 1 ? Q4_OK : Q4_EDEVICE;
+}
+
+}  // namespace q4v
+
+extern "C" int q4_pack_layout(int64_t N, int64_t K, uint32_t layout_id,
+                              q4_layout *out) {
+  if (out == nullptr || layout_id != Q4_LAYOUT_PLANAR) return Q4_EINVAL;
+  uint64_t total;
+  const int st = q4v::packed_bytes(N, K, &total);
+  if (st != Q4_OK) return st;
+  const uint64_t elements = static_cast<uint64_t>(N) * static_cast<uint64_t>(K);
+  q4_layout l;
+  std::memset(&l, 0, sizeof l);
+  l.abi_version = Q4_ABI_VERSION;
+  l.layout_id = layout_id;
+  l.N = N;
+  l.K = K;
+  l.group = Q4_GROUP;
+  l.total_bytes = total;
+  l.code_off = 0;
+  l.code_bytes = elements / 2;
+  l.scale_off = l.code_off + l.code_bytes;
+  l.scale_bytes = (elements / Q4_GROUP) * 2;
+  l.bias_off = l.scale_off + l.scale_bytes;
+  l.bias_bytes = l.scale_bytes;
+  *out = l;
+  return Q4_OK;
+}
+
+extern "C" int q4_gemm_verify_plan(int M, int64_t N, int64_t K,
+                                   q4_plan *out) {
+  if (out == nullptr || M < 1 || M > Q4_MAX_ROWS) return Q4_EINVAL;
+  const int st = q4v::check_matrix_shape(N, K);
+  if (st != Q4_OK) return st;
+  *out = q4v::plan_gemm(M, N, K);
+  return Q4_OK;
+}
+
+extern "C" const char *q4_status_string(int status) {
+  switch (status) {
+    case Q4_OK: return "Q4_OK: success";
+    case Q4_EINVAL: return "Q4_EINVAL: invalid size, pointer or layout id";
+    case Q4_EALIGN: return "Q4_EALIGN: pointer not aligned as required";
+    case Q4_EOVERFLOW: return "Q4_EOVERFLOW: byte count overflows 64 bits";
+    case Q4_EDEVICE: return "Q4_EDEVICE: no HIP device or device is not gfx950";
+    case Q4_ELAUNCH: return "Q4_ELAUNCH: kernel launch failed";
+    default: return "unknown q4 status";
+  }
+}

@@ -1,0 +1,327 @@
+// q4verify_kernels.hip -- gfx950 kernels of the Q4 verify GEMM and the
+// device entry points of the C ABI.
+//
+// The GEMM (y = x * W^T, W in the planar group-affine Q4 layout, M <= 16
+// activation rows) is bound by the weight stream: 9 bytes per 16 weights are
+// read once and every activation row is multiplied while the codes are in
+// registers (qwen-spec page, Notes: one read of each weight tile serves all
+// rows; Splash engine article, "Why Apple silicon, and why not the M5": the
+// verify rows make it a GEMM that still needs little compute per byte).
+//
+// Per wave: a tile of 16 output rows x a range of 64-input groups.  For each
+// group the wave runs two v_mfma_f32_16x16x32_bf16 on the codes:
+//   A = x (16 activation rows, rows >= M are zero),  B = codes as bf16,
+// with the group scale applied afterwards, since it differs per group:
+//   y[m,n] += s[n,g] * sum_k x[m,k] q[n,k]  +  b[n,g] * sum_k x[m,k].
+// Codes reach bf16 without a conversion instruction: OR-ing a 4-bit code into
+// the mantissa of bf16 128.0 (0x4300) gives exactly 128 + q.  The extra
+// 128 * sum_k x is cancelled by seeding the accumulator with an MFMA against
+// a constant -128 operand, which also yields the group sums of x that the
+// bias term needs (XN = -128 * sum_k x, so b * sum_k x = (-b/128) * XN).
+// Products of bf16 x with 128 + q are exact; accumulation is fp32.
+//
+// To make the unpack cheap the 8 codes of a 32-bit word are paired as
+// (q0,q4) (q1,q5) (q2,q6) (q3,q7) -- one mask per pair -- and the activation
+// operand is permuted the same way with v_perm_b32, so both operands agree on
+// which input sits in which MFMA k-slot.
+#include <hip/hip_runtime.h>
+
+#include "q4v_internal.h"
+
+namespace q4v {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr uint32_t kMagic128Pair = 0x43004300u;  // bf16 (128.0, 128.0)
+constexpr uint32_t kNeg128Pair = 0xC300C300u;    // bf16 (-128.0, -128.0)
+constexpr float kMinusInv128 = -0.0078125f;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Codes q0..q7 (bits 4i..4i+3 of w) -> bf16 pairs (128+q0, 128+q4),
+// (128+q1, 128+q5), (128+q2, 128+q6), (128+q3, 128+q7).
+__device__ __forceinline__ u32x4 unpack_codes(uint32_t w) {
+  u32x4 r;
+  r.x = (w & 0x000F000Fu) | kMagic128Pair;
+  r.y = ((w >> 4) & 0x000F000Fu) | kMagic128Pair;
+  r.z = ((w >> 8) & 0x000F000Fu) | kMagic128Pair;
+  r.w = ((w >> 12) & 0x000F000Fu) | kMagic128Pair;
+  return r;
+}
+
+// Eight consecutive bf16 activations (x0,x1)(x2,x3)(x4,x5)(x6,x7) ->
+// (x0,x4)(x1,x5)(x2,x6)(x3,x7), the k-slot order of unpack_codes.
+__device__ __forceinline__ u32x4 pair_activations(u32x4 d) {
+  u32x4 r;
+  r.x = __builtin_amdgcn_perm(d.z, d.x, 0x05040100u);
+  r.y = __builtin_amdgcn_perm(d.z, d.x, 0x07060302u);
+  r.z = __builtin_amdgcn_perm(d.w, d.y, 0x05040100u);
+  r.w = __builtin_amdgcn_perm(d.w, d.y, 0x07060302u);
+  return r;
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+      __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
+      0);
+}
+
+// One workgroup = NTW tiles of 16 output rows x KSW waves splitting the
+// groups of K; U groups are loaded ahead of their use.
+//
+// Lane l of a wave: j = l % 16, kb = l / 16.  MFMA 16x16x32 operand layout:
+//   A (16 x 32): lane holds row j, k-slots 8*kb .. 8*kb+7  -> x row m = j;
+//   B (32 x 16): lane holds column j, k-slots 8*kb .. +7   -> W row n0 + j;
+//   C (16 x 16): lane holds column j, rows 4*kb .. 4*kb+3 -> y[4kb+r][n0+j].
+// In group g the first MFMA covers inputs 64g + 16kb + 0..7 and the second
+// 64g + 16kb + 8..15 of each lane, i.e. 8 code bytes per lane per group.
+template <int NTW, int KSW, int U>
+__global__ __launch_bounds__(64 * NTW * KSW) void gemm_verify_kernel(
+    const uint16_t *__restrict__ x, const uint8_t *__restrict__ W,
+    float *__restrict__ y, int M, int N, int K) {
+  const int G = K >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nt = wave % NTW;
+  const int ks = wave / NTW;
+  const int j = lane & 15;
+  const int kb = lane >> 4;
+  const int n0 = (blockIdx.x * NTW + nt) * 16;
+  const int n = n0 + j;
+  const bool row_ok = n < N;
+  const bool x_ok = j < M;
+  const int gb = static_cast<int>((static_cast<int64_t>(G) * ks) / KSW);
+  const int ge = static_cast<int>((static_cast<int64_t>(G) * (ks + 1)) / KSW);
+
+  const uint64_t NK = static_cast<uint64_t>(N) * static_cast<uint64_t>(K);
+  const uint64_t nrow = row_ok ? static_cast<uint64_t>(n) : 0;
+  const uint8_t *codes = W + nrow * static_cast<uint64_t>(K >> 1) + kb * 8;
+  const uint16_t *scales =
+      reinterpret_cast<const uint16_t *>(W + NK / 2) + nrow * G;
+  const uint16_t *biases =
+      reinterpret_cast<const uint16_t *>(W + NK / 2 + NK / 32) + nrow * G;
+  const uint16_t *xrow =
+      x + static_cast<uint64_t>(x_ok ? j : 0) * static_cast<uint64_t>(K) +
+      kb * 16;
+
+  const u32x4 neg = {kNeg128Pair, kNeg128Pair, kNeg128Pair, kNeg128Pair};
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc = fzero;
+
+  for (int g = gb; g < ge; g += U) {
+    u32x2 cw[U];
+    uint32_t sv[U], bv[U];
+    u32x4 xa[U], xb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int gg = g + u;
+      const bool ok = gg < ge;
+      cw[u] = u32x2{0u, 0u};
+      sv[u] = 0u;
+      bv[u] = 0u;
+      xa[u] = zero4;
+      xb[u] = zero4;
+      if (ok && row_ok) {
+        cw[u] = *reinterpret_cast<const u32x2 *>(codes +
+                                                 static_cast<uint64_t>(gg) * 32);
+        sv[u] = scales[gg];
+        bv[u] = biases[gg];
+      }
+      if (ok && x_ok) {
+        const uint16_t *xp = xrow + static_cast<uint64_t>(gg) * 64;
+        xa[u] = *reinterpret_cast<const u32x4 *>(xp);
+        xb[u] = *reinterpret_cast<const u32x4 *>(xp + 8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const u32x4 a0 = pair_activations(xa[u]);
+      const u32x4 a1 = pair_activations(xb[u]);
+      f32x4 xn = mfma16x16x32(a0, neg, fzero);
+      xn = mfma16x16x32(a1, neg, xn);
+      f32x4 t = mfma16x16x32(a0, unpack_codes(cw[u].x), xn);
+      t = mfma16x16x32(a1, unpack_codes(cw[u].y), t);
+      const float s = bf16_to_f32(sv[u]);
+      const float bn = bf16_to_f32(bv[u]) * kMinusInv128;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        acc[r] = __builtin_fmaf(bn, xn[r], acc[r]);
+        acc[r] = __builtin_fmaf(s, t[r], acc[r]);
+      }
+    }
+  }
+
+  if constexpr (KSW > 1) {
+    __shared__ f32x4 partial[KSW][NTW][64];
+    partial[ks][nt][lane] = acc;
+    __syncthreads();
+    if (ks != 0) return;
+#pragma unroll
+    for (int s = 1; s < KSW; ++s) acc += partial[s][nt][lane];
+  }
+  if (row_ok) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = kb * 4 + r;
+      if (m < M) y[static_cast<uint64_t>(m) * N + n] = acc[r];
+    }
+  }
+}
+
+// W_out[n][k] = s * q + b, one thread per 32-bit code word (8 inputs).
+__global__ __launch_bounds__(256) void dequant_kernel(
+    const uint8_t *__restrict__ W, float *__restrict__ out, int N, int K) {
+  const int G = K >> 6;
+  const uint64_t NK = static_cast<uint64_t>(N) * static_cast<uint64_t>(K);
+  const uint64_t words = NK / 8;
+  const uint64_t words_per_row = static_cast<uint64_t>(K) / 8;
+  const uint32_t *codes = reinterpret_cast<const uint32_t *>(W);
+  const uint16_t *scales = reinterpret_cast<const uint16_t *>(W + NK / 2);
+  const uint16_t *biases = reinterpret_cast<const uint16_t *>(W + NK / 2 + NK / 32);
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
+  for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+       i < words; i += stride) {
+    const uint64_t n = i / words_per_row;
+    const uint64_t k0 = (i % words_per_row) * 8;
+    const uint64_t gi = n * G + k0 / 64;
+    const float s = bf16_to_f32(scales[gi]);
+    const float b = bf16_to_f32(biases[gi]);
+    const uint32_t w = codes[i];
+    float4 lo, hi;
+    lo.x = __builtin_fmaf(s, static_cast<float>(w & 15u), b);
+    lo.y = __builtin_fmaf(s, static_cast<float>((w >> 4) & 15u), b);
+    lo.z = __builtin_fmaf(s, static_cast<float>((w >> 8) & 15u), b);
+    lo.w = __builtin_fmaf(s, static_cast<float>((w >> 12) & 15u), b);
+    hi.x = __builtin_fmaf(s, static_cast<float>((w >> 16) & 15u), b);
+    hi.y = __builtin_fmaf(s, static_cast<float>((w >> 20) & 15u), b);
+    hi.z = __builtin_fmaf(s, static_cast<float>((w >> 24) & 15u), b);
+    hi.w = __builtin_fmaf(s, static_cast<float>(w >> 28), b);
+    float4 *o = reinterpret_cast<float4 *>(out + n * K + k0);
+    o[0] = lo;
+    o[1] = hi;
+  }
+}
+
+// Read-only stream: 4 independent 16-byte loads per thread per step.
+__global__ __launch_bounds__(256) void stream_read_kernel(
+    const u32x4 *__restrict__ buf, uint64_t n16, uint32_t *__restrict__ sink) {
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
+  uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 a = buf[i], b = buf[i + stride], c = buf[i + 2 * stride],
+                d = buf[i + 3 * stride];
+    const u32x4 e = a ^ b ^ c ^ d;
+    acc ^= e.x ^ e.y ^ e.z ^ e.w;
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 a = buf[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (acc == 0x9E3779B9u) *sink = acc;
+}
+
+__global__ __launch_bounds__(256) void stream_copy_kernel(
+    const u32x4 *__restrict__ src, u32x4 *__restrict__ dst, uint64_t n16) {
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
+  uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride],
+                d = src[i + 3 * stride];
+    dst[i] = a;
+    dst[i + stride] = b;
+    dst[i + 2 * stride] = c;
+    dst[i + 3 * stride] = d;
+  }
+  for (; i < n16; i += stride) dst[i] = src[i];
+}
+
+int launch_status() {
+  return hipGetLastError() == hipSuccess ? Q4_OK : Q4_ELAUNCH;
+}
+
+template <int NTW, int KSW>
+int launch_gemm(const q4_plan &p, const void *x, const void *W, float *y,
+                int M, int N, int K, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_verify_kernel<NTW, KSW, 4>), dim3(p.grid),
+                     dim3(p.block), 0, stream, static_cast<const uint16_t *>(x),
+                     static_cast<const uint8_t *>(W), y, M, N, K);
+  return launch_status();
+}
+
+}  // namespace
+}  // namespace q4v
+
+extern "C" int q4_gemm_verify(const void *x, const void *W, float *y, int M,
+                              int64_t N, int64_t K, void *stream) {
+  int st = q4v::check_gemm_args(x, W, y, M, N, K);
+  if (st != Q4_OK) return st;
+  st = q4v::check_device();
+  if (st != Q4_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int n = static_cast<int>(N), k = static_cast<int>(K);
+  const q4_plan p = q4v::plan_gemm(M, N, K);
+  switch (p.k_splits) {
+    case 1: return q4v::launch_gemm<4, 1>(p, x, W, y, M, n, k, s);
+    case 2: return q4v::launch_gemm<2, 2>(p, x, W, y, M, n, k, s);
+    case 4: return q4v::launch_gemm<1, 4>(p, x, W, y, M, n, k, s);
+    case 8: return q4v::launch_gemm<1, 8>(p, x, W, y, M, n, k, s);
+    case 16: return q4v::launch_gemm<1, 16>(p, x, W, y, M, n, k, s);
+    default: return Q4_EINVAL;
+  }
+}
+
+extern "C" int q4_dequant(const void *W, float *W_out, int64_t N, int64_t K,
+                          void *stream) {
+  int st = q4v::check_dequant_args(W, W_out, N, K);
+  if (st != Q4_OK) return st;
+  st = q4v::check_device();
+  if (st != Q4_OK) return st;
+  const uint64_t words = static_cast<uint64_t>(N) * static_cast<uint64_t>(K) / 8;
+  const uint64_t want = (words + 255) / 256;
+  const unsigned blocks = static_cast<unsigned>(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(q4v::dequant_kernel, dim3(blocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream),
+                     static_cast<const uint8_t *>(W), W_out,
+                     static_cast<int>(N), static_cast<int>(K));
+  return q4v::launch_status();
+}
+
+extern "C" int q4_stream_read(const void *buf, uint64_t bytes, uint32_t *sink,
+                              void *stream) {
+  int st = q4v::check_stream_args(buf, sink, bytes);
+  if (st != Q4_OK) return st;
+  st = q4v::check_device();
+  if (st != Q4_OK) return st;
+  const uint64_t n16 = bytes / 16;
+  const uint64_t want = (n16 + 1023) / 1024;
+  const unsigned blocks = static_cast<unsigned>(want < 8192 ? (want ? want : 1) : 8192);
+  hipLaunchKernelGGL(q4v::stream_read_kernel, dim3(blocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream),
+                     static_cast<const q4v::u32x4 *>(buf), n16, sink);
+  return q4v::launch_status();
+}
+
+extern "C" int q4_stream_copy(const void *src, void *dst, uint64_t bytes,
+                              void *stream) {
+  int st = q4v::check_stream_args(src, dst, bytes);
+  if (st != Q4_OK) return st;
+  if ((reinterpret_cast<uintptr_t>(dst) & 15u) != 0) return Q4_EALIGN;
+  st = q4v::check_device();
+  if (st != Q4_OK) return st;
+  const uint64_t n16 = bytes / 16;
+  const uint64_t want = (n16 + 1023) / 1024;
+  const unsigned blocks = static_cast<unsigned>(want < 8192 ? (want ? want : 1) : 8192);
+  hipLaunchKernelGGL(q4v::stream_copy_kernel, dim3(blocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream),
+                     static_cast<const q4v::u32x4 *>(src),
+                     static_cast<q4v::u32x4 *>(dst), n16);
+  return q4v::launch_status();
+}

@@ -1,0 +1,131 @@
+"""The C ABI library on the host (no GPU): exports, layout, argument checks.
+
+Every call here either is host-only (q4_pack_layout, q4_status_string) or is
+rejected by the argument checks before the library touches the HIP runtime.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import oracle
+import synth
+import speculative_verify_gemm_q4_amd as q4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4verify.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(q4.LIB_PATH):
+        pytest.fail("libq4verify.so is not built (run __graft_entry__.build())")
+    return q4.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q4_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_entry_points():
+    assert declared_functions() == q4.lib_exports()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    nm = os.popen(f"nm -D --defined-only {q4.LIB_PATH}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}$", nm, flags=re.M), name
+
+
+def test_status_strings(lib):
+    for st in (0, -1, -2, -3, -4, -5):
+        s = q4.q4_status_string(st)
+        assert s.startswith("Q4_")
+    assert q4.q4_status_string(12345) == "unknown q4 status"
+
+
+@pytest.mark.parametrize("N,K", [(1, 64), (3, 192), (256, 512), (34816, 5120),
+                                 (5120, 17408), (248320, 5120), (5120, 6144),
+                                 (7, 1088)])
+def test_layout_matches_oracle_and_generator(lib, N, K):
+    lay = q4.q4_pack_layout(N, K)
+    assert lay["abi_version"] == 1 and lay["layout_id"] == 0
+    assert lay["N"] == N and lay["K"] == K and lay["group"] == 64
+    assert lay["total_bytes"] == oracle.packed_bytes(N, K)
+    assert lay["total_bytes"] == synth.packed_size(N, K)
+    assert lay["code_off"] == 0 and lay["code_bytes"] == N * K // 2
+    assert lay["scale_off"] == N * K // 2 and lay["scale_bytes"] == N * K // 32
+    assert lay["bias_off"] == lay["scale_off"] + lay["scale_bytes"]
+    assert lay["bias_off"] + lay["bias_bytes"] == lay["total_bytes"]
+    # the generator's plane views start where the library says
+    if N * K <= 1 << 20:
+        W = torch.zeros(lay["total_bytes"], dtype=torch.uint8)
+        c, s, b = synth.planes(W, N, K)
+        base = W.data_ptr()
+        assert c.data_ptr() - base == lay["code_off"]
+        assert s.data_ptr() - base == lay["scale_off"]
+        assert b.data_ptr() - base == lay["bias_off"]
+
+
+def test_layout_errors(lib):
+    from speculative_verify_gemm_q4_amd._lib import _Layout
+    out = _Layout()
+    f = lib.q4_pack_layout
+    assert f(0, 64, 0, ctypes.byref(out)) == -1
+    assert f(4, 96, 0, ctypes.byref(out)) == -1
+    assert f(4, 64, 7, ctypes.byref(out)) == -1
+    assert f(4, 64, 0, None) == -1
+    assert f(1 << 40, 1 << 30, 0, ctypes.byref(out)) == -3
+    assert out.total_bytes == 0  # untouched on error
+
+
+def test_gemm_argument_errors(lib):
+    """Each rejected before any device work (fake, never-dereferenced
+    pointers)."""
+    g = lib.q4_gemm_verify
+    X, W, Y = 0x10000, 0x20000, 0x30000
+    assert g(X, W, Y, 0, 256, 512, None) == -1        # M = 0 (empty block)
+    assert g(X, W, Y, 17, 256, 512, None) == -1       # M above 16
+    assert g(X, W, Y, 1, 0, 512, None) == -1          # N = 0 (empty matrix)
+    assert g(X, W, Y, 1, 256, 0, None) == -1          # K = 0
+    assert g(X, W, Y, 1, 256, 500, None) == -1        # K not a multiple of 64
+    assert g(X, W, Y, 1, 1 << 31, 64, None) == -1     # N beyond int32
+    assert g(None, W, Y, 1, 256, 512, None) == -1
+    assert g(X, None, Y, 1, 256, 512, None) == -1
+    assert g(X, W, None, 1, 256, 512, None) == -1
+    assert g(X + 2, W, Y, 1, 256, 512, None) == -2    # x not 16-B aligned
+    assert g(X, W + 8, Y, 1, 256, 512, None) == -2    # W not 16-B aligned
+    assert g(X, W, Y + 2, 1, 256, 512, None) == -2    # y not 4-B aligned
+
+
+def test_dequant_and_probe_argument_errors(lib):
+    d = lib.q4_dequant
+    assert d(0x10000, 0x20000, 0, 64, None) == -1
+    assert d(0x10000, 0x20000, 4, 100, None) == -1
+    assert d(None, 0x20000, 4, 64, None) == -1
+    assert d(0x10008, 0x20000, 4, 64, None) == -2
+    assert d(0x10000, 0x20004, 4, 64, None) == -2
+    r = lib.q4_stream_read
+    assert r(0x10000, 0, 0x20000, None) == -1
+    assert r(0x10000, 24, 0x20000, None) == -1
+    assert r(None, 64, 0x20000, None) == -1
+    assert r(0x10004, 64, 0x20000, None) == -2
+    c = lib.q4_stream_copy
+    assert c(0x10000, 0x20000, 8, None) == -1
+    assert c(0x10000, 0x20008, 64, None) == -2
+
+
+def test_binding_rejects_host_tensors(lib):
+    x = torch.zeros((1, 64), dtype=torch.bfloat16)
+    W = torch.zeros(36, dtype=torch.uint8)
+    y = torch.zeros((1, 1), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        q4.q4_gemm_verify(x, W, y, 1, 1, 64)

@@ -1,0 +1,261 @@
+"""GPU parity of the HIP path against the CPU oracle (needs an MI355X).
+
+Every case calls the library through the C ABI (via the ctypes binding) on
+seeded inputs and hands the oracle the very bytes the GPU consumed.
+
+Bar (per output element): |y_gpu - y64| <= 2e-3 * sum_k |x_k w_k| + 1e-5,
+with y64 and the absolute sum from the oracle's fp64 accumulation.  The
+dequantisation hook must be bit-exact, and so must the GEMM wherever every
+partial sum is an exact fp32 value (integer-valued inputs, one-hot rows).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.helpers import assemble, bf16_bits_of
+
+pytestmark = pytest.mark.gpu
+
+REL, ABS = 2e-3, 1e-5
+
+
+@pytest.fixture(scope="module")
+def q4():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import speculative_verify_gemm_q4_amd as lib
+    lib.load()
+    return lib
+
+
+def _say(*args):
+    print(*args, flush=True)
+
+
+def gemm(q4, x, W, M, N, K):
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=x.device)
+    q4.q4_gemm_verify(x, W, y, M, N, K)
+    torch.cuda.synchronize()
+    return y
+
+
+def assert_within_bound(y_gpu, y64, a64, what=""):
+    got = y_gpu.cpu().numpy().astype(np.float64) if torch.is_tensor(y_gpu) \
+        else y_gpu.astype(np.float64)
+    assert got.shape == y64.shape
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = np.abs(got - y64)
+    bound = REL * a64 + ABS
+    ratio = float(np.max(err / bound))
+    assert ratio <= 1.0, f"{what}: max err/bound {ratio:.3g}"
+    return ratio
+
+
+def oracle_check(q4, M, N, K, seed, what):
+    dev = torch.device("cuda")
+    W = synth.q4_weights(N, K, seed=seed, device=dev)
+    x = synth.activations(M, K, seed=seed, stream=1, device=dev)
+    _say(f"case {what}: M={M} N={N} K={K} seed={seed}")
+    y = gemm(q4, x, W, M, N, K)
+    _, y64, a64, _ = oracle.gemm(synth.bf16_bits(x), W.cpu().numpy(), N, K)
+    return assert_within_bound(y, y64, a64, what)
+
+
+# -------------------------------------------------------------- dequant
+
+@pytest.mark.parametrize("N,K", [(256, 512), (17, 192), (1, 64), (1000, 1088)])
+def test_dequant_bit_exact(q4, N, K):
+    dev = torch.device("cuda")
+    W = synth.q4_weights(N, K, seed=3, device=dev)
+    out = torch.empty((N, K), dtype=torch.float32, device=dev)
+    _say(f"case dequant N={N} K={K}")
+    q4.q4_dequant(W, out, N, K)
+    torch.cuda.synchronize()
+    want = oracle.dequant(W.cpu().numpy(), N, K)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+# -------------------------------------------------------------- GEMM, small
+
+@pytest.mark.parametrize("M", list(range(1, 17)))
+def test_gemm_tiny_every_M(q4, M):
+    oracle_check(q4, M, 256, 512, 0, "tiny")
+
+
+# Shapes chosen to cover every launch configuration of the kernel family
+# (waves per workgroup splitting K: 1, 2, 4, 8, 16), ragged row tails (N not
+# a multiple of 16 or 64), a single group (K = 64), odd group counts and a
+# long K.
+RAGGED = [(1, 1, 64), (3, 17, 192), (16, 257, 640), (5, 1000, 1088),
+          (16, 33, 4096), (7, 16, 65536), (2, 48000, 512), (16, 48001, 512),
+          (1, 70000, 256), (13, 70001, 256), (16, 4099, 5120)]
+
+
+@pytest.mark.parametrize("M,N,K", RAGGED)
+def test_gemm_ragged_shapes(q4, M, N, K):
+    oracle_check(q4, M, N, K, 1, "ragged")
+
+
+def test_gemm_integer_exact_bitwise(q4):
+    """Integer codes/activations, scale 1, bias -8: every partial sum is an
+    exact fp32 integer, so any summation order must reproduce the oracle's
+    fp32 result bit for bit."""
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(5)
+    for (M, N, K) in [(16, 300, 1024), (1, 64, 64), (9, 2000, 3072)]:
+        q = rng.integers(0, 16, size=(N, K))
+        G = K // 64
+        codes = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+        Wh = assemble(codes, bf16_bits_of(np.ones((N, G))),
+                      bf16_bits_of(np.full((N, G), -8.0)))
+        xi = rng.integers(-4, 5, size=(M, K)).astype(np.float32)
+        W = torch.from_numpy(Wh).to(dev)
+        x = torch.from_numpy(xi).to(torch.bfloat16).to(dev)
+        _say(f"case integer-exact M={M} N={N} K={K}")
+        y = gemm(q4, x, W, M, N, K).cpu().numpy()
+        y32, _, _, _ = oracle.gemm(bf16_bits_of(xi), Wh, N, K)
+        assert np.array_equal(y.view(np.uint32), y32.view(np.uint32))
+
+
+def test_gemm_one_hot_bitwise(q4):
+    """x rows e_k: y[m, n] must be the dequantised weight w[n, k_m] exactly
+    (the scale product is exact and the bias adds with one rounding)."""
+    dev = torch.device("cuda")
+    N, K = 200, 640
+    W = synth.q4_weights(N, K, seed=7, device=dev)
+    ks = [0, 1, 7, 8, 15, 16, 63, 64, 130, 255, 300, 511, 512, 600, 638, 639]
+    x = torch.zeros((len(ks), K), dtype=torch.bfloat16, device=dev)
+    for m, k in enumerate(ks):
+        x[m, k] = 1.0
+    _say("case one-hot")
+    y = gemm(q4, x, W, len(ks), N, K).cpu().numpy()
+    w = oracle.dequant(W.cpu().numpy(), N, K)
+    for m, k in enumerate(ks):
+        assert np.array_equal(y[m].view(np.uint32), w[:, k].view(np.uint32)), k
+
+
+def test_rows_do_not_depend_on_M(q4):
+    """Row m of a 16-row block equals, bit for bit, the same row computed in
+    any smaller block (rows are computed independently, same order)."""
+    dev = torch.device("cuda")
+    N, K = 1000, 2048
+    W = synth.q4_weights(N, K, seed=8, device=dev)
+    x = synth.activations(16, K, seed=8, stream=1, device=dev)
+    _say("case M-invariance")
+    full = gemm(q4, x, W, 16, N, K)
+    for M in range(1, 16):
+        part = gemm(q4, x[:M].contiguous(), W, M, N, K)
+        assert torch.equal(part.view(torch.int32), full[:M].view(torch.int32)), M
+    # and a row alone at another position of the block
+    single = gemm(q4, x[11:12].contiguous(), W, 1, N, K)
+    assert torch.equal(single.view(torch.int32), full[11:12].view(torch.int32))
+
+
+def test_deterministic(q4):
+    dev = torch.device("cuda")
+    N, K, M = 5120, 17408, 16
+    W = synth.q4_weights(N, K, seed=9, device=dev)
+    x = synth.activations(M, K, seed=9, stream=1, device=dev)
+    _say("case determinism")
+    a = gemm(q4, x, W, M, N, K)
+    b = gemm(q4, x, W, M, N, K)
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def test_matches_torch_fp32_reference(q4):
+    """Against plain PyTorch fp32: the kernels' own dequantised matrix times
+    x in fp32 (a cross-check of the GEMM against the dequant hook)."""
+    dev = torch.device("cuda")
+    N, K, M = 3000, 2560, 8
+    W = synth.q4_weights(N, K, seed=10, device=dev)
+    x = synth.activations(M, K, seed=10, stream=1, device=dev)
+    w = torch.empty((N, K), dtype=torch.float32, device=dev)
+    q4.q4_dequant(W, w, N, K)
+    _say("case torch-fp32")
+    y = gemm(q4, x, W, M, N, K)
+    ref = x.float() @ w.t()
+    absum = x.float().abs() @ w.abs().t()
+    assert torch.all((y - ref).abs() <= REL * absum + ABS)
+
+
+# -------------------------------------------------------------- full shapes
+
+FULL = {
+    "gate_up": (34816, 5120),
+    "down": (5120, 17408),
+    "lm_head": (248320, 5120),
+    "attn_in": (14336, 5120),
+    "o_proj": (5120, 6144),
+    "gdn_in": (16640, 5120),
+}
+
+
+def sampled_rows(N, count, seed):
+    rng = np.random.default_rng(seed)
+    rows = set(range(min(16, N))) | set(range(max(0, N - 16), N))
+    rows |= set(rng.integers(0, N, size=count).tolist())
+    return np.array(sorted(rows))
+
+
+def sub_matrix(W, N, K, rows):
+    """Packed bytes of the selected output rows (planar layout)."""
+    codes, scales, biases = synth.planes(W, N, K)
+    idx = torch.as_tensor(rows, device=W.device)
+    c = codes.index_select(0, idx).cpu().numpy()
+    s = scales.view(torch.int16).index_select(0, idx).cpu().numpy().view(np.uint16)
+    b = biases.view(torch.int16).index_select(0, idx).cpu().numpy().view(np.uint16)
+    return assemble(c, s, b)
+
+
+@pytest.mark.parametrize("name,M", [(n, m) for n in FULL for m in (1, 16)] +
+                         [("gate_up", m) for m in (2, 4, 8)] +
+                         [("down", m) for m in (2, 4, 8)])
+def test_full_shape_sampled(q4, name, M):
+    dev = torch.device("cuda")
+    N, K = FULL[name]
+    W = synth.q4_weights(N, K, seed=11, stream=list(FULL).index(name),
+                          device=dev)
+    x = synth.activations(M, K, seed=11, stream=2000 + M, device=dev)
+    _say(f"case full {name}: M={M} N={N} K={K}")
+    y = gemm(q4, x, W, M, N, K)
+    rows = sampled_rows(N, 224, seed=M)
+    Wsub = sub_matrix(W, N, K, rows)
+    _, y64, a64, _ = oracle.gemm(synth.bf16_bits(x), Wsub, len(rows), K)
+    got = y[:, torch.as_tensor(rows, device=dev)]
+    assert_within_bound(got, y64, a64, f"{name} M={M}")
+    assert torch.isfinite(y).all()
+
+
+def test_lm_head_two_calls(q4):
+    """The LM head serves two activation blocks per step (draft readout,
+    then verify) from one resident weight buffer."""
+    dev = torch.device("cuda")
+    N, K, M = 248320, 5120, 16
+    W = synth.q4_weights(N, K, seed=12, device=dev)
+    rows = sampled_rows(N, 128, seed=3)
+    Wsub = sub_matrix(W, N, K, rows)
+    idx = torch.as_tensor(rows, device=dev)
+    for call in range(2):
+        x = synth.activations(M, K, seed=12, stream=call, device=dev)
+        _say(f"case lm-head call {call}")
+        y = gemm(q4, x, W, M, N, K)
+        _, y64, a64, _ = oracle.gemm(synth.bf16_bits(x), Wsub, len(rows), K)
+        assert_within_bound(y[:, idx], y64, a64, f"lm head call {call}")
+
+
+# -------------------------------------------------------------- probes
+
+def test_stream_probes(q4):
+    dev = torch.device("cuda")
+    src = torch.randint(0, 255, (1 << 22,), dtype=torch.uint8, device=dev)
+    dst = torch.zeros_like(src)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    _say("case probes")
+    q4.q4_stream_copy(src, dst, src.numel())
+    q4.q4_stream_read(src, src.numel(), sink)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
