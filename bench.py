@@ -105,13 +105,13 @@ def load_traffic(M, N, K):
     return per_m.get("hbm_bytes_per_launch")
 
 
-def time_calls(torch, q4, xs, Ws, y, M, N, K, steps, warmup):
-    """Warm up, then time `steps` calls; returns (wall ms per step, list of
-    per-launch event durations in ms)."""
+def time_calls(torch, call, xs, Ws, y, M, N, K, steps, warmup):
+    """Warm up, then time `steps` calls of call(x, W, y, M, N, K); returns
+    (event ms per step, wall ms per step, per-launch event durations in ms)."""
     stream = torch.cuda.current_stream()
     n_w = len(Ws)
     for i in range(warmup):
-        q4.q4_gemm_verify(xs, Ws[i % n_w], y, M, N, K)
+        call(xs, Ws[i % n_w], y, M, N, K)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     outer0 = torch.cuda.Event(enable_timing=True)
@@ -121,7 +121,7 @@ def time_calls(torch, q4, xs, Ws, y, M, N, K, steps, warmup):
     outer0.record(stream)
     for i in range(steps):
         starts[i].record(stream)
-        q4.q4_gemm_verify(xs, Ws[i % n_w], y, M, N, K)
+        call(xs, Ws[i % n_w], y, M, N, K)
         ends[i].record(stream)
     outer1.record(stream)
     torch.cuda.synchronize()
@@ -221,30 +221,54 @@ def main():
     x1 = x16[:1].contiguous()
     y16 = torch.empty((Mv, N), dtype=torch.float32, device=dev)
     y1 = torch.empty((1, N), dtype=torch.float32, device=dev)
-    torch.cuda.synchronize()
 
-    # the timed steps (M = 16), then M = 1 the same way; then M = 16 again so
-    # the ratio uses A-B-A order
-    ms16a, wall16, launches16 = time_calls(torch, q4, x16, Ws, y16, Mv, N, K,
-                                           args.steps, args.warmup)
-    ms1, wall1, launches1 = time_calls(torch, q4, x1, Ws, y1, 1, N, K,
+    # one-time repack into the tiled layout, timed on its own
+    Wts = [torch.empty_like(W) for W in Ws]
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for W, Wt in zip(Ws, Wts):
+        q4.q4_repack(W, Wt, N, K)
+    e1.record()
+    torch.cuda.synchronize()
+    repack_ms = e0.elapsed_time(e1) / copies
+    repack = {"ms_per_matrix": round(repack_ms, 4),
+              "gbps_read_plus_write": round(2 * wbytes / (repack_ms * 1e-3)
+                                            / 1e9, 1)}
+    log(f"repack: {repack}")
+
+    tiled = q4.q4_gemm_verify_tiled
+    planar = q4.q4_gemm_verify
+    # timed steps: tiled M = 16, then M = 1, then M = 16 again (A-B-A order
+    # for the ratio); then the planar kernel the same way
+    ms16a, wall16, launches16 = time_calls(torch, tiled, x16, Wts, y16, Mv,
+                                           N, K, args.steps, args.warmup)
+    ms1, wall1, launches1 = time_calls(torch, tiled, x1, Wts, y1, 1, N, K,
                                        args.steps, args.warmup)
-    ms16b, _, launches16b = time_calls(torch, q4, x16, Ws, y16, Mv, N, K,
+    ms16b, _, launches16b = time_calls(torch, tiled, x16, Wts, y16, Mv, N, K,
                                        args.steps, args.warmup)
-    launch16 = sorted(launches16 + launches16b)
-    launch1 = sorted(launches1)
+    pms16, _, plaunch16 = time_calls(torch, planar, x16, Ws, y16, Mv, N, K,
+                                     args.steps, args.warmup)
+    pms1, _, plaunch1 = time_calls(torch, planar, x1, Ws, y1, 1, N, K,
+                                   args.steps, args.warmup)
+    launch16 = launches16 + launches16b
     k16 = sum(launch16) / len(launch16)
-    k1 = sum(launch1) / len(launch1)
+    k1 = sum(launches1) / len(launches1)
+    pk16 = sum(plaunch16) / len(plaunch16)
+    pk1 = sum(plaunch1) / len(plaunch1)
     ms_per_step = ms16a
     gbps16 = b16 / (ms_per_step * 1e-3) / 1e9
     gbps1 = b1 / (ms1 * 1e-3) / 1e9
     ach16 = b16 / (k16 * 1e-3) / 1e9
-    ach1 = b1 / (k1 * 1e-3) / 1e9
-    plan = q4.q4_gemm_verify_plan(Mv, N, K)
+    plan = q4.q4_gemm_verify_plan(Mv, N, K, q4.LAYOUT_TILED16)
     traffic = load_traffic(Mv, N, K)
-    log(f"M=16: {ms_per_step * 1e3:.2f} us/step ({gbps16:.0f} GB/s), kernel "
-        f"{k16 * 1e3:.2f} us ({ach16:.0f} GB/s); M=1: {ms1 * 1e3:.2f} us/step "
-        f"({gbps1:.0f} GB/s), kernel {k1 * 1e3:.2f} us ({ach1:.0f} GB/s)")
+    log(f"tiled M=16: {ms_per_step * 1e3:.2f} us/step ({gbps16:.0f} GB/s), "
+        f"kernel {k16 * 1e3:.2f} us ({ach16:.0f} GB/s); M=1: {ms1 * 1e3:.2f} "
+        f"us/step ({gbps1:.0f} GB/s), kernel {k1 * 1e3:.2f} us")
+    log(f"planar M=16: kernel {pk16 * 1e3:.2f} us "
+        f"({b16 / (pk16 * 1e-3) / 1e9:.0f} GB/s); M=1: kernel "
+        f"{pk1 * 1e3:.2f} us ({b1 / (pk1 * 1e-3) / 1e9:.0f} GB/s)")
 
     probe = None
     if not args.no_probe:
@@ -271,6 +295,7 @@ def main():
         "data": "synthetic (seeded Q4 codes/scales/biases, bf16 N(0,1) x)",
         "config": {"workload": f"{args.workload}_{N}x{K}", "N": N, "K": K,
                    "M": Mv, "weight_copies": copies,
+                   "layout": "tiled16 (one-time q4_repack, timed apart)",
                    "parallelism": "single GPU", "plan": plan},
         "frac_of_peak": round(gbps16 / HBM_PEAK_GBPS, 4),
         "m1": {"ms_per_step": round(ms1, 6), "gbps": round(gbps1, 1),
@@ -278,6 +303,13 @@ def main():
                "kernel_us": round(k1 * 1e3, 3)},
         "ratio_m16_m1": round(ms_per_step / ms1, 4),
         "ratio_m16_m1_kernel": round(k16 / k1, 4),
+        "repack": repack,
+        "planar": {"kernel_us_m16": round(pk16 * 1e3, 3),
+                   "gbps_m16": round(b16 / (pk16 * 1e-3) / 1e9, 1),
+                   "kernel_us_m1": round(pk1 * 1e3, 3),
+                   "gbps_m1": round(b1 / (pk1 * 1e-3) / 1e9, 1),
+                   "ms_per_step_m16": round(pms16, 6),
+                   "ms_per_step_m1": round(pms1, 6)},
         "wall_ms_per_step": round(wall16, 6),
         "stream_read_gbps": None if probe is None else round(probe, 1),
         "frac_of_stream_read": None if probe is None else
@@ -289,7 +321,7 @@ def main():
             "unit": "GB/s",
             "frac": round(ach16 / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": "gemm_verify_kernel",
+            "kernel": "gemm_tiled_kernel",
             "kernel_us": round(k16 * 1e3, 3),
             "alg_bytes_per_launch": b16,
         },

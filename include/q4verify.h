@@ -53,7 +53,8 @@ typedef enum {
 } q4_status;
 
 /* Layout ids accepted by q4_pack_layout. */
-#define Q4_LAYOUT_PLANAR 0u
+#define Q4_LAYOUT_PLANAR 0u  /* planes of codes, scales, biases            */
+#define Q4_LAYOUT_TILED16 1u /* records of 16 rows x 4 groups (q4_repack)   */
 
 typedef struct {
   uint32_t abi_version; /* Q4_ABI_VERSION                                  */
@@ -65,6 +66,10 @@ typedef struct {
   uint64_t code_off, code_bytes;   /* 4-bit codes, N*K/2 bytes              */
   uint64_t scale_off, scale_bytes; /* bf16 scales, N*K/64 values            */
   uint64_t bias_off, bias_bytes;   /* bf16 biases, N*K/64 values            */
+  /* Q4_LAYOUT_TILED16 only (0 for the planar layout): */
+  uint32_t tile_rows;     /* 16 output rows per tile                        */
+  uint32_t record_groups; /* 4 groups (256 inputs) per record               */
+  uint64_t record_bytes;  /* 2304 bytes per record                          */
 } q4_layout;
 
 /*
@@ -80,8 +85,22 @@ typedef struct {
  *   scales at N*K/2       : [N][K/64] bf16, row-major (group g of row n at
  *                           index n*K/64 + g);
  *   biases at N*K/2+N*K/32: [N][K/64] bf16, same order.
- * Arguments: N >= 1, K >= 64 with K % 64 == 0, layout_id
- * Q4_LAYOUT_PLANAR, `out` non-NULL (written only on success).
+ * In the planar layout the code/scale/bias offsets and sizes are filled in.
+ *
+ * Layout Q4_LAYOUT_TILED16 holds the same bytes reordered for the GPU (see
+ * q4_repack); it needs N % 16 == 0, K % 256 == 0 and K <= 2^26 and has the same
+ * total_bytes.  Output rows are cut into tiles of 16, a tile's K into records
+ * of 4 groups; tile t's records follow one another (record r of tile t at
+ * byte (t*K/256 + r) * 2304).  A record is
+ *   [0, 1024)   groups 0 and 1:  16 bytes per lane l = j + 16*kb (j = row in
+ *               tile, kb = 0..3): the 8 code bytes kb*8..kb*8+7 of group 0
+ *               of row j, then the same 8 bytes of group 1;
+ *   [1024,2048) groups 2 and 3, same arrangement;
+ *   [2048,2304) 16 bytes per row j: scale, bias of group 0, scale, bias of
+ *               group 1, ... group 3 (bf16 each).
+ * Code bytes keep their nibble order (low nibble = even input).
+ * Arguments: N >= 1, K >= 64 with K % 64 == 0, a known layout_id, `out`
+ * non-NULL (written only on success).
  * Errors: Q4_EINVAL (bad size, id or NULL), Q4_EOVERFLOW (size > 2^64-1).
  */
 int q4_pack_layout(int64_t N, int64_t K, uint32_t layout_id, q4_layout *out);
@@ -107,6 +126,35 @@ int q4_pack_layout(int64_t N, int64_t K, uint32_t layout_id, q4_layout *out);
  */
 int q4_gemm_verify(const void *x, const void *W, float *y, int M, int64_t N,
                    int64_t K, void *stream);
+
+/*
+ * q4_repack -- one-time reorder of a planar packed matrix into
+ * Q4_LAYOUT_TILED16, the layout q4_gemm_verify_tiled streams.  A pure byte
+ * permutation: the output holds exactly the input's bytes, total_bytes of
+ * them.  The pages' engine loads weights once and keeps them resident (Splash
+ * engine article, section "Why Apple silicon, and why not the M5"); this is
+ * the one-time step before that residency, timed apart from the GEMM.
+ *   W_planar : device, Q4_LAYOUT_PLANAR, 16-byte aligned, read only.
+ *   W_tiled  : device, total_bytes, 16-byte aligned, overwritten, must not
+ *              overlap W_planar.
+ *   N % 16 == 0, K % 256 == 0, K <= 2^26 (else Q4_EINVAL).
+ * Errors: Q4_EINVAL, Q4_EALIGN, Q4_EOVERFLOW, Q4_EDEVICE, Q4_ELAUNCH.
+ */
+int q4_repack(const void *W_planar, void *W_tiled, int64_t N, int64_t K,
+              void *stream);
+
+/*
+ * q4_gemm_verify_tiled -- the product of q4_gemm_verify for weights in
+ * Q4_LAYOUT_TILED16 (same x, y, M and results within the same bound; every
+ * row's result is independent of M).  Each wave streams whole records with
+ * 16-byte loads, so every weight byte is fetched once in full cache lines.
+ *   x, y, M, stream: as q4_gemm_verify.
+ *   W_tiled : device, Q4_LAYOUT_TILED16 of an N x K matrix, 16-byte aligned.
+ *   N % 16 == 0, K % 256 == 0, K <= 2^26 (else Q4_EINVAL).
+ * Errors: Q4_EINVAL, Q4_EALIGN, Q4_EOVERFLOW, Q4_EDEVICE, Q4_ELAUNCH.
+ */
+int q4_gemm_verify_tiled(const void *x, const void *W_tiled, float *y, int M,
+                         int64_t N, int64_t K, void *stream);
 
 /*
  * q4_dequant -- W_out[n][k] = fp32(s * q + b), rounded once (test hook that
@@ -140,25 +188,26 @@ int q4_stream_read(const void *buf, uint64_t bytes, uint32_t *sink,
  */
 int q4_stream_copy(const void *src, void *dst, uint64_t bytes, void *stream);
 
-/* Launch plan of q4_gemm_verify for one shape (host only, pure). */
+/* Launch plan of a verify GEMM for one shape (host only, pure). */
 typedef struct {
   uint32_t grid;         /* workgroups launched                            */
   uint32_t block;        /* threads per workgroup (64 per wave)            */
-  uint32_t row_tiles;    /* 16-row output tiles per workgroup, one per wave
-                            column                                          */
-  uint32_t k_splits;     /* waves per tile, each taking a contiguous range
-                            of the K/64 groups; partial sums are added in
-                            split order inside the workgroup               */
+  uint32_t row_tiles;    /* 16-row output tiles per workgroup              */
+  uint32_t tiles_per_wave; /* 16-row tiles one wave multiplies at once     */
+  uint32_t k_splits;     /* waves per tile set, each taking a contiguous
+                            range of K; partial sums are added in split
+                            order inside the workgroup                     */
   uint32_t lookahead;    /* groups whose loads are issued ahead of use      */
-  uint32_t reserved;
 } q4_plan;
 
 /*
- * q4_gemm_verify_plan -- the plan q4_gemm_verify(M, N, K) launches.  Same
- * argument rules as q4_gemm_verify for M, N and K; `out` non-NULL.
+ * q4_gemm_verify_plan -- the plan q4_gemm_verify (layout_id
+ * Q4_LAYOUT_PLANAR) or q4_gemm_verify_tiled (Q4_LAYOUT_TILED16) launches for
+ * (M, N, K).  Same argument rules as those calls; `out` non-NULL.
  * Errors: Q4_EINVAL, Q4_EOVERFLOW.
  */
-int q4_gemm_verify_plan(int M, int64_t N, int64_t K, q4_plan *out);
+int q4_gemm_verify_plan(int M, int64_t N, int64_t K, uint32_t layout_id,
+                        q4_plan *out);
 
 /* Human-readable name of a q4_status value (static string, never NULL). */
 const char *q4_status_string(int status);

@@ -10,15 +10,21 @@ Functions (same names as the C entry points):
 
 * :func:`q4_pack_layout` -- byte layout of a packed N x K matrix (host only).
 * :func:`q4_gemm_verify` -- y[M, N] = x[M, K] @ W^T for Q4 W, fp32 out.
+* :func:`q4_repack` -- one-time reorder into the tiled layout.
+* :func:`q4_gemm_verify_tiled` -- the same product on tiled weights.
 * :func:`q4_gemm_verify_plan` -- the launch plan of a shape (host only).
 * :func:`q4_dequant` -- fp32 weights of a packed matrix (test hook).
 * :func:`q4_stream_read`, :func:`q4_stream_copy` -- bandwidth probes.
 * :func:`q4_status_string` -- name of a status code.
 """
-from ._lib import (GROUP, MAX_ROWS, Q4Error, LIB_PATH, lib_exports, load,
-                   q4_dequant, q4_gemm_verify, q4_gemm_verify_plan,
-                   q4_pack_layout, q4_status_string, q4_stream_copy, q4_stream_read)
+from ._lib import (GROUP, LAYOUT_PLANAR, LAYOUT_TILED16, MAX_ROWS, Q4Error,
+                   LIB_PATH, lib_exports, load, q4_dequant, q4_gemm_verify,
+                   q4_gemm_verify_plan, q4_gemm_verify_tiled, q4_pack_layout,
+                   q4_repack, q4_status_string, q4_stream_copy,
+                   q4_stream_read)
 
-__all__ = ["GROUP", "MAX_ROWS", "Q4Error", "LIB_PATH", "lib_exports", "load",
-           "q4_dequant", "q4_gemm_verify", "q4_gemm_verify_plan", "q4_pack_layout",
-           "q4_status_string", "q4_stream_copy", "q4_stream_read"]
+__all__ = ["GROUP", "LAYOUT_PLANAR", "LAYOUT_TILED16", "MAX_ROWS", "Q4Error",
+           "LIB_PATH", "lib_exports", "load", "q4_dequant", "q4_gemm_verify",
+           "q4_gemm_verify_plan", "q4_gemm_verify_tiled", "q4_pack_layout",
+           "q4_repack", "q4_status_string", "q4_stream_copy",
+           "q4_stream_read"]

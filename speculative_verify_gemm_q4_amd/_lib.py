@@ -10,6 +10,7 @@ LIB_PATH = os.path.join(PKG, "libq4verify.so")
 GROUP = 64
 MAX_ROWS = 16
 LAYOUT_PLANAR = 0
+LAYOUT_TILED16 = 1
 
 OK, EINVAL, EALIGN, EOVERFLOW, EDEVICE, ELAUNCH = 0, -1, -2, -3, -4, -5
 
@@ -31,13 +32,17 @@ class _Layout(ctypes.Structure):
                 ("code_off", ctypes.c_uint64), ("code_bytes", ctypes.c_uint64),
                 ("scale_off", ctypes.c_uint64),
                 ("scale_bytes", ctypes.c_uint64),
-                ("bias_off", ctypes.c_uint64), ("bias_bytes", ctypes.c_uint64)]
+                ("bias_off", ctypes.c_uint64), ("bias_bytes", ctypes.c_uint64),
+                ("tile_rows", ctypes.c_uint32),
+                ("record_groups", ctypes.c_uint32),
+                ("record_bytes", ctypes.c_uint64)]
 
 
 class _Plan(ctypes.Structure):
     _fields_ = [("grid", ctypes.c_uint32), ("block", ctypes.c_uint32),
-                ("row_tiles", ctypes.c_uint32), ("k_splits", ctypes.c_uint32),
-                ("lookahead", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+                ("row_tiles", ctypes.c_uint32),
+                ("tiles_per_wave", ctypes.c_uint32),
+                ("k_splits", ctypes.c_uint32), ("lookahead", ctypes.c_uint32)]
 
 
 _lib = None
@@ -48,6 +53,11 @@ _SIGNATURES = {
     "q4_gemm_verify": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                         ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                         ctypes.c_void_p], ctypes.c_int),
+    "q4_gemm_verify_tiled": ([ctypes.c_void_p, ctypes.c_void_p,
+                              ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                              ctypes.c_int64, ctypes.c_void_p], ctypes.c_int),
+    "q4_repack": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                   ctypes.c_int64, ctypes.c_void_p], ctypes.c_int),
     "q4_dequant": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                     ctypes.c_int64, ctypes.c_void_p], ctypes.c_int),
     "q4_stream_read": ([ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
@@ -55,7 +65,8 @@ _SIGNATURES = {
     "q4_stream_copy": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
                         ctypes.c_void_p], ctypes.c_int),
     "q4_gemm_verify_plan": ([ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
-                             ctypes.POINTER(_Plan)], ctypes.c_int),
+                             ctypes.c_uint32, ctypes.POINTER(_Plan)],
+                            ctypes.c_int),
     "q4_status_string": ([ctypes.c_int], ctypes.c_char_p),
 }
 
@@ -95,12 +106,15 @@ def q4_pack_layout(N: int, K: int, layout_id: int = LAYOUT_PLANAR) -> dict:
     return {name: getattr(out, name) for name, _ in _Layout._fields_}
 
 
-def q4_gemm_verify_plan(M: int, N: int, K: int) -> dict:
-    """The launch plan q4_gemm_verify uses for this shape (host only)."""
+def q4_gemm_verify_plan(M: int, N: int, K: int,
+                        layout_id: int = LAYOUT_PLANAR) -> dict:
+    """The launch plan q4_gemm_verify (layout 0) or q4_gemm_verify_tiled
+    (layout 1) uses for this shape (host only)."""
     out = _Plan()
-    st = load().q4_gemm_verify_plan(int(M), int(N), int(K), ctypes.byref(out))
+    st = load().q4_gemm_verify_plan(int(M), int(N), int(K), int(layout_id),
+                                    ctypes.byref(out))
     if st != OK:
-        raise Q4Error(st, f"q4_gemm_verify_plan({M}, {N}, {K})")
+        raise Q4Error(st, f"q4_gemm_verify_plan({M}, {N}, {K}, {layout_id})")
     return {name: getattr(out, name) for name, _ in _Plan._fields_}
 
 
@@ -144,6 +158,35 @@ def q4_gemm_verify(x, W, y, M: int, N: int, K: int, stream=None) -> None:
                                _stream_handle(stream))
     if st != OK:
         raise Q4Error(st, "q4_gemm_verify")
+
+
+def q4_gemm_verify_tiled(x, Wt, y, M: int, N: int, K: int,
+                         stream=None) -> None:
+    """y[M, N] = x[M, K] @ W^T with W repacked by q4_repack."""
+    import torch
+    total = q4_pack_layout(N, K, LAYOUT_TILED16)["total_bytes"]
+    px = _ptr(x, "x", torch.bfloat16, shape=(M, K))
+    pw = _ptr(Wt, "Wt", torch.uint8, numel=total)
+    py = _ptr(y, "y", torch.float32, shape=(M, N))
+    if not (x.device == Wt.device == y.device):
+        raise ValueError("x, Wt and y must be on one device")
+    st = load().q4_gemm_verify_tiled(px, pw, py, int(M), int(N), int(K),
+                                     _stream_handle(stream))
+    if st != OK:
+        raise Q4Error(st, "q4_gemm_verify_tiled")
+
+
+def q4_repack(W, Wt, N: int, K: int, stream=None) -> None:
+    """Reorder planar W into the tiled layout Wt (same byte count)."""
+    import torch
+    total = q4_pack_layout(N, K, LAYOUT_TILED16)["total_bytes"]
+    pw = _ptr(W, "W", torch.uint8, numel=total)
+    pt = _ptr(Wt, "Wt", torch.uint8, numel=total)
+    if W.device != Wt.device:
+        raise ValueError("W and Wt must be on one device")
+    st = load().q4_repack(pw, pt, int(N), int(K), _stream_handle(stream))
+    if st != OK:
+        raise Q4Error(st, "q4_repack")
 
 
 def q4_dequant(W, W_out, N: int, K: int, stream=None) -> None:

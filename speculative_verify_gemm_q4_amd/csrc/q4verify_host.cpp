@@ -13,6 +13,7 @@ namespace q4v {
 namespace {
 
 constexpr int64_t kMaxIndex = 2147483647;  // rows and inputs are int32 in kernels
+constexpr int64_t kMaxTiledK = int64_t{1} << 26;
 
 bool aligned(const void *p, uintptr_t a) {
   return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
@@ -76,7 +77,18 @@ int check_stream_args(const void *a, const void *b, uint64_t bytes) {
   return Q4_OK;
 }
 
-q4_plan plan_gemm(int M, int64_t N, int64_t K) {
+int check_tiled_shape(int64_t N, int64_t K) {
+  const int st = check_matrix_shape(N, K);
+  if (st != Q4_OK) return st;
+  if (N % kTileRows != 0 || K % (kRecordGroups * Q4_GROUP) != 0)
+    return Q4_EINVAL;
+  // buffer offsets are 32-bit: M*K*2 activation bytes and K*9 bytes of one
+  // tile's records must stay below 2^32
+  if (K > kMaxTiledK) return Q4_EINVAL;
+  return Q4_OK;
+}
+
+q4_plan plan_gemm_planar(int M, int64_t N, int64_t K) {
   (void)M;
   // Waves per tile splitting K so that the grid holds enough waves (about 16
   // per CU on 256 CUs) to keep the weight stream in flight, with at least
@@ -89,10 +101,37 @@ q4_plan plan_gemm(int M, int64_t N, int64_t K) {
   q4_plan p;
   std::memset(&p, 0, sizeof p);
   p.row_tiles = static_cast<uint32_t>(ntw);
+  p.tiles_per_wave = 1;
   p.k_splits = static_cast<uint32_t>(ksw);
   p.block = static_cast<uint32_t>(64 * ntw * ksw);
   p.grid = static_cast<uint32_t>((tiles + ntw - 1) / ntw);
   p.lookahead = 4;
+  return p;
+}
+
+q4_plan plan_gemm_tiled(int M, int64_t N, int64_t K) {
+  (void)M;
+  // A wave multiplies one or two 16-row tiles (two halve the activation
+  // loads per weight byte when there are tiles to spare); waves splitting K
+  // are added until about 4096 waves stream at once (16 per CU), keeping at
+  // least one 4-group record per wave; small grids put several tile sets
+  // into one workgroup of four waves.
+  const int64_t tiles = N / kTileRows;
+  const int64_t records = K / (kRecordGroups * Q4_GROUP);
+  const int tnt = tiles >= 1024 ? 2 : 1;
+  const int64_t sets = (tiles + tnt - 1) / tnt;
+  int ksw = 1;
+  while (ksw < 16 && sets * ksw < 4096 && records >= 2 * ksw) ksw *= 2;
+  if (tnt == 2 && ksw > 4) ksw = 4;
+  const int ntw = ksw >= 4 ? 1 : 4 / ksw;
+  q4_plan p;
+  std::memset(&p, 0, sizeof p);
+  p.row_tiles = static_cast<uint32_t>(ntw * tnt);
+  p.tiles_per_wave = static_cast<uint32_t>(tnt);
+  p.k_splits = static_cast<uint32_t>(ksw);
+  p.block = static_cast<uint32_t>(64 * ntw * ksw);
+  p.grid = static_cast<uint32_t>((sets + ntw - 1) / ntw);
+  p.lookahead = kRecordGroups;
   return p;
 }
 
@@ -121,10 +160,29 @@ int check_device() {
 
 extern "C" int q4_pack_layout(int64_t N, int64_t K, uint32_t layout_id,
                               q4_layout *out) {
-  if (out == nullptr || layout_id != Q4_LAYOUT_PLANAR) return Q4_EINVAL;
+  if (out == nullptr) return Q4_EINVAL;
+  if (layout_id != Q4_LAYOUT_PLANAR && layout_id != Q4_LAYOUT_TILED16)
+    return Q4_EINVAL;
   uint64_t total;
-  const int st = q4v::packed_bytes(N, K, &total);
+  int st = q4v::packed_bytes(N, K, &total);
   if (st != Q4_OK) return st;
+  if (layout_id == Q4_LAYOUT_TILED16) {
+    st = q4v::check_tiled_shape(N, K);
+    if (st != Q4_OK) return st;
+    q4_layout l;
+    std::memset(&l, 0, sizeof l);
+    l.abi_version = Q4_ABI_VERSION;
+    l.layout_id = layout_id;
+    l.N = N;
+    l.K = K;
+    l.group = Q4_GROUP;
+    l.total_bytes = total;
+    l.tile_rows = q4v::kTileRows;
+    l.record_groups = q4v::kRecordGroups;
+    l.record_bytes = q4v::kRecordBytes;
+    *out = l;
+    return Q4_OK;
+  }
   const uint64_t elements = static_cast<uint64_t>(N) * static_cast<uint64_t>(K);
   q4_layout l;
   std::memset(&l, 0, sizeof l);
@@ -145,12 +203,21 @@ extern "C" int q4_pack_layout(int64_t N, int64_t K, uint32_t layout_id,
 }
 
 extern "C" int q4_gemm_verify_plan(int M, int64_t N, int64_t K,
-                                   q4_plan *out) {
+                                   uint32_t layout_id, q4_plan *out) {
   if (out == nullptr || M < 1 || M > Q4_MAX_ROWS) return Q4_EINVAL;
-  const int st = q4v::check_matrix_shape(N, K);
-  if (st != Q4_OK) return st;
-  *out = q4v::plan_gemm(M, N, K);
-  return Q4_OK;
+  if (layout_id == Q4_LAYOUT_PLANAR) {
+    const int st = q4v::check_matrix_shape(N, K);
+    if (st != Q4_OK) return st;
+    *out = q4v::plan_gemm_planar(M, N, K);
+    return Q4_OK;
+  }
+  if (layout_id == Q4_LAYOUT_TILED16) {
+    const int st = q4v::check_tiled_shape(N, K);
+    if (st != Q4_OK) return st;
+    *out = q4v::plan_gemm_tiled(M, N, K);
+    return Q4_OK;
+  }
+  return Q4_EINVAL;
 }
 
 extern "C" const char *q4_status_string(int status) {

@@ -175,6 +175,207 @@ __global__ __launch_bounds__(64 * NTW * KSW) void gemm_verify_kernel(
   }
 }
 
+// The same product for weights in Q4_LAYOUT_TILED16.  A record (16 rows x 4
+// groups, 2304 bytes = 144 16-byte units) is laid out so that lane l's
+// operands are unit l (groups 0-1), unit 64 + l (groups 2-3) and unit
+// 128 + j (the row's four scale/bias pairs): every load of a wave is a
+// contiguous, fully used 1 KB (codes) or 256 B (scales and biases) block.
+// Each wave multiplies TNT tiles with one activation operand over a
+// contiguous range of records, and issues the loads of record r + 1 before
+// it computes record r (two register stages used in turn).
+//
+// Loads go through buffer resources bounded to the wave's own range: a load
+// past the range returns zeros without touching memory.  That makes the
+// prefetch past the last record free, and gives activation rows m >= M (and
+// tiles past N) zeros without a branch.  Weight loads are non-temporal: each
+// byte is used once and should not displace the activations from the caches.
+constexpr int kBufferWord3 = 0x00020000;  // gfx9 buffer descriptor format
+constexpr int kNonTemporal = 2;           // cache policy bit of the load
+
+template <int kPolicy>
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r,
+                                               uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(
+      u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kPolicy));
+}
+
+template <int TNT>
+struct TiledStage {
+  u32x4 c0[TNT], c1[TNT], sb[TNT];
+  u32x4 xa[4], xb[4];
+};
+
+template <int TNT, int NTW, int KSW>
+__global__ __launch_bounds__(64 * NTW * KSW) void gemm_tiled_kernel(
+    const uint16_t *__restrict__ x, const uint8_t *__restrict__ Wt,
+    float *__restrict__ y, int M, int N, int K) {
+  const int T = N >> 4;
+  const int Q = K >> 8;
+  const int lane = threadIdx.x & 63;
+  // wave-uniform, so the buffer descriptors below live in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nt = wave % NTW;
+  const int ks = wave / NTW;
+  const int j = lane & 15;
+  const int kb = lane >> 4;
+  const int set = blockIdx.x * NTW + nt;
+  const int qb = static_cast<int>((static_cast<int64_t>(Q) * ks) / KSW);
+  const int qe = static_cast<int>((static_cast<int64_t>(Q) * (ks + 1)) / KSW);
+  const int nq = qe - qb;
+
+  __amdgpu_buffer_rsrc_t wr[TNT];
+#pragma unroll
+  for (int t = 0; t < TNT; ++t) {
+    const int tile = set * TNT + t;
+    const bool ok = tile < T;
+    const uint8_t *base =
+        Wt + (static_cast<uint64_t>(ok ? tile : 0) * Q + qb) * kRecordBytes;
+    wr[t] = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(base), 0, ok ? nq * kRecordBytes : 0,
+        kBufferWord3);
+  }
+  // activations: rows >= M fall past the M*K*2 bytes of the resource
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(x), 0,
+      static_cast<int>(static_cast<uint32_t>(M) * static_cast<uint32_t>(K) * 2u),
+      kBufferWord3);
+  const uint32_t xoff =
+      (static_cast<uint32_t>(j) * K + kb * 16 + static_cast<uint32_t>(qb) * 256) *
+      2;
+
+  const u32x4 neg = {kNeg128Pair, kNeg128Pair, kNeg128Pair, kNeg128Pair};
+  const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[TNT];
+#pragma unroll
+  for (int t = 0; t < TNT; ++t) acc[t] = fzero;
+
+  auto load = [&](int q, TiledStage<TNT> &st) {
+    const uint32_t rq = static_cast<uint32_t>(q) * kRecordBytes;
+#pragma unroll
+    for (int t = 0; t < TNT; ++t) {
+      st.c0[t] = buffer_load16<kNonTemporal>(wr[t], lane * 16, rq);
+      st.c1[t] = buffer_load16<kNonTemporal>(wr[t], 1024 + lane * 16, rq);
+      st.sb[t] = buffer_load16<kNonTemporal>(wr[t], 2048 + j * 16, rq);
+    }
+    const uint32_t xq = xoff + static_cast<uint32_t>(q) * 512;
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      st.xa[gi] = buffer_load16<0>(xr, xq + gi * 128, 0);
+      st.xb[gi] = buffer_load16<0>(xr, xq + gi * 128 + 16, 0);
+    }
+  };
+
+  auto compute = [&](const TiledStage<TNT> &st) {
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      const u32x4 a0 = pair_activations(st.xa[gi]);
+      const u32x4 a1 = pair_activations(st.xb[gi]);
+      f32x4 xn = mfma16x16x32(a0, neg, fzero);
+      xn = mfma16x16x32(a1, neg, xn);
+#pragma unroll
+      for (int t = 0; t < TNT; ++t) {
+        const u32x4 cw = gi < 2 ? st.c0[t] : st.c1[t];
+        const uint32_t w0 = (gi & 1) ? cw.z : cw.x;
+        const uint32_t w1 = (gi & 1) ? cw.w : cw.y;
+        f32x4 tq = mfma16x16x32(a0, unpack_codes(w0), xn);
+        tq = mfma16x16x32(a1, unpack_codes(w1), tq);
+        const uint32_t sbw = st.sb[t][gi];
+        const float s = __uint_as_float(sbw << 16);
+        const float bn = __uint_as_float(sbw & 0xFFFF0000u) * kMinusInv128;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          acc[t][r] = __builtin_fmaf(bn, xn[r], acc[t][r]);
+          acc[t][r] = __builtin_fmaf(s, tq[r], acc[t][r]);
+        }
+      }
+    }
+  };
+
+  // Both stages are computed unconditionally: a stage past the range holds
+  // zeros and adds exactly zero, and a branch would let the compiler sink the
+  // prefetch next to its use.
+  // The scheduling barriers keep each stage's loads together, issued before
+  // the other stage's arithmetic, so one whole stage is always in flight.
+  TiledStage<TNT> sa, sbuf;
+  load(0, sa);
+  for (int q = 0; q < nq; q += 2) {
+    load(q + 1, sbuf);  // past the range: zeros, no memory traffic
+    __builtin_amdgcn_sched_barrier(0);
+    compute(sa);
+    __builtin_amdgcn_sched_barrier(0);
+    load(q + 2, sa);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(sbuf);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  if constexpr (KSW > 1) {
+    __shared__ f32x4 partial[KSW][NTW][TNT][64];
+#pragma unroll
+    for (int t = 0; t < TNT; ++t) partial[ks][nt][t][lane] = acc[t];
+    __syncthreads();
+    if (ks != 0) return;
+#pragma unroll
+    for (int s = 1; s < KSW; ++s)
+#pragma unroll
+      for (int t = 0; t < TNT; ++t) acc[t] += partial[s][nt][t][lane];
+  }
+#pragma unroll
+  for (int t = 0; t < TNT; ++t) {
+    const int tile = set * TNT + t;
+    if (tile < T) {
+      const int n = tile * 16 + j;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = kb * 4 + r;
+        if (m < M) y[static_cast<uint64_t>(m) * N + n] = acc[t][r];
+      }
+    }
+  }
+}
+
+// Planar -> tiled, one thread per 16-byte unit of the output.
+__global__ __launch_bounds__(256) void repack_kernel(
+    const uint8_t *__restrict__ W, u32x4 *__restrict__ out, int N, int K) {
+  constexpr int kUnits = kRecordBytes / 16;
+  const int G = K >> 6;
+  const int Q = K >> 8;
+  const uint64_t NK = static_cast<uint64_t>(N) * static_cast<uint64_t>(K);
+  const uint64_t units = NK * 9 / 16 / 16;
+  const uint16_t *scales = reinterpret_cast<const uint16_t *>(W + NK / 2);
+  const uint16_t *biases = reinterpret_cast<const uint16_t *>(W + NK / 2 + NK / 32);
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
+  for (uint64_t u = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+       u < units; u += stride) {
+    const uint64_t record = u / kUnits;
+    const int within = static_cast<int>(u % kUnits);
+    const uint64_t tile = record / Q;
+    const int q = static_cast<int>(record % Q);
+    u32x4 v;
+    if (within < 128) {
+      const int pair = within >> 6;
+      const int l = within & 63;
+      const uint64_t n = tile * 16 + (l & 15);
+      const int kb = l >> 4;
+      const int g0 = 4 * q + 2 * pair;
+      const uint8_t *row = W + n * static_cast<uint64_t>(K >> 1);
+      const u32x2 a = *reinterpret_cast<const u32x2 *>(row + g0 * 32 + kb * 8);
+      const u32x2 b = *reinterpret_cast<const u32x2 *>(row + (g0 + 1) * 32 + kb * 8);
+      v = u32x4{a.x, a.y, b.x, b.y};
+    } else {
+      const uint64_t n = tile * 16 + (within - 128);
+      const uint64_t gi = n * G + 4 * q;
+      const u32x2 sv = *reinterpret_cast<const u32x2 *>(scales + gi);
+      const u32x2 bv = *reinterpret_cast<const u32x2 *>(biases + gi);
+      v.x = (sv.x & 0xFFFFu) | (bv.x << 16);
+      v.y = (sv.x >> 16) | (bv.x & 0xFFFF0000u);
+      v.z = (sv.y & 0xFFFFu) | (bv.y << 16);
+      v.w = (sv.y >> 16) | (bv.y & 0xFFFF0000u);
+    }
+    out[u] = v;
+  }
+}
+
 // W_out[n][k] = s * q + b, one thread per 32-bit code word (8 inputs).
 __global__ __launch_bounds__(256) void dequant_kernel(
     const uint8_t *__restrict__ W, float *__restrict__ out, int N, int K) {
@@ -247,6 +448,15 @@ int launch_status() {
   return hipGetLastError() == hipSuccess ? Q4_OK : Q4_ELAUNCH;
 }
 
+template <int TNT, int NTW, int KSW>
+int launch_tiled(const q4_plan &p, const void *x, const void *W, float *y,
+                 int M, int N, int K, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_tiled_kernel<TNT, NTW, KSW>), dim3(p.grid),
+                     dim3(p.block), 0, stream, static_cast<const uint16_t *>(x),
+                     static_cast<const uint8_t *>(W), y, M, N, K);
+  return launch_status();
+}
+
 template <int NTW, int KSW>
 int launch_gemm(const q4_plan &p, const void *x, const void *W, float *y,
                 int M, int N, int K, hipStream_t stream) {
@@ -267,7 +477,7 @@ extern "C" int q4_gemm_verify(const void *x, const void *W, float *y, int M,
   if (st != Q4_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int n = static_cast<int>(N), k = static_cast<int>(K);
-  const q4_plan p = q4v::plan_gemm(M, N, K);
+  const q4_plan p = q4v::plan_gemm_planar(M, N, K);
   switch (p.k_splits) {
     case 1: return q4v::launch_gemm<4, 1>(p, x, W, y, M, n, k, s);
     case 2: return q4v::launch_gemm<2, 2>(p, x, W, y, M, n, k, s);
@@ -276,6 +486,51 @@ extern "C" int q4_gemm_verify(const void *x, const void *W, float *y, int M,
     case 16: return q4v::launch_gemm<1, 16>(p, x, W, y, M, n, k, s);
     default: return Q4_EINVAL;
   }
+}
+
+extern "C" int q4_gemm_verify_tiled(const void *x, const void *W, float *y,
+                                    int M, int64_t N, int64_t K,
+                                    void *stream) {
+  int st = q4v::check_gemm_args(x, W, y, M, N, K);
+  if (st != Q4_OK) return st;
+  st = q4v::check_tiled_shape(N, K);
+  if (st != Q4_OK) return st;
+  st = q4v::check_device();
+  if (st != Q4_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int n = static_cast<int>(N), k = static_cast<int>(K);
+  const q4_plan p = q4v::plan_gemm_tiled(M, N, K);
+  const int key = static_cast<int>(p.tiles_per_wave * 100 + p.k_splits);
+  switch (key) {
+    case 101: return q4v::launch_tiled<1, 4, 1>(p, x, W, y, M, n, k, s);
+    case 102: return q4v::launch_tiled<1, 2, 2>(p, x, W, y, M, n, k, s);
+    case 104: return q4v::launch_tiled<1, 1, 4>(p, x, W, y, M, n, k, s);
+    case 108: return q4v::launch_tiled<1, 1, 8>(p, x, W, y, M, n, k, s);
+    case 116: return q4v::launch_tiled<1, 1, 16>(p, x, W, y, M, n, k, s);
+    case 201: return q4v::launch_tiled<2, 4, 1>(p, x, W, y, M, n, k, s);
+    case 202: return q4v::launch_tiled<2, 2, 2>(p, x, W, y, M, n, k, s);
+    case 204: return q4v::launch_tiled<2, 1, 4>(p, x, W, y, M, n, k, s);
+    default: return Q4_EINVAL;
+  }
+}
+
+extern "C" int q4_repack(const void *W, void *W_tiled, int64_t N, int64_t K,
+                         void *stream) {
+  int st = q4v::check_dequant_args(W, static_cast<const float *>(W_tiled), N, K);
+  if (st != Q4_OK) return st;
+  st = q4v::check_tiled_shape(N, K);
+  if (st != Q4_OK) return st;
+  st = q4v::check_device();
+  if (st != Q4_OK) return st;
+  const uint64_t units = static_cast<uint64_t>(N) * static_cast<uint64_t>(K) * 9 / 256;
+  const uint64_t want = (units + 255) / 256;
+  const unsigned blocks = static_cast<unsigned>(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(q4v::repack_kernel, dim3(blocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream),
+                     static_cast<const uint8_t *>(W),
+                     static_cast<q4v::u32x4 *>(W_tiled), static_cast<int>(N),
+                     static_cast<int>(K));
+  return q4v::launch_status();
 }
 
 extern "C" int q4_dequant(const void *W, float *W_out, int64_t N, int64_t K,

@@ -98,3 +98,23 @@ def round_f32(v: Fraction) -> np.float32:
     if val >= Fraction(2) ** 128:
         return np.float32(sign * np.inf)
     return np.float32(sign * float(val))
+
+
+def tiled_from_planar(packed: np.ndarray, N: int, K: int) -> np.ndarray:
+    """Bytes of the tiled layout (records of 16 rows x 4 groups), restated
+    from its definition: per record, two 1 KB blocks of 16 bytes per lane
+    l = j + 16*kb (code bytes kb*8..kb*8+7 of group 2p, then of group 2p+1,
+    of row j) and 16 bytes per row j of (scale, bias) for the 4 groups."""
+    codes, s, b = split_planes(packed, N, K)
+    T, Q = N // 16, K // 256
+    c = codes.reshape(T, 16, Q, 4, 4, 8)          # tile, j, q, group, kb, 8
+    out = np.empty((T, Q, 2304), dtype=np.uint8)
+    for p in range(2):
+        pair = np.concatenate([c[:, :, :, 2 * p], c[:, :, :, 2 * p + 1]],
+                              axis=-1)              # tile, j, q, kb, 16
+        out[:, :, 1024 * p:1024 * (p + 1)] = \
+            pair.transpose(0, 2, 3, 1, 4).reshape(T, Q, 1024)
+    sb = np.stack([s.reshape(T, 16, Q, 4), b.reshape(T, 16, Q, 4)], axis=-1)
+    sb = sb.transpose(0, 2, 1, 3, 4).reshape(T, Q, 16 * 8)   # u16 values
+    out[:, :, 2048:] = sb.astype("<u2").view(np.uint8).reshape(T, Q, 256)
+    return out.reshape(-1)

@@ -75,6 +75,39 @@ def test_layout_matches_oracle_and_generator(lib, N, K):
         assert b.data_ptr() - base == lay["bias_off"]
 
 
+@pytest.mark.parametrize("N,K", [(16, 256), (256, 512), (34816, 5120),
+                                 (5120, 17408), (248320, 5120), (5120, 6144)])
+def test_tiled_layout(lib, N, K):
+    lay = q4.q4_pack_layout(N, K, q4.LAYOUT_TILED16)
+    assert lay["layout_id"] == 1
+    assert lay["total_bytes"] == oracle.packed_bytes(N, K)
+    assert lay["tile_rows"] == 16 and lay["record_groups"] == 4
+    assert lay["record_bytes"] == 2304 == 16 * 4 * 64 * 9 // 16
+    assert lay["total_bytes"] == (N // 16) * (K // 256) * lay["record_bytes"]
+    assert lay["code_bytes"] == lay["scale_bytes"] == lay["bias_bytes"] == 0
+
+
+def test_tiled_shape_rules(lib):
+    from speculative_verify_gemm_q4_amd._lib import _Layout
+    out = _Layout()
+    f = lib.q4_pack_layout
+    assert f(17, 256, 1, ctypes.byref(out)) == -1      # N % 16
+    assert f(16, 192, 1, ctypes.byref(out)) == -1      # K % 256
+    assert f(16, (1 << 26) + 256, 1, ctypes.byref(out)) == -1  # K > 2^26
+    g = lib.q4_gemm_verify_tiled
+    X, W, Y = 0x10000, 0x20000, 0x30000
+    assert g(X, W, Y, 1, 17, 256, None) == -1
+    assert g(X, W, Y, 1, 16, 320, None) == -1
+    assert g(X, W, Y, 0, 16, 256, None) == -1
+    assert g(X, W, Y, 17, 16, 256, None) == -1
+    assert g(X + 8, W, Y, 1, 16, 256, None) == -2
+    r = lib.q4_repack
+    assert r(W, X, 17, 256, None) == -1
+    assert r(W, X, 16, 320, None) == -1
+    assert r(W + 4, X, 16, 256, None) == -2
+    assert r(W, X + 4, 16, 256, None) == -2
+
+
 def test_layout_errors(lib):
     from speculative_verify_gemm_q4_amd._lib import _Layout
     out = _Layout()

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import synth
-from tests.helpers import assemble, bf16_bits_of
+from tests.helpers import assemble, bf16_bits_of, tiled_from_planar
 
 pytestmark = pytest.mark.gpu
 
@@ -55,12 +55,29 @@ def assert_within_bound(y_gpu, y64, a64, what=""):
     return ratio
 
 
-def oracle_check(q4, M, N, K, seed, what):
+def repacked(q4, W, N, K):
+    Wt = torch.empty_like(W)
+    q4.q4_repack(W, Wt, N, K)
+    torch.cuda.synchronize()
+    return Wt
+
+
+def gemm_tiled(q4, x, Wt, M, N, K):
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=x.device)
+    q4.q4_gemm_verify_tiled(x, Wt, y, M, N, K)
+    torch.cuda.synchronize()
+    return y
+
+
+def oracle_check(q4, M, N, K, seed, what, tiled=False):
     dev = torch.device("cuda")
     W = synth.q4_weights(N, K, seed=seed, device=dev)
     x = synth.activations(M, K, seed=seed, stream=1, device=dev)
-    _say(f"case {what}: M={M} N={N} K={K} seed={seed}")
-    y = gemm(q4, x, W, M, N, K)
+    _say(f"case {what}: M={M} N={N} K={K} seed={seed} tiled={tiled}")
+    if tiled:
+        y = gemm_tiled(q4, x, repacked(q4, W, N, K), M, N, K)
+    else:
+        y = gemm(q4, x, W, M, N, K)
     _, y64, a64, _ = oracle.gemm(synth.bf16_bits(x), W.cpu().numpy(), N, K)
     return assert_within_bound(y, y64, a64, what)
 
@@ -245,6 +262,96 @@ def test_lm_head_two_calls(q4):
         y = gemm(q4, x, W, M, N, K)
         _, y64, a64, _ = oracle.gemm(synth.bf16_bits(x), Wsub, len(rows), K)
         assert_within_bound(y[:, idx], y64, a64, f"lm head call {call}")
+
+
+# -------------------------------------------------------------- tiled layout
+
+TILED = [(16, 16, 256), (1, 16, 256), (16, 256, 512), (5, 1600, 1024),
+         (5, 1600, 2048), (16, 5120, 6144), (3, 5120, 17408),
+         (16, 80000, 1024), (7, 1040, 256), (16, 2048, 4096)]
+
+
+@pytest.mark.parametrize("N,K", [(16, 256), (256, 512), (1600, 2048),
+                                 (5120, 6144)])
+def test_repack_bytes(q4, N, K):
+    """q4_repack against the layout restated in numpy from its definition."""
+    dev = torch.device("cuda")
+    W = synth.q4_weights(N, K, seed=20, device=dev)
+    _say(f"case repack N={N} K={K}")
+    Wt = repacked(q4, W, N, K).cpu().numpy()
+    assert np.array_equal(Wt, tiled_from_planar(W.cpu().numpy(), N, K))
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 9, 15, 16])
+def test_tiled_tiny(q4, M):
+    oracle_check(q4, M, 256, 512, 0, "tiled tiny", tiled=True)
+
+
+@pytest.mark.parametrize("M,N,K", TILED)
+def test_tiled_shapes(q4, M, N, K):
+    """Shapes covering every launch configuration of the tiled kernel."""
+    oracle_check(q4, M, N, K, 2, "tiled", tiled=True)
+
+
+def test_tiled_integer_exact_and_M_invariance(q4):
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(21)
+    N, K = 2048, 3072
+    q = rng.integers(0, 16, size=(N, K))
+    G = K // 64
+    codes = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    Wh = assemble(codes, bf16_bits_of(np.ones((N, G))),
+                  bf16_bits_of(np.full((N, G), -8.0)))
+    xi = rng.integers(-4, 5, size=(16, K)).astype(np.float32)
+    Wt = repacked(q4, torch.from_numpy(Wh).to(dev), N, K)
+    x = torch.from_numpy(xi).to(torch.bfloat16).to(dev)
+    _say("case tiled integer-exact")
+    y = gemm_tiled(q4, x, Wt, 16, N, K)
+    y32, _, _, _ = oracle.gemm(bf16_bits_of(xi), Wh, N, K)
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), y32.view(np.uint32))
+    # random data: rows do not depend on M, and the planar kernel agrees
+    W = synth.q4_weights(N, K, seed=22, device=dev)
+    Wt = repacked(q4, W, N, K)
+    xr = synth.activations(16, K, seed=22, stream=1, device=dev)
+    full = gemm_tiled(q4, xr, Wt, 16, N, K)
+    for M in (1, 5, 12):
+        part = gemm_tiled(q4, xr[:M].contiguous(), Wt, M, N, K)
+        assert torch.equal(part.view(torch.int32), full[:M].view(torch.int32))
+    _, y64, a64, _ = oracle.gemm(synth.bf16_bits(xr), W.cpu().numpy(), N, K)
+    assert_within_bound(full, y64, a64, "tiled random")
+
+
+def test_tiled_one_hot_bitwise(q4):
+    dev = torch.device("cuda")
+    N, K = 160, 768
+    W = synth.q4_weights(N, K, seed=23, device=dev)
+    ks = [0, 1, 63, 64, 255, 256, 300, 511, 512, 767]
+    x = torch.zeros((len(ks), K), dtype=torch.bfloat16, device=dev)
+    for m, k in enumerate(ks):
+        x[m, k] = 1.0
+    _say("case tiled one-hot")
+    y = gemm_tiled(q4, x, repacked(q4, W, N, K), len(ks), N, K).cpu().numpy()
+    w = oracle.dequant(W.cpu().numpy(), N, K)
+    for m, k in enumerate(ks):
+        assert np.array_equal(y[m].view(np.uint32), w[:, k].view(np.uint32)), k
+
+
+@pytest.mark.parametrize("name,M", [(n, m) for n in FULL for m in (1, 16)])
+def test_tiled_full_shape_sampled(q4, name, M):
+    dev = torch.device("cuda")
+    N, K = FULL[name]
+    W = synth.q4_weights(N, K, seed=13, stream=list(FULL).index(name),
+                          device=dev)
+    Wt = repacked(q4, W, N, K)
+    x = synth.activations(M, K, seed=13, stream=3000 + M, device=dev)
+    _say(f"case tiled full {name}: M={M} N={N} K={K}")
+    y = gemm_tiled(q4, x, Wt, M, N, K)
+    rows = sampled_rows(N, 224, seed=M + 1)
+    Wsub = sub_matrix(W, N, K, rows)
+    _, y64, a64, _ = oracle.gemm(synth.bf16_bits(x), Wsub, len(rows), K)
+    got = y[:, torch.as_tensor(rows, device=dev)]
+    assert_within_bound(got, y64, a64, f"tiled {name} M={M}")
+    assert torch.isfinite(y).all()
 
 
 # -------------------------------------------------------------- probes

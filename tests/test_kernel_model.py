@@ -24,7 +24,7 @@ SHAPES = [(1, 1, 64), (3, 17, 192), (16, 257, 640), (5, 1000, 1088),
 
 
 def model(M, N, K):
-    p = q4.q4_gemm_verify_plan(M, N, K)
+    p = q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_PLANAR)
     ntw, ksw, grid, block = p["row_tiles"], p["k_splits"], p["grid"], p["block"]
     assert block == 64 * ntw * ksw and block <= 1024
     assert ntw * ksw in (4, 8, 16)
@@ -105,3 +105,68 @@ def test_plan_rejects_bad_shapes():
         q4.q4_gemm_verify_plan(17, 16, 64)
     with pytest.raises(q4.Q4Error):
         q4.q4_gemm_verify_plan(1, 16, 96)
+    with pytest.raises(q4.Q4Error):
+        q4.q4_gemm_verify_plan(1, 24, 256, q4.LAYOUT_TILED16)
+    with pytest.raises(q4.Q4Error):
+        q4.q4_gemm_verify_plan(1, 16, 64, 7)
+
+
+# --------------------------------------------------------------------------
+# tiled layout: wave (nt, ks) of block b takes tile set b*NTW + nt, i.e. tiles
+# set*TNT + t, and records [Q*ks/KSW, Q*(ks+1)/KSW) of each; its buffer
+# resources cover exactly those records (tiles past N get an empty range).
+# Lane l reads units l, 64 + l and 128 + j of a record (16-byte units), and
+# activation elements j*K + 16*kb + 256*q + 64*gi + 0..15 (j < M, else the
+# load falls past the M*K*2-byte activation range and reads nothing).
+
+TILED_SHAPES = [(16, 16, 256), (16, 256, 512), (5, 1600, 1024),
+                (5, 1600, 2048), (16, 5120, 6144), (3, 5120, 17408),
+                (16, 80000, 1024), (16, 34816, 5120), (1, 248320, 5120),
+                (16, 14336, 5120), (16, 16640, 5120), (16, 1040, 256)]
+
+
+@pytest.mark.parametrize("M,N,K", TILED_SHAPES)
+def test_tiled_plan_reads_every_record_once(M, N, K):
+    p = q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_TILED16)
+    tnt, ksw, grid, block = (p["tiles_per_wave"], p["k_splits"], p["grid"],
+                             p["block"])
+    ntw = p["row_tiles"] // tnt
+    assert block == 64 * ntw * ksw <= 1024 and ntw * ksw in (4, 8, 16)
+    T, Q = N // 16, K // 256
+    assert grid * ntw * tnt >= T > (grid - 1) * ntw * tnt
+    # LDS of the split-K reduction: f32x4 [KSW][NTW][TNT][64]
+    assert (ksw * ntw * tnt * 64 * 16 if ksw > 1 else 0) <= 65536
+    bounds = [(Q * ks // ksw, Q * (ks + 1) // ksw) for ks in range(ksw)]
+    assert bounds[0][0] == 0 and bounds[-1][1] == Q
+    assert all(bounds[i][1] == bounds[i + 1][0] for i in range(ksw - 1))
+    hits = np.zeros(T * Q, dtype=np.int32)
+    total = T * Q * 2304
+    for b in range(grid):
+        for nt in range(ntw):
+            for t in range(tnt):
+                tile = (b * ntw + nt) * tnt + t
+                if tile >= T:
+                    continue
+                for qb, qe in bounds:
+                    hits[tile * Q + qb: tile * Q + qe] += 1
+                    # the wave's resource range lies inside the buffer
+                    assert (tile * Q + qe) * 2304 <= total
+    assert np.all(hits == 1)
+    # activation offsets in bytes fit the 32-bit buffer offset, and rows < M
+    # stay inside the M*K*2 bytes
+    j = np.arange(16)[:, None]
+    kb = np.arange(4)[None, :]
+    last = (j * K + 16 * kb + 256 * (Q - 1) + 64 * 3 + 8) * 2 + 16
+    assert last.max() < 2 ** 32
+    assert last[:M].max() <= M * K * 2
+    first_out = (j[M:] * K) * 2
+    assert np.all(first_out >= M * K * 2)
+    # every output written once: tiles < T, rows 4kb+r < M
+    out = np.zeros((M, N), dtype=np.int32)
+    for tile in range(T):
+        for kbv in range(4):
+            for r in range(4):
+                m = 4 * kbv + r
+                if m < M:
+                    out[m, tile * 16: tile * 16 + 16] += 1
+    assert np.all(out == 1)
