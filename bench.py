@@ -187,6 +187,10 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="run q4_stream_copy over this many MB three times "
+                         "(the known-traffic kernel the byte counters are "
+                         "scaled against)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -221,6 +225,16 @@ def main():
     x1 = x16[:1].contiguous()
     y16 = torch.empty((Mv, N), dtype=torch.float32, device=dev)
     y1 = torch.empty((1, N), dtype=torch.float32, device=dev)
+
+    if args.copy_calibration_mb:
+        nb = args.copy_calibration_mb * 2 ** 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty(nb, dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            q4.q4_stream_copy(src, dst, nb)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copy calibration: 3 x {nb} bytes read and written")
 
     # one-time repack into the tiled layout, timed on its own
     Wts = [torch.empty_like(W) for W in Ws]

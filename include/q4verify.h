@@ -98,7 +98,10 @@ typedef struct {
  *   [1024,2048) groups 2 and 3, same arrangement;
  *   [2048,2304) 16 bytes per row j: scale, bias of group 0, scale, bias of
  *               group 1, ... group 3 (bf16 each).
- * Code bytes keep their nibble order (low nibble = even input).
+ * Within each 32-bit little-endian code word (8 inputs i = 0..7 of a lane,
+ * input i in nibble i of the planar word) the nibbles are reordered to
+ * inputs 0, 2, 4, 6, 1, 3, 5, 7: even inputs in the low 16 bits, odd inputs
+ * in the high 16 bits.
  * Arguments: N >= 1, K >= 64 with K % 64 == 0, a known layout_id, `out`
  * non-NULL (written only on success).
  * Errors: Q4_EINVAL (bad size, id or NULL), Q4_EOVERFLOW (size > 2^64-1).
@@ -129,9 +132,9 @@ int q4_gemm_verify(const void *x, const void *W, float *y, int M, int64_t N,
 
 /*
  * q4_repack -- one-time reorder of a planar packed matrix into
- * Q4_LAYOUT_TILED16, the layout q4_gemm_verify_tiled streams.  A pure byte
- * permutation: the output holds exactly the input's bytes, total_bytes of
- * them.  The pages' engine loads weights once and keeps them resident (Splash
+ * Q4_LAYOUT_TILED16, the layout q4_gemm_verify_tiled streams.  A pure
+ * permutation of 4-bit codes and bf16 values: the output holds exactly the
+ * input's codes, scales and biases, total_bytes of them.  The pages' engine loads weights once and keeps them resident (Splash
  * engine article, section "Why Apple silicon, and why not the M5"); this is
  * the one-time step before that residency, timed apart from the GEMM.
  *   W_planar : device, Q4_LAYOUT_PLANAR, 16-byte aligned, read only.

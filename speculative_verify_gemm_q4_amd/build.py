@@ -22,6 +22,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Wall", "-Wextra", "-Wno-unused-parameter",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # MFMA results in VGPRs: the epilogue reads them without moves
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I", INCLUDE, "-I", CSRC]
 
 

@@ -111,26 +111,26 @@ q4_plan plan_gemm_planar(int M, int64_t N, int64_t K) {
 
 q4_plan plan_gemm_tiled(int M, int64_t N, int64_t K) {
   (void)M;
-  // A wave multiplies one or two 16-row tiles (two halve the activation
-  // loads per weight byte when there are tiles to spare); waves splitting K
-  // are added until about 4096 waves stream at once (16 per CU), keeping at
-  // least one 4-group record per wave; small grids put several tile sets
-  // into one workgroup of four waves.
+  // Tiles per wave: each wave multiplies its activation operand with 1-4
+  // tiles, so the activation loads per weight byte fall with more tiles
+  // while the registers per wave (and so the waves per SIMD) rise; wide
+  // matrices take more.  Waves splitting K (one workgroup = those waves) are
+  // then added until about 1024 waves stream at once, keeping at least one
+  // 4-group record per wave.  Both rules follow measured sweeps on MI355X of
+  // the 27B model's projection shapes.
   const int64_t tiles = N / kTileRows;
   const int64_t records = K / (kRecordGroups * Q4_GROUP);
-  const int tnt = tiles >= 1024 ? 2 : 1;
+  const int tnt = tiles >= 4096 ? 4 : tiles >= 1536 ? 3 : tiles >= 2 ? 2 : 1;
   const int64_t sets = (tiles + tnt - 1) / tnt;
   int ksw = 1;
-  while (ksw < 16 && sets * ksw < 4096 && records >= 2 * ksw) ksw *= 2;
-  if (tnt == 2 && ksw > 4) ksw = 4;
-  const int ntw = ksw >= 4 ? 1 : 4 / ksw;
+  while (ksw < 8 && sets * ksw < 1024 && records >= 2 * ksw) ksw *= 2;
   q4_plan p;
   std::memset(&p, 0, sizeof p);
-  p.row_tiles = static_cast<uint32_t>(ntw * tnt);
+  p.row_tiles = static_cast<uint32_t>(tnt);
   p.tiles_per_wave = static_cast<uint32_t>(tnt);
   p.k_splits = static_cast<uint32_t>(ksw);
-  p.block = static_cast<uint32_t>(64 * ntw * ksw);
-  p.grid = static_cast<uint32_t>((sets + ntw - 1) / ntw);
+  p.block = static_cast<uint32_t>(64 * ksw);
+  p.grid = static_cast<uint32_t>(sets);
   p.lookahead = kRecordGroups;
   return p;
 }

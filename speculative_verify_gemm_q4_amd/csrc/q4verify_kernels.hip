@@ -44,14 +44,29 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
+// The two constants of the unpack, kept in registers so that each
+// (code pair & mask) | magic is one v_and_or_b32 (gfx9 VOP3 encodings take
+// no literal operands, so with literals it would take two instructions).
+struct UnpackConsts {
+  uint32_t mask;   // scalar register
+  uint32_t magic;  // vector register
+};
+
+__device__ __forceinline__ UnpackConsts unpack_consts() {
+  UnpackConsts c;
+  c.mask = __builtin_amdgcn_readfirstlane(0x000F000Fu);
+  asm volatile("v_mov_b32 %0, %1" : "=v"(c.magic) : "s"(kMagic128Pair));
+  return c;
+}
+
 // Codes q0..q7 (bits 4i..4i+3 of w) -> bf16 pairs (128+q0, 128+q4),
 // (128+q1, 128+q5), (128+q2, 128+q6), (128+q3, 128+q7).
-__device__ __forceinline__ u32x4 unpack_codes(uint32_t w) {
+__device__ __forceinline__ u32x4 unpack_codes(uint32_t w, UnpackConsts c) {
   u32x4 r;
-  r.x = (w & 0x000F000Fu) | kMagic128Pair;
-  r.y = ((w >> 4) & 0x000F000Fu) | kMagic128Pair;
-  r.z = ((w >> 8) & 0x000F000Fu) | kMagic128Pair;
-  r.w = ((w >> 12) & 0x000F000Fu) | kMagic128Pair;
+  r.x = (w & c.mask) | c.magic;
+  r.y = ((w >> 4) & c.mask) | c.magic;
+  r.z = ((w >> 8) & c.mask) | c.magic;
+  r.w = ((w >> 12) & c.mask) | c.magic;
   return r;
 }
 
@@ -113,6 +128,7 @@ __global__ __launch_bounds__(64 * NTW * KSW) void gemm_verify_kernel(
   const u32x4 neg = {kNeg128Pair, kNeg128Pair, kNeg128Pair, kNeg128Pair};
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
   const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
+  const UnpackConsts uc = unpack_consts();
   f32x4 acc = fzero;
 
   for (int g = gb; g < ge; g += U) {
@@ -146,8 +162,8 @@ __global__ __launch_bounds__(64 * NTW * KSW) void gemm_verify_kernel(
       const u32x4 a1 = pair_activations(xb[u]);
       f32x4 xn = mfma16x16x32(a0, neg, fzero);
       xn = mfma16x16x32(a1, neg, xn);
-      f32x4 t = mfma16x16x32(a0, unpack_codes(cw[u].x), xn);
-      t = mfma16x16x32(a1, unpack_codes(cw[u].y), t);
+      f32x4 t = mfma16x16x32(a0, unpack_codes(cw[u].x, uc), xn);
+      t = mfma16x16x32(a1, unpack_codes(cw[u].y, uc), t);
       const float s = bf16_to_f32(sv[u]);
       const float bn = bf16_to_f32(bv[u]) * kMinusInv128;
 #pragma unroll
@@ -180,6 +196,9 @@ __global__ __launch_bounds__(64 * NTW * KSW) void gemm_verify_kernel(
 // operands are unit l (groups 0-1), unit 64 + l (groups 2-3) and unit
 // 128 + j (the row's four scale/bias pairs): every load of a wave is a
 // contiguous, fully used 1 KB (codes) or 256 B (scales and biases) block.
+// The repack stores each code word's even inputs in its low half and its odd
+// inputs in its high half, so the code pairs come out of unpack_codes in the
+// activations' own order and the activation operand needs no permutation.
 // Each wave multiplies TNT tiles with one activation operand over a
 // contiguous range of records, and issues the loads of record r + 1 before
 // it computes record r (two register stages used in turn).
@@ -245,6 +264,7 @@ __global__ __launch_bounds__(64 * NTW * KSW) void gemm_tiled_kernel(
 
   const u32x4 neg = {kNeg128Pair, kNeg128Pair, kNeg128Pair, kNeg128Pair};
   const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
+  const UnpackConsts uc = unpack_consts();
   f32x4 acc[TNT];
 #pragma unroll
   for (int t = 0; t < TNT; ++t) acc[t] = fzero;
@@ -268,8 +288,8 @@ __global__ __launch_bounds__(64 * NTW * KSW) void gemm_tiled_kernel(
   auto compute = [&](const TiledStage<TNT> &st) {
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
-      const u32x4 a0 = pair_activations(st.xa[gi]);
-      const u32x4 a1 = pair_activations(st.xb[gi]);
+      const u32x4 a0 = st.xa[gi];
+      const u32x4 a1 = st.xb[gi];
       f32x4 xn = mfma16x16x32(a0, neg, fzero);
       xn = mfma16x16x32(a1, neg, xn);
 #pragma unroll
@@ -277,8 +297,8 @@ __global__ __launch_bounds__(64 * NTW * KSW) void gemm_tiled_kernel(
         const u32x4 cw = gi < 2 ? st.c0[t] : st.c1[t];
         const uint32_t w0 = (gi & 1) ? cw.z : cw.x;
         const uint32_t w1 = (gi & 1) ? cw.w : cw.y;
-        f32x4 tq = mfma16x16x32(a0, unpack_codes(w0), xn);
-        tq = mfma16x16x32(a1, unpack_codes(w1), tq);
+        f32x4 tq = mfma16x16x32(a0, unpack_codes(w0, uc), xn);
+        tq = mfma16x16x32(a1, unpack_codes(w1, uc), tq);
         const uint32_t sbw = st.sb[t][gi];
         const float s = __uint_as_float(sbw << 16);
         const float bn = __uint_as_float(sbw & 0xFFFF0000u) * kMinusInv128;
@@ -334,6 +354,19 @@ __global__ __launch_bounds__(64 * NTW * KSW) void gemm_tiled_kernel(
   }
 }
 
+// Code word q0..q7 (nibble i = input i) -> nibbles q0 q2 q4 q6 q1 q3 q5 q7,
+// so that unpack_codes yields the pairs (q0,q1) (q2,q3) (q4,q5) (q6,q7):
+// consecutive inputs, the order of the activations in memory.
+__device__ __forceinline__ uint32_t split_even_odd(uint32_t w) {
+  uint32_t e = w & 0x0F0F0F0Fu;
+  uint32_t o = (w >> 4) & 0x0F0F0F0Fu;
+  e = (e | (e >> 4)) & 0x00FF00FFu;
+  o = (o | (o >> 4)) & 0x00FF00FFu;
+  e = (e | (e >> 8)) & 0x0000FFFFu;
+  o = (o | (o >> 8)) & 0x0000FFFFu;
+  return e | (o << 16);
+}
+
 // Planar -> tiled, one thread per 16-byte unit of the output.
 __global__ __launch_bounds__(256) void repack_kernel(
     const uint8_t *__restrict__ W, u32x4 *__restrict__ out, int N, int K) {
@@ -361,7 +394,8 @@ __global__ __launch_bounds__(256) void repack_kernel(
       const uint8_t *row = W + n * static_cast<uint64_t>(K >> 1);
       const u32x2 a = *reinterpret_cast<const u32x2 *>(row + g0 * 32 + kb * 8);
       const u32x2 b = *reinterpret_cast<const u32x2 *>(row + (g0 + 1) * 32 + kb * 8);
-      v = u32x4{a.x, a.y, b.x, b.y};
+      v = u32x4{split_even_odd(a.x), split_even_odd(a.y), split_even_odd(b.x),
+                split_even_odd(b.y)};
     } else {
       const uint64_t n = tile * 16 + (within - 128);
       const uint64_t gi = n * G + 4 * q;
@@ -502,14 +536,16 @@ extern "C" int q4_gemm_verify_tiled(const void *x, const void *W, float *y,
   const q4_plan p = q4v::plan_gemm_tiled(M, N, K);
   const int key = static_cast<int>(p.tiles_per_wave * 100 + p.k_splits);
   switch (key) {
-    case 101: return q4v::launch_tiled<1, 4, 1>(p, x, W, y, M, n, k, s);
-    case 102: return q4v::launch_tiled<1, 2, 2>(p, x, W, y, M, n, k, s);
-    case 104: return q4v::launch_tiled<1, 1, 4>(p, x, W, y, M, n, k, s);
-    case 108: return q4v::launch_tiled<1, 1, 8>(p, x, W, y, M, n, k, s);
-    case 116: return q4v::launch_tiled<1, 1, 16>(p, x, W, y, M, n, k, s);
-    case 201: return q4v::launch_tiled<2, 4, 1>(p, x, W, y, M, n, k, s);
-    case 202: return q4v::launch_tiled<2, 2, 2>(p, x, W, y, M, n, k, s);
-    case 204: return q4v::launch_tiled<2, 1, 4>(p, x, W, y, M, n, k, s);
+#define Q4V_TILED_CASE(TNT, KSW) \
+  case TNT * 100 + KSW:          \
+    return q4v::launch_tiled<TNT, 1, KSW>(p, x, W, y, M, n, k, s);
+    Q4V_TILED_CASE(1, 1) Q4V_TILED_CASE(1, 2) Q4V_TILED_CASE(1, 4)
+    Q4V_TILED_CASE(1, 8) Q4V_TILED_CASE(2, 1) Q4V_TILED_CASE(2, 2)
+    Q4V_TILED_CASE(2, 4) Q4V_TILED_CASE(2, 8) Q4V_TILED_CASE(3, 1)
+    Q4V_TILED_CASE(3, 2) Q4V_TILED_CASE(3, 4) Q4V_TILED_CASE(3, 8)
+    Q4V_TILED_CASE(4, 1) Q4V_TILED_CASE(4, 2) Q4V_TILED_CASE(4, 4)
+    Q4V_TILED_CASE(4, 8)
+#undef Q4V_TILED_CASE
     default: return Q4_EINVAL;
   }
 }

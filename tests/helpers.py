@@ -104,9 +104,17 @@ def tiled_from_planar(packed: np.ndarray, N: int, K: int) -> np.ndarray:
     """Bytes of the tiled layout (records of 16 rows x 4 groups), restated
     from its definition: per record, two 1 KB blocks of 16 bytes per lane
     l = j + 16*kb (code bytes kb*8..kb*8+7 of group 2p, then of group 2p+1,
-    of row j) and 16 bytes per row j of (scale, bias) for the 4 groups."""
+    of row j, each 4-byte word's nibbles reordered to inputs 0,2,4,6,1,3,5,7)
+    and 16 bytes per row j of (scale, bias) for the 4 groups."""
     codes, s, b = split_planes(packed, N, K)
     T, Q = N // 16, K // 256
+    # within each 4-byte word (inputs 0..7, input i in nibble i) reorder the
+    # nibbles to inputs 0, 2, 4, 6, 1, 3, 5, 7
+    q = np.empty((N, K), dtype=np.uint8)
+    q[:, 0::2] = codes & 15
+    q[:, 1::2] = codes >> 4
+    q = q.reshape(N, K // 8, 8)[:, :, [0, 2, 4, 6, 1, 3, 5, 7]].reshape(N, K)
+    codes = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
     c = codes.reshape(T, 16, Q, 4, 4, 8)          # tile, j, q, group, kb, 8
     out = np.empty((T, Q, 2304), dtype=np.uint8)
     for p in range(2):

@@ -131,7 +131,7 @@ def test_tiled_plan_reads_every_record_once(M, N, K):
     tnt, ksw, grid, block = (p["tiles_per_wave"], p["k_splits"], p["grid"],
                              p["block"])
     ntw = p["row_tiles"] // tnt
-    assert block == 64 * ntw * ksw <= 1024 and ntw * ksw in (4, 8, 16)
+    assert block == 64 * ntw * ksw <= 1024 and ntw * ksw in (1, 2, 4, 8, 16)
     T, Q = N // 16, K // 256
     assert grid * ntw * tnt >= T > (grid - 1) * ntw * tnt
     # LDS of the split-K reduction: f32x4 [KSW][NTW][TNT][64]
