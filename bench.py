@@ -14,9 +14,10 @@ warm up, measure):
     the floor time at the 8 TB/s HBM peak, printed before measuring;
   * weights are rotated over >= 1.2 GB of distinct copies so that neither the
     L2 nor the 256 MB Infinity Cache can serve a repeated read;
-  * W warm-up steps, then K timed steps between device synchronisations;
-    each launch is also bracketed by HIP events on the launch stream, which
-    gives the per-launch kernel duration for the roofline figure.
+  * W warm-up steps, then K timed back-to-back steps between two HIP events
+    on the launch stream, bracketed by device synchronisations; the mean per
+    call is both the step time and the launch duration of the roofline
+    figure (the kernel-trace profile of the same command must agree).
 
 Output: one JSON line on stdout.  `value` is the effective bandwidth of the
 M = 16 step (algorithmic bytes / mean step time, inputs resident in HBM).
@@ -106,29 +107,25 @@ def load_traffic(M, N, K):
 
 
 def time_calls(torch, call, xs, Ws, y, M, N, K, steps, warmup):
-    """Warm up, then time `steps` calls of call(x, W, y, M, N, K); returns
-    (event ms per step, wall ms per step, per-launch event durations in ms)."""
+    """Warm up, then time `steps` back-to-back calls of call(x, W, y, M, N,
+    K) between two HIP events recorded on the launch stream (torch's current
+    stream, which the binding launches on); returns (ms per call from the
+    events, ms per call from the host clock between synchronisations)."""
     stream = torch.cuda.current_stream()
     n_w = len(Ws)
     for i in range(warmup):
         call(xs, Ws[i % n_w], y, M, N, K)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    outer0 = torch.cuda.Event(enable_timing=True)
-    outer1 = torch.cuda.Event(enable_timing=True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    outer0.record(stream)
+    e0.record(stream)
     for i in range(steps):
-        starts[i].record(stream)
-        call(xs, Ws[i % n_w], y, M, N, K)
-        ends[i].record(stream)
-    outer1.record(stream)
+        call(xs, Ws[(warmup + i) % n_w], y, M, N, K)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
-    per_launch = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    outer_ms = outer0.elapsed_time(outer1)
-    return outer_ms / steps, wall_ms / steps, per_launch
+    return e0.elapsed_time(e1) / steps, wall_ms / steps
 
 
 def stream_probe(torch, q4, nbytes):
@@ -254,35 +251,30 @@ def main():
 
     tiled = q4.q4_gemm_verify_tiled
     planar = q4.q4_gemm_verify
-    # timed steps: tiled M = 16, then M = 1, then M = 16 again (A-B-A order
-    # for the ratio); then the planar kernel the same way
-    ms16a, wall16, launches16 = time_calls(torch, tiled, x16, Wts, y16, Mv,
-                                           N, K, args.steps, args.warmup)
-    ms1, wall1, launches1 = time_calls(torch, tiled, x1, Wts, y1, 1, N, K,
-                                       args.steps, args.warmup)
-    ms16b, _, launches16b = time_calls(torch, tiled, x16, Wts, y16, Mv, N, K,
-                                       args.steps, args.warmup)
-    pms16, _, plaunch16 = time_calls(torch, planar, x16, Ws, y16, Mv, N, K,
-                                     args.steps, args.warmup)
-    pms1, _, plaunch1 = time_calls(torch, planar, x1, Ws, y1, 1, N, K,
-                                   args.steps, args.warmup)
-    launch16 = launches16 + launches16b
-    k16 = sum(launch16) / len(launch16)
-    k1 = sum(launches1) / len(launches1)
-    pk16 = sum(plaunch16) / len(plaunch16)
-    pk1 = sum(plaunch1) / len(plaunch1)
+    # timed steps: tiled M = 16 (the step), then M = 1, then M = 16 again
+    # (A-B-A order for the ratio); then the planar kernel at M = 16 and 1
+    ms16a, wall16 = time_calls(torch, tiled, x16, Wts, y16, Mv, N, K,
+                               args.steps, args.warmup)
+    ms1, wall1 = time_calls(torch, tiled, x1, Wts, y1, 1, N, K, args.steps,
+                            args.warmup)
+    ms16b, _ = time_calls(torch, tiled, x16, Wts, y16, Mv, N, K, args.steps,
+                          args.warmup)
+    pms16, _ = time_calls(torch, planar, x16, Ws, y16, Mv, N, K, args.steps,
+                          args.warmup)
+    pms1, _ = time_calls(torch, planar, x1, Ws, y1, 1, N, K, args.steps,
+                         args.warmup)
     ms_per_step = ms16a
+    k16 = 0.5 * (ms16a + ms16b)
     gbps16 = b16 / (ms_per_step * 1e-3) / 1e9
     gbps1 = b1 / (ms1 * 1e-3) / 1e9
     ach16 = b16 / (k16 * 1e-3) / 1e9
     plan = q4.q4_gemm_verify_plan(Mv, N, K, q4.LAYOUT_TILED16)
     traffic = load_traffic(Mv, N, K)
-    log(f"tiled M=16: {ms_per_step * 1e3:.2f} us/step ({gbps16:.0f} GB/s), "
-        f"kernel {k16 * 1e3:.2f} us ({ach16:.0f} GB/s); M=1: {ms1 * 1e3:.2f} "
-        f"us/step ({gbps1:.0f} GB/s), kernel {k1 * 1e3:.2f} us")
-    log(f"planar M=16: kernel {pk16 * 1e3:.2f} us "
-        f"({b16 / (pk16 * 1e-3) / 1e9:.0f} GB/s); M=1: kernel "
-        f"{pk1 * 1e3:.2f} us ({b1 / (pk1 * 1e-3) / 1e9:.0f} GB/s)")
+    log(f"tiled M=16: {ms16a * 1e3:.2f} / {ms16b * 1e3:.2f} us per call "
+        f"({gbps16:.0f} GB/s); M=1: {ms1 * 1e3:.2f} us ({gbps1:.0f} GB/s)")
+    log(f"planar M=16: {pms16 * 1e3:.2f} us ({b16 / (pms16 * 1e-3) / 1e9:.0f}"
+        f" GB/s); M=1: {pms1 * 1e3:.2f} us "
+        f"({b1 / (pms1 * 1e-3) / 1e9:.0f} GB/s)")
 
     probe = None
     if not args.no_probe:
@@ -313,17 +305,13 @@ def main():
                    "parallelism": "single GPU", "plan": plan},
         "frac_of_peak": round(gbps16 / HBM_PEAK_GBPS, 4),
         "m1": {"ms_per_step": round(ms1, 6), "gbps": round(gbps1, 1),
-               "frac_of_peak": round(gbps1 / HBM_PEAK_GBPS, 4),
-               "kernel_us": round(k1 * 1e3, 3)},
-        "ratio_m16_m1": round(ms_per_step / ms1, 4),
-        "ratio_m16_m1_kernel": round(k16 / k1, 4),
+               "frac_of_peak": round(gbps1 / HBM_PEAK_GBPS, 4)},
+        "ratio_m16_m1": round(k16 / ms1, 4),
         "repack": repack,
-        "planar": {"kernel_us_m16": round(pk16 * 1e3, 3),
-                   "gbps_m16": round(b16 / (pk16 * 1e-3) / 1e9, 1),
-                   "kernel_us_m1": round(pk1 * 1e3, 3),
-                   "gbps_m1": round(b1 / (pk1 * 1e-3) / 1e9, 1),
-                   "ms_per_step_m16": round(pms16, 6),
-                   "ms_per_step_m1": round(pms1, 6)},
+        "planar": {"ms_per_step_m16": round(pms16, 6),
+                   "gbps_m16": round(b16 / (pms16 * 1e-3) / 1e9, 1),
+                   "ms_per_step_m1": round(pms1, 6),
+                   "gbps_m1": round(b1 / (pms1 * 1e-3) / 1e9, 1)},
         "wall_ms_per_step": round(wall16, 6),
         "stream_read_gbps": None if probe is None else round(probe, 1),
         "frac_of_stream_read": None if probe is None else
@@ -337,6 +325,8 @@ def main():
             "traffic": traffic,
             "kernel": "gemm_tiled_kernel",
             "kernel_us": round(k16 * 1e3, 3),
+            "timing": "HIP events around back-to-back launches on the "
+                      "launch stream, mean of the two M=16 blocks",
             "alg_bytes_per_launch": b16,
         },
         "cpu_baseline": cpu,
