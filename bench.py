@@ -55,6 +55,8 @@ WORKLOADS = {
 }
 KERNEL_SOURCE = os.path.join(ROOT, "speculative_verify_gemm_q4_amd", "csrc",
                              "q4verify_kernels.hip")
+KERNEL_NAMES = {0: "gemm_verify_kernel", 1: "gemm_tiled_kernel",
+                2: "gemm_resident_kernel"}
 COUNTERS = os.path.join(ROOT, "profiles",
                         "q4_gemm_gate_up_34816x5120_counters.txt")
 
@@ -323,7 +325,7 @@ def main():
             "unit": "GB/s",
             "frac": round(ach16 / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": "gemm_tiled_kernel",
+            "kernel": KERNEL_NAMES[plan["kernel"]],
             "kernel_us": round(k16 * 1e3, 3),
             "timing": "HIP events around back-to-back launches on the "
                       "launch stream, mean of the two M=16 blocks",

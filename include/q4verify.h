@@ -151,6 +151,9 @@ int q4_repack(const void *W_planar, void *W_tiled, int64_t N, int64_t K,
  * Q4_LAYOUT_TILED16 (same x, y, M and results within the same bound; every
  * row's result is independent of M).  Each wave streams whole records with
  * 16-byte loads, so every weight byte is fetched once in full cache lines.
+ * For K <= 5120 the activations are first copied once per workgroup into
+ * LDS (Q4_KERNEL_TILED_RESIDENT); larger K loads them per record
+ * (Q4_KERNEL_TILED_STREAM).  q4_gemm_verify_plan reports which.
  *   x, y, M, stream: as q4_gemm_verify.
  *   W_tiled : device, Q4_LAYOUT_TILED16 of an N x K matrix, 16-byte aligned.
  *   N % 16 == 0, K % 256 == 0, K <= 2^26 (else Q4_EINVAL).
@@ -201,7 +204,16 @@ typedef struct {
                             range of K; partial sums are added in split
                             order inside the workgroup                     */
   uint32_t lookahead;    /* groups whose loads are issued ahead of use      */
+  uint32_t kernel;       /* Q4_KERNEL_* below                               */
+  uint32_t lds_bytes;    /* LDS per workgroup                               */
 } q4_plan;
+
+#define Q4_KERNEL_PLANAR 0u          /* q4_gemm_verify                       */
+#define Q4_KERNEL_TILED_STREAM 1u    /* tiled; activations loaded per record */
+#define Q4_KERNEL_TILED_RESIDENT 2u  /* tiled; activations resident in LDS;
+                                        grid = one workgroup per CU (at most
+                                        N/16), each owning whole 16-row tiles
+                                        split evenly across its waves        */
 
 /*
  * q4_gemm_verify_plan -- the plan q4_gemm_verify (layout_id

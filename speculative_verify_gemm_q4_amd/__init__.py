@@ -17,13 +17,15 @@ Functions (same names as the C entry points):
 * :func:`q4_stream_read`, :func:`q4_stream_copy` -- bandwidth probes.
 * :func:`q4_status_string` -- name of a status code.
 """
-from ._lib import (GROUP, LAYOUT_PLANAR, LAYOUT_TILED16, MAX_ROWS, Q4Error,
+from ._lib import (GROUP, KERNEL_PLANAR, KERNEL_TILED_RESIDENT,
+                   KERNEL_TILED_STREAM, LAYOUT_PLANAR, LAYOUT_TILED16, MAX_ROWS, Q4Error,
                    LIB_PATH, lib_exports, load, q4_dequant, q4_gemm_verify,
                    q4_gemm_verify_plan, q4_gemm_verify_tiled, q4_pack_layout,
                    q4_repack, q4_status_string, q4_stream_copy,
                    q4_stream_read)
 
-__all__ = ["GROUP", "LAYOUT_PLANAR", "LAYOUT_TILED16", "MAX_ROWS", "Q4Error",
+__all__ = ["GROUP", "KERNEL_PLANAR", "KERNEL_TILED_RESIDENT",
+           "KERNEL_TILED_STREAM", "LAYOUT_PLANAR", "LAYOUT_TILED16", "MAX_ROWS", "Q4Error",
            "LIB_PATH", "lib_exports", "load", "q4_dequant", "q4_gemm_verify",
            "q4_gemm_verify_plan", "q4_gemm_verify_tiled", "q4_pack_layout",
            "q4_repack", "q4_status_string", "q4_stream_copy",

@@ -11,6 +11,9 @@ GROUP = 64
 MAX_ROWS = 16
 LAYOUT_PLANAR = 0
 LAYOUT_TILED16 = 1
+KERNEL_PLANAR = 0
+KERNEL_TILED_STREAM = 1
+KERNEL_TILED_RESIDENT = 2
 
 OK, EINVAL, EALIGN, EOVERFLOW, EDEVICE, ELAUNCH = 0, -1, -2, -3, -4, -5
 
@@ -42,7 +45,8 @@ class _Plan(ctypes.Structure):
     _fields_ = [("grid", ctypes.c_uint32), ("block", ctypes.c_uint32),
                 ("row_tiles", ctypes.c_uint32),
                 ("tiles_per_wave", ctypes.c_uint32),
-                ("k_splits", ctypes.c_uint32), ("lookahead", ctypes.c_uint32)]
+                ("k_splits", ctypes.c_uint32), ("lookahead", ctypes.c_uint32),
+                ("kernel", ctypes.c_uint32), ("lds_bytes", ctypes.c_uint32)]
 
 
 _lib = None

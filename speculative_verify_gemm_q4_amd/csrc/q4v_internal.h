@@ -21,16 +21,29 @@ int check_tiled_shape(int64_t N, int64_t K);
 
 // Launch plans of the two GEMM kernels (see q4_gemm_verify_plan); the shape
 // has already been checked.
+// `cus` is the compute-unit count of the device the plan is for.
 q4_plan plan_gemm_planar(int M, int64_t N, int64_t K);
-q4_plan plan_gemm_tiled(int M, int64_t N, int64_t K);
+q4_plan plan_gemm_tiled(int M, int64_t N, int64_t K, int cus);
 
 // Bytes of one record of the tiled layout: 16 rows x 4 groups x 36 bytes.
 constexpr int kTileRows = 16;
 constexpr int kRecordGroups = 4;
 constexpr int kRecordBytes = kTileRows * kRecordGroups * 36;
 
+// LDS of one gfx950 CU (and the most one workgroup may use), and the largest
+// K whose 16 activation rows fit in it as bf16.
+constexpr int kLdsBytes = 163840;
+constexpr int kResidentMaxK = kLdsBytes / 32;
+// Waves per workgroup and register stages of the resident-activation kernel.
+constexpr int kResidentWaves = 8;
+constexpr int kResidentStages = 2;
+
 // Q4_OK when a HIP device is current and it is a gfx950; Q4_EDEVICE
 // otherwise.  The answer is cached per device ordinal.
 int check_device();
+
+// Compute units of the current device (cached per ordinal); 256, the
+// MI355X's count, when no device can be queried.
+int device_cus();
 
 }  // namespace q4v

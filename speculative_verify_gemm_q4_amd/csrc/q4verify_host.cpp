@@ -106,11 +106,30 @@ q4_plan plan_gemm_planar(int M, int64_t N, int64_t K) {
   p.block = static_cast<uint32_t>(64 * ntw * ksw);
   p.grid = static_cast<uint32_t>((tiles + ntw - 1) / ntw);
   p.lookahead = 4;
+  p.kernel = Q4_KERNEL_PLANAR;
+  p.lds_bytes = ksw > 1 ? static_cast<uint32_t>(ksw * ntw * 64 * 16) : 0;
   return p;
 }
 
-q4_plan plan_gemm_tiled(int M, int64_t N, int64_t K) {
+q4_plan plan_gemm_tiled(int M, int64_t N, int64_t K, int cus) {
   (void)M;
+  const int64_t tiles = N / kTileRows;
+  if (K <= kResidentMaxK) {
+    // Activations resident in LDS: one workgroup per CU (the LDS admits no
+    // second), each owning whole tiles; its waves split its records evenly.
+    q4_plan p;
+    std::memset(&p, 0, sizeof p);
+    const int64_t g = tiles < cus ? tiles : cus;
+    p.grid = static_cast<uint32_t>(g);
+    p.block = 64 * kResidentWaves;
+    p.row_tiles = static_cast<uint32_t>((tiles + g - 1) / g);
+    p.tiles_per_wave = 1;
+    p.k_splits = 1;
+    p.lookahead = kRecordGroups * (kResidentStages - 1);
+    p.kernel = Q4_KERNEL_TILED_RESIDENT;
+    p.lds_bytes = kLdsBytes;
+    return p;
+  }
   // Tiles per wave: each wave multiplies its activation operand with 1-4
   // tiles, so the activation loads per weight byte fall with more tiles
   // while the registers per wave (and so the waves per SIMD) rise; wide
@@ -118,7 +137,6 @@ q4_plan plan_gemm_tiled(int M, int64_t N, int64_t K) {
   // then added until about 1024 waves stream at once, keeping at least one
   // 4-group record per wave.  Both rules follow measured sweeps on MI355X of
   // the 27B model's projection shapes.
-  const int64_t tiles = N / kTileRows;
   const int64_t records = K / (kRecordGroups * Q4_GROUP);
   const int tnt = tiles >= 4096 ? 4 : tiles >= 1536 ? 3 : tiles >= 2 ? 2 : 1;
   const int64_t sets = (tiles + tnt - 1) / tnt;
@@ -132,6 +150,8 @@ q4_plan plan_gemm_tiled(int M, int64_t N, int64_t K) {
   p.block = static_cast<uint32_t>(64 * ksw);
   p.grid = static_cast<uint32_t>(sets);
   p.lookahead = kRecordGroups;
+  p.kernel = Q4_KERNEL_TILED_STREAM;
+  p.lds_bytes = ksw > 1 ? static_cast<uint32_t>(ksw * tnt * 64 * 16) : 0;
   return p;
 }
 
@@ -154,6 +174,28 @@ int check_device() {
     verdict[dev].store(v, std::memory_order_relaxed);
   }
   return v == 1 ? Q4_OK : Q4_EDEVICE;
+}
+
+int device_cus() {
+  static std::atomic<int> cached[256];  // 0 unknown
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+            hipSuccess ||
+        n < 1) {
+      (void)hipGetLastError();
+      return 256;
+    }
+    v = n;
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
 }
 
 }  // namespace q4v
@@ -214,7 +256,7 @@ extern "C" int q4_gemm_verify_plan(int M, int64_t N, int64_t K,
   if (layout_id == Q4_LAYOUT_TILED16) {
     const int st = q4v::check_tiled_shape(N, K);
     if (st != Q4_OK) return st;
-    *out = q4v::plan_gemm_tiled(M, N, K);
+    *out = q4v::plan_gemm_tiled(M, N, K, q4v::device_cus());
     return Q4_OK;
   }
   return Q4_EINVAL;

@@ -354,6 +354,175 @@ __global__ __launch_bounds__(64 * NTW * KSW) void gemm_tiled_kernel(
   }
 }
 
+// The same product with the activations resident in LDS, for K <= 5120
+// (16 rows x K bf16 fit the 160 KB of a CU).  One workgroup per CU:
+//  * it copies x once into LDS, laid out as MFMA operands -- fragment
+//    (q, gi, h) is 1 KB holding lane l's eight inputs 256q + 64gi + 16kb +
+//    8h .. +7 of row j -- with direct-to-LDS buffer loads (lane l lands at
+//    fragment + 16 l; rows >= M fall past the resource and arrive as zeros);
+//  * it owns whole tiles [t0, t1), i.e. U = (t1 - t0) * Q records in
+//    tile-major order, and gives each of its W waves a contiguous range of
+//    them, so every wave streams the same number of records (+-1) and no
+//    wave reloads activation operands from the memory hierarchy;
+//  * a tile that lies wholly inside one wave's range is written by that wave
+//    as soon as its last record is done; a tile split between waves is
+//    reduced after the loop through LDS, in wave order, by the wave holding
+//    the tile's first record.  The summation order is fixed by (N, K), so
+//    results do not depend on M or on timing.
+// Weight records go through S register stages: the loads of record i + S - 1
+// are issued before record i is multiplied.
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int W, int S>
+__global__ __launch_bounds__(64 * W) void gemm_resident_kernel(
+    const uint16_t *__restrict__ x, const uint8_t *__restrict__ Wt,
+    float *__restrict__ y, int M, int N, int K, int G) {
+  __shared__ u32x4 lds[kLdsBytes / 16];
+  const int T = N >> 4;
+  const int Q = K >> 8;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 15;
+  const int kb = lane >> 4;
+  const int t0 = static_cast<int>(static_cast<int64_t>(T) * blockIdx.x / G);
+  const int t1 = static_cast<int>(static_cast<int64_t>(T) * (blockIdx.x + 1) / G);
+  const int U = (t1 - t0) * Q;
+  const int u0 = static_cast<int>(static_cast<int64_t>(U) * wave / W);
+  const int u1 = static_cast<int>(static_cast<int64_t>(U) * (wave + 1) / W);
+
+  // activations -> LDS, fragment f = 8q + 2gi + h handled by wave f % W
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(x), 0,
+      static_cast<int>(static_cast<uint32_t>(M) * static_cast<uint32_t>(K) * 2u),
+      kBufferWord3);
+  const uint32_t xlane = (static_cast<uint32_t>(j) * K + 16 * kb) * 2;
+  for (int f = wave; f < 8 * Q; f += W) {
+    const int q = f >> 3, gi = (f >> 1) & 3, h = f & 1;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        xr, (lds_void *)&lds[f * 64], 16, xlane + 16 * h,  // address-space cast
+        static_cast<uint32_t>(256 * q + 64 * gi) * 2, 0, 0);
+  }
+
+  // this wave's records only: loads past its range return zeros
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(Wt + (static_cast<uint64_t>(t0) * Q + u0) * kRecordBytes),
+      0, (u1 - u0) * kRecordBytes, kBufferWord3);
+  struct Stage {
+    u32x4 c0, c1, sb;
+  };
+  auto load = [&](int i, Stage &st) {  // record u0 + i
+    const uint32_t o = static_cast<uint32_t>(i) * kRecordBytes;
+    st.c0 = buffer_load16<kNonTemporal>(wr, lane * 16, o);
+    st.c1 = buffer_load16<kNonTemporal>(wr, 1024 + lane * 16, o);
+    st.sb = buffer_load16<kNonTemporal>(wr, 2048 + j * 16, o);
+  };
+  Stage st[S];
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i) load(i, st[i]);
+  // Every outstanding vector memory operation, this wave's activation copies
+  // included, must be complete before the barrier: direct-to-LDS loads need
+  // not complete in order with the weight loads issued after them (a weight
+  // load past the wave's range returns at once), so no partial count would
+  // prove the copies done.  The first weight stage is needed next anyway.
+  __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));  // vmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  const u32x4 neg = {kNeg128Pair, kNeg128Pair, kNeg128Pair, kNeg128Pair};
+  const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
+  const UnpackConsts uc = unpack_consts();
+  auto compute = [&](const Stage &s, int q, f32x4 &acc) {
+    const u32x4 *xf = lds + q * 512 + lane;
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      const u32x4 a0 = xf[(2 * gi) * 64];
+      const u32x4 a1 = xf[(2 * gi + 1) * 64];
+      f32x4 xn = mfma16x16x32(a0, neg, fzero);
+      xn = mfma16x16x32(a1, neg, xn);
+      const u32x4 cw = gi < 2 ? s.c0 : s.c1;
+      const uint32_t w0 = (gi & 1) ? cw.z : cw.x;
+      const uint32_t w1 = (gi & 1) ? cw.w : cw.y;
+      f32x4 tq = mfma16x16x32(a0, unpack_codes(w0, uc), xn);
+      tq = mfma16x16x32(a1, unpack_codes(w1, uc), tq);
+      const uint32_t sbw = s.sb[gi];
+      const float sc = __uint_as_float(sbw << 16);
+      const float bn = __uint_as_float(sbw & 0xFFFF0000u) * kMinusInv128;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        acc[r] = __builtin_fmaf(bn, xn[r], acc[r]);
+        acc[r] = __builtin_fmaf(sc, tq[r], acc[r]);
+      }
+    }
+  };
+  auto store = [&](int tile, const f32x4 &v) {
+    const int n = tile * 16 + j;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = kb * 4 + r;
+      if (m < M) y[static_cast<uint64_t>(m) * N + n] = v[r];
+    }
+  };
+
+  // head: partial sum of a first tile entered past its first record;
+  // tail: partial sum of a last tile left before its last record
+  f32x4 acc = fzero, head_sum = fzero, tail_sum = fzero;
+  int q = u0 % Q;
+  int tl = u0 / Q;
+  bool in_head = q != 0;
+  const int nrec = u1 - u0;
+  for (int i0 = 0; i0 < nrec; i0 += S) {
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      load(i0 + i + S - 1, st[(i + S - 1) % S]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i0 + i < nrec) {
+        compute(st[i], q, acc);
+        if (++q == Q) {
+          if (in_head) {
+            head_sum = acc;
+            in_head = false;
+          } else {
+            store(t0 + tl, acc);
+          }
+          acc = fzero;
+          q = 0;
+          ++tl;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if (q != 0) {
+    if (in_head)
+      head_sum = acc;
+    else
+      tail_sum = acc;
+  }
+
+  // split tiles: the activations are no longer needed, so their LDS holds
+  // each wave's two partial sums
+  __syncthreads();
+  f32x4 *part = reinterpret_cast<f32x4 *>(lds);
+  part[(wave * 2 + 0) * 64 + lane] = head_sum;
+  part[(wave * 2 + 1) * 64 + lane] = tail_sum;
+  __syncthreads();
+  if (u1 > u0) {
+    const int lt = (u1 - 1) / Q;
+    if (lt * Q >= u0 && lt * Q + Q > u1) {
+      // this wave holds lt's first record but not its last: its share is
+      // its tail sum, the following waves' shares their head sums
+      f32x4 v = part[(wave * 2 + 1) * 64 + lane];
+      for (int w2 = wave + 1; w2 < W; ++w2) {
+        const int a0 = static_cast<int>(static_cast<int64_t>(U) * w2 / W);
+        const int a1 = static_cast<int>(static_cast<int64_t>(U) * (w2 + 1) / W);
+        if (a0 >= lt * Q + Q) break;
+        if (a1 > a0) v += part[(w2 * 2) * 64 + lane];
+      }
+      store(t0 + lt, v);
+    }
+  }
+}
+
 // Code word q0..q7 (nibble i = input i) -> nibbles q0 q2 q4 q6 q1 q3 q5 q7,
 // so that unpack_codes yields the pairs (q0,q1) (q2,q3) (q4,q5) (q6,q7):
 // consecutive inputs, the order of the activations in memory.
@@ -491,6 +660,16 @@ int launch_tiled(const q4_plan &p, const void *x, const void *W, float *y,
   return launch_status();
 }
 
+int launch_resident(const q4_plan &p, const void *x, const void *W, float *y,
+                    int M, int N, int K, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_resident_kernel<kResidentWaves, kResidentStages>),
+                     dim3(p.grid), dim3(p.block), 0, stream,
+                     static_cast<const uint16_t *>(x),
+                     static_cast<const uint8_t *>(W), y, M, N, K,
+                     static_cast<int>(p.grid));
+  return launch_status();
+}
+
 template <int NTW, int KSW>
 int launch_gemm(const q4_plan &p, const void *x, const void *W, float *y,
                 int M, int N, int K, hipStream_t stream) {
@@ -533,7 +712,9 @@ extern "C" int q4_gemm_verify_tiled(const void *x, const void *W, float *y,
   if (st != Q4_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int n = static_cast<int>(N), k = static_cast<int>(K);
-  const q4_plan p = q4v::plan_gemm_tiled(M, N, K);
+  const q4_plan p = q4v::plan_gemm_tiled(M, N, K, q4v::device_cus());
+  if (p.kernel == Q4_KERNEL_TILED_RESIDENT)
+    return q4v::launch_resident(p, x, W, y, M, n, k, s);
   const int key = static_cast<int>(p.tiles_per_wave * 100 + p.k_splits);
   switch (key) {
 #define Q4V_TILED_CASE(TNT, KSW) \

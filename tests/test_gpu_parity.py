@@ -287,6 +287,35 @@ def test_tiled_tiny(q4, M):
     oracle_check(q4, M, 256, 512, 0, "tiled tiny", tiled=True)
 
 
+def test_resident_empty_waves_after_other_lds_users(q4):
+    """Resident-activation kernel on shapes where most of a workgroup's waves
+    get no records (their weight loads all fall past their range and return
+    at once), each call preceded by kernels that leave other data in LDS: no
+    wave may start before every activation copy has landed."""
+    dev = torch.device("cuda")
+    Wp = synth.q4_weights(2048, 4096, seed=40, device=dev)
+    Wtp = repacked(q4, Wp, 2048, 4096)
+    xp = synth.activations(16, 4096, seed=40, stream=1, device=dev)
+    yp = torch.empty((16, 2048), dtype=torch.float32, device=dev)
+    for N, K in [(16, 256), (16, 512), (48, 256), (256, 512), (32, 5120)]:
+        p = q4.q4_gemm_verify_plan(16, N, K, q4.LAYOUT_TILED16)
+        assert p["kernel"] == q4.KERNEL_TILED_RESIDENT
+        W = synth.q4_weights(N, K, seed=41, device=dev)
+        Wt = repacked(q4, W, N, K)
+        for M in (1, 4, 16):
+            x = synth.activations(M, K, seed=41 + M, stream=1, device=dev)
+            _, y64, a64, _ = oracle.gemm(synth.bf16_bits(x), W.cpu().numpy(),
+                                         N, K)
+            for rep in range(3):
+                # both other kernels leave their own data in LDS
+                q4.q4_gemm_verify(xp, Wp, yp, 16, 2048, 4096)
+                q4.q4_gemm_verify_tiled(xp, Wtp, yp, 16, 2048, 4096)
+                _say(f"case resident empty waves: N={N} K={K} M={M} rep={rep}")
+                y = gemm_tiled(q4, x, Wt, M, N, K)
+                assert_within_bound(y, y64, a64,
+                                    f"resident N={N} K={K} M={M} rep={rep}")
+
+
 @pytest.mark.parametrize("M,N,K", TILED)
 def test_tiled_shapes(q4, M, N, K):
     """Shapes covering every launch configuration of the tiled kernel."""

@@ -128,6 +128,9 @@ TILED_SHAPES = [(16, 16, 256), (16, 256, 512), (5, 1600, 1024),
 @pytest.mark.parametrize("M,N,K", TILED_SHAPES)
 def test_tiled_plan_reads_every_record_once(M, N, K):
     p = q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_TILED16)
+    if p["kernel"] == q4.KERNEL_TILED_RESIDENT:
+        return resident_model(M, N, K, p)
+    assert p["kernel"] == q4.KERNEL_TILED_STREAM and K > 5120
     tnt, ksw, grid, block = (p["tiles_per_wave"], p["k_splits"], p["grid"],
                              p["block"])
     ntw = p["row_tiles"] // tnt
@@ -170,3 +173,124 @@ def test_tiled_plan_reads_every_record_once(M, N, K):
                 if m < M:
                     out[m, tile * 16: tile * 16 + 16] += 1
     assert np.all(out == 1)
+
+
+# --------------------------------------------------------------------------
+# resident-activation kernel (K <= 5120): workgroup b owns tiles
+# [T b / G, T (b+1) / G); its U = tiles * Q records (tile-major) are split
+# into W contiguous ranges [U w / W, U (w+1) / W).  A tile inside one range is
+# written by that wave; a split tile by the wave holding its first record,
+# which adds its tail sum and then the head sums of the following waves whose
+# ranges start inside the tile.  Activations: fragment f = 8q + 2gi + h at
+# LDS byte 1024 f, lane l at +16 l; partial sums reuse LDS bytes [0, 2 W KB).
+
+LDS_BYTES = 163840
+
+
+def resident_model(M, N, K, p):
+    T, Q = N // 16, K // 256
+    G, W = p["grid"], p["block"] // 64
+    assert p["lds_bytes"] == LDS_BYTES and p["block"] <= 1024
+    assert G == min(T, 256) and p["row_tiles"] == -(-T // G)
+    assert 8 * Q * 1024 <= LDS_BYTES and 2 * W * 1024 <= LDS_BYTES
+    hits = np.zeros(T * Q, dtype=np.int32)
+    writes = np.zeros(T, dtype=np.int32)
+    # record r of a tile belongs to exactly one wave, and the summation of a
+    # split tile visits exactly the waves holding its records, each once
+    for b in range(G):
+        t0, t1 = T * b // G, T * (b + 1) // G
+        U = (t1 - t0) * Q
+        rng = [(U * w // W, U * (w + 1) // W) for w in range(W)]
+        owner_of = {}
+        for w, (u0, u1) in enumerate(rng):
+            if u1 > u0:
+                hits[t0 * Q + u0: t0 * Q + u1] += 1
+                # the wave's resource: records [t0 Q + u0, t0 Q + u1)
+                assert (t0 * Q + u1) * 2304 <= T * Q * 2304
+                assert (u1 - u0) * 2304 < 2 ** 31
+            # tiles completed inside the range are stored by the wave
+            q, tl, head = u0 % Q, u0 // Q, u0 % Q != 0
+            for _ in range(u1 - u0):
+                q += 1
+                if q == Q:
+                    if not head:
+                        writes[t0 + tl] += 1
+                    head, q, tl = False, 0, tl + 1
+            if u1 > u0:
+                lt = (u1 - 1) // Q
+                if lt * Q >= u0 and lt * Q + Q > u1:
+                    owner_of[lt] = w
+        for lt, w in owner_of.items():
+            got = [(w, "tail")]
+            for w2 in range(w + 1, W):
+                a0, a1 = rng[w2]
+                if a0 >= lt * Q + Q:
+                    break
+                if a1 > a0:
+                    got.append((w2, "head"))
+            # the waves whose ranges meet tile lt
+            want = [w2 for w2, (a0, a1) in enumerate(rng)
+                    if a1 > a0 and a0 < lt * Q + Q and a1 > lt * Q]
+            assert [g[0] for g in got] == want
+            # the owner's share starts at the tile's first record and stops
+            # inside it (its tail sum); each follower starts inside the tile
+            u0, u1 = rng[w]
+            assert u0 <= lt * Q < u1 < lt * Q + Q
+            for w2, _ in got[1:]:
+                assert lt * Q < rng[w2][0] < lt * Q + Q
+            writes[t0 + lt] += 1
+    assert np.all(hits == 1)
+    assert np.all(writes == 1)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 256), (16, 16, 5120),
+                                   (16, 48, 256), (7, 4096, 1024),
+                                   (16, 4112, 5120), (1, 6000 * 16, 768),
+                                   (16, 34816, 5120)])
+def test_resident_plan_more_shapes(M, N, K):
+    p = q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_TILED16)
+    assert p["kernel"] == q4.KERNEL_TILED_RESIDENT
+    resident_model(M, N, K, p)
+
+
+def test_resident_split_tile_sums_in_wave_order():
+    # a workgroup of 8 waves over 3 tiles of 20 records: 60 records, 7 or 8
+    # per wave, so tiles are split; check by direct simulation with exact
+    # dyadic numbers that the owner's sum equals the plain sum of the tile
+    W, Q, tiles = 8, 20, 3
+    U = tiles * Q
+    rng = [(U * w // W, U * (w + 1) // W) for w in range(W)]
+    contrib = np.arange(U, dtype=np.float64) + 1.0  # record u adds u + 1
+    head = np.zeros(W)
+    tail = np.zeros(W)
+    out = np.full(tiles, np.nan)
+    for w, (u0, u1) in enumerate(rng):
+        acc, q, tl, in_head = 0.0, u0 % Q, u0 // Q, u0 % Q != 0
+        for u in range(u0, u1):
+            acc += contrib[u]
+            q += 1
+            if q == Q:
+                if in_head:
+                    head[w] = acc
+                    in_head = False
+                else:
+                    out[tl] = acc
+                acc, q, tl = 0.0, 0, tl + 1
+        if q != 0:
+            if in_head:
+                head[w] = acc
+            else:
+                tail[w] = acc
+    for w, (u0, u1) in enumerate(rng):
+        lt = (u1 - 1) // Q
+        if lt * Q >= u0 and lt * Q + Q > u1:
+            v = tail[w]
+            for w2 in range(w + 1, W):
+                a0, a1 = rng[w2]
+                if a0 >= lt * Q + Q:
+                    break
+                if a1 > a0:
+                    v += head[w2]
+            out[lt] = v
+    want = contrib.reshape(tiles, Q).sum(axis=1)
+    assert np.array_equal(out, want)
