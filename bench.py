@@ -176,6 +176,151 @@ def cpu_baseline(torch, W, x16, N, K, budget_s):
             "s_per_call": round(dt / runs, 4), "rows": rows}
 
 
+def rotated_tiled(torch, synth, q4, N, K, rotate_gb, stream0, dev):
+    """Distinct tiled copies of an N x K matrix, >= rotate_gb in total (at
+    least two), each generated planar and repacked."""
+    wbytes = 9 * N * K // 16
+    copies = max(2, math.ceil(rotate_gb * 1e9 / wbytes))
+    out = []
+    for i in range(copies):
+        W = synth.q4_weights(N, K, seed=0, stream=stream0 + i, device=dev)
+        Wt = torch.empty_like(W)
+        q4.q4_repack(W, Wt, N, K)
+        out.append(Wt)
+        del W
+    torch.cuda.synchronize()
+    return out
+
+
+def measure_shapes(torch, synth, q4, names, steps, warmup, rotate_gb, dev):
+    """Every projection shape of the 27B pass at M = 16 and M = 1 (order
+    16, 1, 16), each over its own rotated copies."""
+    res = {}
+    for i, name in enumerate(names):
+        N, K = WORKLOADS[name]
+        Wts = rotated_tiled(torch, synth, q4, N, K, rotate_gb, 1000 * (i + 1),
+                            dev)
+        x16 = synth.activations(16, K, seed=0, stream=100 + i, device=dev)
+        x1 = x16[:1].contiguous()
+        y16 = torch.empty((16, N), dtype=torch.float32, device=dev)
+        y1 = torch.empty((1, N), dtype=torch.float32, device=dev)
+        call = q4.q4_gemm_verify_tiled
+        n = max(10, min(steps, int(20e3 / (9 * N * K / 16 / 5e6))))
+        a, _ = time_calls(torch, call, x16, Wts, y16, 16, N, K, n, warmup)
+        b, _ = time_calls(torch, call, x1, Wts, y1, 1, N, K, n, warmup)
+        c, _ = time_calls(torch, call, x16, Wts, y16, 16, N, K, n, warmup)
+        m16 = 0.5 * (a + c)
+        plan = q4.q4_gemm_verify_plan(16, N, K, q4.LAYOUT_TILED16)
+        rec = {"N": N, "K": K, "weight_bytes": 9 * N * K // 16,
+               "copies": len(Wts), "steps": n,
+               "kernel": KERNEL_NAMES[plan["kernel"]],
+               "us_m1": round(b * 1e3, 3), "us_m16": round(m16 * 1e3, 3),
+               "gbps_m1": round(alg_bytes(1, N, K) / (b * 1e-3) / 1e9, 1),
+               "gbps_m16": round(alg_bytes(16, N, K) / (m16 * 1e-3) / 1e9, 1),
+               "ratio_m16_m1": round(m16 / b, 4)}
+        rec["frac_m1"] = round(rec["gbps_m1"] / HBM_PEAK_GBPS, 4)
+        rec["frac_m16"] = round(rec["gbps_m16"] / HBM_PEAK_GBPS, 4)
+        log(f"shape {name}: {rec}")
+        res[name] = rec
+        del Wts, x16, x1, y16, y1
+        torch.cuda.empty_cache()
+    return res
+
+
+# The 27B model's projection list: 16 attention and 48 gated-DeltaNet layers,
+# each with its input and output projection and the MLP (gate+up, down), and
+# the LM head called twice (draft readout, then verify) on the same weights.
+def pass_calls():
+    calls = []
+    for layer in range(64):
+        attn = layer % 4 == 3            # 16 of 64 layers are attention
+        calls.append(("attn_in" if attn else "gdn_in", layer))
+        calls.append(("o_proj", layer))
+        calls.append(("gate_up", layer))
+        calls.append(("down", layer))
+    calls.append(("lm_head", 0))
+    calls.append(("lm_head", 0))
+    return calls
+
+
+def measure_full_pass(torch, synth, q4, reps, dev):
+    """One 64-layer pass of every projection (distinct weights per layer),
+    captured once per M as a HIP graph and replayed; activations are not
+    chained between calls (only the projections are on the path)."""
+    calls = pass_calls()
+    weights = {}
+    for name, layer in calls:
+        if (name, layer) in weights:
+            continue
+        N, K = WORKLOADS[name]
+        W = synth.q4_weights(N, K, seed=0, stream=50000 + 16 * layer +
+                             sorted(WORKLOADS).index(name), device=dev)
+        Wt = torch.empty_like(W)
+        q4.q4_repack(W, Wt, N, K)
+        weights[(name, layer)] = Wt
+        del W
+    torch.cuda.synchronize()
+    wbytes = sum(9 * WORKLOADS[n][0] * WORKLOADS[n][1] // 16 for n, _ in calls)
+    xs = {K: synth.activations(16, K, seed=0, stream=200 + K, device=dev)
+          for K in {k for _, k in WORKLOADS.values()}}
+    ys = {n: torch.empty((16, N), dtype=torch.float32, device=dev)
+          for n, (N, _) in WORKLOADS.items()}
+    out = {"calls": len(calls), "weight_bytes": wbytes,
+           "graph": "one HIP graph per M, replayed back to back"}
+    graphs = {}
+    for M in (16, 1):
+        x_m = {K: v[:M].contiguous() for K, v in xs.items()}
+
+        def run_pass(M=M, x_m=x_m):
+            for name, layer in calls:
+                N, K = WORKLOADS[name]
+                q4.q4_gemm_verify_tiled(x_m[K], weights[(name, layer)],
+                                        ys[name][:M], M, N, K)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run_pass()                  # warm-up outside the capture
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run_pass()
+        torch.cuda.synchronize()
+        graphs[M] = (g, run_pass)
+
+    def timed(fn, n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    for M in (16, 1, 16):
+        g, run_pass = graphs[M]
+        ms = timed(g.replay, reps)
+        key = f"M={M}"
+        b = sum(alg_bytes(M, *WORKLOADS[n]) for n, _ in calls)
+        rec = out.setdefault(key, {"alg_bytes": b, "ms": []})
+        rec["ms"].append(ms)
+    for M in (16, 1):
+        rec = out[f"M={M}"]
+        ms = sum(rec["ms"]) / len(rec["ms"])
+        rec["ms"] = round(ms, 4)
+        rec["gbps"] = round(rec["alg_bytes"] / (ms * 1e-3) / 1e9, 1)
+        rec["frac_of_peak"] = round(rec["gbps"] / HBM_PEAK_GBPS, 4)
+        rec["eager_ms"] = round(timed(graphs[M][1], max(2, reps // 4)), 4)
+    out["ratio_m16_m1"] = round(out["M=16"]["ms"] / out["M=1"]["ms"], 4)
+    log(f"full pass: {out}")
+    del weights, graphs
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,6 +331,11 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--no-shapes", action="store_true",
+                    help="skip the per-shape table of every projection")
+    ap.add_argument("--no-full-pass", action="store_true",
+                    help="skip the 64-layer pass (15.1 GB of weights)")
+    ap.add_argument("--pass-reps", type=int, default=10)
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="run q4_stream_copy over this many MB three times "
                          "(the known-traffic kernel the byte counters are "
@@ -283,9 +433,21 @@ def main():
         probe = stream_probe(torch, q4, 2 * 1024 ** 3)
         log(f"stream read probe: {probe:.0f} GB/s")
 
+    # free the headline shape's copies before the wider measurements
+    del Ws, Wts
+    torch.cuda.empty_cache()
+    shapes = None
+    if not args.no_shapes:
+        shapes = measure_shapes(torch, synth, q4, [n for n in WORKLOADS],
+                                args.steps, args.warmup, args.rotate_gb, dev)
+    full = None
+    if not args.no_full_pass:
+        full = measure_full_pass(torch, synth, q4, args.pass_reps, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(torch, Ws[0], x16, N, K, args.cpu_budget_s)
+        W0 = synth.q4_weights(N, K, seed=0, stream=0, device=dev)
+        cpu = cpu_baseline(torch, W0, x16, N, K, args.cpu_budget_s)
         log(f"cpu oracle: {cpu}")
 
     rec = {
@@ -332,6 +494,8 @@ def main():
             "alg_bytes_per_launch": b16,
         },
         "cpu_baseline": cpu,
+        "shapes": shapes,
+        "full_pass": full,
         "stamp": st,
     }
     print(json.dumps(rec), flush=True)
