@@ -325,7 +325,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="gate_up", choices=sorted(WORKLOADS))
     ap.add_argument("--rotate-gb", type=float, default=1.2)
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)

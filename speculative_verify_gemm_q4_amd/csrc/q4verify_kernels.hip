@@ -356,10 +356,12 @@ __global__ __launch_bounds__(64 * NTW * KSW) void gemm_tiled_kernel(
 
 // The same product with the activations resident in LDS, for K <= 5120
 // (16 rows x K bf16 fit the 160 KB of a CU).  One workgroup per CU:
-//  * it copies x once into LDS, laid out as MFMA operands -- fragment
-//    (q, gi, h) is 1 KB holding lane l's eight inputs 256q + 64gi + 16kb +
-//    8h .. +7 of row j -- with direct-to-LDS buffer loads (lane l lands at
-//    fragment + 16 l; rows >= M fall past the resource and arrive as zeros);
+//  * it copies x once into LDS with direct-to-LDS buffer loads: block
+//    (q, gi, r) is 1 KB and its 16-byte slot s holds the eight inputs
+//    256q + 64gi + 8(s%8) .. +7 of row 8r + s/8, so one copy instruction
+//    moves 8 whole 128-byte rows (lane l lands at block + 16 l; rows >= M fall
+//    past the resource and arrive as zeros).  The MFMA operand of lane
+//    (j, kb), half h, is slot 8(j%8) + 2kb + h of block (q, gi, j/8);
 //  * it owns whole tiles [t0, t1), i.e. U = (t1 - t0) * Q records in
 //    tile-major order, and gives each of its W waves a contiguous range of
 //    them, so every wave streams the same number of records (+-1) and no
@@ -390,16 +392,18 @@ __global__ __launch_bounds__(64 * W) void gemm_resident_kernel(
   const int u0 = static_cast<int>(static_cast<int64_t>(U) * wave / W);
   const int u1 = static_cast<int>(static_cast<int64_t>(U) * (wave + 1) / W);
 
-  // activations -> LDS, fragment f = 8q + 2gi + h handled by wave f % W
+  // activations -> LDS, block f = 8q + 2gi + r copied by wave f % W
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(x), 0,
       static_cast<int>(static_cast<uint32_t>(M) * static_cast<uint32_t>(K) * 2u),
       kBufferWord3);
-  const uint32_t xlane = (static_cast<uint32_t>(j) * K + 16 * kb) * 2;
+  const uint32_t xslot =
+      (static_cast<uint32_t>(lane >> 3) * K + 8 * (lane & 7)) * 2;
   for (int f = wave; f < 8 * Q; f += W) {
-    const int q = f >> 3, gi = (f >> 1) & 3, h = f & 1;
+    const int q = f >> 3, gi = (f >> 1) & 3, r = f & 1;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        xr, (lds_void *)&lds[f * 64], 16, xlane + 16 * h,  // address-space cast
+        xr, (lds_void *)&lds[f * 64], 16,  // address-space cast
+        xslot + static_cast<uint32_t>(8 * r) * K * 2,
         static_cast<uint32_t>(256 * q + 64 * gi) * 2, 0, 0);
   }
 
@@ -432,11 +436,11 @@ __global__ __launch_bounds__(64 * W) void gemm_resident_kernel(
   const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
   const UnpackConsts uc = unpack_consts();
   auto compute = [&](const Stage &s, int q, f32x4 &acc) {
-    const u32x4 *xf = lds + q * 512 + lane;
+    const u32x4 *xf = lds + q * 512 + (j >> 3) * 64 + (j & 7) * 8 + 2 * kb;
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
-      const u32x4 a0 = xf[(2 * gi) * 64];
-      const u32x4 a1 = xf[(2 * gi + 1) * 64];
+      const u32x4 a0 = xf[gi * 128];
+      const u32x4 a1 = xf[gi * 128 + 1];
       f32x4 xn = mfma16x16x32(a0, neg, fzero);
       xn = mfma16x16x32(a1, neg, xn);
       const u32x4 cw = gi < 2 ? s.c0 : s.c1;

@@ -294,3 +294,38 @@ def test_resident_split_tile_sums_in_wave_order():
             out[lt] = v
     want = contrib.reshape(tiles, Q).sum(axis=1)
     assert np.array_equal(out, want)
+
+
+@pytest.mark.parametrize("M,K", [(1, 256), (16, 256), (5, 1280), (16, 5120)])
+def test_resident_lds_layout_gives_each_lane_its_operand(M, K):
+    """Copy side: block f = 8q + 2gi + r, slot s (lane s of the copy) holds
+    inputs 256q + 64gi + 8(s%8) .. +7 of row 8r + s/8, rows >= M zero.  Read
+    side: lane (j, kb), half h reads slot 8(j%8) + 2kb + h of block
+    (q, gi, j/8), and must get inputs 64gi + 16kb + 8h .. +7 of row j of
+    record q (the MFMA A operand of the tiled layout)."""
+    Q = K // 256
+    x = np.arange(16 * K, dtype=np.int64).reshape(16, K) + 1
+    x[M:] = 0
+    lds = np.zeros((8 * Q, 64, 8), dtype=np.int64)
+    assert lds.size * 2 <= LDS_BYTES
+    for f in range(8 * Q):
+        q, gi, r = f >> 3, (f >> 1) & 3, f & 1
+        for s in range(64):
+            row = 8 * r + s // 8
+            k0 = 256 * q + 64 * gi + 8 * (s % 8)
+            # the copy's byte offset, as the kernel forms it
+            voff = ((s >> 3) * K + 8 * (s & 7)) * 2 + 8 * r * K * 2
+            soff = (256 * q + 64 * gi) * 2
+            assert voff + soff == (row * K + k0) * 2
+            if (voff + soff) + 16 <= M * K * 2:
+                lds[f, s] = x[row, k0:k0 + 8]
+    flat = lds.reshape(-1, 8)
+    for q in range(Q):
+        for gi in range(4):
+            for h in range(2):
+                for lane in range(64):
+                    j, kb = lane & 15, lane >> 4
+                    idx = q * 512 + (j >> 3) * 64 + (j & 7) * 8 + 2 * kb \
+                        + gi * 128 + h
+                    k0 = 256 * q + 64 * gi + 16 * kb + 8 * h
+                    assert np.array_equal(flat[idx], x[j, k0:k0 + 8])
