@@ -206,6 +206,10 @@ typedef struct {
   uint32_t lookahead;    /* groups whose loads are issued ahead of use      */
   uint32_t kernel;       /* Q4_KERNEL_* below                               */
   uint32_t lds_bytes;    /* LDS per workgroup                               */
+  uint32_t k_parts;      /* parts of K taken by separate workgroups; > 1
+                            only on the workspace path                      */
+  uint32_t reserved;     /* 0                                               */
+  uint64_t workspace_bytes; /* device workspace the call needs (0: none)    */
 } q4_plan;
 
 #define Q4_KERNEL_PLANAR 0u          /* q4_gemm_verify                       */
@@ -223,6 +227,33 @@ typedef struct {
  */
 int q4_gemm_verify_plan(int M, int64_t N, int64_t K, uint32_t layout_id,
                         q4_plan *out);
+
+/*
+ * q4_gemm_verify_tiled_ws -- q4_gemm_verify_tiled with a caller-owned device
+ * workspace, which lets workgroups split K for K > 5120 (the output and down
+ * projections, whose N = 5120 gives only 320 tiles and whose 16 activation
+ * rows exceed one CU's LDS): part 0 writes y, parts 1..P-1 write their
+ * partial products into the workspace, and a second kernel adds them to y in
+ * part order, so results are deterministic and do not depend on M.  For
+ * K <= 5120 it runs exactly what q4_gemm_verify_tiled runs.
+ *   x, W_tiled, y, M, N, K, stream: as q4_gemm_verify_tiled.
+ *   workspace : device, 16-byte aligned, at least workspace_bytes as
+ *               reported by q4_gemm_verify_tiled_ws_plan for (M, N, K); may
+ *               be NULL when that is 0.  Overwritten; must not overlap x, W
+ *               or y; two calls in flight at once need two workspaces.
+ *   workspace_bytes : its size.
+ * Errors: as q4_gemm_verify_tiled; Q4_EINVAL if the workspace is too small.
+ */
+int q4_gemm_verify_tiled_ws(const void *x, const void *W_tiled, float *y,
+                            int M, int64_t N, int64_t K, void *workspace,
+                            uint64_t workspace_bytes, void *stream);
+
+/*
+ * q4_gemm_verify_tiled_ws_plan -- the plan q4_gemm_verify_tiled_ws launches
+ * for (M, N, K), including its workspace_bytes (for the current device's CU
+ * count).  Errors: Q4_EINVAL, Q4_EOVERFLOW.
+ */
+int q4_gemm_verify_tiled_ws_plan(int M, int64_t N, int64_t K, q4_plan *out);
 
 /* Human-readable name of a q4_status value (static string, never NULL). */
 const char *q4_status_string(int status);

@@ -12,7 +12,10 @@ Functions (same names as the C entry points):
 * :func:`q4_gemm_verify` -- y[M, N] = x[M, K] @ W^T for Q4 W, fp32 out.
 * :func:`q4_repack` -- one-time reorder into the tiled layout.
 * :func:`q4_gemm_verify_tiled` -- the same product on tiled weights.
-* :func:`q4_gemm_verify_plan` -- the launch plan of a shape (host only).
+* :func:`q4_gemm_verify_tiled_ws` -- the tiled product with a workspace
+  (K split across workgroups for K > 5120); :func:`workspace_for` sizes it.
+* :func:`q4_gemm_verify_plan`, :func:`q4_gemm_verify_tiled_ws_plan` -- launch
+  plans of a shape.
 * :func:`q4_dequant` -- fp32 weights of a packed matrix (test hook).
 * :func:`q4_stream_read`, :func:`q4_stream_copy` -- bandwidth probes.
 * :func:`q4_status_string` -- name of a status code.
@@ -20,13 +23,17 @@ Functions (same names as the C entry points):
 from ._lib import (GROUP, KERNEL_PLANAR, KERNEL_TILED_RESIDENT,
                    KERNEL_TILED_STREAM, LAYOUT_PLANAR, LAYOUT_TILED16, MAX_ROWS, Q4Error,
                    LIB_PATH, lib_exports, load, q4_dequant, q4_gemm_verify,
-                   q4_gemm_verify_plan, q4_gemm_verify_tiled, q4_pack_layout,
+                   q4_gemm_verify_plan, q4_gemm_verify_tiled,
+                   q4_gemm_verify_tiled_ws, q4_gemm_verify_tiled_ws_plan,
+                   q4_pack_layout, workspace_for,
                    q4_repack, q4_status_string, q4_stream_copy,
                    q4_stream_read)
 
 __all__ = ["GROUP", "KERNEL_PLANAR", "KERNEL_TILED_RESIDENT",
            "KERNEL_TILED_STREAM", "LAYOUT_PLANAR", "LAYOUT_TILED16", "MAX_ROWS", "Q4Error",
            "LIB_PATH", "lib_exports", "load", "q4_dequant", "q4_gemm_verify",
-           "q4_gemm_verify_plan", "q4_gemm_verify_tiled", "q4_pack_layout",
+           "q4_gemm_verify_plan", "q4_gemm_verify_tiled",
+           "q4_gemm_verify_tiled_ws", "q4_gemm_verify_tiled_ws_plan",
+           "q4_pack_layout", "workspace_for",
            "q4_repack", "q4_status_string", "q4_stream_copy",
            "q4_stream_read"]

@@ -46,7 +46,9 @@ class _Plan(ctypes.Structure):
                 ("row_tiles", ctypes.c_uint32),
                 ("tiles_per_wave", ctypes.c_uint32),
                 ("k_splits", ctypes.c_uint32), ("lookahead", ctypes.c_uint32),
-                ("kernel", ctypes.c_uint32), ("lds_bytes", ctypes.c_uint32)]
+                ("kernel", ctypes.c_uint32), ("lds_bytes", ctypes.c_uint32),
+                ("k_parts", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("workspace_bytes", ctypes.c_uint64)]
 
 
 _lib = None
@@ -71,6 +73,14 @@ _SIGNATURES = {
     "q4_gemm_verify_plan": ([ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                              ctypes.c_uint32, ctypes.POINTER(_Plan)],
                             ctypes.c_int),
+    "q4_gemm_verify_tiled_ws": ([ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                 ctypes.c_int64, ctypes.c_void_p,
+                                 ctypes.c_uint64, ctypes.c_void_p],
+                                ctypes.c_int),
+    "q4_gemm_verify_tiled_ws_plan": ([ctypes.c_int, ctypes.c_int64,
+                                      ctypes.c_int64, ctypes.POINTER(_Plan)],
+                                     ctypes.c_int),
     "q4_status_string": ([ctypes.c_int], ctypes.c_char_p),
 }
 
@@ -120,6 +130,25 @@ def q4_gemm_verify_plan(M: int, N: int, K: int,
     if st != OK:
         raise Q4Error(st, f"q4_gemm_verify_plan({M}, {N}, {K}, {layout_id})")
     return {name: getattr(out, name) for name, _ in _Plan._fields_}
+
+
+def q4_gemm_verify_tiled_ws_plan(M: int, N: int, K: int) -> dict:
+    """The plan q4_gemm_verify_tiled_ws uses for this shape on the current
+    device, with its ``workspace_bytes``."""
+    out = _Plan()
+    st = load().q4_gemm_verify_tiled_ws_plan(int(M), int(N), int(K),
+                                             ctypes.byref(out))
+    if st != OK:
+        raise Q4Error(st, f"q4_gemm_verify_tiled_ws_plan({M}, {N}, {K})")
+    return {name: getattr(out, name) for name, _ in _Plan._fields_}
+
+
+def workspace_for(M: int, N: int, K: int, device):
+    """A uint8 device tensor of the size q4_gemm_verify_tiled_ws needs for
+    (M, N, K), or None when it needs none."""
+    import torch
+    n = q4_gemm_verify_tiled_ws_plan(M, N, K)["workspace_bytes"]
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
 def _stream_handle(stream):
@@ -178,6 +207,30 @@ def q4_gemm_verify_tiled(x, Wt, y, M: int, N: int, K: int,
                                      _stream_handle(stream))
     if st != OK:
         raise Q4Error(st, "q4_gemm_verify_tiled")
+
+
+def q4_gemm_verify_tiled_ws(x, Wt, y, M: int, N: int, K: int, ws=None,
+                            stream=None) -> None:
+    """q4_gemm_verify_tiled with a device workspace ``ws`` (uint8 tensor
+    of at least the plan's workspace_bytes, or None when that is 0), which
+    lets K > 5120 be split across workgroups."""
+    import torch
+    total = q4_pack_layout(N, K, LAYOUT_TILED16)["total_bytes"]
+    px = _ptr(x, "x", torch.bfloat16, shape=(M, K))
+    pw = _ptr(Wt, "Wt", torch.uint8, numel=total)
+    py = _ptr(y, "y", torch.float32, shape=(M, N))
+    if not (x.device == Wt.device == y.device):
+        raise ValueError("x, Wt and y must be on one device")
+    pws, nws = None, 0
+    if ws is not None:
+        pws = _ptr(ws, "ws", torch.uint8)
+        nws = ws.numel()
+        if ws.device != y.device:
+            raise ValueError("ws must be on the device of y")
+    st = load().q4_gemm_verify_tiled_ws(px, pw, py, int(M), int(N), int(K),
+                                        pws, nws, _stream_handle(stream))
+    if st != OK:
+        raise Q4Error(st, "q4_gemm_verify_tiled_ws")
 
 
 def q4_repack(W, Wt, N: int, K: int, stream=None) -> None:

@@ -24,6 +24,8 @@ int check_tiled_shape(int64_t N, int64_t K);
 // `cus` is the compute-unit count of the device the plan is for.
 q4_plan plan_gemm_planar(int M, int64_t N, int64_t K);
 q4_plan plan_gemm_tiled(int M, int64_t N, int64_t K, int cus);
+// The plan of the workspace path (q4_gemm_verify_tiled_ws).
+q4_plan plan_gemm_tiled_ws(int M, int64_t N, int64_t K, int cus);
 
 // Bytes of one record of the tiled layout: 16 rows x 4 groups x 36 bytes.
 constexpr int kTileRows = 16;
@@ -34,6 +36,7 @@ constexpr int kRecordBytes = kTileRows * kRecordGroups * 36;
 // K whose 16 activation rows fit in it as bf16.
 constexpr int kLdsBytes = 163840;
 constexpr int kResidentMaxK = kLdsBytes / 32;
+constexpr int kResidentMaxRecords = kResidentMaxK / 256;  // per part of K
 // Waves per workgroup and register stages of the resident-activation kernel.
 constexpr int kResidentWaves = 8;
 constexpr int kResidentStages = 2;

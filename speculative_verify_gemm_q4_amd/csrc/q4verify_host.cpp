@@ -107,28 +107,66 @@ q4_plan plan_gemm_planar(int M, int64_t N, int64_t K) {
   p.grid = static_cast<uint32_t>((tiles + ntw - 1) / ntw);
   p.lookahead = 4;
   p.kernel = Q4_KERNEL_PLANAR;
+  p.k_parts = 1;
   p.lds_bytes = ksw > 1 ? static_cast<uint32_t>(ksw * ntw * 64 * 16) : 0;
   return p;
 }
 
+// Plan of the resident-activation kernel with K split into `parts` parts
+// (one group of workgroups per part, one workgroup per CU); false when a
+// part's activations exceed the LDS or a wave's 32-bit buffer offsets could
+// overflow (then the streaming kernel runs).
+bool plan_resident(int M, int64_t N, int64_t K, int cus, int parts,
+                   q4_plan *out) {
+  const int64_t tiles = N / kTileRows;
+  const int64_t records = K / (kRecordGroups * Q4_GROUP);
+  if (parts < 1 || (records + parts - 1) / parts > kResidentMaxRecords)
+    return false;
+  int64_t gt = cus / parts;
+  if (gt < 1) gt = 1;
+  if (gt > tiles) gt = tiles;
+  // a wave's resource spans at most its workgroup's tiles, all records
+  const int64_t span = ((tiles + gt - 1) / gt) * records * kRecordBytes;
+  if (span >= 0x7FFFFFF0LL) return false;
+  q4_plan p;
+  std::memset(&p, 0, sizeof p);
+  p.grid = static_cast<uint32_t>(gt * parts);
+  p.block = 64 * kResidentWaves;
+  p.row_tiles = static_cast<uint32_t>((tiles + gt - 1) / gt);
+  p.tiles_per_wave = 1;
+  p.k_splits = 1;
+  p.lookahead = kRecordGroups * (kResidentStages - 1);
+  p.kernel = Q4_KERNEL_TILED_RESIDENT;
+  p.lds_bytes = kLdsBytes;
+  p.k_parts = static_cast<uint32_t>(parts);
+  p.workspace_bytes = static_cast<uint64_t>(parts - 1) *
+                      static_cast<uint64_t>(M) * static_cast<uint64_t>(N) * 4;
+  *out = p;
+  return true;
+}
+
+q4_plan plan_gemm_tiled_ws(int M, int64_t N, int64_t K, int cus) {
+  if (K > kResidentMaxK) {
+    // Parts of K taken by separate workgroups: enough for a part's
+    // activations to fit the LDS, and at least 4, a power of two, so that
+    // the 320 tiles of the N = 5120 projections give every CU whole tiles.
+    const int64_t records = K / (kRecordGroups * Q4_GROUP);
+    int64_t parts = 4;
+    while (parts * kResidentMaxRecords < records) parts *= 2;
+    q4_plan p;
+    if (parts <= cus && plan_resident(M, N, K, cus, static_cast<int>(parts), &p))
+      return p;
+  }
+  return plan_gemm_tiled(M, N, K, cus);
+}
+
 q4_plan plan_gemm_tiled(int M, int64_t N, int64_t K, int cus) {
-  (void)M;
   const int64_t tiles = N / kTileRows;
   if (K <= kResidentMaxK) {
     // Activations resident in LDS: one workgroup per CU (the LDS admits no
     // second), each owning whole tiles; its waves split its records evenly.
     q4_plan p;
-    std::memset(&p, 0, sizeof p);
-    const int64_t g = tiles < cus ? tiles : cus;
-    p.grid = static_cast<uint32_t>(g);
-    p.block = 64 * kResidentWaves;
-    p.row_tiles = static_cast<uint32_t>((tiles + g - 1) / g);
-    p.tiles_per_wave = 1;
-    p.k_splits = 1;
-    p.lookahead = kRecordGroups * (kResidentStages - 1);
-    p.kernel = Q4_KERNEL_TILED_RESIDENT;
-    p.lds_bytes = kLdsBytes;
-    return p;
+    if (plan_resident(M, N, K, cus, 1, &p)) return p;
   }
   // Tiles per wave: each wave multiplies its activation operand with 1-4
   // tiles, so the activation loads per weight byte fall with more tiles
@@ -151,6 +189,7 @@ q4_plan plan_gemm_tiled(int M, int64_t N, int64_t K, int cus) {
   p.grid = static_cast<uint32_t>(sets);
   p.lookahead = kRecordGroups;
   p.kernel = Q4_KERNEL_TILED_STREAM;
+  p.k_parts = 1;
   p.lds_bytes = ksw > 1 ? static_cast<uint32_t>(ksw * tnt * 64 * 16) : 0;
   return p;
 }
@@ -260,6 +299,15 @@ extern "C" int q4_gemm_verify_plan(int M, int64_t N, int64_t K,
     return Q4_OK;
   }
   return Q4_EINVAL;
+}
+
+extern "C" int q4_gemm_verify_tiled_ws_plan(int M, int64_t N, int64_t K,
+                                            q4_plan *out) {
+  if (out == nullptr || M < 1 || M > Q4_MAX_ROWS) return Q4_EINVAL;
+  const int st = q4v::check_tiled_shape(N, K);
+  if (st != Q4_OK) return st;
+  *out = q4v::plan_gemm_tiled_ws(M, N, K, q4v::device_cus());
+  return Q4_OK;
 }
 
 extern "C" const char *q4_status_string(int status) {

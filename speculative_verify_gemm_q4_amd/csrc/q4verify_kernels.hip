@@ -354,23 +354,30 @@ __global__ __launch_bounds__(64 * NTW * KSW) void gemm_tiled_kernel(
   }
 }
 
-// The same product with the activations resident in LDS, for K <= 5120
-// (16 rows x K bf16 fit the 160 KB of a CU).  One workgroup per CU:
-//  * it copies x once into LDS with direct-to-LDS buffer loads: block
-//    (q, gi, r) is 1 KB and its 16-byte slot s holds the eight inputs
-//    256q + 64gi + 8(s%8) .. +7 of row 8r + s/8, so one copy instruction
-//    moves 8 whole 128-byte rows (lane l lands at block + 16 l; rows >= M fall
-//    past the resource and arrive as zeros).  The MFMA operand of lane
-//    (j, kb), half h, is slot 8(j%8) + 2kb + h of block (q, gi, j/8);
-//  * it owns whole tiles [t0, t1), i.e. U = (t1 - t0) * Q records in
-//    tile-major order, and gives each of its W waves a contiguous range of
-//    them, so every wave streams the same number of records (+-1) and no
-//    wave reloads activation operands from the memory hierarchy;
+// The same product with the activations resident in LDS.  The workgroups
+// form P groups of Gt, one group per part of K: part p is the records
+// [Q p / P, Q (p+1) / P) of every tile, at most 20 of them (16 rows x 20 x 256
+// bf16 = the 160 KB of a CU's LDS).  P = 1 whenever K <= 5120.  One
+// workgroup per CU:
+//  * it copies its part of x once into LDS with direct-to-LDS buffer loads:
+//    block (q, gi, r) is 1 KB and its 16-byte slot s holds the eight inputs
+//    256q + 64gi + 8(s%8) .. +7 of row 8r + s/8 (q counted within the part),
+//    so one copy instruction moves 8 whole 128-byte rows (lane l lands at
+//    block + 16 l; rows >= M fall past the resource and arrive as zeros).
+//    The MFMA operand of lane (j, kb), half h, is slot 8(j%8) + 2kb + h of
+//    block (q, gi, j/8);
+//  * it owns whole tiles [t0, t1) of its group, i.e. U = (t1 - t0) * nq
+//    records in tile-major order, and gives each of its W waves a contiguous
+//    range of them, so every wave streams the same number of records (+-1)
+//    and no wave reloads activation operands from the memory hierarchy;
 //  * a tile that lies wholly inside one wave's range is written by that wave
 //    as soon as its last record is done; a tile split between waves is
 //    reduced after the loop through LDS, in wave order, by the wave holding
-//    the tile's first record.  The summation order is fixed by (N, K), so
-//    results do not depend on M or on timing.
+//    the tile's first record;
+//  * part 0 writes y, part p > 0 its own M x N slice of the workspace, and
+//    reduce_parts_kernel then adds the slices to y in part order.
+// Summation orders depend only on (N, K, P), so results do not depend on M
+// and repeated calls are bitwise equal.
 // Weight records go through S register stages: the loads of record i + S - 1
 // are issued before record i is multiplied.
 typedef __attribute__((address_space(3))) void lds_void;
@@ -378,7 +385,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 template <int W, int S>
 __global__ __launch_bounds__(64 * W) void gemm_resident_kernel(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ Wt,
-    float *__restrict__ y, int M, int N, int K, int G) {
+    float *__restrict__ y, float *__restrict__ ws, int M, int N, int K,
+    int P, int Gt) {
   __shared__ u32x4 lds[kLdsBytes / 16];
   const int T = N >> 4;
   const int Q = K >> 8;
@@ -386,9 +394,13 @@ __global__ __launch_bounds__(64 * W) void gemm_resident_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 15;
   const int kb = lane >> 4;
-  const int t0 = static_cast<int>(static_cast<int64_t>(T) * blockIdx.x / G);
-  const int t1 = static_cast<int>(static_cast<int64_t>(T) * (blockIdx.x + 1) / G);
-  const int U = (t1 - t0) * Q;
+  const int p = blockIdx.x / Gt;
+  const int bt = blockIdx.x % Gt;
+  const int qa = static_cast<int>(static_cast<int64_t>(Q) * p / P);
+  const int nq = static_cast<int>(static_cast<int64_t>(Q) * (p + 1) / P) - qa;
+  const int t0 = static_cast<int>(static_cast<int64_t>(T) * bt / Gt);
+  const int t1 = static_cast<int>(static_cast<int64_t>(T) * (bt + 1) / Gt);
+  const int U = (t1 - t0) * nq;
   const int u0 = static_cast<int>(static_cast<int64_t>(U) * wave / W);
   const int u1 = static_cast<int>(static_cast<int64_t>(U) * (wave + 1) / W);
 
@@ -399,30 +411,43 @@ __global__ __launch_bounds__(64 * W) void gemm_resident_kernel(
       kBufferWord3);
   const uint32_t xslot =
       (static_cast<uint32_t>(lane >> 3) * K + 8 * (lane & 7)) * 2;
-  for (int f = wave; f < 8 * Q; f += W) {
-    const int q = f >> 3, gi = (f >> 1) & 3, r = f & 1;
+  for (int f = wave; f < 8 * nq; f += W) {
+    const int q = qa + (f >> 3), gi = (f >> 1) & 3, r = f & 1;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         xr, (lds_void *)&lds[f * 64], 16,  // address-space cast
         xslot + static_cast<uint32_t>(8 * r) * K * 2,
         static_cast<uint32_t>(256 * q + 64 * gi) * 2, 0, 0);
   }
 
-  // this wave's records only: loads past its range return zeros
+  // This wave's weights: a resource over the whole tiles its range touches;
+  // a record past the range gets an offset past the resource, so that
+  // prefetch returns zeros and moves no bytes.
+  const int nrec = u1 - u0;
+  const int ft = u0 / nq;
+  const int nt = nrec > 0 ? (u1 - 1) / nq + 1 - ft : 0;
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t *>(Wt + (static_cast<uint64_t>(t0) * Q + u0) * kRecordBytes),
-      0, (u1 - u0) * kRecordBytes, kBufferWord3);
+      const_cast<uint8_t *>(Wt + static_cast<uint64_t>(t0 + ft) * Q * kRecordBytes),
+      0, nt * Q * kRecordBytes, kBufferWord3);
   struct Stage {
     u32x4 c0, c1, sb;
   };
-  auto load = [&](int i, Stage &st) {  // record u0 + i
-    const uint32_t o = static_cast<uint32_t>(i) * kRecordBytes;
+  int lq = u0 % nq, ltl = 0, nload = 0;  // next load: record qa + lq of tile ft + ltl
+  auto load = [&](Stage &st) {
+    const uint32_t o = nload < nrec
+                           ? static_cast<uint32_t>((ltl * Q + qa + lq) * kRecordBytes)
+                           : 0x7FFFFFF0u;
     st.c0 = buffer_load16<kNonTemporal>(wr, lane * 16, o);
     st.c1 = buffer_load16<kNonTemporal>(wr, 1024 + lane * 16, o);
     st.sb = buffer_load16<kNonTemporal>(wr, 2048 + j * 16, o);
+    ++nload;
+    if (++lq == nq) {
+      lq = 0;
+      ++ltl;
+    }
   };
   Stage st[S];
 #pragma unroll
-  for (int i = 0; i < S - 1; ++i) load(i, st[i]);
+  for (int i = 0; i < S - 1; ++i) load(st[i]);
   // Every outstanding vector memory operation, this wave's activation copies
   // included, must be complete before the barrier: direct-to-LDS loads need
   // not complete in order with the weight loads issued after them (a weight
@@ -458,30 +483,30 @@ __global__ __launch_bounds__(64 * W) void gemm_resident_kernel(
       }
     }
   };
+  float *dst = p == 0 ? y : ws + static_cast<uint64_t>(p - 1) * M * N;
   auto store = [&](int tile, const f32x4 &v) {
     const int n = tile * 16 + j;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = kb * 4 + r;
-      if (m < M) y[static_cast<uint64_t>(m) * N + n] = v[r];
+      if (m < M) dst[static_cast<uint64_t>(m) * N + n] = v[r];
     }
   };
 
   // head: partial sum of a first tile entered past its first record;
   // tail: partial sum of a last tile left before its last record
   f32x4 acc = fzero, head_sum = fzero, tail_sum = fzero;
-  int q = u0 % Q;
-  int tl = u0 / Q;
+  int q = u0 % nq;
+  int tl = u0 / nq;
   bool in_head = q != 0;
-  const int nrec = u1 - u0;
   for (int i0 = 0; i0 < nrec; i0 += S) {
 #pragma unroll
     for (int i = 0; i < S; ++i) {
-      load(i0 + i + S - 1, st[(i + S - 1) % S]);
+      load(st[(i + S - 1) % S]);
       __builtin_amdgcn_sched_barrier(0);
       if (i0 + i < nrec) {
         compute(st[i], q, acc);
-        if (++q == Q) {
+        if (++q == nq) {
           if (in_head) {
             head_sum = acc;
             in_head = false;
@@ -510,21 +535,33 @@ __global__ __launch_bounds__(64 * W) void gemm_resident_kernel(
   part[(wave * 2 + 0) * 64 + lane] = head_sum;
   part[(wave * 2 + 1) * 64 + lane] = tail_sum;
   __syncthreads();
-  if (u1 > u0) {
-    const int lt = (u1 - 1) / Q;
-    if (lt * Q >= u0 && lt * Q + Q > u1) {
+  if (nrec > 0) {
+    const int lt = (u1 - 1) / nq;
+    if (lt * nq >= u0 && lt * nq + nq > u1) {
       // this wave holds lt's first record but not its last: its share is
       // its tail sum, the following waves' shares their head sums
       f32x4 v = part[(wave * 2 + 1) * 64 + lane];
       for (int w2 = wave + 1; w2 < W; ++w2) {
         const int a0 = static_cast<int>(static_cast<int64_t>(U) * w2 / W);
         const int a1 = static_cast<int>(static_cast<int64_t>(U) * (w2 + 1) / W);
-        if (a0 >= lt * Q + Q) break;
+        if (a0 >= lt * nq + nq) break;
         if (a1 > a0) v += part[(w2 * 2) * 64 + lane];
       }
       store(t0 + lt, v);
     }
   }
+}
+
+// y += sum over parts p = 1 .. P-1 of workspace slice p - 1, in part order
+// (four outputs per thread; M * N is a multiple of 16).
+__global__ __launch_bounds__(256) void reduce_parts_kernel(
+    float *__restrict__ y, const float *__restrict__ ws, uint32_t mn4, int P) {
+  const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+  if (i >= mn4) return;
+  f32x4 v = reinterpret_cast<f32x4 *>(y)[i];
+  for (int p = 1; p < P; ++p)
+    v += reinterpret_cast<const f32x4 *>(ws)[static_cast<uint64_t>(p - 1) * mn4 + i];
+  reinterpret_cast<f32x4 *>(y)[i] = v;
 }
 
 // Code word q0..q7 (nibble i = input i) -> nibbles q0 q2 q4 q6 q1 q3 q5 q7,
@@ -665,12 +702,18 @@ int launch_tiled(const q4_plan &p, const void *x, const void *W, float *y,
 }
 
 int launch_resident(const q4_plan &p, const void *x, const void *W, float *y,
-                    int M, int N, int K, hipStream_t stream) {
+                    float *ws, int M, int N, int K, hipStream_t stream) {
+  const int parts = static_cast<int>(p.k_parts);
   hipLaunchKernelGGL((gemm_resident_kernel<kResidentWaves, kResidentStages>),
                      dim3(p.grid), dim3(p.block), 0, stream,
                      static_cast<const uint16_t *>(x),
-                     static_cast<const uint8_t *>(W), y, M, N, K,
-                     static_cast<int>(p.grid));
+                     static_cast<const uint8_t *>(W), y, ws, M, N, K, parts,
+                     static_cast<int>(p.grid) / parts);
+  int st = launch_status();
+  if (st != Q4_OK || parts == 1) return st;
+  const uint32_t mn4 = static_cast<uint32_t>(M) * static_cast<uint32_t>(N) / 4;
+  hipLaunchKernelGGL(reduce_parts_kernel, dim3((mn4 + 255) / 256), dim3(256), 0,
+                     stream, y, static_cast<const float *>(ws), mn4, parts);
   return launch_status();
 }
 
@@ -718,7 +761,7 @@ extern "C" int q4_gemm_verify_tiled(const void *x, const void *W, float *y,
   const int n = static_cast<int>(N), k = static_cast<int>(K);
   const q4_plan p = q4v::plan_gemm_tiled(M, N, K, q4v::device_cus());
   if (p.kernel == Q4_KERNEL_TILED_RESIDENT)
-    return q4v::launch_resident(p, x, W, y, M, n, k, s);
+    return q4v::launch_resident(p, x, W, y, nullptr, M, n, k, s);
   const int key = static_cast<int>(p.tiles_per_wave * 100 + p.k_splits);
   switch (key) {
 #define Q4V_TILED_CASE(TNT, KSW) \
@@ -733,6 +776,30 @@ extern "C" int q4_gemm_verify_tiled(const void *x, const void *W, float *y,
 #undef Q4V_TILED_CASE
     default: return Q4_EINVAL;
   }
+}
+
+extern "C" int q4_gemm_verify_tiled_ws(const void *x, const void *W, float *y,
+                                       int M, int64_t N, int64_t K,
+                                       void *workspace,
+                                       uint64_t workspace_bytes,
+                                       void *stream) {
+  int st = q4v::check_gemm_args(x, W, y, M, N, K);
+  if (st != Q4_OK) return st;
+  st = q4v::check_tiled_shape(N, K);
+  if (st != Q4_OK) return st;
+  const q4_plan p = q4v::plan_gemm_tiled_ws(M, N, K, q4v::device_cus());
+  if (p.workspace_bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < p.workspace_bytes)
+      return Q4_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0) return Q4_EALIGN;
+  }
+  st = q4v::check_device();
+  if (st != Q4_OK) return st;
+  if (p.kernel != Q4_KERNEL_TILED_RESIDENT)
+    return q4_gemm_verify_tiled(x, W, y, M, N, K, stream);
+  return q4v::launch_resident(p, x, W, y, static_cast<float *>(workspace), M,
+                              static_cast<int>(N), static_cast<int>(K),
+                              static_cast<hipStream_t>(stream));
 }
 
 extern "C" int q4_repack(const void *W, void *W_tiled, int64_t N, int64_t K,

@@ -139,6 +139,26 @@ def test_gemm_argument_errors(lib):
     assert g(X, W, Y + 2, 1, 256, 512, None) == -2    # y not 4-B aligned
 
 
+def test_workspace_gemm_argument_errors(lib):
+    """The workspace path: same rules as the tiled call, plus the workspace
+    (too small, missing or misaligned) -- all rejected before device work."""
+    g = lib.q4_gemm_verify_tiled_ws
+    X, W, Y, S = 0x10000, 0x20000, 0x30000, 0x40000
+    need = q4.q4_gemm_verify_tiled_ws_plan(16, 5120, 17408)["workspace_bytes"]
+    assert need == 3 * 16 * 5120 * 4
+    assert g(X, W, Y, 16, 5120, 17408, None, 0, None) == -1
+    assert g(X, W, Y, 16, 5120, 17408, S, need - 16, None) == -1
+    assert g(X, W, Y, 16, 5120, 17408, S + 8, need, None) == -2
+    assert g(X, W, Y, 0, 5120, 17408, S, need, None) == -1
+    assert g(X, W, Y, 16, 5121, 17408, S, need, None) == -1   # N % 16
+    assert g(X, W, Y, 16, 5120, 17400, S, need, None) == -1   # K % 256
+    # K <= 5120 needs no workspace, K > 5120 needs (P - 1) M N floats
+    assert q4.q4_gemm_verify_tiled_ws_plan(16, 34816, 5120)[
+        "workspace_bytes"] == 0
+    p = q4.q4_gemm_verify_tiled_ws_plan(3, 5120, 6144)
+    assert p["workspace_bytes"] == (p["k_parts"] - 1) * 3 * 5120 * 4
+
+
 def test_dequant_and_probe_argument_errors(lib):
     d = lib.q4_dequant
     assert d(0x10000, 0x20000, 0, 64, None) == -1

@@ -383,6 +383,101 @@ def test_tiled_full_shape_sampled(q4, name, M):
     assert torch.isfinite(y).all()
 
 
+# -------------------------------------------------------------- workspace path
+
+def gemm_tiled_ws(q4, x, Wt, M, N, K, fill=float("nan")):
+    y = torch.full((M, N), fill, dtype=torch.float32, device=x.device)
+    ws = q4.workspace_for(M, N, K, x.device)
+    if ws is not None:
+        ws.fill_(0xFF)  # stale workspace bytes must not matter
+    q4.q4_gemm_verify_tiled_ws(x, Wt, y, M, N, K, ws)
+    torch.cuda.synchronize()
+    return y
+
+
+# K > 5120 (split across workgroups, partial sums reduced in part order),
+# including tiny N (most waves empty) and a part count above 4
+WS_SHAPES = [(16, 5120, 6144), (3, 5120, 17408), (1, 16, 5376),
+             (16, 48, 10240), (5, 1600, 7168), (16, 256, 65536),
+             (9, 32, 5632)]
+
+
+@pytest.mark.parametrize("M,N,K", WS_SHAPES)
+def test_workspace_split_shapes(q4, M, N, K):
+    dev = torch.device("cuda")
+    p = q4.q4_gemm_verify_tiled_ws_plan(M, N, K)
+    assert p["k_parts"] > 1 and p["workspace_bytes"] > 0
+    W = synth.q4_weights(N, K, seed=30, device=dev)
+    x = synth.activations(M, K, seed=30, stream=1, device=dev)
+    _say(f"case workspace split: M={M} N={N} K={K} parts={p['k_parts']}")
+    y = gemm_tiled_ws(q4, x, repacked(q4, W, N, K), M, N, K)
+    _, y64, a64, _ = oracle.gemm(synth.bf16_bits(x), W.cpu().numpy(), N, K)
+    assert_within_bound(y, y64, a64, f"workspace M={M} N={N} K={K}")
+
+
+def test_workspace_integer_exact_M_invariance_determinism(q4):
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(31)
+    N, K = 512, 6144
+    q = rng.integers(0, 16, size=(N, K))
+    G = K // 64
+    codes = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    Wh = assemble(codes, bf16_bits_of(np.ones((N, G))),
+                  bf16_bits_of(np.full((N, G), -8.0)))
+    xi = rng.integers(-4, 5, size=(16, K)).astype(np.float32)
+    Wt = repacked(q4, torch.from_numpy(Wh).to(dev), N, K)
+    x = torch.from_numpy(xi).to(torch.bfloat16).to(dev)
+    _say("case workspace integer-exact")
+    y = gemm_tiled_ws(q4, x, Wt, 16, N, K)
+    y32, _, _, _ = oracle.gemm(bf16_bits_of(xi), Wh, N, K)
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), y32.view(np.uint32))
+    # random data: rows do not depend on M; calls repeat bit for bit
+    N, K = 5120, 17408
+    W = synth.q4_weights(N, K, seed=32, device=dev)
+    Wt = repacked(q4, W, N, K)
+    xr = synth.activations(16, K, seed=32, stream=1, device=dev)
+    _say("case workspace M-invariance")
+    full = gemm_tiled_ws(q4, xr, Wt, 16, N, K)
+    again = gemm_tiled_ws(q4, xr, Wt, 16, N, K, fill=0.0)
+    assert torch.equal(full.view(torch.int32), again.view(torch.int32))
+    for M in (1, 2, 5, 8, 13):
+        part = gemm_tiled_ws(q4, xr[:M].contiguous(), Wt, M, N, K)
+        assert torch.equal(part.view(torch.int32), full[:M].view(torch.int32)), M
+
+
+def test_workspace_path_equals_plain_call_when_unsplit(q4):
+    """For K <= 5120 the workspace call runs the plain call's kernel."""
+    dev = torch.device("cuda")
+    N, K, M = 4096, 5120, 16
+    assert q4.q4_gemm_verify_tiled_ws_plan(M, N, K)["workspace_bytes"] == 0
+    W = synth.q4_weights(N, K, seed=33, device=dev)
+    Wt = repacked(q4, W, N, K)
+    x = synth.activations(M, K, seed=33, stream=1, device=dev)
+    _say("case workspace unsplit")
+    a = gemm_tiled(q4, x, Wt, M, N, K)
+    b = gemm_tiled_ws(q4, x, Wt, M, N, K)
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+@pytest.mark.parametrize("name,M", [("down", 1), ("down", 16), ("o_proj", 1),
+                                    ("o_proj", 16), ("down", 4)])
+def test_workspace_full_shape_sampled(q4, name, M):
+    dev = torch.device("cuda")
+    N, K = FULL[name]
+    W = synth.q4_weights(N, K, seed=14, stream=list(FULL).index(name),
+                          device=dev)
+    Wt = repacked(q4, W, N, K)
+    x = synth.activations(M, K, seed=14, stream=4000 + M, device=dev)
+    _say(f"case workspace full {name}: M={M} N={N} K={K}")
+    y = gemm_tiled_ws(q4, x, Wt, M, N, K)
+    rows = sampled_rows(N, 224, seed=M + 5)
+    Wsub = sub_matrix(W, N, K, rows)
+    _, y64, a64, _ = oracle.gemm(synth.bf16_bits(x), Wsub, len(rows), K)
+    got = y[:, torch.as_tensor(rows, device=dev)]
+    assert_within_bound(got, y64, a64, f"workspace {name} M={M}")
+    assert torch.isfinite(y).all()
+
+
 # -------------------------------------------------------------- probes
 
 def test_stream_probes(q4):

@@ -188,57 +188,68 @@ LDS_BYTES = 163840
 
 
 def resident_model(M, N, K, p):
+    """Work split of the resident-activation kernel for plan p: workgroup b
+    takes part p = b // Gt of K (records [Q p / P, Q (p+1) / P)) and the
+    tiles [T g / Gt, T (g+1) / Gt) of group g = b % Gt."""
     T, Q = N // 16, K // 256
-    G, W = p["grid"], p["block"] // 64
+    P, W = p["k_parts"], p["block"] // 64
+    G = p["grid"]
+    assert G % P == 0
+    Gt = G // P
     assert p["lds_bytes"] == LDS_BYTES and p["block"] <= 1024
-    assert G == min(T, 256) and p["row_tiles"] == -(-T // G)
-    assert 8 * Q * 1024 <= LDS_BYTES and 2 * W * 1024 <= LDS_BYTES
-    hits = np.zeros(T * Q, dtype=np.int32)
-    writes = np.zeros(T, dtype=np.int32)
-    # record r of a tile belongs to exactly one wave, and the summation of a
-    # split tile visits exactly the waves holding its records, each once
+    assert Gt == min(T, max(1, 256 // P))
+    assert p["workspace_bytes"] == (P - 1) * M * N * 4
+    assert 2 * W * 1024 <= LDS_BYTES
+    hits = np.zeros((T, Q), dtype=np.int32)
+    writes = np.zeros((P, T), dtype=np.int32)
     for b in range(G):
-        t0, t1 = T * b // G, T * (b + 1) // G
-        U = (t1 - t0) * Q
+        part, g = b // Gt, b % Gt
+        qa, qb = Q * part // P, Q * (part + 1) // P
+        nq = qb - qa
+        assert 0 < nq and 8 * nq * 1024 <= LDS_BYTES
+        t0, t1 = T * g // Gt, T * (g + 1) // Gt
+        U = (t1 - t0) * nq
         rng = [(U * w // W, U * (w + 1) // W) for w in range(W)]
         owner_of = {}
         for w, (u0, u1) in enumerate(rng):
             if u1 > u0:
-                hits[t0 * Q + u0: t0 * Q + u1] += 1
-                # the wave's resource: records [t0 Q + u0, t0 Q + u1)
-                assert (t0 * Q + u1) * 2304 <= T * Q * 2304
-                assert (u1 - u0) * 2304 < 2 ** 31
-            # tiles completed inside the range are stored by the wave
-            q, tl, head = u0 % Q, u0 // Q, u0 % Q != 0
+                # the wave's resource: whole tiles ft .. lt of its range
+                ft, lt = u0 // nq, (u1 - 1) // nq
+                span = (lt - ft + 1) * Q * 2304
+                assert (t0 + ft) * Q * 2304 + span <= T * Q * 2304
+                assert span < 0x7FFFFFF0
+                for u in range(u0, u1):
+                    tl, rq = u // nq, u % nq
+                    off = ((tl - ft) * Q + qa + rq) * 2304
+                    assert 0 <= off and off + 2304 <= span
+                    hits[t0 + tl, qa + rq] += 1
+            q, tl, head = u0 % nq, u0 // nq, u0 % nq != 0
             for _ in range(u1 - u0):
                 q += 1
-                if q == Q:
+                if q == nq:
                     if not head:
-                        writes[t0 + tl] += 1
+                        writes[part, t0 + tl] += 1
                     head, q, tl = False, 0, tl + 1
             if u1 > u0:
-                lt = (u1 - 1) // Q
-                if lt * Q >= u0 and lt * Q + Q > u1:
+                lt = (u1 - 1) // nq
+                if lt * nq >= u0 and lt * nq + nq > u1:
                     owner_of[lt] = w
         for lt, w in owner_of.items():
-            got = [(w, "tail")]
+            got = [w]
             for w2 in range(w + 1, W):
                 a0, a1 = rng[w2]
-                if a0 >= lt * Q + Q:
+                if a0 >= lt * nq + nq:
                     break
                 if a1 > a0:
-                    got.append((w2, "head"))
-            # the waves whose ranges meet tile lt
+                    got.append(w2)
             want = [w2 for w2, (a0, a1) in enumerate(rng)
-                    if a1 > a0 and a0 < lt * Q + Q and a1 > lt * Q]
-            assert [g[0] for g in got] == want
-            # the owner's share starts at the tile's first record and stops
-            # inside it (its tail sum); each follower starts inside the tile
+                    if a1 > a0 and a0 < lt * nq + nq and a1 > lt * nq]
+            assert got == want
             u0, u1 = rng[w]
-            assert u0 <= lt * Q < u1 < lt * Q + Q
-            for w2, _ in got[1:]:
-                assert lt * Q < rng[w2][0] < lt * Q + Q
-            writes[t0 + lt] += 1
+            assert u0 <= lt * nq < u1 < lt * nq + nq
+            for w2 in got[1:]:
+                assert lt * nq < rng[w2][0] < lt * nq + nq
+            writes[part, t0 + lt] += 1
     assert np.all(hits == 1)
     assert np.all(writes == 1)
 
@@ -329,3 +340,18 @@ def test_resident_lds_layout_gives_each_lane_its_operand(M, K):
                         + gi * 128 + h
                     k0 = 256 * q + 64 * gi + 16 * kb + 8 * h
                     assert np.array_equal(flat[idx], x[j, k0:k0 + 8])
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 5120, 17408), (1, 5120, 6144),
+                                   (7, 5120, 6144), (16, 16, 5376),
+                                   (16, 4096, 65536), (2, 48, 10240),
+                                   (16, 5120, 6144), (3, 5120, 17408),
+                                   (1, 16, 5376), (16, 48, 10240),
+                                   (5, 1600, 7168), (16, 256, 65536),
+                                   (9, 32, 5632), (4, 5120, 17408)])
+def test_workspace_plan_split_parts(M, N, K):
+    p = q4.q4_gemm_verify_tiled_ws_plan(M, N, K)
+    assert p["kernel"] == q4.KERNEL_TILED_RESIDENT and p["k_parts"] > 1
+    P = p["k_parts"]
+    assert P >= 4 and P & (P - 1) == 0 and -(-(K // 256) // P) <= 20
+    resident_model(M, N, K, p)
