@@ -108,28 +108,6 @@ def load_traffic(M, N, K):
     return per_m.get("hbm_bytes_per_launch")
 
 
-def time_calls(torch, call, xs, Ws, y, M, N, K, steps, warmup):
-    """Warm up, then time `steps` back-to-back calls of call(x, W, y, M, N,
-    K) between two HIP events recorded on the launch stream (torch's current
-    stream, which the binding launches on); returns (ms per call from the
-    events, ms per call from the host clock between synchronisations)."""
-    stream = torch.cuda.current_stream()
-    n_w = len(Ws)
-    for i in range(warmup):
-        call(xs, Ws[i % n_w], y, M, N, K)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(steps):
-        call(xs, Ws[(warmup + i) % n_w], y, M, N, K)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3
-    return e0.elapsed_time(e1) / steps, wall_ms / steps
-
-
 def stream_probe(torch, q4, nbytes):
     buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     buf.random_(0, 255)
@@ -192,9 +170,57 @@ def rotated_tiled(torch, synth, q4, N, K, rotate_gb, stream0, dev):
     return out
 
 
+def raw_calls(torch, q4, entry, x, Ws, y, M, N, K, ws=None):
+    """One prepared zero-argument call of the C entry point per weight copy:
+    the binding's argument checks are done here once, so the timed loop pays
+    only the ctypes call (about 1-2 us of host time, below every kernel's
+    duration, so launches queue ahead of the GPU)."""
+    import functools
+    lib = q4.load()
+    fn = getattr(lib, entry)
+    stream = torch.cuda.current_stream().cuda_stream
+    out = []
+    for W in Ws:
+        # validate once through the public binding (raises on misuse)
+        if entry == "q4_gemm_verify_tiled_ws":
+            q4.q4_gemm_verify_tiled_ws(x, W, y, M, N, K, ws)
+            args = (x.data_ptr(), W.data_ptr(), y.data_ptr(), M, N, K,
+                    None if ws is None else ws.data_ptr(),
+                    0 if ws is None else ws.numel(), stream)
+        else:
+            getattr(q4, entry)(x, W, y, M, N, K)
+            args = (x.data_ptr(), W.data_ptr(), y.data_ptr(), M, N, K, stream)
+        f = functools.partial(fn, *args)
+        if f() != 0:
+            raise RuntimeError(f"{entry} failed on a prepared call")
+        out.append(f)
+    torch.cuda.synchronize()
+    return out
+
+
+def time_raw(torch, fns, steps, warmup):
+    """ms per call of `steps` back-to-back calls (rotating over fns) between
+    two HIP events on the launch stream, after `warmup` untimed calls."""
+    n = len(fns)
+    for i in range(warmup):
+        fns[i % n]()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        fns[(warmup + i) % n]()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return e0.elapsed_time(e1) / steps, wall
+
+
 def measure_shapes(torch, synth, q4, names, steps, warmup, rotate_gb, dev):
     """Every projection shape of the 27B pass at M = 16 and M = 1 (order
-    16, 1, 16), each over its own rotated copies."""
+    16, 1, 16), each over its own rotated copies, through the workspace
+    entry point called directly (prepared ctypes calls, back to back)."""
     res = {}
     for i, name in enumerate(names):
         N, K = WORKLOADS[name]
@@ -204,16 +230,21 @@ def measure_shapes(torch, synth, q4, names, steps, warmup, rotate_gb, dev):
         x1 = x16[:1].contiguous()
         y16 = torch.empty((16, N), dtype=torch.float32, device=dev)
         y1 = torch.empty((1, N), dtype=torch.float32, device=dev)
-        call = q4.q4_gemm_verify_tiled
-        n = max(10, min(steps, int(20e3 / (9 * N * K / 16 / 5e6))))
-        a, _ = time_calls(torch, call, x16, Wts, y16, 16, N, K, n, warmup)
-        b, _ = time_calls(torch, call, x1, Wts, y1, 1, N, K, n, warmup)
-        c, _ = time_calls(torch, call, x16, Wts, y16, 16, N, K, n, warmup)
+        ws = q4.workspace_for(16, N, K, dev)
+        f16 = raw_calls(torch, q4, "q4_gemm_verify_tiled_ws", x16, Wts, y16,
+                        16, N, K, ws)
+        f1 = raw_calls(torch, q4, "q4_gemm_verify_tiled_ws", x1, Wts, y1,
+                       1, N, K, ws)
+        n = max(20, min(steps, int(20e3 / (9 * N * K / 16 / 5e6))))
+        a, _ = time_raw(torch, f16, n, warmup)
+        b, _ = time_raw(torch, f1, n, warmup)
+        c, _ = time_raw(torch, f16, n, warmup)
         m16 = 0.5 * (a + c)
-        plan = q4.q4_gemm_verify_plan(16, N, K, q4.LAYOUT_TILED16)
+        plan = q4.q4_gemm_verify_tiled_ws_plan(16, N, K)
         rec = {"N": N, "K": K, "weight_bytes": 9 * N * K // 16,
                "copies": len(Wts), "steps": n,
                "kernel": KERNEL_NAMES[plan["kernel"]],
+               "k_parts": plan["k_parts"],
                "us_m1": round(b * 1e3, 3), "us_m16": round(m16 * 1e3, 3),
                "gbps_m1": round(alg_bytes(1, N, K) / (b * 1e-3) / 1e9, 1),
                "gbps_m16": round(alg_bytes(16, N, K) / (m16 * 1e-3) / 1e9, 1),
@@ -222,7 +253,7 @@ def measure_shapes(torch, synth, q4, names, steps, warmup, rotate_gb, dev):
         rec["frac_m16"] = round(rec["gbps_m16"] / HBM_PEAK_GBPS, 4)
         log(f"shape {name}: {rec}")
         res[name] = rec
-        del Wts, x16, x1, y16, y1
+        del Wts, x16, x1, y16, y1, ws
         torch.cuda.empty_cache()
     return res
 
@@ -265,7 +296,13 @@ def measure_full_pass(torch, synth, q4, reps, dev):
           for K in {k for _, k in WORKLOADS.values()}}
     ys = {n: torch.empty((16, N), dtype=torch.float32, device=dev)
           for n, (N, _) in WORKLOADS.items()}
+    # calls run in order on one stream, so one workspace serves them all
+    need = max(q4.q4_gemm_verify_tiled_ws_plan(16, N, K)["workspace_bytes"]
+               for N, K in WORKLOADS.values())
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     out = {"calls": len(calls), "weight_bytes": wbytes,
+           "entry_point": "q4_gemm_verify_tiled_ws (K > 5120 split across "
+                          "workgroups)",
            "graph": "one HIP graph per M, replayed back to back"}
     graphs = {}
     for M in (16, 1):
@@ -274,8 +311,8 @@ def measure_full_pass(torch, synth, q4, reps, dev):
         def run_pass(M=M, x_m=x_m):
             for name, layer in calls:
                 N, K = WORKLOADS[name]
-                q4.q4_gemm_verify_tiled(x_m[K], weights[(name, layer)],
-                                        ys[name][:M], M, N, K)
+                q4.q4_gemm_verify_tiled_ws(x_m[K], weights[(name, layer)],
+                                           ys[name][:M], M, N, K, ws)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -307,13 +344,32 @@ def measure_full_pass(torch, synth, q4, reps, dev):
         b = sum(alg_bytes(M, *WORKLOADS[n]) for n, _ in calls)
         rec = out.setdefault(key, {"alg_bytes": b, "ms": []})
         rec["ms"].append(ms)
+    import functools
+    lib = q4.load()
+    stream = torch.cuda.current_stream().cuda_stream
     for M in (16, 1):
         rec = out[f"M={M}"]
         ms = sum(rec["ms"]) / len(rec["ms"])
         rec["ms"] = round(ms, 4)
         rec["gbps"] = round(rec["alg_bytes"] / (ms * 1e-3) / 1e9, 1)
         rec["frac_of_peak"] = round(rec["gbps"] / HBM_PEAK_GBPS, 4)
-        rec["eager_ms"] = round(timed(graphs[M][1], max(2, reps // 4)), 4)
+        x_m = {K: v[:M].contiguous() for K, v in xs.items()}
+        fns = [functools.partial(
+            lib.q4_gemm_verify_tiled_ws, x_m[WORKLOADS[n][1]].data_ptr(),
+            weights[(n, layer)].data_ptr(), ys[n].data_ptr(), M,
+            WORKLOADS[n][0], WORKLOADS[n][1], ws.data_ptr(), ws.numel(),
+            stream) for n, layer in calls]
+
+        bad = [st for st in (f() for f in fns) if st != 0]
+        if bad:
+            raise RuntimeError(f"q4_gemm_verify_tiled_ws returned {bad[0]}")
+
+        def eager(fns=fns):
+            for f in fns:
+                f()
+        rec["eager_ms"] = round(timed(eager, max(2, reps // 2)), 4)
+        rec["eager"] = ("the same 258 calls launched directly "
+                        "(prepared C-ABI calls)")
     out["ratio_m16_m1"] = round(out["M=16"]["ms"] / out["M=1"]["ms"], 4)
     log(f"full pass: {out}")
     del weights, graphs
@@ -401,20 +457,18 @@ def main():
                                             / 1e9, 1)}
     log(f"repack: {repack}")
 
-    tiled = q4.q4_gemm_verify_tiled
-    planar = q4.q4_gemm_verify
     # timed steps: tiled M = 16 (the step), then M = 1, then M = 16 again
     # (A-B-A order for the ratio); then the planar kernel at M = 16 and 1
-    ms16a, wall16 = time_calls(torch, tiled, x16, Wts, y16, Mv, N, K,
-                               args.steps, args.warmup)
-    ms1, wall1 = time_calls(torch, tiled, x1, Wts, y1, 1, N, K, args.steps,
-                            args.warmup)
-    ms16b, _ = time_calls(torch, tiled, x16, Wts, y16, Mv, N, K, args.steps,
-                          args.warmup)
-    pms16, _ = time_calls(torch, planar, x16, Ws, y16, Mv, N, K, args.steps,
-                          args.warmup)
-    pms1, _ = time_calls(torch, planar, x1, Ws, y1, 1, N, K, args.steps,
-                         args.warmup)
+    t16 = raw_calls(torch, q4, "q4_gemm_verify_tiled", x16, Wts, y16, Mv,
+                    N, K)
+    t1 = raw_calls(torch, q4, "q4_gemm_verify_tiled", x1, Wts, y1, 1, N, K)
+    ms16a, wall16 = time_raw(torch, t16, args.steps, args.warmup)
+    ms1, wall1 = time_raw(torch, t1, args.steps, args.warmup)
+    ms16b, _ = time_raw(torch, t16, args.steps, args.warmup)
+    p16 = raw_calls(torch, q4, "q4_gemm_verify", x16, Ws, y16, Mv, N, K)
+    p1 = raw_calls(torch, q4, "q4_gemm_verify", x1, Ws, y1, 1, N, K)
+    pms16, _ = time_raw(torch, p16, args.steps, args.warmup)
+    pms1, _ = time_raw(torch, p1, args.steps, args.warmup)
     ms_per_step = ms16a
     k16 = 0.5 * (ms16a + ms16b)
     gbps16 = b16 / (ms_per_step * 1e-3) / 1e9
@@ -489,8 +543,9 @@ def main():
             "traffic": traffic,
             "kernel": KERNEL_NAMES[plan["kernel"]],
             "kernel_us": round(k16 * 1e3, 3),
-            "timing": "HIP events around back-to-back launches on the "
-                      "launch stream, mean of the two M=16 blocks",
+            "timing": "HIP events around back-to-back launches (prepared "
+                      "C-ABI calls) on the launch stream, mean of the two "
+                      "M=16 blocks",
             "alg_bytes_per_launch": b16,
         },
         "cpu_baseline": cpu,

@@ -2,6 +2,7 @@
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -120,6 +121,11 @@ def q4_pack_layout(N: int, K: int, layout_id: int = LAYOUT_PLANAR) -> dict:
     return {name: getattr(out, name) for name, _ in _Layout._fields_}
 
 
+@functools.lru_cache(maxsize=256)
+def _total_bytes(N: int, K: int, layout_id: int) -> int:
+    return q4_pack_layout(N, K, layout_id)["total_bytes"]
+
+
 def q4_gemm_verify_plan(M: int, N: int, K: int,
                         layout_id: int = LAYOUT_PLANAR) -> dict:
     """The launch plan q4_gemm_verify (layout 0) or q4_gemm_verify_tiled
@@ -181,7 +187,7 @@ def q4_gemm_verify(x, W, y, M: int, N: int, K: int, stream=None) -> None:
     [M, N]; all on the same GPU.  Enqueued on ``stream`` (default: torch's
     current stream)."""
     import torch
-    total = q4_pack_layout(N, K)["total_bytes"]
+    total = _total_bytes(int(N), int(K), LAYOUT_PLANAR)
     px = _ptr(x, "x", torch.bfloat16, shape=(M, K))
     pw = _ptr(W, "W", torch.uint8, numel=total)
     py = _ptr(y, "y", torch.float32, shape=(M, N))
@@ -197,7 +203,7 @@ def q4_gemm_verify_tiled(x, Wt, y, M: int, N: int, K: int,
                          stream=None) -> None:
     """y[M, N] = x[M, K] @ W^T with W repacked by q4_repack."""
     import torch
-    total = q4_pack_layout(N, K, LAYOUT_TILED16)["total_bytes"]
+    total = _total_bytes(int(N), int(K), LAYOUT_TILED16)
     px = _ptr(x, "x", torch.bfloat16, shape=(M, K))
     pw = _ptr(Wt, "Wt", torch.uint8, numel=total)
     py = _ptr(y, "y", torch.float32, shape=(M, N))
@@ -215,7 +221,7 @@ def q4_gemm_verify_tiled_ws(x, Wt, y, M: int, N: int, K: int, ws=None,
     of at least the plan's workspace_bytes, or None when that is 0), which
     lets K > 5120 be split across workgroups."""
     import torch
-    total = q4_pack_layout(N, K, LAYOUT_TILED16)["total_bytes"]
+    total = _total_bytes(int(N), int(K), LAYOUT_TILED16)
     px = _ptr(x, "x", torch.bfloat16, shape=(M, K))
     pw = _ptr(Wt, "Wt", torch.uint8, numel=total)
     py = _ptr(y, "y", torch.float32, shape=(M, N))
@@ -236,7 +242,7 @@ def q4_gemm_verify_tiled_ws(x, Wt, y, M: int, N: int, K: int, ws=None,
 def q4_repack(W, Wt, N: int, K: int, stream=None) -> None:
     """Reorder planar W into the tiled layout Wt (same byte count)."""
     import torch
-    total = q4_pack_layout(N, K, LAYOUT_TILED16)["total_bytes"]
+    total = _total_bytes(int(N), int(K), LAYOUT_TILED16)
     pw = _ptr(W, "W", torch.uint8, numel=total)
     pt = _ptr(Wt, "Wt", torch.uint8, numel=total)
     if W.device != Wt.device:
@@ -249,7 +255,7 @@ def q4_repack(W, Wt, N: int, K: int, stream=None) -> None:
 def q4_dequant(W, W_out, N: int, K: int, stream=None) -> None:
     """W_out[N, K] fp32 = dequantised packed W."""
     import torch
-    total = q4_pack_layout(N, K)["total_bytes"]
+    total = _total_bytes(int(N), int(K), LAYOUT_PLANAR)
     pw = _ptr(W, "W", torch.uint8, numel=total)
     po = _ptr(W_out, "W_out", torch.float32, shape=(N, K))
     if W.device != W_out.device:

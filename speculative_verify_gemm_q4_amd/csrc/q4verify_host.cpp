@@ -146,7 +146,11 @@ bool plan_resident(int M, int64_t N, int64_t K, int cus, int parts,
 }
 
 q4_plan plan_gemm_tiled_ws(int M, int64_t N, int64_t K, int cus) {
-  if (K > kResidentMaxK) {
+  // Split when the activations of all of K exceed the LDS -- except for
+  // K <= 2 x 5120 at M < 8, where (measured on MI355X, attention output
+  // projection 5120 x 6144) the streaming kernel is as fast without the
+  // second launch.
+  if (K > kResidentMaxK && (M >= 8 || K > 2 * kResidentMaxK)) {
     // Parts of K taken by separate workgroups: enough for a part's
     // activations to fit the LDS, and at least 4, a power of two, so that
     // the 320 tiles of the N = 5120 projections give every CU whole tiles.

@@ -348,9 +348,15 @@ def test_resident_lds_layout_gives_each_lane_its_operand(M, K):
                                    (16, 5120, 6144), (3, 5120, 17408),
                                    (1, 16, 5376), (16, 48, 10240),
                                    (5, 1600, 7168), (16, 256, 65536),
-                                   (9, 32, 5632), (4, 5120, 17408)])
+                                   (9, 32, 5632), (4, 5120, 17408),
+                                   (1, 16, 10496), (8, 1600, 7168)])
 def test_workspace_plan_split_parts(M, N, K):
     p = q4.q4_gemm_verify_tiled_ws_plan(M, N, K)
+    # split when K > 5120 and (M >= 8 or K > 10240); otherwise the plain plan
+    if not (M >= 8 or K > 10240):
+        assert p == q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_TILED16)
+        assert p["workspace_bytes"] == 0
+        return
     assert p["kernel"] == q4.KERNEL_TILED_RESIDENT and p["k_parts"] > 1
     P = p["k_parts"]
     assert P >= 4 and P & (P - 1) == 0 and -(-(K // 256) // P) <= 20
