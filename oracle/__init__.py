@@ -19,6 +19,9 @@ Functions and the passages they follow:
   article, section "Why Apple silicon, and why not the M5": verify rows make
   decode an M x K x N GEMM; qwen-spec page, Notes: the matmul that multiplies
   all rows at once).
+* :mod:`oracle.sample` -- the verify step's sampling epilogue: top-k
+  candidates, target probabilities, the accept test and the residual draw
+  (``verify_sample.c``).
 """
 from __future__ import annotations
 
@@ -55,10 +58,16 @@ def compile_source(src: str, out: str, extra=()) -> str:
     return out
 
 
+SAMPLE_SOURCE = os.path.join(_HERE, "verify_sample.c")
+SAMPLE_LIB_PATH = os.path.join(_HERE, "libverifysample.so")
+
+
 def build(force: bool = True) -> str:
-    """Compile the oracle (plain IEEE arithmetic, no FMA contraction)."""
+    """Compile the oracles (plain IEEE arithmetic, no FMA contraction)."""
     if force or not os.path.exists(LIB_PATH):
         compile_source(SOURCE, LIB_PATH)
+    if force or not os.path.exists(SAMPLE_LIB_PATH):
+        compile_source(SAMPLE_SOURCE, SAMPLE_LIB_PATH)
     return LIB_PATH
 
 
