@@ -255,6 +255,65 @@ int q4_gemm_verify_tiled_ws(const void *x, const void *W_tiled, float *y,
  */
 int q4_gemm_verify_tiled_ws_plan(int M, int64_t N, int64_t K, q4_plan *out);
 
+/* ------------------------------------------------------------------------
+ * Verify sampling epilogue: the step after the LM head in a verify pass
+ * (Splash engine article, section "Exact, up to top-32"; qwen-spec page, the
+ * fused sampling kernel and the paragraph on sampling).  For each of the M
+ * verify rows of logits:
+ *   1. candidates: the top_k largest logits, larger first, equal logits by
+ *      smaller token index;
+ *   2. target probabilities p over them: softmax at `temperature`, cut to
+ *      the shortest prefix whose mass reaches top_p, renormalised (0 for
+ *      tokens outside it); temperature 0 is greedy (p = 1 on the argmax);
+ *   3. the drafted token d is accepted when u * q(d) < p(d), q(d) being the
+ *      draft's probability of d (0 if d is not among the row's draft
+ *      candidates);
+ *   4. otherwise the emitted token is drawn from max(p - q, 0), normalised:
+ *      the first candidate (in candidate order, skipping zero residuals)
+ *      whose cumulative residual exceeds v * R, R the residual mass; with no
+ *      residual mass the same rule is applied to p.
+ * Arithmetic is fp32; random numbers are inputs.
+ * ------------------------------------------------------------------------ */
+#define Q4_SAMPLE_MAX_TOPK 32
+#define Q4_SAMPLE_MAX_DRAFT 16
+#define Q4_SAMPLE_MAX_ROWS 1024
+
+typedef struct {
+  float temperature; /* >= 0, finite; 0 = greedy                          */
+  float top_p;       /* (0, 1]                                              */
+  int32_t top_k;     /* 1 .. Q4_SAMPLE_MAX_TOPK, at most V                 */
+  int32_t draft_k;   /* draft candidates per row, 0 .. Q4_SAMPLE_MAX_DRAFT */
+} q4_sample_params;
+
+/* Device workspace bytes q4_verify_sample needs for (M, V).
+ * Errors: Q4_EINVAL (M outside 1..Q4_SAMPLE_MAX_ROWS, V < 1 or V >= 2^31). */
+int q4_verify_sample_workspace(int M, int64_t V, uint64_t *bytes);
+
+/*
+ * q4_verify_sample -- steps 1-4 above for M rows.  Device pointers (caller
+ * owned, row-major):
+ *   logits [M][V] fp32 (4-byte aligned; must not hold NaN);
+ *   draft_tok [M] int32; draft_idx [M][draft_k] int32 and draft_q
+ *   [M][draft_k] fp32 (may be NULL when draft_k == 0); u, v [M] fp32 in
+ *   [0, 1);
+ *   outputs top_idx [M][top_k] int32, top_val [M][top_k] fp32 (the
+ *   candidates' logits; -0 reported as +0, the two being equal and tied),
+ *   top_prob [M][top_k] fp32 (p), greedy [M] int32 (the
+ *   argmax), accept [M] int32 (0/1), token [M] int32 (the emitted token);
+ *   workspace of at least q4_verify_sample_workspace bytes, 8-byte aligned.
+ * prm is a host pointer, read before the call returns.  Two kernels are
+ * enqueued on `stream`.
+ * Errors: Q4_EINVAL (sizes, parameters, NULL pointers, small workspace),
+ * Q4_EALIGN, Q4_EDEVICE, Q4_ELAUNCH.
+ */
+int q4_verify_sample(const float *logits, int M, int64_t V,
+                     const q4_sample_params *prm, const int32_t *draft_tok,
+                     const int32_t *draft_idx, const float *draft_q,
+                     const float *u, const float *v, int32_t *top_idx,
+                     float *top_val, float *top_prob, int32_t *greedy,
+                     int32_t *accept, int32_t *token, void *workspace,
+                     uint64_t workspace_bytes, void *stream);
+
 /* Human-readable name of a q4_status value (static string, never NULL). */
 const char *q4_status_string(int status);
 

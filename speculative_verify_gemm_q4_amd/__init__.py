@@ -16,6 +16,9 @@ Functions (same names as the C entry points):
   (K split across workgroups for K > 5120); :func:`workspace_for` sizes it.
 * :func:`q4_gemm_verify_plan`, :func:`q4_gemm_verify_tiled_ws_plan` -- launch
   plans of a shape.
+* :func:`q4_verify_sample` (:func:`verify_sample` allocates its outputs) --
+  the verify sampling epilogue over the LM head's logits: top-k candidates,
+  target probabilities, the accept test and the residual draw.
 * :func:`q4_dequant` -- fp32 weights of a packed matrix (test hook).
 * :func:`q4_stream_read`, :func:`q4_stream_copy` -- bandwidth probes.
 * :func:`q4_status_string` -- name of a status code.
@@ -25,7 +28,9 @@ from ._lib import (GROUP, KERNEL_PLANAR, KERNEL_TILED_RESIDENT,
                    LIB_PATH, lib_exports, load, q4_dequant, q4_gemm_verify,
                    q4_gemm_verify_plan, q4_gemm_verify_tiled,
                    q4_gemm_verify_tiled_ws, q4_gemm_verify_tiled_ws_plan,
-                   q4_pack_layout, workspace_for,
+                   q4_pack_layout, q4_verify_sample,
+                   q4_verify_sample_workspace, verify_sample,
+                   workspace_for,
                    q4_repack, q4_status_string, q4_stream_copy,
                    q4_stream_read)
 
@@ -34,6 +39,7 @@ __all__ = ["GROUP", "KERNEL_PLANAR", "KERNEL_TILED_RESIDENT",
            "LIB_PATH", "lib_exports", "load", "q4_dequant", "q4_gemm_verify",
            "q4_gemm_verify_plan", "q4_gemm_verify_tiled",
            "q4_gemm_verify_tiled_ws", "q4_gemm_verify_tiled_ws_plan",
-           "q4_pack_layout", "workspace_for",
+           "q4_pack_layout", "q4_verify_sample",
+           "q4_verify_sample_workspace", "verify_sample", "workspace_for",
            "q4_repack", "q4_status_string", "q4_stream_copy",
            "q4_stream_read"]

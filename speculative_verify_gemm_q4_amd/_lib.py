@@ -42,6 +42,11 @@ class _Layout(ctypes.Structure):
                 ("record_bytes", ctypes.c_uint64)]
 
 
+class _SampleParams(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("top_p", ctypes.c_float),
+                ("top_k", ctypes.c_int32), ("draft_k", ctypes.c_int32)]
+
+
 class _Plan(ctypes.Structure):
     _fields_ = [("grid", ctypes.c_uint32), ("block", ctypes.c_uint32),
                 ("row_tiles", ctypes.c_uint32),
@@ -82,6 +87,13 @@ _SIGNATURES = {
     "q4_gemm_verify_tiled_ws_plan": ([ctypes.c_int, ctypes.c_int64,
                                       ctypes.c_int64, ctypes.POINTER(_Plan)],
                                      ctypes.c_int),
+    "q4_verify_sample_workspace": ([ctypes.c_int, ctypes.c_int64,
+                                    ctypes.POINTER(ctypes.c_uint64)],
+                                   ctypes.c_int),
+    "q4_verify_sample": ([ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                          ctypes.POINTER(_SampleParams)] +
+                         [ctypes.c_void_p] * 12 +
+                         [ctypes.c_uint64, ctypes.c_void_p], ctypes.c_int),
     "q4_status_string": ([ctypes.c_int], ctypes.c_char_p),
 }
 
@@ -237,6 +249,75 @@ def q4_gemm_verify_tiled_ws(x, Wt, y, M: int, N: int, K: int, ws=None,
                                         pws, nws, _stream_handle(stream))
     if st != OK:
         raise Q4Error(st, "q4_gemm_verify_tiled_ws")
+
+
+def q4_verify_sample_workspace(M: int, V: int) -> int:
+    """Workspace bytes q4_verify_sample needs for M rows of V logits."""
+    out = ctypes.c_uint64(0)
+    st = load().q4_verify_sample_workspace(int(M), int(V), ctypes.byref(out))
+    if st != OK:
+        raise Q4Error(st, f"q4_verify_sample_workspace({M}, {V})")
+    return out.value
+
+
+def q4_verify_sample(logits, temperature: float, top_p: float, top_k: int,
+                     draft_tok, draft_idx, draft_q, u, v, top_idx, top_val,
+                     top_prob, greedy, accept, token, ws,
+                     stream=None) -> None:
+    """The verify sampling epilogue over logits [M, V] (fp32): top-k
+    candidates, target probabilities, accept test and residual draw (see
+    include/q4verify.h).  draft_idx / draft_q are [M, draft_k] (int32 /
+    fp32) or None; u, v [M] fp32; outputs top_idx / top_val / top_prob
+    [M, top_k], greedy / accept / token [M]; ws a uint8 device tensor of at
+    least q4_verify_sample_workspace(M, V) bytes."""
+    import torch
+    M, V = logits.shape
+    k = int(top_k)
+    kd = 0 if draft_idx is None else int(draft_idx.shape[1])
+    pl = _ptr(logits, "logits", torch.float32)
+    pdt = _ptr(draft_tok, "draft_tok", torch.int32, numel=M)
+    pdi = pdq = None
+    if kd:
+        pdi = _ptr(draft_idx, "draft_idx", torch.int32, shape=(M, kd))
+        pdq = _ptr(draft_q, "draft_q", torch.float32, shape=(M, kd))
+    pu = _ptr(u, "u", torch.float32, numel=M)
+    pv = _ptr(v, "v", torch.float32, numel=M)
+    pti = _ptr(top_idx, "top_idx", torch.int32, shape=(M, k))
+    ptv = _ptr(top_val, "top_val", torch.float32, shape=(M, k))
+    ptp = _ptr(top_prob, "top_prob", torch.float32, shape=(M, k))
+    pg = _ptr(greedy, "greedy", torch.int32, numel=M)
+    pa = _ptr(accept, "accept", torch.int32, numel=M)
+    pt = _ptr(token, "token", torch.int32, numel=M)
+    pws = _ptr(ws, "ws", torch.uint8)
+    prm = _SampleParams(float(temperature), float(top_p), k, kd)
+    st = load().q4_verify_sample(pl, int(M), int(V), ctypes.byref(prm), pdt,
+                                 pdi, pdq, pu, pv, pti, ptv, ptp, pg, pa, pt,
+                                 pws, ws.numel(), _stream_handle(stream))
+    if st != OK:
+        raise Q4Error(st, "q4_verify_sample")
+
+
+def verify_sample(logits, temperature: float, top_p: float, top_k: int,
+                  draft_tok, draft_idx, draft_q, u, v, stream=None) -> dict:
+    """q4_verify_sample with its outputs and workspace allocated here
+    (torch tensors on the logits' device); returns the outputs by name."""
+    import torch
+    M, V = logits.shape
+    dev = logits.device
+    out = {"top_idx": torch.empty((M, top_k), dtype=torch.int32, device=dev),
+           "top_val": torch.empty((M, top_k), dtype=torch.float32, device=dev),
+           "top_prob": torch.empty((M, top_k), dtype=torch.float32,
+                                   device=dev),
+           "greedy": torch.empty(M, dtype=torch.int32, device=dev),
+           "accept": torch.empty(M, dtype=torch.int32, device=dev),
+           "token": torch.empty(M, dtype=torch.int32, device=dev)}
+    ws = torch.empty(q4_verify_sample_workspace(M, V), dtype=torch.uint8,
+                     device=dev)
+    q4_verify_sample(logits, temperature, top_p, top_k, draft_tok, draft_idx,
+                     draft_q, u, v, out["top_idx"], out["top_val"],
+                     out["top_prob"], out["greedy"], out["accept"],
+                     out["token"], ws, stream)
+    return out
 
 
 def q4_repack(W, Wt, N: int, K: int, stream=None) -> None:

@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libq4verify.so")
 SOURCES = [os.path.join(CSRC, "q4verify_host.cpp"),
-           os.path.join(CSRC, "q4verify_kernels.hip")]
+           os.path.join(CSRC, "q4verify_kernels.hip"),
+           os.path.join(CSRC, "q4verify_sample.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

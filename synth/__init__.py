@@ -112,3 +112,31 @@ def from_bf16_bits(bits, device="cpu") -> torch.Tensor:
     import numpy as np
     arr = np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)
     return torch.from_numpy(arr.copy()).view(torch.bfloat16).to(device)
+
+
+def sample_inputs(M: int, V: int, draft_k: int, seed: int = 0,
+                  stream: int = 0, device="cpu") -> dict:
+    """Inputs of the verify sampling epilogue beside the logits, seeded:
+    per row draft_k distinct draft candidate tokens (uniform over the
+    vocabulary), their probabilities q (Dirichlet(1), float32), the drafted
+    token drawn from q, and the uniforms u, v in [0, 1) (float32)."""
+    import numpy as np
+    rng = np.random.default_rng(stream_seed(seed, 7, stream))
+    out = {}
+    if draft_k:
+        idx = np.stack([rng.choice(V, size=draft_k, replace=False)
+                        for _ in range(M)]).astype(np.int32)
+        q = rng.dirichlet(np.ones(draft_k), size=M).astype(np.float32)
+        pick = np.array([rng.choice(draft_k, p=q[m] / q[m].sum())
+                         for m in range(M)])
+        tok = idx[np.arange(M), pick]
+    else:
+        idx = np.zeros((M, 0), dtype=np.int32)
+        q = np.zeros((M, 0), dtype=np.float32)
+        tok = rng.integers(0, V, size=M).astype(np.int32)
+    out["draft_idx"] = torch.from_numpy(idx).to(device)
+    out["draft_q"] = torch.from_numpy(q).to(device)
+    out["draft_tok"] = torch.from_numpy(tok.astype(np.int32)).to(device)
+    out["u"] = torch.from_numpy(rng.random(M).astype(np.float32)).to(device)
+    out["v"] = torch.from_numpy(rng.random(M).astype(np.float32)).to(device)
+    return out

@@ -159,6 +159,41 @@ def test_workspace_gemm_argument_errors(lib):
     assert p["workspace_bytes"] == (p["k_parts"] - 1) * 3 * 5120 * 4
 
 
+def test_verify_sample_argument_errors(lib):
+    """Sizes and sampling parameters are rejected before device work."""
+    from speculative_verify_gemm_q4_amd._lib import _SampleParams
+    n = ctypes.c_uint64(0)
+    w = lib.q4_verify_sample_workspace
+    assert w(16, 248320, ctypes.byref(n)) == 0 and n.value == 16 * 16 * 32 * 8
+    assert w(0, 100, ctypes.byref(n)) == -1
+    assert w(1025, 100, ctypes.byref(n)) == -1
+    assert w(1, 0, ctypes.byref(n)) == -1
+    assert w(1, 1 << 31, ctypes.byref(n)) == -1
+    f = lib.q4_verify_sample
+    P = [0x10000 + 0x1000 * i for i in range(12)]   # fake device pointers
+    WS, NWS = 0x90000, 4096
+
+    def call(M=2, V=1000, T=1.0, top_p=0.9, k=20, kd=4, ptrs=P, ws=WS,
+             nws=NWS):
+        prm = _SampleParams(T, top_p, k, kd)
+        return f(ptrs[0], M, V, ctypes.byref(prm), *ptrs[1:], ws, nws, None)
+    assert call(k=0) == -1 and call(k=33) == -1 and call(V=10, k=11) == -1
+    assert call(kd=17) == -1 and call(kd=-1) == -1
+    assert call(T=-1.0) == -1 and call(T=float("nan")) == -1
+    assert call(T=float("inf")) == -1
+    assert call(top_p=0.0) == -1 and call(top_p=1.5) == -1
+    assert call(M=0) == -1 and call(M=1025) == -1
+    assert call(nws=2 * 1 * 32 * 8 - 8) == -1
+    assert call(ws=0) == -1
+    bad = list(P)
+    bad[2] = 0                                        # draft_idx NULL, kd > 0
+    assert call(ptrs=bad) == -1
+    bad = list(P)
+    bad[0] = P[0] + 2                                 # logits misaligned
+    assert call(ptrs=bad) == -2
+    assert call(ws=WS + 4) == -2
+
+
 def test_dequant_and_probe_argument_errors(lib):
     d = lib.q4_dequant
     assert d(0x10000, 0x20000, 0, 64, None) == -1
