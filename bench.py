@@ -261,6 +261,56 @@ def measure_shapes(torch, synth, q4, names, steps, warmup, rotate_gb, dev):
 # The 27B model's projection list: 16 attention and 48 gated-DeltaNet layers,
 # each with its input and output projection and the MLP (gate+up, down), and
 # the LM head called twice (draft readout, then verify) on the same weights.
+def measure_verify_sample(torch, synth, q4, dev, steps, warmup):
+    """The sampling epilogue on the LM head's logits (16 rows x 248320,
+    top_k 20, top_p 0.95, temperature 1, 16 draft candidates per row), alone
+    and after the LM head GEMM (one verify step's tail), as prepared C-ABI
+    calls back to back."""
+    import ctypes
+    import functools
+    from speculative_verify_gemm_q4_amd._lib import _SampleParams
+    M, (V, K) = 16, WORKLOADS["lm_head"]
+    lib = q4.load()
+    gen = torch.Generator(device=dev).manual_seed(0)
+    logits = torch.randn((M, V), generator=gen, device=dev) * 3.0
+    inp = synth.sample_inputs(M, V, 16, seed=0, device=dev)
+    out = q4.verify_sample(logits, 1.0, 0.95, 20, inp["draft_tok"],
+                           inp["draft_idx"], inp["draft_q"], inp["u"],
+                           inp["v"])
+    ws = torch.empty(q4.q4_verify_sample_workspace(M, V), dtype=torch.uint8,
+                     device=dev)
+    prm = _SampleParams(1.0, 0.95, 20, 16)
+    stream = torch.cuda.current_stream().cuda_stream
+    args = [logits.data_ptr(), M, V, ctypes.byref(prm)] + [
+        t.data_ptr() for t in (inp["draft_tok"], inp["draft_idx"],
+                               inp["draft_q"], inp["u"], inp["v"],
+                               out["top_idx"], out["top_val"],
+                               out["top_prob"], out["greedy"], out["accept"],
+                               out["token"])] + [ws.data_ptr(), ws.numel(),
+                                                 stream]
+    f = functools.partial(lib.q4_verify_sample, *args)
+    if f() != 0:
+        raise RuntimeError("q4_verify_sample failed")
+    ms, _ = time_raw(torch, [f], steps, warmup)
+    rec = {"M": M, "V": V, "top_k": 20, "draft_k": 16,
+           "us": round(ms * 1e3, 3), "logits_bytes": M * V * 4,
+           "gbps": round(M * V * 4 / (ms * 1e-3) / 1e9, 1)}
+    # the LM head GEMM writing those logits, then the epilogue
+    Wts = rotated_tiled(torch, synth, q4, V, K, 1.2, 9000, dev)
+    x = synth.activations(M, K, seed=0, stream=300, device=dev)
+    g = raw_calls(torch, q4, "q4_gemm_verify_tiled", x, Wts, logits, M, V, K)
+    steps2 = max(10, steps // 8)
+    ms_g, _ = time_raw(torch, g, steps2, max(2, warmup // 8))
+    both = [lambda gi=gi: (gi(), f()) for gi in g]
+    ms_b, _ = time_raw(torch, both, steps2, max(2, warmup // 8))
+    rec["lm_head_us"] = round(ms_g * 1e3, 3)
+    rec["lm_head_plus_sample_us"] = round(ms_b * 1e3, 3)
+    log(f"verify sample: {rec}")
+    del Wts
+    torch.cuda.empty_cache()
+    return rec
+
+
 def pass_calls():
     calls = []
     for layer in range(64):
@@ -494,6 +544,10 @@ def main():
     if not args.no_shapes:
         shapes = measure_shapes(torch, synth, q4, [n for n in WORKLOADS],
                                 args.steps, args.warmup, args.rotate_gb, dev)
+    vsample = None
+    if not args.no_shapes:
+        vsample = measure_verify_sample(torch, synth, q4, dev, args.steps,
+                                        args.warmup)
     full = None
     if not args.no_full_pass:
         full = measure_full_pass(torch, synth, q4, args.pass_reps, dev)
@@ -550,6 +604,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "shapes": shapes,
+        "verify_sample": vsample,
         "full_pass": full,
         "stamp": st,
     }

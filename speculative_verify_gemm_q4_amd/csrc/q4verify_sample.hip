@@ -23,9 +23,10 @@
 //     cascade leaves the best 32 in lanes 0..31).  The 16 lists are merged
 //     pairwise through LDS and the slice's best 32 written out.
 //  2. sample_rows_kernel: one workgroup per row merges the slices' lists the
-//     same way, writes the top_k candidates, and lane 0 evaluates the
-//     probabilities, the accept test and the residual draw in candidate
-//     order, in fp32.
+//     same way and writes the top_k candidates; then lane i of wave 0 takes
+//     candidate i and the probabilities, the accept test and the residual
+//     draw are evaluated in fp32 with wave reductions, lane scans and
+//     ballots over the candidates in order.
 #include <hip/hip_runtime.h>
 
 #include "q4v_internal.h"
@@ -75,15 +76,73 @@ __device__ __forceinline__ uint64_t sort64_desc(uint64_t key, int lane) {
   return key;
 }
 
+// Every lane takes the value of lane - 1; lane 0 takes UINT64_MAX (DPP
+// wave shift, two 32-bit moves).
+__device__ __forceinline__ uint64_t shift_down_one(uint64_t x) {
+  constexpr int kWaveShr1 = 0x138;
+  const uint32_t lo = __builtin_amdgcn_update_dpp(
+      0xFFFFFFFFu, static_cast<uint32_t>(x), kWaveShr1, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(
+      0xFFFFFFFFu, static_cast<uint32_t>(x >> 32), kWaveShr1, 0xF, 0xF, false);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t read_lane64(uint64_t x, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(x), l);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(x >> 32), l);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Sum over the wave (a fixed butterfly order, so repeatable).
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int j = 32; j > 0; j >>= 1) x += __shfl_xor(x, j, 64);
+  return x;
+}
+
+// Inclusive prefix sum over lanes 0..l.
+__device__ __forceinline__ float lane_scan(float x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 1; j < 64; j <<= 1) {
+    const float y = __shfl_up(x, j, 64);
+    if (lane >= j) x += y;
+  }
+  return x;
+}
+
+// Insert one key (wave-uniform, not already present) into the descending
+// list of lanes 0..31: lanes past its place take their predecessor's key.
+__device__ __forceinline__ uint64_t insert_key(uint64_t list, uint64_t key) {
+  const uint64_t prev = shift_down_one(list);
+  const bool gt = key > list;
+  return gt ? (key < prev ? key : prev) : list;
+}
+
 // list: lanes 0..31 hold the best 32 so far, descending (lanes 32..63
-// unused).  Merge one chunk of 64 keys (one per lane, any order) into it.
+// unused).  Merge one chunk of 64 keys (one per lane, any order) into it:
+// keys that beat the list's 32nd entry are inserted one by one when few,
+// else the chunk is sorted with a bitonic network and merged (the list and
+// the chunk's best 32 reversed form a bitonic sequence of 64, whose
+// half-cleaner cascade leaves the best 32 in lanes 0..31).
 __device__ __forceinline__ uint64_t merge_chunk(uint64_t list, uint64_t chunk,
                                                 int lane) {
-  // skip the chunk when nothing in it beats the list's 32nd entry
-  const uint64_t floor32 = __shfl(list, 31, 64);
-  if (__ballot(chunk > floor32) == 0) return list;
+  uint64_t floor32 = read_lane64(list, 31);
+  uint64_t mask = __ballot(chunk > floor32);
+  if (mask == 0) return list;
+  if (__builtin_popcountll(mask) <= 12) {
+    while (mask != 0) {
+      const int b = __builtin_ctzll(mask);
+      mask &= mask - 1;
+      const uint64_t key = read_lane64(chunk, b);
+      if (key > floor32) {
+        list = insert_key(list, key);
+        floor32 = read_lane64(list, 31);
+      }
+    }
+    return list;
+  }
   const uint64_t c = sort64_desc(chunk, lane);
-  // lanes 32..63 take the chunk's best 32 in ascending order: a bitonic 64
   const uint64_t rev = __shfl(c, 63 - lane, 64);
   uint64_t key = lane < 32 ? list : rev;
 #pragma unroll
@@ -96,20 +155,21 @@ __device__ __forceinline__ uint64_t merge_chunk(uint64_t list, uint64_t chunk,
 }
 
 // Best 32 of the keys get(i), i in [begin, end), for one wave: chunks of
-// 64, four chunks' loads issued together before they are merged.
+// 64, sixteen chunks' loads issued together before they are merged.
 template <typename Get>
 __device__ __forceinline__ uint64_t wave_topk(Get get, int64_t begin,
                                               int64_t end, int lane) {
   uint64_t list = 0;  // empty entries (key 0) sort after every real key
-  for (int64_t b = begin; b < end; b += 4 * 64) {
-    uint64_t key[4];
+  constexpr int kGroup = 16;
+  for (int64_t b = begin; b < end; b += kGroup * 64) {
+    uint64_t key[kGroup];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < kGroup; ++c) {
       const int64_t i = b + 64 * c + lane;
       key[c] = i < end ? get(i) : 0;
     }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) list = merge_chunk(list, key[c], lane);
+    for (int c = 0; c < kGroup; ++c) list = merge_chunk(list, key[c], lane);
   }
   return list;
 }
@@ -172,8 +232,10 @@ __global__ __launch_bounds__(64 * kWaves) void sample_rows_kernel(
     int32_t *__restrict__ greedy, int32_t *__restrict__ accept,
     int32_t *__restrict__ token) {
   __shared__ uint64_t lists[kWaves][kTopMax];
-  __shared__ float val[kTopMax], p[kTopMax], r[kTopMax];
+  __shared__ float val[kTopMax], qc[kTopMax];
   __shared__ int32_t tok[kTopMax];
+  __shared__ int32_t sdi[kDraftMax];
+  __shared__ float sdq[kDraftMax];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int m = blockIdx.x;
@@ -185,91 +247,77 @@ __global__ __launch_bounds__(64 * kWaves) void sample_rows_kernel(
   list = block_merge<kWaves>(list, lists, wave, lane);
   if (wave != 0) return;
   const int k = a.top_k;
+  // the row's draft list, one entry per lane, then q of every candidate
+  if (lane < a.draft_k) {
+    sdi[lane] = draft_idx[m * a.draft_k + lane];
+    sdq[lane] = draft_q[m * a.draft_k + lane];
+  }
+  const int32_t d = draft_tok[m];
+  const float um = u[m], vm = v[m];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   if (lane < k) {
     val[lane] = key_value(list);
     tok[lane] = static_cast<int32_t>(key_token(list));
     top_idx[m * k + lane] = tok[lane];
     top_val[m * k + lane] = val[lane];
+    float q = 0.0f;  // the first matching draft entry, as the scan finds it
+    for (int j = a.draft_k - 1; j >= 0; --j)
+      if (sdi[j] == tok[lane]) q = sdq[j];
+    qc[lane] = q;
   }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  if (lane != 0) return;
+  float qd = 0.0f;  // q of the drafted token
+  for (int j = a.draft_k - 1; j >= 0; --j)
+    if (sdi[j] == d) qd = sdq[j];
 
-  // target probabilities, in candidate order
+  // Lane i < k holds candidate i.  Sums are wave reductions and cumulative
+  // sums lane scans over the candidates in order (fp32).
+  const bool live = lane < k;
+  const float vi = live ? val[lane] : 0.0f;
+  const int32_t ti = live ? tok[lane] : -1;
+  const float qi = live ? qc[lane] : 0.0f;
+  const float v0 = val[0];
+  float pi;
   if (a.temperature == 0.0f) {
-    p[0] = 1.0f;
-    for (int i = 1; i < k; ++i) p[i] = 0.0f;
+    pi = lane == 0 ? 1.0f : 0.0f;
   } else {
-    float z = 0.0f;
-    for (int i = 0; i < k; ++i) {
-      p[i] = expf((val[i] - val[0]) / a.temperature);
-      z += p[i];
-    }
-    for (int i = 0; i < k; ++i) p[i] /= z;
-    int keep = k;
-    float c = 0.0f;
-    for (int i = 0; i < k; ++i) {
-      c += p[i];
-      if (c >= a.top_p) {
-        keep = i + 1;
-        break;
-      }
-    }
-    float kept = 0.0f;
-    for (int i = 0; i < keep; ++i) kept += p[i];
-    for (int i = 0; i < k; ++i) p[i] = i < keep ? p[i] / kept : 0.0f;
+    const float w = live ? expf((vi - v0) / a.temperature) : 0.0f;
+    pi = w / wave_sum(w);
+    // keep the shortest prefix whose mass reaches top_p
+    const float c = lane_scan(pi);
+    const uint64_t reach = __ballot(live && c >= a.top_p);
+    const int keep = reach ? __builtin_ctzll(reach) + 1 : k;
+    const float kept = __shfl(c, keep - 1, 64);
+    pi = lane < keep ? pi / kept : 0.0f;
   }
-  for (int i = 0; i < k; ++i) top_prob[m * k + i] = p[i];
-  greedy[m] = tok[0];
+  if (live) top_prob[m * k + lane] = pi;
+  if (lane == 0) greedy[m] = tok[0];
 
   // accept test of the drafted token
-  const int32_t d = draft_tok[m];
-  const int32_t *di = draft_idx + m * a.draft_k;
-  const float *dq = draft_q + m * a.draft_k;
-  auto qof = [&](int32_t t) {
-    for (int j = 0; j < a.draft_k; ++j)
-      if (di[j] == t) return dq[j];
-    return 0.0f;
-  };
-  float pd = 0.0f;
-  for (int i = 0; i < k; ++i)
-    if (tok[i] == d) pd = p[i];
-  const bool ok = u[m] * qof(d) < pd;
-  accept[m] = ok;
+  const uint64_t at_d = __ballot(live && ti == d);
+  const float pd = at_d ? __shfl(pi, __builtin_ctzll(at_d), 64) : 0.0f;
+  const bool ok = um * qd < pd;
+  if (lane == 0) accept[m] = ok;
   if (ok) {
-    token[m] = d;
+    if (lane == 0) token[m] = d;
     return;
   }
 
-  // residual draw: first candidate whose cumulative residual exceeds v R
-  float R = 0.0f;
-  for (int i = 0; i < k; ++i) {
-    const float qi = qof(tok[i]);
-    r[i] = p[i] > qi ? p[i] - qi : 0.0f;
-    R += r[i];
-  }
+  // residual draw: the first candidate whose cumulative residual exceeds
+  // v R (zero residuals skipped); with no residual mass, the same on p
+  float ri = live && pi > qi ? pi - qi : 0.0f;
+  float R = wave_sum(ri);
   if (!(R > 0.0f)) {
-    for (int i = 0; i < k; ++i) r[i] = p[i];
+    ri = pi;
     R = 1.0f;
   }
-  const float target = v[m] * R;
-  int pick = -1;
-  float c = 0.0f;
-  for (int i = 0; i < k; ++i) {
-    if (r[i] <= 0.0f) continue;
-    c += r[i];
-    if (c > target) {
-      pick = i;
-      break;
-    }
-  }
-  if (pick < 0)
-    for (int i = k - 1; i >= 0; --i)
-      if (r[i] > 0.0f) {
-        pick = i;
-        break;
-      }
-  token[m] = tok[pick];
+  const float cr = lane_scan(ri);
+  const uint64_t past = __ballot(ri > 0.0f && cr > vm * R);
+  const uint64_t pos = __ballot(ri > 0.0f);
+  const int pick = past ? __builtin_ctzll(past) : 63 - __builtin_clzll(pos);
+  const int32_t drawn = __shfl(ti, pick, 64);  // every lane takes part
+  if (lane == 0) token[m] = drawn;
 }
 
 int slices_for(int64_t V) {
