@@ -42,6 +42,7 @@ extern "C" {
 #define Q4_ABI_VERSION 1u
 #define Q4_GROUP 64     /* inputs per scale/bias group                     */
 #define Q4_MAX_ROWS 16  /* largest activation block M of q4_gemm_verify     */
+#define Q4_MAX_ROWS_TILED 32 /* of the tiled calls: two MFMA row tiles    */
 
 typedef enum {
   Q4_OK = 0,
@@ -154,6 +155,9 @@ int q4_repack(const void *W_planar, void *W_tiled, int64_t N, int64_t K,
  * For K <= 5120 the activations are first copied once per workgroup into
  * LDS (Q4_KERNEL_TILED_RESIDENT); larger K loads them per record
  * (Q4_KERNEL_TILED_STREAM).  q4_gemm_verify_plan reports which.
+ * M may be up to Q4_MAX_ROWS_TILED = 32 (two MFMA row tiles multiplying the
+ * same unpacked weights, the Splash engine's multi-lane shapes) when
+ * K <= 2560; larger K at M > 16 needs q4_gemm_verify_tiled_ws.
  *   x, y, M, stream: as q4_gemm_verify.
  *   W_tiled : device, Q4_LAYOUT_TILED16 of an N x K matrix, 16-byte aligned.
  *   N % 16 == 0, K % 256 == 0, K <= 2^26 (else Q4_EINVAL).
@@ -208,7 +212,8 @@ typedef struct {
   uint32_t lds_bytes;    /* LDS per workgroup                               */
   uint32_t k_parts;      /* parts of K taken by separate workgroups; > 1
                             only on the workspace path                      */
-  uint32_t reserved;     /* 0                                               */
+  uint32_t m_tiles;      /* 16-row MFMA tiles of the activation block (1 for
+                            M <= 16, 2 for M <= 32)                         */
   uint64_t workspace_bytes; /* device workspace the call needs (0: none)    */
 } q4_plan;
 
@@ -236,7 +241,8 @@ int q4_gemm_verify_plan(int M, int64_t N, int64_t K, uint32_t layout_id,
  * partial products into the workspace, and a second kernel adds them to y in
  * part order, so results are deterministic and do not depend on M.  For
  * K <= 5120 it runs exactly what q4_gemm_verify_tiled runs.
- *   x, W_tiled, y, M, N, K, stream: as q4_gemm_verify_tiled.
+ *   x, W_tiled, y, M, N, K, stream: as q4_gemm_verify_tiled, with M up to
+ *               Q4_MAX_ROWS_TILED for any K.
  *   workspace : device, 16-byte aligned, at least workspace_bytes as
  *               reported by q4_gemm_verify_tiled_ws_plan for (M, N, K); may
  *               be NULL when that is 0.  Overwritten; must not overlap x, W

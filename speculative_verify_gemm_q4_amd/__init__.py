@@ -24,7 +24,8 @@ Functions (same names as the C entry points):
 * :func:`q4_status_string` -- name of a status code.
 """
 from ._lib import (GROUP, KERNEL_PLANAR, KERNEL_TILED_RESIDENT,
-                   KERNEL_TILED_STREAM, LAYOUT_PLANAR, LAYOUT_TILED16, MAX_ROWS, Q4Error,
+                   KERNEL_TILED_STREAM, LAYOUT_PLANAR, LAYOUT_TILED16, MAX_ROWS,
+                   MAX_ROWS_TILED, Q4Error,
                    LIB_PATH, lib_exports, load, q4_dequant, q4_gemm_verify,
                    q4_gemm_verify_plan, q4_gemm_verify_tiled,
                    q4_gemm_verify_tiled_ws, q4_gemm_verify_tiled_ws_plan,
@@ -35,7 +36,8 @@ from ._lib import (GROUP, KERNEL_PLANAR, KERNEL_TILED_RESIDENT,
                    q4_stream_read)
 
 __all__ = ["GROUP", "KERNEL_PLANAR", "KERNEL_TILED_RESIDENT",
-           "KERNEL_TILED_STREAM", "LAYOUT_PLANAR", "LAYOUT_TILED16", "MAX_ROWS", "Q4Error",
+           "KERNEL_TILED_STREAM", "LAYOUT_PLANAR", "LAYOUT_TILED16", "MAX_ROWS",
+           "MAX_ROWS_TILED", "Q4Error",
            "LIB_PATH", "lib_exports", "load", "q4_dequant", "q4_gemm_verify",
            "q4_gemm_verify_plan", "q4_gemm_verify_tiled",
            "q4_gemm_verify_tiled_ws", "q4_gemm_verify_tiled_ws_plan",

@@ -10,6 +10,7 @@ LIB_PATH = os.path.join(PKG, "libq4verify.so")
 
 GROUP = 64
 MAX_ROWS = 16
+MAX_ROWS_TILED = 32
 LAYOUT_PLANAR = 0
 LAYOUT_TILED16 = 1
 KERNEL_PLANAR = 0
@@ -53,7 +54,7 @@ class _Plan(ctypes.Structure):
                 ("tiles_per_wave", ctypes.c_uint32),
                 ("k_splits", ctypes.c_uint32), ("lookahead", ctypes.c_uint32),
                 ("kernel", ctypes.c_uint32), ("lds_bytes", ctypes.c_uint32),
-                ("k_parts", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("k_parts", ctypes.c_uint32), ("m_tiles", ctypes.c_uint32),
                 ("workspace_bytes", ctypes.c_uint64)]
 
 

@@ -12,7 +12,7 @@ namespace q4v {
 // NULL pointers, alignment and 64-bit overflow.  Return Q4_OK or an error.
 int check_matrix_shape(int64_t N, int64_t K);
 int check_gemm_args(const void *x, const void *W, const float *y, int M,
-                    int64_t N, int64_t K);
+                    int64_t N, int64_t K, int max_rows = Q4_MAX_ROWS);
 int check_dequant_args(const void *W, const float *W_out, int64_t N,
                        int64_t K);
 int check_stream_args(const void *a, const void *b, uint64_t bytes);
@@ -36,7 +36,7 @@ constexpr int kRecordBytes = kTileRows * kRecordGroups * 36;
 // K whose 16 activation rows fit in it as bf16.
 constexpr int kLdsBytes = 163840;
 constexpr int kResidentMaxK = kLdsBytes / 32;
-constexpr int kResidentMaxRecords = kResidentMaxK / 256;  // per part of K
+constexpr int kResidentMaxRecords = kResidentMaxK / 256;  // per part, M <= 16
 // Waves per workgroup and register stages of the resident-activation kernel.
 constexpr int kResidentWaves = 8;
 constexpr int kResidentStages = 2;

@@ -52,8 +52,8 @@ int check_matrix_shape(int64_t N, int64_t K) {
 }
 
 int check_gemm_args(const void *x, const void *W, const float *y, int M,
-                    int64_t N, int64_t K) {
-  if (M < 1 || M > Q4_MAX_ROWS) return Q4_EINVAL;
+                    int64_t N, int64_t K, int max_rows) {
+  if (M < 1 || M > max_rows) return Q4_EINVAL;
   const int st = check_matrix_shape(N, K);
   if (st != Q4_OK) return st;
   if (x == nullptr || W == nullptr || y == nullptr) return Q4_EINVAL;
@@ -108,6 +108,7 @@ q4_plan plan_gemm_planar(int M, int64_t N, int64_t K) {
   p.lookahead = 4;
   p.kernel = Q4_KERNEL_PLANAR;
   p.k_parts = 1;
+  p.m_tiles = 1;
   p.lds_bytes = ksw > 1 ? static_cast<uint32_t>(ksw * ntw * 64 * 16) : 0;
   return p;
 }
@@ -120,7 +121,9 @@ bool plan_resident(int M, int64_t N, int64_t K, int cus, int parts,
                    q4_plan *out) {
   const int64_t tiles = N / kTileRows;
   const int64_t records = K / (kRecordGroups * Q4_GROUP);
-  if (parts < 1 || (records + parts - 1) / parts > kResidentMaxRecords)
+  const int m_tiles = M > Q4_MAX_ROWS ? 2 : 1;
+  if (parts < 1 ||
+      (records + parts - 1) / parts > kResidentMaxRecords / m_tiles)
     return false;
   int64_t gt = cus / parts;
   if (gt < 1) gt = 1;
@@ -139,6 +142,7 @@ bool plan_resident(int M, int64_t N, int64_t K, int cus, int parts,
   p.kernel = Q4_KERNEL_TILED_RESIDENT;
   p.lds_bytes = kLdsBytes;
   p.k_parts = static_cast<uint32_t>(parts);
+  p.m_tiles = static_cast<uint32_t>(m_tiles);
   p.workspace_bytes = static_cast<uint64_t>(parts - 1) *
                       static_cast<uint64_t>(M) * static_cast<uint64_t>(N) * 4;
   *out = p;
@@ -150,13 +154,26 @@ q4_plan plan_gemm_tiled_ws(int M, int64_t N, int64_t K, int cus) {
   // K <= 2 x 5120 at M < 8, where (measured on MI355X, attention output
   // projection 5120 x 6144) the streaming kernel is as fast without the
   // second launch.
+  const int m_tiles = M > Q4_MAX_ROWS ? 2 : 1;
+  const int64_t records = K / (kRecordGroups * Q4_GROUP);
+  const int64_t per_part = kResidentMaxRecords / m_tiles;
+  if (m_tiles == 2 && records > per_part) {
+    // 32 rows: split whenever the activations exceed the LDS, into a power
+    // of two parts (2 for K = 5120, 8 for 17408)
+    int64_t parts = 2;
+    while (parts * per_part < records) parts *= 2;
+    q4_plan p;
+    if (parts <= cus && plan_resident(M, N, K, cus, static_cast<int>(parts), &p))
+      return p;
+    std::memset(&p, 0, sizeof p);  // no plan: the call is rejected
+    return p;
+  }
   if (K > kResidentMaxK && (M >= 8 || K > 2 * kResidentMaxK)) {
     // Parts of K taken by separate workgroups: enough for a part's
     // activations to fit the LDS, and at least 4, a power of two, so that
     // the 320 tiles of the N = 5120 projections give every CU whole tiles.
-    const int64_t records = K / (kRecordGroups * Q4_GROUP);
     int64_t parts = 4;
-    while (parts * kResidentMaxRecords < records) parts *= 2;
+    while (parts * per_part < records) parts *= 2;
     q4_plan p;
     if (parts <= cus && plan_resident(M, N, K, cus, static_cast<int>(parts), &p))
       return p;
@@ -171,6 +188,11 @@ q4_plan plan_gemm_tiled(int M, int64_t N, int64_t K, int cus) {
     // second), each owning whole tiles; its waves split its records evenly.
     q4_plan p;
     if (plan_resident(M, N, K, cus, 1, &p)) return p;
+  }
+  if (M > Q4_MAX_ROWS) {  // 32 rows without a workspace: resident only
+    q4_plan p;
+    std::memset(&p, 0, sizeof p);
+    return p;
   }
   // Tiles per wave: each wave multiplies its activation operand with 1-4
   // tiles, so the activation loads per weight byte fall with more tiles
@@ -194,6 +216,7 @@ q4_plan plan_gemm_tiled(int M, int64_t N, int64_t K, int cus) {
   p.lookahead = kRecordGroups;
   p.kernel = Q4_KERNEL_TILED_STREAM;
   p.k_parts = 1;
+  p.m_tiles = 1;
   p.lds_bytes = ksw > 1 ? static_cast<uint32_t>(ksw * tnt * 64 * 16) : 0;
   return p;
 }
@@ -289,8 +312,9 @@ extern "C" int q4_pack_layout(int64_t N, int64_t K, uint32_t layout_id,
 
 extern "C" int q4_gemm_verify_plan(int M, int64_t N, int64_t K,
                                    uint32_t layout_id, q4_plan *out) {
-  if (out == nullptr || M < 1 || M > Q4_MAX_ROWS) return Q4_EINVAL;
+  if (out == nullptr || M < 1 || M > Q4_MAX_ROWS_TILED) return Q4_EINVAL;
   if (layout_id == Q4_LAYOUT_PLANAR) {
+    if (M > Q4_MAX_ROWS) return Q4_EINVAL;
     const int st = q4v::check_matrix_shape(N, K);
     if (st != Q4_OK) return st;
     *out = q4v::plan_gemm_planar(M, N, K);
@@ -299,7 +323,9 @@ extern "C" int q4_gemm_verify_plan(int M, int64_t N, int64_t K,
   if (layout_id == Q4_LAYOUT_TILED16) {
     const int st = q4v::check_tiled_shape(N, K);
     if (st != Q4_OK) return st;
-    *out = q4v::plan_gemm_tiled(M, N, K, q4v::device_cus());
+    const q4_plan p = q4v::plan_gemm_tiled(M, N, K, q4v::device_cus());
+    if (p.grid == 0) return Q4_EINVAL;
+    *out = p;
     return Q4_OK;
   }
   return Q4_EINVAL;
@@ -307,10 +333,12 @@ extern "C" int q4_gemm_verify_plan(int M, int64_t N, int64_t K,
 
 extern "C" int q4_gemm_verify_tiled_ws_plan(int M, int64_t N, int64_t K,
                                             q4_plan *out) {
-  if (out == nullptr || M < 1 || M > Q4_MAX_ROWS) return Q4_EINVAL;
+  if (out == nullptr || M < 1 || M > Q4_MAX_ROWS_TILED) return Q4_EINVAL;
   const int st = q4v::check_tiled_shape(N, K);
   if (st != Q4_OK) return st;
-  *out = q4v::plan_gemm_tiled_ws(M, N, K, q4v::device_cus());
+  const q4_plan p = q4v::plan_gemm_tiled_ws(M, N, K, q4v::device_cus());
+  if (p.grid == 0) return Q4_EINVAL;
+  *out = p;
   return Q4_OK;
 }
 

@@ -382,7 +382,7 @@ __global__ __launch_bounds__(64 * NTW * KSW) void gemm_tiled_kernel(
 // are issued before record i is multiplied.
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int W, int S>
+template <int W, int S, int RT>
 __global__ __launch_bounds__(64 * W) void gemm_resident_kernel(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ Wt,
     float *__restrict__ y, float *__restrict__ ws, int M, int N, int K,
@@ -404,15 +404,16 @@ __global__ __launch_bounds__(64 * W) void gemm_resident_kernel(
   const int u0 = static_cast<int>(static_cast<int64_t>(U) * wave / W);
   const int u1 = static_cast<int>(static_cast<int64_t>(U) * (wave + 1) / W);
 
-  // activations -> LDS, block f = 8q + 2gi + r copied by wave f % W
+  // activations -> LDS, block f = (4q + gi) 2RT + r (rows 8r .. 8r+7)
+  // copied by wave f % W
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(x), 0,
       static_cast<int>(static_cast<uint32_t>(M) * static_cast<uint32_t>(K) * 2u),
       kBufferWord3);
   const uint32_t xslot =
       (static_cast<uint32_t>(lane >> 3) * K + 8 * (lane & 7)) * 2;
-  for (int f = wave; f < 8 * nq; f += W) {
-    const int q = qa + (f >> 3), gi = (f >> 1) & 3, r = f & 1;
+  for (int f = wave; f < 8 * RT * nq; f += W) {
+    const int q = qa + f / (8 * RT), gi = (f / (2 * RT)) & 3, r = f % (2 * RT);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         xr, (lds_void *)&lds[f * 64], 16,  // address-space cast
         xslot + static_cast<uint32_t>(8 * r) * K * 2,
@@ -460,42 +461,52 @@ __global__ __launch_bounds__(64 * W) void gemm_resident_kernel(
   const u32x4 neg = {kNeg128Pair, kNeg128Pair, kNeg128Pair, kNeg128Pair};
   const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
   const UnpackConsts uc = unpack_consts();
-  auto compute = [&](const Stage &s, int q, f32x4 &acc) {
-    const u32x4 *xf = lds + q * 512 + (j >> 3) * 64 + (j & 7) * 8 + 2 * kb;
+  // Row tile rt (rows 16 rt ..) of lane (j, kb), half h: slot
+  // 8(j%8) + 2kb + h of block (4q + gi) 2RT + 2rt + j/8.  The codes are
+  // unpacked once and multiplied with every row tile.
+  auto compute = [&](const Stage &s, int q, f32x4 (&acc)[RT]) {
+    const u32x4 *xf = lds + q * (512 * RT) + (j >> 3) * 64 + (j & 7) * 8 + 2 * kb;
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
-      const u32x4 a0 = xf[gi * 128];
-      const u32x4 a1 = xf[gi * 128 + 1];
-      f32x4 xn = mfma16x16x32(a0, neg, fzero);
-      xn = mfma16x16x32(a1, neg, xn);
       const u32x4 cw = gi < 2 ? s.c0 : s.c1;
-      const uint32_t w0 = (gi & 1) ? cw.z : cw.x;
-      const uint32_t w1 = (gi & 1) ? cw.w : cw.y;
-      f32x4 tq = mfma16x16x32(a0, unpack_codes(w0, uc), xn);
-      tq = mfma16x16x32(a1, unpack_codes(w1, uc), tq);
+      const u32x4 b0 = unpack_codes((gi & 1) ? cw.z : cw.x, uc);
+      const u32x4 b1 = unpack_codes((gi & 1) ? cw.w : cw.y, uc);
       const uint32_t sbw = s.sb[gi];
       const float sc = __uint_as_float(sbw << 16);
       const float bn = __uint_as_float(sbw & 0xFFFF0000u) * kMinusInv128;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        acc[r] = __builtin_fmaf(bn, xn[r], acc[r]);
-        acc[r] = __builtin_fmaf(sc, tq[r], acc[r]);
+      for (int rt = 0; rt < RT; ++rt) {
+        const u32x4 a0 = xf[(gi * 2 * RT + 2 * rt) * 64];
+        const u32x4 a1 = xf[(gi * 2 * RT + 2 * rt) * 64 + 1];
+        f32x4 xn = mfma16x16x32(a0, neg, fzero);
+        xn = mfma16x16x32(a1, neg, xn);
+        f32x4 tq = mfma16x16x32(a0, b0, xn);
+        tq = mfma16x16x32(a1, b1, tq);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          acc[rt][r] = __builtin_fmaf(bn, xn[r], acc[rt][r]);
+          acc[rt][r] = __builtin_fmaf(sc, tq[r], acc[rt][r]);
+        }
       }
     }
   };
   float *dst = p == 0 ? y : ws + static_cast<uint64_t>(p - 1) * M * N;
-  auto store = [&](int tile, const f32x4 &v) {
+  auto store = [&](int tile, const f32x4 (&v)[RT]) {
     const int n = tile * 16 + j;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = kb * 4 + r;
-      if (m < M) dst[static_cast<uint64_t>(m) * N + n] = v[r];
-    }
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 16 * rt + kb * 4 + r;
+        if (m < M) dst[static_cast<uint64_t>(m) * N + n] = v[rt][r];
+      }
   };
 
   // head: partial sum of a first tile entered past its first record;
   // tail: partial sum of a last tile left before its last record
-  f32x4 acc = fzero, head_sum = fzero, tail_sum = fzero;
+  f32x4 acc[RT], head_sum[RT], tail_sum[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) acc[rt] = head_sum[rt] = tail_sum[rt] = fzero;
   int q = u0 % nq;
   int tl = u0 / nq;
   bool in_head = q != 0;
@@ -508,12 +519,14 @@ __global__ __launch_bounds__(64 * W) void gemm_resident_kernel(
         compute(st[i], q, acc);
         if (++q == nq) {
           if (in_head) {
-            head_sum = acc;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) head_sum[rt] = acc[rt];
             in_head = false;
           } else {
             store(t0 + tl, acc);
           }
-          acc = fzero;
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) acc[rt] = fzero;
           q = 0;
           ++tl;
         }
@@ -522,30 +535,42 @@ __global__ __launch_bounds__(64 * W) void gemm_resident_kernel(
     }
   }
   if (q != 0) {
-    if (in_head)
-      head_sum = acc;
-    else
-      tail_sum = acc;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      if (in_head)
+        head_sum[rt] = acc[rt];
+      else
+        tail_sum[rt] = acc[rt];
+    }
   }
 
   // split tiles: the activations are no longer needed, so their LDS holds
-  // each wave's two partial sums
+  // each wave's two partial sums (slot (2 wave + half) RT + rt)
   __syncthreads();
   f32x4 *part = reinterpret_cast<f32x4 *>(lds);
-  part[(wave * 2 + 0) * 64 + lane] = head_sum;
-  part[(wave * 2 + 1) * 64 + lane] = tail_sum;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    part[((wave * 2 + 0) * RT + rt) * 64 + lane] = head_sum[rt];
+    part[((wave * 2 + 1) * RT + rt) * 64 + lane] = tail_sum[rt];
+  }
   __syncthreads();
   if (nrec > 0) {
     const int lt = (u1 - 1) / nq;
     if (lt * nq >= u0 && lt * nq + nq > u1) {
       // this wave holds lt's first record but not its last: its share is
       // its tail sum, the following waves' shares their head sums
-      f32x4 v = part[(wave * 2 + 1) * 64 + lane];
+      f32x4 v[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        v[rt] = part[((wave * 2 + 1) * RT + rt) * 64 + lane];
       for (int w2 = wave + 1; w2 < W; ++w2) {
         const int a0 = static_cast<int>(static_cast<int64_t>(U) * w2 / W);
         const int a1 = static_cast<int>(static_cast<int64_t>(U) * (w2 + 1) / W);
         if (a0 >= lt * nq + nq) break;
-        if (a1 > a0) v += part[(w2 * 2) * 64 + lane];
+        if (a1 > a0)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+            v[rt] += part[((w2 * 2) * RT + rt) * 64 + lane];
       }
       store(t0 + lt, v);
     }
@@ -704,11 +729,18 @@ int launch_tiled(const q4_plan &p, const void *x, const void *W, float *y,
 int launch_resident(const q4_plan &p, const void *x, const void *W, float *y,
                     float *ws, int M, int N, int K, hipStream_t stream) {
   const int parts = static_cast<int>(p.k_parts);
-  hipLaunchKernelGGL((gemm_resident_kernel<kResidentWaves, kResidentStages>),
-                     dim3(p.grid), dim3(p.block), 0, stream,
-                     static_cast<const uint16_t *>(x),
-                     static_cast<const uint8_t *>(W), y, ws, M, N, K, parts,
-                     static_cast<int>(p.grid) / parts);
+  if (p.m_tiles == 2)
+    hipLaunchKernelGGL((gemm_resident_kernel<kResidentWaves, kResidentStages, 2>),
+                       dim3(p.grid), dim3(p.block), 0, stream,
+                       static_cast<const uint16_t *>(x),
+                       static_cast<const uint8_t *>(W), y, ws, M, N, K, parts,
+                       static_cast<int>(p.grid) / parts);
+  else
+    hipLaunchKernelGGL((gemm_resident_kernel<kResidentWaves, kResidentStages, 1>),
+                       dim3(p.grid), dim3(p.block), 0, stream,
+                       static_cast<const uint16_t *>(x),
+                       static_cast<const uint8_t *>(W), y, ws, M, N, K, parts,
+                       static_cast<int>(p.grid) / parts);
   int st = launch_status();
   if (st != Q4_OK || parts == 1) return st;
   const uint32_t mn4 = static_cast<uint32_t>(M) * static_cast<uint32_t>(N) / 4;
@@ -751,15 +783,16 @@ extern "C" int q4_gemm_verify(const void *x, const void *W, float *y, int M,
 extern "C" int q4_gemm_verify_tiled(const void *x, const void *W, float *y,
                                     int M, int64_t N, int64_t K,
                                     void *stream) {
-  int st = q4v::check_gemm_args(x, W, y, M, N, K);
+  int st = q4v::check_gemm_args(x, W, y, M, N, K, Q4_MAX_ROWS_TILED);
   if (st != Q4_OK) return st;
   st = q4v::check_tiled_shape(N, K);
   if (st != Q4_OK) return st;
+  const q4_plan p = q4v::plan_gemm_tiled(M, N, K, q4v::device_cus());
+  if (p.grid == 0) return Q4_EINVAL;  // M > 16 with K > 2560: needs a workspace
   st = q4v::check_device();
   if (st != Q4_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int n = static_cast<int>(N), k = static_cast<int>(K);
-  const q4_plan p = q4v::plan_gemm_tiled(M, N, K, q4v::device_cus());
   if (p.kernel == Q4_KERNEL_TILED_RESIDENT)
     return q4v::launch_resident(p, x, W, y, nullptr, M, n, k, s);
   const int key = static_cast<int>(p.tiles_per_wave * 100 + p.k_splits);
@@ -783,11 +816,12 @@ extern "C" int q4_gemm_verify_tiled_ws(const void *x, const void *W, float *y,
                                        void *workspace,
                                        uint64_t workspace_bytes,
                                        void *stream) {
-  int st = q4v::check_gemm_args(x, W, y, M, N, K);
+  int st = q4v::check_gemm_args(x, W, y, M, N, K, Q4_MAX_ROWS_TILED);
   if (st != Q4_OK) return st;
   st = q4v::check_tiled_shape(N, K);
   if (st != Q4_OK) return st;
   const q4_plan p = q4v::plan_gemm_tiled_ws(M, N, K, q4v::device_cus());
+  if (p.grid == 0) return Q4_EINVAL;
   if (p.workspace_bytes > 0) {
     if (workspace == nullptr || workspace_bytes < p.workspace_bytes)
       return Q4_EINVAL;

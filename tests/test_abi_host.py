@@ -99,7 +99,10 @@ def test_tiled_shape_rules(lib):
     assert g(X, W, Y, 1, 17, 256, None) == -1
     assert g(X, W, Y, 1, 16, 320, None) == -1
     assert g(X, W, Y, 0, 16, 256, None) == -1
-    assert g(X, W, Y, 17, 16, 256, None) == -1
+    assert g(X, W, Y, 33, 16, 256, None) == -1        # M above 32
+    assert g(X, W, Y, 17, 16, 2816, None) == -1       # M > 16, K > 2560: needs
+    #                                                   the workspace call
+    assert g(X, W, Y, 17, 16, 256, None) == -4        # valid: stops at device
     assert g(X + 8, W, Y, 1, 16, 256, None) == -2
     r = lib.q4_repack
     assert r(W, X, 17, 256, None) == -1

@@ -478,6 +478,77 @@ def test_workspace_full_shape_sampled(q4, name, M):
     assert torch.isfinite(y).all()
 
 
+# -------------------------------------------------------------- 17..32 rows
+
+@pytest.mark.parametrize("M", [17, 20, 24, 31, 32])
+def test_two_row_tiles_tiny(q4, M):
+    """Plain tiled call, K <= 2560: both row tiles from LDS, one split-free
+    pass (the multi-lane shapes of the Splash engine)."""
+    oracle_check(q4, M, 256, 512, 0, "two row tiles", tiled=True)
+
+
+@pytest.mark.parametrize("M,N,K", [(32, 5120, 6144), (24, 48, 10240),
+                                   (17, 16, 5120), (32, 1600, 2560),
+                                   (25, 256, 17408)])
+def test_two_row_tiles_workspace(q4, M, N, K):
+    dev = torch.device("cuda")
+    W = synth.q4_weights(N, K, seed=50, device=dev)
+    x = synth.activations(M, K, seed=50, stream=1, device=dev)
+    p = q4.q4_gemm_verify_tiled_ws_plan(M, N, K)
+    assert p["m_tiles"] == 2
+    _say(f"case two row tiles workspace: M={M} N={N} K={K} "
+         f"parts={p['k_parts']}")
+    y = gemm_tiled_ws(q4, x, repacked(q4, W, N, K), M, N, K)
+    _, y64, a64, _ = oracle.gemm(synth.bf16_bits(x), W.cpu().numpy(), N, K)
+    assert_within_bound(y, y64, a64, f"two row tiles M={M} N={N} K={K}")
+
+
+def test_two_row_tiles_integer_exact_and_M_invariance(q4):
+    """Integer-valued inputs: bitwise equal to the oracle at 32 rows; rows
+    do not depend on M within 17..32 (the same plan and summation order)."""
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(51)
+    N, K = 512, 5120
+    q = rng.integers(0, 16, size=(N, K))
+    G = K // 64
+    codes = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    Wh = assemble(codes, bf16_bits_of(np.ones((N, G))),
+                  bf16_bits_of(np.full((N, G), -8.0)))
+    xi = rng.integers(-4, 5, size=(32, K)).astype(np.float32)
+    Wt = repacked(q4, torch.from_numpy(Wh).to(dev), N, K)
+    x = torch.from_numpy(xi).to(torch.bfloat16).to(dev)
+    _say("case two row tiles integer-exact")
+    y = gemm_tiled_ws(q4, x, Wt, 32, N, K)
+    y32, _, _, _ = oracle.gemm(bf16_bits_of(xi), Wh, N, K)
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), y32.view(np.uint32))
+    W = synth.q4_weights(34816 // 4, K, seed=52, device=dev)
+    Wt = repacked(q4, W, 34816 // 4, K)
+    xr = synth.activations(32, K, seed=52, stream=1, device=dev)
+    full = gemm_tiled_ws(q4, xr, Wt, 32, 34816 // 4, K)
+    for M in (17, 24, 31):
+        part = gemm_tiled_ws(q4, xr[:M].contiguous(), Wt, M, 34816 // 4, K)
+        assert torch.equal(part.view(torch.int32), full[:M].view(torch.int32)), M
+
+
+@pytest.mark.parametrize("name,M", [("gate_up", 32), ("down", 24),
+                                    ("lm_head", 32)])
+def test_two_row_tiles_full_shape_sampled(q4, name, M):
+    dev = torch.device("cuda")
+    N, K = FULL[name]
+    W = synth.q4_weights(N, K, seed=53, stream=list(FULL).index(name),
+                          device=dev)
+    Wt = repacked(q4, W, N, K)
+    x = synth.activations(M, K, seed=53, stream=5000 + M, device=dev)
+    _say(f"case two row tiles full {name}: M={M} N={N} K={K}")
+    y = gemm_tiled_ws(q4, x, Wt, M, N, K)
+    rows = sampled_rows(N, 160, seed=M + 9)
+    Wsub = sub_matrix(W, N, K, rows)
+    _, y64, a64, _ = oracle.gemm(synth.bf16_bits(x), Wsub, len(rows), K)
+    got = y[:, torch.as_tensor(rows, device=dev)]
+    assert_within_bound(got, y64, a64, f"two row tiles {name} M={M}")
+    assert torch.isfinite(y).all()
+
+
 # -------------------------------------------------------------- probes
 
 def test_stream_probes(q4):

@@ -192,21 +192,22 @@ def resident_model(M, N, K, p):
     takes part p = b // Gt of K (records [Q p / P, Q (p+1) / P)) and the
     tiles [T g / Gt, T (g+1) / Gt) of group g = b % Gt."""
     T, Q = N // 16, K // 256
-    P, W = p["k_parts"], p["block"] // 64
+    P, W, RT = p["k_parts"], p["block"] // 64, p["m_tiles"]
+    assert RT == (2 if M > 16 else 1)
     G = p["grid"]
     assert G % P == 0
     Gt = G // P
     assert p["lds_bytes"] == LDS_BYTES and p["block"] <= 1024
     assert Gt == min(T, max(1, 256 // P))
     assert p["workspace_bytes"] == (P - 1) * M * N * 4
-    assert 2 * W * 1024 <= LDS_BYTES
+    assert 2 * W * RT * 1024 <= LDS_BYTES
     hits = np.zeros((T, Q), dtype=np.int32)
     writes = np.zeros((P, T), dtype=np.int32)
     for b in range(G):
         part, g = b // Gt, b % Gt
         qa, qb = Q * part // P, Q * (part + 1) // P
         nq = qb - qa
-        assert 0 < nq and 8 * nq * 1024 <= LDS_BYTES
+        assert 0 < nq and 8 * RT * nq * 1024 <= LDS_BYTES
         t0, t1 = T * g // Gt, T * (g + 1) // Gt
         U = (t1 - t0) * nq
         rng = [(U * w // W, U * (w + 1) // W) for w in range(W)]
@@ -307,20 +308,23 @@ def test_resident_split_tile_sums_in_wave_order():
     assert np.array_equal(out, want)
 
 
-@pytest.mark.parametrize("M,K", [(1, 256), (16, 256), (5, 1280), (16, 5120)])
+@pytest.mark.parametrize("M,K", [(1, 256), (16, 256), (5, 1280), (16, 5120),
+                                 (17, 256), (32, 2560), (24, 768)])
 def test_resident_lds_layout_gives_each_lane_its_operand(M, K):
-    """Copy side: block f = 8q + 2gi + r, slot s (lane s of the copy) holds
-    inputs 256q + 64gi + 8(s%8) .. +7 of row 8r + s/8, rows >= M zero.  Read
-    side: lane (j, kb), half h reads slot 8(j%8) + 2kb + h of block
-    (q, gi, j/8), and must get inputs 64gi + 16kb + 8h .. +7 of row j of
-    record q (the MFMA A operand of the tiled layout)."""
+    """Copy side: block f = (4q + gi) 2RT + r, slot s (lane s of the copy)
+    holds inputs 256q + 64gi + 8(s%8) .. +7 of row 8r + s/8, rows >= M zero
+    (RT = 2 row tiles when M > 16).  Read side: row tile rt of lane (j, kb),
+    half h reads slot 8(j%8) + 2kb + h of block (4q + gi) 2RT + 2rt + j/8,
+    and must get inputs 64gi + 16kb + 8h .. +7 of row 16 rt + j of record q
+    (the MFMA A operand of the tiled layout)."""
+    RT = 2 if M > 16 else 1
     Q = K // 256
-    x = np.arange(16 * K, dtype=np.int64).reshape(16, K) + 1
+    x = np.arange(32 * K, dtype=np.int64).reshape(32, K) + 1
     x[M:] = 0
-    lds = np.zeros((8 * Q, 64, 8), dtype=np.int64)
+    lds = np.zeros((8 * RT * Q, 64, 8), dtype=np.int64)
     assert lds.size * 2 <= LDS_BYTES
-    for f in range(8 * Q):
-        q, gi, r = f >> 3, (f >> 1) & 3, f & 1
+    for f in range(8 * RT * Q):
+        q, gi, r = f // (8 * RT), (f // (2 * RT)) % 4, f % (2 * RT)
         for s in range(64):
             row = 8 * r + s // 8
             k0 = 256 * q + 64 * gi + 8 * (s % 8)
@@ -333,13 +337,15 @@ def test_resident_lds_layout_gives_each_lane_its_operand(M, K):
     flat = lds.reshape(-1, 8)
     for q in range(Q):
         for gi in range(4):
-            for h in range(2):
-                for lane in range(64):
-                    j, kb = lane & 15, lane >> 4
-                    idx = q * 512 + (j >> 3) * 64 + (j & 7) * 8 + 2 * kb \
-                        + gi * 128 + h
-                    k0 = 256 * q + 64 * gi + 16 * kb + 8 * h
-                    assert np.array_equal(flat[idx], x[j, k0:k0 + 8])
+            for rt in range(RT):
+                for h in range(2):
+                    for lane in range(64):
+                        j, kb = lane & 15, lane >> 4
+                        idx = q * 512 * RT + (j >> 3) * 64 + (j & 7) * 8 \
+                            + 2 * kb + (gi * 2 * RT + 2 * rt) * 64 + h
+                        k0 = 256 * q + 64 * gi + 16 * kb + 8 * h
+                        assert np.array_equal(flat[idx],
+                                              x[16 * rt + j, k0:k0 + 8])
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 5120, 17408), (1, 5120, 6144),
@@ -360,4 +366,30 @@ def test_workspace_plan_split_parts(M, N, K):
     assert p["kernel"] == q4.KERNEL_TILED_RESIDENT and p["k_parts"] > 1
     P = p["k_parts"]
     assert P >= 4 and P & (P - 1) == 0 and -(-(K // 256) // P) <= 20
+    resident_model(M, N, K, p)
+
+
+
+@pytest.mark.parametrize("M,N,K", [(17, 16, 256), (24, 34816, 2560),
+                                   (32, 4096, 1024), (32, 256, 2816)])
+def test_plain_plan_32_rows(M, N, K):
+    """M > 16 without a workspace: the resident kernel when the two row
+    tiles' activations fit the LDS (K <= 2560), otherwise no plan."""
+    if K <= 2560:
+        p = q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_TILED16)
+        assert p["kernel"] == q4.KERNEL_TILED_RESIDENT and p["m_tiles"] == 2
+        resident_model(M, N, K, p)
+    else:
+        with pytest.raises(q4.Q4Error):
+            q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_TILED16)
+
+
+@pytest.mark.parametrize("M,N,K", [(24, 34816, 5120), (32, 5120, 17408),
+                                   (32, 248320, 5120), (17, 5120, 6144),
+                                   (32, 16, 5376), (25, 48, 10240)])
+def test_workspace_plan_32_rows(M, N, K):
+    p = q4.q4_gemm_verify_tiled_ws_plan(M, N, K)
+    assert p["kernel"] == q4.KERNEL_TILED_RESIDENT and p["m_tiles"] == 2
+    P = p["k_parts"]
+    assert P & (P - 1) == 0 and -(-(K // 256) // P) <= 10
     resident_model(M, N, K, p)
