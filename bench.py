@@ -239,6 +239,14 @@ def measure_shapes(torch, synth, q4, names, steps, warmup, rotate_gb, dev):
         a, _ = time_raw(torch, f16, n, warmup)
         b, _ = time_raw(torch, f1, n, warmup)
         c, _ = time_raw(torch, f16, n, warmup)
+        # 32 rows (two MFMA row tiles; K split into parts as needed)
+        x32 = synth.activations(32, K, seed=0, stream=400 + i, device=dev)
+        y32 = torch.empty((32, N), dtype=torch.float32, device=dev)
+        ws32 = q4.workspace_for(32, N, K, dev)
+        f32 = raw_calls(torch, q4, "q4_gemm_verify_tiled_ws", x32, Wts, y32,
+                        32, N, K, ws32)
+        d, _ = time_raw(torch, f32, n, warmup)
+        p32 = q4.q4_gemm_verify_tiled_ws_plan(32, N, K)
         m16 = 0.5 * (a + c)
         plan = q4.q4_gemm_verify_tiled_ws_plan(16, N, K)
         rec = {"N": N, "K": K, "weight_bytes": 9 * N * K // 16,
@@ -251,9 +259,13 @@ def measure_shapes(torch, synth, q4, names, steps, warmup, rotate_gb, dev):
                "ratio_m16_m1": round(m16 / b, 4)}
         rec["frac_m1"] = round(rec["gbps_m1"] / HBM_PEAK_GBPS, 4)
         rec["frac_m16"] = round(rec["gbps_m16"] / HBM_PEAK_GBPS, 4)
+        rec["us_m32"] = round(d * 1e3, 3)
+        rec["gbps_m32"] = round(alg_bytes(32, N, K) / (d * 1e-3) / 1e9, 1)
+        rec["ratio_m32_m1"] = round(d / b, 4)
+        rec["k_parts_m32"] = p32["k_parts"]
         log(f"shape {name}: {rec}")
         res[name] = rec
-        del Wts, x16, x1, y16, y1, ws
+        del Wts, x16, x1, y16, y1, ws, x32, y32, ws32
         torch.cuda.empty_cache()
     return res
 
@@ -342,12 +354,12 @@ def measure_full_pass(torch, synth, q4, reps, dev):
         del W
     torch.cuda.synchronize()
     wbytes = sum(9 * WORKLOADS[n][0] * WORKLOADS[n][1] // 16 for n, _ in calls)
-    xs = {K: synth.activations(16, K, seed=0, stream=200 + K, device=dev)
+    xs = {K: synth.activations(32, K, seed=0, stream=200 + K, device=dev)
           for K in {k for _, k in WORKLOADS.values()}}
-    ys = {n: torch.empty((16, N), dtype=torch.float32, device=dev)
+    ys = {n: torch.empty((32, N), dtype=torch.float32, device=dev)
           for n, (N, _) in WORKLOADS.items()}
     # calls run in order on one stream, so one workspace serves them all
-    need = max(q4.q4_gemm_verify_tiled_ws_plan(16, N, K)["workspace_bytes"]
+    need = max(q4.q4_gemm_verify_tiled_ws_plan(32, N, K)["workspace_bytes"]
                for N, K in WORKLOADS.values())
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     out = {"calls": len(calls), "weight_bytes": wbytes,
@@ -355,7 +367,7 @@ def measure_full_pass(torch, synth, q4, reps, dev):
                           "workgroups)",
            "graph": "one HIP graph per M, replayed back to back"}
     graphs = {}
-    for M in (16, 1):
+    for M in (16, 1, 32):
         x_m = {K: v[:M].contiguous() for K, v in xs.items()}
 
         def run_pass(M=M, x_m=x_m):
@@ -387,7 +399,7 @@ def measure_full_pass(torch, synth, q4, reps, dev):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
-    for M in (16, 1, 16):
+    for M in (16, 1, 16, 32):
         g, run_pass = graphs[M]
         ms = timed(g.replay, reps)
         key = f"M={M}"
@@ -397,7 +409,7 @@ def measure_full_pass(torch, synth, q4, reps, dev):
     import functools
     lib = q4.load()
     stream = torch.cuda.current_stream().cuda_stream
-    for M in (16, 1):
+    for M in (16, 1, 32):
         rec = out[f"M={M}"]
         ms = sum(rec["ms"]) / len(rec["ms"])
         rec["ms"] = round(ms, 4)
@@ -421,6 +433,7 @@ def measure_full_pass(torch, synth, q4, reps, dev):
         rec["eager"] = ("the same 258 calls launched directly "
                         "(prepared C-ABI calls)")
     out["ratio_m16_m1"] = round(out["M=16"]["ms"] / out["M=1"]["ms"], 4)
+    out["ratio_m32_m1"] = round(out["M=32"]["ms"] / out["M=1"]["ms"], 4)
     log(f"full pass: {out}")
     del weights, graphs
     torch.cuda.empty_cache()
