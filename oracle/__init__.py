@@ -22,6 +22,9 @@ Functions and the passages they follow:
 * :mod:`oracle.sample` -- the verify step's sampling epilogue: top-k
   candidates, target probabilities, the accept test and the residual draw
   (``verify_sample.c``).
+* :mod:`oracle.gdn` -- the Gated DeltaNet state of a verify pass: each tree
+  node's output from the shared state plus the updates along its path, and
+  the commit of the accepted path (``gdn_state.c``).
 """
 from __future__ import annotations
 
@@ -60,6 +63,8 @@ def compile_source(src: str, out: str, extra=()) -> str:
 
 SAMPLE_SOURCE = os.path.join(_HERE, "verify_sample.c")
 SAMPLE_LIB_PATH = os.path.join(_HERE, "libverifysample.so")
+GDN_SOURCE = os.path.join(_HERE, "gdn_state.c")
+GDN_LIB_PATH = os.path.join(_HERE, "libgdnstate.so")
 
 
 def build(force: bool = True) -> str:
@@ -68,6 +73,8 @@ def build(force: bool = True) -> str:
         compile_source(SOURCE, LIB_PATH)
     if force or not os.path.exists(SAMPLE_LIB_PATH):
         compile_source(SAMPLE_SOURCE, SAMPLE_LIB_PATH)
+    if force or not os.path.exists(GDN_LIB_PATH):
+        compile_source(GDN_SOURCE, GDN_LIB_PATH)
     return LIB_PATH
 
 
