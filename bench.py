@@ -323,6 +323,60 @@ def measure_verify_sample(torch, synth, q4, dev, steps, warmup):
     return rec
 
 
+GDN_SHAPE = {"layers": 48, "heads": 48, "key_heads": 16, "dv": 128,
+             "dk": 128, "tree_nodes": 16}
+
+
+def gdn_alg_bytes(L, H, Hk, dv, dk, n):
+    """Unique bytes of one commit: the state read and written, the accepted
+    nodes' keys, values, gates and strengths, the path and the count."""
+    return (2 * L * H * dv * dk * 4 + L * n * (Hk * dk + H * dv + 2 * H) * 4
+            + (n + 1) * 4)
+
+
+def measure_gdn_commit(torch, synth, q4, dev, steps, warmup):
+    """The Gated DeltaNet state commit of one step: 48 layers x 48 value
+    heads x 128 x 128 fp32 (147 MiB read and written), a 16-node tree, for
+    accepted paths of 1, 7 and 16 nodes.  Three state copies (453 MB, more
+    than the 256 MB last-level cache) are rotated so that each call streams
+    its state from HBM.  Prepared C-ABI calls back to back, HIP events on the
+    launch stream."""
+    import functools
+    g = GDN_SHAPE
+    L, H, Hk, dv, dk, M = (g["layers"], g["heads"], g["key_heads"], g["dv"],
+                           g["dk"], g["tree_nodes"])
+    lib = q4.load()
+    inp = synth.gdn_inputs(L, H, Hk, M, dv=dv, dk=dk, seed=0, device=dev)
+    states = [inp["S"]] + [inp["S"].clone() for _ in range(2)]
+    stream = torch.cuda.current_stream().cuda_stream
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = {"shape": dict(g), "copies": len(states), "paths": []}
+    for n in (1, 7, 16):
+        path = torch.tensor(list(range(n)) + [0] * (M - n), dtype=torch.int32,
+                            device=dev)
+        cnt = torch.tensor([n], dtype=torch.int32, device=dev)
+        fns = [functools.partial(
+            lib.q4_gdn_commit, S.data_ptr(), L, H, Hk, dv, dk, M,
+            inp["k"].data_ptr(), inp["v"].data_ptr(),
+            inp["alpha"].data_ptr(), inp["beta"].data_ptr(), path.data_ptr(),
+            cnt.data_ptr(), status.data_ptr(), stream) for S in states]
+        if any(f() != 0 for f in fns):
+            raise RuntimeError("q4_gdn_commit failed")
+        torch.cuda.synchronize()
+        if int(status.item()) != 0:
+            raise RuntimeError("q4_gdn_commit rejected its path")
+        ms, _ = time_raw(torch, fns, steps, warmup)
+        nb = gdn_alg_bytes(L, H, Hk, dv, dk, n)
+        gbps = nb / (ms * 1e-3) / 1e9
+        out["paths"].append({"accepted": n, "us": round(ms * 1e3, 3),
+                             "alg_bytes": nb, "gbps": round(gbps, 1),
+                             "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)})
+    log(f"gdn commit: {out}")
+    del states, inp
+    torch.cuda.empty_cache()
+    return out
+
+
 def pass_calls():
     calls = []
     for layer in range(64):
@@ -561,6 +615,10 @@ def main():
     if not args.no_shapes:
         vsample = measure_verify_sample(torch, synth, q4, dev, args.steps,
                                         args.warmup)
+    gdn = None
+    if not args.no_shapes:
+        gdn = measure_gdn_commit(torch, synth, q4, dev, args.steps,
+                                 args.warmup)
     full = None
     if not args.no_full_pass:
         full = measure_full_pass(torch, synth, q4, args.pass_reps, dev)
@@ -618,6 +676,7 @@ def main():
         "cpu_baseline": cpu,
         "shapes": shapes,
         "verify_sample": vsample,
+        "gdn_commit": gdn,
         "full_pass": full,
         "stamp": st,
     }

@@ -320,6 +320,49 @@ int q4_verify_sample(const float *logits, int M, int64_t V,
                      int32_t *accept, int32_t *token, void *workspace,
                      uint64_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Gated DeltaNet state commit.
+ *
+ * A recurrent layer carries one dv x dk fp32 state per value head, read and
+ * written back every step (Splash engine article, section on what one step
+ * reads: 48 layers x 48 value heads x 128 x 128).  After the check, the
+ * accepted tree nodes are written into the state in path order (qwen-spec
+ * page, the hybrid-model paragraph), each by the gated delta rule
+ *     S <- alpha S (I - beta k k^T) + beta v k^T,
+ * k being the node's key for key head h / (H / Hk), v its value for head h,
+ * alpha and beta its gate and writing strength for head h.  Arithmetic is
+ * fp32; the gate is carried as one running factor per head.
+ * ------------------------------------------------------------------------ */
+#define Q4_GDN_DK 128
+#define Q4_GDN_MAX_NODES 32
+
+/* Dynamic LDS bytes of the commit kernel for M tree nodes (informational).
+ * Errors: Q4_EINVAL (M outside 1..Q4_GDN_MAX_NODES, NULL). */
+int q4_gdn_commit_lds_bytes(int M, int *bytes);
+
+/*
+ * q4_gdn_commit -- apply the accepted nodes to every layer's state, in
+ * place.  Device pointers (caller owned, row-major, fp32 unless stated):
+ *   S [L][H][dv][dk] (16-byte aligned): row r of a head's state is value
+ *     index r, column c key index c; read and overwritten;
+ *   k [L][M][Hk][dk] (16-byte aligned), v [L][M][H][dv] (16-byte aligned),
+ *   alpha, beta [L][M][H]: every tree node's key, value, gate, strength;
+ *   path [M] int32: the accepted nodes, root first (entries past the count
+ *     are not read); n_accept: one int32, the count, 0 .. M;
+ *   status: NULL or one int32 that receives Q4_OK, or Q4_EINVAL when the
+ *     count or a read path entry is out of range -- then S is not written.
+ * The count and the path are read on the device: the call may be enqueued
+ * right after the step that decides them.  A count of 0 leaves S unread.
+ * Sizes: dk == Q4_GDN_DK, dv a multiple of 64, Hk divides H,
+ * 1 <= M <= Q4_GDN_MAX_NODES, L * H * dv / 64 < 2^31.  One kernel on
+ * `stream`; calls that overlap on the same S race.
+ * Errors: Q4_EINVAL, Q4_EALIGN, Q4_EDEVICE, Q4_ELAUNCH.
+ */
+int q4_gdn_commit(float *S, int L, int H, int Hk, int dv, int dk, int M,
+                  const float *k, const float *v, const float *alpha,
+                  const float *beta, const int32_t *path,
+                  const int32_t *n_accept, int32_t *status, void *stream);
+
 /* Human-readable name of a q4_status value (static string, never NULL). */
 const char *q4_status_string(int status);
 

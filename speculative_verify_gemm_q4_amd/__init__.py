@@ -19,29 +19,31 @@ Functions (same names as the C entry points):
 * :func:`q4_verify_sample` (:func:`verify_sample` allocates its outputs) --
   the verify sampling epilogue over the LM head's logits: top-k candidates,
   target probabilities, the accept test and the residual draw.
+* :func:`q4_gdn_commit` -- writes a verify pass's accepted tree nodes into
+  the Gated DeltaNet recurrent states of every layer (gated delta rule).
 * :func:`q4_dequant` -- fp32 weights of a packed matrix (test hook).
 * :func:`q4_stream_read`, :func:`q4_stream_copy` -- bandwidth probes.
 * :func:`q4_status_string` -- name of a status code.
 """
-from ._lib import (GROUP, KERNEL_PLANAR, KERNEL_TILED_RESIDENT,
+from ._lib import (GDN_DK, GDN_MAX_NODES, GROUP, KERNEL_PLANAR, KERNEL_TILED_RESIDENT,
                    KERNEL_TILED_STREAM, LAYOUT_PLANAR, LAYOUT_TILED16, MAX_ROWS,
                    MAX_ROWS_TILED, Q4Error,
                    LIB_PATH, lib_exports, load, q4_dequant, q4_gemm_verify,
                    q4_gemm_verify_plan, q4_gemm_verify_tiled,
                    q4_gemm_verify_tiled_ws, q4_gemm_verify_tiled_ws_plan,
-                   q4_pack_layout, q4_verify_sample,
+                   q4_gdn_commit, q4_pack_layout, q4_verify_sample,
                    q4_verify_sample_workspace, verify_sample,
                    workspace_for,
                    q4_repack, q4_status_string, q4_stream_copy,
                    q4_stream_read)
 
-__all__ = ["GROUP", "KERNEL_PLANAR", "KERNEL_TILED_RESIDENT",
+__all__ = ["GDN_DK", "GDN_MAX_NODES", "GROUP", "KERNEL_PLANAR", "KERNEL_TILED_RESIDENT",
            "KERNEL_TILED_STREAM", "LAYOUT_PLANAR", "LAYOUT_TILED16", "MAX_ROWS",
            "MAX_ROWS_TILED", "Q4Error",
            "LIB_PATH", "lib_exports", "load", "q4_dequant", "q4_gemm_verify",
            "q4_gemm_verify_plan", "q4_gemm_verify_tiled",
            "q4_gemm_verify_tiled_ws", "q4_gemm_verify_tiled_ws_plan",
-           "q4_pack_layout", "q4_verify_sample",
+           "q4_gdn_commit", "q4_pack_layout", "q4_verify_sample",
            "q4_verify_sample_workspace", "verify_sample", "workspace_for",
            "q4_repack", "q4_status_string", "q4_stream_copy",
            "q4_stream_read"]

@@ -95,6 +95,10 @@ _SIGNATURES = {
                           ctypes.POINTER(_SampleParams)] +
                          [ctypes.c_void_p] * 12 +
                          [ctypes.c_uint64, ctypes.c_void_p], ctypes.c_int),
+    "q4_gdn_commit_lds_bytes": ([ctypes.c_int, ctypes.POINTER(ctypes.c_int)],
+                                ctypes.c_int),
+    "q4_gdn_commit": ([ctypes.c_void_p] + [ctypes.c_int] * 6 +
+                      [ctypes.c_void_p] * 8, ctypes.c_int),
     "q4_status_string": ([ctypes.c_int], ctypes.c_char_p),
 }
 
@@ -319,6 +323,39 @@ def verify_sample(logits, temperature: float, top_p: float, top_k: int,
                      out["top_prob"], out["greedy"], out["accept"],
                      out["token"], ws, stream)
     return out
+
+
+GDN_DK = 128
+GDN_MAX_NODES = 32
+
+
+def q4_gdn_commit(S, k, v, alpha, beta, path, n_accept, status=None,
+                  stream=None) -> None:
+    """Write the accepted tree nodes into the Gated DeltaNet states, in
+    place (see include/q4verify.h).  S [L, H, dv, dk] fp32; k [L, M, Hk, dk],
+    v [L, M, H, dv], alpha / beta [L, M, H] fp32; path [M] int32 (the
+    accepted nodes, root first); n_accept [1] int32 (their count); status
+    None or [1] int32 (receives 0, or -1 for an out-of-range count or path
+    entry, in which case S is left as it was).  All on the same GPU."""
+    import torch
+    if S.dim() != 4 or k.dim() != 4:
+        raise ValueError("S must be [L, H, dv, dk] and k [L, M, Hk, dk]")
+    L, H, dv, dk = S.shape
+    M, Hk = int(k.shape[1]), int(k.shape[2])
+    pS = _ptr(S, "S", torch.float32)
+    pk = _ptr(k, "k", torch.float32, shape=(L, M, Hk, dk))
+    pv = _ptr(v, "v", torch.float32, shape=(L, M, H, dv))
+    pa = _ptr(alpha, "alpha", torch.float32, shape=(L, M, H))
+    pb = _ptr(beta, "beta", torch.float32, shape=(L, M, H))
+    pp = _ptr(path, "path", torch.int32, numel=M)
+    pn = _ptr(n_accept, "n_accept", torch.int32, numel=1)
+    ps = None if status is None else _ptr(status, "status", torch.int32,
+                                          numel=1)
+    st = load().q4_gdn_commit(pS, int(L), int(H), Hk, int(dv), int(dk), M,
+                              pk, pv, pa, pb, pp, pn, ps,
+                              _stream_handle(stream))
+    if st != OK:
+        raise Q4Error(st, "q4_gdn_commit")
 
 
 def q4_repack(W, Wt, N: int, K: int, stream=None) -> None:

@@ -140,3 +140,46 @@ def sample_inputs(M: int, V: int, draft_k: int, seed: int = 0,
     out["u"] = torch.from_numpy(rng.random(M).astype(np.float32)).to(device)
     out["v"] = torch.from_numpy(rng.random(M).astype(np.float32)).to(device)
     return out
+
+
+def gdn_inputs(L: int, H: int, Hk: int, M: int, dv: int = 128,
+               dk: int = 128, seed: int = 0, stream: int = 0,
+               device="cpu") -> dict:
+    """Seeded inputs of the Gated DeltaNet state step, float32:
+
+    * state S [L, H, dv, dk] ~ N(0, 1);
+    * per layer and tree node: queries and keys [L, M, Hk, dk] drawn N(0, 1)
+      and scaled to unit length (the layer normalises them before the state
+      sees them), values [L, M, H, dv] ~ N(0, 1), gates alpha = exp(-U(0, 2))
+      in (0.135, 1] and strengths beta = sigmoid(N(0, 1)) [L, M, H];
+    * a draft tree of M nodes: parent[0] = -1, parent[i] uniform on
+      -1 .. i-1 with a bias towards i - 1 (long chains, as in a draft tree).
+    """
+    g = _gen(device, seed, 11, stream)
+    f32 = torch.float32
+    S = torch.randn((L, H, dv, dk), generator=g, device=device, dtype=f32)
+    q = torch.randn((L, M, Hk, dk), generator=g, device=device, dtype=f32)
+    k = torch.randn((L, M, Hk, dk), generator=g, device=device, dtype=f32)
+    q = q / q.norm(dim=-1, keepdim=True)
+    k = k / k.norm(dim=-1, keepdim=True)
+    v = torch.randn((L, M, H, dv), generator=g, device=device, dtype=f32)
+    alpha = torch.exp(-2.0 * torch.rand((L, M, H), generator=g,
+                                        device=device, dtype=f32))
+    beta = torch.sigmoid(torch.randn((L, M, H), generator=g, device=device,
+                                     dtype=f32))
+    import numpy as np
+    rng = np.random.default_rng(stream_seed(seed, 12, stream))
+    parent = np.full(M, -1, dtype=np.int32)
+    for i in range(1, M):
+        parent[i] = i - 1 if rng.random() < 0.5 else rng.integers(-1, i)
+    return {"S": S, "q": q, "k": k, "v": v, "alpha": alpha, "beta": beta,
+            "parent": parent}
+
+
+def tree_path(parent, node: int):
+    """Node indices from the tree's root down to ``node`` (inclusive)."""
+    path = []
+    while node >= 0:
+        path.append(int(node))
+        node = int(parent[node])
+    return path[::-1]

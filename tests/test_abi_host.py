@@ -197,6 +197,34 @@ def test_verify_sample_argument_errors(lib):
     assert call(ws=WS + 4) == -2
 
 
+def test_gdn_commit_argument_errors(lib):
+    """Sizes, NULL pointers and alignment are rejected before device work."""
+    n = ctypes.c_int(0)
+    assert lib.q4_gdn_commit_lds_bytes(16, ctypes.byref(n)) == 0
+    assert n.value == 16 * (48 * 16 + 8)
+    assert lib.q4_gdn_commit_lds_bytes(0, ctypes.byref(n)) == -1
+    assert lib.q4_gdn_commit_lds_bytes(33, ctypes.byref(n)) == -1
+    f = lib.q4_gdn_commit
+    P = [0x10000 + 0x1000 * i for i in range(7)]    # fake device pointers
+
+    def call(L=48, H=48, Hk=16, dv=128, dk=128, M=16, ptrs=P, status=None):
+        return f(ptrs[0], L, H, Hk, dv, dk, M, *ptrs[1:], status, None)
+    assert call(M=0) == -1 and call(M=33) == -1
+    assert call(dk=64) == -1 and call(dv=32) == -1 and call(dv=96) == -1
+    assert call(Hk=5) == -1 and call(Hk=0) == -1 and call(H=0) == -1
+    assert call(L=0) == -1
+    assert call(L=1 << 20, H=1 << 12, Hk=1) == -1    # grid beyond 2^31
+    for i in range(7):
+        bad = list(P)
+        bad[i] = 0
+        assert call(ptrs=bad) == -1, i
+    for i, off in ((0, 8), (1, 4), (2, 8), (3, 2), (6, 1)):
+        bad = list(P)
+        bad[i] += off
+        assert call(ptrs=bad) == -2, i
+    assert call(status=0x90002) == -2
+
+
 def test_dequant_and_probe_argument_errors(lib):
     d = lib.q4_dequant
     assert d(0x10000, 0x20000, 0, 64, None) == -1
