@@ -25,6 +25,8 @@ Functions and the passages they follow:
 * :mod:`oracle.gdn` -- the Gated DeltaNet state of a verify pass: each tree
   node's output from the shared state plus the updates along its path, and
   the commit of the accepted path (``gdn_state.c``).
+* :mod:`oracle.attn` -- tree-verify attention over the paged int8 KV cache
+  with the ancestor mask (``tree_attn.c``).
 """
 from __future__ import annotations
 
@@ -65,6 +67,8 @@ SAMPLE_SOURCE = os.path.join(_HERE, "verify_sample.c")
 SAMPLE_LIB_PATH = os.path.join(_HERE, "libverifysample.so")
 GDN_SOURCE = os.path.join(_HERE, "gdn_state.c")
 GDN_LIB_PATH = os.path.join(_HERE, "libgdnstate.so")
+ATTN_SOURCE = os.path.join(_HERE, "tree_attn.c")
+ATTN_LIB_PATH = os.path.join(_HERE, "libtreeattn.so")
 
 
 def build(force: bool = True) -> str:
@@ -75,6 +79,8 @@ def build(force: bool = True) -> str:
         compile_source(SAMPLE_SOURCE, SAMPLE_LIB_PATH)
     if force or not os.path.exists(GDN_LIB_PATH):
         compile_source(GDN_SOURCE, GDN_LIB_PATH)
+    if force or not os.path.exists(ATTN_LIB_PATH):
+        compile_source(ATTN_SOURCE, ATTN_LIB_PATH)
     return LIB_PATH
 
 
