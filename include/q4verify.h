@@ -363,6 +363,65 @@ int q4_gdn_commit(float *S, int L, int H, int Hk, int dv, int dk, int M,
                   const float *beta, const int32_t *path,
                   const int32_t *n_accept, int32_t *status, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Tree-verify attention over the paged int8 KV cache.
+ *
+ * One attention layer of the verify pass.  Every tree node attends to the
+ * context and to its own ancestors, reading the cache in place (qwen-spec
+ * page, Notes and the hybrid-model paragraph).  The layer has Hq query heads
+ * over Hkv KV heads of dimension 256.  A page holds 32 tokens in int8 with
+ * an fp32 scale per token per head (Splash engine article, the model listing
+ * and the paged KV pool).
+ *
+ * The tree's own keys and values sit in the cache right after the context:
+ * node j at logical position ctx_len + j.  Node i sees positions
+ * p < ctx_len, and tree position ctx_len + j when bit j of anc[i] is set
+ * (node j is i or one of its ancestors).  Query head h reads KV head
+ * h / (Hq / Hkv).  The output is softmax(scale * q k^T) v over the visible
+ * positions, with k = k8 * k_scale and v = v8 * v_scale.
+ * Arithmetic: bf16 products on MFMA (the int8 values are exact in bf16), fp32
+ * accumulation, the probabilities rounded to bf16 for the value product.
+ * ------------------------------------------------------------------------ */
+#define Q4_ATTN_HEAD_DIM 256
+#define Q4_ATTN_PAGE 32
+#define Q4_ATTN_MAX_NODES 16
+
+/* The split of the context a call would use, and the workspace it needs.
+ * splits = 0 picks a split for the current device, > 0 asks for that many
+ * runs of pages (at most the number of pages).  The shape rules are those of
+ * q4_tree_attn.  Errors: Q4_EINVAL. */
+int q4_tree_attn_plan(int M, int Hq, int Hkv, int D, int64_t ctx_len,
+                      int splits, int *splits_used, uint64_t *workspace_bytes);
+
+/*
+ * q4_tree_attn -- out[i][h][:] for every tree node i < M and query head h.
+ * Device pointers (caller owned, row-major):
+ *   q [M][Hq][D] bf16, 16-byte aligned;
+ *   k_pages [pool_pages][Hkv][32][D] int8 (keys, token-major) and
+ *   v_pages [pool_pages][Hkv][D][32] int8 (values, stored transposed), both
+ *     16-byte aligned;
+ *   k_scale, v_scale [pool_pages][Hkv][32] fp32, 16-byte aligned;
+ *   page_table [ceil((ctx_len + M) / 32)] int32: logical page -> physical
+ *     page; anc [M] uint32 ancestor-or-self sets;
+ *   out [M][Hq][D] fp32, 16-byte aligned, overwritten;
+ *   workspace: q4_tree_attn_plan's bytes (none when the plan uses one run),
+ *     16-byte aligned;
+ *   status: NULL, or one int32 that receives Q4_EINVAL when a page id is
+ *     outside the pool (it is left as it was otherwise; such a page reads as
+ *     zeros).
+ * Sizes: D == Q4_ATTN_HEAD_DIM, 1 <= M <= Q4_ATTN_MAX_NODES, Hq / Hkv one of
+ * 2, 4, 6, 8; 0 <= ctx_len < 2^31 - 64; scale > 0 and finite.  One or two
+ * kernels on `stream`; calls sharing a workspace race.
+ * Errors: Q4_EINVAL, Q4_EALIGN, Q4_EDEVICE, Q4_ELAUNCH.
+ */
+int q4_tree_attn(const void *q, int M, int Hq, int Hkv, int D,
+                 const int8_t *k_pages, const int8_t *v_pages,
+                 const float *k_scale, const float *v_scale,
+                 const int32_t *page_table, int pool_pages, int64_t ctx_len,
+                 const uint32_t *anc, float scale, float *out, int splits,
+                 void *workspace, uint64_t workspace_bytes, int32_t *status,
+                 void *stream);
+
 /* Human-readable name of a q4_status value (static string, never NULL). */
 const char *q4_status_string(int status);
 

@@ -21,11 +21,13 @@ Functions (same names as the C entry points):
   target probabilities, the accept test and the residual draw.
 * :func:`q4_gdn_commit` -- writes a verify pass's accepted tree nodes into
   the Gated DeltaNet recurrent states of every layer (gated delta rule).
+* :func:`q4_tree_attn`, :func:`tree_attn` -- tree-verify attention of one
+  layer over the paged int8 KV cache with the ancestor mask.
 * :func:`q4_dequant` -- fp32 weights of a packed matrix (test hook).
 * :func:`q4_stream_read`, :func:`q4_stream_copy` -- bandwidth probes.
 * :func:`q4_status_string` -- name of a status code.
 """
-from ._lib import (GDN_DK, GDN_MAX_NODES, GROUP, KERNEL_PLANAR, KERNEL_TILED_RESIDENT,
+from ._lib import (ATTN_HEAD_DIM, ATTN_MAX_NODES, ATTN_PAGE, GDN_DK, GDN_MAX_NODES, GROUP, KERNEL_PLANAR, KERNEL_TILED_RESIDENT,
                    KERNEL_TILED_STREAM, LAYOUT_PLANAR, LAYOUT_TILED16, MAX_ROWS,
                    MAX_ROWS_TILED, Q4Error,
                    LIB_PATH, lib_exports, load, q4_dequant, q4_gemm_verify,
@@ -35,9 +37,10 @@ from ._lib import (GDN_DK, GDN_MAX_NODES, GROUP, KERNEL_PLANAR, KERNEL_TILED_RES
                    q4_verify_sample_workspace, verify_sample,
                    workspace_for,
                    q4_repack, q4_status_string, q4_stream_copy,
-                   q4_stream_read)
+                   q4_stream_read, q4_tree_attn, q4_tree_attn_plan,
+                   tree_attn)
 
-__all__ = ["GDN_DK", "GDN_MAX_NODES", "GROUP", "KERNEL_PLANAR", "KERNEL_TILED_RESIDENT",
+__all__ = ["ATTN_HEAD_DIM", "ATTN_MAX_NODES", "ATTN_PAGE", "GDN_DK", "GDN_MAX_NODES", "GROUP", "KERNEL_PLANAR", "KERNEL_TILED_RESIDENT",
            "KERNEL_TILED_STREAM", "LAYOUT_PLANAR", "LAYOUT_TILED16", "MAX_ROWS",
            "MAX_ROWS_TILED", "Q4Error",
            "LIB_PATH", "lib_exports", "load", "q4_dequant", "q4_gemm_verify",
@@ -46,4 +49,4 @@ __all__ = ["GDN_DK", "GDN_MAX_NODES", "GROUP", "KERNEL_PLANAR", "KERNEL_TILED_RE
            "q4_gdn_commit", "q4_pack_layout", "q4_verify_sample",
            "q4_verify_sample_workspace", "verify_sample", "workspace_for",
            "q4_repack", "q4_status_string", "q4_stream_copy",
-           "q4_stream_read"]
+           "q4_stream_read", "q4_tree_attn", "q4_tree_attn_plan", "tree_attn"]

@@ -99,6 +99,16 @@ _SIGNATURES = {
                                 ctypes.c_int),
     "q4_gdn_commit": ([ctypes.c_void_p] + [ctypes.c_int] * 6 +
                       [ctypes.c_void_p] * 8, ctypes.c_int),
+    "q4_tree_attn_plan": ([ctypes.c_int] * 4 + [ctypes.c_int64, ctypes.c_int,
+                           ctypes.POINTER(ctypes.c_int),
+                           ctypes.POINTER(ctypes.c_uint64)], ctypes.c_int),
+    "q4_tree_attn": ([ctypes.c_void_p] + [ctypes.c_int] * 4 +
+                     [ctypes.c_void_p] * 5 + [ctypes.c_int, ctypes.c_int64,
+                                              ctypes.c_void_p, ctypes.c_float,
+                                              ctypes.c_void_p, ctypes.c_int,
+                                              ctypes.c_void_p, ctypes.c_uint64,
+                                              ctypes.c_void_p, ctypes.c_void_p],
+                     ctypes.c_int),
     "q4_status_string": ([ctypes.c_int], ctypes.c_char_p),
 }
 
@@ -356,6 +366,75 @@ def q4_gdn_commit(S, k, v, alpha, beta, path, n_accept, status=None,
                               _stream_handle(stream))
     if st != OK:
         raise Q4Error(st, "q4_gdn_commit")
+
+
+ATTN_HEAD_DIM = 256
+ATTN_PAGE = 32
+ATTN_MAX_NODES = 16
+
+
+def q4_tree_attn_plan(M: int, Hq: int, Hkv: int, ctx_len: int,
+                      splits: int = 0, D: int = ATTN_HEAD_DIM):
+    """(runs of pages, workspace bytes) of a q4_tree_attn call."""
+    s = ctypes.c_int(0)
+    ws = ctypes.c_uint64(0)
+    st = load().q4_tree_attn_plan(int(M), int(Hq), int(Hkv), int(D),
+                                  int(ctx_len), int(splits), ctypes.byref(s),
+                                  ctypes.byref(ws))
+    if st != OK:
+        raise Q4Error(st, f"q4_tree_attn_plan({M}, {Hq}, {Hkv}, {ctx_len})")
+    return s.value, ws.value
+
+
+def q4_tree_attn(q, k_pages, v_pages, k_scale, v_scale, page_table,
+                 ctx_len: int, anc, scale: float, out, splits: int = 0,
+                 ws=None, status=None, stream=None) -> None:
+    """Tree-verify attention of one layer (see include/q4verify.h).
+    q [M, Hq, D] bf16; k_pages [pool, Hkv, 32, D] int8; v_pages
+    [pool, Hkv, D, 32] int8; k_scale / v_scale [pool, Hkv, 32] fp32;
+    page_table int32 (logical -> physical page); anc [M] int32 holding the
+    uint32 ancestor-or-self sets; out [M, Hq, D] fp32; ws a uint8 tensor of
+    q4_tree_attn_plan's bytes when that is not 0; status None or [1] int32."""
+    import torch
+    M, Hq, D = q.shape
+    pool, Hkv = int(k_pages.shape[0]), int(k_pages.shape[1])
+    pages = (int(ctx_len) + M + ATTN_PAGE - 1) // ATTN_PAGE
+    pq = _ptr(q, "q", torch.bfloat16)
+    pk = _ptr(k_pages, "k_pages", torch.int8, shape=(pool, Hkv, ATTN_PAGE, D))
+    pv = _ptr(v_pages, "v_pages", torch.int8, shape=(pool, Hkv, D, ATTN_PAGE))
+    pks = _ptr(k_scale, "k_scale", torch.float32, shape=(pool, Hkv, ATTN_PAGE))
+    pvs = _ptr(v_scale, "v_scale", torch.float32, shape=(pool, Hkv, ATTN_PAGE))
+    if page_table.numel() < pages:
+        raise ValueError(f"page_table must hold {pages} entries")
+    ppt = _ptr(page_table, "page_table", torch.int32)
+    pa = _ptr(anc, "anc", torch.int32, numel=M)
+    po = _ptr(out, "out", torch.float32, shape=(M, Hq, D))
+    pws, nws = None, 0
+    if ws is not None:
+        pws, nws = _ptr(ws, "ws", torch.uint8), ws.numel()
+    ps = None if status is None else _ptr(status, "status", torch.int32,
+                                          numel=1)
+    st = load().q4_tree_attn(pq, int(M), int(Hq), Hkv, int(D), pk, pv, pks,
+                             pvs, ppt, pool, int(ctx_len), pa, float(scale),
+                             po, int(splits), pws, nws, ps,
+                             _stream_handle(stream))
+    if st != OK:
+        raise Q4Error(st, "q4_tree_attn")
+
+
+def tree_attn(q, k_pages, v_pages, k_scale, v_scale, page_table,
+              ctx_len: int, anc, scale: float, splits: int = 0, status=None,
+              stream=None):
+    """q4_tree_attn with its output and workspace allocated here."""
+    import torch
+    M, Hq, D = q.shape
+    Hkv = int(k_pages.shape[1])
+    _, nws = q4_tree_attn_plan(M, Hq, Hkv, ctx_len, splits, D)
+    out = torch.empty((M, Hq, D), dtype=torch.float32, device=q.device)
+    ws = torch.empty(nws, dtype=torch.uint8, device=q.device) if nws else None
+    q4_tree_attn(q, k_pages, v_pages, k_scale, v_scale, page_table, ctx_len,
+                 anc, scale, out, splits, ws, status, stream)
+    return out
 
 
 def q4_repack(W, Wt, N: int, K: int, stream=None) -> None:

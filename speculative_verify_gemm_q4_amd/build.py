@@ -18,7 +18,8 @@ LIB = os.path.join(PKG, "libq4verify.so")
 SOURCES = [os.path.join(CSRC, "q4verify_host.cpp"),
            os.path.join(CSRC, "q4verify_kernels.hip"),
            os.path.join(CSRC, "q4verify_sample.hip"),
-           os.path.join(CSRC, "q4verify_gdn.hip")]
+           os.path.join(CSRC, "q4verify_gdn.hip"),
+           os.path.join(CSRC, "q4verify_attn.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -1,0 +1,607 @@
+// q4verify_attn.hip -- gfx950 kernels of tree-verify attention over the
+// paged int8 KV cache, and their C-ABI entry points.
+//
+// One attention layer of the verify pass: every tree node (up to 16) and
+// query head attends to the context and to its own ancestors in the tree,
+// reading the cache in place (qwen-spec page, Notes and the hybrid-model
+// paragraph).  Shapes and cache format: 24 query heads over 4 KV heads of
+// dimension 256; pages of 32 tokens, int8, an fp32 scale per token per head
+// (Splash engine article, the model listing and the paged KV pool).  The
+// tree's keys and values follow the context in the cache: node j at
+// position ctx_len + j.
+//
+// Kernel 1 (tree_attn_kernel<G>): a workgroup per (KV head, run of pages),
+// one wave per query head of that KV head (G = Hq / Hkv waves).
+//  * Per page the workgroup loads the 8 KiB of keys ([32 tokens][256]) and
+//    8 KiB of values (stored transposed, [256][32]) with their scales, turns
+//    the int8 values into bf16 (exact: |v| <= 128) and writes them to LDS;
+//    the next page's loads are in flight meanwhile (two LDS buffers).
+//  * Scores on MFMA: S^T[token][node] = K Q^T, sixteen
+//    v_mfma_f32_16x16x32_bf16 per page and wave (two token tiles, eight
+//    32-dim steps), the key scale and the softmax scale applied per token
+//    afterwards; the queries stay in registers for the whole run.
+//  * Online softmax per node in base 2; each node's 32 scores of a page sit
+//    in 4 lanes x 8 registers.  The ancestor mask applies to tree positions,
+//    a 32-bit ancestor-or-self set per node.
+//  * Values on MFMA: O^T[dim][node] += V^T P'^T with P' = p * v_scale in
+//    bf16; the value tile's tokens are stored in the order in which the
+//    score tiles hold them in a lane (tokens 4g..4g+3, 16+4g..16+4g+3 for
+//    lane group g), so the probabilities need no shuffle.
+//  * A run over the whole context writes normalised outputs; otherwise the
+//    run writes its unnormalised output and (max, sum) to the workspace.
+// Kernel 2 (attn_combine_kernel): per (node, query head) the runs' partial
+// results are merged with their max and sum.
+#include <hip/hip_runtime.h>
+
+#include "q4v_internal.h"
+
+namespace q4v {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kD = Q4_ATTN_HEAD_DIM;       // 256
+constexpr int kPage = Q4_ATTN_PAGE;        // 32
+constexpr int kKStride = 2 * kD + 16;      // bytes per token row of bf16 keys
+constexpr int kVStride = 2 * kPage + 16;   // bytes per dim row of bf16 values
+constexpr int kKBytes = kPage * kKStride;  // 16896
+constexpr int kVBytes = kD * kVStride;     // 20480
+constexpr int kBufBytes = kKBytes + kVBytes + 2 * kPage * 4;
+constexpr uint32_t kBufferWord3 = 0x00020000u;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct AttnArgs {
+  const uint16_t *q;
+  const int8_t *kp, *vp;
+  const float *ks, *vs;
+  const int32_t *page_table;
+  const uint32_t *anc;
+  float *out, *part;
+  int32_t *status;
+  int M, Hq, Hkv, pool, ctx, pages, splits;
+  float scale2;  // softmax scale times log2(e)
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p,
+                                                       uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0,
+                                           static_cast<int>(bytes),
+                                           kBufferWord3);
+}
+
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r,
+                                        uint32_t off) {
+  return __builtin_bit_cast(u32x4,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// four int8 -> four bf16 (exact), as two packed pairs
+__device__ __forceinline__ u32x2 i8x4_bf16(uint32_t w) {
+  const bf16x2 a = {static_cast<__bf16>(static_cast<float>(static_cast<int8_t>(w))),
+                    static_cast<__bf16>(static_cast<float>(static_cast<int8_t>(w >> 8)))};
+  const bf16x2 b = {static_cast<__bf16>(static_cast<float>(static_cast<int8_t>(w >> 16))),
+                    static_cast<__bf16>(static_cast<float>(static_cast<int8_t>(w >> 24)))};
+  return u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b),
+                                                 c, 0, 0, 0);
+}
+
+// Raw int8 page in LDS, as the direct-to-LDS copies leave it: keys
+// [32][256], values [256][32], then the 32 key and the 32 value scales, each
+// in a 256-byte area (a scale copy is a whole wave: lanes 32..63 read past
+// the 32 scales and land zeros in the area's second half).
+constexpr int kRawV = kPage * kD;
+constexpr int kRawKS = 2 * kPage * kD;
+constexpr int kRawVS = kRawKS + 256;
+constexpr int kRawBytes = kRawVS + 256;  // 16896
+// Copy instructions per page: 8 of keys and 8 of values (1 KiB each, 64
+// lanes x 16 bytes), one of key scales and one of value scales (32 lanes x
+// 4 bytes); wave w issues instructions w, w + G, w + 2G, ..., and every wave
+// issues the same number per page (past the 18, and for pages past the
+// run, a dummy copy into a pad area), so that one vmcnt value fits every
+// wave.
+constexpr int kCopies = 18;
+constexpr int kRing = 4;          // raw pages in flight per workgroup
+constexpr int kMaxRun = 1024;     // pages per workgroup (ids staged in LDS)
+constexpr int kPadBytes = 1024;
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+// The LDS address of a pointer into a __shared__ array (a C-style cast: the
+// generic-to-LDS address-space cast has no C++ cast spelling).
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_char *)p));
+}
+
+// A buffer resource as four SGPRs (raw, dword format).
+__device__ __forceinline__ u32x4 srd(const void *p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  return u32x4{static_cast<uint32_t>(
+                   __builtin_amdgcn_readfirstlane(static_cast<int>(a))),
+               static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
+                   static_cast<int>((a >> 32) & 0xFFFFu))),
+               static_cast<uint32_t>(
+                   __builtin_amdgcn_readfirstlane(static_cast<int>(bytes))),
+               kBufferWord3};
+}
+
+// Direct-to-LDS copies, written as assembly so that the compiler does not
+// treat them as LDS writes of unknown extent (which would make it wait for
+// every copy in flight before any LDS access): the kernel counts them
+// itself.  Lane l's bytes land at the LDS address `dst` + l * size.  M0 is
+// saved and restored around the copy.
+__device__ __forceinline__ void copy16(u32x4 rs, uint32_t dst, uint32_t voff) {
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "s"(dst), "v"(voff), "s"(rs)
+      : "memory");
+}
+
+__device__ __forceinline__ void copy4(u32x4 rs, uint32_t dst, uint32_t voff) {
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "s"(dst), "v"(voff), "s"(rs)
+      : "memory");
+}
+
+// wait until at most n of this wave's vector memory operations are in flight
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14));
+  asm volatile("" ::: "memory");
+}
+
+// A workgroup barrier for LDS only: this wave's LDS accesses are complete,
+// then s_barrier; the copies still in flight (those of later pages) are not
+// waited for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int G>
+struct Pages {
+  static constexpr int NI = (kCopies + G - 1) / G;  // copies per wave and page
+
+  // page pp (of KV head g) into a raw slot, or, for real == false, NI dummy
+  // copies (of page `dummy`) into the pad; a page id outside the pool reads
+  // as zeros
+  __device__ __forceinline__ static void copy(const AttnArgs &a, int pp,
+                                              bool real, int dummy, int g,
+                                              const char *slot,
+                                              const char *pad, int w,
+                                              int lane) {
+    const int id = real ? pp : dummy;
+    const bool ok = id >= 0 && id < a.pool;
+    const size_t pg = ok ? static_cast<size_t>(id) * a.Hkv + g : 0;
+    const uint32_t bytes = ok ? kPage * kD : 0;
+    const u32x4 rk = srd(a.kp + pg * kPage * kD, bytes);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int e = w + G * j;  // wave-uniform
+      if (!real || e >= kCopies) {
+        copy16(rk, lds_addr(pad), 16 * lane);
+      } else if (e < 8) {
+        copy16(rk, lds_addr(slot + 1024 * e), 1024 * e + 16 * lane);
+      } else if (e < 16) {
+        copy16(srd(a.vp + pg * kPage * kD, bytes),
+               lds_addr(slot + kRawV + 1024 * (e - 8)),
+               1024 * (e - 8) + 16 * lane);
+      } else {
+        const float *src = (e == 16 ? a.ks : a.vs) + pg * kPage;
+        copy4(srd(src, ok ? kPage * 4 : 0),
+              lds_addr(slot + (e == 16 ? kRawKS : kRawVS)), 4 * lane);
+      }
+    }
+  }
+  // the same wave's copies turned into bf16 tiles: keys [token][dim] (row
+  // stride kKStride), values [dim][slot] (row stride kVStride) with token
+  // 4g+e of the low half at slot 8g+e and token 16+4g+e at slot 8g+4+e, then
+  // the fp32 key and value scales
+  __device__ __forceinline__ static void convert(const char *slot, char *buf,
+                                                 int w, int lane) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int e = w + G * j;
+      if (e < 8) {
+        const int c = 64 * e + lane;  // token c / 16, dims 16 (c % 16) ..
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(slot + 16 * c);
+        const int tok = c >> 4, d0 = 16 * (c & 15);
+        const u32x2 w0 = i8x4_bf16(v.x), w1 = i8x4_bf16(v.y);
+        const u32x2 w2 = i8x4_bf16(v.z), w3 = i8x4_bf16(v.w);
+        u32x4 *dst = reinterpret_cast<u32x4 *>(buf + tok * kKStride + 2 * d0);
+        dst[0] = u32x4{w0.x, w0.y, w1.x, w1.y};
+        dst[1] = u32x4{w2.x, w2.y, w3.x, w3.y};
+      } else if (e < 16) {
+        const int f = 64 * (e - 8) + lane;  // dim f / 2, tokens 16 (f % 2) ..
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(slot + kRawV + 16 * f);
+        char *row = buf + kKBytes + (f >> 1) * kVStride + 8 * (f & 1);
+        // tokens 16 h + 4 i .. +3 -> slots 8 i + 4 h .. +3
+        *reinterpret_cast<u32x2 *>(row + 0) = i8x4_bf16(v.x);
+        *reinterpret_cast<u32x2 *>(row + 16) = i8x4_bf16(v.y);
+        *reinterpret_cast<u32x2 *>(row + 32) = i8x4_bf16(v.z);
+        *reinterpret_cast<u32x2 *>(row + 48) = i8x4_bf16(v.w);
+      } else if (e < kCopies) {
+        if (lane < kPage)
+          *reinterpret_cast<float *>(buf + kKBytes + kVBytes +
+                                     (e == 16 ? 0 : kPage * 4) + 4 * lane) =
+              *reinterpret_cast<const float *>(
+                  slot + (e == 16 ? kRawKS : kRawVS) + 4 * lane);
+      }
+    }
+  }
+};
+
+template <int G>
+__global__ __launch_bounds__(64 * G) void tree_attn_kernel(AttnArgs a) {
+  using P = Pages<G>;
+  __shared__ __attribute__((aligned(16))) char raw0[kRawBytes];
+  __shared__ __attribute__((aligned(16))) char raw1[kRawBytes];
+  __shared__ __attribute__((aligned(16))) char raw2[kRawBytes];
+  __shared__ __attribute__((aligned(16))) char raw3[kRawBytes];
+  __shared__ __attribute__((aligned(16))) char pad[kPadBytes];
+  __shared__ __attribute__((aligned(16))) char tile0[kBufBytes];
+  __shared__ __attribute__((aligned(16))) char tile1[kBufBytes];
+  __shared__ int ids[kMaxRun];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int n = lane & 15;   // tree node of this lane's score/output column
+  const int gq = lane >> 4;  // lane group: k slots 8 gq .. 8 gq + 7
+  const int g = blockIdx.x % a.Hkv;
+  const int run = blockIdx.x / a.Hkv;
+  const int hq = g * G + w;
+  const int pa = static_cast<int>(static_cast<int64_t>(a.pages) * run / a.splits);
+  const int pb = static_cast<int>(static_cast<int64_t>(a.pages) * (run + 1) / a.splits);
+  const int len = pb - pa;  // 1 .. kMaxRun (the plan sees to it)
+
+  // queries of this wave's head as the B operand: lane (n, gq), step s holds
+  // q[n][hq][32 s + 8 gq .. +7]; nodes >= M read zeros
+  const __amdgpu_buffer_rsrc_t qr =
+      rsrc(a.q, static_cast<uint32_t>(a.M) * a.Hq * kD * 2);
+  u32x4 qreg[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    qreg[s] = load16(qr, static_cast<uint32_t>(((n * a.Hq + hq) * kD + 32 * s + 8 * gq) * 2));
+  const uint32_t anc = n < a.M ? a.anc[n] : 0u;
+  // the run's page ids, staged in LDS before any copy is issued
+  bool bad_page = false;
+  for (int i = tid; i < len; i += 64 * G) {
+    const int pp = a.page_table[pa + i];
+    ids[i] = pp;
+    bad_page |= pp < 0 || pp >= a.pool;
+  }
+  if (__ballot(bad_page) != 0 && lane == 0 && a.status != nullptr)
+    a.status[0] = Q4_EINVAL;
+  __syncthreads();
+
+  auto page_of = [&](int i) { return __builtin_amdgcn_readfirstlane(ids[i]); };
+  const f32x4 fz = {0.f, 0.f, 0.f, 0.f};
+  f32x4 o[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) o[i] = fz;
+  float m = -INFINITY, lsum = 0.0f;
+
+  auto compute_page = [&](const char *buf, int lp) {
+    // scores S^T[token 16 c + 4 gq + r][node n]
+    f32x4 sc[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      sc[c] = fz;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const u32x4 ka = *reinterpret_cast<const u32x4 *>(
+            buf + (16 * c + n) * kKStride + 2 * (32 * s + 8 * gq));
+        sc[c] = mfma(ka, qreg[s], sc[c]);
+      }
+    }
+    const float *kscale = reinterpret_cast<const float *>(buf + kKBytes + kVBytes);
+    const float *vscale = kscale + kPage;
+    float p[8], vsc[8];
+    const int pos0 = kPage * lp;
+    const bool all_visible = pos0 + kPage <= a.ctx;  // uniform
+    float pm = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const f32x4 ksv = *reinterpret_cast<const f32x4 *>(kscale + 16 * c + 4 * gq);
+      const f32x4 vsv = *reinterpret_cast<const f32x4 *>(vscale + 16 * c + 4 * gq);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = 16 * c + 4 * gq + r;
+        float s = sc[c][r] * ksv[r] * a.scale2;
+        bool vis = true;
+        if (!all_visible) {
+          const int t = pos0 + tok - a.ctx;
+          vis = t < 0 || (t < a.M && ((anc >> t) & 1u));
+        }
+        s = vis ? s : -INFINITY;
+        p[4 * c + r] = s;
+        vsc[4 * c + r] = vsv[r];
+        pm = fmaxf(pm, s);
+      }
+    }
+    pm = fmaxf(pm, __shfl_xor(pm, 16, 64));
+    pm = fmaxf(pm, __shfl_xor(pm, 32, 64));
+    const float mn = fmaxf(m, pm);
+    // with nothing visible yet (mn = -inf) every p is 0 and nothing rescales
+    const float alpha = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
+    float ps = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = p[i] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(p[i] - mn);
+      ps += p[i];
+    }
+    lsum = lsum * alpha + ps;
+    m = mn;
+    if (__ballot(alpha != 1.0f) != 0) {  // a wave-uniform test
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[i] *= alpha;
+    }
+    // P'^T as the B operand: slot 8 gq + e <- token 4 gq + e (e < 4) and
+    // 16 + 4 gq + e - 4 (e >= 4), exactly the order of p[]
+    const u32x4 pb4 = {pack_bf16(p[0] * vsc[0], p[1] * vsc[1]),
+                       pack_bf16(p[2] * vsc[2], p[3] * vsc[3]),
+                       pack_bf16(p[4] * vsc[4], p[5] * vsc[5]),
+                       pack_bf16(p[6] * vsc[6], p[7] * vsc[7])};
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) {
+      const u32x4 va = *reinterpret_cast<const u32x4 *>(
+          buf + kKBytes + (16 * dt + n) * kVStride + 16 * gq);
+      o[dt] = mfma(va, pb4, o[dt]);
+    }
+  };
+
+  // Page i of the run lives in raw slot i % 4 and tile i % 2.  Step i:
+  // compute page i; wait for this wave's copies of page i + 1 (pages i + 2
+  // and i + 3 may still be in flight: 2 NI copies) and turn them into its
+  // tile; copy page i + 4 (or dummies) into the slot page i has left; one
+  // barrier.  A wave converts exactly the bytes its own copies brought, so
+  // only the tile needs the barrier.
+  constexpr int NI = P::NI;
+  const int first = page_of(0);
+  auto copy_page = [&](int i, const char *slot) {
+    const bool real = i < len;
+    P::copy(a, real ? page_of(i) : first, real, first, g, slot, pad, w, lane);
+  };
+  // the queries and the ancestor sets are in registers before the first
+  // copy, so that no later wait of the compiler's own counts the copies
+  wait_vm<0>();
+  copy_page(0, raw0);
+  copy_page(1, raw1);
+  copy_page(2, raw2);
+  copy_page(3, raw3);
+  wait_vm<3 * NI>();
+  P::convert(raw0, tile0, w, lane);
+  lds_barrier();
+  auto step = [&](int i, const char *slot, const char *next_slot, char *tile,
+                  char *next_tile) {
+    compute_page(tile, pa + i);
+    wait_vm<2 * NI>();
+    if (i + 1 < len) P::convert(next_slot, next_tile, w, lane);
+    copy_page(i + kRing, slot);
+    lds_barrier();
+  };
+  for (int i = 0; i < len; i += kRing) {
+    step(i, raw0, raw1, tile0, tile1);
+    if (i + 1 >= len) break;
+    step(i + 1, raw1, raw2, tile1, tile0);
+    if (i + 2 >= len) break;
+    step(i + 2, raw2, raw3, tile0, tile1);
+    if (i + 3 >= len) break;
+    step(i + 3, raw3, raw0, tile1, tile0);
+  }
+  wait_vm<0>();  // no copy may land after the workgroup has left its LDS
+
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  if (n >= a.M) return;
+  if (a.splits == 1) {
+    const float inv = 1.0f / lsum;
+    float *dst = a.out + (static_cast<size_t>(n) * a.Hq + hq) * kD + 4 * gq;
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt)
+      *reinterpret_cast<f32x4 *>(dst + 16 * dt) = o[dt] * inv;
+  } else {
+    const size_t row = (static_cast<size_t>(run) * a.Hq + hq) * a.M + n;
+    float *dst = a.part + row * kD + 4 * gq;
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt)
+      *reinterpret_cast<f32x4 *>(dst + 16 * dt) = o[dt];
+    if (gq == 0) {
+      float *ml = a.part + static_cast<size_t>(a.splits) * a.Hq * a.M * kD;
+      ml[2 * row] = m;
+      ml[2 * row + 1] = lsum;
+    }
+  }
+}
+
+// out[n][hq][d] = sum_r 2^(m_r - m) O_r[d] / sum_r 2^(m_r - m) l_r, one
+// workgroup per (node, query head): the runs' weights go to LDS first, then
+// every thread sums its dimension over the runs with eight loads in flight.
+constexpr int kCombineMaxRuns = 2048;
+
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float *part,
+                                                           float *out, int M,
+                                                           int Hq, int splits) {
+  __shared__ float wgt[kCombineMaxRuns];
+  __shared__ float red[8];
+  const int row = blockIdx.x;  // hq * M + n
+  const int hq = row / M, n = row % M;
+  const int d = threadIdx.x;
+  const size_t rows = static_cast<size_t>(Hq) * M;
+  const float *ml = part + static_cast<size_t>(splits) * rows * kD;
+  float mx = -INFINITY;
+  for (int r = d; r < splits; r += 256) mx = fmaxf(mx, ml[2 * (r * rows + row)]);
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  if ((d & 63) == 0) red[d >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float den = 0.0f;
+  for (int r = d; r < splits; r += 256) {
+    const float mr = ml[2 * (r * rows + row)];
+    const float w = mr == -INFINITY ? 0.0f : exp2f(mr - mx);
+    wgt[r] = w;
+    den += w * ml[2 * (r * rows + row) + 1];
+  }
+  for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o, 64);
+  __syncthreads();
+  if ((d & 63) == 0) red[4 + (d >> 6)] = den;
+  __syncthreads();
+  den = red[4] + red[5] + red[6] + red[7];
+  const float *src = part + static_cast<size_t>(row) * kD + d;
+  float acc = 0.0f;
+  int r = 0;
+  for (; r + 8 <= splits; r += 8) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = src[(r + i) * rows * kD];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc += wgt[r + i] * v[i];
+  }
+  for (; r < splits; ++r) acc += wgt[r] * src[r * rows * kD];
+  out[(static_cast<size_t>(n) * Hq + hq) * kD + d] = acc / den;
+}
+
+}  // namespace
+
+// splits: a run of at least 4 pages per workgroup, about two workgroups
+// per compute unit
+int attn_splits(int pages, int Hkv, int cus) {
+  int s = (cus + Hkv - 1) / Hkv;
+  const int cap = pages / 4 > 0 ? pages / 4 : 1;
+  if (s > cap) s = cap;
+  const int least = (pages + kMaxRun - 1) / kMaxRun;
+  if (s < least) s = least;
+  return s < 1 ? 1 : s;
+}
+
+}  // namespace q4v
+
+namespace {
+
+int attn_shape(int M, int Hq, int Hkv, int D, int64_t ctx_len, int *pages) {
+  if (M < 1 || M > Q4_ATTN_MAX_NODES || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 ||
+      D != Q4_ATTN_HEAD_DIM || ctx_len < 0 || ctx_len > 0x7FFFFFFFLL - 64)
+    return Q4_EINVAL;
+  const int G = Hq / Hkv;
+  if (G != 2 && G != 4 && G != 6 && G != 8) return Q4_EINVAL;
+  *pages = static_cast<int>((ctx_len + M + Q4_ATTN_PAGE - 1) / Q4_ATTN_PAGE);
+  return Q4_OK;
+}
+
+}  // namespace
+
+extern "C" int q4_tree_attn_plan(int M, int Hq, int Hkv, int D,
+                                 int64_t ctx_len, int splits,
+                                 int *splits_used,
+                                 uint64_t *workspace_bytes) {
+  int pages = 0;
+  if (splits_used == nullptr || workspace_bytes == nullptr || splits < 0)
+    return Q4_EINVAL;
+  const int st = attn_shape(M, Hq, Hkv, D, ctx_len, &pages);
+  if (st != Q4_OK) return st;
+  int s = splits > 0 ? splits : q4v::attn_splits(pages, Hkv, q4v::device_cus());
+  if (s > pages) s = pages;
+  if ((pages + s - 1) / s > q4v::kMaxRun || s > q4v::kCombineMaxRuns)
+    return Q4_EINVAL;  // runs too long, or too many of them
+  if (static_cast<int64_t>(s) * Hkv > 0x7FFFFFFF) return Q4_EINVAL;
+  *splits_used = s;
+  *workspace_bytes = s == 1 ? 0
+                            : static_cast<uint64_t>(s) * Hq * M *
+                                  (Q4_ATTN_HEAD_DIM + 2) * 4;
+  return Q4_OK;
+}
+
+extern "C" int q4_tree_attn(const void *q, int M, int Hq, int Hkv, int D,
+                            const int8_t *k_pages, const int8_t *v_pages,
+                            const float *k_scale, const float *v_scale,
+                            const int32_t *page_table, int pool_pages,
+                            int64_t ctx_len, const uint32_t *anc, float scale,
+                            float *out, int splits, void *workspace,
+                            uint64_t workspace_bytes, int32_t *status,
+                            void *stream) {
+  int s = 0;
+  uint64_t need = 0;
+  int st = q4_tree_attn_plan(M, Hq, Hkv, D, ctx_len, splits, &s, &need);
+  if (st != Q4_OK) return st;
+  if (q == nullptr || k_pages == nullptr || v_pages == nullptr ||
+      k_scale == nullptr || v_scale == nullptr || page_table == nullptr ||
+      anc == nullptr || out == nullptr || pool_pages < 1 ||
+      !(scale > 0.0f) || !(scale < 3.0e38f) ||
+      (need > 0 && (workspace == nullptr || workspace_bytes < need)))
+    return Q4_EINVAL;
+  if ((static_cast<uint64_t>(pool_pages) * Hkv * Q4_ATTN_PAGE * Q4_ATTN_HEAD_DIM) >>
+      62)
+    return Q4_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(q) & 15u) != 0 ||
+      (reinterpret_cast<uintptr_t>(k_pages) & 15u) != 0 ||
+      (reinterpret_cast<uintptr_t>(v_pages) & 15u) != 0 ||
+      (reinterpret_cast<uintptr_t>(k_scale) & 15u) != 0 ||
+      (reinterpret_cast<uintptr_t>(v_scale) & 15u) != 0 ||
+      (reinterpret_cast<uintptr_t>(out) & 15u) != 0 ||
+      (reinterpret_cast<uintptr_t>(page_table) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(anc) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(status) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(workspace) & 15u) != 0)
+    return Q4_EALIGN;
+  st = q4v::check_device();
+  if (st != Q4_OK) return st;
+  const int pages =
+      static_cast<int>((ctx_len + M + Q4_ATTN_PAGE - 1) / Q4_ATTN_PAGE);
+  q4v::AttnArgs a{static_cast<const uint16_t *>(q), k_pages, v_pages, k_scale,
+                  v_scale, page_table, anc, out,
+                  static_cast<float *>(workspace), status, M, Hq, Hkv,
+                  pool_pages, static_cast<int>(ctx_len), pages, s,
+                  scale * q4v::kLog2e};
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<uint32_t>(s * Hkv));
+  switch (Hq / Hkv) {
+    case 2:
+      hipLaunchKernelGGL(q4v::tree_attn_kernel<2>, grid, dim3(128), 0, hs, a);
+      break;
+    case 4:
+      hipLaunchKernelGGL(q4v::tree_attn_kernel<4>, grid, dim3(256), 0, hs, a);
+      break;
+    case 6:
+      hipLaunchKernelGGL(q4v::tree_attn_kernel<6>, grid, dim3(384), 0, hs, a);
+      break;
+    default:
+      hipLaunchKernelGGL(q4v::tree_attn_kernel<8>, grid, dim3(512), 0, hs, a);
+      break;
+  }
+  if (hipGetLastError() != hipSuccess) return Q4_ELAUNCH;
+  if (s > 1) {
+    hipLaunchKernelGGL(q4v::attn_combine_kernel, dim3(M * Hq), dim3(256), 0,
+                       hs, static_cast<const float *>(workspace), out, M, Hq,
+                       s);
+    if (hipGetLastError() != hipSuccess) return Q4_ELAUNCH;
+  }
+  return Q4_OK;
+}

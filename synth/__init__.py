@@ -183,3 +183,54 @@ def tree_path(parent, node: int):
         path.append(int(node))
         node = int(parent[node])
     return path[::-1]
+
+
+def ancestor_sets(parent):
+    """int32 [M] holding uint32 bit sets: bit j of entry i set iff node j is
+    node i or one of its ancestors (tree bookkeeping for the attention mask;
+    parent[i] < i, -1 for a child of the context)."""
+    import numpy as np
+    out = np.zeros(len(parent), dtype=np.uint32)
+    for i in range(len(parent)):
+        n = i
+        while n >= 0:
+            out[i] |= np.uint32(1) << np.uint32(n)
+            n = int(parent[n])
+    return out.view(np.int32)
+
+
+def attn_inputs(M: int, Hq: int, Hkv: int, ctx_len: int, D: int = 256,
+                seed: int = 0, stream: int = 0, spare_pages: int = 3,
+                device="cpu") -> dict:
+    """Seeded inputs of one tree-verify attention layer:
+
+    * queries q [M, Hq, D] = bf16(N(0, 1));
+    * a paged int8 cache holding ctx_len + M positions (the tree's keys and
+      values after the context): codes round(N(0, 40)) clamped to -127..127,
+      per token and head scales U(0.005, 0.02) for keys and for values; keys
+      [pool, Hkv, 32, D], values stored transposed [pool, Hkv, D, 32];
+    * the pool has spare_pages more pages than needed, filled with codes too,
+      and the page table is a random permutation of the pool;
+    * a draft tree (as gdn_inputs draws it) and its ancestor-or-self sets.
+    """
+    import numpy as np
+    rng = np.random.default_rng(stream_seed(seed, 13, stream))
+    pages = (ctx_len + M + 31) // 32
+    pool = pages + spare_pages
+    kp = np.clip(np.rint(rng.normal(0, 40, size=(pool, Hkv, 32, D))), -127,
+                 127).astype(np.int8)
+    vp = np.clip(np.rint(rng.normal(0, 40, size=(pool, Hkv, D, 32))), -127,
+                 127).astype(np.int8)
+    ks = rng.uniform(0.005, 0.02, size=(pool, Hkv, 32)).astype(np.float32)
+    vs = rng.uniform(0.005, 0.02, size=(pool, Hkv, 32)).astype(np.float32)
+    table = rng.permutation(pool)[:pages].astype(np.int32)
+    parent = np.full(M, -1, dtype=np.int32)
+    for i in range(1, M):
+        parent[i] = i - 1 if rng.random() < 0.5 else rng.integers(-1, i)
+    g = _gen(device, seed, 14, stream)
+    q = torch.randn((M, Hq, D), generator=g, device=device,
+                    dtype=torch.float32).to(torch.bfloat16)
+    t = lambda a: torch.from_numpy(a).to(device)
+    return {"q": q, "k_pages": t(kp), "v_pages": t(vp), "k_scale": t(ks),
+            "v_scale": t(vs), "page_table": t(table), "parent": parent,
+            "anc": t(ancestor_sets(parent)), "ctx_len": ctx_len}
