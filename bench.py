@@ -377,6 +377,59 @@ def measure_gdn_commit(torch, synth, q4, dev, steps, warmup):
     return out
 
 
+ATTN_SHAPE = {"query_heads": 24, "kv_heads": 4, "head_dim": 256,
+              "tree_nodes": 16, "page_tokens": 32}
+
+
+def attn_alg_bytes(M, Hq, Hkv, D, ctx):
+    """Unique bytes of one tree-attention layer: the int8 keys and values of
+    every page touched with their fp32 scales, the bf16 queries, the page
+    table and ancestor sets, and the fp32 output."""
+    pages = (ctx + M + 31) // 32
+    return (pages * Hkv * (2 * 32 * D + 2 * 32 * 4) + M * Hq * D * 2
+            + pages * 4 + M * 4 + M * Hq * D * 4)
+
+
+def measure_tree_attn(torch, synth, q4, dev, steps, warmup):
+    """Tree-verify attention of one layer (24 query heads over 4 KV heads of
+    256, 16 tree nodes) at 4K and 32K tokens of context, the default split,
+    as prepared C-ABI calls back to back (the KV pages of one layer are
+    read per call; at 32K they are 68 MB, more than a quarter of the
+    last-level cache, and two caches are rotated)."""
+    import functools
+    g = ATTN_SHAPE
+    M, Hq, Hkv, D = g["tree_nodes"], g["query_heads"], g["kv_heads"], g["head_dim"]
+    lib = q4.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {"shape": dict(g), "contexts": []}
+    for ctx in (4096, 32768):
+        caches = [synth.attn_inputs(M, Hq, Hkv, ctx, seed=0, stream=i,
+                                    device=dev) for i in range(2)]
+        s, nws = q4.q4_tree_attn_plan(M, Hq, Hkv, ctx)
+        o = torch.empty((M, Hq, D), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+        fns = [functools.partial(
+            lib.q4_tree_attn, c["q"].data_ptr(), M, Hq, Hkv, D,
+            c["k_pages"].data_ptr(), c["v_pages"].data_ptr(),
+            c["k_scale"].data_ptr(), c["v_scale"].data_ptr(),
+            c["page_table"].data_ptr(), int(c["k_pages"].shape[0]), ctx,
+            c["anc"].data_ptr(), 1.0 / 16.0, o.data_ptr(), 0, ws.data_ptr(),
+            ws.numel(), None, stream) for c in caches]
+        if any(f() != 0 for f in fns):
+            raise RuntimeError("q4_tree_attn failed")
+        ms, _ = time_raw(torch, fns, steps, warmup)
+        nb = attn_alg_bytes(M, Hq, Hkv, D, ctx)
+        gbps = nb / (ms * 1e-3) / 1e9
+        out["contexts"].append({"ctx": ctx, "splits": s, "us": round(ms * 1e3, 3),
+                                "alg_bytes": nb, "workspace_bytes": nws,
+                                "gbps": round(gbps, 1),
+                                "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)})
+        del caches
+    log(f"tree attention: {out}")
+    torch.cuda.empty_cache()
+    return out
+
+
 def pass_calls():
     calls = []
     for layer in range(64):
@@ -615,9 +668,11 @@ def main():
     if not args.no_shapes:
         vsample = measure_verify_sample(torch, synth, q4, dev, args.steps,
                                         args.warmup)
-    gdn = None
+    gdn = attn = None
     if not args.no_shapes:
         gdn = measure_gdn_commit(torch, synth, q4, dev, args.steps,
+                                 args.warmup)
+        attn = measure_tree_attn(torch, synth, q4, dev, args.steps,
                                  args.warmup)
     full = None
     if not args.no_full_pass:
@@ -677,6 +732,7 @@ def main():
         "shapes": shapes,
         "verify_sample": vsample,
         "gdn_commit": gdn,
+        "tree_attention": attn,
         "full_pass": full,
         "stamp": st,
     }
