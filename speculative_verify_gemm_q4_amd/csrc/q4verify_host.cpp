@@ -134,8 +134,10 @@ bool plan_resident(int M, int64_t N, int64_t K, int cus, int parts,
   q4_plan p;
   std::memset(&p, 0, sizeof p);
   p.grid = static_cast<uint32_t>(gt * parts);
-  p.block = 64 * kResidentWaves;
   p.row_tiles = static_cast<uint32_t>((tiles + gt - 1) / gt);
+  p.block = 64 * (p.row_tiles >= static_cast<uint32_t>(kResidentWideTiles)
+                      ? kResidentWavesWide
+                      : kResidentWaves);
   p.tiles_per_wave = 1;
   p.k_splits = 1;
   p.lookahead = kRecordGroups * (kResidentStages - 1);

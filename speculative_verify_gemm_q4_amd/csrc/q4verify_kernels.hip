@@ -726,21 +726,33 @@ int launch_tiled(const q4_plan &p, const void *x, const void *W, float *y,
   return launch_status();
 }
 
+template <int W, int RT>
+void launch_resident_kernel(const q4_plan &p, const void *x, const void *Wt,
+                            float *y, float *ws, int M, int N, int K,
+                            hipStream_t stream) {
+  const int parts = static_cast<int>(p.k_parts);
+  hipLaunchKernelGGL((gemm_resident_kernel<W, kResidentStages, RT>),
+                     dim3(p.grid), dim3(64 * W), 0, stream,
+                     static_cast<const uint16_t *>(x),
+                     static_cast<const uint8_t *>(Wt), y, ws, M, N, K, parts,
+                     static_cast<int>(p.grid) / parts);
+}
+
 int launch_resident(const q4_plan &p, const void *x, const void *W, float *y,
                     float *ws, int M, int N, int K, hipStream_t stream) {
   const int parts = static_cast<int>(p.k_parts);
-  if (p.m_tiles == 2)
-    hipLaunchKernelGGL((gemm_resident_kernel<kResidentWaves, kResidentStages, 2>),
-                       dim3(p.grid), dim3(p.block), 0, stream,
-                       static_cast<const uint16_t *>(x),
-                       static_cast<const uint8_t *>(W), y, ws, M, N, K, parts,
-                       static_cast<int>(p.grid) / parts);
-  else
-    hipLaunchKernelGGL((gemm_resident_kernel<kResidentWaves, kResidentStages, 1>),
-                       dim3(p.grid), dim3(p.block), 0, stream,
-                       static_cast<const uint16_t *>(x),
-                       static_cast<const uint8_t *>(W), y, ws, M, N, K, parts,
-                       static_cast<int>(p.grid) / parts);
+  const bool wide = p.block == 64 * kResidentWavesWide;
+  if (p.m_tiles == 2) {
+    if (wide)
+      launch_resident_kernel<kResidentWavesWide, 2>(p, x, W, y, ws, M, N, K, stream);
+    else
+      launch_resident_kernel<kResidentWaves, 2>(p, x, W, y, ws, M, N, K, stream);
+  } else {
+    if (wide)
+      launch_resident_kernel<kResidentWavesWide, 1>(p, x, W, y, ws, M, N, K, stream);
+    else
+      launch_resident_kernel<kResidentWaves, 1>(p, x, W, y, ws, M, N, K, stream);
+  }
   int st = launch_status();
   if (st != Q4_OK || parts == 1) return st;
   const uint32_t mn4 = static_cast<uint32_t>(M) * static_cast<uint32_t>(N) / 4;
