@@ -56,7 +56,7 @@ WORKLOADS = {
 KERNEL_SOURCE = os.path.join(ROOT, "speculative_verify_gemm_q4_amd", "csrc",
                              "q4verify_kernels.hip")
 KERNEL_NAMES = {0: "gemm_verify_kernel", 1: "gemm_tiled_kernel",
-                2: "gemm_resident_kernel"}
+                2: "gemm_resident_kernel", 3: "gemm_kslice_kernel"}
 COUNTERS = os.path.join(ROOT, "profiles",
                         "q4_gemm_gate_up_34816x5120_counters.txt")
 

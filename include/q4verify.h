@@ -223,6 +223,12 @@ typedef struct {
                                         grid = one workgroup per CU (at most
                                         N/16), each owning whole 16-row tiles
                                         split evenly across its waves        */
+#define Q4_KERNEL_TILED_KSLICE 3u    /* tiled, M <= 16, K <= 6144; grid = one
+                                        workgroup per CU (at most N/16) over
+                                        whole tiles; wave w takes records 2w
+                                        and 2w+1 of every tile and keeps that
+                                        slice of the activations in
+                                        registers; block = 64 * ceil(K/512) */
 
 /*
  * q4_gemm_verify_plan -- the plan q4_gemm_verify (layout_id

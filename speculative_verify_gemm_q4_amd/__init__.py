@@ -27,7 +27,8 @@ Functions (same names as the C entry points):
 * :func:`q4_stream_read`, :func:`q4_stream_copy` -- bandwidth probes.
 * :func:`q4_status_string` -- name of a status code.
 """
-from ._lib import (ATTN_HEAD_DIM, ATTN_MAX_NODES, ATTN_PAGE, GDN_DK, GDN_MAX_NODES, GROUP, KERNEL_PLANAR, KERNEL_TILED_RESIDENT,
+from ._lib import (ATTN_HEAD_DIM, ATTN_MAX_NODES, ATTN_PAGE, GDN_DK, GDN_MAX_NODES, GROUP, KERNEL_PLANAR, KERNEL_TILED_KSLICE,
+                   KERNEL_TILED_RESIDENT,
                    KERNEL_TILED_STREAM, LAYOUT_PLANAR, LAYOUT_TILED16, MAX_ROWS,
                    MAX_ROWS_TILED, Q4Error,
                    LIB_PATH, lib_exports, load, q4_dequant, q4_gemm_verify,
@@ -40,7 +41,8 @@ from ._lib import (ATTN_HEAD_DIM, ATTN_MAX_NODES, ATTN_PAGE, GDN_DK, GDN_MAX_NOD
                    q4_stream_read, q4_tree_attn, q4_tree_attn_plan,
                    tree_attn)
 
-__all__ = ["ATTN_HEAD_DIM", "ATTN_MAX_NODES", "ATTN_PAGE", "GDN_DK", "GDN_MAX_NODES", "GROUP", "KERNEL_PLANAR", "KERNEL_TILED_RESIDENT",
+__all__ = ["ATTN_HEAD_DIM", "ATTN_MAX_NODES", "ATTN_PAGE", "GDN_DK", "GDN_MAX_NODES", "GROUP", "KERNEL_PLANAR", "KERNEL_TILED_KSLICE",
+           "KERNEL_TILED_RESIDENT",
            "KERNEL_TILED_STREAM", "LAYOUT_PLANAR", "LAYOUT_TILED16", "MAX_ROWS",
            "MAX_ROWS_TILED", "Q4Error",
            "LIB_PATH", "lib_exports", "load", "q4_dequant", "q4_gemm_verify",

@@ -16,6 +16,7 @@ LAYOUT_TILED16 = 1
 KERNEL_PLANAR = 0
 KERNEL_TILED_STREAM = 1
 KERNEL_TILED_RESIDENT = 2
+KERNEL_TILED_KSLICE = 3
 
 OK, EINVAL, EALIGN, EOVERFLOW, EDEVICE, ELAUNCH = 0, -1, -2, -3, -4, -5
 

@@ -46,6 +46,13 @@ constexpr int kResidentWaves = 8;
 constexpr int kResidentWavesWide = 16;
 constexpr int kResidentWideTiles = 8;
 constexpr int kResidentStages = 2;
+// K-slice kernel: two records of every tile per wave, so at most 12 waves
+// (K <= 6144); tiles per reduction batch fill the LDS with the waves'
+// partial sums (16 x 10 x 1 KiB at K = 5120).
+constexpr int kKsliceMaxRecords = 24;
+constexpr int kKsliceBatchLds = kLdsBytes;
+// LDS of the K-slice kernel's partial sums for W waves.
+constexpr int kslice_batch(int W) { return kKsliceBatchLds / (W * 1024); }
 
 // Q4_OK when a HIP device is current and it is a gfx950; Q4_EDEVICE
 // otherwise.  The answer is cached per device ordinal.

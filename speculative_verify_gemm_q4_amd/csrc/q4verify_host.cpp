@@ -151,11 +151,37 @@ bool plan_resident(int M, int64_t N, int64_t K, int cus, int parts,
   return true;
 }
 
+// Plan of the K-slice kernel (M <= 16, K <= 6144): one workgroup per CU,
+// ceil(Q / 2) waves.
+bool plan_kslice(int M, int64_t N, int64_t K, int cus, q4_plan *out) {
+  const int64_t tiles = N / kTileRows;
+  const int64_t records = K / (kRecordGroups * Q4_GROUP);
+  if (M > Q4_MAX_ROWS || records > kKsliceMaxRecords) return false;
+  const int64_t g = tiles < cus ? tiles : cus;
+  const int64_t per = (tiles + g - 1) / g;
+  if (per * records * kRecordBytes >= 0x7FFFFFF0LL) return false;
+  const int waves = static_cast<int>((records + 1) / 2);
+  q4_plan p;
+  std::memset(&p, 0, sizeof p);
+  p.grid = static_cast<uint32_t>(g);
+  p.block = static_cast<uint32_t>(64 * waves);
+  p.row_tiles = static_cast<uint32_t>(per);
+  p.tiles_per_wave = 1;
+  p.k_splits = static_cast<uint32_t>(waves);
+  p.lookahead = kRecordGroups * 2;
+  p.kernel = Q4_KERNEL_TILED_KSLICE;
+  p.lds_bytes = static_cast<uint32_t>(kslice_batch(waves) * waves * 1024);
+  p.k_parts = 1;
+  p.m_tiles = 1;
+  *out = p;
+  return true;
+}
+
 q4_plan plan_gemm_tiled_ws(int M, int64_t N, int64_t K, int cus) {
-  // Split when the activations of all of K exceed the LDS -- except for
-  // K <= 2 x 5120 at M < 8, where (measured on MI355X, attention output
-  // projection 5120 x 6144) the streaming kernel is as fast without the
-  // second launch.
+  // Up to 16 rows and 24 records per tile the K-slice kernel needs no split.
+  // Beyond, split K across workgroups when its activations exceed the LDS --
+  // except for K <= 2 x 5120 at M < 8, where the streaming kernel is as fast
+  // without the second launch.
   const int m_tiles = M > Q4_MAX_ROWS ? 2 : 1;
   const int64_t records = K / (kRecordGroups * Q4_GROUP);
   const int64_t per_part = kResidentMaxRecords / m_tiles;
@@ -170,6 +196,14 @@ q4_plan plan_gemm_tiled_ws(int M, int64_t N, int64_t K, int cus) {
     std::memset(&p, 0, sizeof p);  // no plan: the call is rejected
     return p;
   }
+  // The K-slice kernel, except for K > 5120 with few tiles at M >= 8 (the
+  // 5120 x 6144 output projections: 320 tiles give a CU 1 or 2 of them,
+  // and the parts of a split K balance better: 10.7 against 11.4 us at
+  // M = 16, measured on MI355X).
+  const int64_t tiles = N / kTileRows;
+  if (M <= Q4_MAX_ROWS && records <= kKsliceMaxRecords &&
+      !(M >= 8 && K > kResidentMaxK && tiles < 2 * cus))
+    return plan_gemm_tiled(M, N, K, cus);
   if (K > kResidentMaxK && (M >= 8 || K > 2 * kResidentMaxK)) {
     // Parts of K taken by separate workgroups: enough for a part's
     // activations to fit the LDS, and at least 4, a power of two, so that
@@ -185,6 +219,14 @@ q4_plan plan_gemm_tiled_ws(int M, int64_t N, int64_t K, int cus) {
 
 q4_plan plan_gemm_tiled(int M, int64_t N, int64_t K, int cus) {
   const int64_t tiles = N / kTileRows;
+  {
+    // Up to 16 rows and 24 records per tile: each wave keeps its slice of
+    // K of the activations in registers (measured on MI355X: gate+up, the
+    // LM head and the GDN in-projection faster than with the activations in
+    // LDS, attention's in-projection at M = 16 even).
+    q4_plan p;
+    if (plan_kslice(M, N, K, cus, &p)) return p;
+  }
   if (K <= kResidentMaxK) {
     // Activations resident in LDS: one workgroup per CU (the LDS admits no
     // second), each owning whole tiles; its waves split its records evenly.

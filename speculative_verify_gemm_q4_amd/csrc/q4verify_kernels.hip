@@ -726,6 +726,169 @@ int launch_tiled(const q4_plan &p, const void *x, const void *W, float *y,
   return launch_status();
 }
 
+// The product for M <= 16 and K <= 6144 with each wave's slice of K of the
+// activations in registers.  One workgroup per CU owns whole tiles
+// [t0, t1); its W = ceil(Q / 2) waves all work on the same tile at once,
+// wave w on records 2w and 2w + 1 of it, so that the workgroup reads each
+// tile's 46 KB (at K = 5120) as one contiguous run:
+//  * the wave loads its two records' activations once, straight into MFMA
+//    operand registers (lane (j, kb), half h: inputs 64 gi + 16 kb + 8 h ..
+//    +7 of row j of record q; rows >= M fall past the resource and read as
+//    zeros), and forms the seed -128 * sum(x) of each of its 8 groups once,
+//    with two MFMAs per group -- not per tile;
+//  * per tile it multiplies its two records (two MFMAs per group, seeded
+//    with that group's sum) and writes its partial 16 x 16 sum to LDS;
+//  * every kslice_batch(W) tiles the workgroup adds the waves' partial sums
+//    in wave order and writes y.
+// The weights of tile t + 1 are in flight while tile t is multiplied; the
+// first tile's weights are issued before the activations.  Summation order
+// depends only on (N, K), so results do not depend on M and repeated calls
+// are bitwise equal.
+template <int W>
+__global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
+    const uint16_t *__restrict__ x, const uint8_t *__restrict__ Wt,
+    float *__restrict__ y, int M, int N, int K) {
+  constexpr int NB = kslice_batch(W);  // tiles per reduction batch
+  __shared__ f32x4 part[NB * W * 64];
+  const int T = N >> 4;
+  const int Q = K >> 8;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 15;
+  const int kb = lane >> 4;
+  const int t0 = static_cast<int>(static_cast<int64_t>(T) * blockIdx.x / gridDim.x);
+  const int t1 = static_cast<int>(static_cast<int64_t>(T) * (blockIdx.x + 1) / gridDim.x);
+  const int q0 = 2 * wave;
+  const int nq = Q - q0 >= 2 ? 2 : Q - q0;  // 1 or 2
+
+  // weights of the workgroup's tiles; a record past them (or past the
+  // wave's slice) gets an offset past the resource and reads zeros
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(Wt + static_cast<uint64_t>(t0) * Q * kRecordBytes), 0,
+      (t1 - t0) * Q * kRecordBytes, kBufferWord3);
+  struct Stage {
+    u32x4 c0[2], c1[2], sb[2];
+  };
+  int tl = 0;  // next tile to load, counted from t0
+  auto load = [&](Stage &st) {
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      const uint32_t o = tl < t1 - t0 && qq < nq
+                             ? static_cast<uint32_t>((tl * Q + q0 + qq) * kRecordBytes)
+                             : 0x7FFFFFF0u;
+      st.c0[qq] = buffer_load16<kNonTemporal>(wr, lane * 16, o);
+      st.c1[qq] = buffer_load16<kNonTemporal>(wr, 1024 + lane * 16, o);
+      st.sb[qq] = buffer_load16<kNonTemporal>(wr, 2048 + j * 16, o);
+    }
+    ++tl;
+  };
+  constexpr int S = 2;
+  Stage st[S];
+  load(st[0]);
+
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(x), 0,
+      static_cast<int>(static_cast<uint32_t>(M) * static_cast<uint32_t>(K) * 2u),
+      kBufferWord3);
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  const u32x4 neg = {kNeg128Pair, kNeg128Pair, kNeg128Pair, kNeg128Pair};
+  const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
+  u32x4 xa[2][4][2];
+  f32x4 xn[2][4];
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t off = (static_cast<uint32_t>(j) * K + 256 * (q0 + qq) +
+                              64 * gi + 16 * kb + 8 * h) * 2;
+        xa[qq][gi][h] = qq < nq ? buffer_load16<0>(xr, off, 0) : zero4;
+      }
+      const f32x4 s = mfma16x16x32(xa[qq][gi][0], neg, fzero);
+      xn[qq][gi] = mfma16x16x32(xa[qq][gi][1], neg, s);
+    }
+
+  const UnpackConsts uc = unpack_consts();
+  auto compute = [&](const Stage &s, f32x4 &acc) {
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const u32x4 cw = gi < 2 ? s.c0[qq] : s.c1[qq];
+        const u32x4 b0 = unpack_codes((gi & 1) ? cw.z : cw.x, uc);
+        const u32x4 b1 = unpack_codes((gi & 1) ? cw.w : cw.y, uc);
+        const uint32_t sbw = s.sb[qq][gi];
+        const float sc = __uint_as_float(sbw << 16);
+        const float bn = __uint_as_float(sbw & 0xFFFF0000u) * kMinusInv128;
+        f32x4 tq = mfma16x16x32(xa[qq][gi][0], b0, xn[qq][gi]);
+        tq = mfma16x16x32(xa[qq][gi][1], b1, tq);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          acc[r] = __builtin_fmaf(bn, xn[qq][gi][r], acc[r]);
+          acc[r] = __builtin_fmaf(sc, tq[r], acc[r]);
+        }
+      }
+    }
+  };
+
+  int tb = t0;  // first tile of the current batch
+  for (int t = t0; t < t1; t += S) {
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      load(st[(i + 1) % S]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + i < t1) {  // the same for every wave: barriers below are safe
+        f32x4 acc = fzero;
+        compute(st[i], acc);
+        part[((t + i - tb) * W + wave) * 64 + lane] = acc;
+        if (t + i - tb == NB - 1 || t + i == t1 - 1) {
+          __syncthreads();
+          const int nb = t + i - tb + 1;
+          for (int e = threadIdx.x; e < nb * 64; e += 64 * W) {
+            const int tt = e >> 6, l = e & 63;
+            f32x4 v = part[(tt * W) * 64 + l];
+            for (int w2 = 1; w2 < W; ++w2) v += part[(tt * W + w2) * 64 + l];
+            const int n = (tb + tt) * 16 + (l & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int m = (l >> 4) * 4 + r;
+              if (m < M) y[static_cast<uint64_t>(m) * N + n] = v[r];
+            }
+          }
+          __syncthreads();
+          tb = t + i + 1;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+template <int W>
+int launch_kslice_w(const q4_plan &p, const void *x, const void *Wt, float *y,
+                    int M, int N, int K, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_kslice_kernel<W>), dim3(p.grid), dim3(64 * W), 0,
+                     stream, static_cast<const uint16_t *>(x),
+                     static_cast<const uint8_t *>(Wt), y, M, N, K);
+  return launch_status();
+}
+
+int launch_kslice(const q4_plan &p, const void *x, const void *Wt, float *y,
+                  int M, int N, int K, hipStream_t stream) {
+  switch (p.block / 64) {
+#define Q4V_KSLICE_CASE(W) \
+  case W:                  \
+    return launch_kslice_w<W>(p, x, Wt, y, M, N, K, stream);
+    Q4V_KSLICE_CASE(1) Q4V_KSLICE_CASE(2) Q4V_KSLICE_CASE(3)
+    Q4V_KSLICE_CASE(4) Q4V_KSLICE_CASE(5) Q4V_KSLICE_CASE(6)
+    Q4V_KSLICE_CASE(7) Q4V_KSLICE_CASE(8) Q4V_KSLICE_CASE(9)
+    Q4V_KSLICE_CASE(10) Q4V_KSLICE_CASE(11) Q4V_KSLICE_CASE(12)
+#undef Q4V_KSLICE_CASE
+    default: return Q4_EINVAL;
+  }
+}
+
 template <int W, int RT>
 void launch_resident_kernel(const q4_plan &p, const void *x, const void *Wt,
                             float *y, float *ws, int M, int N, int K,
@@ -805,6 +968,8 @@ extern "C" int q4_gemm_verify_tiled(const void *x, const void *W, float *y,
   if (st != Q4_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int n = static_cast<int>(N), k = static_cast<int>(K);
+  if (p.kernel == Q4_KERNEL_TILED_KSLICE)
+    return q4v::launch_kslice(p, x, W, y, M, n, k, s);
   if (p.kernel == Q4_KERNEL_TILED_RESIDENT)
     return q4v::launch_resident(p, x, W, y, nullptr, M, n, k, s);
   const int key = static_cast<int>(p.tiles_per_wave * 100 + p.k_splits);

@@ -268,7 +268,10 @@ def test_lm_head_two_calls(q4):
 
 TILED = [(16, 16, 256), (1, 16, 256), (16, 256, 512), (5, 1600, 1024),
          (5, 1600, 2048), (16, 5120, 6144), (3, 5120, 17408),
-         (16, 80000, 1024), (7, 1040, 256), (16, 2048, 4096)]
+         (16, 80000, 1024), (7, 1040, 256), (16, 2048, 4096),
+         # K-slice kernel: an odd record count (the last wave takes one),
+         # 23 records, and 20 tiles per workgroup (two reduction batches)
+         (4, 4800, 1280), (16, 512, 5888), (16, 81920, 5120)]
 
 
 @pytest.mark.parametrize("N,K", [(16, 256), (256, 512), (1600, 2048),
@@ -288,21 +291,26 @@ def test_tiled_tiny(q4, M):
 
 
 def test_resident_empty_waves_after_other_lds_users(q4):
-    """Resident-activation kernel on shapes where most of a workgroup's waves
-    get no records (their weight loads all fall past their range and return
-    at once), each call preceded by kernels that leave other data in LDS: no
-    wave may start before every activation copy has landed."""
+    """Small shapes where most of a workgroup's waves get no records (their
+    weight loads all fall past their range and return at once), each call
+    preceded by kernels that leave other data in LDS: the resident kernel
+    (17..32 rows) must not start a wave before every activation copy has
+    landed, and the K-slice kernel (up to 16 rows) must not read another
+    kernel's LDS for its partial sums."""
     dev = torch.device("cuda")
     Wp = synth.q4_weights(2048, 4096, seed=40, device=dev)
     Wtp = repacked(q4, Wp, 2048, 4096)
     xp = synth.activations(16, 4096, seed=40, stream=1, device=dev)
     yp = torch.empty((16, 2048), dtype=torch.float32, device=dev)
     for N, K in [(16, 256), (16, 512), (48, 256), (256, 512), (32, 5120)]:
-        p = q4.q4_gemm_verify_plan(16, N, K, q4.LAYOUT_TILED16)
-        assert p["kernel"] == q4.KERNEL_TILED_RESIDENT
         W = synth.q4_weights(N, K, seed=41, device=dev)
         Wt = repacked(q4, W, N, K)
-        for M in (1, 4, 16):
+        for M in (1, 4, 16, 24):
+            if M > 16 and K > 2560:
+                continue  # 32 rows of this K need the workspace path
+            p = q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_TILED16)
+            want = q4.KERNEL_TILED_KSLICE if M <= 16 else q4.KERNEL_TILED_RESIDENT
+            assert p["kernel"] == want
             x = synth.activations(M, K, seed=41 + M, stream=1, device=dev)
             _, y64, a64, _ = oracle.gemm(synth.bf16_bits(x), W.cpu().numpy(),
                                          N, K)
@@ -310,10 +318,10 @@ def test_resident_empty_waves_after_other_lds_users(q4):
                 # both other kernels leave their own data in LDS
                 q4.q4_gemm_verify(xp, Wp, yp, 16, 2048, 4096)
                 q4.q4_gemm_verify_tiled(xp, Wtp, yp, 16, 2048, 4096)
-                _say(f"case resident empty waves: N={N} K={K} M={M} rep={rep}")
+                _say(f"case small tiled shapes: N={N} K={K} M={M} rep={rep}")
                 y = gemm_tiled(q4, x, Wt, M, N, K)
                 assert_within_bound(y, y64, a64,
-                                    f"resident N={N} K={K} M={M} rep={rep}")
+                                    f"tiled N={N} K={K} M={M} rep={rep}")
 
 
 @pytest.mark.parametrize("M,N,K", TILED)
@@ -397,9 +405,9 @@ def gemm_tiled_ws(q4, x, Wt, M, N, K, fill=float("nan")):
 
 # K > 5120 (split across workgroups, partial sums reduced in part order),
 # including tiny N (most waves empty) and a part count above 4
-WS_SHAPES = [(16, 5120, 6144), (3, 5120, 17408), (1, 16, 10496),
+WS_SHAPES = [(16, 5120, 6400), (16, 5120, 6144), (3, 5120, 17408), (1, 16, 10496),
              (16, 48, 10240), (8, 1600, 7168), (16, 256, 65536),
-             (9, 32, 5632)]
+             (9, 32, 6656)]
 
 
 @pytest.mark.parametrize("M,N,K", WS_SHAPES)
@@ -418,7 +426,7 @@ def test_workspace_split_shapes(q4, M, N, K):
 def test_workspace_integer_exact_M_invariance_determinism(q4):
     dev = torch.device("cuda")
     rng = np.random.default_rng(31)
-    N, K = 512, 6144
+    N, K = 512, 6656
     q = rng.integers(0, 16, size=(N, K))
     G = K // 64
     codes = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)

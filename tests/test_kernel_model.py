@@ -128,9 +128,11 @@ TILED_SHAPES = [(16, 16, 256), (16, 256, 512), (5, 1600, 1024),
 @pytest.mark.parametrize("M,N,K", TILED_SHAPES)
 def test_tiled_plan_reads_every_record_once(M, N, K):
     p = q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_TILED16)
+    if p["kernel"] == q4.KERNEL_TILED_KSLICE:
+        return kslice_model(M, N, K, p)
     if p["kernel"] == q4.KERNEL_TILED_RESIDENT:
         return resident_model(M, N, K, p)
-    assert p["kernel"] == q4.KERNEL_TILED_STREAM and K > 5120
+    assert p["kernel"] == q4.KERNEL_TILED_STREAM and K > 6144
     tnt, ksw, grid, block = (p["tiles_per_wave"], p["k_splits"], p["grid"],
                              p["block"])
     ntw = p["row_tiles"] // tnt
@@ -176,6 +178,61 @@ def test_tiled_plan_reads_every_record_once(M, N, K):
 
 
 # --------------------------------------------------------------------------
+# K-slice kernel (M <= 16, K <= 6144): workgroup b owns tiles
+# [T b / G, T (b+1) / G) with G = min(T, CUs); its W = ceil(Q / 2) waves take
+# records 2w and 2w + 1 of every one of those tiles (wave w's activations:
+# inputs 256 q + 64 gi + 16 kb + 8 h .. +7 of row j for lane (j, kb)); the
+# tiles are written in batches of NB = LDS / (W KiB), each tile once, the
+# waves' partial sums added in wave order.
+
+def kslice_model(M, N, K, p):
+    T, Q = N // 16, K // 256
+    W = p["block"] // 64
+    assert M <= 16 and Q <= 24 and W == (Q + 1) // 2 and p["k_parts"] == 1
+    G = p["grid"]
+    assert G == min(T, 256) and p["m_tiles"] == 1
+    NB = LDS_BYTES // (W * 1024)
+    assert p["lds_bytes"] == NB * W * 1024 <= LDS_BYTES
+    assert p["workspace_bytes"] == 0
+    hits = np.zeros((T, Q), dtype=np.int32)
+    writes = np.zeros(T, dtype=np.int32)
+    for b in range(G):
+        t0, t1 = T * b // G, T * (b + 1) // G
+        span = (t1 - t0) * Q * 2304
+        assert span < 0x7FFFFFF0
+        for w in range(W):
+            nq = min(2, Q - 2 * w)
+            assert nq >= 1
+            for tl in range(t1 - t0):
+                for qq in range(nq):
+                    off = (tl * Q + 2 * w + qq) * 2304
+                    assert off + 2304 <= span
+                    hits[t0 + tl, 2 * w + qq] += 1
+        # batches: a flush after every NB tiles and after the last
+        tb = t0
+        for t in range(t0, t1):
+            assert (t - tb) < NB
+            if t - tb == NB - 1 or t == t1 - 1:
+                for tt in range(tb, t + 1):
+                    writes[tt] += 1
+                tb = t + 1
+    assert np.all(hits == 1)
+    assert np.all(writes == 1)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 256), (16, 16, 5120),
+                                   (16, 48, 256), (7, 4096, 1024),
+                                   (16, 4112, 5120), (1, 6000 * 16, 768),
+                                   (16, 34816, 5120), (16, 5120, 6144),
+                                   (3, 16, 5888), (16, 248320, 5120)])
+def test_kslice_plan_shapes(M, N, K):
+    p = q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_TILED16)
+    assert p["kernel"] == q4.KERNEL_TILED_KSLICE
+    kslice_model(M, N, K, p)
+    if not (K > 5120 and M >= 8 and N // 16 < 512):
+        assert q4.q4_gemm_verify_tiled_ws_plan(M, N, K) == p
+
+
 # resident-activation kernel (K <= 5120): workgroup b owns tiles
 # [T b / G, T (b+1) / G); its U = tiles * Q records (tile-major) are split
 # into W contiguous ranges [U w / W, U (w+1) / W).  A tile inside one range is
@@ -255,11 +312,13 @@ def resident_model(M, N, K, p):
     assert np.all(writes == 1)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 16, 256), (16, 16, 5120),
-                                   (16, 48, 256), (7, 4096, 1024),
-                                   (16, 4112, 5120), (1, 6000 * 16, 768),
-                                   (16, 34816, 5120)])
+@pytest.mark.parametrize("M,N,K", [(17, 16, 256), (32, 16, 2560),
+                                   (24, 48, 256), (20, 4096, 1024),
+                                   (32, 4112, 2560), (17, 6000 * 16, 768),
+                                   (32, 34816, 2560)])
 def test_resident_plan_more_shapes(M, N, K):
+    """The resident kernel now serves 17..32 rows (two MFMA row tiles) and,
+    on the workspace path, the parts of a split K."""
     p = q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_TILED16)
     assert p["kernel"] == q4.KERNEL_TILED_RESIDENT
     resident_model(M, N, K, p)
@@ -358,8 +417,11 @@ def test_resident_lds_layout_gives_each_lane_its_operand(M, K):
                                    (1, 16, 10496), (8, 1600, 7168)])
 def test_workspace_plan_split_parts(M, N, K):
     p = q4.q4_gemm_verify_tiled_ws_plan(M, N, K)
-    # split when K > 5120 and (M >= 8 or K > 10240); otherwise the plain plan
-    if not (M >= 8 or K > 10240):
+    # up to 24 records the plain plan (the K-slice kernel) unless K > 5120,
+    # M >= 8 and fewer than 512 tiles; beyond 24 records, split when M >= 8
+    # or K > 10240; otherwise the plain plan
+    few_tiles_split = K > 5120 and M >= 8 and N // 16 < 512
+    if (K // 256 <= 24 and not few_tiles_split) or not (M >= 8 or K > 10240):
         assert p == q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_TILED16)
         assert p["workspace_bytes"] == 0
         return
