@@ -196,13 +196,10 @@ q4_plan plan_gemm_tiled_ws(int M, int64_t N, int64_t K, int cus) {
     std::memset(&p, 0, sizeof p);  // no plan: the call is rejected
     return p;
   }
-  // The K-slice kernel, except for K > 5120 with few tiles at M >= 8 (the
-  // 5120 x 6144 output projections: 320 tiles give a CU 1 or 2 of them,
-  // and the parts of a split K balance better: 10.7 against 11.4 us at
-  // M = 16, measured on MI355X).
-  const int64_t tiles = N / kTileRows;
-  if (M <= Q4_MAX_ROWS && records <= kKsliceMaxRecords &&
-      !(M >= 8 && K > kResidentMaxK && tiles < 2 * cus))
+  // The K-slice kernel whenever it applies: on the 5120 x 6144 output
+  // projections it beats four parts of a split K at every M (10.3 against
+  // 12.2 us at M = 16, measured on MI355X).
+  if (M <= Q4_MAX_ROWS && records <= kKsliceMaxRecords)
     return plan_gemm_tiled(M, N, K, cus);
   if (K > kResidentMaxK && (M >= 8 || K > 2 * kResidentMaxK)) {
     // Parts of K taken by separate workgroups: enough for a part's

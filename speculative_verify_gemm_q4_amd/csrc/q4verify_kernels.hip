@@ -733,15 +733,26 @@ int launch_tiled(const q4_plan &p, const void *x, const void *W, float *y,
 // tile's 46 KB (at K = 5120) as one contiguous run:
 //  * the wave loads its two records' activations once, straight into MFMA
 //    operand registers (lane (j, kb), half h: inputs 64 gi + 16 kb + 8 h ..
-//    +7 of row j of record q; rows >= M fall past the resource and read as
-//    zeros), and forms the seed -128 * sum(x) of each of its 8 groups once,
-//    with two MFMAs per group -- not per tile;
+//    +7 of row j of record q; rows >= M, and a second record past K, fall
+//    past the resource and read as zeros), and forms the seed
+//    -128 * sum(x) of each of its 8 groups once, with two MFMAs per group --
+//    not per tile;
 //  * per tile it multiplies its two records (two MFMAs per group, seeded
 //    with that group's sum) and writes its partial 16 x 16 sum to LDS;
 //  * every kslice_batch(W) tiles the workgroup adds the waves' partial sums
 //    in wave order and writes y.
-// The weights of tile t + 1 are in flight while tile t is multiplied; the
-// first tile's weights are issued before the activations.  Summation order
+// The activation loads are issued first, without branches, so that the seed
+// MFMAs wait for them alone; then the first tile's weights.  The weights of
+// tile t + 1 are in flight while tile t is multiplied.
+//
+// Workgroups are dealt to the 8 XCDs in turn (b, b + 8, ... on XCD b % 8), so
+// tiles are assigned by rank XCD after XCD: every XCD streams the same share
+// (+-1 tile per workgroup).  A CU serves the loads of its older waves first,
+// so without a barrier the youngest waves of a long run fall microseconds
+// behind and finish alone, with few loads in flight; with 8 or more tiles
+// per workgroup the waves therefore meet at a barrier once per tile, after
+// issuing the next tile's loads.  (With fewer tiles the barrier costs more
+// than the lag: the first tile's wait then dominates.)  Summation order
 // depends only on (N, K), so results do not depend on M and repeated calls
 // are bitwise equal.
 template <int W>
@@ -756,8 +767,12 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 15;
   const int kb = lane >> 4;
-  const int t0 = static_cast<int>(static_cast<int64_t>(T) * blockIdx.x / gridDim.x);
-  const int t1 = static_cast<int>(static_cast<int64_t>(T) * (blockIdx.x + 1) / gridDim.x);
+  const int G = static_cast<int>(gridDim.x);
+  const int b = static_cast<int>(blockIdx.x);
+  const int rank = (b & 7) * (G >> 3) + min(b & 7, G & 7) + (b >> 3);
+  const int t0 = static_cast<int>(static_cast<int64_t>(T) * rank / G);
+  const int t1 = static_cast<int>(static_cast<int64_t>(T) * (rank + 1) / G);
+  const bool in_step = t1 - t0 >= 8;
   const int q0 = 2 * wave;
   const int nq = Q - q0 >= 2 ? 2 : Q - q0;  // 1 or 2
 
@@ -784,13 +799,10 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
   };
   constexpr int S = 2;
   Stage st[S];
-  load(st[0]);
-
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(x), 0,
       static_cast<int>(static_cast<uint32_t>(M) * static_cast<uint32_t>(K) * 2u),
       kBufferWord3);
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
   const u32x4 neg = {kNeg128Pair, kNeg128Pair, kNeg128Pair, kNeg128Pair};
   const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
   u32x4 xa[2][4][2];
@@ -798,13 +810,18 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
 #pragma unroll
   for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
-    for (int gi = 0; gi < 4; ++gi) {
+    for (int gi = 0; gi < 4; ++gi)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const uint32_t off = (static_cast<uint32_t>(j) * K + 256 * (q0 + qq) +
                               64 * gi + 16 * kb + 8 * h) * 2;
-        xa[qq][gi][h] = qq < nq ? buffer_load16<0>(xr, off, 0) : zero4;
+        xa[qq][gi][h] = buffer_load16<0>(xr, off, qq < nq ? 0u : 0x7FFFFFF0u);
       }
+  load(st[0]);
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
       const f32x4 s = mfma16x16x32(xa[qq][gi][0], neg, fzero);
       xn[qq][gi] = mfma16x16x32(xa[qq][gi][1], neg, s);
     }
@@ -837,6 +854,8 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
 #pragma unroll
     for (int i = 0; i < S; ++i) {
       load(st[(i + 1) % S]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (in_step) __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       if (t + i < t1) {  // the same for every wave: barriers below are safe
         f32x4 acc = fzero;

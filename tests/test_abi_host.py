@@ -7,6 +7,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import subprocess
 import re
 
 import pytest
@@ -28,7 +29,8 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    with open(HEADER) as f:
+        text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(q4_\w+)\s*\(", text)))
 
@@ -40,7 +42,8 @@ def test_header_declares_the_binding_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    nm = os.popen(f"nm -D --defined-only {q4.LIB_PATH}").read()
+    nm = subprocess.run(["nm", "-D", "--defined-only", q4.LIB_PATH],
+                        capture_output=True, text=True, check=True).stdout
     for name in declared_functions():
         assert re.search(rf"\bT {name}$", nm, flags=re.M), name
 

@@ -405,7 +405,7 @@ def gemm_tiled_ws(q4, x, Wt, M, N, K, fill=float("nan")):
 
 # K > 5120 (split across workgroups, partial sums reduced in part order),
 # including tiny N (most waves empty) and a part count above 4
-WS_SHAPES = [(16, 5120, 6400), (16, 5120, 6144), (3, 5120, 17408), (1, 16, 10496),
+WS_SHAPES = [(16, 5120, 6400), (16, 5120, 7168), (3, 5120, 17408), (1, 16, 10496),
              (16, 48, 10240), (8, 1600, 7168), (16, 256, 65536),
              (9, 32, 6656)]
 

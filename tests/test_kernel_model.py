@@ -196,8 +196,31 @@ def kslice_model(M, N, K, p):
     assert p["workspace_bytes"] == 0
     hits = np.zeros((T, Q), dtype=np.int32)
     writes = np.zeros(T, dtype=np.int32)
+    # workgroup b runs on XCD b % 8; ranks are counted XCD after XCD
+    ranks = [(b & 7) * (G >> 3) + min(b & 7, G & 7) + (b >> 3)
+             for b in range(G)]
+    assert sorted(ranks) == list(range(G))
+    # activation operand loads of wave w: a real row's own record, else past
+    # the resource (zeros)
+    x_bytes = M * K * 2
+    for w in range(W):
+        nq = min(2, Q - 2 * w)
+        for lane in range(64):
+            j, kb = lane & 15, lane >> 4
+            for qq in range(2):
+                for gi in range(4):
+                    for h in range(2):
+                        k = 256 * (2 * w + qq) + 64 * gi + 16 * kb + 8 * h
+                        off = (j * K + k) * 2
+                        if qq < nq and j < M:
+                            assert k + 8 <= K and off + 16 <= x_bytes
+                        elif qq < nq:
+                            assert off >= x_bytes
+                        else:
+                            assert x_bytes <= off + 0x7FFFFFF0 < 2 ** 32
     for b in range(G):
-        t0, t1 = T * b // G, T * (b + 1) // G
+        r = ranks[b]
+        t0, t1 = T * r // G, T * (r + 1) // G
         span = (t1 - t0) * Q * 2304
         assert span < 0x7FFFFFF0
         for w in range(W):
@@ -229,8 +252,7 @@ def test_kslice_plan_shapes(M, N, K):
     p = q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_TILED16)
     assert p["kernel"] == q4.KERNEL_TILED_KSLICE
     kslice_model(M, N, K, p)
-    if not (K > 5120 and M >= 8 and N // 16 < 512):
-        assert q4.q4_gemm_verify_tiled_ws_plan(M, N, K) == p
+    assert q4.q4_gemm_verify_tiled_ws_plan(M, N, K) == p
 
 
 # resident-activation kernel (K <= 5120): workgroup b owns tiles
@@ -417,11 +439,9 @@ def test_resident_lds_layout_gives_each_lane_its_operand(M, K):
                                    (1, 16, 10496), (8, 1600, 7168)])
 def test_workspace_plan_split_parts(M, N, K):
     p = q4.q4_gemm_verify_tiled_ws_plan(M, N, K)
-    # up to 24 records the plain plan (the K-slice kernel) unless K > 5120,
-    # M >= 8 and fewer than 512 tiles; beyond 24 records, split when M >= 8
-    # or K > 10240; otherwise the plain plan
-    few_tiles_split = K > 5120 and M >= 8 and N // 16 < 512
-    if (K // 256 <= 24 and not few_tiles_split) or not (M >= 8 or K > 10240):
+    # up to 24 records the plain plan (the K-slice kernel); beyond 24
+    # records, split when M >= 8 or K > 10240; otherwise the plain plan
+    if K // 256 <= 24 or not (M >= 8 or K > 10240):
         assert p == q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_TILED16)
         assert p["workspace_bytes"] == 0
         return
