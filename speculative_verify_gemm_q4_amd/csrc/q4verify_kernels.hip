@@ -726,6 +726,14 @@ int launch_tiled(const q4_plan &p, const void *x, const void *W, float *y,
   return launch_status();
 }
 
+// s_barrier after this wave's LDS accesses have completed; unlike
+// __syncthreads it does not wait for outstanding global loads.
+__device__ __forceinline__ void kslice_lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // The product for M <= 16 and K <= 6144 with each wave's slice of K of the
 // activations in registers.  One workgroup per CU owns whole tiles
 // [t0, t1); its W = ceil(Q / 2) waves all work on the same tile at once,
@@ -741,8 +749,12 @@ int launch_tiled(const q4_plan &p, const void *x, const void *W, float *y,
 //    with that group's sum) and writes its partial 16 x 16 sum to LDS;
 //  * every kslice_batch(W) tiles the workgroup adds the waves' partial sums
 //    in wave order and writes y.
-// The activation loads are issued first, without branches, so that the seed
-// MFMAs wait for them alone; then the first tile's weights.  The weights of
+// The activation loads are issued first, without branches, then the first
+// tile's weights, so that the seed MFMAs wait for the activations alone.
+// For M >= 8 they are row-contiguous (each load brings 512 B runs of two
+// rows) and pass through LDS into the operand layout: loads straight in the
+// operand layout touch 16 rows 2K bytes apart each, which the L2 serves far
+// more slowly (the first tile at M = 16 came 2 us later).  The weights of
 // tile t + 1 are in flight while tile t is multiplied.
 //
 // Workgroups are dealt to the 8 XCDs in turn (b, b + 8, ... on XCD b % 8), so
@@ -755,11 +767,12 @@ int launch_tiled(const q4_plan &p, const void *x, const void *W, float *y,
 // than the lag: the first tile's wait then dominates.)  Summation order
 // depends only on (N, K), so results do not depend on M and repeated calls
 // are bitwise equal.
-template <int W>
+template <int W, bool kRowLoads>
 __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ Wt,
     float *__restrict__ y, int M, int N, int K) {
   constexpr int NB = kslice_batch(W);  // tiles per reduction batch
+  static_assert(NB >= 8, "the activation staging areas (8 KB per wave) fit in part");
   __shared__ f32x4 part[NB * W * 64];
   const int T = N >> 4;
   const int Q = K >> 8;
@@ -772,6 +785,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
   const int rank = (b & 7) * (G >> 3) + min(b & 7, G & 7) + (b >> 3);
   const int t0 = static_cast<int>(static_cast<int64_t>(T) * rank / G);
   const int t1 = static_cast<int>(static_cast<int64_t>(T) * (rank + 1) / G);
+  __builtin_assume(t1 > t0);  // the grid has at most one workgroup per tile
   const bool in_step = t1 - t0 >= 8;
   const int q0 = 2 * wave;
   const int nq = Q - q0 >= 2 ? 2 : Q - q0;  // 1 or 2
@@ -807,17 +821,60 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
   const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
   u32x4 xa[2][4][2];
   f32x4 xn[2][4];
+  if constexpr (kRowLoads) {
+    // Row-contiguous loads (load i of record qq brings rows 2i and 2i + 1,
+    // 512 B each), then through LDS into the operand layout.  Lane l of
+    // load i holds chunk c = l & 31 (inputs 8c .. 8c+7) of row
+    // r = 2i + (l >> 5); it is stored at row r, chunk c ^ (r & 7) of the
+    // wave's 8 KB area, and lane (j, kb) reads chunk 8 gi + 2 kb + h of row
+    // j for operand (gi, h): the XOR keeps both sides free of bank
+    // conflicts.
+    u32x4 xrow[2][8];
 #pragma unroll
-  for (int qq = 0; qq < 2; ++qq)
+    for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
-    for (int gi = 0; gi < 4; ++gi)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t off = (static_cast<uint32_t>(j) * K + 256 * (q0 + qq) +
-                              64 * gi + 16 * kb + 8 * h) * 2;
-        xa[qq][gi][h] = buffer_load16<0>(xr, off, qq < nq ? 0u : 0x7FFFFFF0u);
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t r = 2 * i + (lane >> 5);
+        const uint32_t off = (r * K + 256 * (q0 + qq) + 8 * (lane & 31)) * 2;
+        xrow[qq][i] = buffer_load16<0>(xr, off, qq < nq ? 0u : 0x7FFFFFF0u);
       }
-  load(st[0]);
+    load(st[0]);
+    char *area = reinterpret_cast<char *>(part) + wave * 8192;
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 2 * i + (lane >> 5);
+        const int c = (lane & 31) ^ (r & 7);
+        *reinterpret_cast<u32x4 *>(area + r * 512 + c * 16) = xrow[qq][i];
+      }
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int c = (8 * gi + 2 * kb + h) ^ (j & 7);
+          xa[qq][gi][h] = *reinterpret_cast<const u32x4 *>(area + j * 512 + c * 16);
+        }
+    }
+    // the areas alias the partial sums: every wave has its operands in
+    // registers before any wave writes a partial sum
+    kslice_lds_barrier();
+  } else {
+    // direct loads in the operand layout: lane (j, kb), operand (gi, h)
+    // reads inputs 64 gi + 16 kb + 8 h .. +7 of row j
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t off = (static_cast<uint32_t>(j) * K + 256 * (q0 + qq) +
+                                64 * gi + 16 * kb + 8 * h) * 2;
+          xa[qq][gi][h] = buffer_load16<0>(xr, off, qq < nq ? 0u : 0x7FFFFFF0u);
+        }
+    load(st[0]);
+    __builtin_amdgcn_sched_barrier(0);  // every load issued before the seeds
+  }
 #pragma unroll
   for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
@@ -887,9 +944,16 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
 template <int W>
 int launch_kslice_w(const q4_plan &p, const void *x, const void *Wt, float *y,
                     int M, int N, int K, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_kslice_kernel<W>), dim3(p.grid), dim3(64 * W), 0,
-                     stream, static_cast<const uint16_t *>(x),
-                     static_cast<const uint8_t *>(Wt), y, M, N, K);
+  // M >= 8: row-contiguous activation loads through LDS; below that the rows
+  // past M are zeros anyway and direct loads save the LDS round trip
+  if (M >= 8)
+    hipLaunchKernelGGL((gemm_kslice_kernel<W, true>), dim3(p.grid), dim3(64 * W), 0,
+                       stream, static_cast<const uint16_t *>(x),
+                       static_cast<const uint8_t *>(Wt), y, M, N, K);
+  else
+    hipLaunchKernelGGL((gemm_kslice_kernel<W, false>), dim3(p.grid), dim3(64 * W), 0,
+                       stream, static_cast<const uint16_t *>(x),
+                       static_cast<const uint8_t *>(Wt), y, M, N, K);
   return launch_status();
 }
 

@@ -270,8 +270,11 @@ TILED = [(16, 16, 256), (1, 16, 256), (16, 256, 512), (5, 1600, 1024),
          (5, 1600, 2048), (16, 5120, 6144), (3, 5120, 17408),
          (16, 80000, 1024), (7, 1040, 256), (16, 2048, 4096),
          # K-slice kernel: an odd record count (the last wave takes one),
-         # 23 records, and 20 tiles per workgroup (two reduction batches)
-         (4, 4800, 1280), (16, 512, 5888), (16, 81920, 5120)]
+         # 23 records, and 20 tiles per workgroup (two reduction batches);
+         # M >= 8 stages the activations through LDS: odd records, 8 and
+         # 11 rows, 12 waves
+         (4, 4800, 1280), (16, 512, 5888), (16, 81920, 5120),
+         (8, 4800, 1280), (11, 1600, 6144), (9, 48, 5632)]
 
 
 @pytest.mark.parametrize("N,K", [(16, 256), (256, 512), (1600, 2048),

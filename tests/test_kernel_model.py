@@ -218,6 +218,8 @@ def kslice_model(M, N, K, p):
                             assert off >= x_bytes
                         else:
                             assert x_bytes <= off + 0x7FFFFFF0 < 2 ** 32
+    if M >= 8:
+        kslice_row_staging_model(M, K, W, p["lds_bytes"])
     for b in range(G):
         r = ranks[b]
         t0, t1 = T * r // G, T * (r + 1) // G
@@ -243,8 +245,62 @@ def kslice_model(M, N, K, p):
     assert np.all(writes == 1)
 
 
+def kslice_row_staging_model(M, K, W, lds_bytes):
+    """M >= 8: the activations arrive by row-contiguous loads and pass
+    through an 8 KB LDS area per wave.  Every operand register must end up
+    holding exactly what the direct operand-layout load would have read,
+    the LDS stores of one round must not collide, and the areas must fit."""
+    Q = K // 256
+    x_bytes = M * K * 2
+    assert W * 8192 <= lds_bytes
+    for w in range(W):
+        nq = min(2, Q - 2 * w)
+        for qq in range(2):
+            # what lane l of load i holds: (row, input) or None (zeros)
+            area = {}
+            for i in range(8):
+                for lane in range(64):
+                    r, c = 2 * i + (lane >> 5), lane & 31
+                    k = 256 * (2 * w + qq) + 8 * c
+                    off = (r * K + k) * 2
+                    if qq < nq and r < M:
+                        assert off + 16 <= x_bytes and k + 8 <= K
+                        val = (r, k)
+                    else:
+                        assert off + (0 if qq < nq else 0x7FFFFFF0) >= x_bytes
+                        val = None
+                    addr = w * 8192 + r * 512 + (c ^ (r & 7)) * 16
+                    assert addr not in area
+                    area[addr] = val
+            assert len(area) == 512
+            for lane in range(64):
+                j, kb = lane & 15, lane >> 4
+                for gi in range(4):
+                    for h in range(2):
+                        c = (8 * gi + 2 * kb + h) ^ (j & 7)
+                        got = area[w * 8192 + j * 512 + c * 16]
+                        k = 256 * (2 * w + qq) + 64 * gi + 16 * kb + 8 * h
+                        want = (j, k) if (qq < nq and j < M) else None
+                        assert got == want, (w, qq, lane, gi, h)
+    # bank groups of 16 B (128 B per LDS cycle): the 8 lanes of a group of
+    # stores, and of a group of operand reads, hit 8 distinct groups
+    for i in range(8):
+        for g in range(8):
+            lanes = range(8 * g, 8 * g + 8)
+            banks = {((l & 31) ^ ((2 * i + (l >> 5)) & 7)) & 7 for l in lanes}
+            assert len(banks) == 8
+    for gi in range(4):
+        for h in range(2):
+            for g in range(8):
+                lanes = range(8 * g, 8 * g + 8)
+                banks = {((8 * gi + 2 * (l >> 4) + h) ^ ((l & 15) & 7)) & 7
+                         for l in lanes}
+                assert len(banks) == 8
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 16, 256), (16, 16, 5120),
                                    (16, 48, 256), (7, 4096, 1024),
+                                   (8, 4096, 1280), (9, 512, 6144),
                                    (16, 4112, 5120), (1, 6000 * 16, 768),
                                    (16, 34816, 5120), (16, 5120, 6144),
                                    (3, 16, 5888), (16, 248320, 5120)])
