@@ -151,19 +151,25 @@ bool plan_resident(int M, int64_t N, int64_t K, int cus, int parts,
   return true;
 }
 
-// Plan of the K-slice kernel (M <= 16, K <= 6144): one workgroup per CU,
-// ceil(Q / 2) waves.
-bool plan_kslice(int M, int64_t N, int64_t K, int cus, q4_plan *out) {
+// Plan of the K-slice kernel (M <= 16): ceil(Q_p / 2) waves for parts of
+// Q_p <= 24 records.  With one part (K <= 6144) one workgroup per CU owns a
+// run of tiles; with P parts (a workspace for parts 1 .. P-1) the grid is
+// P groups of min(tiles, CUs / P) workgroups.
+bool plan_kslice(int M, int64_t N, int64_t K, int cus, int parts, q4_plan *out) {
   const int64_t tiles = N / kTileRows;
   const int64_t records = K / (kRecordGroups * Q4_GROUP);
-  if (M > Q4_MAX_ROWS || records > kKsliceMaxRecords) return false;
-  const int64_t g = tiles < cus ? tiles : cus;
+  const int64_t part_records = (records + parts - 1) / parts;
+  if (M > Q4_MAX_ROWS || parts < 1 || part_records > kKsliceMaxRecords ||
+      parts > cus)
+    return false;
+  const int64_t per_part_cus = cus / parts;
+  const int64_t g = tiles < per_part_cus ? tiles : per_part_cus;
   const int64_t per = (tiles + g - 1) / g;
   if (per * records * kRecordBytes >= 0x7FFFFFF0LL) return false;
-  const int waves = static_cast<int>((records + 1) / 2);
+  const int waves = static_cast<int>((part_records + 1) / 2);
   q4_plan p;
   std::memset(&p, 0, sizeof p);
-  p.grid = static_cast<uint32_t>(g);
+  p.grid = static_cast<uint32_t>(g * parts);
   p.block = static_cast<uint32_t>(64 * waves);
   p.row_tiles = static_cast<uint32_t>(per);
   p.tiles_per_wave = 1;
@@ -171,21 +177,36 @@ bool plan_kslice(int M, int64_t N, int64_t K, int cus, q4_plan *out) {
   p.lookahead = kRecordGroups * 2;
   p.kernel = Q4_KERNEL_TILED_KSLICE;
   p.lds_bytes = static_cast<uint32_t>(kslice_batch(waves) * waves * 1024);
-  p.k_parts = 1;
+  p.k_parts = static_cast<uint32_t>(parts);
   p.m_tiles = 1;
+  p.workspace_bytes = static_cast<uint64_t>(parts - 1) *
+                      static_cast<uint64_t>(M) * static_cast<uint64_t>(N) * 4;
   *out = p;
   return true;
 }
 
 q4_plan plan_gemm_tiled_ws(int M, int64_t N, int64_t K, int cus) {
-  // Up to 16 rows and 24 records per tile the K-slice kernel needs no split.
-  // Beyond, split K across workgroups when its activations exceed the LDS --
-  // except for K <= 2 x 5120 at M < 8, where the streaming kernel is as fast
-  // without the second launch.
+  // Up to 16 rows the K-slice kernel: in one part up to 24 records per tile,
+  // beyond that in P parts of K (at least 4, a power of two, so that the 320
+  // tiles of the N = 5120 projections give every CU whole tiles): 15.9
+  // against 16.9 us for the resident kernel's split on 5120 x 17408 at
+  // M = 16, measured on MI355X.  32 rows:
+  // the resident kernel, split whenever its activations exceed the LDS.
   const int m_tiles = M > Q4_MAX_ROWS ? 2 : 1;
   const int64_t records = K / (kRecordGroups * Q4_GROUP);
+  if (m_tiles == 1) {
+    // no split for K <= 6144, nor for K <= 2 x 5120 at M < 8, where the
+    // streaming kernel is as fast without the second launch
+    if (records <= kKsliceMaxRecords || (M < 8 && K <= 2 * kResidentMaxK))
+      return plan_gemm_tiled(M, N, K, cus);
+    int64_t parts = 4;
+    while (parts * kKsliceMaxRecords < records) parts *= 2;
+    q4_plan p;
+    if (plan_kslice(M, N, K, cus, static_cast<int>(parts), &p)) return p;
+    return plan_gemm_tiled(M, N, K, cus);
+  }
   const int64_t per_part = kResidentMaxRecords / m_tiles;
-  if (m_tiles == 2 && records > per_part) {
+  if (records > per_part) {
     // 32 rows: split whenever the activations exceed the LDS, into a power
     // of two parts (2 for K = 5120, 8 for 17408)
     int64_t parts = 2;
@@ -195,21 +216,6 @@ q4_plan plan_gemm_tiled_ws(int M, int64_t N, int64_t K, int cus) {
       return p;
     std::memset(&p, 0, sizeof p);  // no plan: the call is rejected
     return p;
-  }
-  // The K-slice kernel whenever it applies: on the 5120 x 6144 output
-  // projections it beats four parts of a split K at every M (10.3 against
-  // 12.2 us at M = 16, measured on MI355X).
-  if (M <= Q4_MAX_ROWS && records <= kKsliceMaxRecords)
-    return plan_gemm_tiled(M, N, K, cus);
-  if (K > kResidentMaxK && (M >= 8 || K > 2 * kResidentMaxK)) {
-    // Parts of K taken by separate workgroups: enough for a part's
-    // activations to fit the LDS, and at least 4, a power of two, so that
-    // the 320 tiles of the N = 5120 projections give every CU whole tiles.
-    int64_t parts = 4;
-    while (parts * per_part < records) parts *= 2;
-    q4_plan p;
-    if (parts <= cus && plan_resident(M, N, K, cus, static_cast<int>(parts), &p))
-      return p;
   }
   return plan_gemm_tiled(M, N, K, cus);
 }
@@ -222,7 +228,7 @@ q4_plan plan_gemm_tiled(int M, int64_t N, int64_t K, int cus) {
     // LM head and the GDN in-projection faster than with the activations in
     // LDS, attention's in-projection at M = 16 even).
     q4_plan p;
-    if (plan_kslice(M, N, K, cus, &p)) return p;
+    if (plan_kslice(M, N, K, cus, 1, &p)) return p;
   }
   if (K <= kResidentMaxK) {
     // Activations resident in LDS: one workgroup per CU (the LDS admits no

@@ -734,8 +734,8 @@ __device__ __forceinline__ void kslice_lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// The product for M <= 16 and K <= 6144 with each wave's slice of K of the
-// activations in registers.  One workgroup per CU owns whole tiles
+// The product for M <= 16 with each wave's slice of K of the activations in
+// registers (K <= 6144, or parts of K of at most 24 records).  One workgroup per CU owns whole tiles
 // [t0, t1); its W = ceil(Q / 2) waves all work on the same tile at once,
 // wave w on records 2w and 2w + 1 of it, so that the workgroup reads each
 // tile's 46 KB (at K = 5120) as one contiguous run:
@@ -757,9 +757,16 @@ __device__ __forceinline__ void kslice_lds_barrier() {
 // more slowly (the first tile at M = 16 came 2 us later).  The weights of
 // tile t + 1 are in flight while tile t is multiplied.
 //
+// With a workspace, K beyond 24 records is cut into P parts: the grid is P
+// groups of Gt workgroups, the group of part p takes records
+// [Q p / P, Q (p+1) / P) of every tile, part 0 writes y and part p > 0 its
+// M x N slice p - 1 of the workspace, which reduce_parts_kernel then adds to
+// y in part order.
+//
 // Workgroups are dealt to the 8 XCDs in turn (b, b + 8, ... on XCD b % 8), so
-// tiles are assigned by rank XCD after XCD: every XCD streams the same share
-// (+-1 tile per workgroup).  A CU serves the loads of its older waves first,
+// tiles (and parts) are assigned by rank XCD after XCD: every XCD streams the
+// same share (+-1 tile per workgroup), and with parts an XCD reads one or
+// two parts' activations.  A CU serves the loads of its older waves first,
 // so without a barrier the youngest waves of a long run fall microseconds
 // behind and finish alone, with few loads in flight; with 8 or more tiles
 // per workgroup the waves therefore meet at a barrier once per tile, after
@@ -770,7 +777,7 @@ __device__ __forceinline__ void kslice_lds_barrier() {
 template <int W, bool kRowLoads>
 __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ Wt,
-    float *__restrict__ y, int M, int N, int K) {
+    float *__restrict__ y, float *__restrict__ ws, int M, int N, int K, int P) {
   constexpr int NB = kslice_batch(W);  // tiles per reduction batch
   static_assert(NB >= 8, "the activation staging areas (8 KB per wave) fit in part");
   __shared__ f32x4 part[NB * W * 64];
@@ -783,12 +790,19 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
   const int G = static_cast<int>(gridDim.x);
   const int b = static_cast<int>(blockIdx.x);
   const int rank = (b & 7) * (G >> 3) + min(b & 7, G & 7) + (b >> 3);
-  const int t0 = static_cast<int>(static_cast<int64_t>(T) * rank / G);
-  const int t1 = static_cast<int>(static_cast<int64_t>(T) * (rank + 1) / G);
-  __builtin_assume(t1 > t0);  // the grid has at most one workgroup per tile
+  // rank -> part p of K (records [qa, qa + nrec)) and tile group g
+  const int Gt = G / P;
+  const int pk = rank / Gt;
+  const int g = rank - pk * Gt;
+  const int t0 = static_cast<int>(static_cast<int64_t>(T) * g / Gt);
+  const int t1 = static_cast<int>(static_cast<int64_t>(T) * (g + 1) / Gt);
+  __builtin_assume(t1 > t0);  // a part has at most one workgroup per tile
   const bool in_step = t1 - t0 >= 8;
-  const int q0 = 2 * wave;
-  const int nq = Q - q0 >= 2 ? 2 : Q - q0;  // 1 or 2
+  const int qa = Q * pk / P;
+  const int nrec = Q * (pk + 1) / P - qa;
+  const int q0 = qa + 2 * wave;
+  const int nq = min(max(nrec - 2 * wave, 0), 2);  // 0, 1 or 2
+  float *const out = pk == 0 ? y : ws + static_cast<uint64_t>(pk - 1) * M * N;
 
   // weights of the workgroup's tiles; a record past them (or past the
   // wave's slice) gets an offset past the resource and reads zeros
@@ -929,7 +943,10 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int m = (l >> 4) * 4 + r;
-              if (m < M) y[static_cast<uint64_t>(m) * N + n] = v[r];
+              // non-temporal: on the LM head at M = 16 (15.9 MB of y)
+              // plain stores cost 124 us per call against 119
+              if (m < M)
+                __builtin_nontemporal_store(v[r], &out[static_cast<uint64_t>(m) * N + n]);
             }
           }
           __syncthreads();
@@ -942,27 +959,37 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
 }
 
 template <int W>
-int launch_kslice_w(const q4_plan &p, const void *x, const void *Wt, float *y,
-                    int M, int N, int K, hipStream_t stream) {
+void launch_kslice_w(const q4_plan &p, const void *x, const void *Wt, float *y,
+                     float *ws, int M, int N, int K, hipStream_t stream) {
+  const int parts = static_cast<int>(p.k_parts);
   // M >= 8: row-contiguous activation loads through LDS; below that the rows
   // past M are zeros anyway and direct loads save the LDS round trip
   if (M >= 8)
     hipLaunchKernelGGL((gemm_kslice_kernel<W, true>), dim3(p.grid), dim3(64 * W), 0,
                        stream, static_cast<const uint16_t *>(x),
-                       static_cast<const uint8_t *>(Wt), y, M, N, K);
+                       static_cast<const uint8_t *>(Wt), y, ws, M, N, K, parts);
   else
     hipLaunchKernelGGL((gemm_kslice_kernel<W, false>), dim3(p.grid), dim3(64 * W), 0,
                        stream, static_cast<const uint16_t *>(x),
-                       static_cast<const uint8_t *>(Wt), y, M, N, K);
+                       static_cast<const uint8_t *>(Wt), y, ws, M, N, K, parts);
+}
+
+// Part sums of a K split: y += workspace slices 1 .. P-1, in part order.
+int launch_reduce_parts(float *y, const float *ws, int M, int N, int parts,
+                        hipStream_t stream) {
+  const uint32_t mn4 = static_cast<uint32_t>(M) * static_cast<uint32_t>(N) / 4;
+  hipLaunchKernelGGL(reduce_parts_kernel, dim3((mn4 + 255) / 256), dim3(256), 0,
+                     stream, y, ws, mn4, parts);
   return launch_status();
 }
 
 int launch_kslice(const q4_plan &p, const void *x, const void *Wt, float *y,
-                  int M, int N, int K, hipStream_t stream) {
+                  float *ws, int M, int N, int K, hipStream_t stream) {
   switch (p.block / 64) {
-#define Q4V_KSLICE_CASE(W) \
-  case W:                  \
-    return launch_kslice_w<W>(p, x, Wt, y, M, N, K, stream);
+#define Q4V_KSLICE_CASE(W)                                         \
+  case W:                                                          \
+    launch_kslice_w<W>(p, x, Wt, y, ws, M, N, K, stream);          \
+    break;
     Q4V_KSLICE_CASE(1) Q4V_KSLICE_CASE(2) Q4V_KSLICE_CASE(3)
     Q4V_KSLICE_CASE(4) Q4V_KSLICE_CASE(5) Q4V_KSLICE_CASE(6)
     Q4V_KSLICE_CASE(7) Q4V_KSLICE_CASE(8) Q4V_KSLICE_CASE(9)
@@ -970,6 +997,9 @@ int launch_kslice(const q4_plan &p, const void *x, const void *Wt, float *y,
 #undef Q4V_KSLICE_CASE
     default: return Q4_EINVAL;
   }
+  int st = launch_status();
+  if (st != Q4_OK || p.k_parts == 1) return st;
+  return launch_reduce_parts(y, ws, M, N, static_cast<int>(p.k_parts), stream);
 }
 
 template <int W, int RT>
@@ -1001,10 +1031,7 @@ int launch_resident(const q4_plan &p, const void *x, const void *W, float *y,
   }
   int st = launch_status();
   if (st != Q4_OK || parts == 1) return st;
-  const uint32_t mn4 = static_cast<uint32_t>(M) * static_cast<uint32_t>(N) / 4;
-  hipLaunchKernelGGL(reduce_parts_kernel, dim3((mn4 + 255) / 256), dim3(256), 0,
-                     stream, y, static_cast<const float *>(ws), mn4, parts);
-  return launch_status();
+  return launch_reduce_parts(y, ws, M, N, parts, stream);
 }
 
 template <int NTW, int KSW>
@@ -1052,7 +1079,7 @@ extern "C" int q4_gemm_verify_tiled(const void *x, const void *W, float *y,
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int n = static_cast<int>(N), k = static_cast<int>(K);
   if (p.kernel == Q4_KERNEL_TILED_KSLICE)
-    return q4v::launch_kslice(p, x, W, y, M, n, k, s);
+    return q4v::launch_kslice(p, x, W, y, nullptr, M, n, k, s);
   if (p.kernel == Q4_KERNEL_TILED_RESIDENT)
     return q4v::launch_resident(p, x, W, y, nullptr, M, n, k, s);
   const int key = static_cast<int>(p.tiles_per_wave * 100 + p.k_splits);
@@ -1089,11 +1116,14 @@ extern "C" int q4_gemm_verify_tiled_ws(const void *x, const void *W, float *y,
   }
   st = q4v::check_device();
   if (st != Q4_OK) return st;
-  if (p.kernel != Q4_KERNEL_TILED_RESIDENT)
-    return q4_gemm_verify_tiled(x, W, y, M, N, K, stream);
-  return q4v::launch_resident(p, x, W, y, static_cast<float *>(workspace), M,
-                              static_cast<int>(N), static_cast<int>(K),
-                              static_cast<hipStream_t>(stream));
+  float *ws = static_cast<float *>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int n = static_cast<int>(N), k = static_cast<int>(K);
+  if (p.kernel == Q4_KERNEL_TILED_KSLICE)
+    return q4v::launch_kslice(p, x, W, y, ws, M, n, k, s);
+  if (p.kernel == Q4_KERNEL_TILED_RESIDENT)
+    return q4v::launch_resident(p, x, W, y, ws, M, n, k, s);
+  return q4_gemm_verify_tiled(x, W, y, M, N, K, stream);
 }
 
 extern "C" int q4_repack(const void *W, void *W_tiled, int64_t N, int64_t K,

@@ -186,82 +186,95 @@ def test_tiled_plan_reads_every_record_once(M, N, K):
 # waves' partial sums added in wave order.
 
 def kslice_model(M, N, K, p):
+    """Work split of the K-slice kernel for plan p: workgroup b has rank
+    (b % 8) G/8 + b/8 (XCD after XCD), takes part pk = rank // Gt of K
+    (records [Q pk / P, Q (pk+1) / P)) and tile group rank % Gt; wave w
+    takes the part's records 2w and 2w + 1."""
     T, Q = N // 16, K // 256
+    P = p["k_parts"]
     W = p["block"] // 64
-    assert M <= 16 and Q <= 24 and W == (Q + 1) // 2 and p["k_parts"] == 1
+    Qp = -(-Q // P)
+    assert M <= 16 and Qp <= 24 and W == (Qp + 1) // 2 and p["m_tiles"] == 1
     G = p["grid"]
-    assert G == min(T, 256) and p["m_tiles"] == 1
+    Gt = min(T, 256 // P)
+    assert G == Gt * P
     NB = LDS_BYTES // (W * 1024)
     assert p["lds_bytes"] == NB * W * 1024 <= LDS_BYTES
-    assert p["workspace_bytes"] == 0
+    assert p["workspace_bytes"] == (P - 1) * M * N * 4
     hits = np.zeros((T, Q), dtype=np.int32)
-    writes = np.zeros(T, dtype=np.int32)
-    # workgroup b runs on XCD b % 8; ranks are counted XCD after XCD
+    writes = np.zeros((P, T), dtype=np.int32)
     ranks = [(b & 7) * (G >> 3) + min(b & 7, G & 7) + (b >> 3)
              for b in range(G)]
     assert sorted(ranks) == list(range(G))
-    # activation operand loads of wave w: a real row's own record, else past
-    # the resource (zeros)
     x_bytes = M * K * 2
-    for w in range(W):
-        nq = min(2, Q - 2 * w)
-        for lane in range(64):
-            j, kb = lane & 15, lane >> 4
-            for qq in range(2):
-                for gi in range(4):
-                    for h in range(2):
-                        k = 256 * (2 * w + qq) + 64 * gi + 16 * kb + 8 * h
-                        off = (j * K + k) * 2
-                        if qq < nq and j < M:
-                            assert k + 8 <= K and off + 16 <= x_bytes
-                        elif qq < nq:
-                            assert off >= x_bytes
-                        else:
-                            assert x_bytes <= off + 0x7FFFFFF0 < 2 ** 32
-    if M >= 8:
-        kslice_row_staging_model(M, K, W, p["lds_bytes"])
+    for pk in range(P):
+        qa = Q * pk // P
+        nrec = Q * (pk + 1) // P - qa
+        assert 1 <= nrec <= 2 * W
+        # activation operand loads of wave w: a real row's own record, else
+        # past the resource (zeros)
+        for w in range(W):
+            nq = min(max(nrec - 2 * w, 0), 2)
+            for lane in range(64):
+                j, kb = lane & 15, lane >> 4
+                for qq in range(2):
+                    for gi in range(4):
+                        for h in range(2):
+                            k = 256 * (qa + 2 * w + qq) + 64 * gi + 16 * kb + 8 * h
+                            off = (j * K + k) * 2
+                            if qq < nq and j < M:
+                                assert k + 8 <= K and off + 16 <= x_bytes
+                            elif qq < nq:
+                                assert off >= x_bytes
+                            else:
+                                assert x_bytes <= off + 0x7FFFFFF0 < 2 ** 32
+        if M >= 8:
+            kslice_row_staging_model(M, K, W, p["lds_bytes"], qa, nrec)
     for b in range(G):
         r = ranks[b]
-        t0, t1 = T * r // G, T * (r + 1) // G
+        pk, g = r // Gt, r % Gt
+        qa = Q * pk // P
+        nrec = Q * (pk + 1) // P - qa
+        t0, t1 = T * g // Gt, T * (g + 1) // Gt
+        assert t1 > t0
         span = (t1 - t0) * Q * 2304
         assert span < 0x7FFFFFF0
         for w in range(W):
-            nq = min(2, Q - 2 * w)
-            assert nq >= 1
+            nq = min(max(nrec - 2 * w, 0), 2)
             for tl in range(t1 - t0):
                 for qq in range(nq):
-                    off = (tl * Q + 2 * w + qq) * 2304
+                    off = (tl * Q + qa + 2 * w + qq) * 2304
                     assert off + 2304 <= span
-                    hits[t0 + tl, 2 * w + qq] += 1
+                    hits[t0 + tl, qa + 2 * w + qq] += 1
         # batches: a flush after every NB tiles and after the last
         tb = t0
         for t in range(t0, t1):
             assert (t - tb) < NB
             if t - tb == NB - 1 or t == t1 - 1:
                 for tt in range(tb, t + 1):
-                    writes[tt] += 1
+                    writes[pk, tt] += 1
                 tb = t + 1
     assert np.all(hits == 1)
     assert np.all(writes == 1)
 
 
-def kslice_row_staging_model(M, K, W, lds_bytes):
+def kslice_row_staging_model(M, K, W, lds_bytes, qa, nrec):
     """M >= 8: the activations arrive by row-contiguous loads and pass
     through an 8 KB LDS area per wave.  Every operand register must end up
     holding exactly what the direct operand-layout load would have read,
-    the LDS stores of one round must not collide, and the areas must fit."""
-    Q = K // 256
+    the LDS stores of one round must not collide, and the areas must fit.
+    The part's records are [qa, qa + nrec)."""
     x_bytes = M * K * 2
     assert W * 8192 <= lds_bytes
     for w in range(W):
-        nq = min(2, Q - 2 * w)
+        nq = min(max(nrec - 2 * w, 0), 2)
         for qq in range(2):
             # what lane l of load i holds: (row, input) or None (zeros)
             area = {}
             for i in range(8):
                 for lane in range(64):
                     r, c = 2 * i + (lane >> 5), lane & 31
-                    k = 256 * (2 * w + qq) + 8 * c
+                    k = 256 * (qa + 2 * w + qq) + 8 * c
                     off = (r * K + k) * 2
                     if qq < nq and r < M:
                         assert off + 16 <= x_bytes and k + 8 <= K
@@ -279,7 +292,7 @@ def kslice_row_staging_model(M, K, W, lds_bytes):
                     for h in range(2):
                         c = (8 * gi + 2 * kb + h) ^ (j & 7)
                         got = area[w * 8192 + j * 512 + c * 16]
-                        k = 256 * (2 * w + qq) + 64 * gi + 16 * kb + 8 * h
+                        k = 256 * (qa + 2 * w + qq) + 64 * gi + 16 * kb + 8 * h
                         want = (j, k) if (qq < nq and j < M) else None
                         assert got == want, (w, qq, lane, gi, h)
     # bank groups of 16 B (128 B per LDS cycle): the 8 lanes of a group of
@@ -495,16 +508,19 @@ def test_resident_lds_layout_gives_each_lane_its_operand(M, K):
                                    (1, 16, 10496), (8, 1600, 7168)])
 def test_workspace_plan_split_parts(M, N, K):
     p = q4.q4_gemm_verify_tiled_ws_plan(M, N, K)
-    # up to 24 records the plain plan (the K-slice kernel); beyond 24
-    # records, split when M >= 8 or K > 10240; otherwise the plain plan
-    if K // 256 <= 24 or not (M >= 8 or K > 10240):
+    # up to 16 rows the K-slice kernel: one part up to 24 records, beyond
+    # that P >= 4 parts (a power of two) of at most 24 records -- except
+    # K <= 10240 at M < 8: no split
+    Q = K // 256
+    if Q <= 24 or (M < 8 and K <= 10240):
         assert p == q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_TILED16)
         assert p["workspace_bytes"] == 0
         return
-    assert p["kernel"] == q4.KERNEL_TILED_RESIDENT and p["k_parts"] > 1
+    assert p["kernel"] == q4.KERNEL_TILED_KSLICE and p["k_parts"] > 1
     P = p["k_parts"]
-    assert P >= 4 and P & (P - 1) == 0 and -(-(K // 256) // P) <= 20
-    resident_model(M, N, K, p)
+    assert P >= 4 and P & (P - 1) == 0 and -(-Q // P) <= 24
+    assert P == 4 or -(-Q // (P // 2)) > 24
+    kslice_model(M, N, K, p)
 
 
 
