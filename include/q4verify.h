@@ -289,6 +289,8 @@ int q4_gemm_verify_tiled_ws_plan(int M, int64_t N, int64_t K, q4_plan *out);
 #define Q4_SAMPLE_MAX_TOPK 32
 #define Q4_SAMPLE_MAX_DRAFT 16
 #define Q4_SAMPLE_MAX_ROWS 1024
+/* Longest row (vocabulary) q4_verify_sample takes: 512 slices of 16384. */
+#define Q4_SAMPLE_MAX_VOCAB 8388608
 
 typedef struct {
   float temperature; /* >= 0, finite; 0 = greedy                          */
@@ -298,7 +300,8 @@ typedef struct {
 } q4_sample_params;
 
 /* Device workspace bytes q4_verify_sample needs for (M, V).
- * Errors: Q4_EINVAL (M outside 1..Q4_SAMPLE_MAX_ROWS, V < 1 or V >= 2^31). */
+ * Errors: Q4_EINVAL (M outside 1..Q4_SAMPLE_MAX_ROWS, V outside
+ * 1..Q4_SAMPLE_MAX_VOCAB). */
 int q4_verify_sample_workspace(int M, int64_t V, uint64_t *bytes);
 
 /*

@@ -14,19 +14,20 @@
 // where orderable() maps IEEE order onto unsigned order (-0 is keyed as +0,
 // so the two zeros tie; a candidate's reported logit is then +0).  Two kernels:
 //  1. topk_slices_kernel: workgroup (slice of 16384 columns, row) of 16
-//     waves; each wave keeps a sorted top-32 list of keys in lanes 0..31
-//     while it reads its columns 64 at a time (four chunks' loads issued
-//     together): a chunk with no key above the list's 32nd is skipped (one
-//     compare and a ballot), otherwise it is sorted with a bitonic network
-//     across the wave and merged with the list (the list and the chunk's
-//     best 32 reversed form a bitonic sequence of 64, whose half-cleaner
-//     cascade leaves the best 32 in lanes 0..31).  The 16 lists are merged
-//     pairwise through LDS and the slice's best 32 written out.
+//     waves, 16 keys per lane in registers.  A wave sorts its 64 lane maxima;
+//     the 32nd of them, kw, is at most the wave's 32nd best key (32 distinct
+//     keys are >= it), so only keys >= kw can be among its best 32 (usually
+//     a few more than 32 are): they are packed into LDS and sorted.  The 16
+//     waves' lists are merged pairwise through LDS (a list and another
+//     reversed form a bitonic sequence that one half-cleaner cascade sorts)
+//     and the slice's best 32 written out.  Every compare-exchange stage
+//     swaps lanes with DPP or the gfx950 permlane swaps, not through LDS.
 //  2. sample_rows_kernel: one workgroup per row merges the slices' lists the
 //     same way and writes the top_k candidates; then lane i of wave 0 takes
 //     candidate i and the probabilities, the accept test and the residual
 //     draw are evaluated in fp32 with wave reductions, lane scans and
 //     ballots over the candidates in order.
+
 #include <hip/hip_runtime.h>
 
 #include "q4v_internal.h"
@@ -56,47 +57,126 @@ __device__ __forceinline__ uint32_t key_token(uint64_t key) {
   return 0xFFFFFFFFu - static_cast<uint32_t>(key);
 }
 
-__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
-  return __shfl_xor(v, m, 64);
+// Cross-lane exchange with the lane l ^ J, without LDS: DPP for J <= 8
+// (quad permutes and row mirrors: J = 4 is a half-row mirror followed by a
+// quad reversal, J = 8 a row mirror followed by a half-row mirror), the
+// gfx950 permlane swaps for J = 16 and 32.
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v, int lane) {
+  constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kQuadRev = 0x1B;
+  constexpr int kRowMirror = 0x140, kRowHalfMirror = 0x141;
+  if constexpr (J == 1) {
+    return __builtin_amdgcn_update_dpp(0u, v, kQuadXor1, 0xF, 0xF, false);
+  } else if constexpr (J == 2) {
+    return __builtin_amdgcn_update_dpp(0u, v, kQuadXor2, 0xF, 0xF, false);
+  } else if constexpr (J == 4) {
+    const uint32_t t = __builtin_amdgcn_update_dpp(0u, v, kRowHalfMirror, 0xF, 0xF, false);
+    return __builtin_amdgcn_update_dpp(0u, t, kQuadRev, 0xF, 0xF, false);
+  } else if constexpr (J == 8) {
+    const uint32_t t = __builtin_amdgcn_update_dpp(0u, v, kRowMirror, 0xF, 0xF, false);
+    return __builtin_amdgcn_update_dpp(0u, t, kRowHalfMirror, 0xF, 0xF, false);
+  } else if constexpr (J == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane & 16) ? r[0] : r[1];
+  } else {
+    static_assert(J == 32, "xor distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (lane & 32) ? r[0] : r[1];
+  }
 }
 
-// Sort 64 keys (one per lane) descending across the wave.
-__device__ __forceinline__ uint64_t sort64_desc(uint64_t key, int lane) {
-#pragma unroll
-  for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const uint64_t other = shfl_xor64(key, j);
-      const bool desc_block = (lane & k) == 0;
-      const bool lower = (lane & j) == 0;
-      const bool keep_max = lower == desc_block;
-      key = keep_max ? (key > other ? key : other) : (key < other ? key : other);
-    }
-  }
+template <int J>
+__device__ __forceinline__ uint64_t xor_lane64(uint64_t v, int lane) {
+  const uint32_t lo = xor_lane<J>(static_cast<uint32_t>(v), lane);
+  const uint32_t hi = xor_lane<J>(static_cast<uint32_t>(v >> 32), lane);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// One compare-exchange stage of a bitonic network: lanes keep the larger
+// key when keep_max, else the smaller.
+template <int J>
+__device__ __forceinline__ uint64_t cx_stage(uint64_t key, bool keep_max, int lane) {
+  const uint64_t other = xor_lane64<J>(key, lane);
+  const uint64_t hi = key > other ? key : other;
+  const uint64_t lo = key > other ? other : key;
+  return keep_max ? hi : lo;
+}
+
+template <int J>
+__device__ __forceinline__ uint32_t cx_stage32(uint32_t v, bool keep_max, int lane) {
+  const uint32_t other = xor_lane<J>(v, lane);
+  return keep_max ? (v > other ? v : other) : (v > other ? other : v);
+}
+
+__device__ __forceinline__ uint32_t half_cleaner_desc32(uint32_t v, int lane) {
+  v = cx_stage32<32>(v, (lane & 32) == 0, lane);
+  v = cx_stage32<16>(v, (lane & 16) == 0, lane);
+  v = cx_stage32<8>(v, (lane & 8) == 0, lane);
+  v = cx_stage32<4>(v, (lane & 4) == 0, lane);
+  v = cx_stage32<2>(v, (lane & 2) == 0, lane);
+  v = cx_stage32<1>(v, (lane & 1) == 0, lane);
+  return v;
+}
+
+template <int K, int J>
+__device__ __forceinline__ uint32_t sort_stages32(uint32_t v, int lane) {
+  const bool desc_block = K == 64 || (lane & K) == 0;
+  v = cx_stage32<J>(v, ((lane & J) == 0) == desc_block, lane);
+  if constexpr (J > 1) v = sort_stages32<K, J / 2>(v, lane);
+  return v;
+}
+
+// Sort 64 values (one per lane) descending.
+__device__ __forceinline__ uint32_t sort64_desc32(uint32_t v, int lane) {
+  v = sort_stages32<2, 1>(v, lane);
+  v = sort_stages32<4, 2>(v, lane);
+  v = sort_stages32<8, 4>(v, lane);
+  v = sort_stages32<16, 8>(v, lane);
+  v = sort_stages32<32, 16>(v, lane);
+  v = sort_stages32<64, 32>(v, lane);
+  return v;
+}
+
+// Sort a bitonic sequence of 64 keys (one per lane) descending.
+__device__ __forceinline__ uint64_t half_cleaner_desc(uint64_t key, int lane) {
+  key = cx_stage<32>(key, (lane & 32) == 0, lane);
+  key = cx_stage<16>(key, (lane & 16) == 0, lane);
+  key = cx_stage<8>(key, (lane & 8) == 0, lane);
+  key = cx_stage<4>(key, (lane & 4) == 0, lane);
+  key = cx_stage<2>(key, (lane & 2) == 0, lane);
+  key = cx_stage<1>(key, (lane & 1) == 0, lane);
   return key;
 }
 
-// Every lane takes the value of lane - 1; lane 0 takes UINT64_MAX (DPP
-// wave shift, two 32-bit moves).
-__device__ __forceinline__ uint64_t shift_down_one(uint64_t x) {
-  constexpr int kWaveShr1 = 0x138;
-  const uint32_t lo = __builtin_amdgcn_update_dpp(
-      0xFFFFFFFFu, static_cast<uint32_t>(x), kWaveShr1, 0xF, 0xF, false);
-  const uint32_t hi = __builtin_amdgcn_update_dpp(
-      0xFFFFFFFFu, static_cast<uint32_t>(x >> 32), kWaveShr1, 0xF, 0xF, false);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
+// Stages j = J, J/2, .., 1 of the merge of blocks of size K.
+template <int K, int J>
+__device__ __forceinline__ uint64_t sort_stages(uint64_t key, int lane) {
+  const bool desc_block = K == 64 || (lane & K) == 0;
+  key = cx_stage<J>(key, ((lane & J) == 0) == desc_block, lane);
+  if constexpr (J > 1) key = sort_stages<K, J / 2>(key, lane);
+  return key;
 }
 
-__device__ __forceinline__ uint64_t read_lane64(uint64_t x, int l) {
-  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(x), l);
-  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(x >> 32), l);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
+// Sort 64 keys (one per lane) descending: a bitonic network of 21 stages.
+__device__ __forceinline__ uint64_t sort64_desc(uint64_t key, int lane) {
+  key = sort_stages<2, 1>(key, lane);
+  key = sort_stages<4, 2>(key, lane);
+  key = sort_stages<8, 4>(key, lane);
+  key = sort_stages<16, 8>(key, lane);
+  key = sort_stages<32, 16>(key, lane);
+  key = sort_stages<64, 32>(key, lane);
+  return key;
 }
 
 // Sum over the wave (a fixed butterfly order, so repeatable).
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int j = 32; j > 0; j >>= 1) x += __shfl_xor(x, j, 64);
+  const int lane = threadIdx.x & 63;
+  x += __uint_as_float(xor_lane<32>(__float_as_uint(x), lane));
+  x += __uint_as_float(xor_lane<16>(__float_as_uint(x), lane));
+  x += __uint_as_float(xor_lane<8>(__float_as_uint(x), lane));
+  x += __uint_as_float(xor_lane<4>(__float_as_uint(x), lane));
+  x += __uint_as_float(xor_lane<2>(__float_as_uint(x), lane));
+  x += __uint_as_float(xor_lane<1>(__float_as_uint(x), lane));
   return x;
 }
 
@@ -111,95 +191,103 @@ __device__ __forceinline__ float lane_scan(float x) {
   return x;
 }
 
-// Insert one key (wave-uniform, not already present) into the descending
-// list of lanes 0..31: lanes past its place take their predecessor's key.
-__device__ __forceinline__ uint64_t insert_key(uint64_t list, uint64_t key) {
-  const uint64_t prev = shift_down_one(list);
-  const bool gt = key > list;
-  return gt ? (key < prev ? key : prev) : list;
-}
+constexpr int kWaves = 16;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kColsPerThread = kSliceCols / kThreads;  // 16
+// survivor pool of a workgroup: every key it holds (kernel 1: its slice;
+// the row kernel: the 32 candidates of each of up to 512 slices)
+constexpr int kPoolKeys = kColsPerThread * kThreads;
+static_assert(static_cast<int64_t>(Q4_SAMPLE_MAX_VOCAB) <=
+                  static_cast<int64_t>(kPoolKeys / kTopMax) * kSliceCols,
+              "the row kernel's pool holds every slice's candidates");
 
-// list: lanes 0..31 hold the best 32 so far, descending (lanes 32..63
-// unused).  Merge one chunk of 64 keys (one per lane, any order) into it:
-// keys that beat the list's 32nd entry are inserted one by one when few,
-// else the chunk is sorted with a bitonic network and merged (the list and
-// the chunk's best 32 reversed form a bitonic sequence of 64, whose
-// half-cleaner cascade leaves the best 32 in lanes 0..31).
-__device__ __forceinline__ uint64_t merge_chunk(uint64_t list, uint64_t chunk,
-                                                int lane) {
-  uint64_t floor32 = read_lane64(list, 31);
-  uint64_t mask = __ballot(chunk > floor32);
-  if (mask == 0) return list;
-  if (__builtin_popcountll(mask) <= 12) {
-    while (mask != 0) {
-      const int b = __builtin_ctzll(mask);
-      mask &= mask - 1;
-      const uint64_t key = read_lane64(chunk, b);
-      if (key > floor32) {
-        list = insert_key(list, key);
-        floor32 = read_lane64(list, 31);
-      }
-    }
-    return list;
-  }
-  const uint64_t c = sort64_desc(chunk, lane);
-  const uint64_t rev = __shfl(c, 63 - lane, 64);
-  uint64_t key = lane < 32 ? list : rev;
-#pragma unroll
-  for (int j = 32; j > 0; j >>= 1) {
-    const uint64_t other = shfl_xor64(key, j);
-    const bool lower = (lane & j) == 0;
-    key = lower ? (key > other ? key : other) : (key < other ? key : other);
-  }
-  return key;
-}
-
-// Best 32 of the keys get(i), i in [begin, end), for one wave: chunks of
-// 64, sixteen chunks' loads issued together before they are merged.
+// Lanes 0..31: a descending list; merge the descending list `other` (lanes
+// 0..31, read through get(i)) into it: the list and the other list reversed
+// form a bitonic sequence of 64, which one half-cleaner cascade sorts.
 template <typename Get>
-__device__ __forceinline__ uint64_t wave_topk(Get get, int64_t begin,
-                                              int64_t end, int lane) {
-  uint64_t list = 0;  // empty entries (key 0) sort after every real key
-  constexpr int kGroup = 16;
-  for (int64_t b = begin; b < end; b += kGroup * 64) {
-    uint64_t key[kGroup];
-#pragma unroll
-    for (int c = 0; c < kGroup; ++c) {
-      const int64_t i = b + 64 * c + lane;
-      key[c] = i < end ? get(i) : 0;
-    }
-#pragma unroll
-    for (int c = 0; c < kGroup; ++c) list = merge_chunk(list, key[c], lane);
-  }
-  return list;
+__device__ __forceinline__ uint64_t merge_list(uint64_t list, Get get, int lane) {
+  const uint64_t key = lane < kTopMax ? list : get(63 - lane);
+  return half_cleaner_desc(key, lane);
 }
 
-// Merge the lists of the W waves of a workgroup, pairwise through LDS;
-// wave 0 returns with the best 32.
-template <int W>
+// Merge the waves' lists (lanes 0..31) pairwise through LDS; wave 0
+// returns with the best 32.
 __device__ __forceinline__ uint64_t block_merge(uint64_t list,
                                                 uint64_t (*lists)[kTopMax],
                                                 int wave, int lane) {
 #pragma unroll
-  for (int stride = 1; stride < W; stride <<= 1) {
+  for (int stride = 1; stride < kWaves; stride <<= 1) {
     if (lane < kTopMax) lists[wave][lane] = list;
     __syncthreads();
     if ((wave & (2 * stride - 1)) == 0) {
-      const uint64_t other = lane < kTopMax ? lists[wave + stride][lane] : 0;
-      list = merge_chunk(list, other, lane);
+      const uint64_t *o = lists[wave + stride];
+      list = merge_list(list, [&](int i) { return o[i]; }, lane);
     }
     __syncthreads();
   }
   return list;
 }
 
-constexpr int kWaves = 16;
+// LDS of block_best32.
+struct SelectLds {
+  uint32_t vals[kWaves][kTopMax];  // the waves' best 32 thread maxima
+  uint64_t lists[kWaves][kTopMax];
+  uint32_t threshold, count;
+};
 
-// Kernel 1: workgroup (s, m) takes columns [V s / S, V (s+1) / S) of row m.
-__global__ __launch_bounds__(64 * kWaves) void topk_slices_kernel(
+// Best 32 of the keys a workgroup holds, descending in lanes 0..31 of wave
+// 0 (the other waves return 0).  for_each(f) calls f(key) for every key of
+// the calling thread (0 = none), in a fixed order, twice.  The 32nd largest
+// upper half T among the 1024 thread maxima bounds the 32nd best key from
+// below (32 distinct keys reach it), so only keys with an upper half >= T
+// can be in the answer -- usually a few more than 32.  T comes from one
+// 32-bit sort per wave and a merge of the waves' lists; the survivors are
+// packed into `pool` (room for every key) and sorted 64 at a time: by wave 0
+// alone when at most 64 survive, else by all waves, merged through LDS.
+template <typename ForEach>
+__device__ __forceinline__ uint64_t block_best32(ForEach for_each, uint64_t *pool,
+                                                 SelectLds &sh, int wave, int lane) {
+  uint64_t tmax = 0;
+  for_each([&](uint64_t k) { tmax = k > tmax ? k : tmax; });
+  uint32_t v = sort64_desc32(static_cast<uint32_t>(tmax >> 32), lane);
+  if (threadIdx.x == 0) sh.count = 0;
+#pragma unroll
+  for (int stride = 1; stride < kWaves; stride <<= 1) {
+    if (lane < kTopMax) sh.vals[wave][lane] = v;
+    __syncthreads();
+    if ((wave & (2 * stride - 1)) == 0)
+      v = half_cleaner_desc32(lane < kTopMax ? v : sh.vals[wave + stride][63 - lane], lane);
+    __syncthreads();
+  }
+  if (threadIdx.x == kTopMax - 1) sh.threshold = v;
+  __syncthreads();
+  const uint32_t T = sh.threshold;
+  for_each([&](uint64_t k) {
+    if (k != 0 && static_cast<uint32_t>(k >> 32) >= T) pool[atomicAdd(&sh.count, 1u)] = k;
+  });
+  __syncthreads();
+  const uint32_t n = sh.count;
+  if (n <= 64) {
+    if (wave != 0) return 0;
+    return sort64_desc(lane < static_cast<int>(n) ? pool[lane] : 0, lane);
+  }
+  uint64_t list = 0;
+  for (uint32_t b = 64 * wave; b < n; b += 64 * kWaves) {
+    const uint64_t k = sort64_desc(b + lane < n ? pool[b + lane] : 0, lane);
+    const uint64_t rev = __shfl(k, 63 - lane, 64);
+    list = half_cleaner_desc(lane < kTopMax ? list : rev, lane);
+  }
+  list = block_merge(list, sh.lists, wave, lane);
+  return wave == 0 ? list : 0;
+}
+
+// Kernel 1: workgroup (s, m) takes columns [V s / S, V (s+1) / S) of row m,
+// at most 16384: 16 per thread, in registers.
+__global__ __launch_bounds__(kThreads) void topk_slices_kernel(
     const float *__restrict__ logits, int64_t V, int S,
     uint64_t *__restrict__ cand) {
-  __shared__ uint64_t lists[kWaves][kTopMax];
+  __shared__ uint64_t pool[kColsPerThread * kThreads];
+  __shared__ SelectLds sh;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int s = blockIdx.x;
@@ -207,12 +295,17 @@ __global__ __launch_bounds__(64 * kWaves) void topk_slices_kernel(
   const int64_t c0 = V * s / S;
   const int64_t c1 = V * (s + 1) / S;
   const float *row = logits + static_cast<uint64_t>(m) * V;
-  auto get = [&](int64_t col) {
-    return make_key(row[col], static_cast<uint32_t>(col));
+  uint64_t key[kColsPerThread];
+#pragma unroll
+  for (int i = 0; i < kColsPerThread; ++i) {
+    const int64_t col = c0 + i * kThreads + threadIdx.x;
+    key[i] = col < c1 ? make_key(row[col], static_cast<uint32_t>(col)) : 0;
+  }
+  auto for_each = [&](auto f) {
+#pragma unroll
+    for (int i = 0; i < kColsPerThread; ++i) f(key[i]);
   };
-  uint64_t list = wave_topk(get, c0 + (c1 - c0) * wave / kWaves,
-                            c0 + (c1 - c0) * (wave + 1) / kWaves, lane);
-  list = block_merge<kWaves>(list, lists, wave, lane);
+  const uint64_t list = block_best32(for_each, pool, sh, wave, lane);
   if (wave == 0 && lane < kTopMax)
     cand[(static_cast<uint64_t>(m) * S + s) * kTopMax + lane] = list;
 }
@@ -223,7 +316,7 @@ struct SampleArgs {
 };
 
 // Kernel 2: workgroup m merges row m's S lists, then lane 0 samples.
-__global__ __launch_bounds__(64 * kWaves) void sample_rows_kernel(
+__global__ __launch_bounds__(kThreads) void sample_rows_kernel(
     const uint64_t *__restrict__ cand, int S, SampleArgs a,
     const int32_t *__restrict__ draft_tok, const int32_t *__restrict__ draft_idx,
     const float *__restrict__ draft_q, const float *__restrict__ u,
@@ -231,7 +324,8 @@ __global__ __launch_bounds__(64 * kWaves) void sample_rows_kernel(
     float *__restrict__ top_val, float *__restrict__ top_prob,
     int32_t *__restrict__ greedy, int32_t *__restrict__ accept,
     int32_t *__restrict__ token) {
-  __shared__ uint64_t lists[kWaves][kTopMax];
+  __shared__ uint64_t pool[kPoolKeys];
+  __shared__ SelectLds sh;
   __shared__ float val[kTopMax], qc[kTopMax];
   __shared__ int32_t tok[kTopMax];
   __shared__ int32_t sdi[kDraftMax];
@@ -240,11 +334,11 @@ __global__ __launch_bounds__(64 * kWaves) void sample_rows_kernel(
   const int wave = threadIdx.x >> 6;
   const int m = blockIdx.x;
   const uint64_t *rc = cand + static_cast<uint64_t>(m) * S * kTopMax;
-  const int64_t n = static_cast<int64_t>(S) * kTopMax;
-  auto get = [&](int64_t i) { return rc[i]; };
-  uint64_t list = wave_topk(get, n * wave / kWaves, n * (wave + 1) / kWaves,
-                            lane);
-  list = block_merge<kWaves>(list, lists, wave, lane);
+  const int64_t nk = static_cast<int64_t>(S) * kTopMax;
+  auto for_each = [&](auto f) {
+    for (int64_t i = threadIdx.x; i < nk; i += kThreads) f(rc[i]);
+  };
+  const uint64_t list = block_best32(for_each, pool, sh, wave, lane);
   if (wave != 0) return;
   const int k = a.top_k;
   // the row's draft list, one entry per lane, then q of every candidate
@@ -329,7 +423,7 @@ int slices_for(int64_t V) {
 
 extern "C" int q4_verify_sample_workspace(int M, int64_t V, uint64_t *bytes) {
   if (bytes == nullptr || M < 1 || M > Q4_SAMPLE_MAX_ROWS || V < 1 ||
-      V > 0x7FFFFFFFLL)
+      V > Q4_SAMPLE_MAX_VOCAB)
     return Q4_EINVAL;
   *bytes = static_cast<uint64_t>(M) * q4v::slices_for(V) * q4v::kTopMax * 8;
   return Q4_OK;

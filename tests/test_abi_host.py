@@ -175,6 +175,9 @@ def test_verify_sample_argument_errors(lib):
     assert w(1025, 100, ctypes.byref(n)) == -1
     assert w(1, 0, ctypes.byref(n)) == -1
     assert w(1, 1 << 31, ctypes.byref(n)) == -1
+    # the longest row: 512 slices of 16384 columns
+    assert w(1, 8388608, ctypes.byref(n)) == 0 and n.value == 512 * 32 * 8
+    assert w(1, 8388609, ctypes.byref(n)) == -1
     f = lib.q4_verify_sample
     P = [0x10000 + 0x1000 * i for i in range(12)]   # fake device pointers
     WS, NWS = 0x90000, 4096

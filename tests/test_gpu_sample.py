@@ -122,6 +122,13 @@ def test_ties_break_by_smaller_index(q4):
     flat = torch.zeros((2, 3000), device=dev)
     g, _ = run_and_check(q4, flat, 1.0, 1.0, 32, 4, 7, "all equal")
     assert np.array_equal(g["top_idx"][0], np.arange(32))
+    # full width: every slice has more tied keys than the survivor buffer
+    # holds and takes the exact fallback; the row's lists then all tie
+    flat = torch.full((2, 248320), -1.5, device=dev)
+    flat[1, 200000:200005] = 0.25
+    g, _ = run_and_check(q4, flat, 1.0, 1.0, 32, 4, 17, "all equal, full width")
+    assert np.array_equal(g["top_idx"][0], np.arange(32))
+    assert list(g["top_idx"][1][:6]) == [200000, 200001, 200002, 200003, 200004, 0]
 
 
 def test_greedy(q4):
