@@ -163,8 +163,13 @@ bool plan_kslice(int M, int64_t N, int64_t K, int cus, int parts, q4_plan *out) 
       parts > cus)
     return false;
   const int64_t per_part_cus = cus / parts;
-  const int64_t g = tiles < per_part_cus ? tiles : per_part_cus;
-  const int64_t per = (tiles + g - 1) / g;
+  const int64_t g0 = tiles < per_part_cus ? tiles : per_part_cus;
+  const int64_t per = (tiles + g0 - 1) / g0;
+  // With 3 or more tiles per workgroup, just enough workgroups for `per`
+  // tiles each, so that none finishes a tile after the others (gate+up:
+  // 242 x 9 tiles instead of 256 x 8 or 9, 20.9 against 21.9 us at M = 16
+  // on MI355X); with fewer, every CU's share matters more.
+  const int64_t g = per >= 3 ? (tiles + per - 1) / per : g0;
   if (per * records * kRecordBytes >= 0x7FFFFFF0LL) return false;
   const int waves = static_cast<int>((part_records + 1) / 2);
   q4_plan p;

@@ -196,7 +196,9 @@ def kslice_model(M, N, K, p):
     Qp = -(-Q // P)
     assert M <= 16 and Qp <= 24 and W == (Qp + 1) // 2 and p["m_tiles"] == 1
     G = p["grid"]
-    Gt = min(T, 256 // P)
+    g0 = min(T, 256 // P)
+    per = -(-T // g0)
+    Gt = -(-T // per) if per >= 3 else g0
     assert G == Gt * P
     NB = LDS_BYTES // (W * 1024)
     assert p["lds_bytes"] == NB * W * 1024 <= LDS_BYTES
