@@ -198,12 +198,28 @@ def raw_calls(torch, q4, entry, x, Ws, y, M, N, K, ws=None):
     return out
 
 
+# Least untimed warm-up per timed block.  Right after a repack, a block of
+# 200 gate+up calls that followed 200 warm-up calls (4.5 ms) measured 23.0 us
+# per call and every later block 20.6-21.0 us: the clocks take longer than
+# that to settle under a sustained load.
+MIN_WARM_S = 0.05
+
+
 def time_raw(torch, fns, steps, warmup):
     """ms per call of `steps` back-to-back calls (rotating over fns) between
-    two HIP events on the launch stream, after `warmup` untimed calls."""
+    two HIP events on the launch stream, after at least `warmup` untimed
+    calls and at least MIN_WARM_S seconds of them."""
     n = len(fns)
-    for i in range(warmup):
-        fns[i % n]()
+    done = 0
+    t_warm = time.perf_counter()
+    while True:
+        for _ in range(max(warmup, 1)):
+            fns[done % n]()
+            done += 1
+        torch.cuda.synchronize()
+        if done >= warmup and time.perf_counter() - t_warm >= MIN_WARM_S:
+            break
+    warmup = done
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
