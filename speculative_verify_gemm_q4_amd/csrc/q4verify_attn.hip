@@ -20,8 +20,9 @@
 //    v_mfma_f32_16x16x32_bf16 per page and wave (two token tiles, eight
 //    32-dim steps), the key scale and the softmax scale applied per token
 //    afterwards; the queries stay in registers for the whole run.
-//  * Online softmax per node in base 2; each node's 32 scores of a page sit
-//    in 4 lanes x 8 registers.  The ancestor mask applies to tree positions,
+//  * Online softmax per node in base 2, its reference maximum moved only
+//    when a score passes it by more than 2^8; each node's 32 scores of a
+//    page sit in 4 lanes x 8 registers.  The ancestor mask applies to tree positions,
 //    a 32-bit ancestor-or-self set per node.
 //  * Values on MFMA: O^T[dim][node] += V^T P'^T with P' = p * v_scale in
 //    bf16; the value tile's tokens are stored in the order in which the
@@ -53,6 +54,8 @@ constexpr int kVBytes = kD * kVStride;     // 20480
 constexpr int kBufBytes = kKBytes + kVBytes + 2 * kPage * 4;
 constexpr uint32_t kBufferWord3 = 0x00020000u;
 constexpr float kLog2e = 1.4426950408889634f;
+// Headroom of the running maximum in the online softmax (base 2).
+constexpr float kLazyMax = 8.0f;
 
 struct AttnArgs {
   const uint16_t *q;
@@ -349,21 +352,28 @@ __global__ __launch_bounds__(64 * G) void tree_attn_kernel(AttnArgs a) {
     }
     pm = fmaxf(pm, __shfl_xor(pm, 16, 64));
     pm = fmaxf(pm, __shfl_xor(pm, 32, 64));
-    const float mn = fmaxf(m, pm);
-    // with nothing visible yet (mn = -inf) every p is 0 and nothing rescales
-    const float alpha = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
-    float ps = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = p[i] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(p[i] - mn);
-      ps += p[i];
-    }
-    lsum = lsum * alpha + ps;
-    m = mn;
-    if (__ballot(alpha != 1.0f) != 0) {  // a wave-uniform test
+    // The reference maximum m moves only when some node's score passes it
+    // by more than kLazyMax (base 2), so the exponentials stay below
+    // 2^kLazyMax and the running output is rescaled on few pages.  The
+    // final division by the sum (and the merge of runs) removes any common
+    // reference, so the result is the same softmax.
+    if (__ballot(pm > m + kLazyMax) != 0) {  // a wave-uniform test
+      const float mn = fmaxf(m, pm);
+      // with nothing visible yet (mn = -inf) nothing rescales
+      const float alpha = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
+      lsum *= alpha;
+      m = mn;
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[i] *= alpha;
     }
+    float ps = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // a lane whose node has seen nothing visible (m = -inf) has p = -inf
+      p[i] = p[i] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(p[i] - m);
+      ps += p[i];
+    }
+    lsum += ps;
     // P'^T as the B operand: slot 8 gq + e <- token 4 gq + e (e < 4) and
     // 16 + 4 gq + e - 4 (e >= 4), exactly the order of p[]
     const u32x4 pb4 = {pack_bf16(p[0] * vsc[0], p[1] * vsc[1]),
