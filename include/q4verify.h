@@ -372,6 +372,34 @@ int q4_gdn_commit(float *S, int L, int H, int Hk, int dv, int dk, int M,
                   const float *beta, const int32_t *path,
                   const int32_t *n_accept, int32_t *status, void *stream);
 
+/*
+ * q4_gdn_tree_out -- every tree node's output of one recurrent layer from
+ * the shared state (qwen-spec page, the hybrid-model paragraph): node i
+ * reads the state after the context plus the updates, by the rule above, of
+ * the nodes on its own path root .. i, i included, and its output is
+ *     o_i = S_i q_i.
+ * Device pointers (caller owned, row-major, fp32 unless stated):
+ *   S [H][dv][dk] (16-byte aligned): the layer's state, read only;
+ *   q, k [M][Hk][dk] (16-byte aligned): every node's query and key;
+ *   v [M][H][dv], alpha, beta [M][H]: value, gate, strength;
+ *   parent [M] int32: node i's parent, -1 for a child of the context's last
+ *     token; parents precede children (parent[i] < i);
+ *   out [M][H][dv] (16-byte aligned): written;
+ *   status: NULL or one int32 that receives Q4_OK, or Q4_EINVAL when a
+ *     parent entry is out of range -- then out is not written.
+ * The tree is read on the device, so the call may follow the step that
+ * builds it on the stream.  Sizes: dk == Q4_GDN_DK, dv a multiple of 32, Hk
+ * divides H, 1 <= M <= Q4_GDN_MAX_NODES.  Arithmetic is fp32; the updates
+ * along a path are applied through their key and query products (the rows
+ * of S evolve independently), not by rewriting S.  One kernel on `stream`.
+ * Errors: Q4_EINVAL, Q4_EALIGN, Q4_EDEVICE, Q4_ELAUNCH.
+ */
+int q4_gdn_tree_out(const float *S, int H, int Hk, int dv, int dk, int M,
+                    const float *q, const float *k, const float *v,
+                    const float *alpha, const float *beta,
+                    const int32_t *parent, float *out, int32_t *status,
+                    void *stream);
+
 /* ------------------------------------------------------------------------
  * Tree-verify attention over the paged int8 KV cache.
  *

@@ -21,6 +21,8 @@ Functions (same names as the C entry points):
   target probabilities, the accept test and the residual draw.
 * :func:`q4_gdn_commit` -- writes a verify pass's accepted tree nodes into
   the Gated DeltaNet recurrent states of every layer (gated delta rule).
+* :func:`q4_gdn_tree_out` -- every tree node's output of one recurrent layer
+  from the shared state plus the updates along its path.
 * :func:`q4_tree_attn`, :func:`tree_attn` -- tree-verify attention of one
   layer over the paged int8 KV cache with the ancestor mask.
 * :func:`q4_dequant` -- fp32 weights of a packed matrix (test hook).
@@ -34,7 +36,7 @@ from ._lib import (ATTN_HEAD_DIM, ATTN_MAX_NODES, ATTN_PAGE, GDN_DK, GDN_MAX_NOD
                    LIB_PATH, lib_exports, load, q4_dequant, q4_gemm_verify,
                    q4_gemm_verify_plan, q4_gemm_verify_tiled,
                    q4_gemm_verify_tiled_ws, q4_gemm_verify_tiled_ws_plan,
-                   q4_gdn_commit, q4_pack_layout, q4_verify_sample,
+                   q4_gdn_commit, q4_gdn_tree_out, q4_pack_layout, q4_verify_sample,
                    q4_verify_sample_workspace, verify_sample,
                    workspace_for,
                    q4_repack, q4_status_string, q4_stream_copy,
@@ -48,7 +50,7 @@ __all__ = ["ATTN_HEAD_DIM", "ATTN_MAX_NODES", "ATTN_PAGE", "GDN_DK", "GDN_MAX_NO
            "LIB_PATH", "lib_exports", "load", "q4_dequant", "q4_gemm_verify",
            "q4_gemm_verify_plan", "q4_gemm_verify_tiled",
            "q4_gemm_verify_tiled_ws", "q4_gemm_verify_tiled_ws_plan",
-           "q4_gdn_commit", "q4_pack_layout", "q4_verify_sample",
+           "q4_gdn_commit", "q4_gdn_tree_out", "q4_pack_layout", "q4_verify_sample",
            "q4_verify_sample_workspace", "verify_sample", "workspace_for",
            "q4_repack", "q4_status_string", "q4_stream_copy",
            "q4_stream_read", "q4_tree_attn", "q4_tree_attn_plan", "tree_attn"]

@@ -100,6 +100,8 @@ _SIGNATURES = {
                                 ctypes.c_int),
     "q4_gdn_commit": ([ctypes.c_void_p] + [ctypes.c_int] * 6 +
                       [ctypes.c_void_p] * 8, ctypes.c_int),
+    "q4_gdn_tree_out": ([ctypes.c_void_p] + [ctypes.c_int] * 5 +
+                        [ctypes.c_void_p] * 9, ctypes.c_int),
     "q4_tree_attn_plan": ([ctypes.c_int] * 4 + [ctypes.c_int64, ctypes.c_int,
                            ctypes.POINTER(ctypes.c_int),
                            ctypes.POINTER(ctypes.c_uint64)], ctypes.c_int),
@@ -367,6 +369,40 @@ def q4_gdn_commit(S, k, v, alpha, beta, path, n_accept, status=None,
                               _stream_handle(stream))
     if st != OK:
         raise Q4Error(st, "q4_gdn_commit")
+
+
+def q4_gdn_tree_out(S, q, k, v, alpha, beta, parent, out=None, status=None,
+                    stream=None):
+    """Every tree node's output of one recurrent layer from the shared state
+    (see include/q4verify.h): S [H, dv, dk] fp32 (read only); q, k
+    [M, Hk, dk], v [M, H, dv], alpha / beta [M, H] fp32; parent [M] int32 on
+    the device (-1: child of the context; parents precede children); out
+    None or [M, H, dv] fp32; status None or [1] int32 (receives 0, or -1 for
+    an out-of-range parent, in which case out is not written).  Returns
+    out."""
+    import torch
+    if S.dim() != 3 or k.dim() != 3:
+        raise ValueError("S must be [H, dv, dk] and k [M, Hk, dk]")
+    H, dv, dk = S.shape
+    M, Hk = int(k.shape[0]), int(k.shape[1])
+    if out is None:
+        out = torch.empty((M, H, dv), dtype=torch.float32, device=S.device)
+    pS = _ptr(S, "S", torch.float32)
+    pq = _ptr(q, "q", torch.float32, shape=(M, Hk, dk))
+    pk = _ptr(k, "k", torch.float32, shape=(M, Hk, dk))
+    pv = _ptr(v, "v", torch.float32, shape=(M, H, dv))
+    pa = _ptr(alpha, "alpha", torch.float32, shape=(M, H))
+    pb = _ptr(beta, "beta", torch.float32, shape=(M, H))
+    pp = _ptr(parent, "parent", torch.int32, numel=M)
+    po = _ptr(out, "out", torch.float32, shape=(M, H, dv))
+    ps = None if status is None else _ptr(status, "status", torch.int32,
+                                          numel=1)
+    st = load().q4_gdn_tree_out(pS, int(H), Hk, int(dv), int(dk), M, pq, pk,
+                                pv, pa, pb, pp, po, ps,
+                                _stream_handle(stream))
+    if st != OK:
+        raise Q4Error(st, "q4_gdn_tree_out")
+    return out
 
 
 ATTN_HEAD_DIM = 256

@@ -211,8 +211,239 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_commit_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Tree-node outputs of one recurrent layer (qwen-spec page, the hybrid-model
+// paragraph: every tree node reads the shared state after the context plus
+// the updates along its own path).  Node i's output is o_i = S_i q_i, S_i
+// being the state after the updates of the nodes root .. i.
+//
+// Rows stay independent, and along a path the row s evolves as
+//     s_i = alpha_i s_p + c_i k_i,  c_i = beta_i (v_i[r] - alpha_i s_p . k_i)
+// (p the parent), so s_i = A_i s_0 + sum_{m in path(i)} W_im c_m k_m with
+// W_im the product of the gates of the nodes below m on the path and A_i the
+// product over the whole path.  Hence, with the row's dot products
+// s_0 . k_m and s_0 . q_i and the layer's key-key and key-query products,
+//     s_p . k_i = A_p (s_0 . k_i) + sum_{m in path(p)} W_pm (k_m . k_i) c_m,
+//     o_i[r]    = A_i (s_0 . q_i) + sum_{m in path(i)} W_im (k_m . q_i) c_m:
+// a short triangular recurrence per row on the coefficients c, in node
+// order (parents precede children).  The state is read once and not written.
+//  * a workgroup owns 32 rows of one head; lane (rho, j) of wave w holds
+//    columns 4 (j + 8 i) .. +3, i = 0..3, of row 8 w + rho, and a row's dot
+//    product is 16 FMAs per lane and a 3-step DPP sum over its 8 lanes;
+//  * the tree's keys and queries (for the head's key head), its values for
+//    the workgroup's rows and the gates sit in LDS; the products k_m . k_i,
+//    k_m . q_i and the path weights are formed there, the weights by one
+//    thread per node walking its path;
+//  * in the recurrence lane j keeps c_m, s_0 . k_m and s_0 . q_m for the
+//    nodes m = j mod 8, so each step is a few FMAs and one 8-lane sum.
+constexpr int kTreeRows = 32;
+constexpr int kTreeThreads = 256;
+constexpr int kTreeMax = Q4_GDN_MAX_NODES;
+static_assert(kTreeMax == 32, "c, s0.k and s0.q: 4 registers per lane");
+
+struct GdnTreeArgs {
+  const float *S, *q, *k, *v, *alpha, *beta;
+  const int32_t *parent;
+  float *out;
+  int32_t *status;
+  int H, Hk, dv, M, row_blocks;
+};
+
+__global__ __launch_bounds__(kTreeThreads) void gdn_tree_out_kernel(
+    GdnTreeArgs a) {
+  __shared__ float4 kq[2 * kTreeMax * 32];  // keys, then queries [node][32]
+  __shared__ float vsm[kTreeMax * kTreeRows];   // values [node][row]
+  __shared__ float kk[kTreeMax * kTreeMax];     // k_m . k_i at [m][i]
+  __shared__ float kqd[kTreeMax * kTreeMax];    // k_m . q_i at [i][m]
+  __shared__ float ek[kTreeMax * kTreeMax];     // W_pm (k_m . k_i) at [i][m]
+  __shared__ float eq[kTreeMax * kTreeMax];     // W_im (k_m . q_i) at [i][m]
+  __shared__ float obuf[kTreeMax * kTreeRows];  // outputs [node][row]
+  __shared__ float al[kTreeMax], be[kTreeMax], ak[kTreeMax], aq[kTreeMax];
+  __shared__ int par[kTreeMax];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int rho = lane >> 3;
+  const int j = lane & 7;
+  const int M = a.M;
+  const int rb = blockIdx.x % a.row_blocks;
+  const int h = blockIdx.x / a.row_blocks;
+  const int hk = h / (a.H / a.Hk);
+  const int row = 8 * w + rho;  // within the block
+
+  // this lane's part of its state row, issued first
+  const float4 *srow = reinterpret_cast<const float4 *>(
+      a.S + (static_cast<size_t>(h) * a.dv + static_cast<size_t>(rb) * kTreeRows + row) *
+                kGdnDk);
+  float4 st[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) st[i] = srow[j + 8 * i];
+
+  // every wave checks the whole tree: -1 <= parent[i] < i
+  int pi = -1;
+  bool bad_lane = false;
+  if (lane < M) {
+    pi = a.parent[lane];
+    bad_lane = pi < -1 || pi >= lane;
+  }
+  const bool bad = __ballot(bad_lane) != 0;
+  if (blockIdx.x == 0 && tid == 0 && a.status != nullptr)
+    a.status[0] = bad ? Q4_EINVAL : Q4_OK;
+  if (bad) return;  // the same decision in every wave of every workgroup
+
+  if (w == 0 && lane < M) par[lane] = pi;
+  for (int e = tid; e < 2 * M * 32; e += kTreeThreads) {
+    const int node = (e >> 5) % M;
+    const float *src = e < M * 32 ? a.k : a.q;
+    kq[e] = reinterpret_cast<const float4 *>(
+        src + (static_cast<size_t>(node) * a.Hk + hk) * kGdnDk)[e & 31];
+  }
+  for (int e = tid; e < M * kTreeRows; e += kTreeThreads) {
+    const int node = e / kTreeRows;
+    vsm[e] = a.v[(static_cast<size_t>(node) * a.H + h) * a.dv +
+                 static_cast<size_t>(rb) * kTreeRows + e % kTreeRows];
+  }
+  if (tid < M) {
+    al[tid] = a.alpha[static_cast<size_t>(tid) * a.H + h];
+    be[tid] = a.beta[static_cast<size_t>(tid) * a.H + h];
+  }
+  __syncthreads();
+
+  // k_m . k_i and k_m . q_i for every pair
+  for (int e = tid; e < M * M; e += kTreeThreads) {
+    const int i = e / M, m = e % M;
+    const float4 *km = kq + m * 32;
+    const float4 *ki = kq + i * 32;
+    const float4 *qi = kq + (M + i) * 32;
+    float dk = 0.0f, dq = 0.0f;
+    for (int c = 0; c < 32; ++c) {
+      const float4 x = km[c], y = ki[c], z = qi[c];
+      dk = fmaf(x.x, y.x, dk);
+      dk = fmaf(x.y, y.y, dk);
+      dk = fmaf(x.z, y.z, dk);
+      dk = fmaf(x.w, y.w, dk);
+      dq = fmaf(x.x, z.x, dq);
+      dq = fmaf(x.y, z.y, dq);
+      dq = fmaf(x.z, z.z, dq);
+      dq = fmaf(x.w, z.w, dq);
+    }
+    kk[m * kTreeMax + i] = dk;
+    kqd[i * kTreeMax + m] = dq;
+  }
+  __syncthreads();
+
+  // path weights, one thread per node: row i of ek (the parent's path) and
+  // of eq (the node's own path), zero off the path
+  if (tid < M) {
+    const int i = tid;
+    for (int m = 0; m < kTreeMax; ++m) {
+      ek[i * kTreeMax + m] = 0.0f;
+      eq[i * kTreeMax + m] = 0.0f;
+    }
+    float wgt = 1.0f;
+    for (int m = par[i]; m >= 0; m = par[m]) {
+      ek[i * kTreeMax + m] = wgt * kk[m * kTreeMax + i];
+      wgt *= al[m];
+    }
+    ak[i] = wgt;  // A_p (1 for a child of the context)
+    wgt = 1.0f;
+    for (int m = i; m >= 0; m = par[m]) {
+      eq[i * kTreeMax + m] = wgt * kqd[i * kTreeMax + m];
+      wgt *= al[m];
+    }
+    aq[i] = wgt;  // A_i
+  }
+
+  // the row's s_0 . k_m and s_0 . q_m; lane j keeps those of m = j mod 8
+  float s0k[4] = {0.0f, 0.0f, 0.0f, 0.0f}, s0q[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int m = 0; m < kTreeMax; ++m) {
+    if (m < M) {  // uniform
+      float pk = 0.0f, pq = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 x = kq[m * 32 + j + 8 * i];
+        const float4 z = kq[(M + m) * 32 + j + 8 * i];
+        pk = fmaf(st[i].x, x.x, pk);
+        pk = fmaf(st[i].y, x.y, pk);
+        pk = fmaf(st[i].z, x.z, pk);
+        pk = fmaf(st[i].w, x.w, pk);
+        pq = fmaf(st[i].x, z.x, pq);
+        pq = fmaf(st[i].y, z.y, pq);
+        pq = fmaf(st[i].z, z.z, pq);
+        pq = fmaf(st[i].w, z.w, pq);
+      }
+      pk = dpp_sum8(pk);
+      pq = dpp_sum8(pq);
+      if (j == m % 8) {
+        s0k[m / 8] = pk;
+        s0q[m / 8] = pq;
+      }
+    }
+  }
+  __syncthreads();  // ek, eq, ak, aq
+
+  // the recurrence in node order
+  float cl[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < kTreeMax; ++i) {
+    if (i < M) {  // uniform
+      float part = j == i % 8 ? ak[i] * s0k[i / 8] : 0.0f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) part = fmaf(ek[i * kTreeMax + 8 * t + j], cl[t], part);
+      const float d = dpp_sum8(part);  // s_p . k_i
+      const float c = be[i] * (vsm[i * kTreeRows + row] - al[i] * d);
+      if (j == i % 8) cl[i / 8] = c;
+      part = j == i % 8 ? aq[i] * s0q[i / 8] : 0.0f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) part = fmaf(eq[i * kTreeMax + 8 * t + j], cl[t], part);
+      const float o = dpp_sum8(part);
+      if (j == 0) obuf[i * kTreeRows + row] = o;
+    }
+  }
+  __syncthreads();
+  // out [M][H][dv]: 8 float4 of the block's rows per node
+  for (int e = tid; e < M * 8; e += kTreeThreads) {
+    const int node = e >> 3, c = e & 7;
+    reinterpret_cast<float4 *>(a.out + (static_cast<size_t>(node) * a.H + h) * a.dv +
+                               static_cast<size_t>(rb) * kTreeRows)[c] =
+        reinterpret_cast<const float4 *>(obuf + node * kTreeRows)[c];
+  }
+}
+
 }  // namespace
 }  // namespace q4v
+
+extern "C" int q4_gdn_tree_out(const float *S, int H, int Hk, int dv, int dk,
+                               int M, const float *q, const float *k,
+                               const float *v, const float *alpha,
+                               const float *beta, const int32_t *parent,
+                               float *out, int32_t *status, void *stream) {
+  if (S == nullptr || q == nullptr || k == nullptr || v == nullptr ||
+      alpha == nullptr || beta == nullptr || parent == nullptr ||
+      out == nullptr || H < 1 || Hk < 1 || H % Hk != 0 || dk != Q4_GDN_DK ||
+      dv < 1 || dv % q4v::kTreeRows != 0 || M < 1 || M > Q4_GDN_MAX_NODES)
+    return Q4_EINVAL;
+  const int64_t blocks = static_cast<int64_t>(H) * (dv / q4v::kTreeRows);
+  if (blocks > 0x7FFFFFFF) return Q4_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(S) & 15u) != 0 ||
+      (reinterpret_cast<uintptr_t>(q) & 15u) != 0 ||
+      (reinterpret_cast<uintptr_t>(k) & 15u) != 0 ||
+      (reinterpret_cast<uintptr_t>(v) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(out) & 15u) != 0 ||
+      (reinterpret_cast<uintptr_t>(alpha) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(beta) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(parent) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(status) & 3u) != 0)
+    return Q4_EALIGN;
+  const int st = q4v::check_device();
+  if (st != Q4_OK) return st;
+  const q4v::GdnTreeArgs a{S, q, k, v, alpha, beta, parent, out, status,
+                           H, Hk, dv, M, dv / q4v::kTreeRows};
+  hipLaunchKernelGGL(q4v::gdn_tree_out_kernel, dim3(static_cast<uint32_t>(blocks)),
+                     dim3(q4v::kTreeThreads), 0, static_cast<hipStream_t>(stream), a);
+  return hipGetLastError() == hipSuccess ? Q4_OK : Q4_ELAUNCH;
+}
 
 extern "C" int q4_gdn_commit_lds_bytes(int M, int *bytes) {
   if (bytes == nullptr || M < 1 || M > Q4_GDN_MAX_NODES) return Q4_EINVAL;

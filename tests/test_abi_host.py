@@ -231,6 +231,30 @@ def test_gdn_commit_argument_errors(lib):
     assert call(status=0x90002) == -2
 
 
+def test_gdn_tree_out_argument_errors(lib):
+    """Sizes, NULL pointers and alignment are rejected before device work."""
+    f = lib.q4_gdn_tree_out
+    # S, q, k, v, alpha, beta, parent, out (fake device pointers)
+    P = [0x10000 + 0x1000 * i for i in range(8)]
+
+    def call(H=48, Hk=16, dv=128, dk=128, M=16, ptrs=P, status=None):
+        return f(ptrs[0], H, Hk, dv, dk, M, *ptrs[1:], status, None)
+    assert call(M=0) == -1 and call(M=33) == -1
+    assert call(dk=64) == -1 and call(dv=16) == -1 and call(dv=48) == -1
+    assert call(Hk=5) == -1 and call(Hk=0) == -1 and call(H=0) == -1
+    for i in range(8):
+        bad = list(P)
+        bad[i] = 0
+        assert call(ptrs=bad) == -1, i
+    # S, q, k and out 16-byte aligned; v, alpha, beta, parent 4-byte
+    for i, off in ((0, 8), (1, 4), (2, 8), (3, 2), (4, 1), (5, 2), (6, 1),
+                   (7, 8)):
+        bad = list(P)
+        bad[i] += off
+        assert call(ptrs=bad) == -2, i
+    assert call(status=0x90002) == -2
+
+
 def test_dequant_and_probe_argument_errors(lib):
     d = lib.q4_dequant
     assert d(0x10000, 0x20000, 0, 64, None) == -1

@@ -170,3 +170,133 @@ def test_without_status_pointer(q4):
     S, st = _commit(q4, inp, [1, 3], status=False)
     assert st is None
     _check_heads(S, inp, [1, 3], [(0, 0), (0, 1)])
+
+
+# ---------------------------------------------------------------- tree outputs
+# Node i's output is S_i q_i, S_i the state after the updates on i's path.
+# The kernel forms it from the rows' products with the tree's keys and
+# queries and a per-row recurrence on the update coefficients; each of those
+# terms carries the rounding of a 128-term dot product (gamma_19 for the FMA
+# chains and the 8-lane tree) per node on the path, against a state row of
+# norm at most R, the largest row norm of S_0 and of every S_i.  With unit
+# queries an output may be off by (depth + 1) * 64 * eps32 * R; a wrong
+# index, sign, gate or parent gives errors of the order of R / sqrt(128).
+
+def _tree_out(q4, inp, parent=None, status=True):
+    dev = inp["S"].device
+    par = torch.tensor(inp["parent"] if parent is None else parent,
+                       dtype=torch.int32, device=dev)
+    st = torch.full((1,), 12345, dtype=torch.int32, device=dev) \
+        if status else None
+    shape = (inp["k"].shape[1], inp["S"].shape[1], inp["S"].shape[2])
+    out = torch.full(shape, float("nan"), dtype=torch.float32, device=dev)
+    q4.q4_gdn_tree_out(inp["S"][0], inp["q"][0], inp["k"][0], inp["v"][0],
+                       inp["alpha"][0], inp["beta"][0], par, out, st)
+    torch.cuda.synchronize()
+    return out, (None if st is None else int(st.item()))
+
+
+def _check_tree(got, inp, heads=None):
+    """Compare node outputs of the given value heads (all by default; a
+    subset must be whole key heads' groups) with the oracle."""
+    S0 = inp["S"][0].cpu().numpy()
+    q = inp["q"][0].cpu().numpy()
+    k = inp["k"][0].cpu().numpy()
+    v = inp["v"][0].cpu().numpy()
+    a = inp["alpha"][0].cpu().numpy()
+    b = inp["beta"][0].cpu().numpy()
+    parent = np.asarray(inp["parent"], dtype=np.int32)
+    H, Hk = S0.shape[0], k.shape[1]
+    G = H // Hk
+    hs = list(range(H)) if heads is None else list(heads)
+    kh = sorted({h // G for h in hs})
+    assert hs == [h for g in kh for h in range(g * G, (g + 1) * G)]
+    want = go.tree_out(S0[hs], q[:, kh], k[:, kh], v[:, hs], a[:, hs],
+                       b[:, hs], parent)
+    g = got.cpu().numpy()[:, hs].astype(np.float64)
+    assert np.isfinite(g).all()
+    M = len(parent)
+    worst = 0.0
+    for i in range(M):
+        path = synth.tree_path(parent, i)
+        Si = go.commit(S0[hs][None], k[None][:, :, kh], v[None][:, :, hs],
+                       a[None][:, :, hs], b[None][:, :, hs], path)[0]
+        R = max(np.linalg.norm(S0[hs], axis=-1).max(),
+                np.linalg.norm(Si, axis=-1).max())
+        tol = (len(path) + 1) * 64 * EPS32 * R
+        err = np.abs(g[i] - want[i]).max()
+        assert err <= tol, (i, len(path), err, tol)
+        worst = max(worst, err / tol)
+    _say(f"   tree outputs: worst error / bound = {worst:.3e}")
+
+
+@pytest.mark.parametrize("H,Hk,M,dv", [(2, 1, 1, 32), (4, 2, 5, 64),
+                                       (6, 2, 16, 128), (3, 3, 32, 32),
+                                       (4, 1, 9, 96)])
+def test_tree_out_matches_oracle(q4, H, Hk, M, dv):
+    dev = torch.device("cuda")
+    _say(f"case gdn tree out H={H} Hk={Hk} M={M} dv={dv}")
+    inp = synth.gdn_inputs(1, H, Hk, M, dv=dv, seed=20 + M, device=dev)
+    out, st = _tree_out(q4, inp)
+    assert st == 0
+    _check_tree(out, inp)
+
+
+def test_tree_out_full_shape_sampled(q4):
+    """The 27B layer: 48 value heads over 16 key heads of 128 x 128, a
+    16-node tree; one key head's three value heads against the oracle."""
+    dev = torch.device("cuda")
+    _say("case gdn tree out full 48/16 x 128 x 128, M=16")
+    inp = synth.gdn_inputs(1, 48, 16, 16, seed=30, device=dev)
+    out, st = _tree_out(q4, inp)
+    assert st == 0
+    assert torch.isfinite(out).all()
+    _check_tree(out, inp, heads=[21, 22, 23])
+
+
+def test_tree_out_chain_and_star(q4):
+    """A chain (every node the child of the previous) and a star (every
+    node a child of the context): the deepest and the shallowest trees."""
+    dev = torch.device("cuda")
+    for name, par in (("chain", list(range(-1, 15))), ("star", [-1] * 16)):
+        _say(f"case gdn tree out {name}")
+        inp = synth.gdn_inputs(1, 4, 2, 16, seed=31, device=dev)
+        inp["parent"] = np.asarray(par, dtype=np.int32)
+        out, st = _tree_out(q4, inp)
+        assert st == 0
+        _check_tree(out, inp)
+
+
+def test_tree_out_gates_near_zero(q4):
+    """Tiny and zero gates: the path weights underflow towards 0, and a
+    zero gate forgets everything above it on the path."""
+    dev = torch.device("cuda")
+    inp = synth.gdn_inputs(1, 4, 2, 12, seed=32, device=dev)
+    inp["parent"] = np.asarray(list(range(-1, 11)), dtype=np.int32)
+    a = inp["alpha"]
+    a[0, 1:6, :2] = 1e-4
+    a[0, 7, 2] = 0.0
+    out, st = _tree_out(q4, inp)
+    assert st == 0
+    _check_tree(out, inp)
+
+
+@pytest.mark.parametrize("parent", [[-1, 0, 2], [-1, -2, 0], [0, 0, 1],
+                                    [-1, 0, 7]])
+def test_tree_out_bad_parent_is_reported(q4, parent):
+    """A parent that is not an earlier node (or -1): status -1, nothing
+    written."""
+    dev = torch.device("cuda")
+    inp = synth.gdn_inputs(1, 2, 1, 3, dv=32, seed=33, device=dev)
+    out, st = _tree_out(q4, inp, parent=parent)
+    assert st == -1
+    assert torch.isnan(out).all()
+
+
+def test_tree_out_deterministic_and_without_status(q4):
+    dev = torch.device("cuda")
+    inp = synth.gdn_inputs(1, 6, 2, 16, seed=34, device=dev)
+    a, _ = _tree_out(q4, inp)
+    b, st = _tree_out(q4, inp, status=False)
+    assert st is None
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
