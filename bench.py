@@ -387,8 +387,33 @@ def measure_gdn_commit(torch, synth, q4, dev, steps, warmup):
         out["paths"].append({"accepted": n, "us": round(ms * 1e3, 3),
                              "alg_bytes": nb, "gbps": round(gbps, 1),
                              "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)})
+    # every tree node's output of one layer, from that layer's state (one
+    # of the 3 x 48 layer states in turn, so that each call reads from HBM)
+    par = torch.tensor(inp["parent"], dtype=torch.int32, device=dev)
+    outs = torch.empty((M, H, dv), dtype=torch.float32, device=dev)
+    lstates = [S[l] for S in states for l in range(L)]
+    fns = [functools.partial(
+        lib.q4_gdn_tree_out, Sl.data_ptr(), H, Hk, dv, dk, M,
+        inp["q"][0].data_ptr(), inp["k"][0].data_ptr(), inp["v"][0].data_ptr(),
+        inp["alpha"][0].data_ptr(), inp["beta"][0].data_ptr(), par.data_ptr(),
+        outs.data_ptr(), status.data_ptr(), stream) for Sl in lstates]
+    if any(f() != 0 for f in fns[:1]):
+        raise RuntimeError("q4_gdn_tree_out failed")
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise RuntimeError("q4_gdn_tree_out rejected its tree")
+    ms, _ = time_raw(torch, fns, steps, warmup)
+    # the layer's state, the nodes' queries, keys, values, gates and parents,
+    # and the outputs
+    nb = (H * dv * dk * 4 + 2 * M * Hk * dk * 4 + M * H * dv * 4
+          + 2 * M * H * 4 + M * 4 + M * H * dv * 4)
+    gbps = nb / (ms * 1e-3) / 1e9
+    out["tree_out"] = {"layer_states": len(lstates), "tree_nodes": M,
+                       "us": round(ms * 1e3, 3), "alg_bytes": nb,
+                       "gbps": round(gbps, 1),
+                       "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
     log(f"gdn commit: {out}")
-    del states, inp
+    del states, inp, lstates, fns
     torch.cuda.empty_cache()
     return out
 
