@@ -231,9 +231,9 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_commit_kernel(
 //    columns 4 (j + 8 i) .. +3, i = 0..3, of row 8 w + rho, and a row's dot
 //    product is 16 FMAs per lane and a 3-step DPP sum over its 8 lanes;
 //  * the tree's keys and queries (for the head's key head), its values for
-//    the workgroup's rows and the gates sit in LDS; the products k_m . k_i,
-//    k_m . q_i and the path weights are formed there, the weights by one
-//    thread per node walking its path;
+//    the workgroup's rows and the gates sit in LDS; while one wave forms the
+//    path weights (a lane per node walking its path once), the other three
+//    form the products k_m . k_i and k_m . q_i, 8 lanes a pair;
 //  * in the recurrence lane j keeps c_m, s_0 . k_m and s_0 . q_m for the
 //    nodes m = j mod 8, so each step is a few FMAs and one 8-lane sum.
 constexpr int kTreeRows = 32;
@@ -249,14 +249,18 @@ struct GdnTreeArgs {
   int H, Hk, dv, M, row_blocks;
 };
 
+// NMAX (16 or 32) bounds the node loops: they run without per-node branches
+// (the arrays are zero past M), so that the compiler can issue a later
+// node's LDS reads early.
+template <int NMAX>
 __global__ __launch_bounds__(kTreeThreads) void gdn_tree_out_kernel(
     GdnTreeArgs a) {
   __shared__ float4 kq[2 * kTreeMax * 32];  // keys, then queries [node][32]
   __shared__ float vsm[kTreeMax * kTreeRows];   // values [node][row]
   __shared__ float kk[kTreeMax * kTreeMax];     // k_m . k_i at [m][i]
   __shared__ float kqd[kTreeMax * kTreeMax];    // k_m . q_i at [i][m]
-  __shared__ float ek[kTreeMax * kTreeMax];     // W_pm (k_m . k_i) at [i][m]
-  __shared__ float eq[kTreeMax * kTreeMax];     // W_im (k_m . q_i) at [i][m]
+  __shared__ float wk[kTreeMax * kTreeMax];     // W_pm at [i][m] (p = parent of i)
+  __shared__ float wq[kTreeMax * kTreeMax];     // W_im at [i][m]
   __shared__ float obuf[kTreeMax * kTreeRows];  // outputs [node][row]
   __shared__ float al[kTreeMax], be[kTreeMax], ak[kTreeMax], aq[kTreeMax];
   __shared__ int par[kTreeMax];
@@ -279,6 +283,37 @@ __global__ __launch_bounds__(kTreeThreads) void gdn_tree_out_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) st[i] = srow[j + 8 * i];
 
+  // every load of the tree's inputs issued at once, before the tree check,
+  // so that the workgroup waits for one round trip
+  float4 kqr[2 * kTreeMax * 32 / kTreeThreads];
+  float vr[kTreeMax * kTreeRows / kTreeThreads];
+#pragma unroll
+  for (int r = 0; r < 2 * kTreeMax * 32 / kTreeThreads; ++r)
+    kqr[r] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+  for (int r = 0; r < kTreeMax * kTreeRows / kTreeThreads; ++r) vr[r] = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 2 * kTreeMax * 32 / kTreeThreads; ++r) {
+    const int e = tid + kTreeThreads * r;
+    if (e < 2 * M * 32) {
+      const int node = (e >> 5) % M;
+      const float *src = e < M * 32 ? a.k : a.q;
+      kqr[r] = reinterpret_cast<const float4 *>(
+          src + (static_cast<size_t>(node) * a.Hk + hk) * kGdnDk)[e & 31];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kTreeMax * kTreeRows / kTreeThreads; ++r) {
+    const int e = tid + kTreeThreads * r;
+    if (e < M * kTreeRows)
+      vr[r] = a.v[(static_cast<size_t>(e / kTreeRows) * a.H + h) * a.dv +
+                  static_cast<size_t>(rb) * kTreeRows + e % kTreeRows];
+  }
+  float ga = 0.0f, gb = 0.0f;
+  if (tid < M) {
+    ga = a.alpha[static_cast<size_t>(tid) * a.H + h];
+    gb = a.beta[static_cast<size_t>(tid) * a.H + h];
+  }
   // every wave checks the whole tree: -1 <= parent[i] < i
   int pi = -1;
   bool bad_lane = false;
@@ -292,73 +327,85 @@ __global__ __launch_bounds__(kTreeThreads) void gdn_tree_out_kernel(
   if (bad) return;  // the same decision in every wave of every workgroup
 
   if (w == 0 && lane < M) par[lane] = pi;
-  for (int e = tid; e < 2 * M * 32; e += kTreeThreads) {
-    const int node = (e >> 5) % M;
-    const float *src = e < M * 32 ? a.k : a.q;
-    kq[e] = reinterpret_cast<const float4 *>(
-        src + (static_cast<size_t>(node) * a.Hk + hk) * kGdnDk)[e & 31];
+#pragma unroll
+  for (int r = 0; r < 2 * kTreeMax * 32 / kTreeThreads; ++r) {
+    const int e = tid + kTreeThreads * r;
+    if (e < 2 * NMAX * 32) kq[e] = kqr[r];  // zeros past the queries
   }
-  for (int e = tid; e < M * kTreeRows; e += kTreeThreads) {
-    const int node = e / kTreeRows;
-    vsm[e] = a.v[(static_cast<size_t>(node) * a.H + h) * a.dv +
-                 static_cast<size_t>(rb) * kTreeRows + e % kTreeRows];
+#pragma unroll
+  for (int r = 0; r < kTreeMax * kTreeRows / kTreeThreads; ++r) {
+    const int e = tid + kTreeThreads * r;
+    if (e < NMAX * kTreeRows) vsm[e] = vr[r];
   }
-  if (tid < M) {
-    al[tid] = a.alpha[static_cast<size_t>(tid) * a.H + h];
-    be[tid] = a.beta[static_cast<size_t>(tid) * a.H + h];
+  if (tid < NMAX) {
+    al[tid] = ga;  // 0 past M
+    be[tid] = gb;
   }
-  __syncthreads();
-
-  // k_m . k_i and k_m . q_i for every pair
-  for (int e = tid; e < M * M; e += kTreeThreads) {
-    const int i = e / M, m = e % M;
-    const float4 *km = kq + m * 32;
-    const float4 *ki = kq + i * 32;
-    const float4 *qi = kq + (M + i) * 32;
-    float dk = 0.0f, dq = 0.0f;
-    for (int c = 0; c < 32; ++c) {
-      const float4 x = km[c], y = ki[c], z = qi[c];
-      dk = fmaf(x.x, y.x, dk);
-      dk = fmaf(x.y, y.y, dk);
-      dk = fmaf(x.z, y.z, dk);
-      dk = fmaf(x.w, y.w, dk);
-      dq = fmaf(x.x, z.x, dq);
-      dq = fmaf(x.y, z.y, dq);
-      dq = fmaf(x.z, z.z, dq);
-      dq = fmaf(x.w, z.w, dq);
-    }
-    kk[m * kTreeMax + i] = dk;
-    kqd[i * kTreeMax + m] = dq;
+  for (int e = tid; e < kTreeMax * kTreeMax; e += kTreeThreads) {
+    wk[e] = 0.0f;  // zero off the paths
+    wq[e] = 0.0f;
+    kk[e] = 0.0f;  // and past M, so that every product read is finite
+    kqd[e] = 0.0f;
   }
   __syncthreads();
 
-  // path weights, one thread per node: row i of ek (the parent's path) and
-  // of eq (the node's own path), zero off the path
-  if (tid < M) {
-    const int i = tid;
-    for (int m = 0; m < kTreeMax; ++m) {
-      ek[i * kTreeMax + m] = 0.0f;
-      eq[i * kTreeMax + m] = 0.0f;
+  if (w == 0) {
+    // path weights, one lane per node walking its path once: W_im for the
+    // node's own path and W_pm for its parent's (W_pm = W_im / alpha_i,
+    // carried as a second product rather than divided)
+    if (lane >= M && lane < NMAX) {
+      aq[lane] = 0.0f;
+      ak[lane] = 0.0f;
+    } else if (lane < M) {
+      const int i = lane;
+      wq[i * kTreeMax + i] = 1.0f;
+      float wi = al[i], wp = 1.0f;
+      for (int m = par[i]; m >= 0; m = par[m]) {
+        wq[i * kTreeMax + m] = wi;
+        wk[i * kTreeMax + m] = wp;
+        const float g = al[m];
+        wi *= g;
+        wp *= g;
+      }
+      aq[i] = wi;  // A_i
+      ak[i] = wp;  // A_p (1 for a child of the context)
     }
-    float wgt = 1.0f;
-    for (int m = par[i]; m >= 0; m = par[m]) {
-      ek[i * kTreeMax + m] = wgt * kk[m * kTreeMax + i];
-      wgt *= al[m];
+  } else {
+    // k_m . k_i and k_m . q_i for every pair, 8 lanes a pair (the row
+    // layout: 16 columns a lane, a 3-step DPP sum)
+    const int grp = (tid - 64) >> 3;  // 0 .. 23
+    for (int e0 = 0; e0 < M * M; e0 += 24) {  // uniform trip count
+      const int e = e0 + grp;
+      const int i = e < M * M ? e / M : 0, m = e < M * M ? e % M : 0;
+      float dk = 0.0f, dq = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float4 x = kq[m * 32 + j + 8 * c];
+        const float4 y = kq[i * 32 + j + 8 * c];
+        const float4 z = kq[(M + i) * 32 + j + 8 * c];
+        dk = fmaf(x.x, y.x, dk);
+        dk = fmaf(x.y, y.y, dk);
+        dk = fmaf(x.z, y.z, dk);
+        dk = fmaf(x.w, y.w, dk);
+        dq = fmaf(x.x, z.x, dq);
+        dq = fmaf(x.y, z.y, dq);
+        dq = fmaf(x.z, z.z, dq);
+        dq = fmaf(x.w, z.w, dq);
+      }
+      dk = dpp_sum8(dk);
+      dq = dpp_sum8(dq);
+      if (j == 0 && e < M * M) {
+        kk[m * kTreeMax + i] = dk;
+        kqd[i * kTreeMax + m] = dq;
+      }
     }
-    ak[i] = wgt;  // A_p (1 for a child of the context)
-    wgt = 1.0f;
-    for (int m = i; m >= 0; m = par[m]) {
-      eq[i * kTreeMax + m] = wgt * kqd[i * kTreeMax + m];
-      wgt *= al[m];
-    }
-    aq[i] = wgt;  // A_i
   }
 
   // the row's s_0 . k_m and s_0 . q_m; lane j keeps those of m = j mod 8
   float s0k[4] = {0.0f, 0.0f, 0.0f, 0.0f}, s0q[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int m = 0; m < kTreeMax; ++m) {
-    if (m < M) {  // uniform
+  for (int m = 0; m < NMAX; ++m) {
+    {
       float pk = 0.0f, pq = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -381,22 +428,28 @@ __global__ __launch_bounds__(kTreeThreads) void gdn_tree_out_kernel(
       }
     }
   }
-  __syncthreads();  // ek, eq, ak, aq
+  __syncthreads();  // path weights and products
 
   // the recurrence in node order
   float cl[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int i = 0; i < kTreeMax; ++i) {
-    if (i < M) {  // uniform
+  for (int i = 0; i < NMAX; ++i) {
+    {
       float part = j == i % 8 ? ak[i] * s0k[i / 8] : 0.0f;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) part = fmaf(ek[i * kTreeMax + 8 * t + j], cl[t], part);
+      for (int t = 0; t < NMAX / 8; ++t) {
+        const int m = 8 * t + j;
+        part = fmaf(wk[i * kTreeMax + m] * kk[m * kTreeMax + i], cl[t], part);
+      }
       const float d = dpp_sum8(part);  // s_p . k_i
       const float c = be[i] * (vsm[i * kTreeRows + row] - al[i] * d);
       if (j == i % 8) cl[i / 8] = c;
       part = j == i % 8 ? aq[i] * s0q[i / 8] : 0.0f;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) part = fmaf(eq[i * kTreeMax + 8 * t + j], cl[t], part);
+      for (int t = 0; t < NMAX / 8; ++t) {
+        const int m = 8 * t + j;
+        part = fmaf(wq[i * kTreeMax + m] * kqd[i * kTreeMax + m], cl[t], part);
+      }
       const float o = dpp_sum8(part);
       if (j == 0) obuf[i * kTreeRows + row] = o;
     }
@@ -440,8 +493,12 @@ extern "C" int q4_gdn_tree_out(const float *S, int H, int Hk, int dv, int dk,
   if (st != Q4_OK) return st;
   const q4v::GdnTreeArgs a{S, q, k, v, alpha, beta, parent, out, status,
                            H, Hk, dv, M, dv / q4v::kTreeRows};
-  hipLaunchKernelGGL(q4v::gdn_tree_out_kernel, dim3(static_cast<uint32_t>(blocks)),
-                     dim3(q4v::kTreeThreads), 0, static_cast<hipStream_t>(stream), a);
+  if (M <= 16)
+    hipLaunchKernelGGL(q4v::gdn_tree_out_kernel<16>, dim3(static_cast<uint32_t>(blocks)),
+                       dim3(q4v::kTreeThreads), 0, static_cast<hipStream_t>(stream), a);
+  else
+    hipLaunchKernelGGL(q4v::gdn_tree_out_kernel<32>, dim3(static_cast<uint32_t>(blocks)),
+                       dim3(q4v::kTreeThreads), 0, static_cast<hipStream_t>(stream), a);
   return hipGetLastError() == hipSuccess ? Q4_OK : Q4_ELAUNCH;
 }
 
