@@ -275,16 +275,18 @@ __global__ __launch_bounds__(kTreeThreads) void gdn_tree_out_kernel(
   const int hk = h / (a.H / a.Hk);
   const int row = 8 * w + rho;  // within the block
 
-  // this lane's part of its state row, issued first
-  const float4 *srow = reinterpret_cast<const float4 *>(
-      a.S + (static_cast<size_t>(h) * a.dv + static_cast<size_t>(rb) * kTreeRows + row) *
-                kGdnDk);
-  float4 st[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) st[i] = srow[j + 8 * i];
-
-  // every load of the tree's inputs issued at once, before the tree check,
-  // so that the workgroup waits for one round trip
+  // Loads in the order they are needed: the tree and the gates (for the
+  // check and the path weights), the keys, queries and values (for the
+  // products), then this lane's part of its state row (for the row's
+  // products, after the path weights); all issued before the tree check,
+  // so that the workgroup waits for one round trip.
+  int pi = -1;
+  if (lane < M) pi = a.parent[lane];
+  float ga = 0.0f, gb = 0.0f;
+  if (tid < M) {
+    ga = a.alpha[static_cast<size_t>(tid) * a.H + h];
+    gb = a.beta[static_cast<size_t>(tid) * a.H + h];
+  }
   float4 kqr[2 * kTreeMax * 32 / kTreeThreads];
   float vr[kTreeMax * kTreeRows / kTreeThreads];
 #pragma unroll
@@ -309,18 +311,15 @@ __global__ __launch_bounds__(kTreeThreads) void gdn_tree_out_kernel(
       vr[r] = a.v[(static_cast<size_t>(e / kTreeRows) * a.H + h) * a.dv +
                   static_cast<size_t>(rb) * kTreeRows + e % kTreeRows];
   }
-  float ga = 0.0f, gb = 0.0f;
-  if (tid < M) {
-    ga = a.alpha[static_cast<size_t>(tid) * a.H + h];
-    gb = a.beta[static_cast<size_t>(tid) * a.H + h];
-  }
+  const float4 *srow = reinterpret_cast<const float4 *>(
+      a.S + (static_cast<size_t>(h) * a.dv + static_cast<size_t>(rb) * kTreeRows + row) *
+                kGdnDk);
+  float4 st[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) st[i] = srow[j + 8 * i];
+
   // every wave checks the whole tree: -1 <= parent[i] < i
-  int pi = -1;
-  bool bad_lane = false;
-  if (lane < M) {
-    pi = a.parent[lane];
-    bad_lane = pi < -1 || pi >= lane;
-  }
+  const bool bad_lane = lane < M && (pi < -1 || pi >= lane);
   const bool bad = __ballot(bad_lane) != 0;
   if (blockIdx.x == 0 && tid == 0 && a.status != nullptr)
     a.status[0] = bad ? Q4_EINVAL : Q4_OK;
