@@ -220,8 +220,8 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_commit_kernel(
 // Rows stay independent, and along a path the row s evolves as
 //     s_i = alpha_i s_p + c_i k_i,  c_i = beta_i (v_i[r] - alpha_i s_p . k_i)
 // (p the parent), so s_i = A_i s_0 + sum_{m in path(i)} W_im c_m k_m with
-// W_im the product of the gates of the nodes below m on the path and A_i the
-// product over the whole path.  Hence, with the row's dot products
+// W_im the product of the gates of the path's nodes after m, down to i
+// (W_ii = 1), and A_i the product over the whole path.  Hence, with the row's dot products
 // s_0 . k_m and s_0 . q_i and the layer's key-key and key-query products,
 //     s_p . k_i = A_p (s_0 . k_i) + sum_{m in path(p)} W_pm (k_m . k_i) c_m,
 //     o_i[r]    = A_i (s_0 . q_i) + sum_{m in path(i)} W_im (k_m . q_i) c_m:
