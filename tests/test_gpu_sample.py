@@ -139,9 +139,12 @@ def test_greedy(q4):
     assert np.array_equal(g["token"], g["greedy"])
 
 
+# rows of 1 to 62 slices of 16384 columns (1000000 columns: 62 lists of 32
+# candidates in the row merge)
 @pytest.mark.parametrize("M,V,k", [(1, 7, 7), (3, 100, 32), (16, 64, 32),
                                    (2, 16385, 32), (5, 1, 1),
-                                   (1024, 300, 16)])
+                                   (1024, 300, 16), (3, 262144, 32),
+                                   (2, 300000, 32), (1, 1000000, 20)])
 def test_shapes_and_edges(q4, M, V, k):
     dev = torch.device("cuda")
     gen = torch.Generator(device=dev).manual_seed(10 + V)
