@@ -231,9 +231,10 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_commit_kernel(
 //    columns 4 (j + 8 i) .. +3, i = 0..3, of row 8 w + rho, and a row's dot
 //    product is 16 FMAs per lane and a 3-step DPP sum over its 8 lanes;
 //  * the tree's keys and queries (for the head's key head), its values for
-//    the workgroup's rows and the gates sit in LDS; while one wave forms the
-//    path weights (a lane per node walking its path once), the other three
-//    form the products k_m . k_i and k_m . q_i, 8 lanes a pair;
+//    the workgroup's rows and the gates sit in LDS; one wave forms the path
+//    weights (a lane per node walking its path once), then every wave forms
+//    the products k_m . k_i and k_m . q_i in the row layout, the keys and
+//    queries standing in for state rows;
 //  * in the recurrence lane j keeps c_m, s_0 . k_m and s_0 . q_m for the
 //    nodes m = j mod 8, so each step is a few FMAs and one 8-lane sum.
 constexpr int kTreeRows = 32;
@@ -369,33 +370,33 @@ __global__ __launch_bounds__(kTreeThreads) void gdn_tree_out_kernel(
       aq[i] = wi;  // A_i
       ak[i] = wp;  // A_p (1 for a child of the context)
     }
-  } else {
-    // k_m . k_i and k_m . q_i for every pair, 8 lanes a pair (the row
-    // layout: 16 columns a lane, a 3-step DPP sum)
-    const int grp = (tid - 64) >> 3;  // 0 .. 23
-    for (int e0 = 0; e0 < M * M; e0 += 24) {  // uniform trip count
-      const int e = e0 + grp;
-      const int i = e < M * M ? e / M : 0, m = e < M * M ? e % M : 0;
-      float dk = 0.0f, dq = 0.0f;
+  }
+  // k_m . k_i and k_m . q_i for every pair, in the row layout: the keys and
+  // the queries (rows 0 .. 2M-1 of kq) take the place of state rows, 32 a
+  // pass, and each is multiplied with every key m
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float4 x = kq[m * 32 + j + 8 * c];
-        const float4 y = kq[i * 32 + j + 8 * c];
-        const float4 z = kq[(M + i) * 32 + j + 8 * c];
-        dk = fmaf(x.x, y.x, dk);
-        dk = fmaf(x.y, y.y, dk);
-        dk = fmaf(x.z, y.z, dk);
-        dk = fmaf(x.w, y.w, dk);
-        dq = fmaf(x.x, z.x, dq);
-        dq = fmaf(x.y, z.y, dq);
-        dq = fmaf(x.z, z.z, dq);
-        dq = fmaf(x.w, z.w, dq);
+  for (int g0 = 0; g0 < 2 * NMAX; g0 += kTreeRows) {
+    const int gr = g0 + row;  // the key (gr < M) or query (gr - M) of this lane's row
+    float4 kr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kr[i] = kq[gr * 32 + j + 8 * i];
+#pragma unroll 8
+    for (int m = 0; m < NMAX; ++m) {
+      float d = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 x = kq[m * 32 + j + 8 * i];
+        d = fmaf(kr[i].x, x.x, d);
+        d = fmaf(kr[i].y, x.y, d);
+        d = fmaf(kr[i].z, x.z, d);
+        d = fmaf(kr[i].w, x.w, d);
       }
-      dk = dpp_sum8(dk);
-      dq = dpp_sum8(dq);
-      if (j == 0 && e < M * M) {
-        kk[m * kTreeMax + i] = dk;
-        kqd[i * kTreeMax + m] = dq;
+      d = dpp_sum8(d);
+      if (j == 0 && m < M) {
+        if (gr < M)
+          kk[m * kTreeMax + gr] = d;
+        else if (gr < 2 * M)
+          kqd[(gr - M) * kTreeMax + m] = d;
       }
     }
   }
