@@ -373,7 +373,10 @@ __global__ __launch_bounds__(kTreeThreads) void gdn_tree_out_kernel(
   }
   // k_m . k_i and k_m . q_i for every pair, in the row layout: the keys and
   // the queries (rows 0 .. 2M-1 of kq) take the place of state rows, 32 a
-  // pass, and each is multiplied with every key m
+  // pass, and each is multiplied with every key m; the first pass also forms
+  // the row's s_0 . k_m and s_0 . q_m (lane j keeps those of m = j mod 8),
+  // sharing the read of key m
+  float s0k[4] = {0.0f, 0.0f, 0.0f, 0.0f}, s0q[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int g0 = 0; g0 < 2 * NMAX; g0 += kTreeRows) {
     const int gr = g0 + row;  // the key (gr < M) or query (gr - M) of this lane's row
@@ -382,7 +385,7 @@ __global__ __launch_bounds__(kTreeThreads) void gdn_tree_out_kernel(
     for (int i = 0; i < 4; ++i) kr[i] = kq[gr * 32 + j + 8 * i];
 #pragma unroll 8
     for (int m = 0; m < NMAX; ++m) {
-      float d = 0.0f;
+      float d = 0.0f, pk = 0.0f, pq = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float4 x = kq[m * 32 + j + 8 * i];
@@ -390,6 +393,17 @@ __global__ __launch_bounds__(kTreeThreads) void gdn_tree_out_kernel(
         d = fmaf(kr[i].y, x.y, d);
         d = fmaf(kr[i].z, x.z, d);
         d = fmaf(kr[i].w, x.w, d);
+        if (g0 == 0) {
+          const float4 z = kq[(M + m) * 32 + j + 8 * i];
+          pk = fmaf(st[i].x, x.x, pk);
+          pk = fmaf(st[i].y, x.y, pk);
+          pk = fmaf(st[i].z, x.z, pk);
+          pk = fmaf(st[i].w, x.w, pk);
+          pq = fmaf(st[i].x, z.x, pq);
+          pq = fmaf(st[i].y, z.y, pq);
+          pq = fmaf(st[i].z, z.z, pq);
+          pq = fmaf(st[i].w, z.w, pq);
+        }
       }
       d = dpp_sum8(d);
       if (j == 0 && m < M) {
@@ -398,33 +412,13 @@ __global__ __launch_bounds__(kTreeThreads) void gdn_tree_out_kernel(
         else if (gr < 2 * M)
           kqd[(gr - M) * kTreeMax + m] = d;
       }
-    }
-  }
-
-  // the row's s_0 . k_m and s_0 . q_m; lane j keeps those of m = j mod 8
-  float s0k[4] = {0.0f, 0.0f, 0.0f, 0.0f}, s0q[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int m = 0; m < NMAX; ++m) {
-    {
-      float pk = 0.0f, pq = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 x = kq[m * 32 + j + 8 * i];
-        const float4 z = kq[(M + m) * 32 + j + 8 * i];
-        pk = fmaf(st[i].x, x.x, pk);
-        pk = fmaf(st[i].y, x.y, pk);
-        pk = fmaf(st[i].z, x.z, pk);
-        pk = fmaf(st[i].w, x.w, pk);
-        pq = fmaf(st[i].x, z.x, pq);
-        pq = fmaf(st[i].y, z.y, pq);
-        pq = fmaf(st[i].z, z.z, pq);
-        pq = fmaf(st[i].w, z.w, pq);
-      }
-      pk = dpp_sum8(pk);
-      pq = dpp_sum8(pq);
-      if (j == m % 8) {
-        s0k[m / 8] = pk;
-        s0q[m / 8] = pq;
+      if (g0 == 0) {
+        pk = dpp_sum8(pk);
+        pq = dpp_sum8(pq);
+        if (j == m % 8) {
+          s0k[m / 8] = pk;
+          s0q[m / 8] = pq;
+        }
       }
     }
   }
