@@ -417,7 +417,8 @@ int q4_gdn_tree_out(const float *S, int H, int Hk, int dv, int dk, int M,
  * h / (Hq / Hkv).  The output is softmax(scale * q k^T) v over the visible
  * positions, with k = k8 * k_scale and v = v8 * v_scale.
  * Arithmetic: bf16 products on MFMA (the int8 values are exact in bf16), fp32
- * accumulation, the probabilities rounded to bf16 for the value product.
+ * accumulation; each probability times its value scale enters the value
+ * product as a pair of bf16 (head + tail, 16 significant bits).
  * ------------------------------------------------------------------------ */
 #define Q4_ATTN_HEAD_DIM 256
 #define Q4_ATTN_PAGE 32

@@ -49,13 +49,16 @@ class AttnOracle:
         P, I = ctypes.c_void_p, ctypes.c_int
         lib.ta_tree_attention.argtypes = [P, I, I, I, I, P, P, P, P, P, I,
                                           ctypes.c_int64, P, ctypes.c_double,
-                                          P]
+                                          P, P]
         lib.ta_tree_attention.restype = I
         self.lib = lib
 
     def attention(self, q_bits, k_pages, v_pages, k_scale, v_scale,
-                  page_table, ctx_len: int, anc, scale: float):
-        """Outputs [M, Hq, D] (float64).
+                  page_table, ctx_len: int, anc, scale: float,
+                  with_abs: bool = False):
+        """Outputs [M, Hq, D] (float64); with ``with_abs`` the pair
+        (outputs, absw), absw[i, h, d] = sum_p w_p |v_p[d]| with the same
+        softmax weights (the scale of the rounding error of the terms).
 
         q_bits uint16 [M, Hq, D] (bf16 bit patterns); k_pages int8
         [pool, Hkv, 32, D]; v_pages int8 [pool, Hkv, D, 32]; k_scale,
@@ -77,13 +80,15 @@ class AttnOracle:
         if pt.size < (ctx_len + M + PAGE - 1) // PAGE:
             raise ValueError("attention: page table too short")
         out = np.zeros((M, Hq, D), dtype=np.float64)
+        absw = np.zeros((M, Hq, D), dtype=np.float64) if with_abs else None
         st = self.lib.ta_tree_attention(_p(q), M, Hq, Hkv, D, _p(kp), _p(vp),
                                         _p(ks), _p(vs), _p(pt), pool,
                                         int(ctx_len), _p(an), float(scale),
-                                        _p(out))
+                                        _p(out),
+                                        None if absw is None else _p(absw))
         if st != 0:
             raise ValueError(f"ta_tree_attention status {st}")
-        return out
+        return (out, absw) if with_abs else out
 
 
 _default = None

@@ -25,6 +25,14 @@
  *  - Queries arrive as bf16 bit patterns [M][Hq][D].
  *
  * Straight from the definition, IEEE double, no blocking.
+ *
+ * Besides the outputs o[i][h][d] = sum_p w_p v_p[d], it can return
+ * absw[i][h][d] = sum_p w_p |v_p[d]|, the same weights applied to the
+ * magnitudes of the values.  That sum is the scale of the rounding error of
+ * any evaluation that rounds the terms w_p v_p[d] (or w_p times the value
+ * scale) to a shorter format before adding them: a term rounded to relative
+ * precision u moves the output by at most u * w_p |v_p[d]|.  Pass NULL when
+ * it is not needed.
  * Status: 0 ok, -1 invalid argument.
  */
 #include <math.h>
@@ -49,7 +57,7 @@ int ta_tree_attention(const uint16_t *q, int M, int Hq, int Hkv, int D,
                       const float *k_scale, const float *v_scale,
                       const int32_t *page_table, int pool_pages,
                       int64_t ctx_len, const uint32_t *anc, double scale,
-                      double *out) {
+                      double *out, double *absw) {
   if (q == NULL || k_pages == NULL || v_pages == NULL || k_scale == NULL ||
       v_scale == NULL || page_table == NULL || anc == NULL || out == NULL ||
       M < 1 || M > 32 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || D < 1 ||
@@ -95,7 +103,10 @@ int ta_tree_attention(const uint16_t *q, int M, int Hq, int Hkv, int D,
         den += s[p];
       }
       double *o = out + ((size_t)i * Hq + h) * D;
+      double *ao = absw == NULL ? NULL : absw + ((size_t)i * Hq + h) * D;
       for (int d = 0; d < D; ++d) o[d] = 0.0;
+      if (ao != NULL)
+        for (int d = 0; d < D; ++d) ao[d] = 0.0;
       for (int64_t p = 0; p < total; ++p) {
         if (!vis[p]) continue;
         const int64_t pp = page_of(page_table, p);
@@ -106,6 +117,7 @@ int ta_tree_attention(const uint16_t *q, int M, int Hq, int Hkv, int D,
         for (int d = 0; d < D; ++d) {
           const int8_t v8 = v_pages[base * 32 * (size_t)D + (size_t)d * 32 + slot];
           o[d] += w * ((double)v8 * vs);
+          if (ao != NULL) ao[d] += w * fabs((double)v8 * vs);
         }
       }
     }

@@ -24,8 +24,9 @@
 //    when a score passes it by more than 2^8; each node's 32 scores of a
 //    page sit in 4 lanes x 8 registers.  The ancestor mask applies to tree positions,
 //    a 32-bit ancestor-or-self set per node.
-//  * Values on MFMA: O^T[dim][node] += V^T P'^T with P' = p * v_scale in
-//    bf16; the value tile's tokens are stored in the order in which the
+//  * Values on MFMA: O^T[dim][node] += V^T P'^T with P' = p * v_scale as a
+//    pair of bf16 (head + tail, 16 significant bits between them) and two
+//    MFMAs per value tile; the value tile's tokens are stored in the order in which the
 //    score tiles hold them in a lane (tokens 4g..4g+3, 16+4g..16+4g+3 for
 //    lane group g), so the probabilities need no shuffle.
 //  * A run over the whole context writes normalised outputs; otherwise the
@@ -375,16 +376,27 @@ __global__ __launch_bounds__(64 * G) void tree_attn_kernel(AttnArgs a) {
     }
     lsum += ps;
     // P'^T as the B operand: slot 8 gq + e <- token 4 gq + e (e < 4) and
-    // 16 + 4 gq + e - 4 (e >= 4), exactly the order of p[]
-    const u32x4 pb4 = {pack_bf16(p[0] * vsc[0], p[1] * vsc[1]),
-                       pack_bf16(p[2] * vsc[2], p[3] * vsc[3]),
-                       pack_bf16(p[4] * vsc[4], p[5] * vsc[5]),
-                       pack_bf16(p[6] * vsc[6], p[7] * vsc[7])};
+    // 16 + 4 gq + e - 4 (e >= 4), exactly the order of p[].  P' = p * v_scale
+    // is split into a bf16 head and a bf16 tail (P' - head, rounded), and the
+    // value tile is multiplied by both: the pair carries 16 significant bits,
+    // so the value product moves each term by a relative 2^-16 at most
+    // instead of the 2^-8 of one bf16.
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pv[i] = p[i] * vsc[i];
+    u32x4 ph, pl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ph[i] = pack_bf16(pv[2 * i], pv[2 * i + 1]);
+      pl[i] = pack_bf16(pv[2 * i] - __uint_as_float(ph[i] << 16),
+                        pv[2 * i + 1] - __uint_as_float(ph[i] & 0xFFFF0000u));
+    }
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) {
       const u32x4 va = *reinterpret_cast<const u32x4 *>(
           buf + kKBytes + (16 * dt + n) * kVStride + 16 * gq);
-      o[dt] = mfma(va, pb4, o[dt]);
+      o[dt] = mfma(va, ph, o[dt]);
+      o[dt] = mfma(va, pl, o[dt]);
     }
   };
 

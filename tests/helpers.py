@@ -126,3 +126,35 @@ def tiled_from_planar(packed: np.ndarray, N: int, K: int) -> np.ndarray:
     sb = sb.transpose(0, 2, 1, 3, 4).reshape(T, Q, 16 * 8)   # u16 values
     out[:, :, 2048:] = sb.astype("<u2").view(np.uint8).reshape(T, Q, 256)
     return out.reshape(-1)
+
+
+# Tree-verify attention: per-element bound of the GPU outputs against the
+# oracle, |o_gpu - o| <= ATTN_REL * absw + ATTN_ABS, absw = sum_p w_p |v_p|
+# from the oracle.  Error sources of the kernel:
+#  * the value product: each probability times its value scale is carried as
+#    a pair of bf16 (head + rounded tail), 16 significant bits, so each term
+#    moves by a relative 2^-16 at most;
+#  * the scores: bf16 x int8 products are exact; the MFMA adds them into an
+#    fp32 accumulator in 8 steps of 32, so a score is off by at most
+#    8 * 2^-24 * sum_d |q_d k_d| * k_scale * scale.  For the test caches
+#    (|q| < 5, |k8| <= 127, k_scale <= 0.02, scale 1/16) that is below
+#    2^-13.4, which moves each softmax weight by a relative 2^-12.4 at most;
+#  * the exponentials, the fp32 sums and the merge of runs: near 2^-20.
+# Together below 2^-12 + 2^-14 of absw.  The absolute term covers outputs
+# whose absw is itself tiny.
+ATTN_REL = 2.0 ** -12 + 2.0 ** -14
+ATTN_ABS = 1e-7
+
+
+def attn_bound(absw: np.ndarray) -> np.ndarray:
+    return ATTN_REL * absw + ATTN_ABS
+
+
+def oracle_threads() -> int:
+    """Threads for the CPU oracle: the CPUs this process may run on, at most
+    16 (a one-GPU share of the test machine's host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))

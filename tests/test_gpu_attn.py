@@ -1,15 +1,17 @@
 """GPU parity of tree-verify attention against the CPU oracle.
 
-Tolerance, from the arithmetic: the scores are exact bf16 x int8 products
-summed in fp32 (relative error about 256 * 2^-24), the softmax runs in fp32
-with the hardware exp2, and the probabilities times the value scales are
-rounded to bf16 (relative error <= 2^-9) before the value product.  An output
-is therefore within 2^-9 * sum_p w_p |v_p| <= 2^-9 * max |v| of the exact
-result, plus fp32 rounding; the test allows 2^-8 * max |v| + 1e-6, max |v|
-over the cache.  A wrong mask, page, head or layout gives errors of the size
-of the values themselves.
+Tolerance, from the arithmetic (tests/helpers.py, ATTN_REL): the scores are
+exact bf16 x int8 products summed in fp32, the softmax runs in fp32 with the
+hardware exp2, and each probability times its value scale enters the value
+product as a bf16 pair (head + tail, 16 significant bits).  Every output
+element is checked against |o_gpu - o| <= (2^-12 + 2^-14) * sum_p w_p |v_p|
++ 1e-7, with sum_p w_p |v_p| returned by the oracle for that element.  At the
+benchmarked 32K context that bound rejects an output that lost the values of
+1/64 of the pages by a wide margin (tests/test_attn_bound.py).
 """
 from __future__ import annotations
+
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -17,6 +19,7 @@ import torch
 
 import synth
 from oracle import attn as ao
+from tests.helpers import attn_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -44,25 +47,34 @@ def _host(inp):
     return h
 
 
-def _oracle(h, heads=None):
-    """Oracle outputs; `heads` restricts to the query heads of one KV head
-    (g, G) to keep the CPU time small."""
-    q = h["q"]
-    kp, vp, ks, vs = h["k_pages"], h["v_pages"], h["k_scale"], h["v_scale"]
+def _oracle_head(h, g, G):
+    """Oracle outputs and sums of w|v| of the query heads of KV head g."""
     anc = h["anc"].view(np.uint32)
-    if heads is not None:
-        g, G = heads
-        q = q[:, g * G:(g + 1) * G]
-        kp, vp = kp[:, g:g + 1], vp[:, g:g + 1]
-        ks, vs = ks[:, g:g + 1], vs[:, g:g + 1]
-    return ao.attention(q, kp, vp, ks, vs, h["page_table"], h["ctx_len"],
-                        anc, SCALE)
+    return ao.attention(h["q"][:, g * G:(g + 1) * G],
+                        h["k_pages"][:, g:g + 1], h["v_pages"][:, g:g + 1],
+                        h["k_scale"][:, g:g + 1], h["v_scale"][:, g:g + 1],
+                        h["page_table"], h["ctx_len"], anc, SCALE,
+                        with_abs=True)
 
 
-def _tol(h):
-    vmax = float(np.abs(h["v_pages"].astype(np.float64)).max() *
-                 h["v_scale"].max())
-    return 2.0 ** -8 * vmax + 1e-6
+def _oracle(h):
+    """(outputs, sums of w|v|) of every head; the KV heads run on threads
+    (the oracle call releases the interpreter lock)."""
+    Hq, Hkv = h["q"].shape[1], h["k_pages"].shape[1]
+    G = Hq // Hkv
+    with ThreadPoolExecutor(max_workers=min(Hkv, 8)) as ex:
+        parts = list(ex.map(lambda g: _oracle_head(h, g, G), range(Hkv)))
+    return (np.concatenate([p[0] for p in parts], axis=1),
+            np.concatenate([p[1] for p in parts], axis=1))
+
+
+def _check(got, want, absw, what):
+    """Every element within the bound; report the worst ratio."""
+    assert np.isfinite(got).all(), what
+    ratio = np.abs(got - want) / attn_bound(absw)
+    worst = float(ratio.max())
+    _say(f"  {what}: max |err|/bound = {worst:.3f}")
+    assert worst <= 1.0, (what, worst, np.unravel_index(ratio.argmax(), ratio.shape))
 
 
 def _run(q4, inp, splits=0, status=None):
@@ -85,35 +97,32 @@ def test_attention_matches_oracle(q4, M, Hq, Hkv, ctx, splits):
     _say(f"case tree attn M={M} Hq={Hq} Hkv={Hkv} ctx={ctx} splits={splits}")
     inp = synth.attn_inputs(M, Hq, Hkv, ctx, seed=M + ctx, device=dev)
     got = _run(q4, inp, splits)
-    h = _host(inp)
-    want = _oracle(h)
-    err = np.abs(got - want).max()
-    assert err <= _tol(h), (err, _tol(h))
+    want, absw = _oracle(_host(inp))
+    _check(got, want, absw, "all heads")
 
 
-def test_full_shape_sampled(q4):
-    """24 query heads over 4 KV heads, 16 nodes, a 32768-token context, the
-    launch the bench times: one KV head's six query heads against the
-    oracle, every output finite."""
+@pytest.mark.parametrize("ctx", [4096, 32768])
+def test_full_shape(q4, ctx):
+    """24 query heads over 4 KV heads, 16 nodes, the contexts the bench
+    times, in the launch it times: every output element of every head
+    against the oracle."""
     dev = torch.device("cuda")
-    _say("case tree attn full 16 x 24/4 x 256, ctx 32768")
-    inp = synth.attn_inputs(16, 24, 4, 32768, seed=40, device=dev)
+    _say(f"case tree attn full 16 x 24/4 x 256, ctx {ctx}")
+    inp = synth.attn_inputs(16, 24, 4, ctx, seed=40, device=dev)
     got = _run(q4, inp)
-    assert np.isfinite(got).all()
-    h = _host(inp)
-    want = _oracle(h, heads=(2, 6))
-    err = np.abs(got[:, 12:18] - want).max()
-    assert err <= _tol(h), (err, _tol(h))
+    want, absw = _oracle(_host(inp))
+    _check(got, want, absw, f"ctx {ctx}")
 
 
-def test_splits_agree(q4):
+def test_splits_match_oracle(q4):
+    """Every split count, one run per workgroup up to many, against the
+    oracle under the same bound."""
     dev = torch.device("cuda")
     inp = synth.attn_inputs(16, 24, 4, 3000, seed=41, device=dev)
-    a = _run(q4, inp, 1)
-    h = _host(inp)
-    for s in (2, 7, 0):
-        b = _run(q4, inp, s)
-        assert np.abs(a - b).max() <= 2 * _tol(h), s
+    want, absw = _oracle(_host(inp))
+    for s in (1, 2, 7, 0, 94):
+        _say(f"case tree attn ctx 3000 splits={s}")
+        _check(_run(q4, inp, s), want, absw, f"splits {s}")
 
 
 def test_deterministic(q4):

@@ -267,6 +267,35 @@ def test_tree_out_chain_and_star(q4):
         _check_tree(out, inp)
 
 
+@pytest.mark.parametrize("M", [17, 24, 31])
+def test_tree_out_deep_trees_past_16(q4, M):
+    """The 32-node kernel (17..32 nodes): a chain of M nodes (a path 24 and
+    31 deep), a star, and the random tree of the generator; the zero padding
+    past node M - 1 must add nothing."""
+    dev = torch.device("cuda")
+    for name, par in (("chain", list(range(-1, M - 1))), ("star", [-1] * M),
+                      ("random", None)):
+        _say(f"case gdn tree out M={M} {name}")
+        inp = synth.gdn_inputs(1, 6, 2, M, dv=64, seed=35 + M, device=dev)
+        if par is not None:
+            inp["parent"] = np.asarray(par, dtype=np.int32)
+        out, st = _tree_out(q4, inp)
+        assert st == 0
+        _check_tree(out, inp)
+
+
+def test_tree_out_full_shape_32_nodes(q4):
+    """The 27B layer at 32 tree nodes: 48 value heads over 16 key heads of
+    128 x 128; two key heads' value heads against the oracle."""
+    dev = torch.device("cuda")
+    _say("case gdn tree out full 48/16 x 128 x 128, M=32")
+    inp = synth.gdn_inputs(1, 48, 16, 32, seed=36, device=dev)
+    out, st = _tree_out(q4, inp)
+    assert st == 0
+    assert torch.isfinite(out).all()
+    _check_tree(out, inp, heads=[0, 1, 2, 45, 46, 47])
+
+
 def test_tree_out_gates_near_zero(q4):
     """Tiny and zero gates: the path weights underflow towards 0, and a
     zero gate forgets everything above it on the path."""

@@ -21,6 +21,11 @@ What pins what:
 * permuting the physical pages (with the page table) changes nothing;
 * random caches against torch's float64 scaled-dot-product attention with a
   boolean mask on the dequantised keys and values (a library routine).
+
+The second output, sum_p w_p |v_p|, is pinned by: the plain mean of |v| over
+the visible set when the keys are zero; bitwise equality with the outputs
+when every value is non-negative (same weights, same order); torch's
+attention applied to |V|; and |o| <= sum_p w_p |v_p| everywhere.
 """
 from __future__ import annotations
 
@@ -223,6 +228,66 @@ def check_against_torch_sdpa(ao):
             assert np.allclose(out[:, h], ref.numpy(), rtol=1e-11, atol=1e-14), (C, h)
 
 
+def check_abs_zero_keys_mean(ao):
+    rng = np.random.default_rng(7)
+    C, Hq, Hkv, D = 45, 4, 2, 16
+    q, K8, ks, V8, vs = random_case(rng, C, TREE, Hq, Hkv, D)
+    K8[:] = 0
+    cache = make_cache(K8, ks, V8, vs)
+    _, absw = ao.attention(q, *cache, C, attn_mod.ancestor_masks(TREE), 0.5,
+                           with_abs=True)
+    G = Hq // Hkv
+    for i in range(len(TREE)):
+        pos = visible(TREE, C, i)
+        for h in range(Hq):
+            g = h // G
+            want = np.mean([np.abs(V8[p, g].astype(np.float64)) * float(vs[p, g])
+                            for p in pos], axis=0)
+            assert np.allclose(absw[i, h], want, rtol=1e-13, atol=1e-15), (i, h)
+
+
+def check_abs_nonnegative_values(ao):
+    """With every value >= 0 the two sums are the same terms in the same
+    order; with signed values |o| <= sum w |v|, and somewhere strictly."""
+    rng = np.random.default_rng(8)
+    C, Hq, Hkv, D = 60, 6, 2, 16
+    q, K8, ks, V8, vs = random_case(rng, C, TREE, Hq, Hkv, D)
+    anc = attn_mod.ancestor_masks(TREE)
+    Vp = np.abs(V8.astype(np.int16)).clip(0, 127).astype(np.int8)
+    out, absw = ao.attention(q, *make_cache(K8, ks, Vp, vs), C, anc, 0.2,
+                             with_abs=True)
+    assert np.array_equal(out, absw)
+    out, absw = ao.attention(q, *make_cache(K8, ks, V8, vs), C, anc, 0.2,
+                             with_abs=True)
+    assert (np.abs(out) <= absw).all()
+    assert (np.abs(out) < 0.5 * absw).any()
+
+
+def check_abs_against_torch_sdpa(ao):
+    rng = np.random.default_rng(9)
+    for C in (0, 33, 96):
+        Hq, Hkv, D = 4, 2, 16
+        q, K8, ks, V8, vs = random_case(rng, C, TREE, Hq, Hkv, D)
+        anc = attn_mod.ancestor_masks(TREE)
+        _, absw = ao.attention(q, *make_cache(K8, ks, V8, vs), C, anc, 0.23,
+                               with_abs=True)
+        M, T = len(TREE), C + len(TREE)
+        Kd = torch.from_numpy(K8.astype(np.float64) * ks[..., None].astype(np.float64))
+        Va = torch.from_numpy(np.abs(V8.astype(np.float64)) *
+                              vs[..., None].astype(np.float64))
+        Q = torch.from_numpy(bits_to_f64(q))
+        mask = torch.zeros((M, T), dtype=torch.bool)
+        for i in range(M):
+            mask[i, visible(TREE, C, i)] = True
+        G = Hq // Hkv
+        for h in range(Hq):
+            g = h // G
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                Q[:, h][None], Kd[:, g][None], Va[:, g][None],
+                attn_mask=mask[None], scale=0.23)[0]
+            assert np.allclose(absw[:, h], ref.numpy(), rtol=1e-11, atol=1e-14), (C, h)
+
+
 def check_errors(ao):
     q = np.zeros((1, 2, 4), dtype=np.uint16)
     K8 = np.zeros((3, 1, 4), dtype=np.int8)
@@ -243,7 +308,9 @@ def check_errors(ao):
 ALL_CHECKS = [check_zero_keys_mean, check_dominant_key,
               check_two_position_softmax, check_query_head_groups,
               check_mask_invariance, check_page_permutation,
-              check_against_torch_sdpa, check_errors]
+              check_against_torch_sdpa, check_abs_zero_keys_mean,
+              check_abs_nonnegative_values, check_abs_against_torch_sdpa,
+              check_errors]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
@@ -277,6 +344,12 @@ MUTANTS = {
     "page_table_ignored": ("return page_table[p / 32];", "return p / 32;"),
     "score_scale_ignored": ("s[p] = scale * dot;", "s[p] = dot;"),
     "not_normalised": ("const double w = s[p] / den;", "const double w = s[p];"),
+    "abs_signed": ("ao[d] += w * fabs((double)v8 * vs);",
+                   "ao[d] += w * ((double)v8 * vs);"),
+    "abs_unweighted": ("ao[d] += w * fabs((double)v8 * vs);",
+                       "ao[d] += fabs((double)v8 * vs);"),
+    "abs_value_scale_ignored": ("ao[d] += w * fabs((double)v8 * vs);",
+                                "ao[d] += w * fabs((double)v8);"),
 }
 
 
