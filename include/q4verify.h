@@ -50,7 +50,8 @@ typedef enum {
   Q4_EALIGN = -2,    /* a pointer is not aligned as the call requires      */
   Q4_EOVERFLOW = -3, /* a byte count does not fit 64 bits                  */
   Q4_EDEVICE = -4,   /* no HIP device, or the current one is not gfx950    */
-  Q4_ELAUNCH = -5    /* the HIP runtime refused the launch                 */
+  Q4_ELAUNCH = -5,   /* the HIP runtime refused the launch                 */
+  Q4_ESCRATCH = -6   /* more scratch than q4_gemm_verify_tiled_noalloc has */
 } q4_status;
 
 /* Layout ids accepted by q4_pack_layout. */
@@ -259,6 +260,33 @@ int q4_gemm_verify_plan(int M, int64_t N, int64_t K, uint32_t layout_id,
 int q4_gemm_verify_tiled_ws(const void *x, const void *W_tiled, float *y,
                             int M, int64_t N, int64_t K, void *workspace,
                             uint64_t workspace_bytes, void *stream);
+
+/*
+ * q4_gemm_verify_tiled_noalloc -- q4_gemm_verify_tiled_ws for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the K-split partial products go
+ * to a scratch array the library holds in device memory instead of a
+ * caller workspace.  Same kernels, plan and results (bit for bit) as
+ * q4_gemm_verify_tiled_ws.
+ *   x, W_tiled, y, M, N, K, stream: as q4_gemm_verify_tiled_ws.
+ * The scratch is Q4_NOALLOC_SCRATCH_BYTES per device, a static array of the
+ * library's code object that each GPU it runs on holds until the process
+ * ends; nothing is allocated or freed by the call.  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (two streams, or
+ * two host threads) race, and must be ordered by the caller.  Nothing in the
+ * array needs to start at zero (each part writes its whole slice before the
+ * reduction reads it), and a later call overwrites what an earlier one left.
+ * Shapes whose plan needs more workspace than the array holds (see
+ * q4_gemm_verify_tiled_ws_plan) return Q4_ESCRATCH before anything is
+ * enqueued.  Every projection of the 27B model fits at every M <= 32 (the
+ * largest, 5120 x 17408 at M = 32, needs 4.4 MiB) except the 248320-row LM
+ * head at M > 16 (16-30 MiB); at M <= 16 and N <= 5120 every K <= 98304
+ * fits.
+ * Errors: as q4_gemm_verify_tiled_ws; Q4_ESCRATCH as above.
+ */
+#define Q4_NOALLOC_SCRATCH_BYTES (8u << 20)
+int q4_gemm_verify_tiled_noalloc(const void *x, const void *W_tiled, float *y,
+                                 int M, int64_t N, int64_t K, void *stream);
 
 /*
  * q4_gemm_verify_tiled_ws_plan -- the plan q4_gemm_verify_tiled_ws launches

@@ -14,6 +14,8 @@ Functions (same names as the C entry points):
 * :func:`q4_gemm_verify_tiled` -- the same product on tiled weights.
 * :func:`q4_gemm_verify_tiled_ws` -- the tiled product with a workspace
   (K split across workgroups for K > 5120); :func:`workspace_for` sizes it.
+* :func:`q4_gemm_verify_tiled_noalloc` -- the workspace product with the
+  library's static device scratch instead: allocates nothing.
 * :func:`q4_gemm_verify_plan`, :func:`q4_gemm_verify_tiled_ws_plan` -- launch
   plans of a shape.
 * :func:`q4_verify_sample` (:func:`verify_sample` allocates its outputs) --
@@ -29,13 +31,14 @@ Functions (same names as the C entry points):
 * :func:`q4_stream_read`, :func:`q4_stream_copy` -- bandwidth probes.
 * :func:`q4_status_string` -- name of a status code.
 """
-from ._lib import (ATTN_HEAD_DIM, ATTN_MAX_NODES, ATTN_PAGE, GDN_DK, GDN_MAX_NODES, GROUP, KERNEL_PLANAR, KERNEL_TILED_KSLICE,
+from ._lib import (ESCRATCH, ATTN_HEAD_DIM, ATTN_MAX_NODES, ATTN_PAGE, GDN_DK, GDN_MAX_NODES, GROUP, KERNEL_PLANAR, KERNEL_TILED_KSLICE,
                    KERNEL_TILED_RESIDENT,
                    KERNEL_TILED_STREAM, LAYOUT_PLANAR, LAYOUT_TILED16, MAX_ROWS,
                    MAX_ROWS_TILED, Q4Error,
                    LIB_PATH, lib_exports, load, q4_dequant, q4_gemm_verify,
                    q4_gemm_verify_plan, q4_gemm_verify_tiled,
                    q4_gemm_verify_tiled_ws, q4_gemm_verify_tiled_ws_plan,
+                   q4_gemm_verify_tiled_noalloc, NOALLOC_SCRATCH_BYTES,
                    q4_gdn_commit, q4_gdn_tree_out, q4_pack_layout, q4_verify_sample,
                    q4_verify_sample_workspace, verify_sample,
                    workspace_for,
@@ -43,13 +46,14 @@ from ._lib import (ATTN_HEAD_DIM, ATTN_MAX_NODES, ATTN_PAGE, GDN_DK, GDN_MAX_NOD
                    q4_stream_read, q4_tree_attn, q4_tree_attn_plan,
                    tree_attn)
 
-__all__ = ["ATTN_HEAD_DIM", "ATTN_MAX_NODES", "ATTN_PAGE", "GDN_DK", "GDN_MAX_NODES", "GROUP", "KERNEL_PLANAR", "KERNEL_TILED_KSLICE",
+__all__ = ["ESCRATCH", "ATTN_HEAD_DIM", "ATTN_MAX_NODES", "ATTN_PAGE", "GDN_DK", "GDN_MAX_NODES", "GROUP", "KERNEL_PLANAR", "KERNEL_TILED_KSLICE",
            "KERNEL_TILED_RESIDENT",
            "KERNEL_TILED_STREAM", "LAYOUT_PLANAR", "LAYOUT_TILED16", "MAX_ROWS",
            "MAX_ROWS_TILED", "Q4Error",
            "LIB_PATH", "lib_exports", "load", "q4_dequant", "q4_gemm_verify",
            "q4_gemm_verify_plan", "q4_gemm_verify_tiled",
            "q4_gemm_verify_tiled_ws", "q4_gemm_verify_tiled_ws_plan",
+           "q4_gemm_verify_tiled_noalloc", "NOALLOC_SCRATCH_BYTES",
            "q4_gdn_commit", "q4_gdn_tree_out", "q4_pack_layout", "q4_verify_sample",
            "q4_verify_sample_workspace", "verify_sample", "workspace_for",
            "q4_repack", "q4_status_string", "q4_stream_copy",

@@ -18,7 +18,9 @@ KERNEL_TILED_STREAM = 1
 KERNEL_TILED_RESIDENT = 2
 KERNEL_TILED_KSLICE = 3
 
-OK, EINVAL, EALIGN, EOVERFLOW, EDEVICE, ELAUNCH = 0, -1, -2, -3, -4, -5
+OK, EINVAL, EALIGN, EOVERFLOW, EDEVICE, ELAUNCH, ESCRATCH = \
+    0, -1, -2, -3, -4, -5, -6
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 class Q4Error(RuntimeError):
@@ -86,6 +88,10 @@ _SIGNATURES = {
                                  ctypes.c_int64, ctypes.c_void_p,
                                  ctypes.c_uint64, ctypes.c_void_p],
                                 ctypes.c_int),
+    "q4_gemm_verify_tiled_noalloc": ([ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_int,
+                                      ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_void_p], ctypes.c_int),
     "q4_gemm_verify_tiled_ws_plan": ([ctypes.c_int, ctypes.c_int64,
                                       ctypes.c_int64, ctypes.POINTER(_Plan)],
                                      ctypes.c_int),
@@ -267,6 +273,24 @@ def q4_gemm_verify_tiled_ws(x, Wt, y, M: int, N: int, K: int, ws=None,
                                         pws, nws, _stream_handle(stream))
     if st != OK:
         raise Q4Error(st, "q4_gemm_verify_tiled_ws")
+
+
+def q4_gemm_verify_tiled_noalloc(x, Wt, y, M: int, N: int, K: int,
+                                 stream=None) -> None:
+    """q4_gemm_verify_tiled_ws with the library's static device scratch in
+    place of a workspace: the call allocates nothing.  Calls that overlap on
+    one GPU race (they share its scratch)."""
+    import torch
+    total = _total_bytes(int(N), int(K), LAYOUT_TILED16)
+    px = _ptr(x, "x", torch.bfloat16, shape=(M, K))
+    pw = _ptr(Wt, "Wt", torch.uint8, numel=total)
+    py = _ptr(y, "y", torch.float32, shape=(M, N))
+    if not (x.device == Wt.device == y.device):
+        raise ValueError("x, Wt and y must be on one device")
+    st = load().q4_gemm_verify_tiled_noalloc(px, pw, py, int(M), int(N),
+                                             int(K), _stream_handle(stream))
+    if st != OK:
+        raise Q4Error(st, "q4_gemm_verify_tiled_noalloc")
 
 
 def q4_verify_sample_workspace(M: int, V: int) -> int:

@@ -402,6 +402,9 @@ extern "C" const char *q4_status_string(int status) {
     case Q4_EOVERFLOW: return "Q4_EOVERFLOW: byte count overflows 64 bits";
     case Q4_EDEVICE: return "Q4_EDEVICE: no HIP device or device is not gfx950";
     case Q4_ELAUNCH: return "Q4_ELAUNCH: kernel launch failed";
+    case Q4_ESCRATCH:
+      return "Q4_ESCRATCH: the call needs more than the library's static "
+             "scratch (Q4_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown q4 status";
   }
 }

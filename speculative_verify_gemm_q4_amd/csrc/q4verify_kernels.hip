@@ -26,7 +26,16 @@
 // which input sits in which MFMA k-slot.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "q4v_internal.h"
+
+// Scratch of q4_gemm_verify_tiled_noalloc: the partial products of parts
+// 1 .. P-1 of a K split, Q4_NOALLOC_SCRATCH_BYTES per device, held by each
+// GPU the library runs on until the process ends.  Host code never passes
+// this name to a kernel (on the host it is only a handle of the symbol): it
+// uses the device address that noalloc_scratch() looks up once per device.
+static __device__ __align__(256) float scratch[Q4_NOALLOC_SCRATCH_BYTES / 4];
 
 namespace q4v {
 namespace {
@@ -1123,6 +1132,59 @@ extern "C" int q4_gemm_verify_tiled_ws(const void *x, const void *W, float *y,
     return q4v::launch_kslice(p, x, W, y, ws, M, n, k, s);
   if (p.kernel == Q4_KERNEL_TILED_RESIDENT)
     return q4v::launch_resident(p, x, W, y, ws, M, n, k, s);
+  return q4_gemm_verify_tiled(x, W, y, M, N, K, stream);
+}
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up with that
+// device current on the first call there and kept per device ordinal.
+int noalloc_scratch(void **out) {
+  static std::atomic<void *> addr[256];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) {
+    (void)hipGetLastError();
+    return Q4_EDEVICE;
+  }
+  void *p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess ||
+        p == nullptr) {
+      (void)hipGetLastError();
+      return Q4_EDEVICE;
+    }
+    addr[dev].store(p, std::memory_order_release);  // the same value if raced
+  }
+  *out = p;
+  return Q4_OK;
+}
+
+}  // namespace
+
+extern "C" int q4_gemm_verify_tiled_noalloc(const void *x, const void *W,
+                                            float *y, int M, int64_t N,
+                                            int64_t K, void *stream) {
+  int st = q4v::check_gemm_args(x, W, y, M, N, K, Q4_MAX_ROWS_TILED);
+  if (st != Q4_OK) return st;
+  st = q4v::check_tiled_shape(N, K);
+  if (st != Q4_OK) return st;
+  const q4_plan p = q4v::plan_gemm_tiled_ws(M, N, K, q4v::device_cus());
+  if (p.grid == 0) return Q4_EINVAL;
+  if (p.workspace_bytes > Q4_NOALLOC_SCRATCH_BYTES) return Q4_ESCRATCH;
+  st = q4v::check_device();
+  if (st != Q4_OK) return st;
+  void *ws = nullptr;
+  if (p.workspace_bytes > 0) {
+    st = noalloc_scratch(&ws);
+    if (st != Q4_OK) return st;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int n = static_cast<int>(N), k = static_cast<int>(K);
+  float *w = static_cast<float *>(ws);
+  if (p.kernel == Q4_KERNEL_TILED_KSLICE)
+    return q4v::launch_kslice(p, x, W, y, w, M, n, k, s);
+  if (p.kernel == Q4_KERNEL_TILED_RESIDENT)
+    return q4v::launch_resident(p, x, W, y, w, M, n, k, s);
   return q4_gemm_verify_tiled(x, W, y, M, N, K, stream);
 }
 

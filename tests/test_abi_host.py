@@ -49,7 +49,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for st in (0, -1, -2, -3, -4, -5):
+    for st in (0, -1, -2, -3, -4, -5, -6):
         s = q4.q4_status_string(st)
         assert s.startswith("Q4_")
     assert q4.q4_status_string(12345) == "unknown q4 status"
@@ -163,6 +163,30 @@ def test_workspace_gemm_argument_errors(lib):
         "workspace_bytes"] == 0
     p = q4.q4_gemm_verify_tiled_ws_plan(3, 5120, 6144)
     assert p["workspace_bytes"] == (p["k_parts"] - 1) * 3 * 5120 * 4
+
+
+def test_noalloc_gemm_argument_errors(lib):
+    """The no-allocation entry point: the tiled call's rules, and a shape
+    whose K split needs more than the static scratch is refused with
+    Q4_ESCRATCH -- all before any device work."""
+    g = lib.q4_gemm_verify_tiled_noalloc
+    X, W, Y = 0x10000, 0x20000, 0x30000
+    assert q4.ESCRATCH == -6 and q4.NOALLOC_SCRATCH_BYTES == 8 << 20
+    assert g(X, W, Y, 0, 5120, 17408, None) == -1
+    assert g(X, W, Y, 33, 5120, 17408, None) == -1
+    assert g(X, W, Y, 16, 5121, 17408, None) == -1   # N % 16
+    assert g(X, W, Y, 16, 5120, 17400, None) == -1   # K % 256
+    assert g(X + 8, W, Y, 16, 5120, 17408, None) == -2
+    assert g(None, W, Y, 16, 5120, 17408, None) == -1
+    # the LM head at 32 rows splits K in two: 30 MiB of partial products
+    assert q4.q4_gemm_verify_tiled_ws_plan(32, 248320, 5120)[
+        "workspace_bytes"] > q4.NOALLOC_SCRATCH_BYTES
+    assert g(X, W, Y, 32, 248320, 5120, None) == -6
+    # every projection of the model fits at 32 rows but that one
+    for N, K in [(34816, 5120), (5120, 17408), (14336, 5120), (5120, 6144),
+                 (16640, 5120)]:
+        assert q4.q4_gemm_verify_tiled_ws_plan(32, N, K)[
+            "workspace_bytes"] <= q4.NOALLOC_SCRATCH_BYTES
 
 
 def test_verify_sample_argument_errors(lib):
