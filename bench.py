@@ -333,6 +333,26 @@ def measure_verify_sample(torch, synth, q4, dev, steps, warmup):
     ms_b, _ = time_raw(torch, both, steps2, max(2, warmup // 8))
     rec["lm_head_us"] = round(ms_g * 1e3, 3)
     rec["lm_head_plus_sample_us"] = round(ms_b * 1e3, 3)
+    # the same step with the epilogue fused into the LM head (the logits
+    # never written): q4_gemm_verify_sample on the same weights and rows
+    fws = torch.empty(q4.q4_gemm_verify_sample_workspace(M, V, K),
+                      dtype=torch.uint8, device=dev)
+    fargs = lambda Wt: [x.data_ptr(), Wt.data_ptr(), M, V, K,
+                        ctypes.byref(prm)] + [
+        t.data_ptr() for t in (inp["draft_tok"], inp["draft_idx"],
+                               inp["draft_q"], inp["u"], inp["v"],
+                               out["top_idx"], out["top_val"],
+                               out["top_prob"], out["greedy"], out["accept"],
+                               out["token"])] + [fws.data_ptr(), fws.numel(),
+                                                 stream]
+    fused = [functools.partial(lib.q4_gemm_verify_sample, *fargs(Wt))
+             for Wt in Wts]
+    if any(fn() != 0 for fn in fused):
+        raise RuntimeError("q4_gemm_verify_sample failed")
+    ms_f, _ = time_raw(torch, fused, steps2, max(2, warmup // 8))
+    rec["fused_us"] = round(ms_f * 1e3, 3)
+    rec["fused_over_lm_head"] = round(ms_f / ms_g, 4)
+    rec["candidates_bytes"] = fws.numel()
     log(f"verify sample: {rec}")
     del Wts
     torch.cuda.empty_cache()

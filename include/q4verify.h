@@ -357,6 +357,41 @@ int q4_verify_sample(const float *logits, int M, int64_t V,
                      int32_t *accept, int32_t *token, void *workspace,
                      uint64_t workspace_bytes, void *stream);
 
+/*
+ * q4_gemm_verify_sample -- the LM head of a verify step with the sampling
+ * epilogue fused in: the logits x W^T of the M verify rows are never
+ * written to memory.  The product runs as in q4_gemm_verify_tiled, and each
+ * workgroup keeps the logits of its run of 16-row tiles on chip and passes
+ * on only the best 32 candidates of each verify row among its columns; a
+ * second kernel merges those lists per row and applies steps 2-4 above
+ * (Splash engine article, section "Exact, up to top-32", and "The decode
+ * step is one command buffer": sampling and the accept test follow the LM
+ * head in the same step; qwen-spec page, Notes: the fused sampling kernel).
+ * The candidates, probabilities and decisions are those of
+ * q4_gemm_verify_tiled followed by q4_verify_sample on the same inputs, bit
+ * for bit (the logits are the same fp32 values).
+ *   x, W_tiled, M (1..Q4_MAX_ROWS), N (the vocabulary, V), K: as
+ *     q4_gemm_verify_tiled; K <= 6144 and N <= 1024 * (compute units).
+ *   prm, draft_tok .. token: as q4_verify_sample with V = N.
+ *   workspace: q4_gemm_verify_sample_workspace bytes, 8-byte aligned.
+ * Two kernels on `stream`; calls sharing a workspace race.
+ * Errors: Q4_EINVAL (sizes, parameters, NULL pointers, small workspace, a
+ * shape outside the rule above), Q4_EALIGN, Q4_EDEVICE, Q4_ELAUNCH.
+ */
+int q4_gemm_verify_sample(const void *x, const void *W_tiled, int M,
+                          int64_t N, int64_t K, const q4_sample_params *prm,
+                          const int32_t *draft_tok, const int32_t *draft_idx,
+                          const float *draft_q, const float *u, const float *v,
+                          int32_t *top_idx, float *top_val, float *top_prob,
+                          int32_t *greedy, int32_t *accept, int32_t *token,
+                          void *workspace, uint64_t workspace_bytes,
+                          void *stream);
+
+/* Workspace bytes of q4_gemm_verify_sample for (M, N, K) on the current
+ * device: M * (workgroups) * 32 keys of 8 bytes.  Errors: Q4_EINVAL. */
+int q4_gemm_verify_sample_workspace(int M, int64_t N, int64_t K,
+                                    uint64_t *bytes);
+
 /* ------------------------------------------------------------------------
  * Gated DeltaNet state commit.
  *

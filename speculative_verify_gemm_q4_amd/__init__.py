@@ -21,6 +21,9 @@ Functions (same names as the C entry points):
 * :func:`q4_verify_sample` (:func:`verify_sample` allocates its outputs) --
   the verify sampling epilogue over the LM head's logits: top-k candidates,
   target probabilities, the accept test and the residual draw.
+* :func:`q4_gemm_verify_sample` (:func:`gemm_verify_sample` allocates its
+  outputs) -- the LM-head product with that epilogue fused in: the logits
+  never leave the chip.
 * :func:`q4_gdn_commit` -- writes a verify pass's accepted tree nodes into
   the Gated DeltaNet recurrent states of every layer (gated delta rule).
 * :func:`q4_gdn_tree_out` -- every tree node's output of one recurrent layer
@@ -40,6 +43,8 @@ from ._lib import (ESCRATCH, ATTN_HEAD_DIM, ATTN_MAX_NODES, ATTN_PAGE, GDN_DK, G
                    q4_gemm_verify_tiled_ws, q4_gemm_verify_tiled_ws_plan,
                    q4_gemm_verify_tiled_noalloc, NOALLOC_SCRATCH_BYTES,
                    q4_gdn_commit, q4_gdn_tree_out, q4_pack_layout, q4_verify_sample,
+                   q4_gemm_verify_sample, q4_gemm_verify_sample_workspace,
+                   gemm_verify_sample,
                    q4_verify_sample_workspace, verify_sample,
                    workspace_for,
                    q4_repack, q4_status_string, q4_stream_copy,
@@ -55,6 +60,8 @@ __all__ = ["ESCRATCH", "ATTN_HEAD_DIM", "ATTN_MAX_NODES", "ATTN_PAGE", "GDN_DK",
            "q4_gemm_verify_tiled_ws", "q4_gemm_verify_tiled_ws_plan",
            "q4_gemm_verify_tiled_noalloc", "NOALLOC_SCRATCH_BYTES",
            "q4_gdn_commit", "q4_gdn_tree_out", "q4_pack_layout", "q4_verify_sample",
+           "q4_gemm_verify_sample", "q4_gemm_verify_sample_workspace",
+           "gemm_verify_sample",
            "q4_verify_sample_workspace", "verify_sample", "workspace_for",
            "q4_repack", "q4_status_string", "q4_stream_copy",
            "q4_stream_read", "q4_tree_attn", "q4_tree_attn_plan", "tree_attn"]

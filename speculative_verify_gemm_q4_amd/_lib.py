@@ -102,6 +102,15 @@ _SIGNATURES = {
                           ctypes.POINTER(_SampleParams)] +
                          [ctypes.c_void_p] * 12 +
                          [ctypes.c_uint64, ctypes.c_void_p], ctypes.c_int),
+    "q4_gemm_verify_sample_workspace": ([ctypes.c_int, ctypes.c_int64,
+                                         ctypes.c_int64,
+                                         ctypes.POINTER(ctypes.c_uint64)],
+                                        ctypes.c_int),
+    "q4_gemm_verify_sample": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                               ctypes.c_int64, ctypes.c_int64,
+                               ctypes.POINTER(_SampleParams)] +
+                              [ctypes.c_void_p] * 12 +
+                              [ctypes.c_uint64, ctypes.c_void_p], ctypes.c_int),
     "q4_gdn_commit_lds_bytes": ([ctypes.c_int, ctypes.POINTER(ctypes.c_int)],
                                 ctypes.c_int),
     "q4_gdn_commit": ([ctypes.c_void_p] + [ctypes.c_int] * 6 +
@@ -359,6 +368,80 @@ def verify_sample(logits, temperature: float, top_p: float, top_k: int,
                      draft_q, u, v, out["top_idx"], out["top_val"],
                      out["top_prob"], out["greedy"], out["accept"],
                      out["token"], ws, stream)
+    return out
+
+
+def q4_gemm_verify_sample_workspace(M: int, N: int, K: int) -> int:
+    """Workspace bytes q4_gemm_verify_sample needs (current device)."""
+    out = ctypes.c_uint64(0)
+    st = load().q4_gemm_verify_sample_workspace(int(M), int(N), int(K),
+                                                ctypes.byref(out))
+    if st != OK:
+        raise Q4Error(st, f"q4_gemm_verify_sample_workspace({M}, {N}, {K})")
+    return out.value
+
+
+def q4_gemm_verify_sample(x, Wt, M: int, N: int, K: int, temperature: float,
+                          top_p: float, top_k: int, draft_tok, draft_idx,
+                          draft_q, u, v, top_idx, top_val, top_prob, greedy,
+                          accept, token, ws, stream=None) -> None:
+    """The LM-head product x[M, K] @ W^T (W repacked by q4_repack, N the
+    vocabulary) with the sampling epilogue fused in: the outputs of
+    q4_verify_sample without writing the logits.  Same argument meanings as
+    q4_verify_sample; ws a uint8 device tensor of at least
+    q4_gemm_verify_sample_workspace(M, N, K) bytes."""
+    import torch
+    k = int(top_k)
+    kd = 0 if draft_idx is None else int(draft_idx.shape[1])
+    total = _total_bytes(int(N), int(K), LAYOUT_TILED16)
+    px = _ptr(x, "x", torch.bfloat16, shape=(M, K))
+    pw = _ptr(Wt, "Wt", torch.uint8, numel=total)
+    pdt = _ptr(draft_tok, "draft_tok", torch.int32, numel=M)
+    pdi = pdq = None
+    if kd:
+        pdi = _ptr(draft_idx, "draft_idx", torch.int32, shape=(M, kd))
+        pdq = _ptr(draft_q, "draft_q", torch.float32, shape=(M, kd))
+    pu = _ptr(u, "u", torch.float32, numel=M)
+    pv = _ptr(v, "v", torch.float32, numel=M)
+    pti = _ptr(top_idx, "top_idx", torch.int32, shape=(M, k))
+    ptv = _ptr(top_val, "top_val", torch.float32, shape=(M, k))
+    ptp = _ptr(top_prob, "top_prob", torch.float32, shape=(M, k))
+    pg = _ptr(greedy, "greedy", torch.int32, numel=M)
+    pa = _ptr(accept, "accept", torch.int32, numel=M)
+    pt = _ptr(token, "token", torch.int32, numel=M)
+    pws = _ptr(ws, "ws", torch.uint8)
+    if not (x.device == Wt.device == ws.device):
+        raise ValueError("x, Wt and ws must be on one device")
+    prm = _SampleParams(float(temperature), float(top_p), k, kd)
+    st = load().q4_gemm_verify_sample(px, pw, int(M), int(N), int(K),
+                                      ctypes.byref(prm), pdt, pdi, pdq, pu, pv,
+                                      pti, ptv, ptp, pg, pa, pt, pws,
+                                      ws.numel(), _stream_handle(stream))
+    if st != OK:
+        raise Q4Error(st, "q4_gemm_verify_sample")
+
+
+def gemm_verify_sample(x, Wt, N: int, K: int, temperature: float,
+                       top_p: float, top_k: int, draft_tok, draft_idx,
+                       draft_q, u, v, stream=None) -> dict:
+    """q4_gemm_verify_sample with its outputs and workspace allocated here
+    (torch tensors on x's device); returns the outputs by name."""
+    import torch
+    M = x.shape[0]
+    dev = x.device
+    out = {"top_idx": torch.empty((M, top_k), dtype=torch.int32, device=dev),
+           "top_val": torch.empty((M, top_k), dtype=torch.float32, device=dev),
+           "top_prob": torch.empty((M, top_k), dtype=torch.float32,
+                                   device=dev),
+           "greedy": torch.empty(M, dtype=torch.int32, device=dev),
+           "accept": torch.empty(M, dtype=torch.int32, device=dev),
+           "token": torch.empty(M, dtype=torch.int32, device=dev)}
+    ws = torch.empty(q4_gemm_verify_sample_workspace(M, N, K),
+                     dtype=torch.uint8, device=dev)
+    q4_gemm_verify_sample(x, Wt, M, N, K, temperature, top_p, top_k,
+                          draft_tok, draft_idx, draft_q, u, v, out["top_idx"],
+                          out["top_val"], out["top_prob"], out["greedy"],
+                          out["accept"], out["token"], ws, stream)
     return out
 
 

@@ -4,6 +4,8 @@
 
 #include <stdint.h>
 
+#include <hip/hip_runtime.h>
+
 #include "q4verify.h"
 
 namespace q4v {
@@ -53,6 +55,36 @@ constexpr int kKsliceMaxRecords = 24;
 constexpr int kKsliceBatchLds = kLdsBytes;
 // LDS of the K-slice kernel's partial sums for W waves.
 constexpr int kslice_batch(int W) { return kKsliceBatchLds / (W * 1024); }
+
+// The verify sampling epilogue's argument rules (sizes, parameters, NULL
+// pointers) and its second kernel: row m merges the S candidate lists of 32
+// keys each at cand[(m * S + s) * 32 ..] and samples (see
+// q4verify_sample.hip).  Shared by q4_verify_sample and the LM-head GEMM with
+// the fused epilogue.
+int check_sample_args(int M, int64_t V, const q4_sample_params *prm,
+                      const int32_t *draft_tok, const int32_t *draft_idx,
+                      const float *draft_q, const float *u, const float *v,
+                      int32_t *top_idx, float *top_val, float *top_prob,
+                      int32_t *greedy, int32_t *accept, int32_t *token);
+int launch_sample_rows(const uint64_t *cand, int M, int S,
+                       const q4_sample_params &p, const int32_t *draft_tok,
+                       const int32_t *draft_idx, const float *draft_q,
+                       const float *u, const float *v, int32_t *top_idx,
+                       float *top_val, float *top_prob, int32_t *greedy,
+                       int32_t *accept, int32_t *token, hipStream_t s);
+// Candidate lists of the fused LM-head epilogue: 32 keys per workgroup and
+// row; a workgroup holds at most kSampleMaxTiles tiles (1024 logits of each
+// row) in LDS.
+constexpr int kSampleTop = 32;
+constexpr int kSampleMaxTiles = 64;
+constexpr int kSampleMaxCols = kSampleMaxTiles * 16;
+constexpr int kSampleLgStride = kSampleMaxCols;  // floats per row in LDS
+constexpr int kSampleLgBytes = Q4_MAX_ROWS * kSampleLgStride * 4;
+// Tiles per reduction batch of the K-slice kernel with the fused epilogue:
+// the rest of the LDS after the logits.
+constexpr int kslice_sample_batch(int W) {
+  return (kLdsBytes - kSampleLgBytes) / (W * 1024);
+}
 
 // Q4_OK when a HIP device is current and it is a gfx950; Q4_EDEVICE
 // otherwise.  The answer is cached per device ordinal.

@@ -29,6 +29,7 @@
 #include <atomic>
 
 #include "q4v_internal.h"
+#include "q4v_select.h"
 
 // Scratch of q4_gemm_verify_tiled_noalloc: the partial products of parts
 // 1 .. P-1 of a K split, Q4_NOALLOC_SCRATCH_BYTES per device, held by each
@@ -783,13 +784,27 @@ __device__ __forceinline__ void kslice_lds_barrier() {
 // than the lag: the first tile's wait then dominates.)  Summation order
 // depends only on (N, K), so results do not depend on M and repeated calls
 // are bitwise equal.
-template <int W, bool kRowLoads>
+//
+// With kSample (the LM head of a verify step) the logits are not stored:
+// each batch's sums go to an LDS array of the workgroup's logits, and after
+// the last batch each wave takes rows m = wave, wave + W, ... and writes the
+// row's best 32 candidate keys among the workgroup's columns to
+// cand[(m * G + g) * 32 ..] (g the workgroup's tile group, G the grid),
+// which launch_sample_rows then merges.  Selection per row: the 32nd best
+// of the 64 lane maxima's upper halves bounds the row's 32nd best key from
+// below, so only keys at or above it survive; the survivors (usually a few
+// more than 32) are packed into the wave's part of the partial-sum area and
+// sorted 64 at a time with bitonic networks, merging into the running list.
+template <int W, bool kRowLoads, bool kSample>
 __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ Wt,
     float *__restrict__ y, float *__restrict__ ws, int M, int N, int K, int P) {
-  constexpr int NB = kslice_batch(W);  // tiles per reduction batch
+  // tiles per reduction batch
+  constexpr int NB = kSample ? kslice_sample_batch(W) : kslice_batch(W);
   static_assert(NB >= 8, "the activation staging areas (8 KB per wave) fit in part");
   __shared__ f32x4 part[NB * W * 64];
+  __shared__ float lg[kSample ? Q4_MAX_ROWS * kSampleLgStride : 1];
+
   const int T = N >> 4;
   const int Q = K >> 8;
   const int lane = threadIdx.x & 63;
@@ -952,10 +967,14 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int m = (l >> 4) * 4 + r;
-              // non-temporal: on the LM head at M = 16 (15.9 MB of y)
-              // plain stores cost 124 us per call against 119
-              if (m < M)
-                __builtin_nontemporal_store(v[r], &out[static_cast<uint64_t>(m) * N + n]);
+              if constexpr (kSample) {
+                if (m < M) lg[m * kSampleLgStride + (n - t0 * 16)] = v[r];
+              } else {
+                // non-temporal: on the LM head at M = 16 (15.9 MB of y)
+                // plain stores cost 124 us per call against 119
+                if (m < M)
+                  __builtin_nontemporal_store(v[r], &out[static_cast<uint64_t>(m) * N + n]);
+              }
             }
           }
           __syncthreads();
@@ -965,21 +984,67 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  if constexpr (kSample) {
+    // The last batch ended with a barrier: the logits are complete and the
+    // partial-sum area is free.  A wave takes rows m and m + W together
+    // (two independent chains), m = wave, wave + 2W, ...  Per row: its keys
+    // in registers (16 per lane); the bound T = the 32nd largest lane
+    // maximum (32 distinct keys reach it, so the row's 32nd best does);
+    // the keys >= T packed into the wave's part of the area; their best 32
+    // ranked into the candidate list.
+    constexpr int kPer = kSampleMaxCols / 64;
+    static_assert(NB * 128 >= kSampleMaxCols, "survivor area");
+    const int ncols = (t1 - t0) * 16;
+    const uint32_t tok0 = static_cast<uint32_t>(t0) * 16u;
+    uint64_t *area = reinterpret_cast<uint64_t *>(part) + wave * (NB * 128);
+    // appends of up to kSampleMaxCols keys, 64 at a time, stay inside the
+    // wave's area (NB * 128 >= kSampleMaxCols slots)
+    uint64_t *dummy = nullptr;
+    uint64_t *c = reinterpret_cast<uint64_t *>(ws);
+    for (int m0 = wave; m0 < M; m0 += 2 * W) {
+      const int m1 = m0 + W;
+      const bool two = m1 < M;  // wave-uniform
+      uint64_t k0[kPer], k1[kPer];
+      uint64_t mx0 = 0, mx1 = 0;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int col = 64 * i + lane;
+        const bool in = col < ncols;
+        k0[i] = in ? make_key(lg[m0 * kSampleLgStride + col], tok0 + col) : 0;
+        k1[i] = in && two ? make_key(lg[m1 * kSampleLgStride + col], tok0 + col) : 0;
+        mx0 = k0[i] > mx0 ? k0[i] : mx0;
+        mx1 = k1[i] > mx1 ? k1[i] : mx1;
+      }
+      const uint64_t T0 = wave_kth_largest(mx0, kSampleTop);
+      const uint64_t T1 = wave_kth_largest(mx1, kSampleTop);
+      // the area holds one row's survivors at a time
+      uint32_t n = 0;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) wave_append(k0[i], k0[i] != 0 && k0[i] >= T0, area, &n, dummy);
+      wave_top32(area, n, c + (static_cast<uint64_t>(m0) * Gt + g) * kSampleTop, lane);
+      if (two) {
+        n = 0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) wave_append(k1[i], k1[i] != 0 && k1[i] >= T1, area, &n, dummy);
+        wave_top32(area, n, c + (static_cast<uint64_t>(m1) * Gt + g) * kSampleTop, lane);
+      }
+    }
+  }
 }
 
-template <int W>
+template <int W, bool kSample = false>
 void launch_kslice_w(const q4_plan &p, const void *x, const void *Wt, float *y,
                      float *ws, int M, int N, int K, hipStream_t stream) {
   const int parts = static_cast<int>(p.k_parts);
   // M >= 8: row-contiguous activation loads through LDS; below that the rows
   // past M are zeros anyway and direct loads save the LDS round trip
   if (M >= 8)
-    hipLaunchKernelGGL((gemm_kslice_kernel<W, true>), dim3(p.grid), dim3(64 * W), 0,
-                       stream, static_cast<const uint16_t *>(x),
+    hipLaunchKernelGGL((gemm_kslice_kernel<W, true, kSample>), dim3(p.grid),
+                       dim3(64 * W), 0, stream, static_cast<const uint16_t *>(x),
                        static_cast<const uint8_t *>(Wt), y, ws, M, N, K, parts);
   else
-    hipLaunchKernelGGL((gemm_kslice_kernel<W, false>), dim3(p.grid), dim3(64 * W), 0,
-                       stream, static_cast<const uint16_t *>(x),
+    hipLaunchKernelGGL((gemm_kslice_kernel<W, false, kSample>), dim3(p.grid),
+                       dim3(64 * W), 0, stream, static_cast<const uint16_t *>(x),
                        static_cast<const uint8_t *>(Wt), y, ws, M, N, K, parts);
 }
 
@@ -1009,6 +1074,30 @@ int launch_kslice(const q4_plan &p, const void *x, const void *Wt, float *y,
   int st = launch_status();
   if (st != Q4_OK || p.k_parts == 1) return st;
   return launch_reduce_parts(y, ws, M, N, static_cast<int>(p.k_parts), stream);
+}
+
+// The K-slice kernel with the fused sampling epilogue: candidate lists to
+// cand instead of logits to y (one part of K, at most kSampleMaxTiles tiles
+// per workgroup; the caller has checked both).
+int launch_kslice_sample(const q4_plan &p, const void *x, const void *Wt,
+                         uint64_t *cand, int M, int N, int K,
+                         hipStream_t stream) {
+  float *c = reinterpret_cast<float *>(cand);
+  switch (p.block / 64) {
+#define Q4V_KSLICE_SAMPLE_CASE(W)                                         \
+  case W:                                                                 \
+    launch_kslice_w<W, true>(p, x, Wt, nullptr, c, M, N, K, stream);      \
+    break;
+    Q4V_KSLICE_SAMPLE_CASE(1) Q4V_KSLICE_SAMPLE_CASE(2)
+    Q4V_KSLICE_SAMPLE_CASE(3) Q4V_KSLICE_SAMPLE_CASE(4)
+    Q4V_KSLICE_SAMPLE_CASE(5) Q4V_KSLICE_SAMPLE_CASE(6)
+    Q4V_KSLICE_SAMPLE_CASE(7) Q4V_KSLICE_SAMPLE_CASE(8)
+    Q4V_KSLICE_SAMPLE_CASE(9) Q4V_KSLICE_SAMPLE_CASE(10)
+    Q4V_KSLICE_SAMPLE_CASE(11) Q4V_KSLICE_SAMPLE_CASE(12)
+#undef Q4V_KSLICE_SAMPLE_CASE
+    default: return Q4_EINVAL;
+  }
+  return launch_status();
 }
 
 template <int W, int RT>
@@ -1133,6 +1222,60 @@ extern "C" int q4_gemm_verify_tiled_ws(const void *x, const void *W, float *y,
   if (p.kernel == Q4_KERNEL_TILED_RESIDENT)
     return q4v::launch_resident(p, x, W, y, ws, M, n, k, s);
   return q4_gemm_verify_tiled(x, W, y, M, N, K, stream);
+}
+
+// The plan of the LM-head GEMM with the fused sampling epilogue: the
+// K-slice kernel in one part of K, at most kSampleMaxTiles tiles per
+// workgroup; grid == 0 when the shape does not qualify.
+static q4_plan plan_gemm_sample(int M, int64_t N, int64_t K) {
+  q4_plan p = q4v::plan_gemm_tiled(M, N, K, q4v::device_cus());
+  if (p.kernel != Q4_KERNEL_TILED_KSLICE || p.k_parts != 1 ||
+      p.row_tiles > static_cast<uint32_t>(q4v::kSampleMaxTiles) || M > Q4_MAX_ROWS)
+    p.grid = 0;
+  return p;
+}
+
+extern "C" int q4_gemm_verify_sample_workspace(int M, int64_t N, int64_t K,
+                                               uint64_t *bytes) {
+  if (bytes == nullptr || M < 1 || M > Q4_MAX_ROWS) return Q4_EINVAL;
+  int st = q4v::check_tiled_shape(N, K);
+  if (st != Q4_OK) return st;
+  const q4_plan p = plan_gemm_sample(M, N, K);
+  if (p.grid == 0) return Q4_EINVAL;
+  *bytes = static_cast<uint64_t>(M) * p.grid * q4v::kSampleTop * 8;
+  return Q4_OK;
+}
+
+extern "C" int q4_gemm_verify_sample(
+    const void *x, const void *W, int M, int64_t N, int64_t K,
+    const q4_sample_params *prm, const int32_t *draft_tok,
+    const int32_t *draft_idx, const float *draft_q, const float *u,
+    const float *v, int32_t *top_idx, float *top_val, float *top_prob,
+    int32_t *greedy, int32_t *accept, int32_t *token, void *workspace,
+    uint64_t workspace_bytes, void *stream) {
+  uint64_t need = 0;
+  int st = q4_gemm_verify_sample_workspace(M, N, K, &need);
+  if (st != Q4_OK) return st;
+  // y is not written: its alignment rule is checked on a stand-in
+  st = q4v::check_gemm_args(x, W, reinterpret_cast<const float *>(W), M, N, K);
+  if (st != Q4_OK) return st;
+  st = q4v::check_sample_args(M, N, prm, draft_tok, draft_idx, draft_q, u, v,
+                              top_idx, top_val, top_prob, greedy, accept,
+                              token);
+  if (st != Q4_OK) return st;
+  if (workspace == nullptr || workspace_bytes < need) return Q4_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 7u) != 0) return Q4_EALIGN;
+  st = q4v::check_device();
+  if (st != Q4_OK) return st;
+  const q4_plan p = plan_gemm_sample(M, N, K);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint64_t *cand = static_cast<uint64_t *>(workspace);
+  st = q4v::launch_kslice_sample(p, x, W, cand, M, static_cast<int>(N),
+                                 static_cast<int>(K), s);
+  if (st != Q4_OK) return st;
+  return q4v::launch_sample_rows(cand, M, static_cast<int>(p.grid), *prm,
+                                 draft_tok, draft_idx, draft_q, u, v, top_idx,
+                                 top_val, top_prob, greedy, accept, token, s);
 }
 
 namespace {

@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 
 #include "q4v_internal.h"
+#include "q4v_select.h"
 
 namespace q4v {
 namespace {
@@ -38,135 +39,6 @@ namespace {
 constexpr int kTopMax = 32;
 constexpr int kDraftMax = 16;
 constexpr int kSliceCols = 16384;  // columns per workgroup of kernel 1
-
-__device__ __forceinline__ uint64_t make_key(float v, uint32_t token) {
-  // -0 and +0 are equal logits: both take the key of +0, so that they tie
-  // and the smaller token index comes first
-  uint32_t b = v == 0.0f ? 0u : __float_as_uint(v);
-  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return (static_cast<uint64_t>(b) << 32) | (0xFFFFFFFFu - token);
-}
-
-__device__ __forceinline__ float key_value(uint64_t key) {
-  uint32_t b = static_cast<uint32_t>(key >> 32);
-  b = (b & 0x80000000u) ? (b & 0x7FFFFFFFu) : ~b;
-  return __uint_as_float(b);
-}
-
-__device__ __forceinline__ uint32_t key_token(uint64_t key) {
-  return 0xFFFFFFFFu - static_cast<uint32_t>(key);
-}
-
-// Cross-lane exchange with the lane l ^ J, without LDS: DPP for J <= 8
-// (quad permutes and row mirrors: J = 4 is a half-row mirror followed by a
-// quad reversal, J = 8 a row mirror followed by a half-row mirror), the
-// gfx950 permlane swaps for J = 16 and 32.
-template <int J>
-__device__ __forceinline__ uint32_t xor_lane(uint32_t v, int lane) {
-  constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kQuadRev = 0x1B;
-  constexpr int kRowMirror = 0x140, kRowHalfMirror = 0x141;
-  if constexpr (J == 1) {
-    return __builtin_amdgcn_update_dpp(0u, v, kQuadXor1, 0xF, 0xF, false);
-  } else if constexpr (J == 2) {
-    return __builtin_amdgcn_update_dpp(0u, v, kQuadXor2, 0xF, 0xF, false);
-  } else if constexpr (J == 4) {
-    const uint32_t t = __builtin_amdgcn_update_dpp(0u, v, kRowHalfMirror, 0xF, 0xF, false);
-    return __builtin_amdgcn_update_dpp(0u, t, kQuadRev, 0xF, 0xF, false);
-  } else if constexpr (J == 8) {
-    const uint32_t t = __builtin_amdgcn_update_dpp(0u, v, kRowMirror, 0xF, 0xF, false);
-    return __builtin_amdgcn_update_dpp(0u, t, kRowHalfMirror, 0xF, 0xF, false);
-  } else if constexpr (J == 16) {
-    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    return (lane & 16) ? r[0] : r[1];
-  } else {
-    static_assert(J == 32, "xor distance");
-    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-    return (lane & 32) ? r[0] : r[1];
-  }
-}
-
-template <int J>
-__device__ __forceinline__ uint64_t xor_lane64(uint64_t v, int lane) {
-  const uint32_t lo = xor_lane<J>(static_cast<uint32_t>(v), lane);
-  const uint32_t hi = xor_lane<J>(static_cast<uint32_t>(v >> 32), lane);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
-// One compare-exchange stage of a bitonic network: lanes keep the larger
-// key when keep_max, else the smaller.
-template <int J>
-__device__ __forceinline__ uint64_t cx_stage(uint64_t key, bool keep_max, int lane) {
-  const uint64_t other = xor_lane64<J>(key, lane);
-  const uint64_t hi = key > other ? key : other;
-  const uint64_t lo = key > other ? other : key;
-  return keep_max ? hi : lo;
-}
-
-template <int J>
-__device__ __forceinline__ uint32_t cx_stage32(uint32_t v, bool keep_max, int lane) {
-  const uint32_t other = xor_lane<J>(v, lane);
-  return keep_max ? (v > other ? v : other) : (v > other ? other : v);
-}
-
-__device__ __forceinline__ uint32_t half_cleaner_desc32(uint32_t v, int lane) {
-  v = cx_stage32<32>(v, (lane & 32) == 0, lane);
-  v = cx_stage32<16>(v, (lane & 16) == 0, lane);
-  v = cx_stage32<8>(v, (lane & 8) == 0, lane);
-  v = cx_stage32<4>(v, (lane & 4) == 0, lane);
-  v = cx_stage32<2>(v, (lane & 2) == 0, lane);
-  v = cx_stage32<1>(v, (lane & 1) == 0, lane);
-  return v;
-}
-
-template <int K, int J>
-__device__ __forceinline__ uint32_t sort_stages32(uint32_t v, int lane) {
-  const bool desc_block = K == 64 || (lane & K) == 0;
-  v = cx_stage32<J>(v, ((lane & J) == 0) == desc_block, lane);
-  if constexpr (J > 1) v = sort_stages32<K, J / 2>(v, lane);
-  return v;
-}
-
-// Sort 64 values (one per lane) descending.
-__device__ __forceinline__ uint32_t sort64_desc32(uint32_t v, int lane) {
-  v = sort_stages32<2, 1>(v, lane);
-  v = sort_stages32<4, 2>(v, lane);
-  v = sort_stages32<8, 4>(v, lane);
-  v = sort_stages32<16, 8>(v, lane);
-  v = sort_stages32<32, 16>(v, lane);
-  v = sort_stages32<64, 32>(v, lane);
-  return v;
-}
-
-// Sort a bitonic sequence of 64 keys (one per lane) descending.
-__device__ __forceinline__ uint64_t half_cleaner_desc(uint64_t key, int lane) {
-  key = cx_stage<32>(key, (lane & 32) == 0, lane);
-  key = cx_stage<16>(key, (lane & 16) == 0, lane);
-  key = cx_stage<8>(key, (lane & 8) == 0, lane);
-  key = cx_stage<4>(key, (lane & 4) == 0, lane);
-  key = cx_stage<2>(key, (lane & 2) == 0, lane);
-  key = cx_stage<1>(key, (lane & 1) == 0, lane);
-  return key;
-}
-
-// Stages j = J, J/2, .., 1 of the merge of blocks of size K.
-template <int K, int J>
-__device__ __forceinline__ uint64_t sort_stages(uint64_t key, int lane) {
-  const bool desc_block = K == 64 || (lane & K) == 0;
-  key = cx_stage<J>(key, ((lane & J) == 0) == desc_block, lane);
-  if constexpr (J > 1) key = sort_stages<K, J / 2>(key, lane);
-  return key;
-}
-
-// Sort 64 keys (one per lane) descending: a bitonic network of 21 stages.
-__device__ __forceinline__ uint64_t sort64_desc(uint64_t key, int lane) {
-  key = sort_stages<2, 1>(key, lane);
-  key = sort_stages<4, 2>(key, lane);
-  key = sort_stages<8, 4>(key, lane);
-  key = sort_stages<16, 8>(key, lane);
-  key = sort_stages<32, 16>(key, lane);
-  key = sort_stages<64, 32>(key, lane);
-  return key;
-}
 
 // Sum over the wave (a fixed butterfly order, so repeatable).
 __device__ __forceinline__ float wave_sum(float x) {
@@ -315,7 +187,13 @@ struct SampleArgs {
   int top_k, draft_k;
 };
 
-// Kernel 2: workgroup m merges row m's S lists, then lane 0 samples.
+// Kernel 2: workgroup m merges row m's S lists, then wave 0 samples.
+// Selection: every thread holds its keys of the row in registers (at most
+// 16: S <= 512 lists of 32).  The 32nd largest of the 1024 thread maxima
+// (each wave sorts its lane maxima, the waves' lists are merged pairwise)
+// bounds the row's 32nd best key from below, as 32 distinct keys reach it;
+// the keys at or above it are packed into LDS wave by wave and wave 0 ranks
+// their best 32.
 __global__ __launch_bounds__(kThreads) void sample_rows_kernel(
     const uint64_t *__restrict__ cand, int S, SampleArgs a,
     const int32_t *__restrict__ draft_tok, const int32_t *__restrict__ draft_idx,
@@ -324,8 +202,12 @@ __global__ __launch_bounds__(kThreads) void sample_rows_kernel(
     float *__restrict__ top_val, float *__restrict__ top_prob,
     int32_t *__restrict__ greedy, int32_t *__restrict__ accept,
     int32_t *__restrict__ token) {
-  __shared__ uint64_t pool[kPoolKeys];
-  __shared__ SelectLds sh;
+  constexpr int kPer = kPoolKeys / kThreads;  // keys per thread, at most
+  __shared__ uint64_t pool[kPoolKeys + kWaves];  // + a dummy slot per wave
+  __shared__ uint64_t lists[kWaves][kTopMax];
+  __shared__ uint64_t best[kTopMax];
+  __shared__ uint32_t wcount[kWaves];
+  __shared__ uint64_t bound;
   __shared__ float val[kTopMax], qc[kTopMax];
   __shared__ int32_t tok[kTopMax];
   __shared__ int32_t sdi[kDraftMax];
@@ -334,12 +216,43 @@ __global__ __launch_bounds__(kThreads) void sample_rows_kernel(
   const int wave = threadIdx.x >> 6;
   const int m = blockIdx.x;
   const uint64_t *rc = cand + static_cast<uint64_t>(m) * S * kTopMax;
-  const int64_t nk = static_cast<int64_t>(S) * kTopMax;
-  auto for_each = [&](auto f) {
-    for (int64_t i = threadIdx.x; i < nk; i += kThreads) f(rc[i]);
-  };
-  const uint64_t list = block_best32(for_each, pool, sh, wave, lane);
+  const int nk = S * kTopMax;
+  uint64_t key[kPer];
+  uint64_t mx = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = i * kThreads + static_cast<int>(threadIdx.x);
+    key[i] = e < nk ? rc[e] : 0;
+    mx = key[i] > mx ? key[i] : mx;
+  }
+  const uint64_t tl = block_merge(sort64_desc(mx, lane), lists, wave, lane);
+  if (threadIdx.x == kTopMax - 1) bound = tl;
+  __syncthreads();
+  const uint64_t T = bound;
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    cnt += static_cast<uint32_t>(
+        __builtin_popcountll(__ballot(key[i] != 0 && key[i] >= T)));
+  if (lane == 0) wcount[wave] = cnt;
+  __syncthreads();
+  uint32_t base = 0, n = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    base += w < wave ? wcount[w] : 0u;
+    n += wcount[w];
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    wave_append(key[i], key[i] != 0 && key[i] >= T, pool, &base,
+                pool + kPoolKeys + wave);
+  __syncthreads();
   if (wave != 0) return;
+  wave_top32(pool, n, best, lane);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint64_t list = lane < kTopMax ? best[lane] : 0;
   const int k = a.top_k;
   // the row's draft list, one entry per lane, then q of every candidate
   if (lane < a.draft_k) {
@@ -419,6 +332,40 @@ int slices_for(int64_t V) {
 }
 
 }  // namespace
+
+int check_sample_args(int M, int64_t V, const q4_sample_params *prm,
+                      const int32_t *draft_tok, const int32_t *draft_idx,
+                      const float *draft_q, const float *u, const float *v,
+                      int32_t *top_idx, float *top_val, float *top_prob,
+                      int32_t *greedy, int32_t *accept, int32_t *token) {
+  if (M < 1 || M > Q4_SAMPLE_MAX_ROWS || V < 1 || V > Q4_SAMPLE_MAX_VOCAB ||
+      prm == nullptr || draft_tok == nullptr || u == nullptr ||
+      v == nullptr || top_idx == nullptr || top_val == nullptr ||
+      top_prob == nullptr || greedy == nullptr || accept == nullptr ||
+      token == nullptr)
+    return Q4_EINVAL;
+  const q4_sample_params p = *prm;
+  if (p.top_k < 1 || p.top_k > kTopMax || p.top_k > V || p.draft_k < 0 ||
+      p.draft_k > kDraftMax || !(p.temperature >= 0.0f) ||
+      !(p.temperature < 3.0e38f) || !(p.top_p > 0.0f && p.top_p <= 1.0f) ||
+      (p.draft_k > 0 && (draft_idx == nullptr || draft_q == nullptr)))
+    return Q4_EINVAL;
+  return Q4_OK;
+}
+
+int launch_sample_rows(const uint64_t *cand, int M, int S,
+                       const q4_sample_params &p, const int32_t *draft_tok,
+                       const int32_t *draft_idx, const float *draft_q,
+                       const float *u, const float *v, int32_t *top_idx,
+                       float *top_val, float *top_prob, int32_t *greedy,
+                       int32_t *accept, int32_t *token, hipStream_t s) {
+  const SampleArgs a{p.temperature, p.top_p, p.top_k, p.draft_k};
+  hipLaunchKernelGGL(sample_rows_kernel, dim3(M), dim3(64 * kWaves), 0, s,
+                     cand, S, a, draft_tok, draft_idx, draft_q, u, v, top_idx,
+                     top_val, top_prob, greedy, accept, token);
+  return hipGetLastError() == hipSuccess ? Q4_OK : Q4_ELAUNCH;
+}
+
 }  // namespace q4v
 
 extern "C" int q4_verify_sample_workspace(int M, int64_t V, uint64_t *bytes) {
@@ -442,19 +389,13 @@ extern "C" int q4_verify_sample(const float *logits, int M, int64_t V,
   uint64_t need = 0;
   int st = q4_verify_sample_workspace(M, V, &need);
   if (st != Q4_OK) return st;
-  if (prm == nullptr || logits == nullptr || draft_tok == nullptr ||
-      u == nullptr || v == nullptr || top_idx == nullptr ||
-      top_val == nullptr || top_prob == nullptr || greedy == nullptr ||
-      accept == nullptr || token == nullptr || workspace == nullptr)
+  st = q4v::check_sample_args(M, V, prm, draft_tok, draft_idx, draft_q, u, v,
+                              top_idx, top_val, top_prob, greedy, accept,
+                              token);
+  if (st != Q4_OK) return st;
+  if (logits == nullptr || workspace == nullptr || workspace_bytes < need)
     return Q4_EINVAL;
   const q4_sample_params p = *prm;
-  if (p.top_k < 1 || p.top_k > q4v::kTopMax || p.top_k > V ||
-      p.draft_k < 0 || p.draft_k > q4v::kDraftMax ||
-      !(p.temperature >= 0.0f) || !(p.temperature < 3.0e38f) ||
-      !(p.top_p > 0.0f && p.top_p <= 1.0f) ||
-      (p.draft_k > 0 && (draft_idx == nullptr || draft_q == nullptr)) ||
-      workspace_bytes < need)
-    return Q4_EINVAL;
   if ((reinterpret_cast<uintptr_t>(logits) & 3u) != 0 ||
       (reinterpret_cast<uintptr_t>(workspace) & 7u) != 0)
     return Q4_EALIGN;
@@ -466,9 +407,7 @@ extern "C" int q4_verify_sample(const float *logits, int M, int64_t V,
   hipLaunchKernelGGL(q4v::topk_slices_kernel, dim3(S, M), dim3(64 * q4v::kWaves),
                      0, s, logits, V, S, cand);
   if (hipGetLastError() != hipSuccess) return Q4_ELAUNCH;
-  const q4v::SampleArgs a{p.temperature, p.top_p, p.top_k, p.draft_k};
-  hipLaunchKernelGGL(q4v::sample_rows_kernel, dim3(M), dim3(64 * q4v::kWaves), 0, s, cand, S,
-                     a, draft_tok, draft_idx, draft_q, u, v, top_idx, top_val,
-                     top_prob, greedy, accept, token);
-  return hipGetLastError() == hipSuccess ? Q4_OK : Q4_ELAUNCH;
+  return q4v::launch_sample_rows(cand, M, S, p, draft_tok, draft_idx, draft_q,
+                                 u, v, top_idx, top_val, top_prob, greedy,
+                                 accept, token, s);
 }

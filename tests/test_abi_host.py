@@ -189,6 +189,30 @@ def test_noalloc_gemm_argument_errors(lib):
             "workspace_bytes"] <= q4.NOALLOC_SCRATCH_BYTES
 
 
+def test_fused_sample_argument_errors(lib):
+    """q4_gemm_verify_sample: shapes outside its rule (K beyond one part
+    of the K-slice kernel, more than 64 tiles per workgroup, M > 16) and a
+    small workspace are rejected before any device work."""
+    ws = q4.q4_gemm_verify_sample_workspace
+    assert ws(16, 248320, 5120) == 16 * 255 * 32 * 8  # 255 workgroups
+    for M, N, K in [(16, 5120, 6400), (17, 5120, 5120), (16, 16 * 64 * 256 + 16, 5120),
+                    (16, 5120, 5000), (0, 5120, 5120)]:
+        with pytest.raises(q4.Q4Error):
+            ws(M, N, K)
+    g = lib.q4_gemm_verify_sample
+    X, W, P = 0x10000, 0x20000, 0x30000
+    prm = q4._lib._SampleParams(1.0, 0.9, 20, 0)
+    outs = [P] * 9
+    need = ws(16, 34816, 5120)
+    assert g(X, W, 16, 34816, 5120, ctypes.byref(prm), P, None, None, P, P,
+             *outs[:6], P, need - 8, None) == -1
+    assert g(X, W, 16, 34816, 5120, ctypes.byref(prm), P, None, None, P, P,
+             *outs[:6], P + 4, need, None) == -2
+    bad = q4._lib._SampleParams(1.0, 0.9, 33, 0)
+    assert g(X, W, 16, 34816, 5120, ctypes.byref(bad), P, None, None, P, P,
+             *outs[:6], P, need, None) == -1
+
+
 def test_verify_sample_argument_errors(lib):
     """Sizes and sampling parameters are rejected before device work."""
     from speculative_verify_gemm_q4_amd._lib import _SampleParams

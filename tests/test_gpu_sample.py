@@ -203,3 +203,64 @@ def test_after_lm_head_gemm(q4):
     torch.cuda.synchronize()
     assert torch.isfinite(y).all()
     run_and_check(q4, y, 1.0, 0.95, 20, 16, 15, "after lm head")
+
+
+# ------------------------------------------------- fused LM-head epilogue
+
+def _fused_case(q4, N, K, M, T, top_p, k, draft_k, seed, zero_x=False):
+    """q4_gemm_verify_sample against the same product written out by
+    q4_gemm_verify_tiled and sampled by q4_verify_sample (itself checked
+    against the oracle on those logits): every output bit for bit."""
+    dev = torch.device("cuda")
+    W = synth.q4_weights(N, K, seed=seed, device=dev)
+    Wt = torch.empty_like(W)
+    q4.q4_repack(W, Wt, N, K)
+    x = synth.activations(M, K, seed=seed, stream=1, device=dev)
+    if zero_x:
+        x.zero_()
+    logits = torch.empty((M, N), dtype=torch.float32, device=dev)
+    q4.q4_gemm_verify_tiled(x, Wt, logits, M, N, K)
+    torch.cuda.synchronize()
+    g, _ = run_and_check(q4, logits, T, top_p, k, draft_k, seed,
+                         f"unfused N={N} K={K} M={M}")
+    tok, di, dq, u, v = draft_inputs(logits.cpu().numpy(), k, draft_k, seed)
+    t = lambda a: torch.from_numpy(a).to(dev)
+    _say(f"case fused sample N={N} K={K} M={M} T={T} k={k}")
+    f = q4.gemm_verify_sample(x, Wt, N, K, T, top_p, k, t(tok),
+                              t(di) if draft_k else None,
+                              t(dq) if draft_k else None, t(u), t(v))
+    torch.cuda.synchronize()
+    for name, arr in g.items():
+        got = f[name].cpu().numpy()
+        assert np.array_equal(got.view(np.uint32) if got.dtype == np.float32
+                              else got,
+                              arr.view(np.uint32) if arr.dtype == np.float32
+                              else arr), (name, N, K, M)
+    return g
+
+
+def test_fused_lm_head(q4):
+    """The LM head of the 27B model (248320 x 5120) at 16 verify rows with
+    top-20, top_p 0.95 and 16 draft candidates: the configuration the bench
+    times."""
+    g = _fused_case(q4, 248320, 5120, 16, 1.0, 0.95, 20, 16, 70)
+    assert 0 < g["accept"].sum() < 16
+
+
+@pytest.mark.parametrize("N,K,M,T,top_p,k,draft_k", [
+    (50000, 2048, 1, 1.0, 0.9, 32, 8),
+    (50000, 2048, 5, 0.7, 1.0, 16, 16),
+    (16384, 6144, 8, 1.3, 0.8, 32, 4),     # 12 waves, row-staged activations
+    (640, 512, 16, 1.0, 1.0, 32, 2),       # 16 columns per workgroup
+    (48, 1024, 3, 0.0, 1.0, 5, 3),         # greedy, 3 tiles
+])
+def test_fused_shapes(q4, N, K, M, T, top_p, k, draft_k):
+    _fused_case(q4, N, K, M, T, top_p, k, draft_k, 71)
+
+
+def test_fused_all_logits_equal(q4):
+    """Zero activations make every logit 0: every column of a workgroup
+    passes the threshold (the survivor lists run past 64 keys and are merged
+    in chunks), and ties go to the smaller token index."""
+    g = _fused_case(q4, 50000, 1024, 4, 1.0, 1.0, 32, 4, 72, zero_x=True)
+    assert (g["top_idx"] == np.arange(32)[None, :]).all()
