@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 1u
+#define Q4_ABI_VERSION 2u
 #define Q4_GROUP 64     /* inputs per scale/bias group                     */
 #define Q4_MAX_ROWS 16  /* largest activation block M of q4_gemm_verify     */
 #define Q4_MAX_ROWS_TILED 32 /* of the tiled calls: two MFMA row tiles    */
@@ -216,6 +216,10 @@ typedef struct {
   uint32_t m_tiles;      /* 16-row MFMA tiles of the activation block (1 for
                             M <= 16, 2 for M <= 32)                         */
   uint64_t workspace_bytes; /* device workspace the call needs (0: none)    */
+  uint32_t k_seq_parts;  /* parts of K one workgroup takes one after another,
+                            its tiles' running sums kept on chip (1: K in
+                            one part)                                       */
+  uint32_t layout_id;    /* Q4_LAYOUT_* the plan reads                      */
 } q4_plan;
 
 #define Q4_KERNEL_PLANAR 0u          /* q4_gemm_verify                       */

@@ -58,7 +58,9 @@ class _Plan(ctypes.Structure):
                 ("k_splits", ctypes.c_uint32), ("lookahead", ctypes.c_uint32),
                 ("kernel", ctypes.c_uint32), ("lds_bytes", ctypes.c_uint32),
                 ("k_parts", ctypes.c_uint32), ("m_tiles", ctypes.c_uint32),
-                ("workspace_bytes", ctypes.c_uint64)]
+                ("workspace_bytes", ctypes.c_uint64),
+                ("k_seq_parts", ctypes.c_uint32),
+                ("layout_id", ctypes.c_uint32)]
 
 
 _lib = None

@@ -24,8 +24,15 @@ int check_tiled_shape(int64_t N, int64_t K);
 // Launch plans of the two GEMM kernels (see q4_gemm_verify_plan); the shape
 // has already been checked.
 // `cus` is the compute-unit count of the device the plan is for.
-q4_plan plan_gemm_planar(int M, int64_t N, int64_t K);
+q4_plan plan_gemm_planar(int M, int64_t N, int64_t K, int cus);
 q4_plan plan_gemm_tiled(int M, int64_t N, int64_t K, int cus);
+// Plan of the K-slice kernel for `parts` groups of workgroups, each taking
+// `seq` parts of K in turn, on weights in Q4_LAYOUT_* `layout`; false when
+// the shape does not fit it.
+bool plan_kslice(int M, int64_t N, int64_t K, int cus, int parts, int seq,
+                 uint32_t layout, q4_plan *out);
+// Parts of K a K-slice workgroup takes in turn when nothing else splits K.
+int seq_parts_for(int64_t K);
 // The plan of the workspace path (q4_gemm_verify_tiled_ws).
 q4_plan plan_gemm_tiled_ws(int M, int64_t N, int64_t K, int cus);
 
@@ -52,9 +59,19 @@ constexpr int kResidentStages = 2;
 // (K <= 6144); tiles per reduction batch fill the LDS with the waves'
 // partial sums (16 x 10 x 1 KiB at K = 5120).
 constexpr int kKsliceMaxRecords = 24;
-constexpr int kKsliceBatchLds = kLdsBytes;
+// With K beyond kKsliceMaxRecords records and no workspace, a workgroup
+// takes the parts of K one after another and keeps each of its tiles'
+// running sums in LDS: at most kInMaxTiles tiles per workgroup then.
+constexpr int kInMaxTiles = 16;
+constexpr int kKsliceBatchLds = kLdsBytes - kInMaxTiles * 1024;
 // LDS of the K-slice kernel's partial sums for W waves.
 constexpr int kslice_batch(int W) { return kKsliceBatchLds / (W * 1024); }
+// On the planar layout each wave also stages its two records' codes of one
+// tile in LDS (4 KiB per wave).
+constexpr int kPlanarCodeLds = 4096;
+constexpr int kslice_planar_batch(int W) {
+  return (kKsliceBatchLds - W * kPlanarCodeLds) / (W * 1024);
+}
 
 // The verify sampling epilogue's argument rules (sizes, parameters, NULL
 // pointers) and its second kernel: row m merges the S candidate lists of 32

@@ -88,8 +88,13 @@ int check_tiled_shape(int64_t N, int64_t K) {
   return Q4_OK;
 }
 
-q4_plan plan_gemm_planar(int M, int64_t N, int64_t K) {
-  (void)M;
+q4_plan plan_gemm_planar(int M, int64_t N, int64_t K, int cus) {
+  {
+    // the K-slice kernel on the planar codes (K % 256 == 0, up to 16 rows)
+    q4_plan p;
+    if (plan_kslice(M, N, K, cus, 1, seq_parts_for(K), Q4_LAYOUT_PLANAR, &p))
+      return p;
+  }
   // Waves per tile splitting K so that the grid holds enough waves (about 16
   // per CU on 256 CUs) to keep the weight stream in flight, with at least
   // four groups per wave; large-N shapes put several tiles in a workgroup.
@@ -108,6 +113,8 @@ q4_plan plan_gemm_planar(int M, int64_t N, int64_t K) {
   p.lookahead = 4;
   p.kernel = Q4_KERNEL_PLANAR;
   p.k_parts = 1;
+  p.k_seq_parts = 1;
+  p.layout_id = Q4_LAYOUT_PLANAR;
   p.m_tiles = 1;
   p.lds_bytes = ksw > 1 ? static_cast<uint32_t>(ksw * ntw * 64 * 16) : 0;
   return p;
@@ -142,6 +149,8 @@ bool plan_resident(int M, int64_t N, int64_t K, int cus, int parts,
   p.k_splits = 1;
   p.lookahead = kRecordGroups * (kResidentStages - 1);
   p.kernel = Q4_KERNEL_TILED_RESIDENT;
+  p.k_seq_parts = 1;
+  p.layout_id = Q4_LAYOUT_TILED16;
   p.lds_bytes = kLdsBytes;
   p.k_parts = static_cast<uint32_t>(parts);
   p.m_tiles = static_cast<uint32_t>(m_tiles);
@@ -152,16 +161,24 @@ bool plan_resident(int M, int64_t N, int64_t K, int cus, int parts,
 }
 
 // Plan of the K-slice kernel (M <= 16): ceil(Q_p / 2) waves for parts of
-// Q_p <= 24 records.  With one part (K <= 6144) one workgroup per CU owns a
-// run of tiles; with P parts (a workspace for parts 1 .. P-1) the grid is
-// P groups of min(tiles, CUs / P) workgroups.
-bool plan_kslice(int M, int64_t N, int64_t K, int cus, int parts, q4_plan *out) {
-  const int64_t tiles = N / kTileRows;
-  const int64_t records = K / (kRecordGroups * Q4_GROUP);
-  const int64_t part_records = (records + parts - 1) / parts;
-  if (M > Q4_MAX_ROWS || parts < 1 || part_records > kKsliceMaxRecords ||
-      parts > cus)
+// Q_p <= 24 records.  K is cut into P * seq parts: P groups of workgroups
+// take one part each (parts 1 .. P-1 write a workspace), and within a group
+// every workgroup takes its seq parts one after another, keeping its tiles'
+// running sums on chip (then at most kInMaxTiles tiles per workgroup).  With
+// one part group one workgroup per CU owns a run of tiles; with P groups the
+// grid is P groups of min(tiles, CUs / P) workgroups.  layout is the
+// weights' Q4_LAYOUT_*: the planar layout takes any N (the last tile's rows
+// past N read zeros) and K % 256 == 0.
+bool plan_kslice(int M, int64_t N, int64_t K, int cus, int parts, int seq,
+                 uint32_t layout, q4_plan *out) {
+  if (M > Q4_MAX_ROWS || parts < 1 || seq < 1 || parts > cus || N < 1 ||
+      K < kRecordGroups * Q4_GROUP || K % (kRecordGroups * Q4_GROUP) != 0)
     return false;
+  const int64_t tiles = (N + kTileRows - 1) / kTileRows;
+  const int64_t records = K / (kRecordGroups * Q4_GROUP);
+  const int64_t nparts = static_cast<int64_t>(parts) * seq;
+  const int64_t part_records = (records + nparts - 1) / nparts;
+  if (part_records > kKsliceMaxRecords || nparts > records) return false;
   const int64_t per_part_cus = cus / parts;
   const int64_t g0 = tiles < per_part_cus ? tiles : per_part_cus;
   const int64_t per = (tiles + g0 - 1) / g0;
@@ -170,7 +187,12 @@ bool plan_kslice(int M, int64_t N, int64_t K, int cus, int parts, q4_plan *out) 
   // 242 x 9 tiles instead of 256 x 8 or 9, 20.9 against 21.9 us at M = 16
   // on MI355X); with fewer, every CU's share matters more.
   const int64_t g = per >= 3 ? (tiles + per - 1) / per : g0;
-  if (per * records * kRecordBytes >= 0x7FFFFFF0LL) return false;
+  if (seq > 1 && per > kInMaxTiles) return false;
+  // 32-bit buffer offsets over a workgroup's weights
+  const int64_t span = layout == Q4_LAYOUT_PLANAR
+                           ? per * kTileRows * (K / 2)
+                           : per * records * kRecordBytes;
+  if (span >= 0x7FFFFFF0LL) return false;
   const int waves = static_cast<int>((part_records + 1) / 2);
   q4_plan p;
   std::memset(&p, 0, sizeof p);
@@ -181,13 +203,26 @@ bool plan_kslice(int M, int64_t N, int64_t K, int cus, int parts, q4_plan *out) 
   p.k_splits = static_cast<uint32_t>(waves);
   p.lookahead = kRecordGroups * 2;
   p.kernel = Q4_KERNEL_TILED_KSLICE;
-  p.lds_bytes = static_cast<uint32_t>(kslice_batch(waves) * waves * 1024);
+  const bool planar = layout == Q4_LAYOUT_PLANAR;
+  p.lds_bytes = static_cast<uint32_t>(
+      (planar ? kslice_planar_batch(waves) : kslice_batch(waves)) * waves * 1024 +
+      (planar ? waves * kPlanarCodeLds : 0) + (seq > 1 ? kInMaxTiles * 1024 : 0));
   p.k_parts = static_cast<uint32_t>(parts);
+  p.k_seq_parts = static_cast<uint32_t>(seq);
   p.m_tiles = 1;
+  p.layout_id = layout;
   p.workspace_bytes = static_cast<uint64_t>(parts - 1) *
                       static_cast<uint64_t>(M) * static_cast<uint64_t>(N) * 4;
   *out = p;
   return true;
+}
+
+// Parts of K taken one after another by each workgroup, for the K-slice
+// kernel without a workspace.
+int seq_parts_for(int64_t K) {
+  const int64_t records = K / (kRecordGroups * Q4_GROUP);
+  const int64_t s = (records + kKsliceMaxRecords - 1) / kKsliceMaxRecords;
+  return s < 1 ? 1 : s > 0x7FFFFFFF ? 0x7FFFFFFF : static_cast<int>(s);
 }
 
 q4_plan plan_gemm_tiled_ws(int M, int64_t N, int64_t K, int cus) {
@@ -207,7 +242,8 @@ q4_plan plan_gemm_tiled_ws(int M, int64_t N, int64_t K, int cus) {
     int64_t parts = 4;
     while (parts * kKsliceMaxRecords < records) parts *= 2;
     q4_plan p;
-    if (plan_kslice(M, N, K, cus, static_cast<int>(parts), &p)) return p;
+    if (plan_kslice(M, N, K, cus, static_cast<int>(parts), 1, Q4_LAYOUT_TILED16, &p))
+      return p;
     return plan_gemm_tiled(M, N, K, cus);
   }
   const int64_t per_part = kResidentMaxRecords / m_tiles;
@@ -228,12 +264,14 @@ q4_plan plan_gemm_tiled_ws(int M, int64_t N, int64_t K, int cus) {
 q4_plan plan_gemm_tiled(int M, int64_t N, int64_t K, int cus) {
   const int64_t tiles = N / kTileRows;
   {
-    // Up to 16 rows and 24 records per tile: each wave keeps its slice of
-    // K of the activations in registers (measured on MI355X: gate+up, the
-    // LM head and the GDN in-projection faster than with the activations in
-    // LDS, attention's in-projection at M = 16 even).
+    // Up to 16 rows: each wave keeps its slice of K of the activations in
+    // registers (measured on MI355X: gate+up, the LM head and the GDN
+    // in-projection faster than with the activations in LDS, attention's
+    // in-projection at M = 16 even); beyond 24 records per tile the
+    // workgroups take the parts of K one after another.
     q4_plan p;
-    if (plan_kslice(M, N, K, cus, 1, &p)) return p;
+    if (plan_kslice(M, N, K, cus, 1, seq_parts_for(K), Q4_LAYOUT_TILED16, &p))
+      return p;
   }
   if (K <= kResidentMaxK) {
     // Activations resident in LDS: one workgroup per CU (the LDS admits no
@@ -267,6 +305,8 @@ q4_plan plan_gemm_tiled(int M, int64_t N, int64_t K, int cus) {
   p.grid = static_cast<uint32_t>(sets);
   p.lookahead = kRecordGroups;
   p.kernel = Q4_KERNEL_TILED_STREAM;
+  p.k_seq_parts = 1;
+  p.layout_id = Q4_LAYOUT_TILED16;
   p.k_parts = 1;
   p.m_tiles = 1;
   p.lds_bytes = ksw > 1 ? static_cast<uint32_t>(ksw * tnt * 64 * 16) : 0;
@@ -369,7 +409,7 @@ extern "C" int q4_gemm_verify_plan(int M, int64_t N, int64_t K,
     if (M > Q4_MAX_ROWS) return Q4_EINVAL;
     const int st = q4v::check_matrix_shape(N, K);
     if (st != Q4_OK) return st;
-    *out = q4v::plan_gemm_planar(M, N, K);
+    *out = q4v::plan_gemm_planar(M, N, K, q4v::device_cus());
     return Q4_OK;
   }
   if (layout_id == Q4_LAYOUT_TILED16) {

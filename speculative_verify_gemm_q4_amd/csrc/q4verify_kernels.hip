@@ -795,18 +795,29 @@ __device__ __forceinline__ void kslice_lds_barrier() {
 // below, so only keys at or above it survive; the survivors (usually a few
 // more than 32) are packed into the wave's part of the partial-sum area and
 // sorted 64 at a time with bitonic networks, merging into the running list.
-template <int W, bool kRowLoads, bool kSample>
+template <int W, bool kRowLoads, bool kSample, bool kPlanar, bool kSeq>
 __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ Wt,
-    float *__restrict__ y, float *__restrict__ ws, int M, int N, int K, int P) {
+    float *__restrict__ y, float *__restrict__ ws, int M, int N, int K, int P,
+    int Pin_) {
+  // parts of K taken in turn: a run-time count only in the kSeq kernels
+  const int Pin = kSeq ? Pin_ : 1;
   // tiles per reduction batch
-  constexpr int NB = kSample ? kslice_sample_batch(W) : kslice_batch(W);
+  constexpr int NB = kSample   ? kslice_sample_batch(W)
+                     : kPlanar ? kslice_planar_batch(W)
+                               : kslice_batch(W);
   static_assert(NB >= 8, "the activation staging areas (8 KB per wave) fit in part");
   __shared__ f32x4 part[NB * W * 64];
+  // planar: each wave's two records of codes of the next tile (16 rows x
+  // 128 B each), written by the loads themselves
+  __shared__ u32x4 ccode[kPlanar ? W * (kPlanarCodeLds / 16) : 1];
   __shared__ float lg[kSample ? Q4_MAX_ROWS * kSampleLgStride : 1];
+  // running sums of the workgroup's tiles over parts of K taken in turn
+  __shared__ f32x4 tacc[kSeq ? kInMaxTiles * 64 : 1];
 
-  const int T = N >> 4;
+  const int T = (N + 15) >> 4;
   const int Q = K >> 8;
+  const int G8 = K >> 6;  // groups per row
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 15;
@@ -814,7 +825,8 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
   const int G = static_cast<int>(gridDim.x);
   const int b = static_cast<int>(blockIdx.x);
   const int rank = (b & 7) * (G >> 3) + min(b & 7, G & 7) + (b >> 3);
-  // rank -> part p of K (records [qa, qa + nrec)) and tile group g
+  // rank -> part group pk of K and tile group g; part group pk holds parts
+  // pk * Pin .. pk * Pin + Pin - 1, taken one after another
   const int Gt = G / P;
   const int pk = rank / Gt;
   const int g = rank - pk * Gt;
@@ -822,30 +834,78 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
   const int t1 = static_cast<int>(static_cast<int64_t>(T) * (g + 1) / Gt);
   __builtin_assume(t1 > t0);  // a part has at most one workgroup per tile
   const bool in_step = t1 - t0 >= 8;
-  const int qa = Q * pk / P;
-  const int nrec = Q * (pk + 1) / P - qa;
-  const int q0 = qa + 2 * wave;
-  const int nq = min(max(nrec - 2 * wave, 0), 2);  // 0, 1 or 2
+  const int Ptot = P * Pin;
   float *const out = pk == 0 ? y : ws + static_cast<uint64_t>(pk - 1) * M * N;
 
-  // weights of the workgroup's tiles; a record past them (or past the
-  // wave's slice) gets an offset past the resource and reads zeros
+  // Weights of the workgroup's tiles (all of K); a record past them or
+  // past the wave's slice gets an offset past the resource and reads zeros.
+  // Tiled: record (tile, q) at (tile Q + q) * 2304 bytes.  Planar: the
+  // codes of the tiles' rows (rows past N fall past the resource), their
+  // scales and their biases, three resources.
+  const int rows = min(N - 16 * t0, 16 * (t1 - t0));
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t *>(Wt + static_cast<uint64_t>(t0) * Q * kRecordBytes), 0,
-      (t1 - t0) * Q * kRecordBytes, kBufferWord3);
+      const_cast<uint8_t *>(
+          kPlanar ? Wt + static_cast<uint64_t>(t0) * 16 * (K >> 1)
+                  : Wt + static_cast<uint64_t>(t0) * Q * kRecordBytes),
+      0, kPlanar ? rows * (K >> 1) : (t1 - t0) * Q * kRecordBytes, kBufferWord3);
+  const uint64_t NK = static_cast<uint64_t>(N) * static_cast<uint64_t>(K);
+  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(Wt + NK / 2 + static_cast<uint64_t>(t0) * 16 * G8 * 2),
+      0, kPlanar ? rows * G8 * 2 : 0, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(Wt + NK / 2 + NK / 32 +
+                            static_cast<uint64_t>(t0) * 16 * G8 * 2),
+      0, kPlanar ? rows * G8 * 2 : 0, kBufferWord3);
+  // Per stage, two records of one tile: for each, the codes of groups 0-1
+  // (c0) and 2-3 (c1), 16 bytes per lane, and the (scale, bias) words;
+  // tiled: sb[qq] word gi = scale | bias << 16 of group gi; planar: sc and
+  // bi hold the 8 groups' scales and biases (bf16 pairs) of both records.
   struct Stage {
     u32x4 c0[2], c1[2], sb[2];
   };
-  int tl = 0;  // next tile to load, counted from t0
+  int q0 = 0, nq = 0;  // the wave's records in the current part
+  int tl = 0;          // next tile to load, counted from t0
+  // Planar codes go straight from memory to the wave's LDS area: load i of
+  // record qq brings rows 8i .. 8i+7 of the tile, 128 B (the record's 256
+  // codes) each, lane l chunk (l & 7) ^ (l >> 3) of row 8i + (l >> 3), so
+  // every load covers whole 128-byte runs.  Lane l lands at l * 16, which
+  // puts chunk c of row r at r * 128 + (c ^ (r & 7)) * 16.
+  char *const cwave = reinterpret_cast<char *>(ccode) + wave * kPlanarCodeLds;
   auto load = [&](Stage &st) {
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) {
-      const uint32_t o = tl < t1 - t0 && qq < nq
-                             ? static_cast<uint32_t>((tl * Q + q0 + qq) * kRecordBytes)
+      const bool ok = tl < t1 - t0 && qq < nq;
+      if constexpr (kPlanar) {
+        // none past the last tile: the area then belongs to the next part
+        if (tl < t1 - t0) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int r = 8 * i + (lane >> 3);
+            const int c = (lane & 7) ^ (lane >> 3);
+            const uint32_t o = ok ? static_cast<uint32_t>((tl * 16 + r) * (K >> 1) +
+                                                          (q0 + qq) * 128 + c * 16)
+                                  : 0x7FFFFFF0u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                wr, (__attribute__((address_space(3))) void *)(cwave + qq * 2048 + i * 1024),
+                16, o, 0, 0, kNonTemporal);
+          }
+        }
+      } else {
+        const uint32_t o = ok ? static_cast<uint32_t>((tl * Q + q0 + qq) * kRecordBytes)
+                              : 0x7FFFFFF0u;
+        st.c0[qq] = buffer_load16<kNonTemporal>(wr, lane * 16, o);
+        st.c1[qq] = buffer_load16<kNonTemporal>(wr, 1024 + lane * 16, o);
+        st.sb[qq] = buffer_load16<kNonTemporal>(wr, 2048 + j * 16, o);
+      }
+    }
+    if constexpr (kPlanar) {
+      // 8 groups of row j from record q0: scales, then biases (a second
+      // record past the slice contributes only zero activations)
+      const uint32_t o = tl < t1 - t0 && nq > 0
+                             ? static_cast<uint32_t>(((tl * 16 + j) * G8 + 4 * q0) * 2)
                              : 0x7FFFFFF0u;
-      st.c0[qq] = buffer_load16<kNonTemporal>(wr, lane * 16, o);
-      st.c1[qq] = buffer_load16<kNonTemporal>(wr, 1024 + lane * 16, o);
-      st.sb[qq] = buffer_load16<kNonTemporal>(wr, 2048 + j * 16, o);
+      st.sb[0] = buffer_load16<kNonTemporal>(sr, o, 0);
+      st.sb[1] = buffer_load16<kNonTemporal>(br, o, 0);
     }
     ++tl;
   };
@@ -857,70 +917,18 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
       kBufferWord3);
   const u32x4 neg = {kNeg128Pair, kNeg128Pair, kNeg128Pair, kNeg128Pair};
   const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
+  // Activation operand (gi, h) of lane (j, kb): eight inputs of row j.
+  // Tiled: inputs 64 gi + 16 kb + 8 h .. +7 in order (the repack splits each
+  // code word into even and odd inputs).  Planar: lane (j, kb) reads words
+  // 2 kb and 2 kb + 1 of each group of row j from LDS, so operand h meets
+  // inputs 64 gi + 8 (2 kb + h) .. +7, permuted to the pairs (0,4) (1,5)
+  // (2,6) (3,7) in which unpack_codes yields a word's codes.  (The inputs of
+  // an operand slot depend on kb alone: the MFMA pairs slot kb of every row
+  // of x with slot kb of every row of W.)
+  const int w_h0 = 2 * kb;
+  const int w_h1 = 2 * kb + 1;
   u32x4 xa[2][4][2];
   f32x4 xn[2][4];
-  if constexpr (kRowLoads) {
-    // Row-contiguous loads (load i of record qq brings rows 2i and 2i + 1,
-    // 512 B each), then through LDS into the operand layout.  Lane l of
-    // load i holds chunk c = l & 31 (inputs 8c .. 8c+7) of row
-    // r = 2i + (l >> 5); it is stored at row r, chunk c ^ (r & 7) of the
-    // wave's 8 KB area, and lane (j, kb) reads chunk 8 gi + 2 kb + h of row
-    // j for operand (gi, h): the XOR keeps both sides free of bank
-    // conflicts.
-    u32x4 xrow[2][8];
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t r = 2 * i + (lane >> 5);
-        const uint32_t off = (r * K + 256 * (q0 + qq) + 8 * (lane & 31)) * 2;
-        xrow[qq][i] = buffer_load16<0>(xr, off, qq < nq ? 0u : 0x7FFFFFF0u);
-      }
-    load(st[0]);
-    char *area = reinterpret_cast<char *>(part) + wave * 8192;
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = 2 * i + (lane >> 5);
-        const int c = (lane & 31) ^ (r & 7);
-        *reinterpret_cast<u32x4 *>(area + r * 512 + c * 16) = xrow[qq][i];
-      }
-#pragma unroll
-      for (int gi = 0; gi < 4; ++gi)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int c = (8 * gi + 2 * kb + h) ^ (j & 7);
-          xa[qq][gi][h] = *reinterpret_cast<const u32x4 *>(area + j * 512 + c * 16);
-        }
-    }
-    // the areas alias the partial sums: every wave has its operands in
-    // registers before any wave writes a partial sum
-    kslice_lds_barrier();
-  } else {
-    // direct loads in the operand layout: lane (j, kb), operand (gi, h)
-    // reads inputs 64 gi + 16 kb + 8 h .. +7 of row j
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq)
-#pragma unroll
-      for (int gi = 0; gi < 4; ++gi)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t off = (static_cast<uint32_t>(j) * K + 256 * (q0 + qq) +
-                                64 * gi + 16 * kb + 8 * h) * 2;
-          xa[qq][gi][h] = buffer_load16<0>(xr, off, qq < nq ? 0u : 0x7FFFFFF0u);
-        }
-    load(st[0]);
-    __builtin_amdgcn_sched_barrier(0);  // every load issued before the seeds
-  }
-#pragma unroll
-  for (int qq = 0; qq < 2; ++qq)
-#pragma unroll
-    for (int gi = 0; gi < 4; ++gi) {
-      const f32x4 s = mfma16x16x32(xa[qq][gi][0], neg, fzero);
-      xn[qq][gi] = mfma16x16x32(xa[qq][gi][1], neg, s);
-    }
-
   const UnpackConsts uc = unpack_consts();
   auto compute = [&](const Stage &s, f32x4 &acc) {
 #pragma unroll
@@ -930,9 +938,17 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
         const u32x4 cw = gi < 2 ? s.c0[qq] : s.c1[qq];
         const u32x4 b0 = unpack_codes((gi & 1) ? cw.z : cw.x, uc);
         const u32x4 b1 = unpack_codes((gi & 1) ? cw.w : cw.y, uc);
-        const uint32_t sbw = s.sb[qq][gi];
-        const float sc = __uint_as_float(sbw << 16);
-        const float bn = __uint_as_float(sbw & 0xFFFF0000u) * kMinusInv128;
+        float sc, bn;
+        if constexpr (kPlanar) {
+          const int e = 4 * qq + gi;  // group of the wave's pair of records
+          const uint32_t sw = s.sb[0][e >> 1], bw = s.sb[1][e >> 1];
+          sc = __uint_as_float((e & 1) ? (sw & 0xFFFF0000u) : (sw << 16));
+          bn = __uint_as_float((e & 1) ? (bw & 0xFFFF0000u) : (bw << 16)) * kMinusInv128;
+        } else {
+          const uint32_t sbw = s.sb[qq][gi];
+          sc = __uint_as_float(sbw << 16);
+          bn = __uint_as_float(sbw & 0xFFFF0000u) * kMinusInv128;
+        }
         f32x4 tq = mfma16x16x32(xa[qq][gi][0], b0, xn[qq][gi]);
         tq = mfma16x16x32(xa[qq][gi][1], b1, tq);
 #pragma unroll
@@ -943,45 +959,165 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
       }
     }
   };
+  // Planar: once the tile's codes have landed in the wave's LDS area, each
+  // lane takes words 2 kb, 2 kb + 1 of groups 0-1 (c0: .x .y, .z .w) and
+  // 2-3 (c1) of both records of row j.  The area is free again once the
+  // reads have returned.
+  auto fetch = [&](Stage &s) {
+    if constexpr (kPlanar) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the loads have landed
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c = (2 * g + (kb >> 1)) ^ (j & 7);
+          const uint2 v = *reinterpret_cast<const uint2 *>(
+              cwave + qq * 2048 + j * 128 + c * 16 + (kb & 1) * 8);
+          u32x4 &d = g < 2 ? s.c0[qq] : s.c1[qq];
+          if (g & 1) {
+            d.z = v.x;
+            d.w = v.y;
+          } else {
+            d.x = v.x;
+            d.y = v.y;
+          }
+        }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the area is free
+      asm volatile("" ::: "memory");
+    }
+  };
 
-  int tb = t0;  // first tile of the current batch
-  for (int t = t0; t < t1; t += S) {
+  for (int ip = 0; ip < Pin; ++ip) {
+    const int pp = pk * Pin + ip;  // part of K
+    const int qa = static_cast<int>(static_cast<int64_t>(Q) * pp / Ptot);
+    const int nrec = static_cast<int>(static_cast<int64_t>(Q) * (pp + 1) / Ptot) - qa;
+    q0 = qa + 2 * wave;
+    nq = min(max(nrec - 2 * wave, 0), 2);  // 0, 1 or 2
+    tl = 0;
+    if constexpr (kRowLoads) {
+      // Row-contiguous loads (load i of record qq brings rows 2i and 2i + 1,
+      // 512 B each), then through LDS into the operand layout.  Lane l of
+      // load i holds chunk c = l & 31 (inputs 8c .. 8c+7) of row
+      // r = 2i + (l >> 5); it is stored at row r, chunk c ^ (r & 7) of the
+      // wave's 8 KB area, and lane (j, kb) reads chunk 8 gi + w of row j for
+      // operand (gi, h): the XOR keeps both sides free of bank conflicts.
+      u32x4 xrow[2][8];
 #pragma unroll
-    for (int i = 0; i < S; ++i) {
-      load(st[(i + 1) % S]);
-      __builtin_amdgcn_sched_barrier(0);
-      if (in_step) __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      if (t + i < t1) {  // the same for every wave: barriers below are safe
-        f32x4 acc = fzero;
-        compute(st[i], acc);
-        part[((t + i - tb) * W + wave) * 64 + lane] = acc;
-        if (t + i - tb == NB - 1 || t + i == t1 - 1) {
-          __syncthreads();
-          const int nb = t + i - tb + 1;
-          for (int e = threadIdx.x; e < nb * 64; e += 64 * W) {
-            const int tt = e >> 6, l = e & 63;
-            f32x4 v = part[(tt * W) * 64 + l];
-            for (int w2 = 1; w2 < W; ++w2) v += part[(tt * W + w2) * 64 + l];
-            const int n = (tb + tt) * 16 + (l & 15);
+      for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int m = (l >> 4) * 4 + r;
-              if constexpr (kSample) {
-                if (m < M) lg[m * kSampleLgStride + (n - t0 * 16)] = v[r];
-              } else {
-                // non-temporal: on the LM head at M = 16 (15.9 MB of y)
-                // plain stores cost 124 us per call against 119
-                if (m < M)
-                  __builtin_nontemporal_store(v[r], &out[static_cast<uint64_t>(m) * N + n]);
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t r = 2 * i + (lane >> 5);
+          const uint32_t off = (r * K + 256 * (q0 + qq) + 8 * (lane & 31)) * 2;
+          xrow[qq][i] = buffer_load16<0>(xr, off, qq < nq ? 0u : 0x7FFFFFF0u);
+        }
+      load(st[0]);
+      char *area = reinterpret_cast<char *>(part) + wave * 8192;
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = 2 * i + (lane >> 5);
+          const int c = (lane & 31) ^ (r & 7);
+          *reinterpret_cast<u32x4 *>(area + r * 512 + c * 16) = xrow[qq][i];
+        }
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int c = (8 * gi + (h ? w_h1 : w_h0)) ^ (j & 7);
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(area + j * 512 + c * 16);
+            xa[qq][gi][h] = kPlanar ? pair_activations(v) : v;
+          }
+      }
+      // the areas alias the partial sums: every wave has its operands in
+      // registers before any wave writes a partial sum
+      kslice_lds_barrier();
+    } else {
+      // direct loads in the operand layout: lane (j, kb), operand (gi, h)
+      // reads inputs 64 gi + 8 w .. +7 of row j
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t off = (static_cast<uint32_t>(j) * K + 256 * (q0 + qq) +
+                                  64 * gi + 8 * (h ? w_h1 : w_h0)) * 2;
+            xa[qq][gi][h] = buffer_load16<0>(xr, off, qq < nq ? 0u : 0x7FFFFFF0u);
+          }
+      load(st[0]);
+      __builtin_amdgcn_sched_barrier(0);  // every load issued before the seeds
+      if constexpr (kPlanar) {
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+          for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) xa[qq][gi][h] = pair_activations(xa[qq][gi][h]);
+      }
+    }
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const f32x4 s0 = mfma16x16x32(xa[qq][gi][0], neg, fzero);
+        xn[qq][gi] = mfma16x16x32(xa[qq][gi][1], neg, s0);
+      }
+
+    int tb = t0;  // first tile of the current batch
+    for (int t = t0; t < t1; t += S) {
+#pragma unroll
+      for (int i = 0; i < S; ++i) {
+        if (t + i < t1) fetch(st[i]);
+        __builtin_amdgcn_sched_barrier(0);
+        load(st[(i + 1) % S]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (in_step) __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + i < t1) {  // the same for every wave: barriers below are safe
+          f32x4 acc = fzero;
+          compute(st[i], acc);
+          part[((t + i - tb) * W + wave) * 64 + lane] = acc;
+          if (t + i - tb == NB - 1 || t + i == t1 - 1) {
+            __syncthreads();
+            const int nb = t + i - tb + 1;
+            for (int e = threadIdx.x; e < nb * 64; e += 64 * W) {
+              const int tt = e >> 6, l = e & 63;
+              f32x4 v = part[(tt * W) * 64 + l];
+              for (int w2 = 1; w2 < W; ++w2) v += part[(tt * W + w2) * 64 + l];
+              if constexpr (kSeq) {
+                // parts of K in turn: parts before the last keep running
+                // sums, in part order (at most kInMaxTiles tiles then)
+                {
+                  f32x4 *a = &tacc[(tb + tt - t0) * 64 + l];
+                  if (ip > 0) v = *a + v;
+                  if (ip + 1 < Pin) {
+                    *a = v;
+                    continue;
+                  }
+                }
+              }
+              const int n = (tb + tt) * 16 + (l & 15);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int m = (l >> 4) * 4 + r;
+                if constexpr (kSample) {
+                  if (m < M) lg[m * kSampleLgStride + (n - t0 * 16)] = v[r];
+                } else {
+                  // non-temporal: on the LM head at M = 16 (15.9 MB of y)
+                  // plain stores cost 124 us per call against 119
+                  if (m < M && n < N)
+                    __builtin_nontemporal_store(v[r], &out[static_cast<uint64_t>(m) * N + n]);
+                }
               }
             }
+            __syncthreads();
+            tb = t + i + 1;
           }
-          __syncthreads();
-          tb = t + i + 1;
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
   }
   if constexpr (kSample) {
@@ -1032,20 +1168,35 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
   }
 }
 
-template <int W, bool kSample = false>
-void launch_kslice_w(const q4_plan &p, const void *x, const void *Wt, float *y,
+template <int W, bool kSample, bool kPlanar, bool kSeq>
+void launch_kslice_v(const q4_plan &p, const void *x, const void *Wt, float *y,
                      float *ws, int M, int N, int K, hipStream_t stream) {
   const int parts = static_cast<int>(p.k_parts);
+  const int seq = static_cast<int>(p.k_seq_parts);
   // M >= 8: row-contiguous activation loads through LDS; below that the rows
   // past M are zeros anyway and direct loads save the LDS round trip
   if (M >= 8)
-    hipLaunchKernelGGL((gemm_kslice_kernel<W, true, kSample>), dim3(p.grid),
-                       dim3(64 * W), 0, stream, static_cast<const uint16_t *>(x),
-                       static_cast<const uint8_t *>(Wt), y, ws, M, N, K, parts);
+    hipLaunchKernelGGL((gemm_kslice_kernel<W, true, kSample, kPlanar, kSeq>),
+                       dim3(p.grid), dim3(64 * W), 0, stream,
+                       static_cast<const uint16_t *>(x),
+                       static_cast<const uint8_t *>(Wt), y, ws, M, N, K, parts, seq);
   else
-    hipLaunchKernelGGL((gemm_kslice_kernel<W, false, kSample>), dim3(p.grid),
-                       dim3(64 * W), 0, stream, static_cast<const uint16_t *>(x),
-                       static_cast<const uint8_t *>(Wt), y, ws, M, N, K, parts);
+    hipLaunchKernelGGL((gemm_kslice_kernel<W, false, kSample, kPlanar, kSeq>),
+                       dim3(p.grid), dim3(64 * W), 0, stream,
+                       static_cast<const uint16_t *>(x),
+                       static_cast<const uint8_t *>(Wt), y, ws, M, N, K, parts, seq);
+}
+
+template <int W, bool kSample = false, bool kPlanar = false>
+void launch_kslice_w(const q4_plan &p, const void *x, const void *Wt, float *y,
+                     float *ws, int M, int N, int K, hipStream_t stream) {
+  if constexpr (!kSample) {
+    if (p.k_seq_parts > 1) {
+      launch_kslice_v<W, kSample, kPlanar, true>(p, x, Wt, y, ws, M, N, K, stream);
+      return;
+    }
+  }
+  launch_kslice_v<W, kSample, kPlanar, false>(p, x, Wt, y, ws, M, N, K, stream);
 }
 
 // Part sums of a K split: y += workspace slices 1 .. P-1, in part order.
@@ -1059,10 +1210,17 @@ int launch_reduce_parts(float *y, const float *ws, int M, int N, int parts,
 
 int launch_kslice(const q4_plan &p, const void *x, const void *Wt, float *y,
                   float *ws, int M, int N, int K, hipStream_t stream) {
+  // sequential parts keep one running sum per tile of the workgroup
+  if (p.k_seq_parts > 1 && p.row_tiles > static_cast<uint32_t>(kInMaxTiles))
+    return Q4_EINVAL;
+  const bool planar = p.layout_id == Q4_LAYOUT_PLANAR;
   switch (p.block / 64) {
-#define Q4V_KSLICE_CASE(W)                                         \
-  case W:                                                          \
-    launch_kslice_w<W>(p, x, Wt, y, ws, M, N, K, stream);          \
+#define Q4V_KSLICE_CASE(W)                                                  \
+  case W:                                                                   \
+    if (planar)                                                             \
+      launch_kslice_w<W, false, true>(p, x, Wt, y, ws, M, N, K, stream);    \
+    else                                                                    \
+      launch_kslice_w<W, false, false>(p, x, Wt, y, ws, M, N, K, stream);   \
     break;
     Q4V_KSLICE_CASE(1) Q4V_KSLICE_CASE(2) Q4V_KSLICE_CASE(3)
     Q4V_KSLICE_CASE(4) Q4V_KSLICE_CASE(5) Q4V_KSLICE_CASE(6)
@@ -1082,6 +1240,9 @@ int launch_kslice(const q4_plan &p, const void *x, const void *Wt, float *y,
 int launch_kslice_sample(const q4_plan &p, const void *x, const void *Wt,
                          uint64_t *cand, int M, int N, int K,
                          hipStream_t stream) {
+  if (p.k_parts != 1 || p.k_seq_parts != 1 ||
+      p.row_tiles > static_cast<uint32_t>(kSampleMaxTiles))
+    return Q4_EINVAL;
   float *c = reinterpret_cast<float *>(cand);
   switch (p.block / 64) {
 #define Q4V_KSLICE_SAMPLE_CASE(W)                                         \
@@ -1152,7 +1313,9 @@ extern "C" int q4_gemm_verify(const void *x, const void *W, float *y, int M,
   if (st != Q4_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int n = static_cast<int>(N), k = static_cast<int>(K);
-  const q4_plan p = q4v::plan_gemm_planar(M, N, K);
+  const q4_plan p = q4v::plan_gemm_planar(M, N, K, q4v::device_cus());
+  if (p.kernel == Q4_KERNEL_TILED_KSLICE)  // the K-slice kernel, planar codes
+    return q4v::launch_kslice(p, x, W, y, nullptr, M, n, k, s);
   switch (p.k_splits) {
     case 1: return q4v::launch_gemm<4, 1>(p, x, W, y, M, n, k, s);
     case 2: return q4v::launch_gemm<2, 2>(p, x, W, y, M, n, k, s);
@@ -1229,7 +1392,7 @@ extern "C" int q4_gemm_verify_tiled_ws(const void *x, const void *W, float *y,
 // workgroup; grid == 0 when the shape does not qualify.
 static q4_plan plan_gemm_sample(int M, int64_t N, int64_t K) {
   q4_plan p = q4v::plan_gemm_tiled(M, N, K, q4v::device_cus());
-  if (p.kernel != Q4_KERNEL_TILED_KSLICE || p.k_parts != 1 ||
+  if (p.kernel != Q4_KERNEL_TILED_KSLICE || p.k_parts != 1 || p.k_seq_parts != 1 ||
       p.row_tiles > static_cast<uint32_t>(q4v::kSampleMaxTiles) || M > Q4_MAX_ROWS)
     p.grid = 0;
   return p;

@@ -60,7 +60,7 @@ def test_status_strings(lib):
                                  (7, 1088)])
 def test_layout_matches_oracle_and_generator(lib, N, K):
     lay = q4.q4_pack_layout(N, K)
-    assert lay["abi_version"] == 1 and lay["layout_id"] == 0
+    assert lay["abi_version"] == 2 and lay["layout_id"] == 0
     assert lay["N"] == N and lay["K"] == K and lay["group"] == 64
     assert lay["total_bytes"] == oracle.packed_bytes(N, K)
     assert lay["total_bytes"] == synth.packed_size(N, K)
@@ -163,6 +163,43 @@ def test_workspace_gemm_argument_errors(lib):
         "workspace_bytes"] == 0
     p = q4.q4_gemm_verify_tiled_ws_plan(3, 5120, 6144)
     assert p["workspace_bytes"] == (p["k_parts"] - 1) * 3 * 5120 * 4
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_plans_of_many_shapes(lib, layout):
+    """The planners over small, odd and large shapes, every M: each returns
+    a plan (or a clean error) whose grid, waves and parts fit the kernels'
+    limits; none may fault on the host."""
+    Ks = [64, 128, 192, 256, 512, 640, 1024, 5120, 6144, 6400, 6656, 17408,
+          65536, 262144]
+    Ns = [1, 15, 16, 17, 100, 5120, 34816, 248320]
+    for K in Ks:
+        for N in Ns:
+            if layout == 1 and (N % 16 or K % 256):
+                continue
+            for M in (1, 2, 7, 8, 16, 17, 32):
+                try:
+                    p = q4.q4_gemm_verify_plan(M, N, K, layout)
+                except q4.Q4Error:
+                    continue
+                assert 1 <= p["grid"] and 64 <= p["block"] <= 1024, (M, N, K, p)
+                assert p["k_parts"] >= 1 and p["k_seq_parts"] >= 1
+                assert p["layout_id"] == layout
+                if p["kernel"] == q4.KERNEL_TILED_KSLICE:
+                    assert p["block"] // 64 <= 12 and M <= 16
+                    records = K // 256
+                    parts = p["k_parts"] * p["k_seq_parts"]
+                    assert parts <= records
+                    assert -(-records // parts) <= 24
+                    if p["k_seq_parts"] > 1:
+                        assert p["row_tiles"] <= 16
+                # planar: the K-slice kernel whenever one part of K fits, or
+                # the sequential parts' tile accumulators hold a workgroup's
+                # share of the rows
+                per = -(-(-(-N // 16)) // 256)  # 256 CUs without a device
+                if (layout == 0 and M <= 16 and K % 256 == 0 and K >= 256
+                        and (K <= 6144 or per <= 16)):
+                    assert p["kernel"] == q4.KERNEL_TILED_KSLICE, (M, N, K)
 
 
 def test_noalloc_gemm_argument_errors(lib):

@@ -546,3 +546,66 @@ def test_stream_probes(q4):
     q4.q4_stream_read(src, src.numel(), sink)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
+
+
+# -------------------------------------------------------------- planar K-slice
+
+def test_planar_kslice_one_hot_and_integer_exact(q4):
+    """q4_gemm_verify on the planar layout takes the K-slice kernel for
+    K % 256 == 0: one-hot rows reproduce dequantised weights bit for bit
+    (the code words are regrouped across lanes and the activations permuted
+    to match, which must not change any product), and integer-valued inputs
+    give the oracle's fp32 result bit for bit, also with sequential parts of
+    K (K = 6656: two parts) and a ragged N."""
+    dev = torch.device("cuda")
+    for N, K in [(200, 768), (37, 6656)]:
+        plan = q4.q4_gemm_verify_plan(16, N, K, q4.LAYOUT_PLANAR)
+        assert plan["kernel"] == q4.KERNEL_TILED_KSLICE
+        W = synth.q4_weights(N, K, seed=80, device=dev)
+        ks = [0, 1, 7, 8, 63, 64, 130, 255, 256, 300, 511, K - 257, K - 64,
+              K - 9, K - 2, K - 1]
+        x = torch.zeros((len(ks), K), dtype=torch.bfloat16, device=dev)
+        for m, k in enumerate(ks):
+            x[m, k] = 1.0
+        _say(f"case planar one-hot N={N} K={K} seq={plan['k_seq_parts']}")
+        y = gemm(q4, x, W, len(ks), N, K).cpu().numpy()
+        w = oracle.dequant(W.cpu().numpy(), N, K)
+        for m, k in enumerate(ks):
+            assert np.array_equal(y[m].view(np.uint32), w[:, k].view(np.uint32)), (N, K, k)
+    rng = np.random.default_rng(81)
+    for M, N, K in [(16, 300, 1024), (9, 1000, 3072), (16, 77, 6656)]:
+        q = rng.integers(0, 16, size=(N, K))
+        G = K // 64
+        codes = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+        Wh = assemble(codes, bf16_bits_of(np.ones((N, G))),
+                      bf16_bits_of(np.full((N, G), -8.0)))
+        xi = rng.integers(-4, 5, size=(M, K)).astype(np.float32)
+        W = torch.from_numpy(Wh).to(dev)
+        x = torch.from_numpy(xi).to(torch.bfloat16).to(dev)
+        _say(f"case planar integer-exact M={M} N={N} K={K}")
+        y = gemm(q4, x, W, M, N, K).cpu().numpy()
+        y32, _, _, _ = oracle.gemm(bf16_bits_of(xi), Wh, N, K)
+        assert np.array_equal(y.view(np.uint32), y32.view(np.uint32)), (M, N, K)
+
+
+def test_sequential_parts_M_invariance_determinism(q4):
+    """K beyond 24 records without a workspace: each workgroup takes the
+    parts of K in turn (planar and tiled).  Rows do not depend on M, repeated
+    calls agree bit for bit, and the result is within the bound."""
+    dev = torch.device("cuda")
+    N, K = 5120, 17408
+    W = synth.q4_weights(N, K, seed=82, device=dev)
+    Wt = repacked(q4, W, N, K)
+    x = synth.activations(16, K, seed=82, stream=1, device=dev)
+    for layout, Wx, call in ((q4.LAYOUT_PLANAR, W, gemm),
+                             (q4.LAYOUT_TILED16, Wt, gemm_tiled)):
+        plan = q4.q4_gemm_verify_plan(16, N, K, layout)
+        assert plan["k_seq_parts"] > 1 and plan["workspace_bytes"] == 0
+        _say(f"case sequential parts layout={layout} seq={plan['k_seq_parts']}")
+        full = call(q4, x, Wx, 16, N, K)
+        again = call(q4, x, Wx, 16, N, K)
+        assert torch.equal(full.view(torch.int32), again.view(torch.int32))
+        for M in (1, 3, 8, 13):
+            part = call(q4, x[:M].contiguous(), Wx, M, N, K)
+            assert torch.equal(part.view(torch.int32), full[:M].view(torch.int32)), (layout, M)
+        full_check(full, x, W, N, K, f"sequential parts layout {layout}")

@@ -25,6 +25,8 @@ SHAPES = [(1, 1, 64), (3, 17, 192), (16, 257, 640), (5, 1000, 1088),
 
 def model(M, N, K):
     p = q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_PLANAR)
+    if p["kernel"] == q4.KERNEL_TILED_KSLICE:
+        return p, None, None, None, None, None
     ntw, ksw, grid, block = p["row_tiles"], p["k_splits"], p["grid"], p["block"]
     assert block == 64 * ntw * ksw and block <= 1024
     assert ntw * ksw in (4, 8, 16)
@@ -54,7 +56,10 @@ def model(M, N, K):
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_plan_accesses_in_bounds_and_exact(M, N, K):
-    p, n, kb, row_ok, bounds, (cb, so, bo, total) = model(M, N, K)
+    p, n, kb, row_ok, bounds, sizes = model(M, N, K)
+    if n is None:
+        return kslice_model(M, N, K, p)
+    cb, so, bo, total = sizes
     G = K // 64
     nv, kbv = n[row_ok], kb[row_ok]
     # every row < N appears exactly once per kb lane
@@ -185,23 +190,85 @@ def test_tiled_plan_reads_every_record_once(M, N, K):
 # tiles are written in batches of NB = LDS / (W KiB), each tile once, the
 # waves' partial sums added in wave order.
 
+IN_MAX_TILES = 16   # tile running sums of the sequential parts
+PLANAR_CODE_LDS = 4096  # planar: a wave's two records of one tile's codes
+
+
+def planar_word(j, kb, h):
+    """Planar K-slice: the code word of a group (and so the activations)
+    that operand h of lane (j, kb) takes: 2 kb + h."""
+    return 2 * kb + h
+
+
+def test_planar_code_staging():
+    """The planar codes' path through LDS: load i of record qq, lane l,
+    brings chunk (l & 7) ^ (l >> 3) of row 8i + (l >> 3) and lands at
+    qq 2048 + i 1024 + l 16; lane (j, kb) then reads 8 bytes of group g at
+    qq 2048 + j 128 + ((2g + (kb >> 1)) ^ (j & 7)) 16 + (kb & 1) 8, which
+    must be words 2 kb, 2 kb + 1 of group g of row j.  Every load covers
+    whole 128-byte row runs (8 lanes per row).  The inputs in an MFMA
+    operand slot must not depend on the lane's row: slot kb of every row
+    of x meets slot kb of every row of W.  Eight consecutive lanes read 8
+    distinct 16-byte bank groups."""
+    lds = {}
+    for qq in range(2):
+        for i in range(2):
+            rows = {}
+            for lane in range(64):
+                r, c = 8 * i + (lane >> 3), (lane & 7) ^ (lane >> 3)
+                rows.setdefault(r, set()).add(c)
+                for b in range(16):
+                    addr = qq * 2048 + i * 1024 + lane * 16 + b
+                    assert addr not in lds and addr < PLANAR_CODE_LDS
+                    lds[addr] = (qq, r, 16 * c + b)  # byte of the row's record
+            assert len(rows) == 8 and all(v == set(range(8)) for v in rows.values())
+    assert len(lds) == PLANAR_CODE_LDS
+    for qq in range(2):
+        for g in range(4):
+            slots = []
+            for lane in range(64):
+                j, kb = lane & 15, lane >> 4
+                base = qq * 2048 + j * 128 + (((2 * g + (kb >> 1)) ^ (j & 7)) * 16) + (kb & 1) * 8
+                got = [lds[base + b] for b in range(8)]
+                want = [(qq, j, 32 * g + 4 * planar_word(j, kb, 0) + b) for b in range(8)]
+                assert got == want, (qq, g, lane)
+                assert planar_word(j, kb, 1) == planar_word(j, kb, 0) + 1
+                slots.append((base % 128) // 8)
+            for s8 in range(8):
+                assert len({x // 2 for x in slots[8 * s8: 8 * s8 + 8]}) == 8
+    # the slots' words over kb are a permutation of the group's 8 words,
+    # the same for every row
+    for j in range(16):
+        assert sorted(planar_word(j, kb, h) for kb in range(4) for h in range(2)) == list(range(8))
+        assert all(planar_word(j, kb, h) == planar_word(0, kb, h)
+                   for kb in range(4) for h in range(2))
+
+
 def kslice_model(M, N, K, p):
     """Work split of the K-slice kernel for plan p: workgroup b has rank
-    (b % 8) G/8 + b/8 (XCD after XCD), takes part pk = rank // Gt of K
-    (records [Q pk / P, Q (pk+1) / P)) and tile group rank % Gt; wave w
-    takes the part's records 2w and 2w + 1."""
-    T, Q = N // 16, K // 256
-    P = p["k_parts"]
+    (b % 8) G/8 + b/8 (XCD after XCD), takes part group pk = rank // Gt of
+    K and tile group rank % Gt; the part group holds parts pk Pin .. +Pin-1
+    (Pin = k_seq_parts, taken one after another with tile running sums in
+    LDS), part pp = records [Q pp / Ptot, Q (pp+1) / Ptot) with
+    Ptot = P Pin; wave w takes the part's records 2w and 2w + 1."""
+    planar = p["layout_id"] == q4.LAYOUT_PLANAR
+    T, Q = -(-N // 16), K // 256
+    P, Pin = p["k_parts"], p["k_seq_parts"]
+    Ptot = P * Pin
     W = p["block"] // 64
-    Qp = -(-Q // P)
+    Qp = -(-Q // Ptot)
     assert M <= 16 and Qp <= 24 and W == (Qp + 1) // 2 and p["m_tiles"] == 1
+    assert planar or N % 16 == 0
     G = p["grid"]
     g0 = min(T, 256 // P)
     per = -(-T // g0)
     Gt = -(-T // per) if per >= 3 else g0
-    assert G == Gt * P
-    NB = LDS_BYTES // (W * 1024)
-    assert p["lds_bytes"] == NB * W * 1024 <= LDS_BYTES
+    assert G == Gt * P and p["row_tiles"] == per
+    code_lds = W * PLANAR_CODE_LDS if planar else 0
+    NB = (LDS_BYTES - IN_MAX_TILES * 1024 - code_lds) // (W * 1024)
+    assert NB >= 8  # the activation staging areas alias the partial sums
+    tacc = IN_MAX_TILES * 1024 if Pin > 1 else 0
+    assert p["lds_bytes"] == NB * W * 1024 + code_lds + tacc <= LDS_BYTES
     assert p["workspace_bytes"] == (P - 1) * M * N * 4
     hits = np.zeros((T, Q), dtype=np.int32)
     writes = np.zeros((P, T), dtype=np.int32)
@@ -209,9 +276,9 @@ def kslice_model(M, N, K, p):
              for b in range(G)]
     assert sorted(ranks) == list(range(G))
     x_bytes = M * K * 2
-    for pk in range(P):
-        qa = Q * pk // P
-        nrec = Q * (pk + 1) // P - qa
+    for pp in range(Ptot):
+        qa = Q * pp // Ptot
+        nrec = Q * (pp + 1) // Ptot - qa
         assert 1 <= nrec <= 2 * W
         # activation operand loads of wave w: a real row's own record, else
         # past the resource (zeros)
@@ -222,7 +289,8 @@ def kslice_model(M, N, K, p):
                 for qq in range(2):
                     for gi in range(4):
                         for h in range(2):
-                            k = 256 * (qa + 2 * w + qq) + 64 * gi + 16 * kb + 8 * h
+                            wd = planar_word(j, kb, h) if planar else 2 * kb + h
+                            k = 256 * (qa + 2 * w + qq) + 64 * gi + 8 * wd
                             off = (j * K + k) * 2
                             if qq < nq and j < M:
                                 assert k + 8 <= K and off + 16 <= x_bytes
@@ -231,36 +299,70 @@ def kslice_model(M, N, K, p):
                             else:
                                 assert x_bytes <= off + 0x7FFFFFF0 < 2 ** 32
         if M >= 8:
-            kslice_row_staging_model(M, K, W, p["lds_bytes"], qa, nrec)
+            kslice_row_staging_model(M, K, W, p["lds_bytes"] - tacc, qa, nrec,
+                                     planar)
+    G8 = K // 64
     for b in range(G):
         r = ranks[b]
         pk, g = r // Gt, r % Gt
-        qa = Q * pk // P
-        nrec = Q * (pk + 1) // P - qa
         t0, t1 = T * g // Gt, T * (g + 1) // Gt
         assert t1 > t0
-        span = (t1 - t0) * Q * 2304
+        assert Pin == 1 or t1 - t0 <= IN_MAX_TILES
+        rows = min(N - 16 * t0, 16 * (t1 - t0))
+        span = rows * (K // 2) if planar else (t1 - t0) * Q * 2304
         assert span < 0x7FFFFFF0
-        for w in range(W):
-            nq = min(max(nrec - 2 * w, 0), 2)
-            for tl in range(t1 - t0):
-                for qq in range(nq):
-                    off = (tl * Q + qa + 2 * w + qq) * 2304
-                    assert off + 2304 <= span
-                    hits[t0 + tl, qa + 2 * w + qq] += 1
-        # batches: a flush after every NB tiles and after the last
-        tb = t0
-        for t in range(t0, t1):
-            assert (t - tb) < NB
-            if t - tb == NB - 1 or t == t1 - 1:
-                for tt in range(tb, t + 1):
-                    writes[pk, tt] += 1
-                tb = t + 1
+        stored = set()  # tiles whose running sum holds parts so far
+        for ip in range(Pin):
+            pp = pk * Pin + ip
+            qa = Q * pp // Ptot
+            nrec = Q * (pp + 1) // Ptot - qa
+            for w in range(W):
+                nq = min(max(nrec - 2 * w, 0), 2)
+                q0 = qa + 2 * w
+                for tl in range(t1 - t0):
+                    for qq in range(nq):
+                        if planar:
+                            # rows j of the tile, 16 B at kb*16 and 64 + kb*16
+                            # of the record's 128 B
+                            for j in range(16):
+                                o = (tl * 16 + j) * (K // 2) + (q0 + qq) * 128
+                                if 16 * (t0 + tl) + j < N:
+                                    assert o + 128 <= span
+                                else:
+                                    assert o >= span
+                        else:
+                            off = (tl * Q + q0 + qq) * 2304
+                            assert off + 2304 <= span
+                        hits[t0 + tl, q0 + qq] += 1
+                    if planar and nq > 0:
+                        # 8 groups' scales (and biases) from group 4 q0 of
+                        # row j: inside the rows' ranges, or past them
+                        for j in range(16):
+                            o = ((tl * 16 + j) * G8 + 4 * q0) * 2
+                            if 16 * (t0 + tl) + j < N:
+                                assert o + 8 * nq <= rows * G8 * 2
+                            else:
+                                assert o >= rows * G8 * 2
+            # batches: a flush after every NB tiles and after the last; the
+            # sequential parts before the last keep running sums
+            tb = t0
+            for t in range(t0, t1):
+                assert (t - tb) < NB
+                if t - tb == NB - 1 or t == t1 - 1:
+                    for tt in range(tb, t + 1):
+                        if ip > 0:
+                            assert tt in stored
+                        if ip + 1 < Pin:
+                            assert tt - t0 < IN_MAX_TILES
+                            stored.add(tt)
+                        else:
+                            writes[pk, tt] += 1
+                    tb = t + 1
     assert np.all(hits == 1)
     assert np.all(writes == 1)
 
 
-def kslice_row_staging_model(M, K, W, lds_bytes, qa, nrec):
+def kslice_row_staging_model(M, K, W, lds_bytes, qa, nrec, planar=False):
     """M >= 8: the activations arrive by row-contiguous loads and pass
     through an 8 KB LDS area per wave.  Every operand register must end up
     holding exactly what the direct operand-layout load would have read,
@@ -292,9 +394,10 @@ def kslice_row_staging_model(M, K, W, lds_bytes, qa, nrec):
                 j, kb = lane & 15, lane >> 4
                 for gi in range(4):
                     for h in range(2):
-                        c = (8 * gi + 2 * kb + h) ^ (j & 7)
+                        wd = planar_word(j, kb, h) if planar else 2 * kb + h
+                        c = (8 * gi + wd) ^ (j & 7)
                         got = area[w * 8192 + j * 512 + c * 16]
-                        k = 256 * (qa + 2 * w + qq) + 64 * gi + 16 * kb + 8 * h
+                        k = 256 * (qa + 2 * w + qq) + 64 * gi + 8 * wd
                         want = (j, k) if (qq < nq and j < M) else None
                         assert got == want, (w, qq, lane, gi, h)
     # bank groups of 16 B (128 B per LDS cycle): the 8 lanes of a group of
@@ -308,8 +411,10 @@ def kslice_row_staging_model(M, K, W, lds_bytes, qa, nrec):
         for h in range(2):
             for g in range(8):
                 lanes = range(8 * g, 8 * g + 8)
-                banks = {((8 * gi + 2 * (l >> 4) + h) ^ ((l & 15) & 7)) & 7
-                         for l in lanes}
+                wd = [planar_word(l & 15, l >> 4, h) if planar else 2 * (l >> 4) + h
+                      for l in lanes]
+                banks = {((8 * gi + wd[i]) ^ ((l & 15) & 7)) & 7
+                         for i, l in enumerate(lanes)}
                 assert len(banks) == 8
 
 
@@ -324,6 +429,31 @@ def test_kslice_plan_shapes(M, N, K):
     assert p["kernel"] == q4.KERNEL_TILED_KSLICE
     kslice_model(M, N, K, p)
     assert q4.q4_gemm_verify_tiled_ws_plan(M, N, K) == p
+
+
+@pytest.mark.parametrize("layout", [q4.LAYOUT_PLANAR, q4.LAYOUT_TILED16])
+@pytest.mark.parametrize("M,N,K", [(16, 5120, 17408), (3, 5120, 17408),
+                                   (1, 16, 65536), (9, 4096, 6400),
+                                   (16, 1024, 12288), (2, 48, 24832)])
+def test_kslice_sequential_parts(layout, M, N, K):
+    """K beyond one part's 24 records without a workspace: each workgroup
+    takes the parts one after another (every record once, every tile
+    written once after its last part)."""
+    p = q4.q4_gemm_verify_plan(M, N, K, layout)
+    assert p["kernel"] == q4.KERNEL_TILED_KSLICE
+    assert p["k_parts"] == 1 and p["k_seq_parts"] == -(-(K // 256) // 24)
+    assert p["workspace_bytes"] == 0
+    kslice_model(M, N, K, p)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 256), (5, 17, 512), (16, 100, 768),
+                                   (8, 4099, 5120), (13, 70001, 256)])
+def test_planar_kslice_ragged_rows(M, N, K):
+    """The planar K-slice kernel on N not a multiple of 16: rows past N
+    read past their resource."""
+    p = q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_PLANAR)
+    assert p["kernel"] == q4.KERNEL_TILED_KSLICE
+    kslice_model(M, N, K, p)
 
 
 # resident-activation kernel (K <= 5120): workgroup b owns tiles
