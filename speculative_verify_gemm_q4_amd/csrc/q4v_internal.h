@@ -67,10 +67,15 @@ constexpr int kKsliceBatchLds = kLdsBytes - kInMaxTiles * 1024;
 // LDS of the K-slice kernel's partial sums for W waves.
 constexpr int kslice_batch(int W) { return kKsliceBatchLds / (W * 1024); }
 // On the planar layout each wave also stages its two records' codes of one
-// tile in LDS (4 KiB per wave).
+// tile in LDS (4 KiB per wave), and the workgroup the scales and biases of
+// the current and the next tile (at most 24 records: 6 KiB per tile); the
+// sequential parts then keep at most kInMaxTilesPlanar running sums.
 constexpr int kPlanarCodeLds = 4096;
-constexpr int kslice_planar_batch(int W) {
-  return (kKsliceBatchLds - W * kPlanarCodeLds) / (W * 1024);
+constexpr int kPlanarSbLds = 2 * 16 * kKsliceMaxRecords * 8;
+constexpr int kInMaxTilesPlanar = 4;
+constexpr int kslice_planar_batch(int W, bool seq) {
+  return (kLdsBytes - 2 * kPlanarSbLds - (seq ? kInMaxTilesPlanar * 1024 : 0) -
+          W * kPlanarCodeLds) / (W * 1024);
 }
 
 // The verify sampling epilogue's argument rules (sizes, parameters, NULL

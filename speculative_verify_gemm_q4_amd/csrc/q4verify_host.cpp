@@ -187,7 +187,10 @@ bool plan_kslice(int M, int64_t N, int64_t K, int cus, int parts, int seq,
   // 242 x 9 tiles instead of 256 x 8 or 9, 20.9 against 21.9 us at M = 16
   // on MI355X); with fewer, every CU's share matters more.
   const int64_t g = per >= 3 ? (tiles + per - 1) / per : g0;
-  if (seq > 1 && per > kInMaxTiles) return false;
+  const bool planar = layout == Q4_LAYOUT_PLANAR;
+  if (seq > 1 && per > (planar ? kInMaxTilesPlanar : kInMaxTiles)) return false;
+  // planar: one resource over a workgroup's scales and the biases after them
+  if (planar && N * (K / 32) + per * kTileRows * (K / 32) >= 0x7FFFFFF0LL) return false;
   // 32-bit buffer offsets over a workgroup's weights
   const int64_t span = layout == Q4_LAYOUT_PLANAR
                            ? per * kTileRows * (K / 2)
@@ -203,10 +206,11 @@ bool plan_kslice(int M, int64_t N, int64_t K, int cus, int parts, int seq,
   p.k_splits = static_cast<uint32_t>(waves);
   p.lookahead = kRecordGroups * 2;
   p.kernel = Q4_KERNEL_TILED_KSLICE;
-  const bool planar = layout == Q4_LAYOUT_PLANAR;
   p.lds_bytes = static_cast<uint32_t>(
-      (planar ? kslice_planar_batch(waves) : kslice_batch(waves)) * waves * 1024 +
-      (planar ? waves * kPlanarCodeLds : 0) + (seq > 1 ? kInMaxTiles * 1024 : 0));
+      planar ? kslice_planar_batch(waves, seq > 1) * waves * 1024 +
+                   waves * kPlanarCodeLds + 2 * kPlanarSbLds +
+                   (seq > 1 ? kInMaxTilesPlanar * 1024 : 0)
+             : kslice_batch(waves) * waves * 1024 + (seq > 1 ? kInMaxTiles * 1024 : 0));
   p.k_parts = static_cast<uint32_t>(parts);
   p.k_seq_parts = static_cast<uint32_t>(seq);
   p.m_tiles = 1;

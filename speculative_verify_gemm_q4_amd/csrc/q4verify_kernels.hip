@@ -91,6 +91,14 @@ __device__ __forceinline__ u32x4 pair_activations(u32x4 d) {
   return r;
 }
 
+// A per-lane value the compiler must treat as changed here: keeps the
+// values derived from it inside a loop (one register held across the loop
+// instead of every derived offset).
+__device__ __forceinline__ uint32_t opaque_v(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
       __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
@@ -804,16 +812,18 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
   const int Pin = kSeq ? Pin_ : 1;
   // tiles per reduction batch
   constexpr int NB = kSample   ? kslice_sample_batch(W)
-                     : kPlanar ? kslice_planar_batch(W)
+                     : kPlanar ? kslice_planar_batch(W, kSeq)
                                : kslice_batch(W);
   static_assert(NB >= 8, "the activation staging areas (8 KB per wave) fit in part");
   __shared__ f32x4 part[NB * W * 64];
   // planar: each wave's two records of codes of the next tile (16 rows x
-  // 128 B each), written by the loads themselves
+  // 128 B each), and the workgroup's scales and biases of the current and
+  // the next tile, written by the loads themselves
   __shared__ u32x4 ccode[kPlanar ? W * (kPlanarCodeLds / 16) : 1];
+  __shared__ u32x4 csb[kPlanar ? 2 * kPlanarSbLds / 16 : 1];
   __shared__ float lg[kSample ? Q4_MAX_ROWS * kSampleLgStride : 1];
   // running sums of the workgroup's tiles over parts of K taken in turn
-  __shared__ f32x4 tacc[kSeq ? kInMaxTiles * 64 : 1];
+  __shared__ f32x4 tacc[kSeq ? (kPlanar ? kInMaxTilesPlanar : kInMaxTiles) * 64 : 1];
 
   const int T = (N + 15) >> 4;
   const int Q = K >> 8;
@@ -833,7 +843,8 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
   const int t0 = static_cast<int>(static_cast<int64_t>(T) * g / Gt);
   const int t1 = static_cast<int>(static_cast<int64_t>(T) * (g + 1) / Gt);
   __builtin_assume(t1 > t0);  // a part has at most one workgroup per tile
-  const bool in_step = t1 - t0 >= 8;
+  // (planar: the waves meet once per tile anyway, for the shared scales)
+  const bool in_step = !kPlanar && t1 - t0 >= 8;
   const int Ptot = P * Pin;
   float *const out = pk == 0 ? y : ws + static_cast<uint64_t>(pk - 1) * M * N;
 
@@ -849,13 +860,12 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
                   : Wt + static_cast<uint64_t>(t0) * Q * kRecordBytes),
       0, kPlanar ? rows * (K >> 1) : (t1 - t0) * Q * kRecordBytes, kBufferWord3);
   const uint64_t NK = static_cast<uint64_t>(N) * static_cast<uint64_t>(K);
-  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+  // Planar scales of the workgroup's rows and, NK / 32 bytes on, their
+  // biases: one resource whose range ends after the last row's biases (a
+  // scale row past N reads finite biases, and is never stored).
+  const __amdgpu_buffer_rsrc_t sbr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t *>(Wt + NK / 2 + static_cast<uint64_t>(t0) * 16 * G8 * 2),
-      0, kPlanar ? rows * G8 * 2 : 0, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t *>(Wt + NK / 2 + NK / 32 +
-                            static_cast<uint64_t>(t0) * 16 * G8 * 2),
-      0, kPlanar ? rows * G8 * 2 : 0, kBufferWord3);
+      0, kPlanar ? static_cast<int>(NK / 32) + rows * G8 * 2 : 0, kBufferWord3);
   // Per stage, two records of one tile: for each, the codes of groups 0-1
   // (c0) and 2-3 (c1), 16 bytes per lane, and the (scale, bias) words;
   // tiled: sb[qq] word gi = scale | bias << 16 of group gi; planar: sc and
@@ -865,12 +875,26 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
   };
   int q0 = 0, nq = 0;  // the wave's records in the current part
   int tl = 0;          // next tile to load, counted from t0
+  // Planar scales and biases of the part (set per part): this wave's loads
+  // (at most two: ins = wave, wave + W of 2 nk) -- lane offsets at tile 0
+  // and LDS offsets -- and where the wave reads its own chunk.
+  constexpr uint32_t kNoChunk = 0xFFFFFFFFu;
+  int sb_n = 0;                  // loads of this wave
+  uint32_t sb_o0 = 0, sb_o1 = 0;  // lane offsets (past the range: nothing)
+  int sb_l0 = 0, sb_l1 = 0;      // LDS offsets in a buffer
+  int sb_rd = 0, sb_bias = 0;    // the wave's scales, and biases after them
   // Planar codes go straight from memory to the wave's LDS area: load i of
   // record qq brings rows 8i .. 8i+7 of the tile, 128 B (the record's 256
   // codes) each, lane l chunk (l & 7) ^ (l >> 3) of row 8i + (l >> 3), so
   // every load covers whole 128-byte runs.  Lane l lands at l * 16, which
   // puts chunk c of row r at r * 128 + (c ^ (r & 7)) * 16.
   char *const cwave = reinterpret_cast<char *>(ccode) + wave * kPlanarCodeLds;
+  // the lane's part of those offsets: row l >> 3 of the eight, its chunk
+  const uint32_t cl_lane =
+      static_cast<uint32_t>((lane >> 3) * (K >> 1) + (((lane & 7) ^ (lane >> 3)) << 4));
+  // where lane (j, kb) reads group 0 of record 0 (group g: ^ (g << 5))
+  const uint32_t cr_lane = static_cast<uint32_t>(
+      j * 128 + (((kb >> 1) ^ (j & 7)) << 4) + ((kb & 1) << 3));
   auto load = [&](Stage &st) {
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) {
@@ -878,13 +902,12 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
       if constexpr (kPlanar) {
         // none past the last tile: the area then belongs to the next part
         if (tl < t1 - t0) {
+          const uint32_t lo = opaque_v(cl_lane);
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
-            const int r = 8 * i + (lane >> 3);
-            const int c = (lane & 7) ^ (lane >> 3);
-            const uint32_t o = ok ? static_cast<uint32_t>((tl * 16 + r) * (K >> 1) +
-                                                          (q0 + qq) * 128 + c * 16)
-                                  : 0x7FFFFFF0u;
+            const uint32_t o =
+                ok ? lo + static_cast<uint32_t>((tl * 16 + 8 * i) * (K >> 1) + (q0 + qq) * 128)
+                   : 0x7FFFFFF0u;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 wr, (__attribute__((address_space(3))) void *)(cwave + qq * 2048 + i * 1024),
                 16, o, 0, 0, kNonTemporal);
@@ -899,13 +922,30 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
       }
     }
     if constexpr (kPlanar) {
-      // 8 groups of row j from record q0: scales, then biases (a second
-      // record past the slice contributes only zero activations)
-      const uint32_t o = tl < t1 - t0 && nq > 0
-                             ? static_cast<uint32_t>(((tl * 16 + j) * G8 + 4 * q0) * 2)
-                             : 0x7FFFFFF0u;
-      st.sb[0] = buffer_load16<kNonTemporal>(sr, o, 0);
-      st.sb[1] = buffer_load16<kNonTemporal>(br, o, 0);
+      // The tile's scales (array 0) and biases (array 1) of the part's
+      // groups: per array 16 rows of cpr 16-byte chunks (chunk c = groups
+      // 8c .. 8c+7 from the part's first, the records of wave c), each row's
+      // chunks one contiguous run.  Load k of array a brings chunks
+      // 64k .. 64k+63 of it to LDS buffer tl & 1, shared by the workgroup;
+      // the loads are dealt to the waves in turn.
+      // (lanes past the array's chunks stay idle: a load would write zeros
+      // over the other array's chunks)
+      if (tl < t1 - t0 && sb_n > 0) {
+        char *const buf = reinterpret_cast<char *>(csb) + (tl & 1) * kPlanarSbLds;
+        const uint32_t dt = static_cast<uint32_t>(tl * 32 * G8);  // 16 rows
+        const uint32_t o0 = opaque_v(sb_o0);
+        if (o0 != kNoChunk)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              sbr, (__attribute__((address_space(3))) void *)(buf + sb_l0), 16,
+              o0 + dt, 0, 0, kNonTemporal);
+        if (sb_n > 1) {
+          const uint32_t o1 = opaque_v(sb_o1);
+          if (o1 != kNoChunk)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                sbr, (__attribute__((address_space(3))) void *)(buf + sb_l1), 16,
+                o1 + dt, 0, 0, kNonTemporal);
+        }
+      }
     }
     ++tl;
   };
@@ -963,17 +1003,26 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
   // lane takes words 2 kb, 2 kb + 1 of groups 0-1 (c0: .x .y, .z .w) and
   // 2-3 (c1) of both records of row j.  The area is free again once the
   // reads have returned.
-  auto fetch = [&](Stage &s) {
+  auto fetch = [&](Stage &s, int tt) {
     if constexpr (kPlanar) {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the loads have landed
+      __builtin_amdgcn_s_barrier();        // ... those of every wave
       asm volatile("" ::: "memory");
+      // scales and biases of the wave's records (chunk `wave` of row j); a
+      // wave without records takes zeros (the LDS may hold any bits there)
+      {
+        const char *buf = reinterpret_cast<const char *>(csb) + (tt & 1) * kPlanarSbLds;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        const uint32_t rd = opaque_v(sb_rd);
+        s.sb[0] = nq > 0 ? *reinterpret_cast<const u32x4 *>(buf + rd) : zero;
+        s.sb[1] = nq > 0 ? *reinterpret_cast<const u32x4 *>(buf + rd + sb_bias) : zero;
+      }
+      const uint32_t cr = opaque_v(cr_lane);
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int c = (2 * g + (kb >> 1)) ^ (j & 7);
-          const uint2 v = *reinterpret_cast<const uint2 *>(
-              cwave + qq * 2048 + j * 128 + c * 16 + (kb & 1) * 8);
+          const uint2 v = *reinterpret_cast<const uint2 *>(cwave + qq * 2048 + (cr ^ (g << 5)));
           u32x4 &d = g < 2 ? s.c0[qq] : s.c1[qq];
           if (g & 1) {
             d.z = v.x;
@@ -995,6 +1044,38 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
     q0 = qa + 2 * wave;
     nq = min(max(nrec - 2 * wave, 0), 2);  // 0, 1 or 2
     tl = 0;
+    if constexpr (kPlanar) {
+      // Per tile and array (scales 0, biases 1): 16 rows of cpr 16-byte
+      // chunks (chunk c = groups 8c .. 8c+7 from the part's first, the
+      // records of wave c), each row's chunks one contiguous run.  Load k
+      // of array a brings chunks 64k .. 64k+63 of it, lane l chunk
+      // f = 64k + l (row f / cpr), to LDS a 256 cpr + f 16 of the buffer of
+      // the tile's parity, shared by the workgroup.  The 2 nk loads are
+      // dealt to the waves in turn, at most two each (W >= cpr).
+      const int cpr = (nrec + 1) >> 1;
+      const int nk = (16 * cpr + 63) >> 6;
+      sb_n = (wave < 2 * nk) + (wave + W < 2 * nk);
+      uint32_t o[2];
+      int l[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int ins = wave + u * W;
+        const int a = ins >= nk;
+        const int k = ins - a * nk;
+        const int f = 64 * k + lane;
+        const int r = f / cpr;
+        o[u] = f < 16 * cpr ? static_cast<uint32_t>(a * static_cast<int>(NK / 32) +
+                                                    (r * G8 + 4 * qa) * 2 + 16 * (f - r * cpr))
+                            : kNoChunk;
+        l[u] = a * 256 * cpr + k * 1024;
+      }
+      sb_o0 = o[0];
+      sb_o1 = o[1];
+      sb_l0 = l[0];
+      sb_l1 = l[1];
+      sb_rd = (j * cpr + wave) * 16;
+      sb_bias = 256 * cpr;
+    }
     if constexpr (kRowLoads) {
       // Row-contiguous loads (load i of record qq brings rows 2i and 2i + 1,
       // 512 B each), then through LDS into the operand layout.  Lane l of
@@ -1069,7 +1150,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
     for (int t = t0; t < t1; t += S) {
 #pragma unroll
       for (int i = 0; i < S; ++i) {
-        if (t + i < t1) fetch(st[i]);
+        if (t + i < t1) fetch(st[i], t + i - t0);
         __builtin_amdgcn_sched_barrier(0);
         load(st[(i + 1) % S]);
         __builtin_amdgcn_sched_barrier(0);

@@ -198,7 +198,7 @@ def test_plans_of_many_shapes(lib, layout):
                 # share of the rows
                 per = -(-(-(-N // 16)) // 256)  # 256 CUs without a device
                 if (layout == 0 and M <= 16 and K % 256 == 0 and K >= 256
-                        and (K <= 6144 or per <= 16)):
+                        and (K <= 6144 or per <= 4)):
                     assert p["kernel"] == q4.KERNEL_TILED_KSLICE, (M, N, K)
 
 

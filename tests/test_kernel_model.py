@@ -192,6 +192,8 @@ def test_tiled_plan_reads_every_record_once(M, N, K):
 
 IN_MAX_TILES = 16   # tile running sums of the sequential parts
 PLANAR_CODE_LDS = 4096  # planar: a wave's two records of one tile's codes
+PLANAR_SB_LDS = 2 * 16 * 24 * 8  # planar: one tile's scales and biases
+IN_MAX_TILES_PLANAR = 4
 
 
 def planar_word(j, kb, h):
@@ -264,11 +266,18 @@ def kslice_model(M, N, K, p):
     per = -(-T // g0)
     Gt = -(-T // per) if per >= 3 else g0
     assert G == Gt * P and p["row_tiles"] == per
-    code_lds = W * PLANAR_CODE_LDS if planar else 0
-    NB = (LDS_BYTES - IN_MAX_TILES * 1024 - code_lds) // (W * 1024)
+    if planar:
+        # codes per wave, two tiles' scales and biases, running sums of at
+        # most IN_MAX_TILES_PLANAR tiles
+        tacc = IN_MAX_TILES_PLANAR * 1024 if Pin > 1 else 0
+        fixed = W * PLANAR_CODE_LDS + 2 * PLANAR_SB_LDS + tacc
+        NB = (LDS_BYTES - fixed) // (W * 1024)
+    else:
+        tacc = IN_MAX_TILES * 1024 if Pin > 1 else 0
+        fixed = tacc
+        NB = (LDS_BYTES - IN_MAX_TILES * 1024) // (W * 1024)
     assert NB >= 8  # the activation staging areas alias the partial sums
-    tacc = IN_MAX_TILES * 1024 if Pin > 1 else 0
-    assert p["lds_bytes"] == NB * W * 1024 + code_lds + tacc <= LDS_BYTES
+    assert p["lds_bytes"] == NB * W * 1024 + fixed <= LDS_BYTES
     assert p["workspace_bytes"] == (P - 1) * M * N * 4
     hits = np.zeros((T, Q), dtype=np.int32)
     writes = np.zeros((P, T), dtype=np.int32)
@@ -307,7 +316,7 @@ def kslice_model(M, N, K, p):
         pk, g = r // Gt, r % Gt
         t0, t1 = T * g // Gt, T * (g + 1) // Gt
         assert t1 > t0
-        assert Pin == 1 or t1 - t0 <= IN_MAX_TILES
+        assert Pin == 1 or t1 - t0 <= (IN_MAX_TILES_PLANAR if planar else IN_MAX_TILES)
         rows = min(N - 16 * t0, 16 * (t1 - t0))
         span = rows * (K // 2) if planar else (t1 - t0) * Q * 2304
         assert span < 0x7FFFFFF0
@@ -334,15 +343,9 @@ def kslice_model(M, N, K, p):
                             off = (tl * Q + q0 + qq) * 2304
                             assert off + 2304 <= span
                         hits[t0 + tl, q0 + qq] += 1
-                    if planar and nq > 0:
-                        # 8 groups' scales (and biases) from group 4 q0 of
-                        # row j: inside the rows' ranges, or past them
-                        for j in range(16):
-                            o = ((tl * 16 + j) * G8 + 4 * q0) * 2
-                            if 16 * (t0 + tl) + j < N:
-                                assert o + 8 * nq <= rows * G8 * 2
-                            else:
-                                assert o >= rows * G8 * 2
+
+            if planar:
+                planar_scale_loads(N, K, W, t0, t1, rows, qa, nrec)
             # batches: a flush after every NB tiles and after the last; the
             # sequential parts before the last keep running sums
             tb = t0
@@ -360,6 +363,51 @@ def kslice_model(M, N, K, p):
                     tb = t + 1
     assert np.all(hits == 1)
     assert np.all(writes == 1)
+
+
+def planar_scale_loads(N, K, W, t0, t1, rows, qa, nrec):
+    """Planar scales and biases of one part for each tile: load k of array
+    a (dealt to wave (a nk + k) mod W) lane l brings chunk f = 64k + l < 16
+    cpr (row f // cpr, chunk f % cpr of the part's run) to LDS
+    a 256 cpr + f 16.  Every chunk a wave with records reads (row j, chunk
+    = wave) is loaded once, from the right bytes, inside the resource (one
+    range over the scales and then the biases) or past it."""
+    G8 = K // 64
+    NK32 = N * K // 32
+    cpr = (nrec + 1) // 2
+    nk = -(-16 * cpr // 64)
+    rng = NK32 + rows * G8 * 2  # the resource's range from the scales of t0
+    assert rng < 0x7FFFFFF0
+    for tl in range(t1 - t0):
+        lds = {}
+        for ins in range(2 * nk):
+            a, k = ins >= nk, ins - (ins >= nk) * nk
+            for lane in range(64):
+                f = 64 * k + lane
+                if f >= 16 * cpr:
+                    continue
+                r, c = f // cpr, f % cpr
+                o = a * NK32 + ((tl * 16 + r) * G8 + 4 * qa) * 2 + 16 * c
+                addr = a * 256 * cpr + f * 16
+                assert addr + 16 <= PLANAR_SB_LDS and addr not in lds
+                lds[addr] = (a, r, c, o)
+                row = 16 * (t0 + tl) + r
+                if row < N:
+                    # a real row's run lies inside the range
+                    assert o + 8 * min(2, nrec - 2 * c) <= rng
+                elif a == 1:
+                    # biases of a row past N: past the range (zeros); a
+                    # scale row past N reads biases (finite) or zeros
+                    assert o >= rng
+        for w in range(W):
+            if min(max(nrec - 2 * w, 0), 2) == 0:
+                continue
+            for j in range(16):
+                for a in range(2):
+                    got = lds[(a * 16 + j) * cpr * 16 + w * 16]
+                    # scales of groups 4 (qa + 2w) .. +7 of row j
+                    want_o = a * NK32 + ((tl * 16 + j) * G8 + 4 * (qa + 2 * w)) * 2
+                    assert got == (a, j, w, want_o)
 
 
 def kslice_row_staging_model(M, K, W, lds_bytes, qa, nrec, planar=False):
