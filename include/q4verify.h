@@ -179,8 +179,8 @@ int q4_dequant(const void *W, float *W_out, int64_t N, int64_t K,
 
 /*
  * q4_stream_read -- measurement probe: read `bytes` bytes at `buf` once with
- * 16-byte loads and write nothing unless a checksum hits a sentinel (then
- * one uint32 to *sink).  Gives the streaming read rate the GEMM is measured
+ * 16-byte non-temporal loads, one contiguous share per CU, and write nothing
+ * unless a checksum hits a sentinel (then one uint32 to *sink).  Gives the streaming read rate the GEMM is measured
  * against besides the HBM peak (the prediction-first page, section "What a
  * Measurement Record Contains", keeps both the vendor figure and a measured
  * streaming rate as denominators).
