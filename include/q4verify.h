@@ -124,9 +124,19 @@ int q4_pack_layout(int64_t N, int64_t K, uint32_t layout_id, q4_layout *out);
  *       x or W.
  *   M : 1..Q4_MAX_ROWS.  N : 1..2^31-1.  K : multiple of 64, 64..2^31-64.
  *   stream : hipStream_t or NULL.
+ * Kernel (q4_gemm_verify_plan reports it): for K % 256 == 0 the K-slice
+ * kernel (Q4_KERNEL_TILED_KSLICE with layout_id Q4_LAYOUT_PLANAR): each
+ * wave keeps two 256-input records of the activations in registers and
+ * streams those records of every 16-row tile as whole 128-byte row runs
+ * through LDS; K beyond 24 records is taken in parts one after another by
+ * the same workgroup (k_seq_parts), so no workspace is needed at any K.
+ * Other K, K beyond 24 records with more than 4 tiles per workgroup
+ * (N > 16384 on 256 CUs), and shapes whose 32-bit offsets would overflow run
+ * Q4_KERNEL_PLANAR.
  * Accumulation is fp32; results stay within 2e-3 * sum_k |x*w| + 1e-5 of the
- * exact product, and a row's result does not depend on M or on the other
- * rows of the block (rows are computed independently, in the same order).
+ * exact product.  The plan depends on (N, K) only, never on M, and rows are
+ * summed in an order fixed by (N, K): a row's result does not depend on M or
+ * on the other rows of the block, and repeated calls are bitwise equal.
  * Errors: Q4_EINVAL, Q4_EALIGN, Q4_EOVERFLOW, Q4_EDEVICE, Q4_ELAUNCH.
  */
 int q4_gemm_verify(const void *x, const void *W, float *y, int M, int64_t N,
@@ -150,15 +160,21 @@ int q4_repack(const void *W_planar, void *W_tiled, int64_t N, int64_t K,
 
 /*
  * q4_gemm_verify_tiled -- the product of q4_gemm_verify for weights in
- * Q4_LAYOUT_TILED16 (same x, y, M and results within the same bound; every
- * row's result is independent of M).  Each wave streams whole records with
- * 16-byte loads, so every weight byte is fetched once in full cache lines.
- * For K <= 5120 the activations are first copied once per workgroup into
- * LDS (Q4_KERNEL_TILED_RESIDENT); larger K loads them per record
- * (Q4_KERNEL_TILED_STREAM).  q4_gemm_verify_plan reports which.
- * M may be up to Q4_MAX_ROWS_TILED = 32 (two MFMA row tiles multiplying the
- * same unpacked weights, the Splash engine's multi-lane shapes) when
- * K <= 2560; larger K at M > 16 needs q4_gemm_verify_tiled_ws.
+ * Q4_LAYOUT_TILED16 (same x, y, M and results within the same bound).  Each
+ * wave streams whole 2304-byte records with 16-byte loads, so every weight
+ * byte is fetched once in full cache lines.  Kernels (q4_gemm_verify_plan
+ * reports which): M <= 16 runs the K-slice kernel (Q4_KERNEL_TILED_KSLICE;
+ * K beyond 24 records in parts taken one after another, no workspace)
+ * whenever a workgroup's tiles fit its running sums (at most 16 tiles per
+ * workgroup once K is cut in parts), otherwise Q4_KERNEL_TILED_RESIDENT
+ * (K <= 5120, activations in LDS) or Q4_KERNEL_TILED_STREAM.  For M <= 16
+ * the plan depends on (N, K) only: within M = 1..16 a row's bits do not
+ * depend on M, and for the model's shapes (K in {5120, 6144, 17408}) they
+ * equal q4_gemm_verify's on the same weights.  M = 17..32 (two MFMA row
+ * tiles multiplying the same unpacked weights, the Splash engine's
+ * multi-lane shapes) runs another kernel, whose rows agree with the M <= 16
+ * rows within the bound, not bit for bit; without a workspace it needs
+ * K <= 2560 (larger K at M > 16: q4_gemm_verify_tiled_ws).
  *   x, y, M, stream: as q4_gemm_verify.
  *   W_tiled : device, Q4_LAYOUT_TILED16 of an N x K matrix, 16-byte aligned.
  *   N % 16 == 0, K % 256 == 0, K <= 2^26 (else Q4_EINVAL).
@@ -228,12 +244,16 @@ typedef struct {
                                         grid = one workgroup per CU (at most
                                         N/16), each owning whole 16-row tiles
                                         split evenly across its waves        */
-#define Q4_KERNEL_TILED_KSLICE 3u    /* tiled, M <= 16, K <= 6144; grid = one
-                                        workgroup per CU (at most N/16) over
-                                        whole tiles; wave w takes records 2w
-                                        and 2w+1 of every tile and keeps that
-                                        slice of the activations in
-                                        registers; block = 64 * ceil(K/512) */
+#define Q4_KERNEL_TILED_KSLICE 3u    /* M <= 16, either layout (layout_id);
+                                        grid = about one workgroup per CU
+                                        (times k_parts) over whole tiles;
+                                        wave w takes records 2w and 2w+1 of
+                                        every tile of its part of K and keeps
+                                        that slice of the activations in
+                                        registers; k_seq_parts parts of K are
+                                        taken one after another;
+                                        block = 64 * ceil(records/2) of a
+                                        part (at most 12 waves)             */
 
 /*
  * q4_gemm_verify_plan -- the plan q4_gemm_verify (layout_id
@@ -250,8 +270,11 @@ int q4_gemm_verify_plan(int M, int64_t N, int64_t K, uint32_t layout_id,
  * projections, whose N = 5120 gives only 320 tiles and whose 16 activation
  * rows exceed one CU's LDS): part 0 writes y, parts 1..P-1 write their
  * partial products into the workspace, and a second kernel adds them to y in
- * part order, so results are deterministic and do not depend on M.  For
- * K <= 5120 it runs exactly what q4_gemm_verify_tiled runs.
+ * part order, so results are deterministic.  Up to 16 rows the split (P = 4
+ * or more, a power of two, at most 24 records per part) depends on (N, K)
+ * only, so within M = 1..16 a row's bits do not depend on M; M = 17..32
+ * splits differently and agrees with those rows within the bound.  For
+ * K <= 6144 it runs exactly what q4_gemm_verify_tiled runs.
  *   x, W_tiled, y, M, N, K, stream: as q4_gemm_verify_tiled, with M up to
  *               Q4_MAX_ROWS_TILED for any K.
  *   workspace : device, 16-byte aligned, at least workspace_bytes as

@@ -239,10 +239,9 @@ q4_plan plan_gemm_tiled_ws(int M, int64_t N, int64_t K, int cus) {
   const int m_tiles = M > Q4_MAX_ROWS ? 2 : 1;
   const int64_t records = K / (kRecordGroups * Q4_GROUP);
   if (m_tiles == 1) {
-    // no split for K <= 6144, nor for K <= 2 x 5120 at M < 8, where the
-    // streaming kernel is as fast without the second launch
-    if (records <= kKsliceMaxRecords || (M < 8 && K <= 2 * kResidentMaxK))
-      return plan_gemm_tiled(M, N, K, cus);
+    // no split for K <= 6144; the rule looks at (N, K) only, so that every
+    // M <= 16 runs the same plan and a row's bits do not depend on M
+    if (records <= kKsliceMaxRecords) return plan_gemm_tiled(M, N, K, cus);
     int64_t parts = 4;
     while (parts * kKsliceMaxRecords < records) parts *= 2;
     q4_plan p;

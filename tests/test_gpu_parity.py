@@ -609,3 +609,26 @@ def test_sequential_parts_M_invariance_determinism(q4):
             part = call(q4, x[:M].contiguous(), Wx, M, N, K)
             assert torch.equal(part.view(torch.int32), full[:M].view(torch.int32)), (layout, M)
         full_check(full, x, W, N, K, f"sequential parts layout {layout}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M,N,K", [(1, 34816, 5120), (16, 5120, 6144),
+                                   (5, 5120, 17408), (16, 5120, 17408),
+                                   (8, 4112, 6656)])
+def test_planar_equals_tiled_bitwise(q4, M, N, K):
+    """The planar entry point and the tiled one multiply the same products
+    in the same order (the same K slice per MFMA operand slot, the same
+    parts): their outputs are equal bit for bit on the model's shapes, and
+    both within the oracle's bound."""
+    dev = torch.device("cuda")
+    W = synth.q4_weights(N, K, seed=21, device=dev)
+    x = synth.activations(M, K, seed=21, stream=1, device=dev)
+    _say(f"case planar==tiled: M={M} N={N} K={K}")
+    pl = q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_PLANAR)
+    tl = q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_TILED16)
+    assert pl["kernel"] == tl["kernel"] == q4.KERNEL_TILED_KSLICE
+    assert pl["k_seq_parts"] == tl["k_seq_parts"]
+    yp = gemm(q4, x, W, M, N, K)
+    yt = gemm_tiled(q4, x, repacked(q4, W, N, K), M, N, K)
+    assert torch.equal(yp.view(torch.int32), yt.view(torch.int32))
+    full_check(yp, x, W, N, K, "planar==tiled")

@@ -689,10 +689,12 @@ def test_resident_lds_layout_gives_each_lane_its_operand(M, K):
 def test_workspace_plan_split_parts(M, N, K):
     p = q4.q4_gemm_verify_tiled_ws_plan(M, N, K)
     # up to 16 rows the K-slice kernel: one part up to 24 records, beyond
-    # that P >= 4 parts (a power of two) of at most 24 records -- except
-    # K <= 10240 at M < 8: no split
+    # that P >= 4 parts (a power of two) of at most 24 records, whatever M
     Q = K // 256
-    if Q <= 24 or (M < 8 and K <= 10240):
+    launch = lambda q: {k: v for k, v in q.items() if k != "workspace_bytes"}
+    for M2 in range(1, 17):
+        assert launch(q4.q4_gemm_verify_tiled_ws_plan(M2, N, K)) == launch(p)
+    if Q <= 24:
         assert p == q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_TILED16)
         assert p["workspace_bytes"] == 0
         return
