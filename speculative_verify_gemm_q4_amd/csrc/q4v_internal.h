@@ -32,7 +32,7 @@ q4_plan plan_gemm_tiled(int M, int64_t N, int64_t K, int cus);
 bool plan_kslice(int M, int64_t N, int64_t K, int cus, int parts, int seq,
                  uint32_t layout, q4_plan *out);
 // Parts of K a K-slice workgroup takes in turn when nothing else splits K.
-int seq_parts_for(int64_t K);
+int seq_parts_for(int64_t K, int M);
 // The plan of the workspace path (q4_gemm_verify_tiled_ws).
 q4_plan plan_gemm_tiled_ws(int M, int64_t N, int64_t K, int cus);
 
@@ -66,6 +66,13 @@ constexpr int kInMaxTiles = 16;
 constexpr int kKsliceBatchLds = kLdsBytes - kInMaxTiles * 1024;
 // LDS of the K-slice kernel's partial sums for W waves.
 constexpr int kslice_batch(int W) { return kKsliceBatchLds / (W * 1024); }
+// M = 17..32: two row tiles, so 2 KiB of partial sums per wave and tile, and
+// the sequential parts' running sums (kInMaxTiles tiles) take 2 KiB a tile.
+constexpr int kslice_batch2(int W, bool seq) {
+  return (kLdsBytes - 1024 - (seq ? kInMaxTiles * 2048 : 0)) / (W * 2048);
+}
+// At most this many records per part at M = 17..32 (one per wave).
+constexpr int kKsliceMaxRecords2 = 12;
 // On the planar layout each wave also stages its two records' codes of one
 // tile in LDS (4 KiB per wave), and the workgroup the scales and biases of
 // the current and the next tile (at most 24 records: 6 KiB per tile); the

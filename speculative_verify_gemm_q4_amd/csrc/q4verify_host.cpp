@@ -92,7 +92,7 @@ q4_plan plan_gemm_planar(int M, int64_t N, int64_t K, int cus) {
   {
     // the K-slice kernel on the planar codes (K % 256 == 0, up to 16 rows)
     q4_plan p;
-    if (plan_kslice(M, N, K, cus, 1, seq_parts_for(K), Q4_LAYOUT_PLANAR, &p))
+    if (plan_kslice(M, N, K, cus, 1, seq_parts_for(K, M), Q4_LAYOUT_PLANAR, &p))
       return p;
   }
   // Waves per tile splitting K so that the grid holds enough waves (about 16
@@ -171,14 +171,19 @@ bool plan_resident(int M, int64_t N, int64_t K, int cus, int parts,
 // past N read zeros) and K % 256 == 0.
 bool plan_kslice(int M, int64_t N, int64_t K, int cus, int parts, int seq,
                  uint32_t layout, q4_plan *out) {
-  if (M > Q4_MAX_ROWS || parts < 1 || seq < 1 || parts > cus || N < 1 ||
-      K < kRecordGroups * Q4_GROUP || K % (kRecordGroups * Q4_GROUP) != 0)
+  // M = 17..32: two row tiles, one record per wave (tiled layout only)
+  const int rt = M > Q4_MAX_ROWS ? 2 : 1;
+  if (M > Q4_MAX_ROWS_TILED || parts < 1 || seq < 1 || parts > cus || N < 1 ||
+      K < kRecordGroups * Q4_GROUP || K % (kRecordGroups * Q4_GROUP) != 0 ||
+      (rt == 2 && layout != Q4_LAYOUT_TILED16))
     return false;
   const int64_t tiles = (N + kTileRows - 1) / kTileRows;
   const int64_t records = K / (kRecordGroups * Q4_GROUP);
   const int64_t nparts = static_cast<int64_t>(parts) * seq;
   const int64_t part_records = (records + nparts - 1) / nparts;
-  if (part_records > kKsliceMaxRecords || nparts > records) return false;
+  if (part_records > (rt == 2 ? kKsliceMaxRecords2 : kKsliceMaxRecords) ||
+      nparts > records)
+    return false;
   const int64_t per_part_cus = cus / parts;
   const int64_t g0 = tiles < per_part_cus ? tiles : per_part_cus;
   const int64_t per = (tiles + g0 - 1) / g0;
@@ -196,7 +201,7 @@ bool plan_kslice(int M, int64_t N, int64_t K, int cus, int parts, int seq,
                            ? per * kTileRows * (K / 2)
                            : per * records * kRecordBytes;
   if (span >= 0x7FFFFFF0LL) return false;
-  const int waves = static_cast<int>((part_records + 1) / 2);
+  const int waves = static_cast<int>(rt == 2 ? part_records : (part_records + 1) / 2);
   q4_plan p;
   std::memset(&p, 0, sizeof p);
   p.grid = static_cast<uint32_t>(g * parts);
@@ -207,13 +212,15 @@ bool plan_kslice(int M, int64_t N, int64_t K, int cus, int parts, int seq,
   p.lookahead = kRecordGroups * 2;
   p.kernel = Q4_KERNEL_TILED_KSLICE;
   p.lds_bytes = static_cast<uint32_t>(
-      planar ? kslice_planar_batch(waves, seq > 1) * waves * 1024 +
-                   waves * kPlanarCodeLds + 2 * kPlanarSbLds +
-                   (seq > 1 ? kInMaxTilesPlanar * 1024 : 0)
-             : kslice_batch(waves) * waves * 1024 + (seq > 1 ? kInMaxTiles * 1024 : 0));
+      planar    ? kslice_planar_batch(waves, seq > 1) * waves * 1024 +
+                      waves * kPlanarCodeLds + 2 * kPlanarSbLds +
+                      (seq > 1 ? kInMaxTilesPlanar * 1024 : 0)
+      : rt == 2 ? kslice_batch2(waves, seq > 1) * waves * 2048 +
+                      (seq > 1 ? kInMaxTiles * 2048 : 0)
+                : kslice_batch(waves) * waves * 1024 + (seq > 1 ? kInMaxTiles * 1024 : 0));
   p.k_parts = static_cast<uint32_t>(parts);
   p.k_seq_parts = static_cast<uint32_t>(seq);
-  p.m_tiles = 1;
+  p.m_tiles = static_cast<uint32_t>(rt);
   p.layout_id = layout;
   p.workspace_bytes = static_cast<uint64_t>(parts - 1) *
                       static_cast<uint64_t>(M) * static_cast<uint64_t>(N) * 4;
@@ -222,10 +229,11 @@ bool plan_kslice(int M, int64_t N, int64_t K, int cus, int parts, int seq,
 }
 
 // Parts of K taken one after another by each workgroup, for the K-slice
-// kernel without a workspace.
-int seq_parts_for(int64_t K) {
+// kernel without a workspace (at most 24 records a part, 12 at M > 16).
+int seq_parts_for(int64_t K, int M) {
   const int64_t records = K / (kRecordGroups * Q4_GROUP);
-  const int64_t s = (records + kKsliceMaxRecords - 1) / kKsliceMaxRecords;
+  const int64_t most = M > Q4_MAX_ROWS ? kKsliceMaxRecords2 : kKsliceMaxRecords;
+  const int64_t s = (records + most - 1) / most;
   return s < 1 ? 1 : s > 0x7FFFFFFF ? 0x7FFFFFFF : static_cast<int>(s);
 }
 
@@ -234,8 +242,9 @@ q4_plan plan_gemm_tiled_ws(int M, int64_t N, int64_t K, int cus) {
   // beyond that in P parts of K (at least 4, a power of two, so that the 320
   // tiles of the N = 5120 projections give every CU whole tiles): 15.9
   // against 16.9 us for the resident kernel's split on 5120 x 17408 at
-  // M = 16, measured on MI355X.  32 rows:
-  // the resident kernel, split whenever its activations exceed the LDS.
+  // M = 16, measured on MI355X.  32 rows: the K-slice kernel with two row
+  // tiles, else the resident kernel, split whenever its activations exceed
+  // the LDS.
   const int m_tiles = M > Q4_MAX_ROWS ? 2 : 1;
   const int64_t records = K / (kRecordGroups * Q4_GROUP);
   if (m_tiles == 1) {
@@ -248,6 +257,16 @@ q4_plan plan_gemm_tiled_ws(int M, int64_t N, int64_t K, int cus) {
     if (plan_kslice(M, N, K, cus, static_cast<int>(parts), 1, Q4_LAYOUT_TILED16, &p))
       return p;
     return plan_gemm_tiled(M, N, K, cus);
+  }
+  {
+    // 32 rows: the K-slice kernel with two row tiles on the same unpacked
+    // codes, one record per wave, so at most 12 records a part: P parts of
+    // K across workgroups (a power of two)
+    int64_t parts = 1;
+    while (parts * kKsliceMaxRecords2 < records) parts *= 2;
+    q4_plan p;
+    if (plan_kslice(M, N, K, cus, static_cast<int>(parts), 1, Q4_LAYOUT_TILED16, &p))
+      return p;
   }
   const int64_t per_part = kResidentMaxRecords / m_tiles;
   if (records > per_part) {
@@ -273,7 +292,7 @@ q4_plan plan_gemm_tiled(int M, int64_t N, int64_t K, int cus) {
     // in-projection at M = 16 even); beyond 24 records per tile the
     // workgroups take the parts of K one after another.
     q4_plan p;
-    if (plan_kslice(M, N, K, cus, 1, seq_parts_for(K), Q4_LAYOUT_TILED16, &p))
+    if (plan_kslice(M, N, K, cus, 1, seq_parts_for(K, M), Q4_LAYOUT_TILED16, &p))
       return p;
   }
   if (K <= kResidentMaxK) {

@@ -815,19 +815,25 @@ __device__ __forceinline__ void kslice_lds_barrier() {
 // below, so only keys at or above it survive; the survivors (usually a few
 // more than 32) are packed into the wave's part of the partial-sum area and
 // sorted 64 at a time with bitonic networks, merging into the running list.
-template <int W, bool kRowLoads, bool kSample, bool kPlanar, bool kSeq>
+template <int W, bool kRowLoads, bool kSample, bool kPlanar, bool kSeq, int RT>
 __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ Wt,
     float *__restrict__ y, float *__restrict__ ws, int M, int N, int K, int P,
     int Pin_) {
+  // RT = 2 (M = 17..32): two MFMA row tiles multiply the same unpacked codes,
+  // and a wave owns one record (R = 1) so that its activation operands stay
+  // at the registers of two records of one row tile
+  static_assert(RT == 1 || (RT == 2 && !kSample && !kPlanar), "row tiles");
+  constexpr int R = RT == 1 ? 2 : 1;  // records per wave
   // parts of K taken in turn: a run-time count only in the kSeq kernels
   const int Pin = kSeq ? Pin_ : 1;
   // tiles per reduction batch
   constexpr int NB = kSample   ? kslice_sample_batch(W)
                      : kPlanar ? kslice_planar_batch(W, kSeq)
+                     : RT == 2 ? kslice_batch2(W, kSeq)
                                : kslice_batch(W);
-  static_assert(NB >= 8, "the activation staging areas (8 KB per wave) fit in part");
-  __shared__ f32x4 part[NB * W * 64];
+  static_assert(NB * RT >= 8, "the activation staging areas (8 KB per wave) fit in part");
+  __shared__ f32x4 part[NB * W * RT * 64];
   // planar: each wave's two records of codes of the next tile (16 rows x
   // 128 B each), and the workgroup's scales and biases of the current and
   // the next tile, written by the loads themselves
@@ -835,7 +841,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
   __shared__ u32x4 csb[kPlanar ? 2 * kPlanarSbLds / 16 : 1];
   __shared__ float lg[kSample ? Q4_MAX_ROWS * kSampleLgStride : 1];
   // running sums of the workgroup's tiles over parts of K taken in turn
-  __shared__ f32x4 tacc[kSeq ? (kPlanar ? kInMaxTilesPlanar : kInMaxTiles) * 64 : 1];
+  __shared__ f32x4 tacc[kSeq ? (kPlanar ? kInMaxTilesPlanar : kInMaxTiles) * RT * 64 : 1];
 
   const int T = (N + 15) >> 4;
   const int Q = K >> 8;
@@ -883,7 +889,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
   // tiled: sb[qq] word gi = scale | bias << 16 of group gi; planar: sc and
   // bi hold the 8 groups' scales and biases (bf16 pairs) of both records.
   struct Stage {
-    u32x4 c0[2], c1[2], sb[2];
+    u32x4 c0[R], c1[R], sb[2];
   };
   int q0 = 0, nq = 0;  // the wave's records in the current part
   int tl = 0;          // next tile to load, counted from t0
@@ -909,7 +915,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
       j * 128 + (((kb >> 1) ^ (j & 7)) << 4) + ((kb & 1) << 3));
   auto load = [&](Stage &st) {
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
+    for (int qq = 0; qq < R; ++qq) {
       const bool ok = tl < t1 - t0 && qq < nq;
       if constexpr (kPlanar) {
         // none past the last tile: the area then belongs to the next part
@@ -961,6 +967,11 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
     }
     ++tl;
   };
+  // register stages: S - 1 tiles' weights in flight while one is
+  // multiplied.  (Two row tiles hold one record a stage; a third stage for
+  // them kept twice the bytes in flight but measured the same on MI355X:
+  // gate+up at M = 32 29.0 us with either, and spilled once parts of K are
+  // taken in turn.)
   constexpr int S = 2;
   Stage st[S];
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
@@ -979,12 +990,14 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
   // of x with slot kb of every row of W.)
   const int w_h0 = 2 * kb;
   const int w_h1 = 2 * kb + 1;
+  // activation operand units u = 0, 1: records 0 and 1 of the wave's pair
+  // (RT = 1), or row tiles 0 and 1 of its one record (RT = 2)
   u32x4 xa[2][4][2];
   f32x4 xn[2][4];
   const UnpackConsts uc = unpack_consts();
-  auto compute = [&](const Stage &s, f32x4 &acc) {
+  auto compute = [&](const Stage &s, f32x4 (&acc)[RT]) {
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
+    for (int qq = 0; qq < R; ++qq) {
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) {
         const u32x4 cw = gi < 2 ? s.c0[qq] : s.c1[qq];
@@ -1001,12 +1014,16 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
           sc = __uint_as_float(sbw << 16);
           bn = __uint_as_float(sbw & 0xFFFF0000u) * kMinusInv128;
         }
-        f32x4 tq = mfma16x16x32(xa[qq][gi][0], b0, xn[qq][gi]);
-        tq = mfma16x16x32(xa[qq][gi][1], b1, tq);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          acc[r] = __builtin_fmaf(bn, xn[qq][gi][r], acc[r]);
-          acc[r] = __builtin_fmaf(sc, tq[r], acc[r]);
+        for (int rt = 0; rt < RT; ++rt) {
+          const int u = qq + rt;  // the unit of (record qq, row tile rt)
+          f32x4 tq = mfma16x16x32(xa[u][gi][0], b0, xn[u][gi]);
+          tq = mfma16x16x32(xa[u][gi][1], b1, tq);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            acc[rt][r] = __builtin_fmaf(bn, xn[u][gi][r], acc[rt][r]);
+            acc[rt][r] = __builtin_fmaf(sc, tq[r], acc[rt][r]);
+          }
         }
       }
     }
@@ -1053,8 +1070,8 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
     const int pp = pk * Pin + ip;  // part of K
     const int qa = static_cast<int>(static_cast<int64_t>(Q) * pp / Ptot);
     const int nrec = static_cast<int>(static_cast<int64_t>(Q) * (pp + 1) / Ptot) - qa;
-    q0 = qa + 2 * wave;
-    nq = min(max(nrec - 2 * wave, 0), 2);  // 0, 1 or 2
+    q0 = qa + R * wave;
+    nq = min(max(nrec - R * wave, 0), R);  // 0 .. R
     tl = 0;
     if constexpr (kPlanar) {
       // Per tile and array (scales 0, biases 1): 16 rows of cpr 16-byte
@@ -1095,24 +1112,28 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
       // r = 2i + (l >> 5); it is stored at row r, chunk c ^ (r & 7) of the
       // wave's 8 KB area, and lane (j, kb) reads chunk 8 gi + w of row j for
       // operand (gi, h): the XOR keeps both sides free of bank conflicts.
+      // (unit u: record qu of the wave's records, rows 16 ru .. 16 ru + 15)
       u32x4 xrow[2][8];
 #pragma unroll
-      for (int qq = 0; qq < 2; ++qq)
+      for (int u = 0; u < 2; ++u) {
+        const int qu = RT == 1 ? u : 0, ru = RT == 1 ? 0 : u;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const uint32_t r = 2 * i + (lane >> 5);
-          const uint32_t off = (r * K + 256 * (q0 + qq) + 8 * (lane & 31)) * 2;
-          xrow[qq][i] = buffer_load16<0>(xr, off, qq < nq ? 0u : 0x7FFFFFF0u);
+          const uint32_t r = 16 * ru + 2 * i + (lane >> 5);
+          const uint32_t off = (r * K + 256 * (q0 + qu) + 8 * (lane & 31)) * 2;
+          xrow[u][i] = buffer_load16<0>(xr, off, qu < nq ? 0u : 0x7FFFFFF0u);
         }
+      }
       load(st[0]);
+      if constexpr (S > 2) load(st[1]);
       char *area = reinterpret_cast<char *>(part) + wave * 8192;
 #pragma unroll
-      for (int qq = 0; qq < 2; ++qq) {
+      for (int u = 0; u < 2; ++u) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int r = 2 * i + (lane >> 5);
           const int c = (lane & 31) ^ (r & 7);
-          *reinterpret_cast<u32x4 *>(area + r * 512 + c * 16) = xrow[qq][i];
+          *reinterpret_cast<u32x4 *>(area + r * 512 + c * 16) = xrow[u][i];
         }
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi)
@@ -1120,7 +1141,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
           for (int h = 0; h < 2; ++h) {
             const int c = (8 * gi + (h ? w_h1 : w_h0)) ^ (j & 7);
             const u32x4 v = *reinterpret_cast<const u32x4 *>(area + j * 512 + c * 16);
-            xa[qq][gi][h] = kPlanar ? pair_activations(v) : v;
+            xa[u][gi][h] = kPlanar ? pair_activations(v) : v;
           }
       }
       // the areas alias the partial sums: every wave has its operands in
@@ -1130,16 +1151,19 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
       // direct loads in the operand layout: lane (j, kb), operand (gi, h)
       // reads inputs 64 gi + 8 w .. +7 of row j
 #pragma unroll
-      for (int qq = 0; qq < 2; ++qq)
+      for (int u = 0; u < 2; ++u) {
+        const int qu = RT == 1 ? u : 0, ru = RT == 1 ? 0 : u;
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi)
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            const uint32_t off = (static_cast<uint32_t>(j) * K + 256 * (q0 + qq) +
+            const uint32_t off = (static_cast<uint32_t>(16 * ru + j) * K + 256 * (q0 + qu) +
                                   64 * gi + 8 * (h ? w_h1 : w_h0)) * 2;
-            xa[qq][gi][h] = buffer_load16<0>(xr, off, qq < nq ? 0u : 0x7FFFFFF0u);
+            xa[u][gi][h] = buffer_load16<0>(xr, off, qu < nq ? 0u : 0x7FFFFFF0u);
           }
+      }
       load(st[0]);
+      if constexpr (S > 2) load(st[1]);
       __builtin_amdgcn_sched_barrier(0);  // every load issued before the seeds
       if constexpr (kPlanar) {
 #pragma unroll
@@ -1164,26 +1188,31 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
       for (int i = 0; i < S; ++i) {
         if (t + i < t1) fetch(st[i], t + i - t0);
         __builtin_amdgcn_sched_barrier(0);
-        load(st[(i + 1) % S]);
+        load(st[(i + S - 1) % S]);
         __builtin_amdgcn_sched_barrier(0);
         if (in_step) __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         if (t + i < t1) {  // the same for every wave: barriers below are safe
-          f32x4 acc = fzero;
+          f32x4 acc[RT];
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) acc[rt] = fzero;
           compute(st[i], acc);
-          part[((t + i - tb) * W + wave) * 64 + lane] = acc;
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+            part[(((t + i - tb) * W + wave) * RT + rt) * 64 + lane] = acc[rt];
           if (t + i - tb == NB - 1 || t + i == t1 - 1) {
             __syncthreads();
             const int nb = t + i - tb + 1;
-            for (int e = threadIdx.x; e < nb * 64; e += 64 * W) {
-              const int tt = e >> 6, l = e & 63;
-              f32x4 v = part[(tt * W) * 64 + l];
-              for (int w2 = 1; w2 < W; ++w2) v += part[(tt * W + w2) * 64 + l];
+            // entry e: tile tt, row tile rt, lane l of the partial sums
+            for (int e = threadIdx.x; e < nb * RT * 64; e += 64 * W) {
+              const int tt = e / (RT * 64), rt = (e >> 6) - tt * RT, l = e & 63;
+              f32x4 v = part[((tt * W) * RT + rt) * 64 + l];
+              for (int w2 = 1; w2 < W; ++w2) v += part[(((tt * W + w2) * RT) + rt) * 64 + l];
               if constexpr (kSeq) {
                 // parts of K in turn: parts before the last keep running
                 // sums, in part order (at most kInMaxTiles tiles then)
                 {
-                  f32x4 *a = &tacc[(tb + tt - t0) * 64 + l];
+                  f32x4 *a = &tacc[((tb + tt - t0) * RT + rt) * 64 + l];
                   if (ip > 0) v = *a + v;
                   if (ip + 1 < Pin) {
                     *a = v;
@@ -1194,7 +1223,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
               const int n = (tb + tt) * 16 + (l & 15);
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
-                const int m = (l >> 4) * 4 + r;
+                const int m = 16 * rt + (l >> 4) * 4 + r;
                 if constexpr (kSample) {
                   if (m < M) lg[m * kSampleLgStride + (n - t0 * 16)] = v[r];
                 } else {
@@ -1261,20 +1290,21 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
   }
 }
 
-template <int W, bool kSample, bool kPlanar, bool kSeq>
+template <int W, bool kSample, bool kPlanar, bool kSeq, int RT = 1>
 void launch_kslice_v(const q4_plan &p, const void *x, const void *Wt, float *y,
                      float *ws, int M, int N, int K, hipStream_t stream) {
   const int parts = static_cast<int>(p.k_parts);
   const int seq = static_cast<int>(p.k_seq_parts);
   // M >= 8: row-contiguous activation loads through LDS; below that the rows
-  // past M are zeros anyway and direct loads save the LDS round trip
-  if (M >= 8)
-    hipLaunchKernelGGL((gemm_kslice_kernel<W, true, kSample, kPlanar, kSeq>),
+  // past M are zeros anyway and direct loads save the LDS round trip (two
+  // row tiles always take the row loads)
+  if (RT == 2 || M >= 8)
+    hipLaunchKernelGGL((gemm_kslice_kernel<W, true, kSample, kPlanar, kSeq, RT>),
                        dim3(p.grid), dim3(64 * W), 0, stream,
                        static_cast<const uint16_t *>(x),
                        static_cast<const uint8_t *>(Wt), y, ws, M, N, K, parts, seq);
-  else
-    hipLaunchKernelGGL((gemm_kslice_kernel<W, false, kSample, kPlanar, kSeq>),
+  else if constexpr (RT == 1)
+    hipLaunchKernelGGL((gemm_kslice_kernel<W, false, kSample, kPlanar, kSeq, 1>),
                        dim3(p.grid), dim3(64 * W), 0, stream,
                        static_cast<const uint16_t *>(x),
                        static_cast<const uint8_t *>(Wt), y, ws, M, N, K, parts, seq);
@@ -1283,6 +1313,15 @@ void launch_kslice_v(const q4_plan &p, const void *x, const void *Wt, float *y,
 template <int W, bool kSample = false, bool kPlanar = false>
 void launch_kslice_w(const q4_plan &p, const void *x, const void *Wt, float *y,
                      float *ws, int M, int N, int K, hipStream_t stream) {
+  if constexpr (!kSample && !kPlanar) {
+    if (p.m_tiles == 2) {
+      if (p.k_seq_parts > 1)
+        launch_kslice_v<W, false, false, true, 2>(p, x, Wt, y, ws, M, N, K, stream);
+      else
+        launch_kslice_v<W, false, false, false, 2>(p, x, Wt, y, ws, M, N, K, stream);
+      return;
+    }
+  }
   if constexpr (!kSample) {
     if (p.k_seq_parts > 1) {
       launch_kslice_v<W, kSample, kPlanar, true>(p, x, Wt, y, ws, M, N, K, stream);
@@ -1303,9 +1342,13 @@ int launch_reduce_parts(float *y, const float *ws, int M, int N, int parts,
 
 int launch_kslice(const q4_plan &p, const void *x, const void *Wt, float *y,
                   float *ws, int M, int N, int K, hipStream_t stream) {
-  // sequential parts keep one running sum per tile of the workgroup
+  // sequential parts keep one running sum per tile of the workgroup; two
+  // row tiles come on the tiled layout only, one record per wave
   if (p.k_seq_parts > 1 && p.row_tiles > static_cast<uint32_t>(kInMaxTiles))
     return Q4_EINVAL;
+  if (p.m_tiles == 2 && (p.layout_id != Q4_LAYOUT_TILED16 || M <= Q4_MAX_ROWS))
+    return Q4_EINVAL;
+  if (p.m_tiles == 1 && M > Q4_MAX_ROWS) return Q4_EINVAL;
   const bool planar = p.layout_id == Q4_LAYOUT_PLANAR;
   switch (p.block / 64) {
 #define Q4V_KSLICE_CASE(W)                                                  \

@@ -103,8 +103,11 @@ def test_tiled_shape_rules(lib):
     assert g(X, W, Y, 1, 16, 320, None) == -1
     assert g(X, W, Y, 0, 16, 256, None) == -1
     assert g(X, W, Y, 33, 16, 256, None) == -1        # M above 32
-    assert g(X, W, Y, 17, 16, 2816, None) == -1       # M > 16, K > 2560: needs
-    #                                                   the workspace call
+    # M > 16 and K beyond 12 records: parts in turn, valid (stops at the
+    # device check); with more than 16 tiles per workgroup (the LM head) it
+    # needs the workspace call
+    assert g(X, W, Y, 17, 16, 2816, None) == -4
+    assert g(X, W, Y, 32, 248320, 5120, None) == -1
     assert g(X, W, Y, 17, 16, 256, None) == -4        # valid: stops at device
     assert g(X + 8, W, Y, 1, 16, 256, None) == -2
     r = lib.q4_repack
@@ -186,11 +189,12 @@ def test_plans_of_many_shapes(lib, layout):
                 assert p["k_parts"] >= 1 and p["k_seq_parts"] >= 1
                 assert p["layout_id"] == layout
                 if p["kernel"] == q4.KERNEL_TILED_KSLICE:
-                    assert p["block"] // 64 <= 12 and M <= 16
+                    assert p["block"] // 64 <= 12
+                    assert p["m_tiles"] == (2 if M > 16 else 1)
                     records = K // 256
                     parts = p["k_parts"] * p["k_seq_parts"]
                     assert parts <= records
-                    assert -(-records // parts) <= 24
+                    assert -(-records // parts) <= (12 if M > 16 else 24)
                     if p["k_seq_parts"] > 1:
                         assert p["row_tiles"] <= 16
                 # planar: the K-slice kernel whenever one part of K fits, or

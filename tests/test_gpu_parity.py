@@ -280,10 +280,9 @@ def test_tiled_tiny(q4, M):
 def test_resident_empty_waves_after_other_lds_users(q4):
     """Small shapes where most of a workgroup's waves get no records (their
     weight loads all fall past their range and return at once), each call
-    preceded by kernels that leave other data in LDS: the resident kernel
-    (17..32 rows) must not start a wave before every activation copy has
-    landed, and the K-slice kernel (up to 16 rows) must not read another
-    kernel's LDS for its partial sums."""
+    preceded by kernels that leave other data in LDS: the K-slice kernel
+    (one or two row tiles, parts of K in turn) must not read another
+    kernel's LDS for its partial sums or running sums."""
     dev = torch.device("cuda")
     Wp = synth.q4_weights(2048, 4096, seed=40, device=dev)
     Wtp = repacked(q4, Wp, 2048, 4096)
@@ -293,11 +292,9 @@ def test_resident_empty_waves_after_other_lds_users(q4):
         W = synth.q4_weights(N, K, seed=41, device=dev)
         Wt = repacked(q4, W, N, K)
         for M in (1, 4, 16, 24):
-            if M > 16 and K > 2560:
-                continue  # 32 rows of this K need the workspace path
             p = q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_TILED16)
-            want = q4.KERNEL_TILED_KSLICE if M <= 16 else q4.KERNEL_TILED_RESIDENT
-            assert p["kernel"] == want
+            assert p["kernel"] == q4.KERNEL_TILED_KSLICE
+            assert p["m_tiles"] == (2 if M > 16 else 1)
             x = synth.activations(M, K, seed=41 + M, stream=1, device=dev)
             _, y64, a64, _ = oracle.gemm(synth.bf16_bits(x), W.cpu().numpy(),
                                          N, K)
@@ -491,6 +488,28 @@ def test_two_row_tiles_workspace(q4, M, N, K):
     y = gemm_tiled_ws(q4, x, repacked(q4, W, N, K), M, N, K)
     _, y64, a64, _ = oracle.gemm(synth.bf16_bits(x), W.cpu().numpy(), N, K)
     assert_within_bound(y, y64, a64, f"two row tiles M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(32, 34816, 5120), (24, 5120, 17408),
+                                   (17, 5120, 6144), (32, 16, 3072),
+                                   (29, 2064, 6656)])
+def test_two_row_tiles_plain_call(q4, M, N, K):
+    """17..32 rows without a workspace: two row tiles, K beyond 12 records
+    in parts taken one after another; every output against the oracle, and
+    bitwise equal to the workspace call when that one runs unsplit."""
+    dev = torch.device("cuda")
+    W = synth.q4_weights(N, K, seed=54, device=dev)
+    x = synth.activations(M, K, seed=54, stream=1, device=dev)
+    p = q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_TILED16)
+    assert p["kernel"] == q4.KERNEL_TILED_KSLICE and p["m_tiles"] == 2
+    _say(f"case two row tiles plain: M={M} N={N} K={K} "
+         f"seq={p['k_seq_parts']}")
+    Wt = repacked(q4, W, N, K)
+    y = gemm_tiled(q4, x, Wt, M, N, K)
+    full_check(y, x, W, N, K, f"two row tiles plain M={M} N={N} K={K}")
+    if p["k_seq_parts"] == 1:
+        assert torch.equal(y.view(torch.int32),
+                           gemm_tiled_ws(q4, x, Wt, M, N, K).view(torch.int32))
 
 
 def test_two_row_tiles_integer_exact_and_M_invariance(q4):

@@ -252,15 +252,21 @@ def kslice_model(M, N, K, p):
     K and tile group rank % Gt; the part group holds parts pk Pin .. +Pin-1
     (Pin = k_seq_parts, taken one after another with tile running sums in
     LDS), part pp = records [Q pp / Ptot, Q (pp+1) / Ptot) with
-    Ptot = P Pin; wave w takes the part's records 2w and 2w + 1."""
+    Ptot = P Pin; wave w takes the part's records R w .. R w + R - 1
+    (R = 2, or R = 1 with two row tiles at M = 17..32: the activation
+    operand units u = 0, 1 are then rows 16 u .. 16 u + 15 of one record)."""
     planar = p["layout_id"] == q4.LAYOUT_PLANAR
     T, Q = -(-N // 16), K // 256
     P, Pin = p["k_parts"], p["k_seq_parts"]
     Ptot = P * Pin
     W = p["block"] // 64
     Qp = -(-Q // Ptot)
-    assert M <= 16 and Qp <= 24 and W == (Qp + 1) // 2 and p["m_tiles"] == 1
+    RT = p["m_tiles"]
+    R = 1 if RT == 2 else 2
+    assert RT == (2 if M > 16 else 1) and M <= 32
+    assert Qp <= (12 if RT == 2 else 24) and W == -(-Qp // R)
     assert planar or N % 16 == 0
+    assert not (planar and RT == 2)
     G = p["grid"]
     g0 = min(T, 256 // P)
     per = -(-T // g0)
@@ -272,12 +278,17 @@ def kslice_model(M, N, K, p):
         tacc = IN_MAX_TILES_PLANAR * 1024 if Pin > 1 else 0
         fixed = W * PLANAR_CODE_LDS + 2 * PLANAR_SB_LDS + tacc
         NB = (LDS_BYTES - fixed) // (W * 1024)
+    elif RT == 2:
+        # two row tiles: 2 KiB of partial sums per wave and tile
+        tacc = IN_MAX_TILES * 2048 if Pin > 1 else 0
+        fixed = tacc
+        NB = (LDS_BYTES - 1024 - tacc) // (W * 2048)
     else:
         tacc = IN_MAX_TILES * 1024 if Pin > 1 else 0
         fixed = tacc
         NB = (LDS_BYTES - IN_MAX_TILES * 1024) // (W * 1024)
-    assert NB >= 8  # the activation staging areas alias the partial sums
-    assert p["lds_bytes"] == NB * W * 1024 + fixed <= LDS_BYTES
+    assert NB * RT >= 8  # the activation staging areas alias the partial sums
+    assert p["lds_bytes"] == NB * W * 1024 * RT + fixed <= LDS_BYTES
     assert p["workspace_bytes"] == (P - 1) * M * N * 4
     hits = np.zeros((T, Q), dtype=np.int32)
     writes = np.zeros((P, T), dtype=np.int32)
@@ -288,28 +299,30 @@ def kslice_model(M, N, K, p):
     for pp in range(Ptot):
         qa = Q * pp // Ptot
         nrec = Q * (pp + 1) // Ptot - qa
-        assert 1 <= nrec <= 2 * W
+        assert 1 <= nrec <= R * W
         # activation operand loads of wave w: a real row's own record, else
         # past the resource (zeros)
         for w in range(W):
-            nq = min(max(nrec - 2 * w, 0), 2)
+            nq = min(max(nrec - R * w, 0), R)
             for lane in range(64):
                 j, kb = lane & 15, lane >> 4
-                for qq in range(2):
+                for u in range(2):
+                    qu, ru = (u, 0) if RT == 1 else (0, u)
+                    row = 16 * ru + j
                     for gi in range(4):
                         for h in range(2):
                             wd = planar_word(j, kb, h) if planar else 2 * kb + h
-                            k = 256 * (qa + 2 * w + qq) + 64 * gi + 8 * wd
-                            off = (j * K + k) * 2
-                            if qq < nq and j < M:
+                            k = 256 * (qa + R * w + qu) + 64 * gi + 8 * wd
+                            off = (row * K + k) * 2
+                            if qu < nq and row < M:
                                 assert k + 8 <= K and off + 16 <= x_bytes
-                            elif qq < nq:
+                            elif qu < nq:
                                 assert off >= x_bytes
                             else:
                                 assert x_bytes <= off + 0x7FFFFFF0 < 2 ** 32
         if M >= 8:
             kslice_row_staging_model(M, K, W, p["lds_bytes"] - tacc, qa, nrec,
-                                     planar)
+                                     planar, RT)
     G8 = K // 64
     for b in range(G):
         r = ranks[b]
@@ -317,6 +330,7 @@ def kslice_model(M, N, K, p):
         t0, t1 = T * g // Gt, T * (g + 1) // Gt
         assert t1 > t0
         assert Pin == 1 or t1 - t0 <= (IN_MAX_TILES_PLANAR if planar else IN_MAX_TILES)
+        assert t1 - t0 <= per
         rows = min(N - 16 * t0, 16 * (t1 - t0))
         span = rows * (K // 2) if planar else (t1 - t0) * Q * 2304
         assert span < 0x7FFFFFF0
@@ -326,8 +340,8 @@ def kslice_model(M, N, K, p):
             qa = Q * pp // Ptot
             nrec = Q * (pp + 1) // Ptot - qa
             for w in range(W):
-                nq = min(max(nrec - 2 * w, 0), 2)
-                q0 = qa + 2 * w
+                nq = min(max(nrec - R * w, 0), R)
+                q0 = qa + R * w
                 for tl in range(t1 - t0):
                     for qq in range(nq):
                         if planar:
@@ -410,27 +424,32 @@ def planar_scale_loads(N, K, W, t0, t1, rows, qa, nrec):
                     assert got == (a, j, w, want_o)
 
 
-def kslice_row_staging_model(M, K, W, lds_bytes, qa, nrec, planar=False):
+def kslice_row_staging_model(M, K, W, lds_bytes, qa, nrec, planar=False,
+                             RT=1):
     """M >= 8: the activations arrive by row-contiguous loads and pass
     through an 8 KB LDS area per wave.  Every operand register must end up
     holding exactly what the direct operand-layout load would have read,
     the LDS stores of one round must not collide, and the areas must fit.
-    The part's records are [qa, qa + nrec)."""
+    The part's records are [qa, qa + nrec); unit u is record u of the
+    wave's two (RT = 1) or rows 16 u .. of its one record (RT = 2)."""
     x_bytes = M * K * 2
+    R = 1 if RT == 2 else 2
     assert W * 8192 <= lds_bytes
     for w in range(W):
-        nq = min(max(nrec - 2 * w, 0), 2)
-        for qq in range(2):
+        nq = min(max(nrec - R * w, 0), R)
+        for u in range(2):
+            qq, ru = (u, 0) if RT == 1 else (0, u)
             # what lane l of load i holds: (row, input) or None (zeros)
             area = {}
             for i in range(8):
                 for lane in range(64):
                     r, c = 2 * i + (lane >> 5), lane & 31
-                    k = 256 * (qa + 2 * w + qq) + 8 * c
-                    off = (r * K + k) * 2
-                    if qq < nq and r < M:
+                    row = 16 * ru + r
+                    k = 256 * (qa + R * w + qq) + 8 * c
+                    off = (row * K + k) * 2
+                    if qq < nq and row < M:
                         assert off + 16 <= x_bytes and k + 8 <= K
-                        val = (r, k)
+                        val = (row, k)
                     else:
                         assert off + (0 if qq < nq else 0x7FFFFFF0) >= x_bytes
                         val = None
@@ -445,9 +464,10 @@ def kslice_row_staging_model(M, K, W, lds_bytes, qa, nrec, planar=False):
                         wd = planar_word(j, kb, h) if planar else 2 * kb + h
                         c = (8 * gi + wd) ^ (j & 7)
                         got = area[w * 8192 + j * 512 + c * 16]
-                        k = 256 * (qa + 2 * w + qq) + 64 * gi + 8 * wd
-                        want = (j, k) if (qq < nq and j < M) else None
-                        assert got == want, (w, qq, lane, gi, h)
+                        k = 256 * (qa + R * w + qq) + 64 * gi + 8 * wd
+                        row = 16 * ru + j
+                        want = (row, k) if (qq < nq and row < M) else None
+                        assert got == want, (w, u, lane, gi, h)
     # bank groups of 16 B (128 B per LDS cycle): the 8 lanes of a group of
     # stores, and of a group of operand reads, hit 8 distinct groups
     for i in range(8):
@@ -587,12 +607,12 @@ def resident_model(M, N, K, p):
                                    (24, 48, 256), (20, 4096, 1024),
                                    (32, 4112, 2560), (17, 6000 * 16, 768),
                                    (32, 34816, 2560)])
-def test_resident_plan_more_shapes(M, N, K):
-    """The resident kernel now serves 17..32 rows (two MFMA row tiles) and,
-    on the workspace path, the parts of a split K."""
+def test_two_row_tile_plan_more_shapes(M, N, K):
+    """17..32 rows run the K-slice kernel with two MFMA row tiles (one
+    record per wave, at most 12 records a part)."""
     p = q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_TILED16)
-    assert p["kernel"] == q4.KERNEL_TILED_RESIDENT
-    resident_model(M, N, K, p)
+    assert p["kernel"] == q4.KERNEL_TILED_KSLICE and p["m_tiles"] == 2
+    kslice_model(M, N, K, p)
 
 
 def test_resident_split_tile_sums_in_wave_order():
@@ -709,23 +729,34 @@ def test_workspace_plan_split_parts(M, N, K):
 @pytest.mark.parametrize("M,N,K", [(17, 16, 256), (24, 34816, 2560),
                                    (32, 4096, 1024), (32, 256, 2816)])
 def test_plain_plan_32_rows(M, N, K):
-    """M > 16 without a workspace: the resident kernel when the two row
-    tiles' activations fit the LDS (K <= 2560), otherwise no plan."""
-    if K <= 2560:
-        p = q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_TILED16)
-        assert p["kernel"] == q4.KERNEL_TILED_RESIDENT and p["m_tiles"] == 2
-        resident_model(M, N, K, p)
-    else:
-        with pytest.raises(q4.Q4Error):
-            q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_TILED16)
+    """M > 16 without a workspace: the K-slice kernel with two row tiles,
+    K beyond 12 records in parts taken one after another when a
+    workgroup's tiles fit its running sums."""
+    p = q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_TILED16)
+    assert p["kernel"] == q4.KERNEL_TILED_KSLICE and p["m_tiles"] == 2
+    assert p["k_parts"] == 1 and p["k_seq_parts"] == -(-(K // 256) // 12)
+    assert p["workspace_bytes"] == 0
+    kslice_model(M, N, K, p)
+
+
+def test_plain_plan_32_rows_without_room():
+    """32 rows, no workspace, K beyond 12 records and more than 16 tiles
+    per workgroup (the LM head): no plan, before any device work."""
+    with pytest.raises(q4.Q4Error):
+        q4.q4_gemm_verify_plan(32, 248320, 5120, q4.LAYOUT_TILED16)
 
 
 @pytest.mark.parametrize("M,N,K", [(24, 34816, 5120), (32, 5120, 17408),
                                    (32, 248320, 5120), (17, 5120, 6144),
                                    (32, 16, 5376), (25, 48, 10240)])
 def test_workspace_plan_32_rows(M, N, K):
+    """32 rows with a workspace: the K-slice kernel with two row tiles, K in
+    P parts across workgroups (the least power of two with at most 12
+    records a part)."""
     p = q4.q4_gemm_verify_tiled_ws_plan(M, N, K)
-    assert p["kernel"] == q4.KERNEL_TILED_RESIDENT and p["m_tiles"] == 2
-    P = p["k_parts"]
-    assert P & (P - 1) == 0 and -(-(K // 256) // P) <= 10
-    resident_model(M, N, K, p)
+    assert p["kernel"] == q4.KERNEL_TILED_KSLICE and p["m_tiles"] == 2
+    P, Q = p["k_parts"], K // 256
+    assert P & (P - 1) == 0 and -(-Q // P) <= 12
+    assert P == 1 or -(-Q // (P // 2)) > 12
+    assert p["k_seq_parts"] == 1
+    kslice_model(M, N, K, p)
