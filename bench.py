@@ -284,13 +284,14 @@ def parity(torch, synth, x, y, W_host, N, K, threads):
 
 
 ENTRY_LAYOUT = {"q4_gemm_verify": "planar", "q4_gemm_verify_tiled": "tiled",
-                "q4_gemm_verify_tiled_ws": "tiled"}
+                "q4_gemm_verify_tiled_ws": "tiled",
+                "q4_gemm_verify_tiled_dot": "tiled"}
 
 
 def plan_brief(q4, entry, M, N, K):
     if entry == "q4_gemm_verify":
         p = q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_PLANAR)
-    elif entry == "q4_gemm_verify_tiled":
+    elif entry in ("q4_gemm_verify_tiled", "q4_gemm_verify_tiled_dot"):
         p = q4.q4_gemm_verify_plan(M, N, K, q4.LAYOUT_TILED16)
     else:
         p = q4.q4_gemm_verify_tiled_ws_plan(M, N, K)
@@ -870,7 +871,8 @@ def repeat_mode(spec, copy_mb):
     entry, shape, M, reps = spec.split(":")
     M, reps = int(M), int(reps)
     entry = {"planar": "q4_gemm_verify", "tiled": "q4_gemm_verify_tiled",
-             "ws": "q4_gemm_verify_tiled_ws"}.get(entry, entry)
+             "ws": "q4_gemm_verify_tiled_ws",
+             "dot": "q4_gemm_verify_tiled_dot"}.get(entry, entry)
     N, K = WORKLOADS[shape]
     dev = torch.device("cuda:0")
     q4.load()

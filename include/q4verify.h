@@ -43,6 +43,7 @@ extern "C" {
 #define Q4_GROUP 64     /* inputs per scale/bias group                     */
 #define Q4_MAX_ROWS 16  /* largest activation block M of q4_gemm_verify     */
 #define Q4_MAX_ROWS_TILED 32 /* of the tiled calls: two MFMA row tiles    */
+#define Q4_DOT_MAX_ROWS 4    /* of q4_gemm_verify_tiled_dot                */
 
 typedef enum {
   Q4_OK = 0,
@@ -182,6 +183,22 @@ int q4_repack(const void *W_planar, void *W_tiled, int64_t N, int64_t K,
  */
 int q4_gemm_verify_tiled(const void *x, const void *W_tiled, float *y, int M,
                          int64_t N, int64_t K, void *stream);
+
+/*
+ * q4_gemm_verify_tiled_dot -- q4_gemm_verify_tiled for M <= 4 on the vector
+ * ALU: the same K-slice kernel and weight stream, with the row dot products
+ * on v_dot2_f32_bf16 instead of MFMA tiles padded to 16 rows.  The Splash
+ * engine article (section "Why Apple silicon, and why not the M5") makes
+ * the case for matrix hardware at 8 verify rows; this entry point measures
+ * the other side at 1, 2 and 4 rows.  Results within the same bound as
+ * q4_gemm_verify (a different summation order: not bit-equal to the MFMA
+ * path); the plan depends on (N, K) only.
+ *   x, W_tiled, y, N, K, stream: as q4_gemm_verify_tiled.
+ *   M : 1..Q4_DOT_MAX_ROWS.  K <= 6144 (one part of K).
+ * Errors: as q4_gemm_verify_tiled; Q4_EINVAL for M > 4 or K > 6144.
+ */
+int q4_gemm_verify_tiled_dot(const void *x, const void *W_tiled, float *y,
+                             int M, int64_t N, int64_t K, void *stream);
 
 /*
  * q4_dequant -- W_out[n][k] = fp32(s * q + b), rounded once (test hook that

@@ -12,6 +12,8 @@ Functions (same names as the C entry points):
 * :func:`q4_gemm_verify` -- y[M, N] = x[M, K] @ W^T for Q4 W, fp32 out.
 * :func:`q4_repack` -- one-time reorder into the tiled layout.
 * :func:`q4_gemm_verify_tiled` -- the same product on tiled weights.
+* :func:`q4_gemm_verify_tiled_dot` -- the tiled product for M <= 4 on the
+  vector ALU (v_dot2) instead of MFMA.
 * :func:`q4_gemm_verify_tiled_ws` -- the tiled product with a workspace
   (K split across workgroups for K > 5120); :func:`workspace_for` sizes it.
 * :func:`q4_gemm_verify_tiled_noalloc` -- the workspace product with the
@@ -40,6 +42,7 @@ from ._lib import (ESCRATCH, ATTN_HEAD_DIM, ATTN_MAX_NODES, ATTN_PAGE, GDN_DK, G
                    MAX_ROWS_TILED, Q4Error,
                    LIB_PATH, lib_exports, load, q4_dequant, q4_gemm_verify,
                    q4_gemm_verify_plan, q4_gemm_verify_tiled,
+                   q4_gemm_verify_tiled_dot,
                    q4_gemm_verify_tiled_ws, q4_gemm_verify_tiled_ws_plan,
                    q4_gemm_verify_tiled_noalloc, NOALLOC_SCRATCH_BYTES,
                    q4_gdn_commit, q4_gdn_tree_out, q4_pack_layout, q4_verify_sample,

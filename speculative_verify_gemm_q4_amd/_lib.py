@@ -74,6 +74,10 @@ _SIGNATURES = {
     "q4_gemm_verify_tiled": ([ctypes.c_void_p, ctypes.c_void_p,
                               ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                               ctypes.c_int64, ctypes.c_void_p], ctypes.c_int),
+    "q4_gemm_verify_tiled_dot": ([ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_int,
+                                  ctypes.c_int64, ctypes.c_int64,
+                                  ctypes.c_void_p], ctypes.c_int),
     "q4_repack": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                    ctypes.c_int64, ctypes.c_void_p], ctypes.c_int),
     "q4_dequant": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
@@ -260,6 +264,23 @@ def q4_gemm_verify_tiled(x, Wt, y, M: int, N: int, K: int,
                                      _stream_handle(stream))
     if st != OK:
         raise Q4Error(st, "q4_gemm_verify_tiled")
+
+
+def q4_gemm_verify_tiled_dot(x, Wt, y, M: int, N: int, K: int,
+                             stream=None) -> None:
+    """q4_gemm_verify_tiled for M <= 4 with the dot products on the vector
+    ALU (v_dot2_f32_bf16) instead of MFMA."""
+    import torch
+    total = _total_bytes(int(N), int(K), LAYOUT_TILED16)
+    px = _ptr(x, "x", torch.bfloat16, shape=(M, K))
+    pw = _ptr(Wt, "Wt", torch.uint8, numel=total)
+    py = _ptr(y, "y", torch.float32, shape=(M, N))
+    if not (x.device == Wt.device == y.device):
+        raise ValueError("x, Wt and y must be on one device")
+    st = load().q4_gemm_verify_tiled_dot(px, pw, py, int(M), int(N), int(K),
+                                         _stream_handle(stream))
+    if st != OK:
+        raise Q4Error(st, "q4_gemm_verify_tiled_dot")
 
 
 def q4_gemm_verify_tiled_ws(x, Wt, y, M: int, N: int, K: int, ws=None,

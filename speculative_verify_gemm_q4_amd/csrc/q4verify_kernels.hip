@@ -42,6 +42,13 @@ namespace q4v {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// A 32-bit word as a bf16 pair.  (Passing a vector element straight to
+// __builtin_bit_cast made the compiler read element 0 for every index.)
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(bf16x2, w);
+}
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -815,7 +822,8 @@ __device__ __forceinline__ void kslice_lds_barrier() {
 // below, so only keys at or above it survive; the survivors (usually a few
 // more than 32) are packed into the wave's part of the partial-sum area and
 // sorted 64 at a time with bitonic networks, merging into the running list.
-template <int W, bool kRowLoads, bool kSample, bool kPlanar, bool kSeq, int RT>
+template <int W, bool kRowLoads, bool kSample, bool kPlanar, bool kSeq, int RT,
+          bool kDot = false>
 __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ Wt,
     float *__restrict__ y, float *__restrict__ ws, int M, int N, int K, int P,
@@ -824,6 +832,9 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
   // and a wave owns one record (R = 1) so that its activation operands stay
   // at the registers of two records of one row tile
   static_assert(RT == 1 || (RT == 2 && !kSample && !kPlanar), "row tiles");
+  // kDot: the VALU variant for M <= 4 (v_dot2_f32_bf16 instead of MFMA)
+  static_assert(!kDot || (RT == 1 && !kSample && !kPlanar && !kSeq && !kRowLoads),
+                "dot variant");
   constexpr int R = RT == 1 ? 2 : 1;  // records per wave
   // parts of K taken in turn: a run-time count only in the kSeq kernels
   const int Pin = kSeq ? Pin_ : 1;
@@ -831,6 +842,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
   constexpr int NB = kSample   ? kslice_sample_batch(W)
                      : kPlanar ? kslice_planar_batch(W, kSeq)
                      : RT == 2 ? kslice_batch2(W, kSeq)
+                     : kDot    ? kslice_batch(W) - 4
                                : kslice_batch(W);
   static_assert(NB * RT >= 8, "the activation staging areas (8 KB per wave) fit in part");
   __shared__ f32x4 part[NB * W * RT * 64];
@@ -839,6 +851,9 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
   // the next tile, written by the loads themselves
   __shared__ u32x4 ccode[kPlanar ? W * (kPlanarCodeLds / 16) : 1];
   __shared__ u32x4 csb[kPlanar ? 2 * kPlanarSbLds / 16 : 1];
+  // kDot: rows 0..3 of the activations of the wave's two records (1 KiB a
+  // row), read back as broadcast operands
+  __shared__ u32x4 xdot[kDot ? W * 4 * 64 : 1];
   __shared__ float lg[kSample ? Q4_MAX_ROWS * kSampleLgStride : 1];
   // running sums of the workgroup's tiles over parts of K taken in turn
   __shared__ f32x4 tacc[kSeq ? (kPlanar ? kInMaxTilesPlanar : kInMaxTiles) * RT * 64 : 1];
@@ -1028,6 +1043,62 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
       }
     }
   };
+  // kDot: lane (j, kb) multiplies row j of the tile with rows m < M of the
+  // activations over its slots (inputs 64 gi + 16 kb .. +15 of each group,
+  // read from LDS, where all 16 lanes of a kb group read the same bytes)
+  // with v_dot2_f32_bf16, 8 per group and row; the codes enter as
+  // bf16 128 + q as in the MFMA path, and xs, the slot's sum of x, removes
+  // the offset and carries the bias: per group s (dot - 128 xs) + b xs.  The
+  // four kb lanes' sums of a row are added with two permlane swaps, and
+  // lane (j, 0) returns rows 0..3 in the MFMA result's layout (rows 4..15,
+  // in the other lanes, are zero).
+  float xs[2][4][4];
+  auto compute_dot = [&](const Stage &s, f32x4 &res) {
+    float am[4] = {0.f, 0.f, 0.f, 0.f};
+    const u32x4 *xw = xdot + wave * 256;
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const u32x4 cw = gi < 2 ? s.c0[qq] : s.c1[qq];
+        const u32x4 b0 = unpack_codes((gi & 1) ? cw.z : cw.x, uc);
+        const u32x4 b1 = unpack_codes((gi & 1) ? cw.w : cw.y, uc);
+        const uint32_t sbw = s.sb[qq][gi];
+        const float sc = __uint_as_float(sbw << 16);
+        const float bb = __uint_as_float(sbw & 0xFFFF0000u);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          if (m < M) {  // uniform
+            const u32x4 v0 = xw[m * 64 + qq * 32 + 8 * gi + 2 * kb];
+            const u32x4 v1 = xw[m * 64 + qq * 32 + 8 * gi + 2 * kb + 1];
+            float d = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(b0[e]), as_bf16x2(v0[e]), d,
+                                                  false);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(b1[e]), as_bf16x2(v1[e]), d,
+                                                  false);
+            const float x1 = xs[qq][gi][m];
+            am[m] = __builtin_fmaf(sc, __builtin_fmaf(-128.0f, x1, d), am[m]);
+            am[m] = __builtin_fmaf(bb, x1, am[m]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t v = __float_as_uint(am[m]);
+      const auto p16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      const float s16 = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+      const uint32_t w = __float_as_uint(s16);
+      const auto p32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+      am[m] = __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+    }
+    const f32x4 mine = {am[0], am[1], am[2], am[3]};
+    res = kb == 0 ? mine : fzero;
+  };
   // Planar: once the tile's codes have landed in the wave's LDS area, each
   // lane takes words 2 kb, 2 kb + 1 of groups 0-1 (c0: .x .y, .z .w) and
   // 2-3 (c1) of both records of row j.  The area is free again once the
@@ -1105,7 +1176,41 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
       sb_rd = (j * cpr + wave) * 16;
       sb_bias = 256 * cpr;
     }
-    if constexpr (kRowLoads) {
+    if constexpr (kDot) {
+      // rows m < M of the wave's two records (inputs 256 q0 .. +511), 16
+      // bytes a lane, into the wave's LDS area (a record past the part
+      // reads zeros); then each lane's slot sums xs
+      const u32x4 zero4 = {0u, 0u, 0u, 0u};
+      u32x4 xv[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        xv[m] = m < M ? buffer_load16<0>(xr, static_cast<uint32_t>((m * K + 256 * q0 + 8 * lane) * 2),
+                                         (lane >> 5) < nq ? 0u : 0x7FFFFFF0u)
+                      : zero4;
+      load(st[0]);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) xdot[wave * 256 + m * 64 + lane] = xv[m];
+      const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            float t = 0.f;
+            if (m < M) {
+              const u32x4 v0 = xdot[wave * 256 + m * 64 + qq * 32 + 8 * gi + 2 * kb];
+              const u32x4 v1 = xdot[wave * 256 + m * 64 + qq * 32 + 8 * gi + 2 * kb + 1];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                t = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v0[e]), ones, t, false);
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                t = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v1[e]), ones, t, false);
+            }
+            xs[qq][gi][m] = t;
+          }
+    } else if constexpr (kRowLoads) {
       // Row-contiguous loads (load i of record qq brings rows 2i and 2i + 1,
       // 512 B each), then through LDS into the operand layout.  Lane l of
       // load i holds chunk c = l & 31 (inputs 8c .. 8c+7) of row
@@ -1174,13 +1279,15 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
             for (int h = 0; h < 2; ++h) xa[qq][gi][h] = pair_activations(xa[qq][gi][h]);
       }
     }
+    if constexpr (!kDot) {
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq)
+      for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        const f32x4 s0 = mfma16x16x32(xa[qq][gi][0], neg, fzero);
-        xn[qq][gi] = mfma16x16x32(xa[qq][gi][1], neg, s0);
-      }
+        for (int gi = 0; gi < 4; ++gi) {
+          const f32x4 s0 = mfma16x16x32(xa[qq][gi][0], neg, fzero);
+          xn[qq][gi] = mfma16x16x32(xa[qq][gi][1], neg, s0);
+        }
+    }
 
     int tb = t0;  // first tile of the current batch
     for (int t = t0; t < t1; t += S) {
@@ -1196,7 +1303,10 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
           f32x4 acc[RT];
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) acc[rt] = fzero;
-          compute(st[i], acc);
+          if constexpr (kDot)
+            compute_dot(st[i], acc[0]);
+          else
+            compute(st[i], acc);
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt)
             part[(((t + i - tb) * W + wave) * RT + rt) * 64 + lane] = acc[rt];
@@ -1340,6 +1450,31 @@ int launch_reduce_parts(float *y, const float *ws, int M, int N, int parts,
   return launch_status();
 }
 
+// The VALU (v_dot2_f32_bf16) variant of the K-slice kernel, M <= 4, one
+// pass of K, tiled layout (the caller has checked all three).
+int launch_kslice_dot(const q4_plan &p, const void *x, const void *Wt, float *y,
+                      int M, int N, int K, hipStream_t stream) {
+  if (p.k_parts != 1 || p.k_seq_parts != 1 || p.m_tiles != 1 || M > 4 ||
+      p.layout_id != Q4_LAYOUT_TILED16)
+    return Q4_EINVAL;
+  switch (p.block / 64) {
+#define Q4V_KSLICE_DOT_CASE(W)                                                  \
+  case W:                                                                       \
+    hipLaunchKernelGGL((gemm_kslice_kernel<W, false, false, false, false, 1, true>), \
+                       dim3(p.grid), dim3(64 * W), 0, stream,                   \
+                       static_cast<const uint16_t *>(x),                        \
+                       static_cast<const uint8_t *>(Wt), y, nullptr, M, N, K, 1, 1); \
+    break;
+    Q4V_KSLICE_DOT_CASE(1) Q4V_KSLICE_DOT_CASE(2) Q4V_KSLICE_DOT_CASE(3)
+    Q4V_KSLICE_DOT_CASE(4) Q4V_KSLICE_DOT_CASE(5) Q4V_KSLICE_DOT_CASE(6)
+    Q4V_KSLICE_DOT_CASE(7) Q4V_KSLICE_DOT_CASE(8) Q4V_KSLICE_DOT_CASE(9)
+    Q4V_KSLICE_DOT_CASE(10) Q4V_KSLICE_DOT_CASE(11) Q4V_KSLICE_DOT_CASE(12)
+#undef Q4V_KSLICE_DOT_CASE
+    default: return Q4_EINVAL;
+  }
+  return launch_status();
+}
+
 int launch_kslice(const q4_plan &p, const void *x, const void *Wt, float *y,
                   float *ws, int M, int N, int K, hipStream_t stream) {
   // sequential parts keep one running sum per tile of the workgroup; two
@@ -1460,6 +1595,22 @@ extern "C" int q4_gemm_verify(const void *x, const void *W, float *y, int M,
     case 16: return q4v::launch_gemm<1, 16>(p, x, W, y, M, n, k, s);
     default: return Q4_EINVAL;
   }
+}
+
+extern "C" int q4_gemm_verify_tiled_dot(const void *x, const void *W, float *y,
+                                        int M, int64_t N, int64_t K,
+                                        void *stream) {
+  int st = q4v::check_gemm_args(x, W, y, M, N, K, Q4_DOT_MAX_ROWS);
+  if (st != Q4_OK) return st;
+  st = q4v::check_tiled_shape(N, K);
+  if (st != Q4_OK) return st;
+  const q4_plan p = q4v::plan_gemm_tiled(M, N, K, q4v::device_cus());
+  if (p.kernel != Q4_KERNEL_TILED_KSLICE || p.k_parts != 1 || p.k_seq_parts != 1)
+    return Q4_EINVAL;  // K beyond 24 records
+  st = q4v::check_device();
+  if (st != Q4_OK) return st;
+  return q4v::launch_kslice_dot(p, x, W, y, M, static_cast<int>(N),
+                                static_cast<int>(K), static_cast<hipStream_t>(stream));
 }
 
 extern "C" int q4_gemm_verify_tiled(const void *x, const void *W, float *y,

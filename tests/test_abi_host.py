@@ -367,3 +367,16 @@ def test_binding_rejects_host_tensors(lib):
     y = torch.zeros((1, 1), dtype=torch.float32)
     with pytest.raises(ValueError):
         q4.q4_gemm_verify(x, W, y, 1, 1, 64)
+
+
+def test_dot_variant_argument_errors(lib):
+    """q4_gemm_verify_tiled_dot: M up to 4 and one part of K (K <= 6144),
+    the tiled shape rules; all checked before any device work."""
+    g = lib.q4_gemm_verify_tiled_dot
+    X, W, Y = 0x10000, 0x20000, 0x30000
+    assert g(X, W, Y, 0, 5120, 5120, None) == -1
+    assert g(X, W, Y, 5, 5120, 5120, None) == -1
+    assert g(X, W, Y, 1, 5120, 17408, None) == -1   # K beyond 24 records
+    assert g(X, W, Y, 1, 5121, 5120, None) == -1    # N % 16
+    assert g(X + 8, W, Y, 1, 5120, 5120, None) == -2
+    assert g(X, W, Y, 4, 34816, 5120, None) == -4   # valid: stops at device

@@ -651,3 +651,53 @@ def test_planar_equals_tiled_bitwise(q4, M, N, K):
     yt = gemm_tiled(q4, x, repacked(q4, W, N, K), M, N, K)
     assert torch.equal(yp.view(torch.int32), yt.view(torch.int32))
     full_check(yp, x, W, N, K, "planar==tiled")
+
+
+# -------------------------------------------------------------- VALU variant
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M,N,K", [(1, 256, 512), (4, 256, 512), (3, 48, 256),
+                                   (2, 4112, 5120), (4, 5120, 6144),
+                                   (1, 34816, 5120), (4, 34816, 5120)])
+def test_dot_variant(q4, M, N, K):
+    """The v_dot2 variant (M <= 4): every output within the oracle's bound;
+    it sums in another order than the MFMA path, so only the bound ties
+    the two."""
+    dev = torch.device("cuda")
+    W = synth.q4_weights(N, K, seed=60, device=dev)
+    x = synth.activations(M, K, seed=60, stream=1, device=dev)
+    Wt = repacked(q4, W, N, K)
+    _say(f"case dot variant: M={M} N={N} K={K}")
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
+    q4.q4_gemm_verify_tiled_dot(x, Wt, y, M, N, K)
+    torch.cuda.synchronize()
+    full_check(y, x, W, N, K, f"dot M={M} N={N} K={K}")
+
+
+@pytest.mark.gpu
+def test_dot_variant_integer_exact_and_M_invariance(q4):
+    """Integer-valued codes and activations (scale 1, bias -8): every
+    partial sum is an exact fp32 integer, so the v_dot2 path equals the
+    oracle bit for bit; rows do not depend on M."""
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(61)
+    N, K = 1024, 6144
+    q = rng.integers(0, 16, size=(N, K))
+    G = K // 64
+    codes = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    Wh = assemble(codes, bf16_bits_of(np.ones((N, G))),
+                  bf16_bits_of(np.full((N, G), -8.0)))
+    xi = rng.integers(-4, 5, size=(4, K)).astype(np.float32)
+    Wt = repacked(q4, torch.from_numpy(Wh).to(dev), N, K)
+    x = torch.from_numpy(xi).to(torch.bfloat16).to(dev)
+    _say("case dot variant integer-exact")
+    y = torch.empty((4, N), dtype=torch.float32, device=dev)
+    q4.q4_gemm_verify_tiled_dot(x, Wt, y, 4, N, K)
+    torch.cuda.synchronize()
+    y32, _, _, _ = oracle.gemm(bf16_bits_of(xi), Wh, N, K)
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), y32.view(np.uint32))
+    for M in (1, 2, 3):
+        part = torch.empty((M, N), dtype=torch.float32, device=dev)
+        q4.q4_gemm_verify_tiled_dot(x[:M].contiguous(), Wt, part, M, N, K)
+        torch.cuda.synchronize()
+        assert torch.equal(part.view(torch.int32), y[:M].view(torch.int32)), M
