@@ -1246,6 +1246,15 @@ def main():
                 torch, synth, q4, "gate_up", (1, 2, 4, 8, 16),
                 ("q4_gemm_verify_tiled", "q4_gemm_verify"), args.steps,
                 args.warmup, args.rotate_gb, dev, threads),
+            # the VALU dot-product form against MFMA where it applies
+            "gate_up_dot": measure_sweep(
+                torch, synth, q4, "gate_up", (1, 2, 4),
+                ("q4_gemm_verify_tiled_dot",), args.steps, args.warmup,
+                args.rotate_gb, dev, threads),
+            "o_proj": measure_sweep(
+                torch, synth, q4, "o_proj", (1, 2, 4),
+                ("q4_gemm_verify_tiled", "q4_gemm_verify_tiled_dot"),
+                args.steps, args.warmup, args.rotate_gb, dev, threads),
             "down": measure_sweep(
                 torch, synth, q4, "down", (1, 2, 4, 8, 16),
                 ("q4_gemm_verify_tiled", "q4_gemm_verify",
