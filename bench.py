@@ -84,8 +84,8 @@ def alg_bytes(M, N, K):
     return 9 * N * K // 16 + 2 * M * K + 4 * M * N
 
 
-def kernel_source_hash():
-    with open(KERNEL_SOURCE, "rb") as fh:
+def kernel_source_hash(path=None):
+    with open(path or KERNEL_SOURCE, "rb") as fh:
         return hashlib.sha256(fh.read()).hexdigest()
 
 
@@ -870,6 +870,8 @@ def repeat_mode(spec, copy_mb):
     import speculative_verify_gemm_q4_amd as q4
     entry, shape, M, reps = spec.split(":")
     M, reps = int(M), int(reps)
+    if entry in ("attn", "fused"):
+        return repeat_other(entry, shape, M, reps)
     entry = {"planar": "q4_gemm_verify", "tiled": "q4_gemm_verify_tiled",
              "ws": "q4_gemm_verify_tiled_ws",
              "dot": "q4_gemm_verify_tiled_dot"}.get(entry, entry)
@@ -915,6 +917,70 @@ def repeat_mode(spec, copy_mb):
         r = parity(torch, synth, x, y, Ws[0].cpu().numpy(), N, K,
                    min(16, len(os.sched_getaffinity(0))))
         print(f"parity max err/bound {r:.3g}", flush=True)
+    print(f"done {entry} {shape} M={M} reps={reps}", flush=True)
+
+
+def repeat_other(entry, shape, M, reps):
+    """Profiling aid for the steps beside the GEMM: `attn:CTX:M:REPS` runs
+    the tree-verify attention layer of measure_tree_attn at CTX tokens of
+    context (two caches rotated), `fused:lm_head:16:REPS` the LM head with
+    the sampling epilogue fused in (rotated weights), REPS prepared calls
+    each after 0.1 s of warm-up."""
+    import ctypes
+    import functools
+    import torch
+    import synth
+    import speculative_verify_gemm_q4_amd as q4
+    dev = torch.device("cuda:0")
+    lib = q4.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    if entry == "attn":
+        g = ATTN_SHAPE
+        Hq, Hkv, D = g["query_heads"], g["kv_heads"], g["head_dim"]
+        ctx = int(shape)
+        caches = [synth.attn_inputs(M, Hq, Hkv, ctx, seed=0, stream=i,
+                                    device=dev) for i in range(2)]
+        _, nws = q4.q4_tree_attn_plan(M, Hq, Hkv, ctx)
+        o = torch.empty((M, Hq, D), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+        fns = [functools.partial(
+            lib.q4_tree_attn, c["q"].data_ptr(), M, Hq, Hkv, D,
+            c["k_pages"].data_ptr(), c["v_pages"].data_ptr(),
+            c["k_scale"].data_ptr(), c["v_scale"].data_ptr(),
+            c["page_table"].data_ptr(), int(c["k_pages"].shape[0]), ctx,
+            c["anc"].data_ptr(), 1.0 / 16.0, o.data_ptr(), 0, ws.data_ptr(),
+            ws.numel(), None, stream) for c in caches]
+    else:
+        from speculative_verify_gemm_q4_amd._lib import _SampleParams
+        V, K = WORKLOADS[shape]
+        Wts = rotated_tiled(torch, synth, q4, V, K, 1.2, 9000, dev)
+        x = synth.activations(M, K, seed=0, stream=300, device=dev)
+        inp = synth.sample_inputs(M, V, 16, seed=0, device=dev)
+        out = {k: torch.empty(s, dtype=t, device=dev) for k, s, t in (
+            ("top_idx", (M, 20), torch.int32), ("top_val", (M, 20), torch.float32),
+            ("top_prob", (M, 20), torch.float32), ("greedy", (M,), torch.int32),
+            ("accept", (M,), torch.int32), ("token", (M,), torch.int32))}
+        prm = _SampleParams(1.0, 0.95, 20, 16)
+        fws = torch.empty(q4.q4_gemm_verify_sample_workspace(M, V, K),
+                          dtype=torch.uint8, device=dev)
+        fns = [functools.partial(
+            lib.q4_gemm_verify_sample, x.data_ptr(), Wt.data_ptr(), M, V, K,
+            ctypes.byref(prm), *[inp[k].data_ptr() for k in (
+                "draft_tok", "draft_idx", "draft_q", "u", "v")],
+            *[out[k].data_ptr() for k in (
+                "top_idx", "top_val", "top_prob", "greedy", "accept", "token")],
+            fws.data_ptr(), fws.numel(), stream) for Wt in Wts]
+    if any(f() != 0 for f in fns):
+        raise RuntimeError(f"{entry} failed")
+    t0, i = time.perf_counter(), 0
+    while time.perf_counter() - t0 < 0.1:
+        for _ in range(10):
+            fns[i % len(fns)]()
+            i += 1
+        torch.cuda.synchronize()
+    for i in range(reps):
+        fns[i % len(fns)]()
+    torch.cuda.synchronize()
     print(f"done {entry} {shape} M={M} reps={reps}", flush=True)
 
 
@@ -1016,12 +1082,21 @@ def summarize_pmc(dirs, kernel, title, cmds, duration_us, spec, copy_mb):
     print(f"# derived figures use {SIMDS} SIMDs, {CLOCK_GHZ} GHz and the "
           "kernel-trace median duration per dispatch")
     entry, shape, M, _ = spec.split(":")
-    N, K = WORKLOADS[shape]
     M = int(M)
+    if entry == "attn":
+        g = ATTN_SHAPE
+        ab = attn_alg_bytes(M, g["query_heads"], g["kv_heads"], g["head_dim"],
+                            int(shape))
+        N = K = None
+    else:
+        N, K = WORKLOADS[shape]
+        ab = alg_bytes(M, N, K)
     out = {"entry": entry, "shape": shape, "N": N, "K": K, "M": M,
            "kernel_filter": kernel, "duration_us": duration_us,
-           "alg_bytes_per_dispatch": alg_bytes(M, N, K),
-           "kernel_source_sha256": kernel_source_hash(), "kernels": {}}
+           "alg_bytes_per_dispatch": ab,
+           "kernel_source_sha256": kernel_source_hash(
+               os.path.join(os.path.dirname(KERNEL_SOURCE), "q4verify_attn.hip")
+               if entry == "attn" else None), "kernels": {}}
     fscale = wscale = None
     if copy_mb and copy.get("FETCH_SIZE") and copy.get("WRITE_SIZE"):
         kib = copy_mb * 1024.0
