@@ -105,6 +105,9 @@ int launch_sample_rows(const uint64_t *cand, int M, int S,
 // row; a workgroup holds at most kSampleMaxTiles tiles (1024 logits of each
 // row) in LDS.
 constexpr int kSampleTop = 32;
+// Lists per row that the row kernel merges (workgroups of the fused GEMM,
+// slices of the standalone epilogue).
+constexpr int kSampleMaxLists = 512;
 constexpr int kSampleMaxTiles = 64;
 constexpr int kSampleMaxCols = kSampleMaxTiles * 16;
 constexpr int kSampleLgStride = kSampleMaxCols;  // floats per row in LDS

@@ -22,11 +22,14 @@
 //     reversed form a bitonic sequence that one half-cleaner cascade sorts)
 //     and the slice's best 32 written out.  Every compare-exchange stage
 //     swaps lanes with DPP or the gfx950 permlane swaps, not through LDS.
-//  2. sample_rows_kernel: one workgroup per row merges the slices' lists the
-//     same way and writes the top_k candidates; then lane i of wave 0 takes
-//     candidate i and the probabilities, the accept test and the residual
-//     draw are evaluated in fp32 with wave reductions, lane scans and
-//     ballots over the candidates in order.
+//  2. sample_rows_kernel: one wave per row.  Each list is descending, so
+//     its head bounds the rest of it: the row's 32nd largest head bounds
+//     the row's 32nd best key from below, and only the (at most 32) lists
+//     whose heads reach it are read whole; their keys at or above it are
+//     ranked into the top_k candidates.  Lane i then takes candidate i, and
+//     the probabilities, the accept test and the residual draw are
+//     evaluated in fp32 with wave reductions, lane scans and ballots over
+//     the candidates in order.
 
 #include <hip/hip_runtime.h>
 
@@ -66,12 +69,12 @@ __device__ __forceinline__ float lane_scan(float x) {
 constexpr int kWaves = 16;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kColsPerThread = kSliceCols / kThreads;  // 16
-// survivor pool of a workgroup: every key it holds (kernel 1: its slice;
-// the row kernel: the 32 candidates of each of up to 512 slices)
+// survivor pool of kernel 1: every key of its slice
 constexpr int kPoolKeys = kColsPerThread * kThreads;
 static_assert(static_cast<int64_t>(Q4_SAMPLE_MAX_VOCAB) <=
-                  static_cast<int64_t>(kPoolKeys / kTopMax) * kSliceCols,
-              "the row kernel's pool holds every slice's candidates");
+                  static_cast<int64_t>(kSampleMaxLists) * kSliceCols,
+              "the row kernel reads at most kSampleMaxLists lists a row");
+static_assert(kTopMax == kSampleTop, "one list length");
 
 // Lanes 0..31: a descending list; merge the descending list `other` (lanes
 // 0..31, read through get(i)) into it: the list and the other list reversed
@@ -158,7 +161,7 @@ __device__ __forceinline__ uint64_t block_best32(ForEach for_each, uint64_t *poo
 __global__ __launch_bounds__(kThreads) void topk_slices_kernel(
     const float *__restrict__ logits, int64_t V, int S,
     uint64_t *__restrict__ cand) {
-  __shared__ uint64_t pool[kColsPerThread * kThreads];
+  __shared__ uint64_t pool[kPoolKeys];
   __shared__ SelectLds sh;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -187,14 +190,29 @@ struct SampleArgs {
   int top_k, draft_k;
 };
 
-// Kernel 2: workgroup m merges row m's S lists, then wave 0 samples.
-// Selection: every thread holds its keys of the row in registers (at most
-// 16: S <= 512 lists of 32).  The 32nd largest of the 1024 thread maxima
-// (each wave sorts its lane maxima, the waves' lists are merged pairwise)
-// bounds the row's 32nd best key from below, as 32 distinct keys reach it;
-// the keys at or above it are packed into LDS wave by wave and wave 0 ranks
-// their best 32.
-__global__ __launch_bounds__(kThreads) void sample_rows_kernel(
+// Wave-wide order of the wave's LDS accesses: earlier writes by any lane
+// are seen by later reads of any lane.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+constexpr int kListsPerLane = kSampleMaxLists / 64;
+constexpr int kLead = 4;  // keys read first from every list
+
+// Kernel 2: one wave per row m merges the row's S lists, then samples.
+// Every list is descending, so its first key (its head) is its largest.
+// Lane l reads the first 4 keys of lists l, l + 64, ..  T = the 32nd
+// largest lane maximum of the heads: 32 distinct heads reach it, so the
+// row's 32nd best key does too, and every key of the row's best 32 is
+// >= T.  The keys read that are >= T are kept (usually 40 to 60; at most
+// 32 lanes x 8 lists x 4).  A key of the best 32 past a list's first 4
+// needs that list's 4th key >= T; when some list has one, T is raised to
+// the 32nd best kept key (again a lower bound of the row's 32nd best, now
+// with at most 8 lists, or all S < 32, whose 4th key reaches it) and those
+// lists are read whole.  The best 32 kept keys are the row's best 32.
+__global__ __launch_bounds__(64) void sample_rows_kernel(
     const uint64_t *__restrict__ cand, int S, SampleArgs a,
     const int32_t *__restrict__ draft_tok, const int32_t *__restrict__ draft_idx,
     const float *__restrict__ draft_q, const float *__restrict__ u,
@@ -202,68 +220,78 @@ __global__ __launch_bounds__(kThreads) void sample_rows_kernel(
     float *__restrict__ top_val, float *__restrict__ top_prob,
     int32_t *__restrict__ greedy, int32_t *__restrict__ accept,
     int32_t *__restrict__ token) {
-  constexpr int kPer = kPoolKeys / kThreads;  // keys per thread, at most
-  __shared__ uint64_t pool[kPoolKeys + kWaves];  // + a dummy slot per wave
-  __shared__ uint64_t lists[kWaves][kTopMax];
+  // kept keys: the first 4 of at most 32 x 8 lists, the other 28 of at
+  // most 31 lists read whole, + 8 slots for the ranking
+  constexpr int kPool = kTopMax * kListsPerLane * kLead + (kTopMax - 1) * (kTopMax - kLead);
+  __shared__ uint64_t pool[kPool + 8];
+  __shared__ uint64_t sel[kTopMax];  // the lists read whole
   __shared__ uint64_t best[kTopMax];
-  __shared__ uint32_t wcount[kWaves];
-  __shared__ uint64_t bound;
+  __shared__ uint64_t dummy;
   __shared__ float val[kTopMax], qc[kTopMax];
   __shared__ int32_t tok[kTopMax];
   __shared__ int32_t sdi[kDraftMax];
   __shared__ float sdq[kDraftMax];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x;
   const int m = blockIdx.x;
   const uint64_t *rc = cand + static_cast<uint64_t>(m) * S * kTopMax;
-  const int nk = S * kTopMax;
-  uint64_t key[kPer];
+  uint64_t lead[kListsPerLane][kLead];
   uint64_t mx = 0;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int e = i * kThreads + static_cast<int>(threadIdx.x);
-    key[i] = e < nk ? rc[e] : 0;
-    mx = key[i] > mx ? key[i] : mx;
+  for (int i = 0; i < kListsPerLane; ++i) {
+    const int g = i * 64 + lane;
+#pragma unroll
+    for (int j = 0; j < kLead; ++j)
+      lead[i][j] = g < S ? rc[static_cast<uint64_t>(g) * kTopMax + j] : 0;
+    mx = lead[i][0] > mx ? lead[i][0] : mx;
   }
-  const uint64_t tl = block_merge(sort64_desc(mx, lane), lists, wave, lane);
-  if (threadIdx.x == kTopMax - 1) bound = tl;
-  __syncthreads();
-  const uint64_t T = bound;
-  uint32_t cnt = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i)
-    cnt += static_cast<uint32_t>(
-        __builtin_popcountll(__ballot(key[i] != 0 && key[i] >= T)));
-  if (lane == 0) wcount[wave] = cnt;
-  __syncthreads();
-  uint32_t base = 0, n = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    base += w < wave ? wcount[w] : 0u;
-    n += wcount[w];
-  }
-#pragma unroll
-  for (int i = 0; i < kPer; ++i)
-    wave_append(key[i], key[i] != 0 && key[i] >= T, pool, &base,
-                pool + kPoolKeys + wave);
-  __syncthreads();
-  if (wave != 0) return;
-  wave_top32(pool, n, best, lane);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const uint64_t list = lane < kTopMax ? best[lane] : 0;
-  const int k = a.top_k;
-  // the row's draft list, one entry per lane, then q of every candidate
+  // the row's draft list and scalars, loaded while the lists arrive
   if (lane < a.draft_k) {
     sdi[lane] = draft_idx[m * a.draft_k + lane];
     sdq[lane] = draft_q[m * a.draft_k + lane];
   }
   const int32_t d = draft_tok[m];
   const float um = u[m], vm = v[m];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  uint64_t T = wave_kth_largest(mx, kTopMax);
+  uint32_t n = 0;
+  bool deep = false;  // some list's 4th key reaches T
+#pragma unroll
+  for (int i = 0; i < kListsPerLane; ++i) {
+    if (i * 64 >= S) break;  // wave-uniform
+#pragma unroll
+    for (int j = 0; j < kLead; ++j) {
+      const bool keep = lead[i][j] != 0 && lead[i][j] >= T;
+      if (__ballot(keep) != 0) wave_append(lead[i][j], keep, pool, &n, &dummy);
+      if (j == kLead - 1) deep = deep || keep;
+    }
+  }
+  wave_sync();
+  if (__ballot(deep) != 0) {
+    // raise T to the 32nd best kept key; the lists whose 4th key reaches it
+    // are read whole: lane l takes key l & 31 (past the first 4) of lists
+    // l >> 5, (l >> 5) + 2, ..
+    wave_top32(pool, n, best, lane);
+    wave_sync();
+    T = n >= kTopMax ? best[kTopMax - 1] : 0;
+    uint32_t ns = 0;
+#pragma unroll
+    for (int i = 0; i < kListsPerLane; ++i) {
+      const bool whole = lead[i][kLead - 1] != 0 && lead[i][kLead - 1] >= T;
+      wave_append(static_cast<uint64_t>(i * 64 + lane), whole, sel, &ns, &dummy);
+    }
+    wave_sync();
+    for (uint32_t l0 = 0; l0 < ns; l0 += 2) {
+      const uint32_t li = l0 + static_cast<uint32_t>(lane >> 5);
+      const bool past = (lane & 31) >= kLead;
+      const uint64_t key = li < ns && past ? rc[sel[li] * kTopMax + (lane & 31)] : 0;
+      wave_append(key, key != 0 && key >= T, pool, &n, &dummy);
+    }
+    wave_sync();
+  }
+  wave_top32(pool, n, best, lane);
+  wave_sync();
+  const uint64_t list = lane < kTopMax ? best[lane] : 0;
+  const int k = a.top_k;
+  // q of every candidate from the row's draft list
   if (lane < k) {
     val[lane] = key_value(list);
     tok[lane] = static_cast<int32_t>(key_token(list));
@@ -359,8 +387,9 @@ int launch_sample_rows(const uint64_t *cand, int M, int S,
                        const float *u, const float *v, int32_t *top_idx,
                        float *top_val, float *top_prob, int32_t *greedy,
                        int32_t *accept, int32_t *token, hipStream_t s) {
+  if (S < 1 || S > kSampleMaxLists) return Q4_EINVAL;
   const SampleArgs a{p.temperature, p.top_p, p.top_k, p.draft_k};
-  hipLaunchKernelGGL(sample_rows_kernel, dim3(M), dim3(64 * kWaves), 0, s,
+  hipLaunchKernelGGL(sample_rows_kernel, dim3(M), dim3(64), 0, s,
                      cand, S, a, draft_tok, draft_idx, draft_q, u, v, top_idx,
                      top_val, top_prob, greedy, accept, token);
   return hipGetLastError() == hipSuccess ? Q4_OK : Q4_ELAUNCH;

@@ -188,6 +188,25 @@ def test_deterministic(q4):
         assert torch.equal(a[n].view(torch.int32), b[n].view(torch.int32)), n
 
 
+def test_row_merge_structures(q4):
+    """37 slices of about 16216 columns (more lists than candidates), with
+    the best 32 all in one slice, one per slice near its start, after two
+    slices' second keys, in a row of equal logits and all in the last
+    slice: the row kernel reads only the lists whose heads reach the 32nd
+    largest head."""
+    dev = torch.device("cuda")
+    V = 600000
+    gen = torch.Generator(device=dev).manual_seed(16)
+    logits = torch.randn((5, V), generator=gen, device=dev)
+    logits[0, 300000:300040] = 10.0 + torch.arange(40, device=dev) * 0.01
+    logits[1, ::16384] = 8.0 + torch.arange(37, device=dev) * 0.01
+    logits[2, [5, 6, 20000, 20001]] = torch.tensor([9.0, 8.9, 9.05, 8.95],
+                                                   device=dev)
+    logits[3] = 1.5
+    logits[4, V - 40:] = 6.0 - torch.arange(40, device=dev) * 0.01
+    run_and_check(q4, logits, 1.0, 0.9, 32, 8, 17, "row merge")
+
+
 def test_after_lm_head_gemm(q4):
     """The verify step end to end: the LM head (248320 x 5120 Q4, 16 verify
     rows) on the resident-activation kernel, then the sampling epilogue on
