@@ -11,11 +11,13 @@
 // position ctx_len + j.
 //
 // Kernel 1 (tree_attn_kernel<G>): a workgroup per (KV head, run of pages),
-// one wave per query head of that KV head (G = Hq / Hkv waves).
-//  * Per page the workgroup loads the 8 KiB of keys ([32 tokens][256]) and
-//    8 KiB of values (stored transposed, [256][32]) with their scales, turns
-//    the int8 values into bf16 (exact: |v| <= 128) and writes them to LDS;
-//    the next page's loads are in flight meanwhile (two LDS buffers).
+// one compute wave per query head of that KV head (G = Hq / Hkv) and two
+// loader waves.
+//  * Per page the loader waves load the 8 KiB of keys ([32 tokens][256])
+//    and 8 KiB of values (stored transposed, [256][32]) with their scales
+//    into their registers, four pages ahead, turn the int8 values into bf16
+//    (exact: |v| <= 128) and write them to an LDS tile (two tiles: the
+//    compute waves read one page while the next is written).
 //  * Scores on MFMA: S^T[token][node] = K Q^T, sixteen
 //    v_mfma_f32_16x16x32_bf16 per page and wave (two token tiles, eight
 //    32-dim steps), the key scale and the softmax scale applied per token
@@ -35,6 +37,8 @@
 // results are merged with their max and sum.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "q4v_internal.h"
 
 namespace q4v {
@@ -52,7 +56,11 @@ constexpr int kKStride = 2 * kD + 16;      // bytes per token row of bf16 keys
 constexpr int kVStride = 2 * kPage + 16;   // bytes per dim row of bf16 values
 constexpr int kKBytes = kPage * kKStride;  // 16896
 constexpr int kVBytes = kD * kVStride;     // 20480
-constexpr int kBufBytes = kKBytes + kVBytes + 2 * kPage * 4;
+// the scales: 32 key scales, then 32 value scales, each in a 1 KiB area
+// that a whole wave's 16-byte writes fill (lanes 8..63 write the zeros they
+// loaded past the scales), so that the write needs no branch on the lane
+constexpr int kScaleArea = 64 * 16;
+constexpr int kBufBytes = kKBytes + kVBytes + 2 * kScaleArea;
 constexpr uint32_t kBufferWord3 = 0x00020000u;
 constexpr float kLog2e = 1.4426950408889634f;
 // Headroom of the running maximum in the online softmax (base 2).
@@ -103,140 +111,81 @@ __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
                                                  c, 0, 0, 0);
 }
 
-// Raw int8 page in LDS, as the direct-to-LDS copies leave it: keys
-// [32][256], values [256][32], then the 32 key and the 32 value scales, each
-// in a 256-byte area (a scale copy is a whole wave: lanes 32..63 read past
-// the 32 scales and land zeros in the area's second half).
-constexpr int kRawV = kPage * kD;
-constexpr int kRawKS = 2 * kPage * kD;
-constexpr int kRawVS = kRawKS + 256;
-constexpr int kRawBytes = kRawVS + 256;  // 16896
-// Copy instructions per page: 8 of keys and 8 of values (1 KiB each, 64
-// lanes x 16 bytes), one of key scales and one of value scales (32 lanes x
-// 4 bytes); wave w issues instructions w, w + G, w + 2G, ..., and every wave
-// issues the same number per page (past the 18, and for pages past the
-// run, a dummy copy into a pad area), so that one vmcnt value fits every
-// wave.
+// A page of one KV head is loaded in 18 parts: 8 of keys and 8 of values
+// (1 KiB each: 64 lanes x 16 bytes), one of the 32 key scales and one of
+// the 32 value scales (8 lanes x 16 bytes).  Loader wave h of H takes parts
+// h, h + H, .. into its own registers, and every loader issues the same
+// number of loads per page (past the 18, and for pages past the run, a
+// load whose data is not used), so that the loads of four pages stay in
+// flight in every loader alike.
 constexpr int kCopies = 18;
-constexpr int kRing = 4;          // raw pages in flight per workgroup
+constexpr int kRing = 4;          // pages in flight per workgroup
+constexpr int kLoaders = 2;       // loader waves per workgroup
 constexpr int kMaxRun = 1024;     // pages per workgroup (ids staged in LDS)
-constexpr int kPadBytes = 1024;
-
-typedef __attribute__((address_space(3))) char lds_char;
-
-// The LDS address of a pointer into a __shared__ array (a C-style cast: the
-// generic-to-LDS address-space cast has no C++ cast spelling).
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_char *)p));
-}
-
-// A buffer resource as four SGPRs (raw, dword format).
-__device__ __forceinline__ u32x4 srd(const void *p, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(p);
-  return u32x4{static_cast<uint32_t>(
-                   __builtin_amdgcn_readfirstlane(static_cast<int>(a))),
-               static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
-                   static_cast<int>((a >> 32) & 0xFFFFu))),
-               static_cast<uint32_t>(
-                   __builtin_amdgcn_readfirstlane(static_cast<int>(bytes))),
-               kBufferWord3};
-}
-
-// Direct-to-LDS copies, written as assembly so that the compiler does not
-// treat them as LDS writes of unknown extent (which would make it wait for
-// every copy in flight before any LDS access): the kernel counts them
-// itself.  Lane l's bytes land at the LDS address `dst` + l * size.  M0 is
-// saved and restored around the copy.
-__device__ __forceinline__ void copy16(u32x4 rs, uint32_t dst, uint32_t voff) {
-  uint32_t keep;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(keep)
-      : "s"(dst), "v"(voff), "s"(rs)
-      : "memory");
-}
-
-__device__ __forceinline__ void copy4(u32x4 rs, uint32_t dst, uint32_t voff) {
-  uint32_t keep;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dword %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(keep)
-      : "s"(dst), "v"(voff), "s"(rs)
-      : "memory");
-}
-
-// wait until at most n of this wave's vector memory operations are in flight
-template <int n>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(n >= 0 && n < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt((n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14));
-  asm volatile("" ::: "memory");
-}
 
 // A workgroup barrier for LDS only: this wave's LDS accesses are complete,
-// then s_barrier; the copies still in flight (those of later pages) are not
-// waited for.
+// then s_barrier; the loads of later pages still in flight are not waited
+// for (__syncthreads would wait for them too).
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));  // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-template <int G>
-struct Pages {
-  static constexpr int NI = (kCopies + G - 1) / G;  // copies per wave and page
+// wait until none of this wave's vector memory operations is in flight
+__device__ __forceinline__ void wait_vm0() {
+  __builtin_amdgcn_s_waitcnt(0x0 | (0x7 << 4) | (0xF << 8) | (0x0 << 14));
+  asm volatile("" ::: "memory");
+}
 
-  // page pp (of KV head g) into a raw slot, or, for real == false, NI dummy
-  // copies (of page `dummy`) into the pad; a page id outside the pool reads
-  // as zeros
-  __device__ __forceinline__ static void copy(const AttnArgs &a, int pp,
+template <int H>
+struct Pages {
+  static constexpr int NI = (kCopies + H - 1) / H;  // loads per wave and page
+
+  // this wave's parts of a page, as loaded
+  struct Stage {
+    u32x4 d[NI];
+  };
+
+  // page pp (of KV head g) into st, or, for real == false, loads of page
+  // `dummy` whose data is never used; a page id outside the pool reads as
+  // zeros (the buffer's size is then 0).  One 16-byte load per part, with
+  // no branch (the part's source is selected), so that the compiler's wait
+  // before a conversion counts exactly the loads issued after it.  A scale
+  // part is 128 bytes: lanes 0..7 get 4 scales each, the rest zeros.
+  template <int h>
+  __device__ __forceinline__ static void load(const AttnArgs &a, int pp,
                                               bool real, int dummy, int g,
-                                              const char *slot,
-                                              const char *pad, int w,
-                                              int lane) {
+                                              Stage &st, int lane) {
     const int id = real ? pp : dummy;
     const bool ok = id >= 0 && id < a.pool;
     const size_t pg = ok ? static_cast<size_t>(id) * a.Hkv + g : 0;
-    const uint32_t bytes = ok ? kPage * kD : 0;
-    const u32x4 rk = srd(a.kp + pg * kPage * kD, bytes);
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      const int e = w + G * j;  // wave-uniform
-      if (!real || e >= kCopies) {
-        copy16(rk, lds_addr(pad), 16 * lane);
-      } else if (e < 8) {
-        copy16(rk, lds_addr(slot + 1024 * e), 1024 * e + 16 * lane);
-      } else if (e < 16) {
-        copy16(srd(a.vp + pg * kPage * kD, bytes),
-               lds_addr(slot + kRawV + 1024 * (e - 8)),
-               1024 * (e - 8) + 16 * lane);
-      } else {
-        const float *src = (e == 16 ? a.ks : a.vs) + pg * kPage;
-        copy4(srd(src, ok ? kPage * 4 : 0),
-              lds_addr(slot + (e == 16 ? kRawKS : kRawVS)), 4 * lane);
-      }
+      const int e0 = h + H * j;  // a constant once unrolled
+      const int e = real && e0 < kCopies ? e0 : 0;
+      const char *base =
+          e < 8    ? reinterpret_cast<const char *>(a.kp + pg * kPage * kD)
+          : e < 16 ? reinterpret_cast<const char *>(a.vp + pg * kPage * kD)
+          : reinterpret_cast<const char *>((e == 16 ? a.ks : a.vs) + pg * kPage);
+      const uint32_t bytes = !ok ? 0 : e < 16 ? kPage * kD : kPage * 4;
+      const uint32_t off = (e < 16 ? 1024 * (e & 7) : 0) + 16 * lane;
+      st.d[j] = load16(rsrc(base, bytes), off);
     }
   }
-  // the same wave's copies turned into bf16 tiles: keys [token][dim] (row
+  // the same wave's parts turned into bf16 tiles: keys [token][dim] (row
   // stride kKStride), values [dim][slot] (row stride kVStride) with token
   // 4g+e of the low half at slot 8g+e and token 16+4g+e at slot 8g+4+e, then
   // the fp32 key and value scales
-  __device__ __forceinline__ static void convert(const char *slot, char *buf,
-                                                 int w, int lane) {
+  template <int h>
+  __device__ __forceinline__ static void convert(const Stage &st, char *buf,
+                                                 int lane) {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      const int e = w + G * j;
+      const int e = h + H * j;  // a constant once unrolled
+      const u32x4 v = st.d[j];
       if (e < 8) {
         const int c = 64 * e + lane;  // token c / 16, dims 16 (c % 16) ..
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(slot + 16 * c);
         const int tok = c >> 4, d0 = 16 * (c & 15);
         const u32x2 w0 = i8x4_bf16(v.x), w1 = i8x4_bf16(v.y);
         const u32x2 w2 = i8x4_bf16(v.z), w3 = i8x4_bf16(v.w);
@@ -245,7 +194,6 @@ struct Pages {
         dst[1] = u32x4{w2.x, w2.y, w3.x, w3.y};
       } else if (e < 16) {
         const int f = 64 * (e - 8) + lane;  // dim f / 2, tokens 16 (f % 2) ..
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(slot + kRawV + 16 * f);
         char *row = buf + kKBytes + (f >> 1) * kVStride + 8 * (f & 1);
         // tokens 16 h + 4 i .. +3 -> slots 8 i + 4 h .. +3
         *reinterpret_cast<u32x2 *>(row + 0) = i8x4_bf16(v.x);
@@ -253,24 +201,16 @@ struct Pages {
         *reinterpret_cast<u32x2 *>(row + 32) = i8x4_bf16(v.z);
         *reinterpret_cast<u32x2 *>(row + 48) = i8x4_bf16(v.w);
       } else if (e < kCopies) {
-        if (lane < kPage)
-          *reinterpret_cast<float *>(buf + kKBytes + kVBytes +
-                                     (e == 16 ? 0 : kPage * 4) + 4 * lane) =
-              *reinterpret_cast<const float *>(
-                  slot + (e == 16 ? kRawKS : kRawVS) + 4 * lane);
+        *reinterpret_cast<u32x4 *>(buf + kKBytes + kVBytes +
+                                   (e == 16 ? 0 : kScaleArea) + 16 * lane) = v;
       }
     }
   }
 };
 
 template <int G>
-__global__ __launch_bounds__(64 * G) void tree_attn_kernel(AttnArgs a) {
-  using P = Pages<G>;
-  __shared__ __attribute__((aligned(16))) char raw0[kRawBytes];
-  __shared__ __attribute__((aligned(16))) char raw1[kRawBytes];
-  __shared__ __attribute__((aligned(16))) char raw2[kRawBytes];
-  __shared__ __attribute__((aligned(16))) char raw3[kRawBytes];
-  __shared__ __attribute__((aligned(16))) char pad[kPadBytes];
+__global__ __launch_bounds__(64 * (G + kLoaders)) void tree_attn_kernel(AttnArgs a) {
+  using P = Pages<kLoaders>;
   __shared__ __attribute__((aligned(16))) char tile0[kBufBytes];
   __shared__ __attribute__((aligned(16))) char tile1[kBufBytes];
   __shared__ int ids[kMaxRun];
@@ -281,7 +221,7 @@ __global__ __launch_bounds__(64 * G) void tree_attn_kernel(AttnArgs a) {
   const int gq = lane >> 4;  // lane group: k slots 8 gq .. 8 gq + 7
   const int g = blockIdx.x % a.Hkv;
   const int run = blockIdx.x / a.Hkv;
-  const int hq = g * G + w;
+  const int hq = g * G + (w < G ? w : 0);  // (loader waves: unused)
   const int pa = static_cast<int>(static_cast<int64_t>(a.pages) * run / a.splits);
   const int pb = static_cast<int>(static_cast<int64_t>(a.pages) * (run + 1) / a.splits);
   const int len = pb - pa;  // 1 .. kMaxRun (the plan sees to it)
@@ -297,7 +237,7 @@ __global__ __launch_bounds__(64 * G) void tree_attn_kernel(AttnArgs a) {
   const uint32_t anc = n < a.M ? a.anc[n] : 0u;
   // the run's page ids, staged in LDS before any copy is issued
   bool bad_page = false;
-  for (int i = tid; i < len; i += 64 * G) {
+  for (int i = tid; i < len; i += 64 * (G + kLoaders)) {
     const int pp = a.page_table[pa + i];
     ids[i] = pp;
     bad_page |= pp < 0 || pp >= a.pool;
@@ -327,7 +267,7 @@ __global__ __launch_bounds__(64 * G) void tree_attn_kernel(AttnArgs a) {
       }
     }
     const float *kscale = reinterpret_cast<const float *>(buf + kKBytes + kVBytes);
-    const float *vscale = kscale + kPage;
+    const float *vscale = kscale + kScaleArea / 4;
     float p[8], vsc[8];
     const int pos0 = kPage * lp;
     const bool all_visible = pos0 + kPage <= a.ctx;  // uniform
@@ -400,46 +340,74 @@ __global__ __launch_bounds__(64 * G) void tree_attn_kernel(AttnArgs a) {
     }
   };
 
-  // Page i of the run lives in raw slot i % 4 and tile i % 2.  Step i:
-  // compute page i; wait for this wave's copies of page i + 1 (pages i + 2
-  // and i + 3 may still be in flight: 2 NI copies) and turn them into its
-  // tile; copy page i + 4 (or dummies) into the slot page i has left; one
-  // barrier.  A wave converts exactly the bytes its own copies brought, so
-  // only the tile needs the barrier.
-  constexpr int NI = P::NI;
-  const int first = page_of(0);
-  auto copy_page = [&](int i, const char *slot) {
-    const bool real = i < len;
-    P::copy(a, real ? page_of(i) : first, real, first, g, slot, pad, w, lane);
-  };
-  // the queries and the ancestor sets are in registers before the first
-  // copy, so that no later wait of the compiler's own counts the copies
-  wait_vm<0>();
-  copy_page(0, raw0);
-  copy_page(1, raw1);
-  copy_page(2, raw2);
-  copy_page(3, raw3);
-  wait_vm<3 * NI>();
-  P::convert(raw0, tile0, w, lane);
-  lds_barrier();
-  auto step = [&](int i, const char *slot, const char *next_slot, char *tile,
-                  char *next_tile) {
-    compute_page(tile, pa + i);
-    wait_vm<2 * NI>();
-    if (i + 1 < len) P::convert(next_slot, next_tile, w, lane);
-    copy_page(i + kRing, slot);
-    lds_barrier();
-  };
-  for (int i = 0; i < len; i += kRing) {
-    step(i, raw0, raw1, tile0, tile1);
-    if (i + 1 >= len) break;
-    step(i + 1, raw1, raw2, tile1, tile0);
-    if (i + 2 >= len) break;
-    step(i + 2, raw2, raw3, tile0, tile1);
-    if (i + 3 >= len) break;
-    step(i + 3, raw3, raw0, tile1, tile0);
+  // Waves G and G + 1 load the pages and turn them into bf16 tiles; waves
+  // 0 .. G - 1 (one per query head) only compute, so that the compute units'
+  // MFMA work is not held up by conversions.  Page i of the run is loaded
+  // into stage i % 4 (a loader's registers) and turned into tile i % 2.
+  // Step i: the loaders turn their parts of page i + 1 into its tile (the
+  // loads of pages i + 2 .. i + 4 stay in flight: the compiler's wait
+  // before the conversion counts them) and load page i + 5 (or unused
+  // data) into the stage just freed, while the compute waves compute page
+  // i; then one barrier of all waves: tile i % 2 is free for page i + 2 and
+  // tile (i + 1) % 2 complete.
+  if (w >= G) {
+    // the loader's index as a constant: its parts (and so every branch on
+    // them) are known at compile time
+    auto loader = [&](auto hc) {
+      constexpr int h = decltype(hc)::value;
+      using Stage = typename P::Stage;
+      const int first = page_of(0);
+      auto load_page = [&](int i, Stage &st) {
+        const bool real = i < len;
+        P::template load<h>(a, real ? page_of(i) : first, real, first, g, st, lane);
+      };
+      Stage st0, st1, st2, st3;
+      load_page(0, st0);
+      load_page(1, st1);
+      load_page(2, st2);
+      load_page(3, st3);
+      P::template convert<h>(st0, tile0, lane);
+      load_page(kRing, st0);
+      lds_barrier();
+      // A stage is reloaded right after its conversion, so that its
+      // registers are never free between the two (a temporary there would
+      // make the compiler wait for every load in flight).  Past the run the
+      // conversion writes unused data into a tile no wave reads any more.
+      auto step = [&](int i, Stage &st, char *tile) {
+        P::template convert<h>(st, tile, lane);
+        load_page(i + 1 + kRing, st);
+        lds_barrier();
+      };
+      // whole rounds of four steps with no exit inside (an exit would make
+      // the compiler's waits at the loop's head drain the loads), then the
+      // last steps
+      int i = 0;
+      for (; i + kRing <= len; i += kRing) {
+        step(i, st1, tile1);
+        step(i + 1, st2, tile0);
+        step(i + 2, st3, tile1);
+        step(i + 3, st0, tile0);
+      }
+      if (i < len) step(i, st1, tile1);
+      if (i + 1 < len) step(i + 1, st2, tile0);
+      if (i + 2 < len) step(i + 2, st3, tile1);
+      wait_vm0();  // the unused loads past the run too
+    };
+    static_assert(kLoaders == 2, "two loader instantiations");
+    if (w == G)
+      loader(std::integral_constant<int, 0>{});
+    else
+      loader(std::integral_constant<int, 1>{});
+    return;
   }
-  wait_vm<0>();  // no copy may land after the workgroup has left its LDS
+  lds_barrier();  // page 0 is in tile 0
+  for (int i = 0; i < len; i += 2) {
+    compute_page(tile0, pa + i);
+    lds_barrier();
+    if (i + 1 >= len) break;
+    compute_page(tile1, pa + i + 1);
+    lds_barrier();
+  }
 
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
@@ -606,16 +574,16 @@ extern "C" int q4_tree_attn(const void *q, int M, int Hq, int Hkv, int D,
   const dim3 grid(static_cast<uint32_t>(s * Hkv));
   switch (Hq / Hkv) {
     case 2:
-      hipLaunchKernelGGL(q4v::tree_attn_kernel<2>, grid, dim3(128), 0, hs, a);
+      hipLaunchKernelGGL(q4v::tree_attn_kernel<2>, grid, dim3(128 + 64 * q4v::kLoaders), 0, hs, a);
       break;
     case 4:
-      hipLaunchKernelGGL(q4v::tree_attn_kernel<4>, grid, dim3(256), 0, hs, a);
+      hipLaunchKernelGGL(q4v::tree_attn_kernel<4>, grid, dim3(256 + 64 * q4v::kLoaders), 0, hs, a);
       break;
     case 6:
-      hipLaunchKernelGGL(q4v::tree_attn_kernel<6>, grid, dim3(384), 0, hs, a);
+      hipLaunchKernelGGL(q4v::tree_attn_kernel<6>, grid, dim3(384 + 64 * q4v::kLoaders), 0, hs, a);
       break;
     default:
-      hipLaunchKernelGGL(q4v::tree_attn_kernel<8>, grid, dim3(512), 0, hs, a);
+      hipLaunchKernelGGL(q4v::tree_attn_kernel<8>, grid, dim3(512 + 64 * q4v::kLoaders), 0, hs, a);
       break;
   }
   if (hipGetLastError() != hipSuccess) return Q4_ELAUNCH;
