@@ -870,7 +870,7 @@ def repeat_mode(spec, copy_mb):
     import speculative_verify_gemm_q4_amd as q4
     entry, shape, M, reps = spec.split(":")
     M, reps = int(M), int(reps)
-    if entry in ("attn", "fused"):
+    if entry in ("attn", "fused", "sample"):
         return repeat_other(entry, shape, M, reps)
     entry = {"planar": "q4_gemm_verify", "tiled": "q4_gemm_verify_tiled",
              "ws": "q4_gemm_verify_tiled_ws",
@@ -924,8 +924,9 @@ def repeat_other(entry, shape, M, reps):
     """Profiling aid for the steps beside the GEMM: `attn:CTX:M:REPS` runs
     the tree-verify attention layer of measure_tree_attn at CTX tokens of
     context (two caches rotated), `fused:lm_head:16:REPS` the LM head with
-    the sampling epilogue fused in (rotated weights), REPS prepared calls
-    each after 0.1 s of warm-up."""
+    the sampling epilogue fused in (rotated weights), `sample:lm_head:16:REPS`
+    the standalone epilogue on the LM head's logits (two logit arrays
+    rotated), REPS prepared calls each after 0.1 s of warm-up."""
     import ctypes
     import functools
     import torch
@@ -950,6 +951,27 @@ def repeat_other(entry, shape, M, reps):
             c["page_table"].data_ptr(), int(c["k_pages"].shape[0]), ctx,
             c["anc"].data_ptr(), 1.0 / 16.0, o.data_ptr(), 0, ws.data_ptr(),
             ws.numel(), None, stream) for c in caches]
+    elif entry == "sample":
+        from speculative_verify_gemm_q4_amd._lib import _SampleParams
+        V, _ = WORKLOADS[shape]
+        gen = torch.Generator(device=dev).manual_seed(0)
+        logits = [torch.randn((M, V), generator=gen, device=dev) * 3.0
+                  for _ in range(2)]
+        inp = synth.sample_inputs(M, V, 16, seed=0, device=dev)
+        out = {k: torch.empty(s, dtype=t, device=dev) for k, s, t in (
+            ("top_idx", (M, 20), torch.int32), ("top_val", (M, 20), torch.float32),
+            ("top_prob", (M, 20), torch.float32), ("greedy", (M,), torch.int32),
+            ("accept", (M,), torch.int32), ("token", (M,), torch.int32))}
+        prm = _SampleParams(1.0, 0.95, 20, 16)
+        sws = torch.empty(q4.q4_verify_sample_workspace(M, V), dtype=torch.uint8,
+                          device=dev)
+        fns = [functools.partial(
+            lib.q4_verify_sample, lg.data_ptr(), M, V, ctypes.byref(prm),
+            *[inp[k].data_ptr() for k in (
+                "draft_tok", "draft_idx", "draft_q", "u", "v")],
+            *[out[k].data_ptr() for k in (
+                "top_idx", "top_val", "top_prob", "greedy", "accept", "token")],
+            sws.data_ptr(), sws.numel(), stream) for lg in logits]
     else:
         from speculative_verify_gemm_q4_amd._lib import _SampleParams
         V, K = WORKLOADS[shape]

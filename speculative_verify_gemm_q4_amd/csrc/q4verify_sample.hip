@@ -22,14 +22,19 @@
 //     reversed form a bitonic sequence that one half-cleaner cascade sorts)
 //     and the slice's best 32 written out.  Every compare-exchange stage
 //     swaps lanes with DPP or the gfx950 permlane swaps, not through LDS.
-//  2. sample_rows_kernel: one wave per row.  Each list is descending, so
-//     its head bounds the rest of it: the row's 32nd largest head bounds
-//     the row's 32nd best key from below, and only the (at most 32) lists
-//     whose heads reach it are read whole; their keys at or above it are
-//     ranked into the top_k candidates.  Lane i then takes candidate i, and
-//     the probabilities, the accept test and the residual draw are
-//     evaluated in fp32 with wave reductions, lane scans and ballots over
-//     the candidates in order.
+//  2. The row's candidates from its lists of 32, then the sampling:
+//     - sample_rows_kernel (more than 32 lists a row, as the fused LM head
+//       writes): one wave per row reads the first 4 keys of every list.
+//       Each list is descending, so the lane maxima of the lists' heads
+//       bound the row's 32nd best key from below; the keys read at or above
+//       the bound are ranked, and the rare list that may hold more of them
+//       past its first 4 is read whole.
+//     - sample_rows_few_kernel (at most 32 lists, as the standalone
+//       epilogue writes for rows of up to 524288 columns): 16 waves, one
+//       key per thread, the waves' best 32 merged as in kernel 1.
+//     Lane i of one wave then takes candidate i, and the probabilities, the
+//     accept test and the residual draw are evaluated in fp32 with wave
+//     reductions, lane scans and ballots over the candidates in order.
 
 #include <hip/hip_runtime.h>
 
@@ -198,121 +203,59 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-constexpr int kListsPerLane = kSampleMaxLists / 64;
-constexpr int kLead = 4;  // keys read first from every list
+// LDS of the sampling tail: the candidates' values and tokens, q of each
+// candidate, the row's draft list.
+struct TailLds {
+  float val[kTopMax], qc[kTopMax];
+  int32_t tok[kTopMax];
+  int32_t sdi[kDraftMax];
+  float sdq[kDraftMax];
+};
 
-// Kernel 2: one wave per row m merges the row's S lists, then samples.
-// Every list is descending, so its first key (its head) is its largest.
-// Lane l reads the first 4 keys of lists l, l + 64, ..  T = the 32nd
-// largest lane maximum of the heads: 32 distinct heads reach it, so the
-// row's 32nd best key does too, and every key of the row's best 32 is
-// >= T.  The keys read that are >= T are kept (usually 40 to 60; at most
-// 32 lanes x 8 lists x 4).  A key of the best 32 past a list's first 4
-// needs that list's 4th key >= T; when some list has one, T is raised to
-// the 32nd best kept key (again a lower bound of the row's 32nd best, now
-// with at most 8 lists, or all S < 32, whose 4th key reaches it) and those
-// lists are read whole.  The best 32 kept keys are the row's best 32.
-__global__ __launch_bounds__(64) void sample_rows_kernel(
-    const uint64_t *__restrict__ cand, int S, SampleArgs a,
-    const int32_t *__restrict__ draft_tok, const int32_t *__restrict__ draft_idx,
-    const float *__restrict__ draft_q, const float *__restrict__ u,
-    const float *__restrict__ v, int32_t *__restrict__ top_idx,
-    float *__restrict__ top_val, float *__restrict__ top_prob,
-    int32_t *__restrict__ greedy, int32_t *__restrict__ accept,
-    int32_t *__restrict__ token) {
-  // kept keys: the first 4 of at most 32 x 8 lists, the other 28 of at
-  // most 31 lists read whole, + 8 slots for the ranking
-  constexpr int kPool = kTopMax * kListsPerLane * kLead + (kTopMax - 1) * (kTopMax - kLead);
-  __shared__ uint64_t pool[kPool + 8];
-  __shared__ uint64_t sel[kTopMax];  // the lists read whole
-  __shared__ uint64_t best[kTopMax];
-  __shared__ uint64_t dummy;
-  __shared__ float val[kTopMax], qc[kTopMax];
-  __shared__ int32_t tok[kTopMax];
-  __shared__ int32_t sdi[kDraftMax];
-  __shared__ float sdq[kDraftMax];
-  const int lane = threadIdx.x;
-  const int m = blockIdx.x;
-  const uint64_t *rc = cand + static_cast<uint64_t>(m) * S * kTopMax;
-  uint64_t lead[kListsPerLane][kLead];
-  uint64_t mx = 0;
-#pragma unroll
-  for (int i = 0; i < kListsPerLane; ++i) {
-    const int g = i * 64 + lane;
-#pragma unroll
-    for (int j = 0; j < kLead; ++j)
-      lead[i][j] = g < S ? rc[static_cast<uint64_t>(g) * kTopMax + j] : 0;
-    mx = lead[i][0] > mx ? lead[i][0] : mx;
-  }
-  // the row's draft list and scalars, loaded while the lists arrive
+// The row's draft list into LDS (lanes < draft_k of one wave).
+__device__ __forceinline__ void load_draft(TailLds &tl, const SampleArgs &a, int m,
+                                           const int32_t *__restrict__ draft_idx,
+                                           const float *__restrict__ draft_q,
+                                           int lane) {
   if (lane < a.draft_k) {
-    sdi[lane] = draft_idx[m * a.draft_k + lane];
-    sdq[lane] = draft_q[m * a.draft_k + lane];
+    tl.sdi[lane] = draft_idx[m * a.draft_k + lane];
+    tl.sdq[lane] = draft_q[m * a.draft_k + lane];
   }
-  const int32_t d = draft_tok[m];
-  const float um = u[m], vm = v[m];
-  uint64_t T = wave_kth_largest(mx, kTopMax);
-  uint32_t n = 0;
-  bool deep = false;  // some list's 4th key reaches T
-#pragma unroll
-  for (int i = 0; i < kListsPerLane; ++i) {
-    if (i * 64 >= S) break;  // wave-uniform
-#pragma unroll
-    for (int j = 0; j < kLead; ++j) {
-      const bool keep = lead[i][j] != 0 && lead[i][j] >= T;
-      if (__ballot(keep) != 0) wave_append(lead[i][j], keep, pool, &n, &dummy);
-      if (j == kLead - 1) deep = deep || keep;
-    }
-  }
-  wave_sync();
-  if (__ballot(deep) != 0) {
-    // raise T to the 32nd best kept key; the lists whose 4th key reaches it
-    // are read whole: lane l takes key l & 31 (past the first 4) of lists
-    // l >> 5, (l >> 5) + 2, ..
-    wave_top32(pool, n, best, lane);
-    wave_sync();
-    T = n >= kTopMax ? best[kTopMax - 1] : 0;
-    uint32_t ns = 0;
-#pragma unroll
-    for (int i = 0; i < kListsPerLane; ++i) {
-      const bool whole = lead[i][kLead - 1] != 0 && lead[i][kLead - 1] >= T;
-      wave_append(static_cast<uint64_t>(i * 64 + lane), whole, sel, &ns, &dummy);
-    }
-    wave_sync();
-    for (uint32_t l0 = 0; l0 < ns; l0 += 2) {
-      const uint32_t li = l0 + static_cast<uint32_t>(lane >> 5);
-      const bool past = (lane & 31) >= kLead;
-      const uint64_t key = li < ns && past ? rc[sel[li] * kTopMax + (lane & 31)] : 0;
-      wave_append(key, key != 0 && key >= T, pool, &n, &dummy);
-    }
-    wave_sync();
-  }
-  wave_top32(pool, n, best, lane);
-  wave_sync();
-  const uint64_t list = lane < kTopMax ? best[lane] : 0;
+}
+
+// One wave samples row m from its candidates (lane i < 32: the i-th best
+// key): lane i then holds candidate i, and the probabilities, the accept
+// test and the residual draw are evaluated in fp32 with wave reductions,
+// lane scans and ballots over the candidates in order.  The draft list must
+// be in tl, visible to the wave.
+__device__ __forceinline__ void sample_row(
+    uint64_t list, int m, const SampleArgs &a, TailLds &tl, int32_t d, float um,
+    float vm, int32_t *__restrict__ top_idx, float *__restrict__ top_val,
+    float *__restrict__ top_prob, int32_t *__restrict__ greedy,
+    int32_t *__restrict__ accept, int32_t *__restrict__ token, int lane) {
   const int k = a.top_k;
   // q of every candidate from the row's draft list
   if (lane < k) {
-    val[lane] = key_value(list);
-    tok[lane] = static_cast<int32_t>(key_token(list));
-    top_idx[m * k + lane] = tok[lane];
-    top_val[m * k + lane] = val[lane];
+    tl.val[lane] = key_value(list);
+    tl.tok[lane] = static_cast<int32_t>(key_token(list));
+    top_idx[m * k + lane] = tl.tok[lane];
+    top_val[m * k + lane] = tl.val[lane];
     float q = 0.0f;  // the first matching draft entry, as the scan finds it
     for (int j = a.draft_k - 1; j >= 0; --j)
-      if (sdi[j] == tok[lane]) q = sdq[j];
-    qc[lane] = q;
+      if (tl.sdi[j] == tl.tok[lane]) q = tl.sdq[j];
+    tl.qc[lane] = q;
   }
   float qd = 0.0f;  // q of the drafted token
   for (int j = a.draft_k - 1; j >= 0; --j)
-    if (sdi[j] == d) qd = sdq[j];
+    if (tl.sdi[j] == d) qd = tl.sdq[j];
 
   // Lane i < k holds candidate i.  Sums are wave reductions and cumulative
   // sums lane scans over the candidates in order (fp32).
   const bool live = lane < k;
-  const float vi = live ? val[lane] : 0.0f;
-  const int32_t ti = live ? tok[lane] : -1;
-  const float qi = live ? qc[lane] : 0.0f;
-  const float v0 = val[0];
+  const float vi = live ? tl.val[lane] : 0.0f;
+  const int32_t ti = live ? tl.tok[lane] : -1;
+  const float qi = live ? tl.qc[lane] : 0.0f;
+  const float v0 = tl.val[0];
   float pi;
   if (a.temperature == 0.0f) {
     pi = lane == 0 ? 1.0f : 0.0f;
@@ -327,7 +270,7 @@ __global__ __launch_bounds__(64) void sample_rows_kernel(
     pi = lane < keep ? pi / kept : 0.0f;
   }
   if (live) top_prob[m * k + lane] = pi;
-  if (lane == 0) greedy[m] = tok[0];
+  if (lane == 0) greedy[m] = tl.tok[0];
 
   // accept test of the drafted token
   const uint64_t at_d = __ballot(live && ti == d);
@@ -353,6 +296,129 @@ __global__ __launch_bounds__(64) void sample_rows_kernel(
   const int pick = past ? __builtin_ctzll(past) : 63 - __builtin_clzll(pos);
   const int32_t drawn = __shfl(ti, pick, 64);  // every lane takes part
   if (lane == 0) token[m] = drawn;
+}
+
+constexpr int kListsPerLane = kSampleMaxLists / 64;
+constexpr int kLead = 4;  // keys read first from every list
+
+// Kernel 2: one wave per row m merges the row's S lists, then samples.
+// Every list is descending, so its first key (its head) is its largest.
+// Lane l reads the first 4 keys of lists l,
+// l + 64, ..  T = the 32nd largest lane maximum of the heads: 32 distinct
+// heads reach it, so the row's 32nd best key does too, and every key of
+// the row's best 32 is >= T.  The keys read that are >= T are kept
+// (usually 40 to 60; at most 32 lanes x 8 lists x 4).  A key of the best
+// 32 past a list's first 4 needs that list's 4th key >= T; when some list
+// has one, T is raised to the 32nd best kept key (again a lower bound of
+// the row's 32nd best, now with at most 8 lists whose 4th key reaches it)
+// and those lists are read whole.  The best 32 kept keys are the row's
+// best 32.  (Rows of at most 32 lists go to sample_rows_few_kernel.)
+__global__ __launch_bounds__(64) void sample_rows_kernel(
+    const uint64_t *__restrict__ cand, int S, SampleArgs a,
+    const int32_t *__restrict__ draft_tok, const int32_t *__restrict__ draft_idx,
+    const float *__restrict__ draft_q, const float *__restrict__ u,
+    const float *__restrict__ v, int32_t *__restrict__ top_idx,
+    float *__restrict__ top_val, float *__restrict__ top_prob,
+    int32_t *__restrict__ greedy, int32_t *__restrict__ accept,
+    int32_t *__restrict__ token) {
+  // kept keys: the first 4 of at most 32 x 8 lists and the other 28 of at
+  // most 8 lists read whole, + 8 slots for the ranking
+  constexpr int kPool = kTopMax * kListsPerLane * kLead + 8 * (kTopMax - kLead);
+  __shared__ uint64_t pool[kPool + 8];
+  __shared__ uint64_t sel[kTopMax];  // the lists read whole
+  __shared__ uint64_t best[kTopMax];
+  __shared__ uint64_t dummy;
+  __shared__ TailLds tl;
+  const int lane = threadIdx.x;
+  const int m = blockIdx.x;
+  const uint64_t *rc = cand + static_cast<uint64_t>(m) * S * kTopMax;
+  // the row's draft list and scalars, loaded while the lists arrive
+  load_draft(tl, a, m, draft_idx, draft_q, lane);
+  const int32_t d = draft_tok[m];
+  const float um = u[m], vm = v[m];
+  uint32_t n = 0;
+  {
+    uint64_t lead[kListsPerLane][kLead];
+    uint64_t mx = 0;
+#pragma unroll
+    for (int i = 0; i < kListsPerLane; ++i) {
+      const int g = i * 64 + lane;
+#pragma unroll
+      for (int j = 0; j < kLead; ++j)
+        lead[i][j] = g < S ? rc[static_cast<uint64_t>(g) * kTopMax + j] : 0;
+      mx = lead[i][0] > mx ? lead[i][0] : mx;
+    }
+    uint64_t T = wave_kth_largest(mx, kTopMax);
+    bool deep = false;  // some list's 4th key reaches T
+#pragma unroll
+    for (int i = 0; i < kListsPerLane; ++i) {
+      if (i * 64 >= S) break;  // wave-uniform
+#pragma unroll
+      for (int j = 0; j < kLead; ++j) {
+        const bool keep = lead[i][j] != 0 && lead[i][j] >= T;
+        if (__ballot(keep) != 0) wave_append(lead[i][j], keep, pool, &n, &dummy);
+        if (j == kLead - 1) deep = deep || keep;
+      }
+    }
+    wave_sync();
+    if (__ballot(deep) != 0) {
+      // raise T to the 32nd best kept key; the lists whose 4th key reaches
+      // it (at most 8: 32 kept keys reach T) are read whole: lane l takes
+      // key l & 31 (past the first 4) of lists l >> 5, (l >> 5) + 2, ..
+      wave_top32(pool, n, best, lane);
+      wave_sync();
+      T = best[kTopMax - 1];
+      uint32_t ns = 0;
+#pragma unroll
+      for (int i = 0; i < kListsPerLane; ++i) {
+        const bool whole = lead[i][kLead - 1] != 0 && lead[i][kLead - 1] >= T;
+        wave_append(static_cast<uint64_t>(i * 64 + lane), whole, sel, &ns, &dummy);
+      }
+      wave_sync();
+      for (uint32_t l0 = 0; l0 < ns; l0 += 2) {
+        const uint32_t li = l0 + static_cast<uint32_t>(lane >> 5);
+        const bool past = (lane & 31) >= kLead;
+        const uint64_t key = li < ns && past ? rc[sel[li] * kTopMax + (lane & 31)] : 0;
+        wave_append(key, key != 0 && key >= T, pool, &n, &dummy);
+      }
+      wave_sync();
+    }
+  }
+  wave_top32(pool, n, best, lane);
+  wave_sync();
+  const uint64_t list = lane < kTopMax ? best[lane] : 0;
+  sample_row(list, m, a, tl, d, um, vm, top_idx, top_val, top_prob, greedy,
+             accept, token, lane);
+}
+
+// Kernel 2 for rows of at most 32 lists (the standalone epilogue on rows
+// of up to 32 slices): one workgroup of 16 waves per row, one key per
+// thread.  Each wave sorts its 64 keys and the waves' best 32 are merged
+// pairwise through LDS, which leaves the row's best 32 in wave 0; wave 0
+// then samples.
+__global__ __launch_bounds__(kThreads) void sample_rows_few_kernel(
+    const uint64_t *__restrict__ cand, int S, SampleArgs a,
+    const int32_t *__restrict__ draft_tok, const int32_t *__restrict__ draft_idx,
+    const float *__restrict__ draft_q, const float *__restrict__ u,
+    const float *__restrict__ v, int32_t *__restrict__ top_idx,
+    float *__restrict__ top_val, float *__restrict__ top_prob,
+    int32_t *__restrict__ greedy, int32_t *__restrict__ accept,
+    int32_t *__restrict__ token) {
+  __shared__ uint64_t lists[kWaves][kTopMax];
+  __shared__ TailLds tl;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int m = blockIdx.x;
+  const uint64_t *rc = cand + static_cast<uint64_t>(m) * S * kTopMax;
+  const uint64_t key =
+      static_cast<int>(threadIdx.x) < S * kTopMax ? rc[threadIdx.x] : 0;
+  if (wave == 0) load_draft(tl, a, m, draft_idx, draft_q, lane);
+  const int32_t d = draft_tok[m];
+  const float um = u[m], vm = v[m];
+  const uint64_t list = block_merge(sort64_desc(key, lane), lists, wave, lane);
+  if (wave != 0) return;
+  sample_row(lane < kTopMax ? list : 0, m, a, tl, d, um, vm, top_idx, top_val,
+             top_prob, greedy, accept, token, lane);
 }
 
 int slices_for(int64_t V) {
@@ -389,7 +455,12 @@ int launch_sample_rows(const uint64_t *cand, int M, int S,
                        int32_t *accept, int32_t *token, hipStream_t s) {
   if (S < 1 || S > kSampleMaxLists) return Q4_EINVAL;
   const SampleArgs a{p.temperature, p.top_p, p.top_k, p.draft_k};
-  hipLaunchKernelGGL(sample_rows_kernel, dim3(M), dim3(64), 0, s,
+  if (S <= kTopMax)
+    hipLaunchKernelGGL(sample_rows_few_kernel, dim3(M), dim3(kThreads), 0, s,
+                       cand, S, a, draft_tok, draft_idx, draft_q, u, v, top_idx,
+                       top_val, top_prob, greedy, accept, token);
+  else
+    hipLaunchKernelGGL(sample_rows_kernel, dim3(M), dim3(64), 0, s,
                      cand, S, a, draft_tok, draft_idx, draft_q, u, v, top_idx,
                      top_val, top_prob, greedy, accept, token);
   return hipGetLastError() == hipSuccess ? Q4_OK : Q4_ELAUNCH;
