@@ -415,7 +415,8 @@ int q4_verify_sample(const float *logits, int M, int64_t V,
  * q4_gemm_verify_tiled followed by q4_verify_sample on the same inputs, bit
  * for bit (the logits are the same fp32 values).
  *   x, W_tiled, M (1..Q4_MAX_ROWS), N (the vocabulary, V), K: as
- *     q4_gemm_verify_tiled; K <= 6144 and N <= 1024 * (compute units).
+ *     q4_gemm_verify_tiled; K <= 6144 and N <= 1024 * (compute units), the
+ *     compute units counted up to 512 (the merge takes at most 512 lists).
  *   prm, draft_tok .. token: as q4_verify_sample with V = N.
  *   workspace: q4_gemm_verify_sample_workspace bytes, 8-byte aligned.
  * Two kernels on `stream`; calls sharing a workspace race.
