@@ -27,6 +27,9 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          # MFMA results in VGPRs: the epilogue reads them without moves
          "-mllvm", "-amdgpu-mfma-vgpr-form",
+         # kernel arguments arrive in SGPRs at wave launch (no scalar load
+         # round trip before a kernel's first memory access)
+         "-mllvm", "-amdgpu-kernarg-preload-count=16",
          "-I", INCLUDE, "-I", CSRC]
 
 

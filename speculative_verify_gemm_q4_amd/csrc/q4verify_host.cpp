@@ -192,6 +192,9 @@ bool plan_kslice(int M, int64_t N, int64_t K, int cus, int parts, int seq,
   // 242 x 9 tiles instead of 256 x 8 or 9, 20.9 against 21.9 us at M = 16
   // on MI355X); with fewer, every CU's share matters more.
   const int64_t g = per >= 3 ? (tiles + per - 1) / per : g0;
+  // the kernel's index arithmetic (packed arguments, fp32 quotients) takes
+  // fewer than 4096 workgroups per part and parts
+  if (g >= 4096 || nparts >= 4096) return false;
   const bool planar = layout == Q4_LAYOUT_PLANAR;
   if (seq > 1 && per > (planar ? kInMaxTilesPlanar : kInMaxTiles)) return false;
   // planar: one resource over a workgroup's scales and the biases after them

@@ -106,6 +106,18 @@ __device__ __forceinline__ uint32_t opaque_v(uint32_t v) {
   return v;
 }
 
+// floor(a / d) for 0 <= a < 2^24, 1 <= d < 2^24 and a / d < 2^21 (a few
+// instructions instead of an integer division): the fp32 product with the
+// reciprocal lies within 0.2 of a / d, so the truncated quotient is off by
+// at most one, and one step on the remainder corrects it.
+__device__ __forceinline__ int small_div(int a, int d) {
+  int q = static_cast<int>(static_cast<float>(a) *
+                           __builtin_amdgcn_rcpf(static_cast<float>(d)));
+  const int r = a - q * d;
+  q += static_cast<int>(r >= d) - static_cast<int>(r < 0);
+  return q;
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
       __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
@@ -826,8 +838,16 @@ template <int W, bool kRowLoads, bool kSample, bool kPlanar, bool kSeq, int RT,
           bool kDot = false>
 __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ Wt,
-    float *__restrict__ y, float *__restrict__ ws, int M, int N, int K, int P,
-    int Pin_) {
+    float *__restrict__ y, float *__restrict__ ws, int N, int K, uint32_t mp,
+    int per, uint32_t gr) {
+  // Packed by the host (kslice_args): mp = M | P << 8 | Pin << 20 (rows,
+  // part groups, parts per group), gr = Gt | rem << 16 with Gt workgroups
+  // per part group and T = per * Gt + rem tiles.  Every argument arrives in
+  // SGPRs at wave launch (kernarg preload), and no integer division stands
+  // between the launch and the first loads.
+  const int M = static_cast<int>(mp & 0xFFu);
+  const int P = static_cast<int>((mp >> 8) & 0xFFFu);
+  const int Pin_ = static_cast<int>(mp >> 20);
   // RT = 2 (M = 17..32): two MFMA row tiles multiply the same unpacked codes,
   // and a wave owns one record (R = 1) so that its activation operands stay
   // at the registers of two records of one row tile
@@ -865,16 +885,20 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 15;
   const int kb = lane >> 4;
-  const int G = static_cast<int>(gridDim.x);
+  // the grid: P part groups of Gt workgroups (from the arguments rather than
+  // the dispatch packet, which would cost a load)
+  const int G = static_cast<int>(gr & 0xFFFFu) * P;
   const int b = static_cast<int>(blockIdx.x);
   const int rank = (b & 7) * (G >> 3) + min(b & 7, G & 7) + (b >> 3);
   // rank -> part group pk of K and tile group g; part group pk holds parts
   // pk * Pin .. pk * Pin + Pin - 1, taken one after another
-  const int Gt = G / P;
-  const int pk = rank / Gt;
+  // t0 = floor(T g / Gt) = per g + floor(rem g / Gt), likewise t1
+  const int Gt = static_cast<int>(gr & 0xFFFFu);
+  const int rem = static_cast<int>(gr >> 16);
+  const int pk = P == 1 ? 0 : small_div(rank, Gt);
   const int g = rank - pk * Gt;
-  const int t0 = static_cast<int>(static_cast<int64_t>(T) * g / Gt);
-  const int t1 = static_cast<int>(static_cast<int64_t>(T) * (g + 1) / Gt);
+  const int t0 = g * per + small_div(g * rem, Gt);
+  const int t1 = (g + 1) * per + small_div((g + 1) * rem, Gt);
   __builtin_assume(t1 > t0);  // a part has at most one workgroup per tile
   // (planar: the waves meet once per tile anyway, for the shared scales)
   const bool in_step = !kPlanar && t1 - t0 >= 8;
@@ -1139,8 +1163,12 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
 
   for (int ip = 0; ip < Pin; ++ip) {
     const int pp = pk * Pin + ip;  // part of K
-    const int qa = static_cast<int>(static_cast<int64_t>(Q) * pp / Ptot);
-    const int nrec = static_cast<int>(static_cast<int64_t>(Q) * (pp + 1) / Ptot) - qa;
+    // records [floor(Q pp / Ptot), floor(Q (pp + 1) / Ptot)), with
+    // Q = qd Ptot + qr
+    const int qd = Ptot == 1 ? Q : small_div(Q, Ptot);
+    const int qr = Q - qd * Ptot;
+    const int qa = qd * pp + (Ptot == 1 ? 0 : small_div(qr * pp, Ptot));
+    const int nrec = qd * (pp + 1) + (Ptot == 1 ? 0 : small_div(qr * (pp + 1), Ptot)) - qa;
     q0 = qa + R * wave;
     nq = min(max(nrec - R * wave, 0), R);  // 0 .. R
     tl = 0;
@@ -1400,11 +1428,26 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
   }
 }
 
+// The K-slice kernel's packed arguments (see gemm_kslice_kernel): the plan
+// keeps P, the parts in turn and Gt below 4096, and M <= 32.
+struct KsliceArgs {
+  uint32_t mp;
+  int per;
+  uint32_t gr;
+};
+
+KsliceArgs kslice_args(const q4_plan &p, int M, int N) {
+  const uint32_t parts = p.k_parts, seq = p.k_seq_parts;
+  const int gt = static_cast<int>(p.grid / parts);
+  const int T = (N + 15) / 16;
+  return {static_cast<uint32_t>(M) | parts << 8 | seq << 20, T / gt,
+          static_cast<uint32_t>(gt) | static_cast<uint32_t>(T % gt) << 16};
+}
+
 template <int W, bool kSample, bool kPlanar, bool kSeq, int RT = 1>
 void launch_kslice_v(const q4_plan &p, const void *x, const void *Wt, float *y,
                      float *ws, int M, int N, int K, hipStream_t stream) {
-  const int parts = static_cast<int>(p.k_parts);
-  const int seq = static_cast<int>(p.k_seq_parts);
+  const KsliceArgs a = kslice_args(p, M, N);
   // M >= 8: row-contiguous activation loads through LDS; below that the rows
   // past M are zeros anyway and direct loads save the LDS round trip (two
   // row tiles always take the row loads)
@@ -1412,12 +1455,12 @@ void launch_kslice_v(const q4_plan &p, const void *x, const void *Wt, float *y,
     hipLaunchKernelGGL((gemm_kslice_kernel<W, true, kSample, kPlanar, kSeq, RT>),
                        dim3(p.grid), dim3(64 * W), 0, stream,
                        static_cast<const uint16_t *>(x),
-                       static_cast<const uint8_t *>(Wt), y, ws, M, N, K, parts, seq);
+                       static_cast<const uint8_t *>(Wt), y, ws, N, K, a.mp, a.per, a.gr);
   else if constexpr (RT == 1)
     hipLaunchKernelGGL((gemm_kslice_kernel<W, false, kSample, kPlanar, kSeq, 1>),
                        dim3(p.grid), dim3(64 * W), 0, stream,
                        static_cast<const uint16_t *>(x),
-                       static_cast<const uint8_t *>(Wt), y, ws, M, N, K, parts, seq);
+                       static_cast<const uint8_t *>(Wt), y, ws, N, K, a.mp, a.per, a.gr);
 }
 
 template <int W, bool kSample = false, bool kPlanar = false>
@@ -1457,13 +1500,15 @@ int launch_kslice_dot(const q4_plan &p, const void *x, const void *Wt, float *y,
   if (p.k_parts != 1 || p.k_seq_parts != 1 || p.m_tiles != 1 || M > 4 ||
       p.layout_id != Q4_LAYOUT_TILED16)
     return Q4_EINVAL;
+  const KsliceArgs a = kslice_args(p, M, N);
   switch (p.block / 64) {
 #define Q4V_KSLICE_DOT_CASE(W)                                                  \
   case W:                                                                       \
     hipLaunchKernelGGL((gemm_kslice_kernel<W, false, false, false, false, 1, true>), \
                        dim3(p.grid), dim3(64 * W), 0, stream,                   \
                        static_cast<const uint16_t *>(x),                        \
-                       static_cast<const uint8_t *>(Wt), y, nullptr, M, N, K, 1, 1); \
+                       static_cast<const uint8_t *>(Wt), y, nullptr, N, K, a.mp, a.per, \
+                       a.gr);                                                   \
     break;
     Q4V_KSLICE_DOT_CASE(1) Q4V_KSLICE_DOT_CASE(2) Q4V_KSLICE_DOT_CASE(3)
     Q4V_KSLICE_DOT_CASE(4) Q4V_KSLICE_DOT_CASE(5) Q4V_KSLICE_DOT_CASE(6)
