@@ -834,7 +834,7 @@ __device__ __forceinline__ void kslice_lds_barrier() {
 // below, so only keys at or above it survive; the survivors (usually a few
 // more than 32) are packed into the wave's part of the partial-sum area and
 // sorted 64 at a time with bitonic networks, merging into the running list.
-template <int W, bool kRowLoads, bool kSample, bool kPlanar, bool kSeq, int RT,
+template <int W, int kRowLoads, bool kSample, bool kPlanar, bool kSeq, int RT,
           bool kDot = false>
 __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ Wt,
@@ -855,6 +855,9 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
   // kDot: the VALU variant for M <= 4 (v_dot2_f32_bf16 instead of MFMA)
   static_assert(!kDot || (RT == 1 && !kSample && !kPlanar && !kSeq && !kRowLoads),
                 "dot variant");
+  // kRowLoads: activation row pairs loaded per record (1, 2 or 8)
+  static_assert(kDot || kRowLoads == 1 || kRowLoads == 2 || kRowLoads == 8,
+                "row pairs");
   constexpr int R = RT == 1 ? 2 : 1;  // records per wave
   // parts of K taken in turn: a run-time count only in the kSeq kernels
   const int Pin = kSeq ? Pin_ : 1;
@@ -1238,9 +1241,10 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
             }
             xs[qq][gi][m] = t;
           }
-    } else if constexpr (kRowLoads) {
-      // Row-contiguous loads (load i of record qq brings rows 2i and 2i + 1,
-      // 512 B each), then through LDS into the operand layout.  Lane l of
+    } else if constexpr (kRowLoads > 0) {
+      // Row-contiguous loads (load i < kRowLoads of record qq brings rows 2i
+      // and 2i + 1, 512 B each), then through LDS into the operand layout;
+      // rows from 2 kRowLoads on (all >= M) are zeros without a load.  Lane l of
       // load i holds chunk c = l & 31 (inputs 8c .. 8c+7) of row
       // r = 2i + (l >> 5); it is stored at row r, chunk c ^ (r & 7) of the
       // wave's 8 KB area, and lane (j, kb) reads chunk 8 gi + w of row j for
@@ -1251,7 +1255,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
       for (int u = 0; u < 2; ++u) {
         const int qu = RT == 1 ? u : 0, ru = RT == 1 ? 0 : u;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < kRowLoads; ++i) {
           const uint32_t r = 16 * ru + 2 * i + (lane >> 5);
           const uint32_t off = (r * K + 256 * (q0 + qu) + 8 * (lane & 31)) * 2;
           xrow[u][i] = buffer_load16<0>(xr, off, qu < nq ? 0u : 0x7FFFFFF0u);
@@ -1263,7 +1267,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < kRowLoads; ++i) {
           const int r = 2 * i + (lane >> 5);
           const int c = (lane & 31) ^ (r & 7);
           *reinterpret_cast<u32x4 *>(area + r * 512 + c * 16) = xrow[u][i];
@@ -1273,39 +1277,16 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const int c = (8 * gi + (h ? w_h1 : w_h0)) ^ (j & 7);
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(area + j * 512 + c * 16);
+            // rows past the loaded pairs are zeros (not in the area)
+            const u32x4 v = j < 2 * kRowLoads
+                                 ? *reinterpret_cast<const u32x4 *>(area + j * 512 + c * 16)
+                                 : u32x4{0u, 0u, 0u, 0u};
             xa[u][gi][h] = kPlanar ? pair_activations(v) : v;
           }
       }
       // the areas alias the partial sums: every wave has its operands in
       // registers before any wave writes a partial sum
       kslice_lds_barrier();
-    } else {
-      // direct loads in the operand layout: lane (j, kb), operand (gi, h)
-      // reads inputs 64 gi + 8 w .. +7 of row j
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int qu = RT == 1 ? u : 0, ru = RT == 1 ? 0 : u;
-#pragma unroll
-        for (int gi = 0; gi < 4; ++gi)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const uint32_t off = (static_cast<uint32_t>(16 * ru + j) * K + 256 * (q0 + qu) +
-                                  64 * gi + 8 * (h ? w_h1 : w_h0)) * 2;
-            xa[u][gi][h] = buffer_load16<0>(xr, off, qu < nq ? 0u : 0x7FFFFFF0u);
-          }
-      }
-      load(st[0]);
-      if constexpr (S > 2) load(st[1]);
-      __builtin_amdgcn_sched_barrier(0);  // every load issued before the seeds
-      if constexpr (kPlanar) {
-#pragma unroll
-        for (int qq = 0; qq < 2; ++qq)
-#pragma unroll
-          for (int gi = 0; gi < 4; ++gi)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) xa[qq][gi][h] = pair_activations(xa[qq][gi][h]);
-      }
     }
     if constexpr (!kDot) {
 #pragma unroll
@@ -1448,19 +1429,25 @@ template <int W, bool kSample, bool kPlanar, bool kSeq, int RT = 1>
 void launch_kslice_v(const q4_plan &p, const void *x, const void *Wt, float *y,
                      float *ws, int M, int N, int K, hipStream_t stream) {
   const KsliceArgs a = kslice_args(p, M, N);
-  // M >= 8: row-contiguous activation loads through LDS; below that the rows
-  // past M are zeros anyway and direct loads save the LDS round trip (two
-  // row tiles always take the row loads)
-  if (RT == 2 || M >= 8)
-    hipLaunchKernelGGL((gemm_kslice_kernel<W, true, kSample, kPlanar, kSeq, RT>),
+  // Activation rows come as row-contiguous pairs through LDS, only the
+  // pairs that hold rows < M at M <= 4 (one load per pair and record): at
+  // M = 1 a wave issues 2 activation loads instead of 16 operand-layout
+  // loads of 4 active lanes each (o/out 7.37 -> 7.07 us, gate+up 19.35 ->
+  // 19.18 us on MI355X).  From M = 5 on all 8 pairs are loaded: 4 pairs at
+  // M = 8 measured 0.05-0.4 us slower than 8 (the pairs past M read nothing).
+  // Two row tiles take all 16 rows of each.
+  auto go = [&](auto lr) {
+    hipLaunchKernelGGL((gemm_kslice_kernel<W, decltype(lr)::value, kSample, kPlanar, kSeq, RT>),
                        dim3(p.grid), dim3(64 * W), 0, stream,
                        static_cast<const uint16_t *>(x),
                        static_cast<const uint8_t *>(Wt), y, ws, N, K, a.mp, a.per, a.gr);
-  else if constexpr (RT == 1)
-    hipLaunchKernelGGL((gemm_kslice_kernel<W, false, kSample, kPlanar, kSeq, 1>),
-                       dim3(p.grid), dim3(64 * W), 0, stream,
-                       static_cast<const uint16_t *>(x),
-                       static_cast<const uint8_t *>(Wt), y, ws, N, K, a.mp, a.per, a.gr);
+  };
+  if (RT == 2 || M > 4)
+    go(std::integral_constant<int, 8>{});
+  else if (M > 2)
+    go(std::integral_constant<int, 2>{});
+  else
+    go(std::integral_constant<int, 1>{});
 }
 
 template <int W, bool kSample = false, bool kPlanar = false>
@@ -1504,7 +1491,7 @@ int launch_kslice_dot(const q4_plan &p, const void *x, const void *Wt, float *y,
   switch (p.block / 64) {
 #define Q4V_KSLICE_DOT_CASE(W)                                                  \
   case W:                                                                       \
-    hipLaunchKernelGGL((gemm_kslice_kernel<W, false, false, false, false, 1, true>), \
+    hipLaunchKernelGGL((gemm_kslice_kernel<W, 0, false, false, false, 1, true>), \
                        dim3(p.grid), dim3(64 * W), 0, stream,                   \
                        static_cast<const uint16_t *>(x),                        \
                        static_cast<const uint8_t *>(Wt), y, nullptr, N, K, a.mp, a.per, \

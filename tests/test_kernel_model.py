@@ -295,34 +295,30 @@ def kslice_model(M, N, K, p):
     ranks = [(b & 7) * (G >> 3) + min(b & 7, G & 7) + (b >> 3)
              for b in range(G)]
     assert sorted(ranks) == list(range(G))
-    x_bytes = M * K * 2
+    # the packed arguments (M | P << 8 | Pin << 20, per, Gt | rem << 16)
+    # and the kernel's division-free index arithmetic
+    assert M < 256 and P < 4096 and Pin < 4096 and Gt < 4096
+    per_k, rem_k = T // Gt, T % Gt
+    assert per_k * Gt + rem_k == T
+    for b in range(G):
+        r = ranks[b]
+        pk = 0 if P == 1 else small_div_model(r, Gt)
+        g = r - pk * Gt
+        assert (pk, g) == divmod(r, Gt)
+        assert g * per_k + small_div_model(g * rem_k, Gt) == T * g // Gt
+        assert (g + 1) * per_k + small_div_model((g + 1) * rem_k, Gt) == T * (g + 1) // Gt
+    qd = Q if Ptot == 1 else small_div_model(Q, Ptot)
+    qr = Q - qd * Ptot
+    assert (qd, qr) == divmod(Q, Ptot)
     for pp in range(Ptot):
         qa = Q * pp // Ptot
         nrec = Q * (pp + 1) // Ptot - qa
         assert 1 <= nrec <= R * W
-        # activation operand loads of wave w: a real row's own record, else
-        # past the resource (zeros)
-        for w in range(W):
-            nq = min(max(nrec - R * w, 0), R)
-            for lane in range(64):
-                j, kb = lane & 15, lane >> 4
-                for u in range(2):
-                    qu, ru = (u, 0) if RT == 1 else (0, u)
-                    row = 16 * ru + j
-                    for gi in range(4):
-                        for h in range(2):
-                            wd = planar_word(j, kb, h) if planar else 2 * kb + h
-                            k = 256 * (qa + R * w + qu) + 64 * gi + 8 * wd
-                            off = (row * K + k) * 2
-                            if qu < nq and row < M:
-                                assert k + 8 <= K and off + 16 <= x_bytes
-                            elif qu < nq:
-                                assert off >= x_bytes
-                            else:
-                                assert x_bytes <= off + 0x7FFFFFF0 < 2 ** 32
-        if M >= 8:
-            kslice_row_staging_model(M, K, W, p["lds_bytes"] - tacc, qa, nrec,
-                                     planar, RT)
+        if Ptot > 1:
+            assert qd * pp + small_div_model(qr * pp, Ptot) == qa
+            assert qd * (pp + 1) + small_div_model(qr * (pp + 1), Ptot) - qa == nrec
+        kslice_row_staging_model(M, K, W, p["lds_bytes"] - tacc, qa, nrec,
+                                 planar, RT)
     G8 = K // 64
     for b in range(G):
         r = ranks[b]
@@ -424,16 +420,44 @@ def planar_scale_loads(N, K, W, t0, t1, rows, qa, nrec):
                     assert got == (a, j, w, want_o)
 
 
+def row_pairs(M, RT):
+    """Activation row pairs a wave loads per record (or row tile)."""
+    return 8 if RT == 2 or M > 4 else 2 if M > 2 else 1
+
+
+def small_div_model(a, d):
+    """The kernel's floor(a / d) for 0 <= a < 2^24, 1 <= d < 2^24: the fp32
+    product of a with the reciprocal of d, truncated, then one correction
+    step on the remainder.  The reciprocal instruction is accurate to one
+    ulp, so the product is tried with the correctly rounded reciprocal and
+    its neighbours one ulp either side."""
+    assert 0 <= a < 2 ** 24 and 1 <= d < 2 ** 24
+    r0 = np.float32(1.0) / np.float32(d)
+    out = set()
+    for rc in (np.nextafter(r0, np.float32(0)), r0, np.nextafter(r0, np.float32(1))):
+        q = int(np.float32(a) * np.float32(rc))
+        rm = a - q * d
+        q += int(rm >= d) - int(rm < 0)
+        out.add(q)
+    assert len(out) == 1, (a, d, out)
+    return out.pop()
+
+
 def kslice_row_staging_model(M, K, W, lds_bytes, qa, nrec, planar=False,
                              RT=1):
-    """M >= 8: the activations arrive by row-contiguous loads and pass
-    through an 8 KB LDS area per wave.  Every operand register must end up
-    holding exactly what the direct operand-layout load would have read,
-    the LDS stores of one round must not collide, and the areas must fit.
-    The part's records are [qa, qa + nrec); unit u is record u of the
-    wave's two (RT = 1) or rows 16 u .. of its one record (RT = 2)."""
+    """The activations arrive by row-contiguous loads (row_pairs(M, RT)
+    loads of two rows per record) and pass through an 8 KB LDS area per
+    wave; rows from 2 row_pairs on are zeros without a load or an LDS read.
+    Every operand register must end up holding exactly the inputs of its
+    operand-layout slot (row j, inputs 64 gi + 8 word .. +7 of the wave's
+    record), or zeros for rows >= M; the LDS stores of one round must not
+    collide, and the areas must fit.  The part's records are
+    [qa, qa + nrec); unit u is record u of the wave's two (RT = 1) or rows
+    16 u .. of its one record (RT = 2)."""
     x_bytes = M * K * 2
     R = 1 if RT == 2 else 2
+    LR = row_pairs(M, RT)
+    assert 2 * LR >= min(M, 16)
     assert W * 8192 <= lds_bytes
     for w in range(W):
         nq = min(max(nrec - R * w, 0), R)
@@ -441,7 +465,7 @@ def kslice_row_staging_model(M, K, W, lds_bytes, qa, nrec, planar=False,
             qq, ru = (u, 0) if RT == 1 else (0, u)
             # what lane l of load i holds: (row, input) or None (zeros)
             area = {}
-            for i in range(8):
+            for i in range(LR):
                 for lane in range(64):
                     r, c = 2 * i + (lane >> 5), lane & 31
                     row = 16 * ru + r
@@ -456,14 +480,14 @@ def kslice_row_staging_model(M, K, W, lds_bytes, qa, nrec, planar=False,
                     addr = w * 8192 + r * 512 + (c ^ (r & 7)) * 16
                     assert addr not in area
                     area[addr] = val
-            assert len(area) == 512
+            assert len(area) == 64 * LR
             for lane in range(64):
                 j, kb = lane & 15, lane >> 4
                 for gi in range(4):
                     for h in range(2):
                         wd = planar_word(j, kb, h) if planar else 2 * kb + h
                         c = (8 * gi + wd) ^ (j & 7)
-                        got = area[w * 8192 + j * 512 + c * 16]
+                        got = area[w * 8192 + j * 512 + c * 16] if j < 2 * LR else None
                         k = 256 * (qa + R * w + qq) + 64 * gi + 8 * wd
                         row = 16 * ru + j
                         want = (row, k) if (qq < nq and row < M) else None
@@ -760,3 +784,28 @@ def test_workspace_plan_32_rows(M, N, K):
     assert P == 1 or -(-Q // (P // 2)) > 12
     assert p["k_seq_parts"] == 1
     kslice_model(M, N, K, p)
+
+
+def test_small_div_domain():
+    """The kernel's fp32 quotient with one correction step equals floor(a/d)
+    over the ranges its index arithmetic uses (d < 4096 workgroups or parts,
+    a < 4096 d, and the record counts Q < 2^18 over a part count), for the
+    correctly rounded reciprocal and for one ulp either side."""
+    rng = np.random.default_rng(7)
+    d = np.arange(1, 4096, dtype=np.int64)
+    cols = [np.zeros_like(d), d - 1, d, d + 1, 4095 * d - 1, 4095 * d,
+            rng.integers(0, 4096, size=d.size) * d + rng.integers(0, d),
+            rng.integers(0, 4096 * d)]
+    a = np.concatenate(cols)
+    dd = np.tile(d, len(cols))
+    q_big = rng.integers(0, 2 ** 18, size=20000)
+    a = np.concatenate([a, q_big])
+    dd = np.concatenate([dd, rng.integers(1, 4096, size=q_big.size)])
+    keep = (a >= 0) & (a < 2 ** 24)
+    a, dd = a[keep], dd[keep]
+    r0 = np.float32(1.0) / dd.astype(np.float32)
+    for rc in (np.nextafter(r0, np.float32(0)), r0, np.nextafter(r0, np.float32(1))):
+        q = (a.astype(np.float32) * rc).astype(np.int64)
+        rm = a - q * dd
+        q = q + (rm >= dd) - (rm < 0)
+        assert np.array_equal(q, a // dd)
