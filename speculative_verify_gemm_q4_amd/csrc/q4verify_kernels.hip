@@ -855,8 +855,10 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
   // kDot: the VALU variant for M <= 4 (v_dot2_f32_bf16 instead of MFMA)
   static_assert(!kDot || (RT == 1 && !kSample && !kPlanar && !kSeq && !kRowLoads),
                 "dot variant");
-  // kRowLoads: activation row pairs loaded per record (1, 2 or 8)
-  static_assert(kDot || kRowLoads == 1 || kRowLoads == 2 || kRowLoads == 8,
+  // kRowLoads: activation row pairs loaded per record (1, 2 or 8), or 0
+  // for direct operand-layout loads (parts in turn at M <= 4)
+  static_assert(kDot || kRowLoads == 1 || kRowLoads == 2 || kRowLoads == 8 ||
+                    (kRowLoads == 0 && kSeq),
                 "row pairs");
   constexpr int R = RT == 1 ? 2 : 1;  // records per wave
   // parts of K taken in turn: a run-time count only in the kSeq kernels
@@ -1287,6 +1289,32 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
       // the areas alias the partial sums: every wave has its operands in
       // registers before any wave writes a partial sum
       kslice_lds_barrier();
+    } else {
+      // kRowLoads == 0 (parts of K in turn at M <= 4): loads straight in the
+      // operand layout, no LDS round trip and no barrier per part -- lane
+      // (j, kb), operand (gi, h) reads inputs 64 gi + 8 w .. +7 of row j
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int qu = RT == 1 ? u : 0, ru = RT == 1 ? 0 : u;
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t off = (static_cast<uint32_t>(16 * ru + j) * K + 256 * (q0 + qu) +
+                                  64 * gi + 8 * (h ? w_h1 : w_h0)) * 2;
+            xa[u][gi][h] = buffer_load16<0>(xr, off, qu < nq ? 0u : 0x7FFFFFF0u);
+          }
+      }
+      load(st[0]);
+      __builtin_amdgcn_sched_barrier(0);  // every load issued before the seeds
+      if constexpr (kPlanar) {
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+          for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) xa[qq][gi][h] = pair_activations(xa[qq][gi][h]);
+      }
     }
     if constexpr (!kDot) {
 #pragma unroll
@@ -1444,6 +1472,11 @@ void launch_kslice_v(const q4_plan &p, const void *x, const void *Wt, float *y,
   };
   if (RT == 2 || M > 4)
     go(std::integral_constant<int, 8>{});
+  else if constexpr (kSeq)
+    // parts of K in turn repeat the activation staging per part: there the
+    // direct loads measured faster at M <= 4 (down, three parts: 20.3
+    // against 22.0 us at M = 1)
+    go(std::integral_constant<int, 0>{});
   else if (M > 2)
     go(std::integral_constant<int, 2>{});
   else

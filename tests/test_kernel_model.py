@@ -317,8 +317,11 @@ def kslice_model(M, N, K, p):
         if Ptot > 1:
             assert qd * pp + small_div_model(qr * pp, Ptot) == qa
             assert qd * (pp + 1) + small_div_model(qr * (pp + 1), Ptot) - qa == nrec
-        kslice_row_staging_model(M, K, W, p["lds_bytes"] - tacc, qa, nrec,
-                                 planar, RT)
+        if row_pairs(M, RT, Pin > 1):
+            kslice_row_staging_model(M, K, W, p["lds_bytes"] - tacc, qa, nrec,
+                                     planar, RT)
+        else:
+            direct_operand_loads(M, K, W, qa, nrec, planar, RT)
     G8 = K // 64
     for b in range(G):
         r = ranks[b]
@@ -420,9 +423,40 @@ def planar_scale_loads(N, K, W, t0, t1, rows, qa, nrec):
                     assert got == (a, j, w, want_o)
 
 
-def row_pairs(M, RT):
-    """Activation row pairs a wave loads per record (or row tile)."""
-    return 8 if RT == 2 or M > 4 else 2 if M > 2 else 1
+def row_pairs(M, RT, seq=False):
+    """Activation row pairs a wave loads per record (or row tile); 0 for
+    direct operand-layout loads (parts of K in turn at M <= 4)."""
+    if RT == 2 or M > 4:
+        return 8
+    if seq:
+        return 0
+    return 2 if M > 2 else 1
+
+
+def direct_operand_loads(M, K, W, qa, nrec, planar=False, RT=1):
+    """Direct loads: lane (j, kb), operand (gi, h) of wave w reads inputs
+    64 gi + 8 word .. +7 of row j of its record, inside the M x K
+    activations for a real row of a real record, past them otherwise."""
+    x_bytes = M * K * 2
+    R = 1 if RT == 2 else 2
+    for w in range(W):
+        nq = min(max(nrec - R * w, 0), R)
+        for lane in range(64):
+            j, kb = lane & 15, lane >> 4
+            for u in range(2):
+                qu, ru = (u, 0) if RT == 1 else (0, u)
+                row = 16 * ru + j
+                for gi in range(4):
+                    for h in range(2):
+                        wd = planar_word(j, kb, h) if planar else 2 * kb + h
+                        k = 256 * (qa + R * w + qu) + 64 * gi + 8 * wd
+                        off = (row * K + k) * 2
+                        if qu < nq and row < M:
+                            assert k + 8 <= K and off + 16 <= x_bytes
+                        elif qu < nq:
+                            assert off >= x_bytes
+                        else:
+                            assert x_bytes <= off + 0x7FFFFFF0 < 2 ** 32
 
 
 def small_div_model(a, d):
