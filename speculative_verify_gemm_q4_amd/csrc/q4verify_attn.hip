@@ -15,9 +15,10 @@
 // loader waves.
 //  * Per page the loader waves load the 8 KiB of keys ([32 tokens][256])
 //    and 8 KiB of values (stored transposed, [256][32]) with their scales
-//    into their registers, four pages ahead, turn the int8 values into bf16
-//    (exact: |v| <= 128) and write them to an LDS tile (two tiles: the
-//    compute waves read one page while the next is written).
+//    into their registers, four pages ahead, turn the int8 keys into bf16
+//    and the int8 values into fp16 (both exact: |v| <= 128) and write them
+//    to an LDS tile (two tiles: the compute waves read one page while the
+//    next is written).
 //  * Scores on MFMA: S^T[token][node] = K Q^T, sixteen
 //    v_mfma_f32_16x16x32_bf16 per page and wave (two token tiles, eight
 //    32-dim steps), the key scale and the softmax scale applied per token
@@ -26,11 +27,12 @@
 //    when a score passes it by more than 2^8; each node's 32 scores of a
 //    page sit in 4 lanes x 8 registers.  The ancestor mask applies to tree positions,
 //    a 32-bit ancestor-or-self set per node.
-//  * Values on MFMA: O^T[dim][node] += V^T P'^T with P' = p * v_scale as a
-//    pair of bf16 (head + tail, 16 significant bits between them) and two
-//    MFMAs per value tile; the value tile's tokens are stored in the order in which the
-//    score tiles hold them in a lane (tokens 4g..4g+3, 16+4g..16+4g+3 for
-//    lane group g), so the probabilities need no shuffle.
+//  * Values on MFMA: O^T[dim][node] += V^T P''^T with P'' = p * v_scale /
+//    vlim rounded to fp16 (vlim a power of two at or above the value scales
+//    seen, so P'' <= 2^8) and one v_mfma_f32_16x16x32_f16 per value tile;
+//    the value tile's tokens are stored in the order in which the score
+//    tiles hold them in a lane (tokens 4g..4g+3, 16+4g..16+4g+3 for lane
+//    group g), so the probabilities need no shuffle.
 //  * A run over the whole context writes normalised outputs; otherwise the
 //    run writes its unnormalised output and (max, sum) to the workspace.
 // Kernel 2 (attn_combine_kernel): per (node, query head) the runs' partial
@@ -46,6 +48,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -100,8 +104,18 @@ __device__ __forceinline__ u32x2 i8x4_bf16(uint32_t w) {
   return u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
 }
 
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+// four int8 -> four fp16 (exact: |v| <= 128 < 2^11), as two packed pairs
+__device__ __forceinline__ u32x2 i8x4_f16(uint32_t w) {
+  const f16x2 a = {static_cast<_Float16>(static_cast<float>(static_cast<int8_t>(w))),
+                   static_cast<_Float16>(static_cast<float>(static_cast<int8_t>(w >> 8)))};
+  const f16x2 b = {static_cast<_Float16>(static_cast<float>(static_cast<int8_t>(w >> 16))),
+                   static_cast<_Float16>(static_cast<float>(static_cast<int8_t>(w >> 24)))};
+  return u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+}
+
+// two floats -> a packed fp16 pair, each rounded to nearest
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  const f16x2 v = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
   return __builtin_bit_cast(uint32_t, v);
 }
 
@@ -109,6 +123,12 @@ __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b),
                                                  c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b),
+                                                c, 0, 0, 0);
 }
 
 // A page of one KV head is loaded in 18 parts: 8 of keys and 8 of values
@@ -173,8 +193,8 @@ struct Pages {
       st.d[j] = load16(rsrc(base, bytes), off);
     }
   }
-  // the same wave's parts turned into bf16 tiles: keys [token][dim] (row
-  // stride kKStride), values [dim][slot] (row stride kVStride) with token
+  // the same wave's parts turned into tiles: bf16 keys [token][dim] (row
+  // stride kKStride), fp16 values [dim][slot] (row stride kVStride) with token
   // 4g+e of the low half at slot 8g+e and token 16+4g+e at slot 8g+4+e, then
   // the fp32 key and value scales
   template <int h>
@@ -196,10 +216,10 @@ struct Pages {
         const int f = 64 * (e - 8) + lane;  // dim f / 2, tokens 16 (f % 2) ..
         char *row = buf + kKBytes + (f >> 1) * kVStride + 8 * (f & 1);
         // tokens 16 h + 4 i .. +3 -> slots 8 i + 4 h .. +3
-        *reinterpret_cast<u32x2 *>(row + 0) = i8x4_bf16(v.x);
-        *reinterpret_cast<u32x2 *>(row + 16) = i8x4_bf16(v.y);
-        *reinterpret_cast<u32x2 *>(row + 32) = i8x4_bf16(v.z);
-        *reinterpret_cast<u32x2 *>(row + 48) = i8x4_bf16(v.w);
+        *reinterpret_cast<u32x2 *>(row + 0) = i8x4_f16(v.x);
+        *reinterpret_cast<u32x2 *>(row + 16) = i8x4_f16(v.y);
+        *reinterpret_cast<u32x2 *>(row + 32) = i8x4_f16(v.z);
+        *reinterpret_cast<u32x2 *>(row + 48) = i8x4_f16(v.w);
       } else if (e < kCopies) {
         *reinterpret_cast<u32x4 *>(buf + kKBytes + kVBytes +
                                    (e == 16 ? 0 : kScaleArea) + 16 * lane) = v;
@@ -252,6 +272,13 @@ __global__ __launch_bounds__(64 * (G + kLoaders)) void tree_attn_kernel(AttnArgs
 #pragma unroll
   for (int i = 0; i < 16; ++i) o[i] = fz;
   float m = -INFINITY, lsum = 0.0f;
+  // A power of two at or above every value scale seen so far: the value
+  // product's B operand is P'' = p * v_scale / vlim, at most 2^8, so fp16
+  // carries it without overflow whatever the scales, and vlim tracks the
+  // largest scale so that typical terms stay normal fp16 numbers.  When a
+  // page's scale passes vlim, vlim moves up to a power of two at or above it
+  // and the running output is rescaled by the (exact) ratio of the two.
+  float vlim = 0x1.0p-126f;
 
   auto compute_page = [&](const char *buf, int lp) {
     // scores S^T[token 16 c + 4 gq + r][node n]
@@ -315,28 +342,35 @@ __global__ __launch_bounds__(64 * (G + kLoaders)) void tree_attn_kernel(AttnArgs
       ps += p[i];
     }
     lsum += ps;
-    // P'^T as the B operand: slot 8 gq + e <- token 4 gq + e (e < 4) and
-    // 16 + 4 gq + e - 4 (e >= 4), exactly the order of p[].  P' = p * v_scale
-    // is split into a bf16 head and a bf16 tail (P' - head, rounded), and the
-    // value tile is multiplied by both: the pair carries 16 significant bits,
-    // so the value product moves each term by a relative 2^-16 at most
-    // instead of the 2^-8 of one bf16.
-    float pv[8];
+    // the page's largest value scale (all 32 tokens: 8 in each lane group)
+    float vm = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pv[i] = p[i] * vsc[i];
-    u32x4 ph, pl;
+    for (int i = 0; i < 8; ++i) vm = fmaxf(vm, fabsf(vsc[i]));
+    vm = fmaxf(vm, __shfl_xor(vm, 16, 64));
+    vm = fmaxf(vm, __shfl_xor(vm, 32, 64));
+    if (__ballot(vm > vlim) != 0) {  // wave-uniform: vm is the same in every lane
+      int ex;
+      (void)frexpf(vm, &ex);  // vm < 2^ex
+      const float nl = ldexpf(1.0f, ex);
+      const float f = vlim / nl;  // a power of two, exact
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ph[i] = pack_bf16(pv[2 * i], pv[2 * i + 1]);
-      pl[i] = pack_bf16(pv[2 * i] - __uint_as_float(ph[i] << 16),
-                        pv[2 * i + 1] - __uint_as_float(ph[i] & 0xFFFF0000u));
+      for (int i = 0; i < 16; ++i) o[i] *= f;
+      vlim = nl;
     }
+    const float rl = 1.0f / vlim;  // exact: vlim is a power of two
+    // P''^T as the B operand: slot 8 gq + e <- token 4 gq + e (e < 4) and
+    // 16 + 4 gq + e - 4 (e >= 4), exactly the order of p[].  Each P'' is
+    // rounded to fp16 (11 significant bits, a relative 2^-11 at most) and
+    // meets the exact fp16 values in one MFMA per value tile.
+    u32x4 pf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      pf[i] = pack_f16(p[2 * i] * vsc[2 * i] * rl, p[2 * i + 1] * vsc[2 * i + 1] * rl);
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) {
       const u32x4 va = *reinterpret_cast<const u32x4 *>(
           buf + kKBytes + (16 * dt + n) * kVStride + 16 * gq);
-      o[dt] = mfma(va, ph, o[dt]);
-      o[dt] = mfma(va, pl, o[dt]);
+      o[dt] = mfma_f16(va, pf, o[dt]);
     }
   };
 
@@ -413,7 +447,7 @@ __global__ __launch_bounds__(64 * (G + kLoaders)) void tree_attn_kernel(AttnArgs
   lsum += __shfl_xor(lsum, 32, 64);
   if (n >= a.M) return;
   if (a.splits == 1) {
-    const float inv = 1.0f / lsum;
+    const float inv = vlim / lsum;
     float *dst = a.out + (static_cast<size_t>(n) * a.Hq + hq) * kD + 4 * gq;
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt)
@@ -423,7 +457,7 @@ __global__ __launch_bounds__(64 * (G + kLoaders)) void tree_attn_kernel(AttnArgs
     float *dst = a.part + row * kD + 4 * gq;
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt)
-      *reinterpret_cast<f32x4 *>(dst + 16 * dt) = o[dt];
+      *reinterpret_cast<f32x4 *>(dst + 16 * dt) = o[dt] * vlim;
     if (gq == 0) {
       float *ml = a.part + static_cast<size_t>(a.splits) * a.Hq * a.M * kD;
       ml[2 * row] = m;

@@ -2,12 +2,13 @@
 
 Tolerance, from the arithmetic (tests/helpers.py, ATTN_REL): the scores are
 exact bf16 x int8 products summed in fp32, the softmax runs in fp32 with the
-hardware exp2, and each probability times its value scale enters the value
-product as a bf16 pair (head + tail, 16 significant bits).  Every output
-element is checked against |o_gpu - o| <= (2^-12 + 2^-14) * sum_p w_p |v_p|
-+ 1e-7, with sum_p w_p |v_p| returned by the oracle for that element.  At the
-benchmarked 32K context that bound rejects an output that lost the values of
-1/64 of the pages by a wide margin (tests/test_attn_bound.py).
+hardware exp2, and each probability times its value scale (over a power of
+two) enters the value product rounded to fp16 against exact fp16 values.
+Every output element is checked against |o_gpu - o| <= (2^-11 + 2^-12 +
+2^-14) * sum_p w_p |v_p| + 1e-7, with sum_p w_p |v_p| returned by the oracle
+for that element.  At the benchmarked 32K context that bound rejects an
+output that lost the values of 1/256 of the pages
+(tests/test_attn_bound.py).
 """
 from __future__ import annotations
 
