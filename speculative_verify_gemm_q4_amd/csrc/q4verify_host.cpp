@@ -4,6 +4,7 @@
 // device's architecture.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstring>
 
@@ -220,7 +221,10 @@ bool plan_kslice(int M, int64_t N, int64_t K, int cus, int parts, int seq,
                       (seq > 1 ? kInMaxTilesPlanar * 1024 : 0)
       : rt == 2 ? kslice_batch2(waves, seq > 1) * waves * 2048 +
                       (seq > 1 ? kInMaxTiles * 2048 : 0)
-                : kslice_batch(waves) * waves * 1024 + (seq > 1 ? kInMaxTiles * 1024 : 0));
+      : seq > 1 ? kslice_batch(waves) * waves * 1024 + kInMaxTiles * 1024
+                // one part, at most 10 waves: the activation rows go straight
+                // to LDS, 16 KB per wave, in the partial-sum area
+                : std::max(kslice_batch(waves), waves <= 10 ? 16 : 0) * waves * 1024);
   p.k_parts = static_cast<uint32_t>(parts);
   p.k_seq_parts = static_cast<uint32_t>(seq);
   p.m_tiles = static_cast<uint32_t>(rt);

@@ -870,7 +870,11 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
                      : kDot    ? kslice_batch(W) - 4
                                : kslice_batch(W);
   static_assert(NB * RT >= 8, "the activation staging areas (8 KB per wave) fit in part");
-  __shared__ f32x4 part[NB * W * RT * 64];
+  // kDmaX: the activation rows go from memory straight to LDS, both of a
+  // wave's units at once (16 KB per wave, at most 10 waves in 160 KB)
+  constexpr bool kDmaX = !kPlanar && !kSample && !kSeq && !kDot && RT == 1 && W <= 10;
+  constexpr int kPartTiles = kDmaX && NB < 16 ? 16 : NB;  // 1 KB per wave and tile
+  __shared__ f32x4 part[kPartTiles * W * RT * 64];
   // planar: each wave's two records of codes of the next tile (16 rows x
   // 128 B each), and the workgroup's scales and biases of the current and
   // the next tile, written by the loads themselves
@@ -1252,27 +1256,53 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
       // wave's 8 KB area, and lane (j, kb) reads chunk 8 gi + w of row j for
       // operand (gi, h): the XOR keeps both sides free of bank conflicts.
       // (unit u: record qu of the wave's records, rows 16 ru .. 16 ru + 15)
+      // Without planar codes, and when the partial-sum area holds 16 KB per
+      // wave, both units go straight from memory to LDS (load i of unit u
+      // to u * 8 KB + i * 1 KB, lane l at l * 16, so lane l loads the chunk
+      // that belongs at its place: (l & 31) ^ (r & 7)), and only then are
+      // the first tile's weights requested.
+      char *area = reinterpret_cast<char *>(part) + wave * (kDmaX ? 16384 : 8192);
       u32x4 xrow[2][8];
+      if constexpr (kDmaX) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int qu = RT == 1 ? u : 0, ru = RT == 1 ? 0 : u;
+        for (int u = 0; u < 2; ++u) {
+          const int qu = RT == 1 ? u : 0, ru = RT == 1 ? 0 : u;
 #pragma unroll
-        for (int i = 0; i < kRowLoads; ++i) {
-          const uint32_t r = 16 * ru + 2 * i + (lane >> 5);
-          const uint32_t off = (r * K + 256 * (q0 + qu) + 8 * (lane & 31)) * 2;
-          xrow[u][i] = buffer_load16<0>(xr, off, qu < nq ? 0u : 0x7FFFFFF0u);
+          for (int i = 0; i < kRowLoads; ++i) {
+            const uint32_t rl = 2 * i + (lane >> 5);
+            const uint32_t off = ((16 * ru + rl) * K + 256 * (q0 + qu) +
+                                  8 * ((lane & 31) ^ (rl & 7))) * 2;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                xr, (__attribute__((address_space(3))) void *)(area + u * 8192 + i * 1024), 16,
+                off, qu < nq ? 0u : 0x7FFFFFF0u, 0, 0);
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the rows are in LDS
+        asm volatile("" ::: "memory");
+      } else {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int qu = RT == 1 ? u : 0, ru = RT == 1 ? 0 : u;
+#pragma unroll
+          for (int i = 0; i < kRowLoads; ++i) {
+            const uint32_t r = 16 * ru + 2 * i + (lane >> 5);
+            const uint32_t off = (r * K + 256 * (q0 + qu) + 8 * (lane & 31)) * 2;
+            xrow[u][i] = buffer_load16<0>(xr, off, qu < nq ? 0u : 0x7FFFFFF0u);
+          }
         }
       }
       load(st[0]);
       if constexpr (S > 2) load(st[1]);
-      char *area = reinterpret_cast<char *>(part) + wave * 8192;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
+        char *uarea = area + (kDmaX ? u * 8192 : 0);
+        if constexpr (!kDmaX) {
 #pragma unroll
-        for (int i = 0; i < kRowLoads; ++i) {
-          const int r = 2 * i + (lane >> 5);
-          const int c = (lane & 31) ^ (r & 7);
-          *reinterpret_cast<u32x4 *>(area + r * 512 + c * 16) = xrow[u][i];
+          for (int i = 0; i < kRowLoads; ++i) {
+            const int r = 2 * i + (lane >> 5);
+            const int c = (lane & 31) ^ (r & 7);
+            *reinterpret_cast<u32x4 *>(area + r * 512 + c * 16) = xrow[u][i];
+          }
         }
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi)
@@ -1281,7 +1311,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
             const int c = (8 * gi + (h ? w_h1 : w_h0)) ^ (j & 7);
             // rows past the loaded pairs are zeros (not in the area)
             const u32x4 v = j < 2 * kRowLoads
-                                 ? *reinterpret_cast<const u32x4 *>(area + j * 512 + c * 16)
+                                 ? *reinterpret_cast<const u32x4 *>(uarea + j * 512 + c * 16)
                                  : u32x4{0u, 0u, 0u, 0u};
             xa[u][gi][h] = kPlanar ? pair_activations(v) : v;
           }

@@ -288,7 +288,8 @@ def kslice_model(M, N, K, p):
         fixed = tacc
         NB = (LDS_BYTES - IN_MAX_TILES * 1024) // (W * 1024)
     assert NB * RT >= 8  # the activation staging areas alias the partial sums
-    assert p["lds_bytes"] == NB * W * 1024 * RT + fixed <= LDS_BYTES
+    part_tiles = max(NB, 16) if kslice_dma_x(W, planar, RT, Pin > 1) else NB
+    assert p["lds_bytes"] == part_tiles * W * 1024 * RT + fixed <= LDS_BYTES
     assert p["workspace_bytes"] == (P - 1) * M * N * 4
     hits = np.zeros((T, Q), dtype=np.int32)
     writes = np.zeros((P, T), dtype=np.int32)
@@ -319,7 +320,7 @@ def kslice_model(M, N, K, p):
             assert qd * (pp + 1) + small_div_model(qr * (pp + 1), Ptot) - qa == nrec
         if row_pairs(M, RT, Pin > 1):
             kslice_row_staging_model(M, K, W, p["lds_bytes"] - tacc, qa, nrec,
-                                     planar, RT)
+                                     planar, RT, kslice_dma_x(W, planar, RT, Pin > 1))
         else:
             direct_operand_loads(M, K, W, qa, nrec, planar, RT)
     G8 = K // 64
@@ -477,8 +478,15 @@ def small_div_model(a, d):
     return out.pop()
 
 
+def kslice_dma_x(W, planar, RT, seq):
+    """Whether the activation rows go from memory straight to LDS: both
+    units of a wave at once in a 16 KB area (tiled layout, one part of K,
+    one row tile, at most 10 waves)."""
+    return not planar and RT == 1 and not seq and W <= 10
+
+
 def kslice_row_staging_model(M, K, W, lds_bytes, qa, nrec, planar=False,
-                             RT=1):
+                             RT=1, dma=False):
     """The activations arrive by row-contiguous loads (row_pairs(M, RT)
     loads of two rows per record) and pass through an 8 KB LDS area per
     wave; rows from 2 row_pairs on are zeros without a load or an LDS read.
@@ -487,21 +495,27 @@ def kslice_row_staging_model(M, K, W, lds_bytes, qa, nrec, planar=False,
     record), or zeros for rows >= M; the LDS stores of one round must not
     collide, and the areas must fit.  The part's records are
     [qa, qa + nrec); unit u is record u of the wave's two (RT = 1) or rows
-    16 u .. of its one record (RT = 2)."""
+    16 u .. of its one record (RT = 2).  With dma the loads write LDS
+    themselves: lane l of load i of unit u lands at the wave's area + 8 KB u
+    + 1 KB i + 16 l, so it loads the chunk that belongs there,
+    (l & 31) ^ (r & 7), and the area is 16 KB per wave."""
     x_bytes = M * K * 2
     R = 1 if RT == 2 else 2
     LR = row_pairs(M, RT)
     assert 2 * LR >= min(M, 16)
-    assert W * 8192 <= lds_bytes
+    span = 16384 if dma else 8192
+    assert W * span <= lds_bytes
     for w in range(W):
         nq = min(max(nrec - R * w, 0), R)
         for u in range(2):
             qq, ru = (u, 0) if RT == 1 else (0, u)
+            base = w * span + (8192 * u if dma else 0)
             # what lane l of load i holds: (row, input) or None (zeros)
             area = {}
             for i in range(LR):
                 for lane in range(64):
-                    r, c = 2 * i + (lane >> 5), lane & 31
+                    r = 2 * i + (lane >> 5)
+                    c = (lane & 31) ^ (r & 7) if dma else lane & 31
                     row = 16 * ru + r
                     k = 256 * (qa + R * w + qq) + 8 * c
                     off = (row * K + k) * 2
@@ -511,7 +525,9 @@ def kslice_row_staging_model(M, K, W, lds_bytes, qa, nrec, planar=False,
                     else:
                         assert off + (0 if qq < nq else 0x7FFFFFF0) >= x_bytes
                         val = None
-                    addr = w * 8192 + r * 512 + (c ^ (r & 7)) * 16
+                    addr = (base + 1024 * i + 16 * lane if dma
+                            else base + r * 512 + (c ^ (r & 7)) * 16)
+                    assert addr == base + r * 512 + (c ^ (r & 7)) * 16
                     assert addr not in area
                     area[addr] = val
             assert len(area) == 64 * LR
@@ -521,7 +537,7 @@ def kslice_row_staging_model(M, K, W, lds_bytes, qa, nrec, planar=False,
                     for h in range(2):
                         wd = planar_word(j, kb, h) if planar else 2 * kb + h
                         c = (8 * gi + wd) ^ (j & 7)
-                        got = area[w * 8192 + j * 512 + c * 16] if j < 2 * LR else None
+                        got = area[base + j * 512 + c * 16] if j < 2 * LR else None
                         k = 256 * (qa + R * w + qq) + 64 * gi + 8 * wd
                         row = 16 * ru + j
                         want = (row, k) if (qq < nq and row < M) else None
