@@ -871,9 +871,12 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
                                : kslice_batch(W);
   static_assert(NB * RT >= 8, "the activation staging areas (8 KB per wave) fit in part");
   // kDmaX: the activation rows go from memory straight to LDS, both of a
-  // wave's units at once (16 KB per wave, at most 10 waves in 160 KB)
-  constexpr bool kDmaX = !kPlanar && !kSample && !kSeq && !kDot && RT == 1 && W <= 10;
-  constexpr int kPartTiles = kDmaX && NB < 16 ? 16 : NB;  // 1 KB per wave and tile
+  // wave's units at once (kXU KB each: 1 KB per row pair), when the
+  // partial-sum area holds them or can grow to (tiled, at most 10 waves)
+  constexpr int kXU = kRowLoads > 0 ? kRowLoads : 1;
+  constexpr bool kDmaX = !kSample && !kSeq && !kDot && RT == 1 && kRowLoads > 0 &&
+                         (2 * kXU <= NB || (!kPlanar && W <= 10));
+  constexpr int kPartTiles = kDmaX && NB < 2 * kXU ? 2 * kXU : NB;  // 1 KB per wave and tile
   __shared__ f32x4 part[kPartTiles * W * RT * 64];
   // planar: each wave's two records of codes of the next tile (16 rows x
   // 128 B each), and the workgroup's scales and biases of the current and
@@ -1256,12 +1259,11 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
       // wave's 8 KB area, and lane (j, kb) reads chunk 8 gi + w of row j for
       // operand (gi, h): the XOR keeps both sides free of bank conflicts.
       // (unit u: record qu of the wave's records, rows 16 ru .. 16 ru + 15)
-      // Without planar codes, and when the partial-sum area holds 16 KB per
-      // wave, both units go straight from memory to LDS (load i of unit u
-      // to u * 8 KB + i * 1 KB, lane l at l * 16, so lane l loads the chunk
-      // that belongs at its place: (l & 31) ^ (r & 7)), and only then are
-      // the first tile's weights requested.
-      char *area = reinterpret_cast<char *>(part) + wave * (kDmaX ? 16384 : 8192);
+      // With kDmaX both units go straight from memory to LDS (load i of
+      // unit u to u kXU KB + i KB, lane l at l * 16, so lane l loads the
+      // chunk that belongs at its place: (l & 31) ^ (r & 7)), and only then
+      // are the first tile's weights requested.
+      char *area = reinterpret_cast<char *>(part) + wave * (kDmaX ? 2 * kXU * 1024 : 8192);
       u32x4 xrow[2][8];
       if constexpr (kDmaX) {
 #pragma unroll
@@ -1273,7 +1275,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
             const uint32_t off = ((16 * ru + rl) * K + 256 * (q0 + qu) +
                                   8 * ((lane & 31) ^ (rl & 7))) * 2;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                xr, (__attribute__((address_space(3))) void *)(area + u * 8192 + i * 1024), 16,
+                xr, (__attribute__((address_space(3))) void *)(area + (u * kXU + i) * 1024), 16,
                 off, qu < nq ? 0u : 0x7FFFFFF0u, 0, 0);
           }
         }
@@ -1295,7 +1297,7 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
       if constexpr (S > 2) load(st[1]);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        char *uarea = area + (kDmaX ? u * 8192 : 0);
+        char *uarea = area + (kDmaX ? u * kXU * 1024 : 0);
         if constexpr (!kDmaX) {
 #pragma unroll
           for (int i = 0; i < kRowLoads; ++i) {

@@ -288,7 +288,8 @@ def kslice_model(M, N, K, p):
         fixed = tacc
         NB = (LDS_BYTES - IN_MAX_TILES * 1024) // (W * 1024)
     assert NB * RT >= 8  # the activation staging areas alias the partial sums
-    part_tiles = max(NB, 16) if kslice_dma_x(W, planar, RT, Pin > 1) else NB
+    # the plan sizes the area for the tiled kernel's 8 row pairs (M > 4)
+    part_tiles = max(NB, 16) if kslice_dma_x(W, planar, RT, Pin > 1, 8, NB) else NB
     assert p["lds_bytes"] == part_tiles * W * 1024 * RT + fixed <= LDS_BYTES
     assert p["workspace_bytes"] == (P - 1) * M * N * 4
     hits = np.zeros((T, Q), dtype=np.int32)
@@ -318,9 +319,11 @@ def kslice_model(M, N, K, p):
         if Ptot > 1:
             assert qd * pp + small_div_model(qr * pp, Ptot) == qa
             assert qd * (pp + 1) + small_div_model(qr * (pp + 1), Ptot) - qa == nrec
-        if row_pairs(M, RT, Pin > 1):
+        LR = row_pairs(M, RT, Pin > 1)
+        if LR:
             kslice_row_staging_model(M, K, W, p["lds_bytes"] - tacc, qa, nrec,
-                                     planar, RT, kslice_dma_x(W, planar, RT, Pin > 1))
+                                     planar, RT,
+                                     kslice_dma_x(W, planar, RT, Pin > 1, LR, NB))
         else:
             direct_operand_loads(M, K, W, qa, nrec, planar, RT)
     G8 = K // 64
@@ -478,11 +481,13 @@ def small_div_model(a, d):
     return out.pop()
 
 
-def kslice_dma_x(W, planar, RT, seq):
+def kslice_dma_x(W, planar, RT, seq, LR, NB):
     """Whether the activation rows go from memory straight to LDS: both
-    units of a wave at once in a 16 KB area (tiled layout, one part of K,
-    one row tile, at most 10 waves)."""
-    return not planar and RT == 1 and not seq and W <= 10
+    units of a wave at once, LR KB each (one part of K, one row tile), when
+    the partial-sum area of NB tiles holds them or, tiled with at most 10
+    waves, grows to."""
+    return (RT == 1 and not seq and LR > 0 and
+            (2 * LR <= NB or (not planar and W <= 10)))
 
 
 def kslice_row_staging_model(M, K, W, lds_bytes, qa, nrec, planar=False,
@@ -503,13 +508,13 @@ def kslice_row_staging_model(M, K, W, lds_bytes, qa, nrec, planar=False,
     R = 1 if RT == 2 else 2
     LR = row_pairs(M, RT)
     assert 2 * LR >= min(M, 16)
-    span = 16384 if dma else 8192
+    span = 2048 * LR if dma else 8192
     assert W * span <= lds_bytes
     for w in range(W):
         nq = min(max(nrec - R * w, 0), R)
         for u in range(2):
             qq, ru = (u, 0) if RT == 1 else (0, u)
-            base = w * span + (8192 * u if dma else 0)
+            base = w * span + (1024 * LR * u if dma else 0)
             # what lane l of load i holds: (row, input) or None (zeros)
             area = {}
             for i in range(LR):
