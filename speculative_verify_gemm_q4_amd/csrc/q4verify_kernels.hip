@@ -788,23 +788,25 @@ __device__ __forceinline__ void kslice_lds_barrier() {
 // [t0, t1); its W = ceil(Q / 2) waves all work on the same tile at once,
 // wave w on records 2w and 2w + 1 of it, so that the workgroup reads each
 // tile's 46 KB (at K = 5120) as one contiguous run:
-//  * the wave loads its two records' activations once, straight into MFMA
-//    operand registers (lane (j, kb), half h: inputs 64 gi + 16 kb + 8 h ..
-//    +7 of row j of record q; rows >= M, and a second record past K, fall
-//    past the resource and read as zeros), and forms the seed
-//    -128 * sum(x) of each of its 8 groups once, with two MFMAs per group --
-//    not per tile;
+//  * the wave loads its two records' activations once into MFMA operand
+//    registers (lane (j, kb), half h: inputs 64 gi + 16 kb + 8 h .. +7 of
+//    row j of record q; rows >= M, and a second record past K, are zeros),
+//    and forms the seed -128 * sum(x) of each of its 8 groups once, with
+//    two MFMAs per group -- not per tile;
 //  * per tile it multiplies its two records (two MFMAs per group, seeded
 //    with that group's sum) and writes its partial 16 x 16 sum to LDS;
 //  * every kslice_batch(W) tiles the workgroup adds the waves' partial sums
 //    in wave order and writes y.
-// The activation loads are issued first, without branches, then the first
-// tile's weights, so that the seed MFMAs wait for the activations alone.
-// For M >= 8 they are row-contiguous (each load brings 512 B runs of two
-// rows) and pass through LDS into the operand layout: loads straight in the
-// operand layout touch 16 rows 2K bytes apart each, which the L2 serves far
-// more slowly (the first tile at M = 16 came 2 us later).  The weights of
-// tile t + 1 are in flight while tile t is multiplied.
+// The activation loads are issued first, without branches, and the first
+// tile's weights after them.  They are row-contiguous (each load brings
+// 512 B runs of two rows; only the row pairs below M at M <= 4) and pass
+// through LDS into the operand layout, most often written by the loads
+// themselves: loads straight in the operand layout touch 16 rows 2K bytes
+// apart each, which the L2 serves far more slowly (the first tile at M = 16
+// came 2 us later), and at small M they issue 16 instructions for a few
+// active lanes each.  Only parts of K taken in turn at M <= 4 keep the
+// operand-layout loads.  The weights of tile t + 1 are in flight while tile
+// t is multiplied.
 //
 // With a workspace, K beyond 24 records is cut into P parts: the grid is P
 // groups of Gt workgroups, the group of part p takes records
@@ -1505,9 +1507,10 @@ void launch_kslice_v(const q4_plan &p, const void *x, const void *Wt, float *y,
   if (RT == 2 || M > 4)
     go(std::integral_constant<int, 8>{});
   else if constexpr (kSeq)
-    // parts of K in turn repeat the activation staging per part: there the
-    // direct loads measured faster at M <= 4 (down, three parts: 20.3
-    // against 22.0 us at M = 1)
+    // parts of K in turn repeat the activation staging per part, with its
+    // barrier: there the direct loads measured faster at M <= 4 (down, three
+    // parts: 19.3 against 22.0 us at M = 1 with the rows staged in LDS
+    // through registers, and against 22.1 us with the loads writing LDS)
     go(std::integral_constant<int, 0>{});
   else if (M > 2)
     go(std::integral_constant<int, 2>{});
