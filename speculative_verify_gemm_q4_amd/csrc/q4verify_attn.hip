@@ -12,7 +12,8 @@
 //
 // Kernel 1 (tree_attn_kernel<G>): a workgroup per (KV head, run of pages),
 // one compute wave per query head of that KV head (G = Hq / Hkv) and two
-// loader waves.
+// loader waves; when the runs fill at most half the CUs, two workgroups per
+// (KV head, run), each with G = Hq / Hkv / 2 of its query heads.
 //  * Per page the loader waves load the 8 KiB of keys ([32 tokens][256])
 //    and 8 KiB of values (stored transposed, [256][32]) with their scales
 //    into their registers, four pages ahead, turn the int8 keys into bf16
@@ -80,6 +81,7 @@ struct AttnArgs {
   int32_t *status;
   int M, Hq, Hkv, pool, ctx, pages, splits;
   float scale2;  // softmax scale times log2(e)
+  int hsplit;    // workgroups per (KV head, run), each G of its query heads
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p,
@@ -239,9 +241,15 @@ __global__ __launch_bounds__(64 * (G + kLoaders)) void tree_attn_kernel(AttnArgs
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int n = lane & 15;   // tree node of this lane's score/output column
   const int gq = lane >> 4;  // lane group: k slots 8 gq .. 8 gq + 7
-  const int g = blockIdx.x % a.Hkv;
-  const int run = blockIdx.x / a.Hkv;
-  const int hq = g * G + (w < G ? w : 0);  // (loader waves: unused)
+  // block = (head group, run, KV head), the KV head fastest: the head
+  // groups of one (KV head, run) read the same pages, on the same XCD when
+  // runs x KV heads is a multiple of 8
+  const int per = a.splits * a.Hkv;
+  const int hgrp = static_cast<int>(blockIdx.x) / per;
+  const int bb = static_cast<int>(blockIdx.x) - hgrp * per;
+  const int g = bb % a.Hkv;
+  const int run = bb / a.Hkv;
+  const int hq = (g * a.hsplit + hgrp) * G + (w < G ? w : 0);  // (loader waves: unused)
   const int pa = static_cast<int>(static_cast<int64_t>(a.pages) * run / a.splits);
   const int pb = static_cast<int>(static_cast<int64_t>(a.pages) * (run + 1) / a.splits);
   const int len = pb - pa;  // 1 .. kMaxRun (the plan sees to it)
@@ -603,12 +611,24 @@ extern "C" int q4_tree_attn(const void *q, int M, int Hq, int Hkv, int D,
                   v_scale, page_table, anc, out,
                   static_cast<float *>(workspace), status, M, Hq, Hkv,
                   pool_pages, static_cast<int>(ctx_len), pages, s,
-                  scale * q4v::kLog2e};
+                  scale * q4v::kLog2e, 1};
+  // When the runs leave half the CUs or more idle (short contexts: at least
+  // 4 pages a run), each (KV head, run) takes two workgroups of half its
+  // query heads: each page is computed by twice as many SIMDs, and read
+  // twice, the second time mostly from the XCD's L2.
+  const int G = Hq / Hkv;
+  if (G % 2 == 0 && 2 * static_cast<int64_t>(s) * Hkv <= q4v::device_cus()) a.hsplit = 2;
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  const dim3 grid(static_cast<uint32_t>(s * Hkv));
-  switch (Hq / Hkv) {
+  const dim3 grid(static_cast<uint32_t>(s * Hkv * a.hsplit));
+  switch (G / a.hsplit) {
+    case 1:
+      hipLaunchKernelGGL(q4v::tree_attn_kernel<1>, grid, dim3(64 + 64 * q4v::kLoaders), 0, hs, a);
+      break;
     case 2:
       hipLaunchKernelGGL(q4v::tree_attn_kernel<2>, grid, dim3(128 + 64 * q4v::kLoaders), 0, hs, a);
+      break;
+    case 3:
+      hipLaunchKernelGGL(q4v::tree_attn_kernel<3>, grid, dim3(192 + 64 * q4v::kLoaders), 0, hs, a);
       break;
     case 4:
       hipLaunchKernelGGL(q4v::tree_attn_kernel<4>, grid, dim3(256 + 64 * q4v::kLoaders), 0, hs, a);
