@@ -160,6 +160,28 @@ __device__ __forceinline__ void wait_vm0() {
   asm volatile("" ::: "memory");
 }
 
+// Reductions over the four lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48)
+// with the gfx950 permlane swaps: each swap of a register with itself leaves
+// x[l] in one result and x[l ^ J] in the other, on the VALU, so the softmax's
+// maxima and sums take no LDS round trip (an LDS permute would also wait for
+// every tile read issued before it).
+__device__ __forceinline__ float group_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t v = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group_sum(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t v = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <int H>
 struct Pages {
   static constexpr int NI = (kCopies + H - 1) / H;  // loads per wave and page
@@ -326,8 +348,7 @@ __global__ __launch_bounds__(64 * (G + kLoaders)) void tree_attn_kernel(AttnArgs
         pm = fmaxf(pm, s);
       }
     }
-    pm = fmaxf(pm, __shfl_xor(pm, 16, 64));
-    pm = fmaxf(pm, __shfl_xor(pm, 32, 64));
+    pm = group_max(pm);
     // The reference maximum m moves only when some node's score passes it
     // by more than kLazyMax (base 2), so the exponentials stay below
     // 2^kLazyMax and the running output is rescaled on few pages.  The
@@ -354,8 +375,7 @@ __global__ __launch_bounds__(64 * (G + kLoaders)) void tree_attn_kernel(AttnArgs
     float vm = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) vm = fmaxf(vm, fabsf(vsc[i]));
-    vm = fmaxf(vm, __shfl_xor(vm, 16, 64));
-    vm = fmaxf(vm, __shfl_xor(vm, 32, 64));
+    vm = group_max(vm);
     if (__ballot(vm > vlim) != 0) {  // wave-uniform: vm is the same in every lane
       int ex;
       (void)frexpf(vm, &ex);  // vm < 2^ex
@@ -451,8 +471,7 @@ __global__ __launch_bounds__(64 * (G + kLoaders)) void tree_attn_kernel(AttnArgs
     lds_barrier();
   }
 
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
+  lsum = group_sum(lsum);
   if (n >= a.M) return;
   if (a.splits == 1) {
     const float inv = vlim / lsum;
