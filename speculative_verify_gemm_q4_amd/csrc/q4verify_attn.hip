@@ -40,6 +40,7 @@
 // results are merged with their max and sum.
 #include <hip/hip_runtime.h>
 
+#include <cfloat>
 #include <type_traits>
 
 #include "q4v_internal.h"
@@ -223,7 +224,7 @@ struct Pages {
   // the fp32 key and value scales
   template <int h>
   __device__ __forceinline__ static void convert(const Stage &st, char *buf,
-                                                 int lane) {
+                                                 int lane, float scale2) {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int e = h + H * j;  // a constant once unrolled
@@ -244,9 +245,26 @@ struct Pages {
         *reinterpret_cast<u32x2 *>(row + 16) = i8x4_f16(v.y);
         *reinterpret_cast<u32x2 *>(row + 32) = i8x4_f16(v.z);
         *reinterpret_cast<u32x2 *>(row + 48) = i8x4_f16(v.w);
-      } else if (e < kCopies) {
-        *reinterpret_cast<u32x4 *>(buf + kKBytes + kVBytes +
-                                   (e == 16 ? 0 : kScaleArea) + 16 * lane) = v;
+      } else if (e == 16) {
+        // the key scales times the softmax scale (base 2)
+        const f32x4 ks = __builtin_bit_cast(f32x4, v) * scale2;
+        *reinterpret_cast<f32x4 *>(buf + kKBytes + kVBytes + 16 * lane) = ks;
+      } else if (e == 17) {
+        // the value scales, and after them (lane 8's first word, otherwise
+        // a zero) the page's largest |value scale|: the maximum over lanes
+        // 0..7 by quad swaps and a half-row mirror (DPP), taken from lane 0
+        float mx = fmaxf(fmaxf(fabsf(__uint_as_float(v.x)), fabsf(__uint_as_float(v.y))),
+                         fmaxf(fabsf(__uint_as_float(v.z)), fabsf(__uint_as_float(v.w))));
+        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_update_dpp(
+                           0, __float_as_int(mx), 0xB1, 0xF, 0xF, false)));
+        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_update_dpp(
+                           0, __float_as_int(mx), 0x4E, 0xF, 0xF, false)));
+        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_update_dpp(
+                           0, __float_as_int(mx), 0x141, 0xF, 0xF, false)));
+        const uint32_t pmx = __builtin_amdgcn_readlane(__float_as_uint(mx), 0);
+        u32x4 vv = v;
+        vv.x = lane == 8 ? pmx : vv.x;
+        *reinterpret_cast<u32x4 *>(buf + kKBytes + kVBytes + kScaleArea + 16 * lane) = vv;
       }
     }
   }
@@ -301,7 +319,10 @@ __global__ __launch_bounds__(64 * (G + kLoaders)) void tree_attn_kernel(AttnArgs
   f32x4 o[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) o[i] = fz;
-  float m = -INFINITY, lsum = 0.0f;
+  // The reference maximum starts at the lowest finite float rather than
+  // -inf, so that p - m is never inf - inf: a masked score (-inf) then
+  // gives exp2 = 0 with no test, and the first visible score moves m.
+  float m = -FLT_MAX, lsum = 0.0f;
   // A power of two at or above every value scale seen so far: the value
   // product's B operand is P'' = p * v_scale / vlim, at most 2^8, so fp16
   // carries it without overflow whatever the scales, and vlim tracks the
@@ -336,7 +357,7 @@ __global__ __launch_bounds__(64 * (G + kLoaders)) void tree_attn_kernel(AttnArgs
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tok = 16 * c + 4 * gq + r;
-        float s = sc[c][r] * ksv[r] * a.scale2;
+        float s = sc[c][r] * ksv[r];  // ksv: key scale x softmax scale
         bool vis = true;
         if (!all_visible) {
           const int t = pos0 + tok - a.ctx;
@@ -356,8 +377,9 @@ __global__ __launch_bounds__(64 * (G + kLoaders)) void tree_attn_kernel(AttnArgs
     // reference, so the result is the same softmax.
     if (__ballot(pm > m + kLazyMax) != 0) {  // a wave-uniform test
       const float mn = fmaxf(m, pm);
-      // with nothing visible yet (mn = -inf) nothing rescales
-      const float alpha = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
+      // exp2 of -FLT_MAX - mn is 0 at a node's first visible score, and
+      // 1 where nothing is visible yet (mn = m)
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
       lsum *= alpha;
       m = mn;
 #pragma unroll
@@ -366,16 +388,12 @@ __global__ __launch_bounds__(64 * (G + kLoaders)) void tree_attn_kernel(AttnArgs
     float ps = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      // a lane whose node has seen nothing visible (m = -inf) has p = -inf
-      p[i] = p[i] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(p[i] - m);
+      p[i] = __builtin_amdgcn_exp2f(p[i] - m);  // masked: exp2(-inf) = 0
       ps += p[i];
     }
     lsum += ps;
-    // the page's largest value scale (all 32 tokens: 8 in each lane group)
-    float vm = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) vm = fmaxf(vm, fabsf(vsc[i]));
-    vm = group_max(vm);
+    // the page's largest value scale, left by the loader after the scales
+    const float vm = vscale[kPage];
     if (__ballot(vm > vlim) != 0) {  // wave-uniform: vm is the same in every lane
       int ex;
       (void)frexpf(vm, &ex);  // vm < 2^ex
@@ -428,7 +446,7 @@ __global__ __launch_bounds__(64 * (G + kLoaders)) void tree_attn_kernel(AttnArgs
       load_page(1, st1);
       load_page(2, st2);
       load_page(3, st3);
-      P::template convert<h>(st0, tile0, lane);
+      P::template convert<h>(st0, tile0, lane, a.scale2);
       load_page(kRing, st0);
       lds_barrier();
       // A stage is reloaded right after its conversion, so that its
@@ -436,7 +454,7 @@ __global__ __launch_bounds__(64 * (G + kLoaders)) void tree_attn_kernel(AttnArgs
       // make the compiler wait for every load in flight).  Past the run the
       // conversion writes unused data into a tile no wave reads any more.
       auto step = [&](int i, Stage &st, char *tile) {
-        P::template convert<h>(st, tile, lane);
+        P::template convert<h>(st, tile, lane, a.scale2);
         load_page(i + 1 + kRing, st);
         lds_barrier();
       };
