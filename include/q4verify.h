@@ -524,17 +524,20 @@ int q4_gdn_tree_out(const float *S, int H, int Hk, int dv, int dk, int M,
  * (node j is i or one of its ancestors).  Query head h reads KV head
  * h / (Hq / Hkv).  The output is softmax(scale * q k^T) v over the visible
  * positions, with k = k8 * k_scale and v = v8 * v_scale.
- * Arithmetic: bf16 products on MFMA (the int8 values are exact in bf16), fp32
- * accumulation; each probability times its value scale enters the value
- * product as a pair of bf16 (head + tail, 16 significant bits).
+ * Arithmetic: scores as bf16 products on MFMA (the int8 keys are exact in
+ * bf16), fp32 accumulation; each probability times its value scale, divided
+ * by a power of two at or above every value scale seen so far, enters the
+ * value product rounded to fp16 (11 significant bits; the int8 values are
+ * exact in fp16).
  * ------------------------------------------------------------------------ */
 #define Q4_ATTN_HEAD_DIM 256
 #define Q4_ATTN_PAGE 32
 #define Q4_ATTN_MAX_NODES 16
 
 /* The split of the context a call would use, and the workspace it needs.
- * splits = 0 picks a split for the current device, > 0 asks for that many
- * runs of pages (at most the number of pages).  The shape rules are those of
+ * splits = 0 picks a split for the current device (runs of about 8 pages,
+ * at least 16 runs and at most one per CU for each KV head), > 0 asks for
+ * that many runs of pages (at most the number of pages).  The shape rules are those of
  * q4_tree_attn.  Errors: Q4_EINVAL. */
 int q4_tree_attn_plan(int M, int Hq, int Hkv, int D, int64_t ctx_len,
                       int splits, int *splits_used, uint64_t *workspace_bytes);

@@ -380,3 +380,27 @@ def test_dot_variant_argument_errors(lib):
     assert g(X, W, Y, 1, 5121, 5120, None) == -1    # N % 16
     assert g(X + 8, W, Y, 1, 5120, 5120, None) == -2
     assert g(X, W, Y, 4, 34816, 5120, None) == -4   # valid: stops at device
+
+
+def test_attention_split_plan(lib):
+    """The default split of q4_tree_attn_plan (256 CUs without a device):
+    runs of about 8 pages, at least 16 runs as the pages allow, at most one
+    per CU for each KV head, and never more than 1024 pages a run; the
+    workspace holds each run's partial outputs and (max, sum) pairs."""
+    M, Hq, Hkv = 16, 24, 4
+    cases = {32: 2, 2048: 16, 4096: 16, 8192: 32, 16384: 64, 32768: 64,
+             262144: 64, 1 << 20: 64}
+    for ctx, want in cases.items():
+        s, ws = q4.q4_tree_attn_plan(M, Hq, Hkv, ctx)
+        pages = -(-(ctx + M) // 32)
+        assert s == min(want, pages), (ctx, s)
+        assert -(-pages // s) <= 1024
+        assert ws == (0 if s == 1 else s * Hq * M * (256 + 2) * 4)
+    # runs longer than 1024 pages are split further (131073 pages)
+    assert q4.q4_tree_attn_plan(M, Hq, Hkv, 4 << 20)[0] == 129
+    assert q4.q4_tree_attn_plan(M, 12, 2, 4 << 20)[0] == 129
+    # fewer KV heads: up to one run per CU each
+    assert q4.q4_tree_attn_plan(M, 12, 2, 32768)[0] == 128
+    # an explicit split is taken as asked, capped at the pages
+    assert q4.q4_tree_attn_plan(M, Hq, Hkv, 4096, splits=7)[0] == 7
+    assert q4.q4_tree_attn_plan(M, Hq, Hkv, 100, splits=50)[0] == 4
