@@ -515,6 +515,7 @@ __global__ __launch_bounds__(64 * (G + kLoaders)) void tree_attn_kernel(AttnArgs
 // workgroup per (node, query head): the runs' weights go to LDS first, then
 // every thread sums its dimension over the runs with eight loads in flight.
 constexpr int kCombineMaxRuns = 2048;
+constexpr int kCombinePre = 16;  // runs whose partial outputs are all requested at once
 
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float *part,
                                                            float *out, int M,
@@ -526,6 +527,38 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float *part,
   const int d = threadIdx.x;
   const size_t rows = static_cast<size_t>(Hq) * M;
   const float *ml = part + static_cast<size_t>(splits) * rows * kD;
+  const float *src = part + static_cast<size_t>(row) * kD + d;
+  if (splits <= kCombinePre) {
+    // Few runs (short contexts): every partial output is requested at once,
+    // beside the runs' (max, sum) pairs, so the merge waits for one memory
+    // round trip instead of three; same sums in the same order.
+    float pv[kCombinePre];
+#pragma unroll
+    for (int i = 0; i < kCombinePre; ++i)
+      pv[i] = src[static_cast<size_t>(i < splits ? i : splits - 1) * rows * kD];
+    const int dr = d < splits ? d : splits - 1;
+    const float2 pr = *reinterpret_cast<const float2 *>(&ml[2 * (dr * rows + row)]);
+    const float mr = d < splits ? pr.x : -INFINITY;
+    float mx = mr;
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if ((d & 63) == 0) red[d >> 6] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float w = mr == -INFINITY ? 0.0f : exp2f(mr - mx);
+    if (d < splits) wgt[d] = w;
+    float den = d < splits ? w * pr.y : 0.0f;
+    for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o, 64);
+    __syncthreads();
+    if ((d & 63) == 0) red[4 + (d >> 6)] = den;
+    __syncthreads();
+    den = red[4] + red[5] + red[6] + red[7];
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kCombinePre; ++i)
+      if (i < splits) acc += wgt[i] * pv[i];
+    out[(static_cast<size_t>(n) * Hq + hq) * kD + d] = acc / den;
+    return;
+  }
   float mx = -INFINITY;
   for (int r = d; r < splits; r += 256) mx = fmaxf(mx, ml[2 * (r * rows + row)]);
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
@@ -544,7 +577,6 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float *part,
   if ((d & 63) == 0) red[4 + (d >> 6)] = den;
   __syncthreads();
   den = red[4] + red[5] + red[6] + red[7];
-  const float *src = part + static_cast<size_t>(row) * kD + d;
   float acc = 0.0f;
   int r = 0;
   for (; r + 8 <= splits; r += 8) {
