@@ -92,6 +92,10 @@ def _run(q4, inp, splits=0, status=None):
     (16, 12, 2, 0, 0), (1, 6, 1, 0, 0), (16, 24, 4, 31, 0), (16, 24, 4, 32, 2),
     (5, 8, 4, 257, 0), (9, 16, 4, 1000, 5), (16, 16, 2, 64, 0),
     (3, 32, 4, 500, 0),
+    # each workgroup width the launch picks (256 CUs): 3 of 6 heads (two
+    # head groups), 4 of 8, all 8, 4 of 4 and 2 of 2 (one group)
+    (16, 24, 4, 2100, 24), (16, 32, 4, 2100, 24), (16, 32, 4, 2100, 64),
+    (16, 16, 4, 2100, 64), (16, 8, 4, 2100, 64),
 ])
 def test_attention_matches_oracle(q4, M, Hq, Hkv, ctx, splits):
     dev = torch.device("cuda")
