@@ -12,8 +12,8 @@
 //
 // Kernel 1 (tree_attn_kernel<G>): a workgroup per (KV head, run of pages),
 // one compute wave per query head of that KV head (G = Hq / Hkv) and two
-// loader waves; when the runs fill at most half the CUs, two workgroups per
-// (KV head, run), each with G = Hq / Hkv / 2 of its query heads.
+// loader waves; when the runs leave CUs idle, h workgroups per (KV head,
+// run), each with G = Hq / Hkv / h of its query heads (h up to 6).
 //  * Per page the loader waves load the 8 KiB of keys ([32 tokens][256])
 //    and 8 KiB of values (stored transposed, [256][32]) with their scales
 //    into their registers, four pages ahead, turn the int8 keys into bf16
@@ -22,8 +22,9 @@
 //    next is written).
 //  * Scores on MFMA: S^T[token][node] = K Q^T, sixteen
 //    v_mfma_f32_16x16x32_bf16 per page and wave (two token tiles, eight
-//    32-dim steps), the key scale and the softmax scale applied per token
-//    afterwards; the queries stay in registers for the whole run.
+//    32-dim steps), the key scale times the softmax scale (the loaders
+//    form the product) applied per token afterwards; the queries stay in
+//    registers for the whole run.
 //  * Online softmax per node in base 2, its reference maximum moved only
 //    when a score passes it by more than 2^8; each node's 32 scores of a
 //    page sit in 4 lanes x 8 registers.  The ancestor mask applies to tree positions,
@@ -36,6 +37,8 @@
 //    group g), so the probabilities need no shuffle.
 //  * A run over the whole context writes normalised outputs; otherwise the
 //    run writes its unnormalised output and (max, sum) to the workspace.
+//  * Maxima and sums over a node's four lane groups use the gfx950 permlane
+//    swaps; the page's largest value scale comes from the loader.
 // Kernel 2 (attn_combine_kernel): per (node, query head) the runs' partial
 // results are merged with their max and sum.
 #include <hip/hip_runtime.h>
