@@ -892,7 +892,6 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
   // running sums of the workgroup's tiles over parts of K taken in turn
   __shared__ f32x4 tacc[kSeq ? (kPlanar ? kInMaxTilesPlanar : kInMaxTiles) * RT * 64 : 1];
 
-  const int T = (N + 15) >> 4;
   const int Q = K >> 8;
   const int G8 = K >> 6;  // groups per row
   const int lane = threadIdx.x & 63;
@@ -906,7 +905,8 @@ __global__ __launch_bounds__(64 * W) void gemm_kslice_kernel(
   const int rank = (b & 7) * (G >> 3) + min(b & 7, G & 7) + (b >> 3);
   // rank -> part group pk of K and tile group g; part group pk holds parts
   // pk * Pin .. pk * Pin + Pin - 1, taken one after another
-  // t0 = floor(T g / Gt) = per g + floor(rem g / Gt), likewise t1
+  // t0 = floor(T g / Gt) = per g + floor(rem g / Gt) for T = ceil(N / 16)
+  // tiles (per and rem come from the host), likewise t1
   const int Gt = static_cast<int>(gr & 0xFFFFu);
   const int rem = static_cast<int>(gr >> 16);
   const int pk = P == 1 ? 0 : small_div(rank, Gt);
