@@ -130,6 +130,22 @@ def test_splits_match_oracle(q4):
         _check(_run(q4, inp, s), want, absw, f"splits {s}")
 
 
+def test_longest_run(q4):
+    """Runs of exactly 1024 pages, the most the kernel stages (its page ids
+    fill its LDS list): 65520 context tokens and 16 nodes make 2048 pages,
+    taken in two runs; every output against the oracle. One run of 2048
+    pages is refused."""
+    dev = torch.device("cuda")
+    ctx = 65520
+    _say(f"case tree attn longest run, ctx {ctx}, splits 2")
+    inp = synth.attn_inputs(16, 24, 4, ctx, seed=43, device=dev)
+    assert q4.q4_tree_attn_plan(16, 24, 4, ctx, splits=2)[0] == 2
+    with pytest.raises(q4.Q4Error):
+        q4.q4_tree_attn_plan(16, 24, 4, ctx, splits=1)
+    want, absw = _oracle(_host(inp))
+    _check(_run(q4, inp, 2), want, absw, "runs of 1024 pages")
+
+
 def test_deterministic(q4):
     dev = torch.device("cuda")
     inp = synth.attn_inputs(16, 24, 4, 2000, seed=42, device=dev)
